@@ -1,0 +1,6 @@
+"""CPU oracle for the Parallax attention operator (test infrastructure only).
+
+Imported only by tests/, the smoke check and the benchmark's CPU-baseline leg.
+It shares no code with the GPU library.
+"""
+from .parallax_oracle import fwd, bwd, decode, exact_lla_projector, visible_range  # noqa: F401

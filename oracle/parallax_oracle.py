@@ -1,0 +1,257 @@
+"""CPU oracle for the Parallax attention operator (test infrastructure only).
+
+Plain, slow, float64 numpy.  Only the tests, the smoke check and the
+benchmark's CPU-baseline leg may import this module; the GPU library never
+does, and this module imports nothing from it.
+
+What is computed, per batch b, query head h (key/value head g = h // (Hq/Hkv))
+and query row i with visible key set J_i:
+
+  s_ij  = scale * q_i . k_j                       (scale = 1/sqrt(d) by default)
+  p_ij  = softmax over j in J_i of s_ij
+  o_i   = sum_j p_ij v_j                          softmax attention output
+  kbar_i= sum_j p_ij k_j                          softmax-weighted key mean
+  u_i   = P_h^T (q_i - kbar_i)                    u_i[a] = sum_b P_h[b][a] (q_i - kbar_i)[b]
+  out_i = o_i + sum_j p_ij (u_i . (k_j - kbar_i)) (v_j - o_i)
+
+Sources: the gist.science technical summary of "Parallax: Parameterized Local
+Linear Attention for Language Modeling", section "Core mechanism": the output
+is the softmax-attention output plus the key/value covariance of the query's
+softmax neighbourhood applied to a probe vector (printed as o^SA - Sigma_KV rho;
+with rho = -u this is the + form above), and the probe replaces the per-query
+solve that exact local linear attention needs (the solve inverts the key
+covariance).  The probe's form u = P^T (q - kbar) with one learned d x d
+projector P per query head is the reading this operator takes (the pages only
+say that a learned map produces the probe); the same section says the boundary
+amplification factor eta is set to zero, so no eta term appears.  Setting P = 0
+gives plain softmax attention (encorp.ai blog, "Parallax keeps softmax", and the
+FAQ answer on converting a pretrained Transformer).
+
+Masks are bottom-right aligned: with offset = Tk - Tq, key j is visible to
+query i iff (not causal or j <= i + offset) and (window <= 0 or
+j > i + offset - window).  A decode query is the newest token: it sees every
+key of its sequence.
+
+Each function also states which tests pin it.  Parity: every function here is
+pinned (see the module docstrings of tests/test_oracle_pins.py).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+ROW_BLOCK = 256
+
+
+def _as_f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def visible_range(i: int, Tq: int, Tk: int, causal: bool, window: int):
+    """Half-open range [lo, hi) of keys that query row i sees (bottom-right aligned mask)."""
+    off = Tk - Tq
+    hi = min(Tk, i + off + 1) if causal else Tk
+    lo = max(0, i + off - window + 1) if window > 0 else 0
+    return lo, max(lo, hi)
+
+
+def _softmax_rows(s, mask):
+    """Softmax of each row over its visible entries; rows with no visible key give all-zero weights."""
+    s = np.where(mask, s, -np.inf)
+    mx = np.max(s, axis=1, keepdims=True)
+    mx = np.where(np.isfinite(mx), mx, 0.0)
+    e = np.where(mask, np.exp(s - mx), 0.0)
+    den = e.sum(axis=1, keepdims=True)
+    p = np.divide(e, den, out=np.zeros_like(e), where=den > 0)
+    lse = np.where(den[:, 0] > 0, mx[:, 0] + np.log(np.where(den[:, 0] > 0, den[:, 0], 1.0)), -np.inf)
+    return p, lse
+
+
+def _row_blocks(Tq, Tk, causal, window, rows):
+    """Yield (query-row index array, lo, hi) groups covering the requested rows."""
+    rows = np.arange(Tq) if rows is None else np.asarray(rows)
+    for b0 in range(0, len(rows), ROW_BLOCK):
+        rr = rows[b0:b0 + ROW_BLOCK]
+        ranges = [visible_range(int(i), Tq, Tk, causal, window) for i in rr]
+        lo = min(r[0] for r in ranges)
+        hi = max(r[1] for r in ranges)
+        yield rr, lo, max(lo, hi)
+
+
+def _mask_rows(rr, lo, hi, Tq, Tk, causal, window):
+    off = Tk - Tq
+    i = rr[:, None] + off
+    j = np.arange(lo, hi)[None, :]
+    m = np.ones((len(rr), hi - lo), dtype=bool)
+    if causal:
+        m &= j <= i
+    if window > 0:
+        m &= j > i - window
+    return m
+
+
+def fwd(q, k, v, P, causal=True, window=0, scale=None, rows=None):
+    """Parallax forward.
+
+    q [B,Tq,Hq,d]; k, v [B,Tk,Hkv,d]; P [Hq,d,d] (one projector per query head)
+    or [B,Tq,Hq,d,d] (one per query, used only for the exact-LLA check case).
+    ``rows`` restricts the computation to a subset of query rows (the others
+    are returned as NaN), which lets tests sample rows of full-size problems.
+
+    Returns float64 arrays out [B,Tq,Hq,d], lse [B,Hq,Tq] (natural log of the
+    softmax denominator, scores scaled), kbar [B,Tq,Hq,d], o [B,Tq,Hq,d].
+    Pinned by: P=0 vs torch SDPA; exact-LLA vs brute-force ridge WLS; constant
+    and affine V; first causal row and window=1; weighted-covariance form
+    (numpy.cov) with rank-one projectors; linearity in P; mask counts.
+    """
+    q, k, v, P = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(P)
+    B, Tq, Hq, d = q.shape
+    _, Tk, Hkv, _ = k.shape
+    assert Hq % Hkv == 0
+    grp = Hq // Hkv
+    per_query = P.ndim == 5
+    if scale is None or scale <= 0:
+        scale = 1.0 / np.sqrt(d)
+    out = np.full(q.shape, np.nan)
+    kbar = np.full(q.shape, np.nan)
+    osa = np.full(q.shape, np.nan)
+    lse = np.full((B, Hq, Tq), np.nan)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // grp
+            K, V = k[b, :, g, :], v[b, :, g, :]
+            for rr, lo, hi in _row_blocks(Tq, Tk, causal, window, rows):
+                Qr = q[b, rr, h, :]
+                mask = _mask_rows(rr, lo, hi, Tq, Tk, causal, window)
+                Kj, Vj = K[lo:hi], V[lo:hi]
+                p, l = _softmax_rows(scale * (Qr @ Kj.T), mask)
+                o = p @ Vj
+                kb = p @ Kj
+                x = Qr - kb
+                if per_query:
+                    u = np.einsum("ib,iba->ia", x, P[b, rr, h])
+                else:
+                    u = x @ P[h]                                   # u[a] = sum_b x[b] P[b][a]
+                # t_ij = u_i . (k_j - kbar_i); centred value v_j - o_i
+                t = u @ Kj.T - np.sum(u * kb, axis=1, keepdims=True)
+                w = p * t
+                c = w @ Vj - np.sum(w, axis=1, keepdims=True) * o   # sum_j w_ij (v_j - o_i)
+                out[b, rr, h] = o + c
+                kbar[b, rr, h] = kb
+                osa[b, rr, h] = o
+                lse[b, h, rr] = l
+    return out, lse, kbar, osa
+
+
+def bwd(q, k, v, P, dout, causal=True, window=0, scale=None):
+    """Gradients of sum(dout * out) with respect to q, k, v and P (chain rule of ``fwd``).
+
+    The pages give no backward; this is the chain rule of the forward definition,
+    written with g = dout, alpha_i = u_i . kbar_i, t_ij = u_i . k_j:
+      out_i = (1 - alpha_i) o_i + sum_j p_ij t_ij v_j
+      du_i  = sum_j p_ij (g_i.v_j) k_j - (g_i.o_i) kbar_i
+      dkbar_i = -(g_i.o_i) u_i - P du_i        dq_i += P du_i     dP += sum_i (q_i - kbar_i) du_i^T
+      dp_ij = (g_i.v_j)(t_ij + 1 - alpha_i) + dkbar_i . k_j
+      ds_ij = p_ij (dp_ij - sum_l p_il dp_il)
+      dq_i += scale sum_j ds_ij k_j
+      dk_j += sum_i [p_ij (g_i.v_j) u_i + p_ij dkbar_i + scale ds_ij q_i]
+      dv_j += sum_i p_ij (t_ij + 1 - alpha_i) g_i
+    dk, dv are summed over the query heads sharing a key/value head; dP over
+    batch and rows, in the orientation of P.  Pinned by: central finite
+    differences of ``fwd``; torch.autograd of an independent torch forward;
+    P=0 against torch SDPA's backward.
+    """
+    q, k, v, P, g_all = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(P), _as_f64(dout)
+    B, Tq, Hq, d = q.shape
+    _, Tk, Hkv, _ = k.shape
+    grp = Hq // Hkv
+    if scale is None or scale <= 0:
+        scale = 1.0 / np.sqrt(d)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dP = np.zeros_like(P)
+    for b in range(B):
+        for h in range(Hq):
+            gk = h // grp
+            K, V = k[b, :, gk, :], v[b, :, gk, :]
+            Ph = P[h]
+            for rr, lo, hi in _row_blocks(Tq, Tk, causal, window, None):
+                Qr, G = q[b, rr, h, :], g_all[b, rr, h, :]
+                mask = _mask_rows(rr, lo, hi, Tq, Tk, causal, window)
+                Kj, Vj = K[lo:hi], V[lo:hi]
+                p, _ = _softmax_rows(scale * (Qr @ Kj.T), mask)
+                o = p @ Vj
+                kb = p @ Kj
+                x = Qr - kb
+                u = x @ Ph
+                alpha = np.sum(u * kb, axis=1, keepdims=True)
+                t = u @ Kj.T
+                gv = G @ Vj.T                                    # g_i . v_j
+                go = np.sum(G * o, axis=1, keepdims=True)        # g_i . o_i
+                du = (p * gv) @ Kj - go * kb
+                Pdu = du @ Ph.T                                  # (P du)[b] = sum_a P[b][a] du[a]
+                dkb = -go * u - Pdu
+                dP[h] += x.T @ du
+                dp = gv * (t + 1.0 - alpha) + dkb @ Kj.T
+                delta = np.sum(p * dp, axis=1, keepdims=True)
+                ds = p * (dp - delta)
+                dq[b, rr, h] += Pdu + scale * (ds @ Kj)
+                dk[b, lo:hi, gk] += (p * gv).T @ u + p.T @ dkb + scale * (ds.T @ Qr)
+                dv[b, lo:hi, gk] += (p * (t + 1.0 - alpha)).T @ G
+    return dq, dk, dv, dP
+
+
+def decode(q, k_cache, v_cache, P, seqlens=None, scale=None):
+    """One new query per sequence against a key/value cache.
+
+    q [B,Hq,d]; caches [B,Lmax,Hkv,d]; seqlens [B] (None: every sequence has
+    length Lmax).  The new token's key and value are already the last cache
+    entry, so query b sees keys 0..seqlens[b]-1.  Equals the last row of
+    ``fwd`` over the cache prefix (that is how it is computed here).
+    Pinned by: P=0 vs torch SDPA, and (through ``fwd``) all forward pins.
+    """
+    q = _as_f64(q)
+    B, Hq, d = q.shape
+    Lmax = k_cache.shape[1]
+    out = np.zeros((B, Hq, d))
+    for b in range(B):
+        L = Lmax if seqlens is None else int(seqlens[b])
+        if L == 0:
+            continue
+        o, _, _, _ = fwd(q[b:b + 1, None], k_cache[b:b + 1, :L], v_cache[b:b + 1, :L], P,
+                         causal=True, window=0, scale=scale)
+        out[b] = o[0, 0]
+    return out
+
+
+def exact_lla_projector(q, k, causal=True, window=0, scale=None, lam=1e-2):
+    """Per-query projector P_i = (Sigma_q,i + lam I)^-1 that turns the operator into exact ridge LLA.
+
+    Sigma_q,i = sum_j p_ij (k_j - kbar_i)(k_j - kbar_i)^T is the softmax-weighted
+    key covariance of query i (the matrix exact local linear attention inverts,
+    per the "Core mechanism" section cited in the module docstring).  With this
+    P (symmetric, so P^T = P) the output is the intercept of the weighted ridge
+    regression of the values on the keys centred at the query.
+    Returns [B,Tq,Hq,d,d] float64.
+    """
+    q, k = _as_f64(q), _as_f64(k)
+    B, Tq, Hq, d = q.shape
+    _, Tk, Hkv, _ = k.shape
+    grp = Hq // Hkv
+    if scale is None or scale <= 0:
+        scale = 1.0 / np.sqrt(d)
+    Pq = np.zeros((B, Tq, Hq, d, d))
+    for b in range(B):
+        for h in range(Hq):
+            K = k[b, :, h // grp, :]
+            for i in range(Tq):
+                lo, hi = visible_range(i, Tq, Tk, causal, window)
+                Kj = K[lo:hi]
+                s = scale * (Kj @ q[b, i, h])
+                p = np.exp(s - s.max())
+                p /= p.sum()
+                kb = p @ Kj
+                Kc = Kj - kb
+                cov = (Kc * p[:, None]).T @ Kc
+                Pq[b, i, h] = np.linalg.inv(cov + lam * np.eye(d))
+    return Pq
