@@ -1,0 +1,232 @@
+"""Benchmark of the Parallax attention operator on one MI355X.
+
+A step is one forward plus one backward of the 1.7B-like layer (B=2, T=8192,
+16 query / 8 key-value heads, d=128, bf16 inputs, causal) on synthetic seeded
+inputs already resident in HBM.  `value` is the algorithmic TFLOP/s of the step
+(forward 12d flop per visible pair + 2d^2 per row, backward 24d per pair + 4d^2
+per row; the fp32 early-row path and precision splits are not counted).  The
+decode workload (64 queries against a 32768-long cache) is timed after the
+steps and reported in its own object.  One JSON line goes to stdout; progress
+goes to stderr.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Parallax attn fwd/bwd TFLOP/s + tokens/s at T=8192,d=128 bf16; % MFMA peak"
+PEAK_F16_TFLOPS = 2516.6     # MI355X dense fp16/bf16 MFMA
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def visible_pairs_rows(w, row_begin=0):
+    """(pairs, rows) over batch and query heads for query rows >= row_begin."""
+    off = w.seqlen_k - w.seqlen_q
+    pairs = 0
+    for i in range(row_begin, w.seqlen_q):
+        hi = min(w.seqlen_k, i + off + 1) if w.causal else w.seqlen_k
+        lo = max(0, i + off - w.window + 1) if w.window > 0 else 0
+        pairs += max(0, hi - lo)
+    nbh = w.batch * w.heads_q
+    return pairs * nbh, max(0, w.seqlen_q - row_begin) * nbh
+
+
+def fwd_flops(w, row_begin=0):
+    pairs, rows = visible_pairs_rows(w, row_begin)
+    return 12 * w.head_dim * pairs + 2 * w.head_dim ** 2 * rows
+
+
+def bwd_flops(w, row_begin=0):
+    pairs, rows = visible_pairs_rows(w, row_begin)
+    return 24 * w.head_dim * pairs + 4 * w.head_dim ** 2 * rows
+
+
+class HipEvents:
+    """Thin ctypes access to HIP events (timing on the library's stream)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        assert self.hip.hipEventCreate(ctypes.byref(ev)) == 0
+        return ev
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+
+def cpu_baseline(w, target_s=15.0):
+    """The oracle (numpy float64) timed on this host on a bounded sample of the workload.
+
+    Sample: batch 0, the two query heads of key/value head 0, all T rows,
+    forward + backward; scaled to TFLOP/s with the same algorithmic count.
+    """
+    import numpy as np
+    import torch
+    import oracle
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    ws = W.scaled(w, batch=1, heads_q=2, heads_kv=1)
+    q, k, v, P, dout = W.make_inputs(ws, device="cpu", with_dout=True)
+    h = lambda t: t.to(torch.float64).numpy()  # noqa: E731
+    t0 = time.perf_counter()
+    oracle.fwd(h(q), h(k), h(v), h(P), causal=True)
+    oracle.bwd(h(q), h(k), h(v), h(P), h(dout), causal=True)
+    dt = time.perf_counter() - t0
+    fl = fwd_flops(ws) + bwd_flops(ws)
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"numpy float64 oracle, forward+backward of batch 0, query heads 0-1 (key/value head 0), "
+                      f"all {ws.seqlen_q} rows of the {w.name} workload: {fl / 1e9:.1f} GFLOP in {dt:.1f} s",
+            "seconds": round(dt, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="layer17")
+    ap.add_argument("--split-rows", type=int, default=-1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the Parallax operator here is a single-GPU kernel "
+              "library with no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    if not os.path.exists(os.path.join(ROOT, "softmax_learned_covariance_amd", "libparallax.so")):
+        from softmax_learned_covariance_amd import build as b
+        b.build()
+    import torch
+    import softmax_learned_covariance_amd as plx
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    w = W.WORKLOADS[args.workload]
+    log(f"workload {w}")
+    q, k, v, P, dout = W.make_inputs(w, device=dev, with_dout=True)
+    torch.cuda.synchronize()
+    lib = plx.get_lib()
+    ev = HipEvents()
+    split = args.split_rows
+
+    def step():
+        out, lse, kbar, o = plx.parallax_attn_fwd(q, k, v, P, split_rows=split)
+        plx.parallax_attn_bwd(q, k, v, P, out, dout, lse, kbar, o, split_rows=split)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"warmup step {i + 1}/{args.warmup} done")
+
+    K = args.steps
+    evs = {n: [(ev.create(), ev.create()) for _ in range(K)] for n in ("fwd", "bwd")}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        lib.parallax_set_kernel_events(*evs["fwd"][i])
+        out, lse, kbar, o = plx.parallax_attn_fwd(q, k, v, P, split_rows=split)
+        lib.parallax_set_kernel_events(*evs["bwd"][i])
+        plx.parallax_attn_bwd(q, k, v, P, out, dout, lse, kbar, o, split_rows=split)
+    lib.parallax_set_kernel_events(None, None)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    log(f"timed {K} steps in {elapsed:.3f} s")
+
+    # main-kernel rows: the fast path leaves rows < split_rows to the fp32 kernel
+    fast = w.dtype == "bf16" and w.head_dim == 128
+    r0 = (256 if split < 0 else split) if fast else 0
+    r0 = min(r0, w.seqlen_q)
+    kern = {}
+    for n, flops_fn in (("fwd", fwd_flops), ("bwd", bwd_flops)):
+        ms = sorted(ev.elapsed_ms(a, b) for a, b in evs[n])
+        avg = sum(ms) / len(ms)
+        fl = flops_fn(w, r0)
+        kern[n] = {"avg_ms": round(avg, 4), "median_ms": round(ms[len(ms) // 2], 4),
+                   "algorithmic_flop": fl, "tflops": round(fl / (avg * 1e-3) / 1e12, 3)}
+    ms_step = elapsed / K * 1e3
+    step_flops = fwd_flops(w) + bwd_flops(w)
+    value = step_flops / (ms_step * 1e-3) / 1e12
+    dom = max(kern, key=lambda n: kern[n]["avg_ms"])
+    dk = kern[dom]
+    roofline = {"bound": "mfma", "achieved": dk["tflops"], "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(dk["tflops"] / PEAK_F16_TFLOPS, 4), "traffic": None,
+                "kernel": f"{dom} main kernel", "avg_ms": dk["avg_ms"],
+                "algorithmic_flop_per_launch": dk["algorithmic_flop"]}
+    result = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (seeded N(0,1) inputs rounded to bf16, K rows normed to sqrt(d), P ~ N(0, 0.02^2))",
+        "config": {"workload": f"{w.name}: Parallax layer forward+backward, B={w.batch}, T={w.seqlen_q}, "
+                               f"Hq={w.heads_q}, Hkv={w.heads_kv}, d={w.head_dim}, causal, bf16 inputs, fp32 outputs",
+                   "global_batch": w.batch, "seq_len": w.seqlen_q, "parallelism": "single GPU",
+                   "split_rows": r0},
+        "tokens_per_s": round(w.batch * w.seqlen_q / (ms_step * 1e-3), 1),
+        "kernels": kern,
+        "roofline": roofline,
+    }
+
+    if not args.no_decode:
+        wd = W.WORKLOADS["decode"]
+        log("decode workload")
+        del q, k, v, P, dout
+        torch.cuda.empty_cache()
+        qd, kc, vc, Pd = W.make_inputs(wd, device=dev)
+        for _ in range(2):
+            plx.parallax_attn_decode(qd, kc, vc, Pd)
+        torch.cuda.synchronize()
+        Kd = max(5, K)
+        dev_ev = [(ev.create(), ev.create()) for _ in range(Kd)]
+        t0 = time.perf_counter()
+        for i in range(Kd):
+            lib.parallax_set_kernel_events(*dev_ev[i])
+            plx.parallax_attn_decode(qd, kc, vc, Pd)
+        lib.parallax_set_kernel_events(None, None)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / Kd
+        kms = sum(ev.elapsed_ms(a, b) for a, b in dev_ev) / Kd
+        cache_bytes = 2 * wd.batch * wd.seqlen_k * wd.heads_kv * wd.head_dim * 2
+        other = (wd.batch * wd.heads_q * wd.head_dim) * (2 + 4) + wd.heads_q * wd.head_dim ** 2 * 2
+        gbs = (cache_bytes + other) / (kms * 1e-3) / 1e9
+        result["decode"] = {
+            "workload": f"decode: B={wd.batch} new queries, cache L={wd.seqlen_k}, Hq={wd.heads_q}, "
+                        f"Hkv={wd.heads_kv}, d={wd.head_dim}, bf16",
+            "ms_per_call": round(dt * 1e3, 4), "tokens_per_s": round(wd.batch / dt, 1),
+            "main_kernel_avg_ms": round(kms, 4),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "algorithmic_bytes_per_launch": cache_bytes + other}}
+        log(f"decode {kms:.3f} ms/kernel, {gbs:.0f} GB/s")
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on host cores)")
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

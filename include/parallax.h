@@ -1,0 +1,161 @@
+/*
+ * parallax.h -- C ABI of the Parallax attention operator for AMD Instinct MI355X (gfx950).
+ *
+ * The operator (gist.science technical summary of "Parallax: Parameterized Local
+ * Linear Attention for Language Modeling", section "Core mechanism": softmax
+ * attention plus the softmax-weighted key/value covariance applied to a probe
+ * vector; the probe comes from a learned projector instead of the per-query
+ * linear solve of exact local linear attention).  Per batch b, query head h
+ * (key/value head g = h / (heads_q / heads_kv)) and query row i:
+ *
+ *   p_ij   = softmax_j (scale * q_i . k_j)      over the keys j visible to i
+ *   o_i    = sum_j p_ij v_j                      kbar_i = sum_j p_ij k_j
+ *   u_i    = P_h^T (q_i - kbar_i)                u_i[a] = sum_b P_h[b][a] (q_i - kbar_i)[b]
+ *   out_i  = o_i + sum_j p_ij (u_i . (k_j - kbar_i)) (v_j - o_i)
+ *
+ * P = 0 gives plain softmax attention (encorp.ai blog, "Parallax keeps softmax"
+ * and its FAQ).  The probe's form u = P^T (q - kbar) with one d x d projector
+ * per query head is this library's reading of "a learned map produces the probe".
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates no device memory; scratch space is the caller's `workspace`.
+ *   - Tensors are dense and contiguous in the layouts stated per argument
+ *     (row-major, last index fastest).  Inputs q, k, v, P, dout have the dtype
+ *     `desc->dtype` (fp32 or bf16); every output is fp32.
+ *   - Masks are bottom-right aligned: with off = seqlen_k - seqlen_q, key j is
+ *     visible to query i iff (!causal || j <= i + off) && (window <= 0 ||
+ *     j > i + off - window).  A row that sees no key gets out = o = kbar = 0 and
+ *     lse = -inf.
+ *   - Arguments are validated before anything is launched; on any error status
+ *     nothing is launched and no output is written.  parallax_last_error()
+ *     then returns a description (thread-local).
+ *   - Work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL is
+ *     the default stream).  Faults during execution surface at the caller's next
+ *     synchronisation, not as a status here.  Apart from the thread-local
+ *     profiling hook below, the library keeps no state between calls and is
+ *     safe to call from several threads.
+ */
+#ifndef PARALLAX_H
+#define PARALLAX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PARALLAX_ABI_VERSION 1
+
+typedef enum {
+  PLX_OK = 0,
+  PLX_ERR_INVALID = 1,      /* null pointer, negative size, heads_q % heads_kv != 0, ... */
+  PLX_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. head_dim > 128) */
+  PLX_ERR_WORKSPACE = 3,    /* workspace_bytes smaller than the matching *_workspace() query */
+  PLX_ERR_HIP = 4           /* a HIP launch call returned an error */
+} plx_status;
+
+typedef enum { PLX_F32 = 0, PLX_BF16 = 1 } plx_dtype;
+
+typedef struct {
+  int32_t batch;          /* B  >= 0 */
+  int32_t seqlen_q;       /* Tq >= 0 (decode: must be 1) */
+  int32_t seqlen_k;       /* Tk >= 0 (decode: cache capacity Lmax) */
+  int32_t heads_q;        /* Hq >= 1 */
+  int32_t heads_kv;       /* Hkv >= 1, Hq % Hkv == 0; query head h uses key/value head h / (Hq/Hkv) */
+  int32_t head_dim;       /* d, 1..128 */
+  int32_t causal;         /* nonzero: bottom-right aligned causal mask (ignored by decode) */
+  int32_t window;         /* <= 0: no window; > 0: keep only the `window` newest visible keys (the query's own included) */
+  float   softmax_scale;  /* <= 0 selects 1/sqrt(head_dim) */
+  int32_t dtype;          /* plx_dtype of q, k, v, P, dout */
+  int32_t p_per_query;    /* 0: P is [Hq][d][d]; 1: P is [B][Tq][Hq][d][d] (forward only) */
+  int32_t split_rows;     /* bf16 fast path: query rows < split_rows run on the fp32 path; < 0 selects the default */
+} plx_attn_desc;
+
+/*
+ * Profiling hook.  While set, every forward, backward and decode call made on
+ * this thread records `before` (a hipEvent_t) on its stream immediately before
+ * launching its main kernel and `after` immediately after it, so the caller can
+ * time that one kernel with hipEventElapsedTime.  The main kernel is the fused
+ * MFMA kernel of the fast path (the forward's two-pass kernel, the backward's
+ * key-block kernel, the decode's split-KV kernel) and the widest generic kernel
+ * otherwise.  Pass NULL, NULL to turn it off.  This thread-local pair is the
+ * library's only state.
+ */
+void parallax_set_kernel_events(void* before, void* after);
+
+/* Library version of this header's ABI (PARALLAX_ABI_VERSION). */
+int parallax_abi_version(void);
+
+/* Static description of a status code. */
+const char* parallax_status_string(plx_status s);
+
+/* Thread-local detail of the last non-OK status returned on this thread ("" if none). */
+const char* parallax_last_error(void);
+
+/*
+ * Forward.  Bytes of workspace needed for `desc` (0 if none); returns 0 for an invalid desc.
+ */
+size_t parallax_attn_fwd_workspace(const plx_attn_desc* desc);
+
+/*
+ * Forward: the output equation above for every query row.
+ *   q     [B][Tq][Hq][d]              k, v  [B][Tk][Hkv][d]
+ *   P     [Hq][d][d], or [B][Tq][Hq][d][d] when desc->p_per_query
+ *   out   [B][Tq][Hq][d] fp32 (required)
+ *   lse   [B][Hq][Tq]    fp32, natural-log softmax denominator of the scaled scores (nullable)
+ *   kbar  [B][Tq][Hq][d] fp32 softmax-weighted key mean (nullable)
+ *   o_sa  [B][Tq][Hq][d] fp32 softmax-attention output o (nullable)
+ * The backward needs lse, kbar and o_sa from the same call.
+ */
+plx_status parallax_attn_fwd(const plx_attn_desc* desc,
+                             const void* q, const void* k, const void* v, const void* P,
+                             float* out, float* lse, float* kbar, float* o_sa,
+                             void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Backward.  Bytes of workspace needed for `desc`; returns 0 for an invalid desc. */
+size_t parallax_attn_bwd_workspace(const plx_attn_desc* desc);
+
+/*
+ * Backward: gradients of sum(dout * out).  The pages give no backward; this is
+ * the chain rule of the forward definition.
+ *   q, k, v, P        as in the forward (p_per_query must be 0)
+ *   out, lse, kbar, o_sa   the forward's outputs for the same inputs (all required)
+ *   dout  [B][Tq][Hq][d]   dtype desc->dtype
+ *   dq    [B][Tq][Hq][d] fp32     dk, dv [B][Tk][Hkv][d] fp32 (summed over the query heads of each group)
+ *   dP    [Hq][d][d] fp32 (summed over batch and rows; same orientation as P)
+ * Every gradient is overwritten (not accumulated).  Results are deterministic.
+ */
+plx_status parallax_attn_bwd(const plx_attn_desc* desc,
+                             const void* q, const void* k, const void* v, const void* P,
+                             const float* out, const void* dout,
+                             const float* lse, const float* kbar, const float* o_sa,
+                             float* dq, float* dk, float* dv, float* dP,
+                             void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Decode.  Bytes of workspace needed for `desc`; returns 0 for an invalid desc. */
+size_t parallax_attn_decode_workspace(const plx_attn_desc* desc);
+
+/*
+ * Decode: one new query per sequence against a key/value cache (the decode path
+ * of the pages' hardware section).  The new token's key and value are already
+ * the last entry of its sequence, so query b sees cache rows
+ * [max(0, L_b - window), L_b) with L_b = seqlens_k[b] (or Lmax when seqlens_k is
+ * NULL).  desc->seqlen_q must be 1, desc->seqlen_k is Lmax, desc->causal is
+ * ignored, desc->p_per_query must be 0.  seqlens_k values are clamped to
+ * [0, Lmax]; a sequence of length 0 gets out = 0.
+ *   q        [B][Hq][d]            k_cache, v_cache [B][Lmax][Hkv][d]
+ *   seqlens_k [B] int32 device array (nullable)
+ *   P        [Hq][d][d]            out [B][Hq][d] fp32
+ */
+plx_status parallax_attn_decode(const plx_attn_desc* desc,
+                                const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* seqlens_k, const void* P, float* out,
+                                void* workspace, size_t workspace_bytes, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PARALLAX_H */

@@ -1,0 +1,207 @@
+"""Parallax attention on AMD Instinct MI355X: thin Python binding of libparallax.so.
+
+The binding only marshals arguments: it checks shapes and dtypes, allocates the
+output tensors and the workspace with PyTorch, and calls the C entry points
+declared in include/parallax.h on the current HIP stream.  Every step of the
+operator runs in the library's HIP kernels; there is no Python or CPU fallback,
+and the first call raises ImportError when the library has not been built
+(``python -m softmax_learned_covariance_amd.build``).
+
+Functions (same names as the C entry points):
+
+    out, lse, kbar, o = parallax_attn_fwd(q, k, v, P, causal=True, window=0, scale=None)
+    dq, dk, dv, dP    = parallax_attn_bwd(q, k, v, P, out, dout, lse, kbar, o, causal=True, ...)
+    out               = parallax_attn_decode(q, k_cache, v_cache, P, seqlens=None, window=0, scale=None)
+
+Layouts: q [B,Tq,Hq,d] (decode [B,Hq,d]); k, v [B,Tk,Hkv,d]; P [Hq,d,d] (or
+[B,Tq,Hq,d,d] per query, forward only); outputs float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libparallax.so")
+
+PLX_OK, PLX_ERR_INVALID, PLX_ERR_UNSUPPORTED, PLX_ERR_WORKSPACE, PLX_ERR_HIP = range(5)
+PLX_F32, PLX_BF16 = 0, 1
+
+
+class PlxAttnDesc(ctypes.Structure):
+    """Mirror of plx_attn_desc (include/parallax.h)."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("seqlen_q", ctypes.c_int32), ("seqlen_k", ctypes.c_int32),
+        ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("causal", ctypes.c_int32), ("window", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32), ("p_per_query", ctypes.c_int32), ("split_rows", ctypes.c_int32),
+    ]
+
+
+class ParallaxError(RuntimeError):
+    def __init__(self, status, detail):
+        super().__init__(f"{detail} [status {status}]")
+        self.status = status
+
+
+_vp, _sz, _st = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+_DESC = ctypes.POINTER(PlxAttnDesc)
+SIGNATURES = {
+    "parallax_set_kernel_events": (None, [_vp, _vp]),
+    "parallax_abi_version": (ctypes.c_int, []),
+    "parallax_status_string": (ctypes.c_char_p, [_st]),
+    "parallax_last_error": (ctypes.c_char_p, []),
+    "parallax_attn_fwd_workspace": (_sz, [_DESC]),
+    "parallax_attn_fwd": (_st, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "parallax_attn_bwd_workspace": (_sz, [_DESC]),
+    "parallax_attn_bwd": (_st, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "parallax_attn_decode_workspace": (_sz, [_DESC]),
+    "parallax_attn_decode": (_st, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+}
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Loads libparallax.so and declares the C signatures; raises if it is missing."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m softmax_learned_covariance_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_LIB = None
+
+
+def get_lib() -> ctypes.CDLL:
+    """The loaded library (loaded on first use)."""
+    global _LIB
+    if _LIB is None:
+        _LIB = load_library()
+    return _LIB
+
+
+def _check(status):
+    if status != PLX_OK:
+        raise ParallaxError(status, get_lib().parallax_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return PLX_F32
+    if t.dtype == torch.bfloat16:
+        return PLX_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: use float32 or bfloat16")
+
+
+def _need(t, name, dtype, shape, device):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype} != {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def make_desc(B, Tq, Tk, Hq, Hkv, d, causal=True, window=0, scale=None, dtype=PLX_BF16,
+              p_per_query=False, split_rows=-1) -> PlxAttnDesc:
+    return PlxAttnDesc(B, Tq, Tk, Hq, Hkv, d, int(bool(causal)), int(window or 0),
+                       float(scale) if scale else 0.0, dtype, int(bool(p_per_query)), int(split_rows))
+
+
+def _workspace(nbytes, device):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def parallax_attn_fwd(q, k, v, P, causal=True, window=0, scale=None, split_rows=-1):
+    """Forward; returns (out, lse, kbar, o_sa), all float32 (see include/parallax.h)."""
+    B, Tq, Hq, d = q.shape
+    Tk, Hkv = k.shape[1], k.shape[2]
+    dt = _dtype_code(q)
+    per_query = P.dim() == 5
+    _need(q, "q", q.dtype, (B, Tq, Hq, d), q.device)
+    _need(k, "k", q.dtype, (B, Tk, Hkv, d), q.device)
+    _need(v, "v", q.dtype, (B, Tk, Hkv, d), q.device)
+    _need(P, "P", q.dtype, (B, Tq, Hq, d, d) if per_query else (Hq, d, d), q.device)
+    desc = make_desc(B, Tq, Tk, Hq, Hkv, d, causal, window, scale, dt, per_query, split_rows)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    out = torch.empty((B, Tq, Hq, d), **f32)
+    lse = torch.empty((B, Hq, Tq), **f32)
+    kbar = torch.empty((B, Tq, Hq, d), **f32)
+    osa = torch.empty((B, Tq, Hq, d), **f32)
+    lib = get_lib()
+    nws = lib.parallax_attn_fwd_workspace(ctypes.byref(desc))
+    ws = _workspace(nws, q.device)
+    _check(lib.parallax_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(P), _ptr(out),
+                                 _ptr(lse), _ptr(kbar), _ptr(osa), _ptr(ws), nws, _stream()))
+    return out, lse, kbar, osa
+
+
+def parallax_attn_bwd(q, k, v, P, out, dout, lse, kbar, o_sa, causal=True, window=0, scale=None,
+                      split_rows=-1):
+    """Backward; returns (dq, dk, dv, dP), all float32 (see include/parallax.h)."""
+    B, Tq, Hq, d = q.shape
+    Tk, Hkv = k.shape[1], k.shape[2]
+    dt = _dtype_code(q)
+    dev = q.device
+    _need(k, "k", q.dtype, (B, Tk, Hkv, d), dev)
+    _need(v, "v", q.dtype, (B, Tk, Hkv, d), dev)
+    _need(P, "P", q.dtype, (Hq, d, d), dev)
+    _need(dout, "dout", q.dtype, (B, Tq, Hq, d), dev)
+    for name, t in (("out", out), ("kbar", kbar), ("o_sa", o_sa)):
+        _need(t, name, torch.float32, (B, Tq, Hq, d), dev)
+    _need(lse, "lse", torch.float32, (B, Hq, Tq), dev)
+    desc = make_desc(B, Tq, Tk, Hq, Hkv, d, causal, window, scale, dt, False, split_rows)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq = torch.empty((B, Tq, Hq, d), **f32)
+    dk = torch.empty((B, Tk, Hkv, d), **f32)
+    dv = torch.empty((B, Tk, Hkv, d), **f32)
+    dP = torch.empty((Hq, d, d), **f32)
+    lib = get_lib()
+    nws = lib.parallax_attn_bwd_workspace(ctypes.byref(desc))
+    ws = _workspace(nws, dev)
+    _check(lib.parallax_attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(P), _ptr(out),
+                                 _ptr(dout), _ptr(lse), _ptr(kbar), _ptr(o_sa), _ptr(dq), _ptr(dk),
+                                 _ptr(dv), _ptr(dP), _ptr(ws), nws, _stream()))
+    return dq, dk, dv, dP
+
+
+def parallax_attn_decode(q, k_cache, v_cache, P, seqlens=None, window=0, scale=None):
+    """Decode; q [B,Hq,d], caches [B,Lmax,Hkv,d], seqlens int32 [B] or None; returns out [B,Hq,d] float32."""
+    B, Hq, d = q.shape
+    Lmax, Hkv = k_cache.shape[1], k_cache.shape[2]
+    dt = _dtype_code(q)
+    dev = q.device
+    _need(k_cache, "k_cache", q.dtype, (B, Lmax, Hkv, d), dev)
+    _need(v_cache, "v_cache", q.dtype, (B, Lmax, Hkv, d), dev)
+    _need(P, "P", q.dtype, (Hq, d, d), dev)
+    if seqlens is not None:
+        _need(seqlens, "seqlens", torch.int32, (B,), dev)
+    desc = make_desc(B, 1, Lmax, Hq, Hkv, d, True, window, scale, dt, False, -1)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    lib = get_lib()
+    nws = lib.parallax_attn_decode_workspace(ctypes.byref(desc))
+    ws = _workspace(nws, dev)
+    _check(lib.parallax_attn_decode(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                    _ptr(seqlens), _ptr(P), _ptr(out), _ptr(ws), nws, _stream()))
+    return out
+
+
+fwd = parallax_attn_fwd
+bwd = parallax_attn_bwd
+decode = parallax_attn_decode

@@ -1,0 +1,233 @@
+// C ABI of the Parallax attention library: argument validation, workspace sizing,
+// and dispatch between the bf16 MFMA fast path and the generic fp32 kernels.
+// Declarations and the argument contract live in include/parallax.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "plx_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+thread_local hipEvent_t g_ev_before = nullptr;
+thread_local hipEvent_t g_ev_after = nullptr;
+
+plx_status fail(plx_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+plx_status ok() {
+  g_last_error[0] = '\0';
+  return PLX_OK;
+}
+
+constexpr int kDefaultSplitRows = 256;
+
+// Checks the descriptor and fills the geometry.  `what` names the entry point.
+plx_status check_desc(const plx_attn_desc* d, const char* what, plx::Geom* g) {
+  if (!d) return fail(PLX_ERR_INVALID, "%s: desc is NULL", what);
+  if (d->batch < 0 || d->seqlen_q < 0 || d->seqlen_k < 0)
+    return fail(PLX_ERR_INVALID, "%s: negative size (batch=%d seqlen_q=%d seqlen_k=%d)", what,
+                d->batch, d->seqlen_q, d->seqlen_k);
+  if (d->heads_q < 1 || d->heads_kv < 1)
+    return fail(PLX_ERR_INVALID, "%s: heads_q=%d heads_kv=%d must be >= 1", what, d->heads_q,
+                d->heads_kv);
+  if (d->heads_q % d->heads_kv != 0)
+    return fail(PLX_ERR_INVALID, "%s: heads_q=%d is not a multiple of heads_kv=%d", what,
+                d->heads_q, d->heads_kv);
+  if (d->head_dim < 1) return fail(PLX_ERR_INVALID, "%s: head_dim=%d < 1", what, d->head_dim);
+  if (d->head_dim > 128)
+    return fail(PLX_ERR_UNSUPPORTED, "%s: head_dim=%d > 128 is not supported", what, d->head_dim);
+  if (d->dtype != PLX_F32 && d->dtype != PLX_BF16)
+    return fail(PLX_ERR_INVALID, "%s: unknown dtype %d", what, d->dtype);
+  if (d->p_per_query != 0 && d->p_per_query != 1)
+    return fail(PLX_ERR_INVALID, "%s: p_per_query must be 0 or 1", what);
+  if (!(d->softmax_scale == d->softmax_scale) || isinf(d->softmax_scale))
+    return fail(PLX_ERR_INVALID, "%s: softmax_scale is not finite", what);
+  g->B = d->batch;
+  g->Tq = d->seqlen_q;
+  g->Tk = d->seqlen_k;
+  g->Hq = d->heads_q;
+  g->Hkv = d->heads_kv;
+  g->d = d->head_dim;
+  g->causal = d->causal != 0;
+  g->window = d->window > 0 ? d->window : 0;
+  g->scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.f / sqrtf(static_cast<float>(d->head_dim));
+  g->bf16 = d->dtype == PLX_BF16;
+  g->p_per_query = d->p_per_query;
+  return PLX_OK;
+}
+
+int split_rows_of(const plx_attn_desc* d) {
+  return d->split_rows < 0 ? kDefaultSplitRows : d->split_rows;
+}
+
+plx_status check_ws(size_t need, const void* ws, size_t have, const char* what) {
+  if (have < need)
+    return fail(PLX_ERR_WORKSPACE, "%s: workspace_bytes=%zu < required %zu", what, have, need);
+  if (need > 0 && !ws) return fail(PLX_ERR_INVALID, "%s: workspace is NULL but %zu bytes are required", what, need);
+  return PLX_OK;
+}
+
+plx_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(PLX_ERR_HIP, "%s: HIP error %d (%s)", what, static_cast<int>(e), hipGetErrorString(e));
+  return ok();
+}
+
+size_t fwd_ws(const plx::Geom& g) {
+  return plx::fast_fwd_supported(g) ? plx::fast_fwd_workspace(g) : 0;
+}
+
+size_t bwd_ws(const plx::Geom& g) {
+  return plx::fast_bwd_supported(g) ? plx::fast_bwd_workspace(g) : plx::generic_bwd_workspace(g);
+}
+
+size_t dec_ws(const plx::Geom& g) {
+  return plx::fast_decode_supported(g) ? plx::fast_decode_workspace(g) : 0;
+}
+
+}  // namespace
+
+namespace plx {
+void mark_main_begin(hipStream_t stream) {
+  if (g_ev_before) (void)hipEventRecord(g_ev_before, stream);
+}
+void mark_main_end(hipStream_t stream) {
+  if (g_ev_after) (void)hipEventRecord(g_ev_after, stream);
+}
+}  // namespace plx
+
+extern "C" {
+
+void parallax_set_kernel_events(void* before, void* after) {
+  g_ev_before = static_cast<hipEvent_t>(before);
+  g_ev_after = static_cast<hipEvent_t>(after);
+}
+
+int parallax_abi_version(void) { return PARALLAX_ABI_VERSION; }
+
+const char* parallax_status_string(plx_status s) {
+  switch (s) {
+    case PLX_OK: return "PLX_OK";
+    case PLX_ERR_INVALID: return "PLX_ERR_INVALID: invalid argument";
+    case PLX_ERR_UNSUPPORTED: return "PLX_ERR_UNSUPPORTED: valid but not supported";
+    case PLX_ERR_WORKSPACE: return "PLX_ERR_WORKSPACE: workspace too small";
+    case PLX_ERR_HIP: return "PLX_ERR_HIP: HIP runtime error";
+  }
+  return "unknown plx_status";
+}
+
+const char* parallax_last_error(void) { return g_last_error; }
+
+size_t parallax_attn_fwd_workspace(const plx_attn_desc* desc) {
+  plx::Geom g;
+  if (check_desc(desc, "parallax_attn_fwd_workspace", &g) != PLX_OK) return 0;
+  return fwd_ws(g);
+}
+
+plx_status parallax_attn_fwd(const plx_attn_desc* desc, const void* q, const void* k,
+                             const void* v, const void* P, float* out, float* lse, float* kbar,
+                             float* o_sa, void* workspace, size_t workspace_bytes,
+                             void* hip_stream) {
+  const char* what = "parallax_attn_fwd";
+  plx::Geom g;
+  plx_status st = check_desc(desc, what, &g);
+  if (st != PLX_OK) return st;
+  const bool empty = g.B == 0 || g.Tq == 0;
+  if (!empty && (!q || !P || !out))
+    return fail(PLX_ERR_INVALID, "%s: q, P and out must not be NULL", what);
+  if (!empty && g.Tk > 0 && (!k || !v)) return fail(PLX_ERR_INVALID, "%s: k and v must not be NULL", what);
+  st = check_ws(fwd_ws(g), workspace, workspace_bytes, what);
+  if (st != PLX_OK) return st;
+  if (empty) return ok();
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  hipError_t e;
+  if (plx::fast_fwd_supported(g))
+    e = plx::launch_fast_fwd(g, q, k, v, P, out, lse, kbar, o_sa, split_rows_of(desc), workspace, stream);
+  else
+    e = plx::launch_generic_fwd(g, q, k, v, P, nullptr, out, lse, kbar, o_sa, 0, g.Tq, stream, true);
+  return hip_status(e, what);
+}
+
+size_t parallax_attn_bwd_workspace(const plx_attn_desc* desc) {
+  plx::Geom g;
+  if (check_desc(desc, "parallax_attn_bwd_workspace", &g) != PLX_OK) return 0;
+  return bwd_ws(g);
+}
+
+plx_status parallax_attn_bwd(const plx_attn_desc* desc, const void* q, const void* k,
+                             const void* v, const void* P, const float* out, const void* dout,
+                             const float* lse, const float* kbar, const float* o_sa, float* dq,
+                             float* dk, float* dv, float* dP, void* workspace,
+                             size_t workspace_bytes, void* hip_stream) {
+  const char* what = "parallax_attn_bwd";
+  plx::Geom g;
+  plx_status st = check_desc(desc, what, &g);
+  if (st != PLX_OK) return st;
+  if (g.p_per_query)
+    return fail(PLX_ERR_UNSUPPORTED, "%s: per-query projectors have no backward", what);
+  if (!P || !dP) return fail(PLX_ERR_INVALID, "%s: P and dP must not be NULL", what);
+  const bool rows = g.B > 0 && g.Tq > 0;
+  const bool keys = g.B > 0 && g.Tk > 0;
+  if (rows && (!q || !out || !dout || !lse || !kbar || !o_sa || !dq))
+    return fail(PLX_ERR_INVALID, "%s: q, out, dout, lse, kbar, o_sa and dq must not be NULL", what);
+  if (keys && (!k || !v || !dk || !dv))
+    return fail(PLX_ERR_INVALID, "%s: k, v, dk and dv must not be NULL", what);
+  st = check_ws(bwd_ws(g), workspace, workspace_bytes, what);
+  if (st != PLX_OK) return st;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  hipError_t e;
+  if (plx::fast_bwd_supported(g))
+    e = plx::launch_fast_bwd(g, q, k, v, P, out, dout, lse, kbar, o_sa, dq, dk, dv, dP,
+                             split_rows_of(desc), workspace, stream);
+  else
+    e = plx::launch_generic_bwd(g, q, k, v, P, out, dout, lse, kbar, o_sa, dq, dk, dv, dP,
+                                workspace, stream);
+  return hip_status(e, what);
+}
+
+size_t parallax_attn_decode_workspace(const plx_attn_desc* desc) {
+  plx::Geom g;
+  if (check_desc(desc, "parallax_attn_decode_workspace", &g) != PLX_OK) return 0;
+  if (g.Tq != 1 || g.p_per_query) return 0;
+  g.causal = 1;
+  return dec_ws(g);
+}
+
+plx_status parallax_attn_decode(const plx_attn_desc* desc, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* seqlens_k, const void* P,
+                                float* out, void* workspace, size_t workspace_bytes,
+                                void* hip_stream) {
+  const char* what = "parallax_attn_decode";
+  plx::Geom g;
+  plx_status st = check_desc(desc, what, &g);
+  if (st != PLX_OK) return st;
+  if (g.Tq != 1) return fail(PLX_ERR_INVALID, "%s: seqlen_q must be 1 (got %d)", what, g.Tq);
+  if (g.p_per_query) return fail(PLX_ERR_UNSUPPORTED, "%s: per-query projectors are not supported", what);
+  g.causal = 1;  // the new token is the last entry of its sequence: it sees all of it
+  if (g.B == 0) {
+    st = check_ws(dec_ws(g), workspace, workspace_bytes, what);
+    return st != PLX_OK ? st : ok();
+  }
+  if (!q || !P || !out) return fail(PLX_ERR_INVALID, "%s: q, P and out must not be NULL", what);
+  if (g.Tk > 0 && (!k_cache || !v_cache))
+    return fail(PLX_ERR_INVALID, "%s: k_cache and v_cache must not be NULL", what);
+  st = check_ws(dec_ws(g), workspace, workspace_bytes, what);
+  if (st != PLX_OK) return st;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  hipError_t e;
+  if (plx::fast_decode_supported(g))
+    e = plx::launch_fast_decode(g, q, k_cache, v_cache, seqlens_k, P, out, workspace, stream);
+  else
+    e = plx::launch_generic_fwd(g, q, k_cache, v_cache, P, seqlens_k, out, nullptr, nullptr,
+                                nullptr, 0, 1, stream, true);
+  return hip_status(e, what);
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Internal declarations shared by the library's translation units (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "parallax.h"
+
+namespace plx {
+
+// Problem geometry after validation (all counts are non-negative, Hq % Hkv == 0).
+struct Geom {
+  int B, Tq, Tk, Hq, Hkv, d;
+  int causal, window;
+  float scale;
+  int bf16;          // 1: inputs are bf16, 0: fp32
+  int p_per_query;
+};
+
+// ---- generic kernels: fp32 arithmetic on fp32 or bf16 inputs, any head_dim <= 128 ----
+
+// Forward rows [row_begin, row_end) of every (batch, query head).  seqlens (nullable)
+// overrides Tk per batch (decode); q/out/kbar/osa row stride is Hq*d, lse is [B][Hq][Tq].
+hipError_t launch_generic_fwd(const Geom& g, const void* q, const void* k, const void* v,
+                              const void* P, const int32_t* seqlens, float* out, float* lse,
+                              float* kbar, float* osa, int row_begin, int row_end,
+                              hipStream_t stream, bool mark);
+
+// Workspace of the generic backward in bytes.
+size_t generic_bwd_workspace(const Geom& g);
+
+hipError_t launch_generic_bwd(const Geom& g, const void* q, const void* k, const void* v,
+                              const void* P, const float* out, const void* dout,
+                              const float* lse, const float* kbar, const float* osa,
+                              float* dq, float* dk, float* dv, float* dP, void* ws,
+                              hipStream_t stream);
+
+// ---- bf16 MFMA fast path (head_dim 128) ----
+bool fast_fwd_supported(const Geom& g);
+size_t fast_fwd_workspace(const Geom& g);
+hipError_t launch_fast_fwd(const Geom& g, const void* q, const void* k, const void* v,
+                           const void* P, float* out, float* lse, float* kbar, float* osa,
+                           int split_rows, void* ws, hipStream_t stream);
+
+bool fast_bwd_supported(const Geom& g);
+size_t fast_bwd_workspace(const Geom& g);
+hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const void* v,
+                           const void* P, const float* out, const void* dout,
+                           const float* lse, const float* kbar, const float* osa,
+                           float* dq, float* dk, float* dv, float* dP, int split_rows, void* ws,
+                           hipStream_t stream);
+
+bool fast_decode_supported(const Geom& g);
+size_t fast_decode_workspace(const Geom& g);
+hipError_t launch_fast_decode(const Geom& g, const void* q, const void* kc, const void* vc,
+                              const int32_t* seqlens, const void* P, float* out, void* ws,
+                              hipStream_t stream);
+
+// Records the profiling hook's `before` / `after` event on `stream` (no-op when unset).
+void mark_main_begin(hipStream_t stream);
+void mark_main_end(hipStream_t stream);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace plx

@@ -1,0 +1,130 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and
+rejects bad arguments with the documented status before launching anything."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from tests.util import ROOT, ensure_built
+
+HEADER = os.path.join(ROOT, "include", "parallax.h")
+
+
+@pytest.fixture(scope="module")
+def plx():
+    ensure_built()
+    import softmax_learned_covariance_amd as m
+    m.get_lib()
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(parallax_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(plx):
+    names = declared_functions()
+    assert len(names) == 10, names
+    out = subprocess.run(["nm", "-D", "--defined-only", plx.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (parallax_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    # and the binding declares a signature for each of them
+    assert sorted(plx.SIGNATURES) == names
+
+
+def test_abi_version_and_status_strings(plx):
+    lib = plx.get_lib()
+    hv = int(re.search(r"#define PARALLAX_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert lib.parallax_abi_version() == hv
+    for s in range(5):
+        assert lib.parallax_status_string(s).startswith(b"PLX_")
+    assert lib.parallax_status_string(99) == b"unknown plx_status"
+
+
+def test_desc_layout_matches_header(plx):
+    # 11 int32 fields and one float, no padding
+    assert ctypes.sizeof(plx.PlxAttnDesc) == 48
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def _desc(plx, **kw):
+    base = dict(B=1, Tq=8, Tk=8, Hq=2, Hkv=1, d=16, causal=True, window=0, scale=None,
+                dtype=plx.PLX_F32, p_per_query=False, split_rows=-1)
+    base.update(kw)
+    return plx.make_desc(base["B"], base["Tq"], base["Tk"], base["Hq"], base["Hkv"], base["d"],
+                         base["causal"], base["window"], base["scale"], base["dtype"],
+                         base["p_per_query"], base["split_rows"])
+
+
+def _fwd(plx, desc, q=FAKE, k=FAKE, v=FAKE, P=FAKE, out=FAKE, ws=None, nws=0):
+    lib = plx.get_lib()
+    return lib.parallax_attn_fwd(ctypes.byref(desc) if desc is not None else None, q, k, v, P, out,
+                                 None, None, None, ws, nws, None)
+
+
+def _bwd(plx, desc, ws=FAKE, nws=1 << 40, **null):
+    lib = plx.get_lib()
+    args = {n: FAKE for n in ("q", "k", "v", "P", "out", "dout", "lse", "kbar", "osa", "dq", "dk", "dv", "dP")}
+    args.update(null)
+    return lib.parallax_attn_bwd(ctypes.byref(desc), *args.values(), ws, nws, None)
+
+
+def _dec(plx, desc, q=FAKE, P=FAKE, out=FAKE, ws=FAKE, nws=1 << 40):
+    lib = plx.get_lib()
+    return lib.parallax_attn_decode(ctypes.byref(desc), q, FAKE, FAKE, None, P, out, ws, nws, None)
+
+
+def test_forward_validation(plx):
+    E = plx
+    assert _fwd(plx, None) == E.PLX_ERR_INVALID
+    assert b"NULL" in plx.get_lib().parallax_last_error()
+    assert _fwd(plx, _desc(plx, Hq=3, Hkv=2)) == E.PLX_ERR_INVALID
+    assert _fwd(plx, _desc(plx, B=-1)) == E.PLX_ERR_INVALID
+    assert _fwd(plx, _desc(plx, Hkv=0)) == E.PLX_ERR_INVALID
+    assert _fwd(plx, _desc(plx, d=0)) == E.PLX_ERR_INVALID
+    assert _fwd(plx, _desc(plx, d=129)) == E.PLX_ERR_UNSUPPORTED
+    assert _fwd(plx, _desc(plx, dtype=7)) == E.PLX_ERR_INVALID
+    assert _fwd(plx, _desc(plx, scale=float("nan"))) == E.PLX_ERR_INVALID
+    assert _fwd(plx, _desc(plx), q=None) == E.PLX_ERR_INVALID
+    assert _fwd(plx, _desc(plx), out=None) == E.PLX_ERR_INVALID
+    assert _fwd(plx, _desc(plx), k=None) == E.PLX_ERR_INVALID
+    # empty problems are valid and launch nothing
+    assert _fwd(plx, _desc(plx, B=0)) == E.PLX_OK
+    assert _fwd(plx, _desc(plx, Tq=0), q=None, out=None) == E.PLX_OK
+    assert plx.get_lib().parallax_last_error() == b""
+
+
+def test_workspace_queries(plx):
+    lib = plx.get_lib()
+    assert lib.parallax_attn_fwd_workspace(None) == 0
+    assert lib.parallax_attn_bwd_workspace(ctypes.byref(_desc(plx))) > 0
+    assert lib.parallax_attn_bwd_workspace(ctypes.byref(_desc(plx, Hq=3, Hkv=2))) == 0
+    assert lib.parallax_attn_decode_workspace(ctypes.byref(_desc(plx, Tq=2))) == 0
+
+
+def test_backward_validation(plx):
+    E = plx
+    d = _desc(plx)
+    need = plx.get_lib().parallax_attn_bwd_workspace(ctypes.byref(d))
+    assert _bwd(plx, d, nws=need - 1) == E.PLX_ERR_WORKSPACE
+    assert b"workspace" in plx.get_lib().parallax_last_error()
+    assert _bwd(plx, d, ws=None, nws=need) == E.PLX_ERR_INVALID
+    assert _bwd(plx, _desc(plx, p_per_query=True)) == E.PLX_ERR_UNSUPPORTED
+    assert _bwd(plx, d, lse=None) == E.PLX_ERR_INVALID
+    assert _bwd(plx, d, dP=None) == E.PLX_ERR_INVALID
+    assert _bwd(plx, d, dk=None) == E.PLX_ERR_INVALID
+
+
+def test_decode_validation(plx):
+    E = plx
+    assert _dec(plx, _desc(plx, Tq=2)) == E.PLX_ERR_INVALID
+    assert _dec(plx, _desc(plx, Tq=1, p_per_query=True)) == E.PLX_ERR_UNSUPPORTED
+    assert _dec(plx, _desc(plx, Tq=1), q=None) == E.PLX_ERR_INVALID
+    assert _dec(plx, _desc(plx, Tq=1, B=0)) == E.PLX_OK

@@ -1,0 +1,280 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on the same seeded inputs.
+
+Tolerance metric: max |gpu - oracle| / sqrt(mean(oracle^2)) per output tensor.
+Bars: 1e-5 for fp32 inputs, 2e-2 for bf16 inputs; integer results (visible-key
+counts read back from the log-sum-exp) bit-exact.  Full-size workloads are
+checked on sampled rows (or batch entries) that the oracle computes one by one;
+the normaliser is then the rms over an unbiased random row sample.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.util import ensure_built, host, rel_err, sampled_rel_err
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = 1e-5
+BF16_TOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def plx():
+    ensure_built()
+    import softmax_learned_covariance_amd as m
+    return m
+
+
+def _announce(msg):
+    print(f"[parity] {msg}", flush=True)
+
+
+def _run_fwd(plx, q, k, v, P, **kw):
+    out = plx.parallax_attn_fwd(q, k, v, P, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+# --------------------------------------------------------------------------------------
+# tiny fp32 workload: random P, P = 0, per-query exact-LLA P
+# --------------------------------------------------------------------------------------
+
+def test_tiny_fp32_forward(plx):
+    w = W.WORKLOADS["tiny"]
+    _announce("tiny fp32 forward")
+    q, k, v, P = W.make_inputs(w, device="cuda")
+    for name, PP in (("random P", P), ("P = 0", torch.zeros_like(P))):
+        out, lse, kbar, o = _run_fwd(plx, q, k, v, PP)
+        ref = oracle.fwd(host(q), host(k), host(v), host(PP), causal=True)
+        for got, want, what in ((out, ref[0], "out"), (o, ref[3], "o"), (kbar, ref[2], "kbar")):
+            e = rel_err(host(got), want)
+            assert e <= F32_TOL, f"{name} {what}: {e:.2e}"
+        assert np.max(np.abs(host(lse) - ref[1])) <= 1e-5
+
+
+def test_tiny_fp32_exact_lla(plx):
+    """Per-query P = (Sigma_q + 1e-2 I)^-1.  The fp32 error is conditioning-limited: kappa(Sigma_q + lam I)
+    reaches ~1.6e3 on the first rows, so the bar is 10 * kappa * 2^-24 * (|out| / rms) ~ 3e-3 instead of 1e-5."""
+    w = W.WORKLOADS["tiny"]
+    _announce("tiny fp32 exact-LLA per-query projector")
+    q, k, v, _ = W.make_inputs(w, device="cuda")
+    Pq = oracle.exact_lla_projector(host(q), host(k), causal=True, lam=1e-2)
+    Pt = torch.from_numpy(Pq).to("cuda", torch.float32)
+    out, _, _, _ = _run_fwd(plx, q, k, v, Pt)
+    ref = oracle.fwd(host(q), host(k), host(v), host(Pt), causal=True)[0]
+    e = rel_err(host(out), ref)
+    assert e <= 3e-3, e
+
+
+def test_tiny_fp32_backward(plx):
+    w = W.WORKLOADS["tiny"]
+    _announce("tiny fp32 backward")
+    q, k, v, P, dout = W.make_inputs(w, device="cuda", with_dout=True)
+    out, lse, kbar, o = _run_fwd(plx, q, k, v, P)
+    grads = plx.parallax_attn_bwd(q, k, v, P, out, dout, lse, kbar, o)
+    torch.cuda.synchronize()
+    ref = oracle.bwd(host(q), host(k), host(v), host(P), host(dout), causal=True)
+    for name, got, want in zip(("dq", "dk", "dv", "dP"), grads, ref):
+        e = rel_err(host(got), want)
+        assert e <= F32_TOL, f"{name}: {e:.2e}"
+
+
+# --------------------------------------------------------------------------------------
+# masks and indices: bit-exact visible-key counts
+# --------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("Tq,Tk,causal,window", [(200, 200, True, 0), (77, 301, True, 0),
+                                                  (300, 300, True, 33), (130, 130, False, 0),
+                                                  (129, 257, False, 64), (64, 40, True, 0)])
+def test_mask_counts(plx, dtype, Tq, Tk, causal, window):
+    """Q = 0 gives uniform weights, so round(exp(lse)) is each row's visible-key count."""
+    _announce(f"mask counts {dtype} Tq={Tq} Tk={Tk} causal={causal} window={window}")
+    g = torch.Generator(device="cuda").manual_seed(5)
+    d = 128 if dtype == torch.bfloat16 else 32
+    q = torch.zeros((2, Tq, 4, d), device="cuda", dtype=dtype)
+    k = torch.randn((2, Tk, 2, d), generator=g, device="cuda").to(dtype)
+    v = torch.randn((2, Tk, 2, d), generator=g, device="cuda").to(dtype)
+    P = (torch.randn((4, d, d), generator=g, device="cuda") * 0.02).to(dtype)
+    out, lse, _, _ = _run_fwd(plx, q, k, v, P, causal=causal, window=window)
+    got = np.rint(np.exp(host(lse))).astype(np.int64)
+    want = np.array([oracle.visible_range(i, Tq, Tk, causal, window)[1] -
+                     oracle.visible_range(i, Tq, Tk, causal, window)[0] for i in range(Tq)])
+    assert np.array_equal(got, np.broadcast_to(want, got.shape))
+    empty = want == 0
+    if empty.any():
+        assert np.all(host(out)[:, empty] == 0)
+
+
+def test_gqa_head_mapping(plx):
+    """Each key/value head holds a distinct constant value vector: query head h must return that of head h // 2."""
+    _announce("gqa head mapping")
+    B, T, Hq, Hkv, d = 2, 96, 8, 4, 128
+    g = torch.Generator(device="cuda").manual_seed(6)
+    q = torch.randn((B, T, Hq, d), generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn((B, T, Hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.empty((B, T, Hkv, d), device="cuda", dtype=torch.bfloat16)
+    for hk in range(Hkv):
+        v[:, :, hk, :] = float(hk + 1)
+    P = (torch.randn((Hq, d, d), generator=g, device="cuda") * 0.05).to(torch.bfloat16)
+    out, _, _, _ = _run_fwd(plx, q, k, v, P)
+    for h in range(Hq):
+        assert np.allclose(host(out)[:, :, h], h // 2 + 1, atol=1e-4, rtol=0)
+
+
+# --------------------------------------------------------------------------------------
+# bf16 workloads at reduced size (whole tensors compared), ragged lengths
+# --------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,Tk,window", [(1000, 1000, 0), (333, 333, 0), (300, 700, 0), (700, 700, 100), (1, 1, 0)])
+def test_bf16_forward_small(plx, T, Tk, window):
+    w = W.scaled(W.WORKLOADS["layer06"], batch=2, seqlen_q=T, seqlen_k=Tk, window=window)
+    _announce(f"bf16 forward B=2 T={T} Tk={Tk} window={window}")
+    q, k, v, P = W.make_inputs(w, device="cuda")
+    out, lse, kbar, o = _run_fwd(plx, q, k, v, P, window=window)
+    ref = oracle.fwd(host(q), host(k), host(v), host(P), causal=True, window=window)
+    e = rel_err(host(out), ref[0])
+    assert e <= BF16_TOL, e
+    assert rel_err(host(o), ref[3]) <= BF16_TOL
+    assert rel_err(host(kbar), ref[2]) <= BF16_TOL
+    assert np.max(np.abs(host(lse) - ref[1])) <= 1e-3
+
+
+@pytest.mark.parametrize("T", [520, 257])
+def test_bf16_backward_small(plx, T):
+    w = W.scaled(W.WORKLOADS["train06"], batch=2, seqlen_q=T, seqlen_k=T)
+    _announce(f"bf16 backward B=2 T={T}")
+    q, k, v, P, dout = W.make_inputs(w, device="cuda", with_dout=True)
+    out, lse, kbar, o = _run_fwd(plx, q, k, v, P)
+    grads = plx.parallax_attn_bwd(q, k, v, P, out, dout, lse, kbar, o)
+    torch.cuda.synchronize()
+    ref = oracle.bwd(host(q), host(k), host(v), host(P), host(dout), causal=True)
+    for name, got, want in zip(("dq", "dk", "dv", "dP"), grads, ref):
+        e = rel_err(host(got), want)
+        assert e <= BF16_TOL, f"{name}: {e:.2e}"
+
+
+def test_empty_and_degenerate(plx):
+    _announce("empty and degenerate shapes")
+    dev = "cuda"
+    bf = torch.bfloat16
+    # no keys at all: every row sees nothing
+    q = torch.randn((1, 5, 2, 128), device=dev).to(bf)
+    k = torch.empty((1, 0, 1, 128), device=dev, dtype=bf)
+    P = torch.zeros((2, 128, 128), device=dev, dtype=bf)
+    out, lse, _, _ = _run_fwd(plx, q, k, k, P)
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+    # no queries
+    q0 = torch.empty((1, 0, 2, 128), device=dev, dtype=bf)
+    k1 = torch.randn((1, 4, 1, 128), device=dev).to(bf)
+    out, _, _, _ = _run_fwd(plx, q0, k1, k1, P)
+    assert out.numel() == 0
+    # no batch
+    qb = torch.empty((0, 4, 2, 128), device=dev, dtype=bf)
+    kb = torch.empty((0, 4, 1, 128), device=dev, dtype=bf)
+    out, _, _, _ = _run_fwd(plx, qb, kb, kb, P)
+    assert out.numel() == 0
+
+
+def test_determinism(plx):
+    _announce("determinism")
+    w = W.scaled(W.WORKLOADS["layer06"], batch=1, seqlen_q=640, seqlen_k=640)
+    q, k, v, P, dout = W.make_inputs(w, device="cuda", with_dout=True)
+    a = _run_fwd(plx, q, k, v, P)
+    b = _run_fwd(plx, q, k, v, P)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    ga = plx.parallax_attn_bwd(q, k, v, P, *a[:1], dout, *a[1:])
+    gb = plx.parallax_attn_bwd(q, k, v, P, *a[:1], dout, *a[1:])
+    torch.cuda.synchronize()
+    for x, y in zip(ga, gb):
+        assert torch.equal(x, y)
+
+
+# --------------------------------------------------------------------------------------
+# full-size workloads, sampled rows
+# --------------------------------------------------------------------------------------
+
+def _sample_rows(T, seed, n_uniform=24):
+    r = np.random.default_rng(seed)
+    uniform = np.sort(r.choice(T, size=min(n_uniform, T), replace=False))
+    special = [0, 1, 2, 3, 7, 63, 64, 127, 128, 255, 256, 257, 511, T // 2, T - 2, T - 1]
+    special = [i for i in special if 0 <= i < T]
+    return uniform, np.unique(np.concatenate([uniform, special]))
+
+
+@pytest.mark.parametrize("name", ["layer06", "layer17"])
+def test_full_size_forward_sampled(plx, name):
+    w = W.WORKLOADS[name]
+    _announce(f"full-size forward {name} (sampled rows)")
+    q, k, v, P = W.make_inputs(w, device="cuda")
+    out, lse, _, _ = _run_fwd(plx, q, k, v, P)
+    uniform, rows = _sample_rows(w.seqlen_q, 17)
+    bsel = [0, w.batch - 1]
+    qh, kh, vh = host(q[bsel]), host(k[bsel]), host(v[bsel])
+    Ph = host(P)
+    ref, ref_lse, _, _ = oracle.fwd(qh, kh, vh, Ph, causal=True, rows=rows)
+    got = host(out[bsel])
+    norm = ref[:, uniform]
+    e = sampled_rel_err(got[:, rows], ref[:, rows], norm)
+    assert e <= BF16_TOL, e
+    assert np.max(np.abs(host(lse[bsel])[:, :, rows] - ref_lse[:, :, rows])) <= 1e-3
+
+
+def test_full_size_train_step_sampled(plx):
+    """train06 forward + backward at full size.  dq rows are row-local and sampled; dk and dv are
+    checked for batch 0, key/value head 0 (exact column sums over all rows); dP for query heads 0-1."""
+    w = W.WORKLOADS["train06"]
+    _announce("full-size train06 forward + backward (sampled)")
+    q, k, v, P, dout = W.make_inputs(w, device="cuda", with_dout=True)
+    out, lse, kbar, o = _run_fwd(plx, q, k, v, P)
+    dq, dk, dv, dP = plx.parallax_attn_bwd(q, k, v, P, out, dout, lse, kbar, o)
+    torch.cuda.synchronize()
+    # batch 0, query heads 0 and 1 (key/value head 0) computed exactly by the oracle
+    sl = (slice(0, 1), slice(None), slice(0, 2))
+    rdq, rdk, rdv, rdP = oracle.bwd(host(q[sl]), host(k[0:1, :, 0:1]), host(v[0:1, :, 0:1]),
+                                    host(P[0:2]), host(dout[sl]), causal=True)
+    assert rel_err(host(dq[sl]), rdq) <= BF16_TOL
+    assert rel_err(host(dk[0:1, :, 0:1]), rdk) <= BF16_TOL
+    assert rel_err(host(dv[0:1, :, 0:1]), rdv) <= BF16_TOL
+    # dP sums over the batch: add the remaining batch entries for heads 0-1
+    total = rdP.copy()
+    for b in range(1, w.batch):
+        total += oracle.bwd(host(q[b:b + 1, :, 0:2]), host(k[b:b + 1, :, 0:1]), host(v[b:b + 1, :, 0:1]),
+                            host(P[0:2]), host(dout[b:b + 1, :, 0:2]), causal=True)[3]
+    assert rel_err(host(dP[0:2]), total) <= BF16_TOL
+
+
+def test_full_size_decode_sampled(plx):
+    w = W.WORKLOADS["decode"]
+    _announce("full-size decode (sampled batch entries)")
+    q, kc, vc, P = W.make_inputs(w, device="cuda")
+    out = plx.parallax_attn_decode(q, kc, vc, P)
+    torch.cuda.synchronize()
+    bsel = [0, 21, 63]
+    ref = oracle.decode(host(q[bsel]), host(kc[bsel]), host(vc[bsel]), host(P))
+    e = rel_err(host(out[bsel]), ref)
+    assert e <= BF16_TOL, e
+
+
+def test_decode_seqlens_and_window(plx):
+    _announce("decode with ragged sequence lengths and a window")
+    w = W.scaled(W.WORKLOADS["decode"], batch=5, seqlen_k=1500)
+    q, kc, vc, P = W.make_inputs(w, device="cuda")
+    seqlens = torch.tensor([1500, 1, 0, 777, 1024], dtype=torch.int32, device="cuda")
+    for window in (0, 100):
+        out = plx.parallax_attn_decode(q, kc, vc, P, seqlens=seqlens, window=window)
+        torch.cuda.synchronize()
+        sl = host(seqlens).astype(int)
+        ref = np.zeros(out.shape)
+        for b in range(5):
+            L = sl[b]
+            lo = max(0, L - window) if window else 0
+            if L > 0:
+                ref[b] = oracle.decode(host(q[b:b + 1]), host(kc[b:b + 1, lo:L]), host(vc[b:b + 1, lo:L]), host(P))[0]
+        assert np.all(host(out)[2] == 0)
+        assert rel_err(host(out), ref) <= BF16_TOL
