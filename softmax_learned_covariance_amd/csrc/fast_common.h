@@ -1,0 +1,130 @@
+// Shared pieces of the MFMA fast path (head_dim 128, bf16 inputs): operand
+// types, the fp16 staging layout, power-of-two range scales and wave helpers.
+//
+// Staging.  The MFMA kernels compute with fp16 operands (11 significant bits)
+// and fp32 accumulation.  K, V and P are converted once per call by the prep
+// kernels into fp16 copies laid out for the v_mfma_f32_32x32x16_f16 operand
+// registers, so every LDS read in the hot loops is one 16-byte access:
+//   K16   [B][Tk_pad][Hkv][128]  key rows, d permuted within groups of 16
+//   K16t  [B][Hkv][128][Tk_pad]  transposed, keys permuted within groups of 16
+//   V16t  [B][Hkv][128][Tk_pad]  transposed, keys permuted within groups of 16
+//   P16t  [Hq][128][128]         P16t[h][a][b'] = P[h][b][a], b permuted within groups of 16
+// The permutation of a group of 16 is the involution
+//   position 8*hh + e  <->  element 8*(e/4) + 4*hh + (e%4)      (hh in {0,1}, e in 0..7)
+// which is exactly the order in which a 32x32 accumulator tile holds its rows
+// (lane half hh, register r: row 8*(r/4) + 4*hh + r%4), so an accumulator tile
+// converted to fp16 is directly the B operand of the next MFMA over that index.
+//
+// Range.  bf16 has fp32's exponent range, fp16 does not.  Each tensor X in
+// {Q, K, V, P} is multiplied by s_X = 2^(15 - E(max|X|)) (E(m) = exponent with
+// 2^(E-1) <= m < 2^E), so its largest magnitude lies in [2^14, 2^15): exact
+// (a power of two), never overflows fp16 and keeps small values out of the
+// subnormal range.  Per-row quantities (q - kbar, the probe u) get per-row
+// scales of the same form; results are unscaled in fp32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace plx {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint16_t u16;
+
+constexpr int kD = 128;        // head_dim of the fast path
+constexpr int kKeyTile = 64;   // keys per LDS tile
+
+// permuted position <-> element within a group of 16 (an involution)
+__host__ __device__ constexpr int perm16(int p) { return 8 * ((p & 7) >> 2) + 4 * (p >> 3) + (p & 3); }
+
+__device__ __forceinline__ float bf16_to_f32(u16 b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
+
+// 2^(15 - E(m)) for the magnitude bound m (1 for m == 0 or non-finite m).
+__device__ __forceinline__ float range_scale(float m) {
+  const uint32_t bits = __float_as_uint(m);
+  const int ex = static_cast<int>((bits >> 23) & 0xff);
+  if (m <= 0.f || ex == 0xff) return 1.f;
+  const int E = (ex == 0) ? -126 : ex - 126;   // m < 2^E (subnormals: bound by 2^-126)
+  return __builtin_ldexpf(1.f, 15 - E);
+}
+
+// x from lane l ^ 32 combined with x (sum / max) via the gfx950 half-wave swap.
+__device__ __forceinline__ float xor32_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Packs 8 floats to an fp16 x8 operand (round to nearest even).
+__device__ __forceinline__ f16x8 pack8(float a0, float a1, float a2, float a3, float a4, float a5,
+                                       float a6, float a7) {
+  f16x8 r;
+  r[0] = static_cast<_Float16>(a0);
+  r[1] = static_cast<_Float16>(a1);
+  r[2] = static_cast<_Float16>(a2);
+  r[3] = static_cast<_Float16>(a3);
+  r[4] = static_cast<_Float16>(a4);
+  r[5] = static_cast<_Float16>(a5);
+  r[6] = static_cast<_Float16>(a6);
+  r[7] = static_cast<_Float16>(a7);
+  return r;
+}
+
+// Sum of the 8 fp16 values of an operand, accumulated in fp32 (v_dot2 with ones).
+__device__ __forceinline__ float sum8(f16x8 v, float acc) {
+  const f16x2 one = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+  acc = __builtin_amdgcn_fdot2(f16x2{v[0], v[1]}, one, acc, false);
+  acc = __builtin_amdgcn_fdot2(f16x2{v[2], v[3]}, one, acc, false);
+  acc = __builtin_amdgcn_fdot2(f16x2{v[4], v[5]}, one, acc, false);
+  acc = __builtin_amdgcn_fdot2(f16x2{v[6], v[7]}, one, acc, false);
+  return acc;
+}
+
+// ---- staging buffers inside the caller's workspace ----
+struct Staging {
+  uint32_t* maxbits;   // [4]: max |Q|, |K|, |V|, |P| as float bits (non-negative floats order as uints)
+  _Float16* k16;
+  _Float16* k16t;
+  _Float16* v16t;
+  _Float16* p16t;
+  int Tk_pad;
+  size_t bytes;        // total workspace used
+};
+
+inline Staging staging_layout(void* ws, int B, int Tk, int Hkv, int Hq) {
+  Staging s{};
+  s.Tk_pad = (Tk + kKeyTile - 1) / kKeyTile * kKeyTile;
+  const size_t kv = static_cast<size_t>(B) * s.Tk_pad * Hkv * kD * sizeof(_Float16);
+  const size_t p = static_cast<size_t>(Hq) * kD * kD * sizeof(_Float16);
+  char* base = static_cast<char*>(ws);
+  size_t off = 0;
+  s.maxbits = reinterpret_cast<uint32_t*>(base + off);
+  off += 256;
+  s.k16 = reinterpret_cast<_Float16*>(base + off);
+  off += (kv + 255) / 256 * 256;
+  s.k16t = reinterpret_cast<_Float16*>(base + off);
+  off += (kv + 255) / 256 * 256;
+  s.v16t = reinterpret_cast<_Float16*>(base + off);
+  off += (kv + 255) / 256 * 256;
+  s.p16t = reinterpret_cast<_Float16*>(base + off);
+  off += (p + 255) / 256 * 256;
+  s.bytes = off;
+  return s;
+}
+
+// Launches the staging kernels: max-abs of q (rows [0, Tq)), k, v, P, then the fp16 copies.
+// q may be nullptr (decode stages q itself).
+hipError_t launch_staging(const Staging& s, const void* q, int64_t q_elems, const void* k,
+                          const void* v, const void* P, int B, int Tk, int Hkv, int Hq,
+                          hipStream_t stream);
+
+}  // namespace plx

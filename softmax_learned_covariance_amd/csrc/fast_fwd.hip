@@ -1,0 +1,478 @@
+// Fused two-pass Parallax forward for gfx950 (head_dim 128, bf16 inputs, fp16 MFMA).
+//
+// What it computes (gist.science technical summary of "Parallax: Parameterized
+// Local Linear Attention for Language Modeling", "Core mechanism": softmax
+// output plus the key/value covariance applied to the probe; "Hardware-aware
+// algorithm": a FlashAttention-style streaming algorithm in which both branches
+// share one stream of K/V tiles):
+//   pass 1  online softmax over key tiles, accumulating o and kbar together
+//           (K is streamed as extra value columns next to V);
+//   probe   u = P^T (q - kbar) with MFMA, alpha = u . kbar;
+//   pass 2  the same key tiles again: S = Q K^T and R = U K^T share the K operand
+//           (the pages' joint QK / RK product), p = exp(S - lse),
+//           W = p (R - alpha), c += W V, rs += rowsum(W);
+//   out     o + c - rs * o        (= o + sum_j p_j (u.(k_j - kbar)) (v_j - o)).
+//
+// Work split.  One 512-thread workgroup (8 waves, 2 per SIMD) owns one
+// (batch, key/value head) and a block of query rows for every query head of the
+// group, so the group's heads share each K/V tile in LDS.  Each wave owns 32
+// query rows of one head; in the accumulator tiles lane l (l % 32 = query,
+// l / 32 = half) holds 16 key or feature rows, so row statistics are lane-local
+// plus one half-wave swap.  S^T = K Q^T puts keys in registers: P~^T is then
+// directly the B operand of o^T = V^T P~^T and kbar^T = K^T P~^T (fp16 staging
+// layouts in fast_common.h).  Lazy rescaling: the running maximum only moves
+// when a tile's maximum exceeds it by 8 (log2 units), so the accumulators are
+// rarely rescaled; exp2 arguments are then <= 8 and p~ <= 256 still fits fp16.
+// Key tiles are double-buffered in LDS with XOR-swizzled 16-byte chunks.
+// Blocks are mapped so that all blocks of one (batch, kv head) run on the same
+// XCD (their K/V stay in that XCD's L2), longest (most keys) first.
+#include <math.h>
+
+#include "fast_common.h"
+#include "plx_internal.h"
+
+namespace plx {
+namespace {
+
+constexpr int kWaves = 8;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kTau = 8.f;
+
+struct FwdParams {
+  const u16* q;
+  const _Float16 *k16, *k16t, *v16t, *p16t;
+  const uint32_t* maxbits;
+  float *out, *lse, *kbar, *osa;
+  int B, Tq, Tk, Tk_pad, Hq, Hkv, G, causal, window;
+  float scale;
+  int row_begin, rows_per_block, n_rb;
+};
+
+struct __align__(16) Tiles {
+  _Float16 k[2][kKeyTile * kD];    // [key][d'] 16 chunks per row, chunk ^= key & 7
+  _Float16 kt[2][kD * kKeyTile];   // [d][key'] 8 chunks per row, chunk ^= d & 7
+  _Float16 vt[2][kD * kKeyTile];
+};
+
+__device__ __forceinline__ f16x8 lds_k(const Tiles& T, int buf, int r, int c) {
+  return *reinterpret_cast<const f16x8*>(&T.k[buf][r * kD + ((c ^ (r & 7)) << 3)]);
+}
+__device__ __forceinline__ f16x8 lds_kt(const Tiles& T, int buf, int d, int c) {
+  return *reinterpret_cast<const f16x8*>(&T.kt[buf][d * kKeyTile + ((c ^ (d & 7)) << 3)]);
+}
+__device__ __forceinline__ f16x8 lds_vt(const Tiles& T, int buf, int d, int c) {
+  return *reinterpret_cast<const f16x8*>(&T.vt[buf][d * kKeyTile + ((c ^ (d & 7)) << 3)]);
+}
+
+// Global -> registers for one key tile: 2 chunks of K rows, 2 of Kt, 2 of Vt per thread.
+struct TileRegs {
+  uint4 k[2], kt[2], vt[2];
+};
+
+__device__ __forceinline__ void tile_load(const FwdParams& p, int b, int g, int key0, bool with_kt,
+                                          int tid, TileRegs& R) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int ci = tid + 512 * j;
+    const int r = ci >> 4, c = ci & 15;
+    R.k[j] = *reinterpret_cast<const uint4*>(
+        p.k16 + ((static_cast<int64_t>(b) * p.Tk_pad + key0 + r) * p.Hkv + g) * kD + c * 8);
+    const int d = ci >> 3, c2 = ci & 7;
+    const int64_t toff = ((static_cast<int64_t>(b) * p.Hkv + g) * kD + d) * p.Tk_pad + key0 + c2 * 8;
+    if (with_kt) R.kt[j] = *reinterpret_cast<const uint4*>(p.k16t + toff);
+    R.vt[j] = *reinterpret_cast<const uint4*>(p.v16t + toff);
+  }
+}
+
+__device__ __forceinline__ void tile_store(Tiles& T, int buf, bool with_kt, int tid, const TileRegs& R) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int ci = tid + 512 * j;
+    const int r = ci >> 4, c = ci & 15;
+    *reinterpret_cast<uint4*>(&T.k[buf][r * kD + ((c ^ (r & 7)) << 3)]) = R.k[j];
+    const int d = ci >> 3, c2 = ci & 7;
+    if (with_kt) *reinterpret_cast<uint4*>(&T.kt[buf][d * kKeyTile + ((c2 ^ (d & 7)) << 3)]) = R.kt[j];
+    *reinterpret_cast<uint4*>(&T.vt[buf][d * kKeyTile + ((c2 ^ (d & 7)) << 3)]) = R.vt[j];
+  }
+}
+
+// Loads 4 consecutive bf16 values as floats.
+__device__ __forceinline__ void load4_bf16(const u16* src, float* dst) {
+  const uint2 w = *reinterpret_cast<const uint2*>(src);
+  dst[0] = __uint_as_float(w.x << 16);
+  dst[1] = __uint_as_float(w.x & 0xffff0000u);
+  dst[2] = __uint_as_float(w.y << 16);
+  dst[3] = __uint_as_float(w.y & 0xffff0000u);
+}
+
+// B operand of a product over d for one query row: d in the permuted-16 order, scaled by s.
+__device__ __forceinline__ void load_q_operand(const u16* qrow, bool ok, int hh, float s, f16x8 (&qB)[8]) {
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+    float a[4] = {0.f, 0.f, 0.f, 0.f}, c[4] = {0.f, 0.f, 0.f, 0.f};
+    if (ok) {
+      load4_bf16(qrow + 16 * st + 4 * hh, a);
+      load4_bf16(qrow + 16 * st + 8 + 4 * hh, c);
+    }
+    qB[st] = pack8(a[0] * s, a[1] * s, a[2] * s, a[3] * s, c[0] * s, c[1] * s, c[2] * s, c[3] * s);
+  }
+}
+
+__global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
+  __shared__ Tiles T;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, ql = l & 31, hh = l >> 5;
+
+  // block -> (batch, kv head, row block)
+  int pair, rb;
+  {
+    const int npairs = p.B * p.Hkv, id = blockIdx.x;
+    if ((npairs & 7) == 0) {
+      const int ppx = npairs >> 3, slot = id >> 3;
+      rb = p.n_rb - 1 - slot / ppx;
+      pair = (id & 7) + 8 * (slot % ppx);
+    } else {
+      rb = p.n_rb - 1 - id / npairs;
+      pair = id % npairs;
+    }
+  }
+  const int b = pair / p.Hkv, g = pair % p.Hkv;
+  const int wph = kWaves / p.G;
+  const int h = g * p.G + w / wph;
+  const int r0 = p.row_begin + rb * p.rows_per_block;
+  const int i0 = r0 + (w % wph) * 32;
+  const int row = i0 + ql;
+  const bool row_ok = row < p.Tq;
+  const int off = p.Tk - p.Tq;
+
+  const float sQ = range_scale(__uint_as_float(p.maxbits[0]));
+  const float sK = range_scale(__uint_as_float(p.maxbits[1]));
+  const float sV = range_scale(__uint_as_float(p.maxbits[2]));
+  const float sP = range_scale(__uint_as_float(p.maxbits[3]));
+  const float cS = p.scale * kLog2e / (sQ * sK);
+
+  const int64_t qoff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * kD;
+  const u16* qrow = p.q + qoff;
+
+  // key ranges: block, wave (first / last row), lane (its row)
+  const int rlast = min(r0 + p.rows_per_block, p.Tq) - 1;
+  const int kend = p.causal ? min(p.Tk, rlast + off + 1) : p.Tk;
+  const int kbeg = p.window > 0 ? max(0, r0 + off - p.window + 1) : 0;
+  const int t_beg = kbeg / kKeyTile;
+  const int t_end = kend > kbeg ? (kend + kKeyTile - 1) / kKeyTile : t_beg;
+  const int wlast = min(i0 + 31, p.Tq - 1);
+  const bool wave_rows = i0 < p.Tq;
+  const int w_kend = wave_rows ? (p.causal ? min(p.Tk, wlast + off + 1) : p.Tk) : 0;
+  const int w_kbeg = p.window > 0 ? max(0, i0 + off - p.window + 1) : 0;
+  const int w_full_end = p.causal ? min(p.Tk, i0 + off + 1) : p.Tk;                       // every row sees keys < this
+  const int w_full_beg = p.window > 0 ? max(0, wlast + off - p.window + 1) : 0;           // ... and >= this
+  const int r_kend = row_ok ? (p.causal ? min(p.Tk, row + off + 1) : p.Tk) : 0;
+  const int r_kbeg = p.window > 0 ? max(0, row + off - p.window + 1) : 0;
+
+  f16x8 qB[8];
+  load_q_operand(qrow, row_ok, hh, sQ, qB);
+
+  // ---------------- pass 1 ----------------
+  f32x16 accO[4], accK[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    accO[mt] = f32x16{};
+    accK[mt] = f32x16{};
+  }
+  float m_used = -INFINITY, lpart = 0.f;
+  TileRegs st;
+  if (t_beg < t_end) {
+    tile_load(p, b, g, t_beg * kKeyTile, true, tid, st);
+    tile_store(T, 0, true, tid, st);
+  }
+  __syncthreads();
+  for (int kt = t_beg; kt < t_end; ++kt) {
+    const int buf = (kt - t_beg) & 1;
+    const bool more = kt + 1 < t_end;
+    if (more) tile_load(p, b, g, (kt + 1) * kKeyTile, true, tid, st);
+    const int key0 = kt * kKeyTile;
+    if (key0 < w_kend && key0 + kKeyTile > w_kbeg) {
+      f32x16 S[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        S[0] = mfma(lds_k(T, buf, ql, 2 * s + hh), qB[s], S[0]);
+        S[1] = mfma(lds_k(T, buf, 32 + ql, 2 * s + hh), qB[s], S[1]);
+      }
+      const bool full = key0 + kKeyTile <= w_full_end && key0 >= w_full_beg;
+      if (!full) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (key >= r_kend || key < r_kbeg) S[kb][r] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][r]);
+      mx = xor32_max(mx);
+      const float mt_ = mx * cS;
+      const bool need = mt_ > m_used + kTau;
+      if (__ballot(need) != 0) {
+        const float f = need ? exp2f(m_used - mt_) : 1.f;
+        m_used = need ? mt_ : m_used;
+        lpart *= f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          accO[mt] *= f;
+          accK[mt] *= f;
+        }
+      }
+      const float mb = m_used == -INFINITY ? 0.f : m_used;
+      f16x8 pB[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kb = i >> 1, t8 = (i & 1) * 8;
+        float e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[j] = __builtin_amdgcn_exp2f(fmaf(S[kb][t8 + j], cS, -mb));
+        pB[i] = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+        lpart = sum8(pB[i], lpart);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          accO[mt] = mfma(lds_vt(T, buf, 32 * mt + ql, 2 * i + hh), pB[i], accO[mt]);
+          accK[mt] = mfma(lds_kt(T, buf, 32 * mt + ql, 2 * i + hh), pB[i], accK[mt]);
+        }
+    }
+    if (more) tile_store(T, buf ^ 1, true, tid, st);
+    __syncthreads();
+  }
+
+  // ---------------- epilogue 1: o, kbar, lse ----------------
+  const float L = xor32_sum(lpart);
+  const bool has = L > 0.f;
+  const float invL = has ? 1.f / L : 0.f;
+  const float lse2 = has ? m_used + __log2f(L) : -INFINITY;
+  float* obuf = p.osa;
+  if (row_ok) {
+    if (p.lse && hh == 0) p.lse[(static_cast<int64_t>(b) * p.Hq + h) * p.Tq + row] = lse2 * kLn2;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * mt + 8 * j + 4 * hh;
+        const float fo = invL / sV, fk = invL / sK;
+        const float4 ov = {accO[mt][4 * j] * fo, accO[mt][4 * j + 1] * fo, accO[mt][4 * j + 2] * fo,
+                           accO[mt][4 * j + 3] * fo};
+        *reinterpret_cast<float4*>(obuf + qoff + d) = ov;
+        if (p.kbar) {
+          const float4 kv = {accK[mt][4 * j] * fk, accK[mt][4 * j + 1] * fk, accK[mt][4 * j + 2] * fk,
+                             accK[mt][4 * j + 3] * fk};
+          *reinterpret_cast<float4*>(p.kbar + qoff + d) = kv;
+        }
+      }
+  }
+
+  // ---------------- probe u = P^T (q - kbar) ----------------
+  // kbar (unscaled) and x = q - kbar in the accumulator layout: lane (row, hh), d = 32 mt + 8 (r/4) + 4 hh + r%4
+  float kbv[4][16];
+  f16x8 xB[8];
+  float alpha_s = 0.f, sU = 1.f;
+  {
+    float xv[4][16];
+    float xmax = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float qv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (row_ok) load4_bf16(qrow + 32 * mt + 8 * j + 4 * hh, qv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * j + e;
+          kbv[mt][r] = accK[mt][r] * (invL / sK);
+          xv[mt][r] = qv[e] - kbv[mt][r];
+          xmax = fmaxf(xmax, fabsf(xv[mt][r]));
+        }
+      }
+    xmax = xor32_max(xmax);
+    const float sX = range_scale(xmax);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int mt = s >> 1, t8 = (s & 1) * 8;
+      xB[s] = pack8(xv[mt][t8] * sX, xv[mt][t8 + 1] * sX, xv[mt][t8 + 2] * sX, xv[mt][t8 + 3] * sX,
+                    xv[mt][t8 + 4] * sX, xv[mt][t8 + 5] * sX, xv[mt][t8 + 6] * sX, xv[mt][t8 + 7] * sX);
+    }
+    // U^T = P16t X^T
+    f32x16 accU[4];
+    const _Float16* prow = p.p16t + (static_cast<int64_t>(h) * kD + ql) * kD + hh * 8;
+#pragma unroll
+    for (int am = 0; am < 4; ++am) {
+      accU[am] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        accU[am] = mfma(*reinterpret_cast<const f16x8*>(prow + 32 * am * kD + 16 * s), xB[s], accU[am]);
+    }
+    const float fu = 1.f / (sX * sP);
+    float umax = 0.f;
+#pragma unroll
+    for (int am = 0; am < 4; ++am)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        accU[am][r] *= fu;
+        umax = fmaxf(umax, fabsf(accU[am][r]));
+      }
+    umax = xor32_max(umax);
+    sU = range_scale(umax);
+    // U-hat operand (reusing xB's registers) and alpha = U-hat . kbar in the scaled units of pass 2
+    float alpha = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int am = s >> 1, t8 = (s & 1) * 8;
+      xB[s] = pack8(accU[am][t8] * sU, accU[am][t8 + 1] * sU, accU[am][t8 + 2] * sU, accU[am][t8 + 3] * sU,
+                    accU[am][t8 + 4] * sU, accU[am][t8 + 5] * sU, accU[am][t8 + 6] * sU, accU[am][t8 + 7] * sU);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) alpha += static_cast<float>(xB[s][e]) * (kbv[am][t8 + e] * sK);
+    }
+    alpha_s = xor32_sum(alpha);
+  }
+  const f16x8* uB = xB;
+
+  // ---------------- pass 2 ----------------
+  load_q_operand(qrow, row_ok, hh, sQ, qB);
+  f32x16 accC[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) accC[mt] = f32x16{};
+  float rpart = 0.f;
+  const float mb2 = has ? lse2 + 24.f : 0.f;  // p * 2^-24 keeps W = p (R - alpha) inside fp16
+  if (t_beg < t_end) {
+    tile_load(p, b, g, t_beg * kKeyTile, false, tid, st);
+    tile_store(T, 0, false, tid, st);
+  }
+  __syncthreads();
+  for (int kt = t_beg; kt < t_end; ++kt) {
+    const int buf = (kt - t_beg) & 1;
+    const bool more = kt + 1 < t_end;
+    if (more) tile_load(p, b, g, (kt + 1) * kKeyTile, false, tid, st);
+    const int key0 = kt * kKeyTile;
+    if (key0 < w_kend && key0 + kKeyTile > w_kbeg) {
+      const bool full = key0 + kKeyTile <= w_full_end && key0 >= w_full_beg;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16 S = {}, R = {};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const f16x8 a = lds_k(T, buf, 32 * kb + ql, 2 * s + hh);
+          S = mfma(a, qB[s], S);
+          R = mfma(a, uB[s], R);
+        }
+        if (!full) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (key >= r_kend || key < r_kbeg) S[r] = -INFINITY;
+          }
+        }
+        f16x8 wB[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          float e[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int r = 8 * t + j;
+            e[j] = __builtin_amdgcn_exp2f(fmaf(S[r], cS, -mb2)) * (R[r] - alpha_s);
+          }
+          wB[t] = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+          rpart = sum8(wB[t], rpart);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            accC[mt] = mfma(lds_vt(T, buf, 32 * mt + ql, 4 * kb + 2 * t + hh), wB[t], accC[mt]);
+      }
+    }
+    if (more) tile_store(T, buf ^ 1, false, tid, st);
+    __syncthreads();
+  }
+
+  // ---------------- epilogue 2: out = o + c - rs o ----------------
+  const float RS = xor32_sum(rpart);
+  if (row_ok) {
+    const float fc = 16777216.f / (sU * sK * sV);
+    const float frs = RS * (16777216.f / (sU * sK));
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * mt + 8 * j + 4 * hh;
+        const float4 ov = *reinterpret_cast<const float4*>(obuf + qoff + d);
+        const float o4[4] = {ov.x, ov.y, ov.z, ov.w};
+        float r4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r4[e] = o4[e] + accC[mt][4 * j + e] * fc - frs * o4[e];
+        *reinterpret_cast<float4*>(p.out + qoff + d) = float4{r4[0], r4[1], r4[2], r4[3]};
+      }
+  }
+}
+
+}  // namespace
+
+bool fast_fwd_supported(const Geom& g) {
+  const int G = g.Hq / g.Hkv;
+  return g.bf16 && g.d == kD && !g.p_per_query && (G == 1 || G == 2 || G == 4 || G == 8);
+}
+
+size_t fast_fwd_workspace(const Geom& g) {
+  const Staging s = staging_layout(nullptr, g.B, g.Tk, g.Hkv, g.Hq);
+  return s.bytes + align_up(static_cast<size_t>(g.B) * g.Tq * g.Hq * kD * sizeof(float), 256);
+}
+
+hipError_t launch_fast_fwd(const Geom& g, const void* q, const void* k, const void* v,
+                           const void* P, float* out, float* lse, float* kbar, float* osa,
+                           int split_rows, void* ws, hipStream_t stream) {
+  const Staging s = staging_layout(ws, g.B, g.Tk, g.Hkv, g.Hq);
+  float* o_ws = reinterpret_cast<float*>(static_cast<char*>(ws) + s.bytes);
+  const int split = split_rows < 0 ? 0 : (split_rows > g.Tq ? g.Tq : split_rows);
+  hipError_t e = launch_staging(s, q, static_cast<int64_t>(g.B) * g.Tq * g.Hq * kD, k, v, P, g.B, g.Tk,
+                                g.Hkv, g.Hq, stream);
+  if (e != hipSuccess) return e;
+  if (split < g.Tq) {
+    FwdParams p{};
+    p.q = static_cast<const u16*>(q);
+    p.k16 = s.k16;
+    p.k16t = s.k16t;
+    p.v16t = s.v16t;
+    p.p16t = s.p16t;
+    p.maxbits = s.maxbits;
+    p.out = out;
+    p.lse = lse;
+    p.kbar = kbar;
+    p.osa = osa ? osa : o_ws;
+    p.B = g.B;
+    p.Tq = g.Tq;
+    p.Tk = g.Tk;
+    p.Tk_pad = s.Tk_pad;
+    p.Hq = g.Hq;
+    p.Hkv = g.Hkv;
+    p.G = g.Hq / g.Hkv;
+    p.causal = g.causal;
+    p.window = g.window;
+    p.scale = g.scale;
+    p.row_begin = split;
+    p.rows_per_block = 32 * kWaves / p.G;
+    p.n_rb = (g.Tq - split + p.rows_per_block - 1) / p.rows_per_block;
+    const int blocks = g.B * g.Hkv * p.n_rb;
+    mark_main_begin(stream);
+    hipLaunchKernelGGL(k_fwd_fast, dim3(blocks), dim3(512), 0, stream, p);
+    mark_main_end(stream);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (split > 0)
+    e = launch_generic_fwd(g, q, k, v, P, nullptr, out, lse, kbar, osa, 0, split, stream, false);
+  return e;
+}
+
+}  // namespace plx

@@ -1,0 +1,138 @@
+// Staging kernels of the fast path: max-abs of the inputs, then fp16 copies of
+// K, V and P in the MFMA operand layouts described in fast_common.h.
+#include "fast_common.h"
+
+namespace plx {
+namespace {
+
+__global__ __launch_bounds__(64) void k_zero_max(uint32_t* maxbits) {
+  if (threadIdx.x < 4) maxbits[threadIdx.x] = 0u;
+}
+
+// blockIdx.y selects the tensor: 0 q, 1 k, 2 v, 3 P.  Elements are bf16, counts multiples of 8.
+__global__ __launch_bounds__(256) void k_absmax(const u16* q, int64_t nq, const u16* k, const u16* v,
+                                                int64_t nkv, const u16* P, int64_t np,
+                                                uint32_t* maxbits) {
+  const int which = blockIdx.y;
+  const u16* src = which == 0 ? q : which == 1 ? k : which == 2 ? v : P;
+  const int64_t n = which == 0 ? nq : which == 3 ? np : nkv;
+  float m = 0.f;
+  if (src) {
+    const int64_t nvec = n / 8;
+    const uint4* s4 = reinterpret_cast<const uint4*>(src);
+    for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < nvec; i += 256LL * gridDim.x) {
+      const uint4 w = s4[i];
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        m = fmaxf(m, fabsf(__uint_as_float(ws[j] << 16)));
+        m = fmaxf(m, fabsf(__uint_as_float(ws[j] & 0xffff0000u)));
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float b = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    atomicMax(&maxbits[which], __float_as_uint(b));
+  }
+}
+
+// One block per (64-key tile, kv head, batch): K16 rows, K16t and V16t columns.
+__global__ __launch_bounds__(256) void k_stage_kv(const u16* k, const u16* v, const uint32_t* maxbits,
+                                                  _Float16* k16, _Float16* k16t, _Float16* v16t,
+                                                  int Tk, int Tk_pad, int Hkv) {
+  constexpr int LD = kD + 2;  // padded LDS row (halves) for conflict-light column reads
+  __shared__ _Float16 ks[kKeyTile * LD];
+  __shared__ _Float16 vs[kKeyTile * LD];
+  const int kt = blockIdx.x, g = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const int key0 = kt * kKeyTile;
+  const float sK = range_scale(__uint_as_float(maxbits[1]));
+  const float sV = range_scale(__uint_as_float(maxbits[2]));
+  // load 64 rows x 16 chunks of 8 bf16, scale, store fp16 (natural order)
+  for (int ci = t; ci < kKeyTile * 16; ci += 256) {
+    const int r = ci >> 4, c = ci & 15;
+    const int key = key0 + r;
+    uint4 kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
+    if (key < Tk) {
+      const int64_t off = ((static_cast<int64_t>(b) * Tk + key) * Hkv + g) * kD + c * 8;
+      kw = *reinterpret_cast<const uint4*>(k + off);
+      vw = *reinterpret_cast<const uint4*>(v + off);
+    }
+    const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w};
+    const uint32_t vv[4] = {vw.x, vw.y, vw.z, vw.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ks[r * LD + c * 8 + 2 * j] = static_cast<_Float16>(__uint_as_float(kk[j] << 16) * sK);
+      ks[r * LD + c * 8 + 2 * j + 1] = static_cast<_Float16>(__uint_as_float(kk[j] & 0xffff0000u) * sK);
+      vs[r * LD + c * 8 + 2 * j] = static_cast<_Float16>(__uint_as_float(vv[j] << 16) * sV);
+      vs[r * LD + c * 8 + 2 * j + 1] = static_cast<_Float16>(__uint_as_float(vv[j] & 0xffff0000u) * sV);
+    }
+  }
+  __syncthreads();
+  // K16: key rows with d permuted within groups of 16
+  for (int ci = t; ci < kKeyTile * 16; ci += 256) {
+    const int r = ci >> 4, c = ci & 15;
+    f16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = ks[r * LD + 16 * (c >> 1) + perm16(8 * (c & 1) + e)];
+    *reinterpret_cast<f16x8*>(k16 + ((static_cast<int64_t>(b) * Tk_pad + key0 + r) * Hkv + g) * kD + c * 8) = o;
+  }
+  // K16t, V16t: d rows, keys permuted within groups of 16
+  const int64_t trow = (static_cast<int64_t>(b) * Hkv + g) * kD;
+  for (int ci = t; ci < kD * 8; ci += 256) {
+    const int d = ci >> 3, c = ci & 7;
+    f16x8 ok, ov;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int key = 16 * (c >> 1) + perm16(8 * (c & 1) + e);
+      ok[e] = ks[key * LD + d];
+      ov[e] = vs[key * LD + d];
+    }
+    const int64_t off = (trow + d) * Tk_pad + key0 + c * 8;
+    *reinterpret_cast<f16x8*>(k16t + off) = ok;
+    *reinterpret_cast<f16x8*>(v16t + off) = ov;
+  }
+}
+
+// One block per query head: P16t[h][a][b'] = sP * P[h][perm(b')][a].
+__global__ __launch_bounds__(256) void k_stage_p(const u16* P, const uint32_t* maxbits, _Float16* p16t) {
+  constexpr int LD = kD + 2;
+  __shared__ _Float16 ps[kD * LD];
+  const int h = blockIdx.x, t = threadIdx.x;
+  const float sP = range_scale(__uint_as_float(maxbits[3]));
+  const u16* src = P + static_cast<int64_t>(h) * kD * kD;
+  for (int e = t; e < kD * kD; e += 256) ps[(e / kD) * LD + (e % kD)] = static_cast<_Float16>(bf16_to_f32(src[e]) * sP);
+  __syncthreads();
+  for (int ci = t; ci < kD * 16; ci += 256) {
+    const int a = ci >> 4, c = ci & 15;
+    f16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = ps[(16 * (c >> 1) + perm16(8 * (c & 1) + e)) * LD + a];
+    *reinterpret_cast<f16x8*>(p16t + (static_cast<int64_t>(h) * kD + a) * kD + c * 8) = o;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_staging(const Staging& s, const void* q, int64_t q_elems, const void* k,
+                          const void* v, const void* P, int B, int Tk, int Hkv, int Hq,
+                          hipStream_t stream) {
+  const int64_t nkv = static_cast<int64_t>(B) * Tk * Hkv * kD;
+  const int64_t np = static_cast<int64_t>(Hq) * kD * kD;
+  hipLaunchKernelGGL(k_zero_max, dim3(1), dim3(64), 0, stream, s.maxbits);
+  hipLaunchKernelGGL(k_absmax, dim3(512, 4), dim3(256), 0, stream, static_cast<const u16*>(q), q_elems,
+                     static_cast<const u16*>(k), static_cast<const u16*>(v), nkv,
+                     static_cast<const u16*>(P), np, s.maxbits);
+  if (B > 0 && s.Tk_pad > 0)
+    hipLaunchKernelGGL(k_stage_kv, dim3(s.Tk_pad / kKeyTile, Hkv, B), dim3(256), 0, stream,
+                       static_cast<const u16*>(k), static_cast<const u16*>(v), s.maxbits, s.k16, s.k16t,
+                       s.v16t, Tk, s.Tk_pad, Hkv);
+  hipLaunchKernelGGL(k_stage_p, dim3(Hq), dim3(256), 0, stream, static_cast<const u16*>(P), s.maxbits, s.p16t);
+  return hipGetLastError();
+}
+
+}  // namespace plx

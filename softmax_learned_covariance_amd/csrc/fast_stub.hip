@@ -1,14 +1,8 @@
-// Placeholder for the bf16 MFMA fast path: reports "not supported" so every call
-// takes the generic kernels.
+// Fast backward and decode are not written yet: report "not supported" so the
+// generic kernels serve those calls.
 #include "plx_internal.h"
 
 namespace plx {
-bool fast_fwd_supported(const Geom&) { return false; }
-size_t fast_fwd_workspace(const Geom&) { return 0; }
-hipError_t launch_fast_fwd(const Geom&, const void*, const void*, const void*, const void*, float*,
-                           float*, float*, float*, int, void*, hipStream_t) {
-  return hipErrorNotSupported;
-}
 bool fast_bwd_supported(const Geom&) { return false; }
 size_t fast_bwd_workspace(const Geom&) { return 0; }
 hipError_t launch_fast_bwd(const Geom&, const void*, const void*, const void*, const void*,
