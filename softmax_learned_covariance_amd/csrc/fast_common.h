@@ -79,6 +79,14 @@ __device__ __forceinline__ f16x8 pack8(float a0, float a1, float a2, float a3, f
   return r;
 }
 
+// fp16 of (x - hi) for the 8 values whose rounded fp16 is hi: the low half of a hi + lo pair.
+__device__ __forceinline__ f16x8 pack_lo(const float* x, f16x8 hi) {
+  return pack8(x[0] - static_cast<float>(hi[0]), x[1] - static_cast<float>(hi[1]),
+               x[2] - static_cast<float>(hi[2]), x[3] - static_cast<float>(hi[3]),
+               x[4] - static_cast<float>(hi[4]), x[5] - static_cast<float>(hi[5]),
+               x[6] - static_cast<float>(hi[6]), x[7] - static_cast<float>(hi[7]));
+}
+
 // Sum of the 8 fp16 values of an operand, accumulated in fp32 (v_dot2 with ones).
 __device__ __forceinline__ float sum8(f16x8 v, float acc) {
   const f16x2 one = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};

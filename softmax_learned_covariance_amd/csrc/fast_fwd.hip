@@ -46,7 +46,7 @@ struct FwdParams {
   float *out, *lse, *kbar, *osa;
   int B, Tq, Tk, Tk_pad, Hq, Hkv, G, causal, window;
   float scale;
-  int row_begin, rows_per_block, n_rb;
+  int row_begin, row_end, rows_per_block, n_rb;  // rows [row_begin, row_end)
 };
 
 struct __align__(16) Tiles {
@@ -119,6 +119,10 @@ __device__ __forceinline__ void load_q_operand(const u16* qrow, bool ok, int hh,
   }
 }
 
+// SPLIT: every operand the kernel computes (p~, q - kbar, u, W) is carried as an
+// fp16 hi + lo pair (two MFMAs, ~22 significant bits); used for the first query
+// rows, whose few visible keys make the output large relative to its rms.
+template <bool SPLIT>
 __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
   __shared__ Tiles T;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, ql = l & 31, hh = l >> 5;
@@ -142,7 +146,7 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
   const int r0 = p.row_begin + rb * p.rows_per_block;
   const int i0 = r0 + (w % wph) * 32;
   const int row = i0 + ql;
-  const bool row_ok = row < p.Tq;
+  const bool row_ok = row < p.row_end;
   const int off = p.Tk - p.Tq;
 
   const float sQ = range_scale(__uint_as_float(p.maxbits[0]));
@@ -155,13 +159,13 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
   const u16* qrow = p.q + qoff;
 
   // key ranges: block, wave (first / last row), lane (its row)
-  const int rlast = min(r0 + p.rows_per_block, p.Tq) - 1;
+  const int rlast = min(r0 + p.rows_per_block, p.row_end) - 1;
   const int kend = p.causal ? min(p.Tk, rlast + off + 1) : p.Tk;
   const int kbeg = p.window > 0 ? max(0, r0 + off - p.window + 1) : 0;
   const int t_beg = kbeg / kKeyTile;
   const int t_end = kend > kbeg ? (kend + kKeyTile - 1) / kKeyTile : t_beg;
-  const int wlast = min(i0 + 31, p.Tq - 1);
-  const bool wave_rows = i0 < p.Tq;
+  const int wlast = min(i0 + 31, p.row_end - 1);
+  const bool wave_rows = i0 < p.row_end;
   const int w_kend = wave_rows ? (p.causal ? min(p.Tk, wlast + off + 1) : p.Tk) : 0;
   const int w_kbeg = p.window > 0 ? max(0, i0 + off - p.window + 1) : 0;
   const int w_full_end = p.causal ? min(p.Tk, i0 + off + 1) : p.Tk;                       // every row sees keys < this
@@ -227,7 +231,7 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
         }
       }
       const float mb = m_used == -INFINITY ? 0.f : m_used;
-      f16x8 pB[4];
+      f16x8 pB[4], pL[SPLIT ? 4 : 1];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int kb = i >> 1, t8 = (i & 1) * 8;
@@ -236,13 +240,23 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
         for (int j = 0; j < 8; ++j) e[j] = __builtin_amdgcn_exp2f(fmaf(S[kb][t8 + j], cS, -mb));
         pB[i] = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
         lpart = sum8(pB[i], lpart);
+        if constexpr (SPLIT) {
+          pL[i] = pack_lo(e, pB[i]);
+          lpart = sum8(pL[i], lpart);
+        }
       }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          accO[mt] = mfma(lds_vt(T, buf, 32 * mt + ql, 2 * i + hh), pB[i], accO[mt]);
-          accK[mt] = mfma(lds_kt(T, buf, 32 * mt + ql, 2 * i + hh), pB[i], accK[mt]);
+          const f16x8 av = lds_vt(T, buf, 32 * mt + ql, 2 * i + hh);
+          const f16x8 ak = lds_kt(T, buf, 32 * mt + ql, 2 * i + hh);
+          accO[mt] = mfma(av, pB[i], accO[mt]);
+          accK[mt] = mfma(ak, pB[i], accK[mt]);
+          if constexpr (SPLIT) {
+            accO[mt] = mfma(av, pL[i], accO[mt]);
+            accK[mt] = mfma(ak, pL[i], accK[mt]);
+          }
         }
     }
     if (more) tile_store(T, buf ^ 1, true, tid, st);
@@ -277,7 +291,7 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
   // ---------------- probe u = P^T (q - kbar) ----------------
   // kbar (unscaled) and x = q - kbar in the accumulator layout: lane (row, hh), d = 32 mt + 8 (r/4) + 4 hh + r%4
   float kbv[4][16];
-  f16x8 xB[8];
+  f16x8 xB[8], xL[SPLIT ? 8 : 1];
   float alpha_s = 0.f, sU = 1.f;
   {
     float xv[4][16];
@@ -301,8 +315,11 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int mt = s >> 1, t8 = (s & 1) * 8;
-      xB[s] = pack8(xv[mt][t8] * sX, xv[mt][t8 + 1] * sX, xv[mt][t8 + 2] * sX, xv[mt][t8 + 3] * sX,
-                    xv[mt][t8 + 4] * sX, xv[mt][t8 + 5] * sX, xv[mt][t8 + 6] * sX, xv[mt][t8 + 7] * sX);
+      float e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e[j] = xv[mt][t8 + j] * sX;
+      xB[s] = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+      if constexpr (SPLIT) xL[s] = pack_lo(e, xB[s]);
     }
     // U^T = P16t X^T
     f32x16 accU[4];
@@ -311,8 +328,11 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
     for (int am = 0; am < 4; ++am) {
       accU[am] = f32x16{};
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
-        accU[am] = mfma(*reinterpret_cast<const f16x8*>(prow + 32 * am * kD + 16 * s), xB[s], accU[am]);
+      for (int s = 0; s < 8; ++s) {
+        const f16x8 a = *reinterpret_cast<const f16x8*>(prow + 32 * am * kD + 16 * s);
+        accU[am] = mfma(a, xB[s], accU[am]);
+        if constexpr (SPLIT) accU[am] = mfma(a, xL[s], accU[am]);
+      }
     }
     const float fu = 1.f / (sX * sP);
     float umax = 0.f;
@@ -330,14 +350,22 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int am = s >> 1, t8 = (s & 1) * 8;
-      xB[s] = pack8(accU[am][t8] * sU, accU[am][t8 + 1] * sU, accU[am][t8 + 2] * sU, accU[am][t8 + 3] * sU,
-                    accU[am][t8 + 4] * sU, accU[am][t8 + 5] * sU, accU[am][t8 + 6] * sU, accU[am][t8 + 7] * sU);
+      float e[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) alpha += static_cast<float>(xB[s][e]) * (kbv[am][t8 + e] * sK);
+      for (int j = 0; j < 8; ++j) e[j] = accU[am][t8 + j] * sU;
+      xB[s] = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+      if constexpr (SPLIT) xL[s] = pack_lo(e, xB[s]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float uh = static_cast<float>(xB[s][j]);
+        if constexpr (SPLIT) uh += static_cast<float>(xL[s][j]);
+        alpha += uh * (kbv[am][t8 + j] * sK);
+      }
     }
     alpha_s = xor32_sum(alpha);
   }
   const f16x8* uB = xB;
+  const f16x8* uL = xL;
 
   // ---------------- pass 2 ----------------
   load_q_operand(qrow, row_ok, hh, sQ, qB);
@@ -366,6 +394,7 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
           const f16x8 a = lds_k(T, buf, 32 * kb + ql, 2 * s + hh);
           S = mfma(a, qB[s], S);
           R = mfma(a, uB[s], R);
+          if constexpr (SPLIT) R = mfma(a, uL[s], R);
         }
         if (!full) {
 #pragma unroll
@@ -374,7 +403,7 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
             if (key >= r_kend || key < r_kbeg) S[r] = -INFINITY;
           }
         }
-        f16x8 wB[2];
+        f16x8 wB[2], wL[SPLIT ? 2 : 1];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           float e[8];
@@ -385,12 +414,19 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
           }
           wB[t] = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
           rpart = sum8(wB[t], rpart);
+          if constexpr (SPLIT) {
+            wL[t] = pack_lo(e, wB[t]);
+            rpart = sum8(wL[t], rpart);
+          }
         }
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int t = 0; t < 2; ++t)
-            accC[mt] = mfma(lds_vt(T, buf, 32 * mt + ql, 4 * kb + 2 * t + hh), wB[t], accC[mt]);
+          for (int t = 0; t < 2; ++t) {
+            const f16x8 av = lds_vt(T, buf, 32 * mt + ql, 4 * kb + 2 * t + hh);
+            accC[mt] = mfma(av, wB[t], accC[mt]);
+            if constexpr (SPLIT) accC[mt] = mfma(av, wL[t], accC[mt]);
+          }
       }
     }
     if (more) tile_store(T, buf ^ 1, false, tid, st);
@@ -438,8 +474,9 @@ hipError_t launch_fast_fwd(const Geom& g, const void* q, const void* k, const vo
   hipError_t e = launch_staging(s, q, static_cast<int64_t>(g.B) * g.Tq * g.Hq * kD, k, v, P, g.B, g.Tk,
                                 g.Hkv, g.Hq, stream);
   if (e != hipSuccess) return e;
-  if (split < g.Tq) {
-    FwdParams p{};
+  FwdParams base{};
+  {
+    FwdParams& p = base;
     p.q = static_cast<const u16*>(q);
     p.k16 = s.k16;
     p.k16t = s.k16t;
@@ -460,18 +497,29 @@ hipError_t launch_fast_fwd(const Geom& g, const void* q, const void* k, const vo
     p.causal = g.causal;
     p.window = g.window;
     p.scale = g.scale;
-    p.row_begin = split;
     p.rows_per_block = 32 * kWaves / p.G;
+  }
+  if (split < g.Tq) {
+    FwdParams p = base;
+    p.row_begin = split;
+    p.row_end = g.Tq;
     p.n_rb = (g.Tq - split + p.rows_per_block - 1) / p.rows_per_block;
     const int blocks = g.B * g.Hkv * p.n_rb;
     mark_main_begin(stream);
-    hipLaunchKernelGGL(k_fwd_fast, dim3(blocks), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL(k_fwd_fast<false>, dim3(blocks), dim3(512), 0, stream, p);
     mark_main_end(stream);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (split > 0)
-    e = launch_generic_fwd(g, q, k, v, P, nullptr, out, lse, kbar, osa, 0, split, stream, false);
+  if (split > 0) {
+    // rows [0, split): the same kernel with hi + lo operands
+    FwdParams p = base;
+    p.row_begin = 0;
+    p.n_rb = (split + p.rows_per_block - 1) / p.rows_per_block;
+    p.row_end = split;
+    hipLaunchKernelGGL(k_fwd_fast<true>, dim3(g.B * g.Hkv * p.n_rb), dim3(512), 0, stream, p);
+    e = hipGetLastError();
+  }
   return e;
 }
 
