@@ -1,0 +1,1009 @@
+// Parallax backward for gfx950 (head_dim 128, bf16 inputs, fp16 MFMA).
+//
+// The pages give no backward; these kernels evaluate the chain rule of the
+// forward definition (output = softmax output plus the key/value covariance
+// applied to the probe u = P^T (q - kbar), gist.science technical summary of
+// "Parallax: Parameterized Local Linear Attention for Language Modeling",
+// "Core mechanism").  With g = dout, alpha = u.kbar, t_ij = u_i.k_j,
+// G_ij = g_i.v_j, p_ij the softmax weights:
+//   du_i    = sum_j p_ij G_ij k_j - (g_i.o_i) kbar_i
+//   dkbar_i = -(g_i.o_i) u_i - P du_i          dq_i = P du_i + scale sum_j ds_ij k_j
+//   Delta_i = g_i.out_i + dkbar_i.kbar_i       dP   = sum_i (q_i - kbar_i) du_i^T
+//   ds_ij   = p_ij (G_ij (t_ij + 1 - alpha_i) + dkbar_i.k_j - Delta_i)
+//   dv_j    = sum_i p_ij (t_ij + 1 - alpha_i) g_i
+//   dk_j    = sum_i p_ij G_ij u_i + p_ij dkbar_i + scale ds_ij q_i
+//
+// Kernels (one stream, in order):
+//   staging   fp16 copies of K, V, P and of q, dout in the MFMA operand layouts;
+//   rows      query-major, two passes over the key tiles like the forward:
+//             pass 1 accumulates du (S, G and (p G) K on MFMA), the epilogue forms
+//             u, alpha, P du, dkbar, Delta, and pass 2 accumulates dq (S, T, E, G and
+//             ds K on MFMA) -- every quantity of a row stays in its lane;
+//   staging 2 fp16 copies of u and dkbar (per-tensor scales from the row pass);
+//   keys      key-major: each wave owns 32 keys and streams query tiles, recomputing
+//             S, T, E, G and accumulating dv = (p tt)^T g and
+//             dk = (p G)^T u + p^T dkbar + scale ds^T q on MFMA;
+//   dP        sum over rows of (q - kbar) du^T, then a fixed-order reduction.
+// Rows below split_rows run the same kernels with hi + lo fp16 operand pairs.
+// Everything is deterministic (no atomics on results).
+#include <math.h>
+
+#include "fast_common.h"
+#include "plx_internal.h"
+
+namespace plx {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ------------------------------------------------------------------------------------------
+// shared helpers
+// ------------------------------------------------------------------------------------------
+
+__device__ __forceinline__ float mx(const uint32_t* maxbits, int slot) { return __uint_as_float(maxbits[slot]); }
+
+__device__ __forceinline__ void load4_bf16(const u16* src, float* dst) {
+  const uint2 w = *reinterpret_cast<const uint2*>(src);
+  dst[0] = __uint_as_float(w.x << 16);
+  dst[1] = __uint_as_float(w.x & 0xffff0000u);
+  dst[2] = __uint_as_float(w.y << 16);
+  dst[3] = __uint_as_float(w.y & 0xffff0000u);
+}
+
+__device__ __forceinline__ void load_row_operand(const u16* row, bool ok, int hh, float s, f16x8 (&B)[8]) {
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+    float a[4] = {0.f, 0.f, 0.f, 0.f}, c[4] = {0.f, 0.f, 0.f, 0.f};
+    if (ok) {
+      load4_bf16(row + 16 * st + 4 * hh, a);
+      load4_bf16(row + 16 * st + 8 + 4 * hh, c);
+    }
+    B[st] = pack8(a[0] * s, a[1] * s, a[2] * s, a[3] * s, c[0] * s, c[1] * s, c[2] * s, c[3] * s);
+  }
+}
+
+// 8 fp32 accumulator values (registers 8t..8t+7 of a tile, times s) as an fp16 operand, and its lo part.
+__device__ __forceinline__ void to_operand(const float* v, float s, f16x8& hi, f16x8* lo) {
+  float e[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) e[j] = v[j] * s;
+  hi = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+  if (lo) *lo = pack_lo(e, hi);
+}
+
+// Same for registers 8t..8t+7 of an accumulator tile.
+__device__ __forceinline__ void tile_operand(const f32x16& v, int t, float s, f16x8& hi, f16x8* lo) {
+  float e[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) e[j] = v[8 * t + j];
+  to_operand(e, s, hi, lo);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+// ------------------------------------------------------------------------------------------
+// query-major row kernel
+// ------------------------------------------------------------------------------------------
+
+struct RowParams {
+  const u16 *q, *dout;
+  const float *out, *lse, *kbar, *osa;
+  const _Float16 *k16, *k16t, *v16, *p16t, *p16;
+  uint32_t* maxbits;
+  float *dq, *u32, *dkb32, *x32, *du32, *st_alpha, *st_delta;
+  int B, Tq, Tk, Tk_pad, Hq, Hkv, G, causal, window;
+  float scale;
+  int row_begin, row_end, rows_per_block, n_rb;
+};
+
+struct __align__(16) RowTiles {
+  _Float16 k[2][kKeyTile * kD];
+  _Float16 v[2][kKeyTile * kD];
+  _Float16 kt[2][kD * kKeyTile];
+};
+
+__device__ __forceinline__ f16x8 lds_rows(const _Float16* t, int r, int c) {
+  return *reinterpret_cast<const f16x8*>(&t[r * kD + ((c ^ (r & 7)) << 3)]);
+}
+__device__ __forceinline__ f16x8 lds_cols(const _Float16* t, int d, int c) {
+  return *reinterpret_cast<const f16x8*>(&t[d * kKeyTile + ((c ^ (d & 7)) << 3)]);
+}
+
+// Global -> LDS copy of one key tile through registers (256 threads, 4 chunks per array each).
+__device__ __forceinline__ void row_tile_copy(const RowParams& p, RowTiles& T, int buf, int b, int g, int key0,
+                                              int tid) {
+  uint4 rk[4], rv[4], rt[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ci = tid + 256 * j;
+    const int r = ci >> 4, c = ci & 15;
+    const int64_t roff = ((static_cast<int64_t>(b) * p.Tk_pad + key0 + r) * p.Hkv + g) * kD + c * 8;
+    rk[j] = *reinterpret_cast<const uint4*>(p.k16 + roff);
+    rv[j] = *reinterpret_cast<const uint4*>(p.v16 + roff);
+    const int d = ci >> 3, c2 = ci & 7;
+    rt[j] = *reinterpret_cast<const uint4*>(
+        p.k16t + ((static_cast<int64_t>(b) * p.Hkv + g) * kD + d) * p.Tk_pad + key0 + c2 * 8);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ci = tid + 256 * j;
+    const int r = ci >> 4, c = ci & 15;
+    *reinterpret_cast<uint4*>(&T.k[buf][r * kD + ((c ^ (r & 7)) << 3)]) = rk[j];
+    *reinterpret_cast<uint4*>(&T.v[buf][r * kD + ((c ^ (r & 7)) << 3)]) = rv[j];
+    const int d = ci >> 3, c2 = ci & 7;
+    *reinterpret_cast<uint4*>(&T.kt[buf][d * kKeyTile + ((c2 ^ (d & 7)) << 3)]) = rt[j];
+  }
+}
+
+template <bool SPLIT>
+__global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
+  __shared__ RowTiles T;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, ql = l & 31, hh = l >> 5;
+  const int npairs = p.B * p.Hkv;
+  int pair, rb;
+  {
+    const int id = blockIdx.x;
+    if ((npairs & 7) == 0) {
+      const int ppx = npairs >> 3, slot = id >> 3;
+      rb = p.n_rb - 1 - slot / ppx;
+      pair = (id & 7) + 8 * (slot % ppx);
+    } else {
+      rb = p.n_rb - 1 - id / npairs;
+      pair = id % npairs;
+    }
+  }
+  const int b = pair / p.Hkv, g = pair % p.Hkv;
+  const int wph = 4 / p.G;
+  const int h = g * p.G + w / wph;
+  const int r0 = p.row_begin + rb * p.rows_per_block;
+  const int i0 = r0 + (w % wph) * 32;
+  const int row = i0 + ql;
+  const bool row_ok = row < p.row_end;
+  const int off = p.Tk - p.Tq;
+  const uint32_t* MB = p.maxbits;
+  const float sQ = range_scale(mx(MB, kMaxQ)), sK = range_scale(mx(MB, kMaxK));
+  const float sV = range_scale(mx(MB, kMaxV)), sP = range_scale(mx(MB, kMaxP));
+  const float sG = range_scale(mx(MB, kMaxDO));
+  const float maxK = mx(MB, kMaxK);
+  const float cS = p.scale * kLog2e / (sQ * sK);
+  const float boundG = 128.f * mx(MB, kMaxDO) * mx(MB, kMaxV);
+  const float sPG = range_scale(boundG);
+
+  const int64_t qoff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * kD;
+  const int64_t soff = (static_cast<int64_t>(b) * p.Hq + h) * p.Tq + (row_ok ? row : 0);
+  float lse2 = row_ok ? p.lse[soff] * kLog2e : 0.f;
+  if (!(lse2 > -INFINITY && lse2 < INFINITY)) lse2 = 0.f;  // a row without keys: every S is masked
+
+  const int rlast = min(r0 + p.rows_per_block, p.row_end) - 1;
+  const int kend = p.causal ? min(p.Tk, rlast + off + 1) : p.Tk;
+  const int kbeg = p.window > 0 ? max(0, r0 + off - p.window + 1) : 0;
+  const int t_beg = kbeg / kKeyTile;
+  const int t_end = kend > kbeg ? (kend + kKeyTile - 1) / kKeyTile : t_beg;
+  const int wlast = min(i0 + 31, p.row_end - 1);
+  const bool wave_rows = i0 < p.row_end;
+  const int w_kend = wave_rows ? (p.causal ? min(p.Tk, wlast + off + 1) : p.Tk) : 0;
+  const int w_kbeg = p.window > 0 ? max(0, i0 + off - p.window + 1) : 0;
+  const int w_full_end = p.causal ? min(p.Tk, i0 + off + 1) : p.Tk;
+  const int w_full_beg = p.window > 0 ? max(0, wlast + off - p.window + 1) : 0;
+  const int r_kend = row_ok ? (p.causal ? min(p.Tk, row + off + 1) : p.Tk) : 0;
+  const int r_kbeg = p.window > 0 ? max(0, row + off - p.window + 1) : 0;
+
+  f16x8 qB[8], gB[8];
+  load_row_operand(p.q + qoff, row_ok, hh, sQ, qB);
+  load_row_operand(p.dout + qoff, row_ok, hh, sG, gB);
+
+  // ---------------- pass 1: du ----------------
+  f32x16 accDU[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) accDU[mt] = f32x16{};
+  const float fPG = sPG / (sG * sV);
+  if (t_beg < t_end) row_tile_copy(p, T, 0, b, g, t_beg * kKeyTile, tid);
+  __syncthreads();
+  for (int kt = t_beg; kt < t_end; ++kt) {
+    const int buf = (kt - t_beg) & 1;
+    const int key0 = kt * kKeyTile;
+    if (key0 < w_kend && key0 + kKeyTile > w_kbeg) {
+      const bool full = key0 + kKeyTile <= w_full_end && key0 >= w_full_beg;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16 S = {}, Gt = {};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          S = mfma(lds_rows(T.k[buf], 32 * kb + ql, 2 * s + hh), qB[s], S);
+          Gt = mfma(lds_rows(T.v[buf], 32 * kb + ql, 2 * s + hh), gB[s], Gt);
+        }
+        float pg[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+          float sv = S[r];
+          if (!full && (key >= r_kend || key < r_kbeg)) sv = -INFINITY;
+          pg[r] = __builtin_amdgcn_exp2f(fmaf(sv, cS, -lse2)) * Gt[r] * fPG;
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          f16x8 hi, lo;
+          to_operand(pg + 8 * t, 1.f, hi, SPLIT ? &lo : nullptr);
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            const f16x8 a = lds_cols(T.kt[buf], 32 * mt + ql, 4 * kb + 2 * t + hh);
+            accDU[mt] = mfma(a, hi, accDU[mt]);
+            if constexpr (SPLIT) accDU[mt] = mfma(a, lo, accDU[mt]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (kt + 1 < t_end) {
+      row_tile_copy(p, T, buf ^ 1, b, g, (kt + 1) * kKeyTile, tid);
+      __syncthreads();
+    }
+  }
+
+  // ---------------- epilogue: u, alpha, P du, dkbar, Delta ----------------
+  // row vectors in the accumulator layout: element (mt, r) is d = 32 mt + 8 (r/4) + 4 hh + r%4
+  float go = 0.f, gout = 0.f, gabs = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d = 32 * mt + 8 * j + 4 * hh;
+      float gv[4] = {0.f, 0.f, 0.f, 0.f};
+      float4 ov = {0.f, 0.f, 0.f, 0.f}, outv = {0.f, 0.f, 0.f, 0.f};
+      if (row_ok) {
+        load4_bf16(p.dout + qoff + d, gv);
+        ov = *reinterpret_cast<const float4*>(p.osa + qoff + d);
+        outv = *reinterpret_cast<const float4*>(p.out + qoff + d);
+      }
+      go += gv[0] * ov.x + gv[1] * ov.y + gv[2] * ov.z + gv[3] * ov.w;
+      gout += gv[0] * outv.x + gv[1] * outv.y + gv[2] * outv.z + gv[3] * outv.w;
+      gabs += fabsf(gv[0]) + fabsf(gv[1]) + fabsf(gv[2]) + fabsf(gv[3]);
+    }
+  go = xor32_sum(go);
+  gout = xor32_sum(gout);
+  gabs = xor32_sum(gabs);
+  // kbar, x = q - kbar (written out for dP), du = sum p G k - (g.o) kbar (in place, written out)
+  float kbv[4][16], xv[4][16];
+  float xmax = 0.f, dumax = 0.f;
+  {
+    const float fdu = 1.f / (sPG * sK);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * mt + 8 * j + 4 * hh;
+        float qv[4] = {0.f, 0.f, 0.f, 0.f};
+        float4 kv = {0.f, 0.f, 0.f, 0.f};
+        if (row_ok) {
+          load4_bf16(p.q + qoff + d, qv);
+          kv = *reinterpret_cast<const float4*>(p.kbar + qoff + d);
+        }
+        const float k4[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * j + e;
+          kbv[mt][r] = k4[e];
+          xv[mt][r] = qv[e] - k4[e];
+          accDU[mt][r] = accDU[mt][r] * fdu - go * k4[e];
+          xmax = fmaxf(xmax, fabsf(xv[mt][r]));
+          dumax = fmaxf(dumax, fabsf(accDU[mt][r]));
+        }
+        if (row_ok) {
+          *reinterpret_cast<float4*>(p.x32 + qoff + d) =
+              float4{xv[mt][4 * j], xv[mt][4 * j + 1], xv[mt][4 * j + 2], xv[mt][4 * j + 3]};
+          *reinterpret_cast<float4*>(p.du32 + qoff + d) =
+              float4{accDU[mt][4 * j], accDU[mt][4 * j + 1], accDU[mt][4 * j + 2], accDU[mt][4 * j + 3]};
+        }
+      }
+  }
+  xmax = xor32_max(xmax);
+  dumax = xor32_max(dumax);
+  const float sX = range_scale(xmax), sDU = range_scale(dumax);
+  // U^T = P16t X^T, then (P du)^T = P16 du^T
+  f32x16 accU[4], accPD[4];
+  {
+    f16x8 xB[8], xL[SPLIT ? 8 : 1];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) to_operand(&xv[s >> 1][(s & 1) * 8], sX, xB[s], SPLIT ? &xL[SPLIT ? s : 0] : nullptr);
+    const _Float16* prt = p.p16t + (static_cast<int64_t>(h) * kD + ql) * kD + hh * 8;
+#pragma unroll
+    for (int am = 0; am < 4; ++am) {
+      accU[am] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const f16x8 at = *reinterpret_cast<const f16x8*>(prt + 32 * am * kD + 16 * s);
+        accU[am] = mfma(at, xB[s], accU[am]);
+        if constexpr (SPLIT) accU[am] = mfma(at, xL[SPLIT ? s : 0], accU[am]);
+      }
+    }
+  }
+  {
+    f16x8 dB[8], dL[SPLIT ? 8 : 1];
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      tile_operand(accDU[s >> 1], s & 1, sDU, dB[s], SPLIT ? &dL[SPLIT ? s : 0] : nullptr);
+    const _Float16* pr = p.p16 + (static_cast<int64_t>(h) * kD + ql) * kD + hh * 8;
+#pragma unroll
+    for (int am = 0; am < 4; ++am) {
+      accPD[am] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const f16x8 a = *reinterpret_cast<const f16x8*>(pr + 32 * am * kD + 16 * s);
+        accPD[am] = mfma(a, dB[s], accPD[am]);
+        if constexpr (SPLIT) accPD[am] = mfma(a, dL[SPLIT ? s : 0], accPD[am]);
+      }
+    }
+  }
+  // u (in accU), dq0 = P du (written to dq now, completed after pass 2), dkbar (in accPD), alpha, Delta
+  float alpha = 0.f, dkk = 0.f, umax = 0.f, emax = 0.f, u1 = 0.f, e1 = 0.f;
+  {
+    const float fu = 1.f / (sX * sP), fpd = 1.f / (sP * sDU);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * mt + 8 * j + 4 * hh;
+        float pd4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * j + e;
+          const float u = accU[mt][r] * fu;
+          const float pd = accPD[mt][r] * fpd;
+          const float dk = -go * u - pd;
+          pd4[e] = pd;
+          accU[mt][r] = u;
+          accPD[mt][r] = dk;
+          alpha += u * kbv[mt][r];
+          dkk += dk * kbv[mt][r];
+          umax = fmaxf(umax, fabsf(u));
+          emax = fmaxf(emax, fabsf(dk));
+          u1 += fabsf(u);
+          e1 += fabsf(dk);
+        }
+        if (row_ok) {
+          *reinterpret_cast<float4*>(p.dq + qoff + d) = float4{pd4[0], pd4[1], pd4[2], pd4[3]};
+          *reinterpret_cast<float4*>(p.u32 + qoff + d) =
+              float4{accU[mt][4 * j], accU[mt][4 * j + 1], accU[mt][4 * j + 2], accU[mt][4 * j + 3]};
+          *reinterpret_cast<float4*>(p.dkb32 + qoff + d) =
+              float4{accPD[mt][4 * j], accPD[mt][4 * j + 1], accPD[mt][4 * j + 2], accPD[mt][4 * j + 3]};
+        }
+      }
+  }
+  alpha = xor32_sum(alpha);
+  dkk = xor32_sum(dkk);
+  umax = xor32_max(umax);
+  emax = xor32_max(emax);
+  u1 = xor32_sum(u1);
+  e1 = xor32_sum(e1);
+  const float delta = gout + dkk;
+  if (row_ok && hh == 0) {
+    p.st_alpha[soff] = alpha;
+    p.st_delta[soff] = delta;
+  }
+  {
+    // per-tensor maxima for the key-major pass (rows outside the range contribute 0)
+    const float wu = wave_max(row_ok ? umax : 0.f), we = wave_max(row_ok ? emax : 0.f);
+    const float wd = wave_max(row_ok ? fabsf(delta) : 0.f), wa = wave_max(row_ok ? fabsf(alpha) : 0.f);
+    if (l == 0) {
+      atomicMax(&p.maxbits[kMaxU], __float_as_uint(wu));
+      atomicMax(&p.maxbits[kMaxDKB], __float_as_uint(we));
+      atomicMax(&p.maxbits[kMaxDelta], __float_as_uint(wd));
+      atomicMax(&p.maxbits[kMaxAlpha], __float_as_uint(wa));
+    }
+  }
+
+  // ---------------- pass 2: dq ----------------
+  const float sU = range_scale(umax), sE = range_scale(emax);
+  f16x8 uB[8], uL[SPLIT ? 8 : 1], eB[8], eL[SPLIT ? 8 : 1];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    tile_operand(accU[s >> 1], s & 1, sU, uB[s], SPLIT ? &uL[SPLIT ? s : 0] : nullptr);
+    tile_operand(accPD[s >> 1], s & 1, sE, eB[s], SPLIT ? &eL[SPLIT ? s : 0] : nullptr);
+  }
+  // |ds| <= |G| |tt| + |E| + |Delta| with |G| <= |g|_1 max|v|, |tt| <= |u|_1 max|k| + 1 + |alpha|, |E| <= |dkbar|_1 max|k|
+  const float bound_ds = gabs * mx(MB, kMaxV) * (u1 * maxK + 1.f + fabsf(alpha)) + e1 * maxK + fabsf(delta);
+  const float sDS = range_scale(bound_ds);
+  const float fT = 1.f / (sU * sK), fE = 1.f / (sE * sK), fG = 1.f / (sG * sV);
+  const float one_m_alpha = 1.f - alpha;
+  f32x16 accDQ[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) accDQ[mt] = f32x16{};
+  if (t_beg < t_end) row_tile_copy(p, T, 0, b, g, t_beg * kKeyTile, tid);
+  __syncthreads();
+  for (int kt = t_beg; kt < t_end; ++kt) {
+    const int buf = (kt - t_beg) & 1;
+    const int key0 = kt * kKeyTile;
+    if (key0 < w_kend && key0 + kKeyTile > w_kbeg) {
+      const bool full = key0 + kKeyTile <= w_full_end && key0 >= w_full_beg;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16 S = {}, Tt = {}, E = {}, Gt = {};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const f16x8 a = lds_rows(T.k[buf], 32 * kb + ql, 2 * s + hh);
+          S = mfma(a, qB[s], S);
+          Tt = mfma(a, uB[s], Tt);
+          E = mfma(a, eB[s], E);
+          if constexpr (SPLIT) {
+            Tt = mfma(a, uL[s], Tt);
+            E = mfma(a, eL[s], E);
+          }
+          Gt = mfma(lds_rows(T.v[buf], 32 * kb + ql, 2 * s + hh), gB[s], Gt);
+        }
+        float ds[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+          float sv = S[r];
+          if (!full && (key >= r_kend || key < r_kbeg)) sv = -INFINITY;
+          const float pr = __builtin_amdgcn_exp2f(fmaf(sv, cS, -lse2));
+          const float tt = fmaf(Tt[r], fT, one_m_alpha);
+          const float dp = fmaf(Gt[r] * fG, tt, E[r] * fE);
+          ds[r] = pr * (dp - delta) * sDS;
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          f16x8 hi, lo;
+          to_operand(ds + 8 * t, 1.f, hi, SPLIT ? &lo : nullptr);
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            const f16x8 a = lds_cols(T.kt[buf], 32 * mt + ql, 4 * kb + 2 * t + hh);
+            accDQ[mt] = mfma(a, hi, accDQ[mt]);
+            if constexpr (SPLIT) accDQ[mt] = mfma(a, lo, accDQ[mt]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (kt + 1 < t_end) {
+      row_tile_copy(p, T, buf ^ 1, b, g, (kt + 1) * kKeyTile, tid);
+      __syncthreads();
+    }
+  }
+  if (row_ok) {
+    const float fq = p.scale / (sDS * sK);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * mt + 8 * j + 4 * hh;
+        const int r = 4 * j;
+        const float4 q0 = *reinterpret_cast<const float4*>(p.dq + qoff + d);  // P du from the epilogue
+        *reinterpret_cast<float4*>(p.dq + qoff + d) =
+            float4{q0.x + accDQ[mt][r] * fq, q0.y + accDQ[mt][r + 1] * fq, q0.z + accDQ[mt][r + 2] * fq,
+                   q0.w + accDQ[mt][r + 3] * fq};
+      }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// key-major kernel: dk, dv
+// ------------------------------------------------------------------------------------------
+
+struct KeyParams {
+  const _Float16 *k16, *v16;
+  const _Float16 *q16, *q16t, *do16, *do16t, *u16, *u16t, *e16, *e16t;
+  const _Float16 *u16lo, *u16tlo, *e16lo, *e16tlo;
+  const float *lse, *alpha, *delta;
+  const uint32_t* maxbits;
+  float *dk, *dv;
+  int B, Tq, Tk, Tk_pad, Tq_pad, lo_pad, Hq, Hkv, G, causal, window;
+  float scale;
+  int row_lo, row_hi, accumulate, n_kb, key_hi;
+};
+
+// One query tile in LDS.  Row-major tiles [32 rows][128 d'] (16 chunks per row, chunk ^= row & 7);
+// transposed tiles [128 d][32 rows'] (4 chunks per row, chunk ^= (d >> 1) & 3).
+template <bool SPLIT>
+struct __align__(16) KeyTiles {
+  static constexpr int NR = SPLIT ? 6 : 4;   // q, dO, u, e (+ u lo, e lo)
+  static constexpr int NB = SPLIT ? 1 : 2;
+  _Float16 r[NB][NR][32 * kD];
+  _Float16 t[NB][NR][kD * 32];
+  float stat[NB][3][32];                     // lse2, alpha, delta of the tile's rows
+};
+
+__device__ __forceinline__ f16x8 kt_rows(const _Float16* t, int r, int c) {
+  return *reinterpret_cast<const f16x8*>(&t[r * kD + ((c ^ (r & 7)) << 3)]);
+}
+__device__ __forceinline__ f16x8 kt_cols(const _Float16* t, int d, int c) {
+  return *reinterpret_cast<const f16x8*>(&t[d * 32 + ((c ^ ((d >> 1) & 3)) << 3)]);
+}
+
+template <bool SPLIT>
+__device__ __forceinline__ void key_tile_copy(const KeyParams& p, KeyTiles<SPLIT>& T, int buf, int b, int h, int q0,
+                                              int tid) {
+  constexpr int NR = KeyTiles<SPLIT>::NR;
+  const _Float16* srcr[6] = {p.q16, p.do16, p.u16, p.e16, p.u16lo, p.e16lo};
+  const _Float16* srct[6] = {p.q16t, p.do16t, p.u16t, p.e16t, p.u16tlo, p.e16tlo};
+  const int64_t bh = static_cast<int64_t>(b) * p.Hq + h;
+  // row-major: 32 rows x 16 chunks = 512 chunks per array, 2 per thread
+#pragma unroll
+  for (int a = 0; a < NR; ++a) {
+    const int pad = a < 4 ? p.Tq_pad : p.lo_pad;
+    uint4 v[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int ci = tid + 256 * j, r = ci >> 4, c = ci & 15;
+      v[j] = *reinterpret_cast<const uint4*>(srcr[a] + (bh * pad + q0 + r) * kD + c * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int ci = tid + 256 * j, r = ci >> 4, c = ci & 15;
+      *reinterpret_cast<uint4*>(&T.r[buf][a][r * kD + ((c ^ (r & 7)) << 3)]) = v[j];
+    }
+    // transposed: 128 rows x 4 chunks
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int ci = tid + 256 * j, d = ci >> 2, c = ci & 3;
+      v[j] = *reinterpret_cast<const uint4*>(srct[a] + (bh * kD + d) * pad + q0 + c * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int ci = tid + 256 * j, d = ci >> 2, c = ci & 3;
+      *reinterpret_cast<uint4*>(&T.t[buf][a][d * 32 + ((c ^ ((d >> 1) & 3)) << 3)]) = v[j];
+    }
+  }
+  if (tid < 96) {
+    const int which = tid >> 5, r = tid & 31, row = q0 + r;
+    float val = 0.f;
+    if (row < p.Tq) {
+      const int64_t so = bh * p.Tq + row;
+      if (which == 0) {
+        val = p.lse[so] * kLog2e;
+        if (!(val > -INFINITY && val < INFINITY)) val = 0.f;
+      } else {
+        val = which == 1 ? p.alpha[so] : p.delta[so];
+      }
+    }
+    T.stat[buf][which][r] = val;
+  }
+}
+
+template <bool SPLIT>
+__global__ __launch_bounds__(256) void k_bwd_keys_fast(KeyParams p) {
+  __shared__ KeyTiles<SPLIT> T;
+  constexpr int NB = KeyTiles<SPLIT>::NB;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, ql = l & 31, hh = l >> 5;
+  const int npairs = p.B * p.Hkv;
+  int pair, kbk;
+  {
+    const int id = blockIdx.x;
+    if ((npairs & 7) == 0) {
+      const int ppx = npairs >> 3, slot = id >> 3;
+      kbk = slot / ppx;  // causal: the first key blocks see the most rows
+      pair = (id & 7) + 8 * (slot % ppx);
+    } else {
+      kbk = id / npairs;
+      pair = id % npairs;
+    }
+  }
+  const int b = pair / p.Hkv, g = pair % p.Hkv;
+  const int off = p.Tk - p.Tq;
+  const int jb = kbk * 128;            // block's first key
+  const int jw = jb + 32 * w;          // wave's first key
+  const int key = jw + ql;
+  const bool key_ok = key < p.Tk;
+  const uint32_t* MB = p.maxbits;
+  const float sQ = range_scale(mx(MB, kMaxQ)), sK = range_scale(mx(MB, kMaxK));
+  const float sV = range_scale(mx(MB, kMaxV)), sG = range_scale(mx(MB, kMaxDO));
+  const float maxU = mx(MB, kMaxU), maxE = mx(MB, kMaxDKB), maxK = mx(MB, kMaxK);
+  const float sU = range_scale(maxU), sE = range_scale(maxE);
+  const float cS = p.scale * kLog2e / (sQ * sK);
+  const float fT = 1.f / (sU * sK), fE = 1.f / (sE * sK), fG = 1.f / (sG * sV);
+  const float boundG = 128.f * mx(MB, kMaxDO) * mx(MB, kMaxV);
+  const float boundT = 128.f * maxU * maxK + 1.f + mx(MB, kMaxAlpha);
+  const float boundDS = boundG * boundT + 128.f * maxE * maxK + mx(MB, kMaxDelta);
+  const float cV = range_scale(boundT);
+  float C = range_scale(boundG) * sU;
+  C = fminf(C, 16384.f * sE);
+  C = fminf(C, range_scale(p.scale * boundDS) * sQ);
+  const float c1 = C / sU, c2 = C / sE, c3 = p.scale * C / sQ;
+
+  // this wave's key rows as B operands (d permuted, as staged)
+  f16x8 kB[8], vB[8];
+  {
+    const int kr = key_ok ? key : 0;
+    const int64_t roff = ((static_cast<int64_t>(b) * p.Tk_pad + kr) * p.Hkv + g) * kD + hh * 8;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      kB[s] = *reinterpret_cast<const f16x8*>(p.k16 + roff + 16 * s);
+      vB[s] = *reinterpret_cast<const f16x8*>(p.v16 + roff + 16 * s);
+    }
+  }
+  f32x16 accK[4], accV[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    accK[mt] = f32x16{};
+    accV[mt] = f32x16{};
+  }
+  // query rows that see some key of the block: [i_lo, i_hi)
+  const int jmax_b = min(jb + 128, p.key_hi) - 1;
+  int i_lo = p.causal ? max(p.row_lo, jb - off) : p.row_lo;
+  int i_hi = p.window > 0 ? min(p.row_hi, jmax_b - off + p.window) : p.row_hi;
+  const int n_qt = i_hi > i_lo ? (i_hi - 1) / 32 - i_lo / 32 + 1 : 0;
+  const int qt0 = i_lo / 32;
+  const int total = n_qt * p.G;
+  const int jw_last = min(jw + 31, p.Tk - 1);
+  if (total > 0) key_tile_copy<SPLIT>(p, T, 0, b, g * p.G, qt0 * 32, tid);
+  __syncthreads();
+  for (int it = 0; it < total; ++it) {
+    const int buf = NB == 2 ? (it & 1) : 0;
+    const int qt = qt0 + it % n_qt;
+    const int q0 = qt * 32;
+    // wave-uniform skip: no visible pair between these 32 rows and this wave's keys
+    const bool any = jw < p.Tk && (!p.causal || jw <= q0 + 31 + off) &&
+                     (p.window <= 0 || jw_last > q0 + off - p.window) && q0 + 31 >= p.row_lo && q0 < p.row_hi;
+    if (any) {
+      const bool full = jw + 32 <= p.Tk && (!p.causal || jw + 31 <= q0 + off) &&
+                        (p.window <= 0 || jw > q0 + 31 + off - p.window) && q0 >= p.row_lo &&
+                        q0 + 32 <= min(p.row_hi, p.Tq);
+      f32x16 S = {}, Tt = {}, E = {}, Gt = {};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        S = mfma(kt_rows(T.r[buf][0], ql, 2 * s + hh), kB[s], S);
+        Gt = mfma(kt_rows(T.r[buf][1], ql, 2 * s + hh), vB[s], Gt);
+        Tt = mfma(kt_rows(T.r[buf][2], ql, 2 * s + hh), kB[s], Tt);
+        E = mfma(kt_rows(T.r[buf][3], ql, 2 * s + hh), kB[s], E);
+        if constexpr (SPLIT) {
+          Tt = mfma(kt_rows(T.r[buf][4], ql, 2 * s + hh), kB[s], Tt);
+          E = mfma(kt_rows(T.r[buf][5], ql, 2 * s + hh), kB[s], E);
+        }
+      }
+      float wv[16], wk[16], wp[16], wd[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rr = 8 * j + 4 * hh;  // first of 4 consecutive rows held in registers 4j..4j+3
+        const float4 L2 = *reinterpret_cast<const float4*>(&T.stat[buf][0][rr]);
+        const float4 AL = *reinterpret_cast<const float4*>(&T.stat[buf][1][rr]);
+        const float4 DL = *reinterpret_cast<const float4*>(&T.stat[buf][2][rr]);
+        const float l2[4] = {L2.x, L2.y, L2.z, L2.w}, al[4] = {AL.x, AL.y, AL.z, AL.w};
+        const float dl[4] = {DL.x, DL.y, DL.z, DL.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * j + e, i = q0 + rr + e;
+          float sv = S[r];
+          if (!full) {
+            const bool vis = key_ok && i >= p.row_lo && i < p.row_hi && i < p.Tq && (!p.causal || key <= i + off) &&
+                             (p.window <= 0 || key > i + off - p.window);
+            if (!vis) sv = -INFINITY;
+          }
+          const float pr = __builtin_amdgcn_exp2f(fmaf(sv, cS, -l2[e]));
+          const float tt = fmaf(Tt[r], fT, 1.f - al[e]);
+          const float gt = Gt[r] * fG;
+          const float dp = fmaf(gt, tt, E[r] * fE);
+          wv[r] = pr * tt * cV;
+          wk[r] = pr * gt * c1;
+          wp[r] = pr * c2;
+          wd[r] = pr * (dp - dl[e]) * c3;
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        f16x8 vh, vl, kh, kl, ph, pl, dh, dlo;
+        to_operand(wv + 8 * t, 1.f, vh, SPLIT ? &vl : nullptr);
+        to_operand(wk + 8 * t, 1.f, kh, SPLIT ? &kl : nullptr);
+        to_operand(wp + 8 * t, 1.f, ph, SPLIT ? &pl : nullptr);
+        to_operand(wd + 8 * t, 1.f, dh, SPLIT ? &dlo : nullptr);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const int d = 32 * mt + ql, c = 2 * t + hh;
+          const f16x8 ag = kt_cols(T.t[buf][1], d, c), aq = kt_cols(T.t[buf][0], d, c);
+          const f16x8 au = kt_cols(T.t[buf][2], d, c), ae = kt_cols(T.t[buf][3], d, c);
+          accV[mt] = mfma(ag, vh, accV[mt]);
+          accK[mt] = mfma(au, kh, accK[mt]);
+          accK[mt] = mfma(ae, ph, accK[mt]);
+          accK[mt] = mfma(aq, dh, accK[mt]);
+          if constexpr (SPLIT) {
+            const f16x8 aul = kt_cols(T.t[buf][4], d, c), ael = kt_cols(T.t[buf][5], d, c);
+            accV[mt] = mfma(ag, vl, accV[mt]);
+            accK[mt] = mfma(au, kl, accK[mt]);
+            accK[mt] = mfma(aul, kh, accK[mt]);
+            accK[mt] = mfma(ae, pl, accK[mt]);
+            accK[mt] = mfma(ael, ph, accK[mt]);
+            accK[mt] = mfma(aq, dlo, accK[mt]);
+          }
+        }
+      }
+    }
+    if (NB == 2) {
+      __syncthreads();
+      if (it + 1 < total) {
+        const int nit = it + 1;
+        key_tile_copy<SPLIT>(p, T, nit & 1, b, g * p.G + nit / n_qt, (qt0 + nit % n_qt) * 32, tid);
+        __syncthreads();
+      }
+    } else {
+      __syncthreads();
+      if (it + 1 < total) {
+        const int nit = it + 1;
+        key_tile_copy<SPLIT>(p, T, 0, b, g * p.G + nit / n_qt, (qt0 + nit % n_qt) * 32, tid);
+      }
+      __syncthreads();
+    }
+  }
+  if (key_ok) {
+    const float fk = 1.f / C, fv = 1.f / (sG * cV);
+    float* dkr = p.dk + ((static_cast<int64_t>(b) * p.Tk + key) * p.Hkv + g) * kD;
+    float* dvr = p.dv + ((static_cast<int64_t>(b) * p.Tk + key) * p.Hkv + g) * kD;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * mt + 8 * j + 4 * hh, r = 4 * j;
+        float4 kv = {accK[mt][r] * fk, accK[mt][r + 1] * fk, accK[mt][r + 2] * fk, accK[mt][r + 3] * fk};
+        float4 vv = {accV[mt][r] * fv, accV[mt][r + 1] * fv, accV[mt][r + 2] * fv, accV[mt][r + 3] * fv};
+        if (p.accumulate) {
+          const float4 k0 = *reinterpret_cast<const float4*>(dkr + d);
+          const float4 v0 = *reinterpret_cast<const float4*>(dvr + d);
+          kv = float4{kv.x + k0.x, kv.y + k0.y, kv.z + k0.z, kv.w + k0.w};
+          vv = float4{vv.x + v0.x, vv.y + v0.y, vv.z + v0.z, vv.w + v0.w};
+        }
+        *reinterpret_cast<float4*>(dkr + d) = kv;
+        *reinterpret_cast<float4*>(dvr + d) = vv;
+      }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// dP = sum over batch and rows of x du^T: partial sums per row chunk, then a fixed-order sum
+// ------------------------------------------------------------------------------------------
+
+constexpr int kPChunk = 256;  // rows per partial
+
+// block (chunk, head): 256 threads, each owns an 8 x 8 block of the 128 x 128 result
+__global__ __launch_bounds__(256) void k_dp_partial(const float* x32, const float* du32, float* part, int R, int Hq) {
+  __shared__ float xs[32][kD + 4];
+  __shared__ float ds_[32][kD + 4];
+  const int c = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  const int bi = (t >> 4) * 8, ai = (t & 15) * 8;
+  float acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
+  const int r_beg = c * kPChunk, r_end = min(R, r_beg + kPChunk);
+  for (int r0 = r_beg; r0 < r_end; r0 += 32) {
+    for (int e = t; e < 32 * kD; e += 256) {
+      const int rr = e / kD, d = e % kD, r = r0 + rr;
+      float xv = 0.f, dv = 0.f;
+      if (r < r_end) {
+        const int64_t o = (static_cast<int64_t>(r) * Hq + h) * kD + d;
+        xv = x32[o];
+        dv = du32[o];
+      }
+      xs[rr][d] = xv;
+      ds_[rr][d] = dv;
+    }
+    __syncthreads();
+    for (int rr = 0; rr < 32; ++rr) {
+      float xa[8], da[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        xa[i] = xs[rr][bi + i];
+        da[i] = ds_[rr][ai + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(xa[i], da[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  float* dst = part + (static_cast<int64_t>(c) * Hq + h) * kD * kD;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; j += 4)
+      *reinterpret_cast<float4*>(dst + (bi + i) * kD + ai + j) =
+          float4{acc[i][j], acc[i][j + 1], acc[i][j + 2], acc[i][j + 3]};
+}
+
+__global__ __launch_bounds__(256) void k_dp_reduce(const float* part, float* dP, int nchunks, int Hq) {
+  const int64_t n = static_cast<int64_t>(Hq) * kD * kD;
+  for (int64_t e = blockIdx.x * 256LL + threadIdx.x; e < n; e += 256LL * gridDim.x) {
+    float s = 0.f;
+    for (int c = 0; c < nchunks; ++c) s += part[c * n + e];
+    dP[e] = s;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// workspace layout
+// ------------------------------------------------------------------------------------------
+
+struct BwdWs {
+  Staging st;
+  _Float16 *q16, *q16t, *do16, *do16t, *u16, *u16t, *e16, *e16t;
+  _Float16 *u16lo, *u16tlo, *e16lo, *e16tlo;
+  float *u32, *dkb32, *x32, *du32, *alpha, *delta, *part;
+  int Tq_pad, lo_rows, lo_pad, nchunks;
+  size_t bytes;
+};
+
+BwdWs bwd_layout(const Geom& g, int split, void* ws) {
+  BwdWs w{};
+  w.st = staging_layout(ws, g.B, g.Tk, g.Hkv, g.Hq, true);
+  size_t off = w.st.bytes;
+  char* base = static_cast<char*>(ws);
+  w.Tq_pad = (g.Tq + 31) / 32 * 32;
+  w.lo_rows = split;
+  w.lo_pad = (split + 31) / 32 * 32;
+  const size_t qh = static_cast<size_t>(g.B) * g.Hq * w.Tq_pad * kD * sizeof(_Float16);
+  const size_t lh = static_cast<size_t>(g.B) * g.Hq * w.lo_pad * kD * sizeof(_Float16);
+  const size_t rf = static_cast<size_t>(g.B) * g.Tq * g.Hq * kD * sizeof(float);
+  const size_t sf = static_cast<size_t>(g.B) * g.Hq * g.Tq * sizeof(float);
+  _Float16** h16[8] = {&w.q16, &w.q16t, &w.do16, &w.do16t, &w.u16, &w.u16t, &w.e16, &w.e16t};
+  for (auto pp : h16) *pp = reinterpret_cast<_Float16*>(base + ws_take(off, qh));
+  _Float16** l16[4] = {&w.u16lo, &w.u16tlo, &w.e16lo, &w.e16tlo};
+  for (auto pp : l16) *pp = reinterpret_cast<_Float16*>(base + ws_take(off, lh));
+  float** f32[4] = {&w.u32, &w.dkb32, &w.x32, &w.du32};
+  for (auto pp : f32) *pp = reinterpret_cast<float*>(base + ws_take(off, rf));
+  w.alpha = reinterpret_cast<float*>(base + ws_take(off, sf));
+  w.delta = reinterpret_cast<float*>(base + ws_take(off, sf));
+  const int64_t R = static_cast<int64_t>(g.B) * g.Tq;
+  w.nchunks = static_cast<int>((R + kPChunk - 1) / kPChunk);
+  w.part = reinterpret_cast<float*>(base + ws_take(off, static_cast<size_t>(w.nchunks) * g.Hq * kD * kD * 4));
+  w.bytes = off;
+  return w;
+}
+
+int bwd_split(const Geom& g) { return 256 < g.Tq ? 256 : g.Tq; }
+
+}  // namespace
+
+bool fast_bwd_supported(const Geom& g) {
+  const int G = g.Hq / g.Hkv;
+  return g.bf16 && g.d == kD && !g.p_per_query && (G == 1 || G == 2 || G == 4) && g.B > 0 && g.Tq > 0 &&
+         g.Tk > 0;
+}
+
+size_t fast_bwd_workspace(const Geom& g) { return bwd_layout(g, bwd_split(g), nullptr).bytes; }
+
+hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const void* v, const void* P,
+                           const float* out, const void* dout, const float* lse, const float* kbar,
+                           const float* osa, float* dq, float* dk, float* dv, float* dP, int split_rows,
+                           void* ws, hipStream_t stream) {
+  // The workspace is sized for the default split; a larger request is clamped to it.
+  int split = split_rows < 0 ? bwd_split(g) : split_rows;
+  if (split > bwd_split(g)) split = bwd_split(g);
+  const BwdWs w = bwd_layout(g, bwd_split(g), ws);
+  const int G = g.Hq / g.Hkv;
+  hipError_t e = launch_staging(w.st, q, static_cast<int64_t>(g.B) * g.Tq * g.Hq * kD, k, v, P, g.B, g.Tk, g.Hkv,
+                                g.Hq, stream);
+  if (e != hipSuccess) return e;
+  e = launch_absmax(w.st.maxbits, kMaxDO, dout, static_cast<int64_t>(g.B) * g.Tq * g.Hq * kD, stream);
+  if (e != hipSuccess) return e;
+  launch_stage_rows(q, false, w.st.maxbits, kMaxQ, w.q16, w.q16t, nullptr, nullptr, g.B, g.Tq, w.Tq_pad, g.Hq, 0,
+                    0, stream);
+  e = launch_stage_rows(dout, false, w.st.maxbits, kMaxDO, w.do16, w.do16t, nullptr, nullptr, g.B, g.Tq, w.Tq_pad,
+                        g.Hq, 0, 0, stream);
+  if (e != hipSuccess) return e;
+
+  RowParams rp{};
+  rp.q = static_cast<const u16*>(q);
+  rp.dout = static_cast<const u16*>(dout);
+  rp.out = out;
+  rp.lse = lse;
+  rp.kbar = kbar;
+  rp.osa = osa;
+  rp.k16 = w.st.k16;
+  rp.k16t = w.st.k16t;
+  rp.v16 = w.st.v16;
+  rp.p16t = w.st.p16t;
+  rp.p16 = w.st.p16;
+  rp.maxbits = w.st.maxbits;
+  rp.dq = dq;
+  rp.u32 = w.u32;
+  rp.dkb32 = w.dkb32;
+  rp.x32 = w.x32;
+  rp.du32 = w.du32;
+  rp.st_alpha = w.alpha;
+  rp.st_delta = w.delta;
+  rp.B = g.B;
+  rp.Tq = g.Tq;
+  rp.Tk = g.Tk;
+  rp.Tk_pad = w.st.Tk_pad;
+  rp.Hq = g.Hq;
+  rp.Hkv = g.Hkv;
+  rp.G = G;
+  rp.causal = g.causal;
+  rp.window = g.window;
+  rp.scale = g.scale;
+  rp.rows_per_block = 32 * 4 / G;
+  if (split < g.Tq) {
+    RowParams r = rp;
+    r.row_begin = split;
+    r.row_end = g.Tq;
+    r.n_rb = (g.Tq - split + r.rows_per_block - 1) / r.rows_per_block;
+    hipLaunchKernelGGL(k_bwd_rows_fast<false>, dim3(g.B * g.Hkv * r.n_rb), dim3(256), 0, stream, r);
+  }
+  if (split > 0) {
+    RowParams r = rp;
+    r.row_begin = 0;
+    r.row_end = split;
+    r.n_rb = (split + r.rows_per_block - 1) / r.rows_per_block;
+    hipLaunchKernelGGL(k_bwd_rows_fast<true>, dim3(g.B * g.Hkv * r.n_rb), dim3(256), 0, stream, r);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // fp16 copies of u and dkbar (lo parts for rows < split)
+  launch_stage_rows(w.u32, true, w.st.maxbits, kMaxU, w.u16, w.u16t, split > 0 ? w.u16lo : nullptr, w.u16tlo, g.B,
+                    g.Tq, w.Tq_pad, g.Hq, split, w.lo_pad, stream);
+  e = launch_stage_rows(w.dkb32, true, w.st.maxbits, kMaxDKB, w.e16, w.e16t, split > 0 ? w.e16lo : nullptr,
+                        w.e16tlo, g.B, g.Tq, w.Tq_pad, g.Hq, split, w.lo_pad, stream);
+  if (e != hipSuccess) return e;
+
+  KeyParams kp{};
+  kp.k16 = w.st.k16;
+  kp.v16 = w.st.v16;
+  kp.q16 = w.q16;
+  kp.q16t = w.q16t;
+  kp.do16 = w.do16;
+  kp.do16t = w.do16t;
+  kp.u16 = w.u16;
+  kp.u16t = w.u16t;
+  kp.e16 = w.e16;
+  kp.e16t = w.e16t;
+  kp.u16lo = w.u16lo;
+  kp.u16tlo = w.u16tlo;
+  kp.e16lo = w.e16lo;
+  kp.e16tlo = w.e16tlo;
+  kp.lse = lse;
+  kp.alpha = w.alpha;
+  kp.delta = w.delta;
+  kp.maxbits = w.st.maxbits;
+  kp.dk = dk;
+  kp.dv = dv;
+  kp.B = g.B;
+  kp.Tq = g.Tq;
+  kp.Tk = g.Tk;
+  kp.Tk_pad = w.st.Tk_pad;
+  kp.Tq_pad = w.Tq_pad;
+  kp.lo_pad = w.lo_pad;
+  kp.Hq = g.Hq;
+  kp.Hkv = g.Hkv;
+  kp.G = G;
+  kp.causal = g.causal;
+  kp.window = g.window;
+  kp.scale = g.scale;
+  kp.n_kb = (g.Tk + 127) / 128;
+  kp.key_hi = g.Tk;
+  {
+    // every key block, rows >= split, writing
+    KeyParams k2 = kp;
+    k2.row_lo = split;
+    k2.row_hi = g.Tq;
+    k2.accumulate = 0;
+    mark_main_begin(stream);
+    hipLaunchKernelGGL(k_bwd_keys_fast<false>, dim3(g.B * g.Hkv * k2.n_kb), dim3(256), 0, stream, k2);
+    mark_main_end(stream);
+  }
+  if (split > 0) {
+    // rows < split: only keys those rows can see, accumulated on top
+    const int off = g.Tk - g.Tq;
+    int khi = g.causal ? split - 1 + off + 1 : g.Tk;
+    khi = khi > g.Tk ? g.Tk : khi;
+    if (khi > 0) {
+      KeyParams k2 = kp;
+      k2.row_lo = 0;
+      k2.row_hi = split;
+      k2.accumulate = 1;
+      k2.key_hi = khi;
+      k2.n_kb = (khi + 127) / 128;
+      hipLaunchKernelGGL(k_bwd_keys_fast<true>, dim3(g.B * g.Hkv * k2.n_kb), dim3(256), 0, stream, k2);
+    }
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int R = g.B * g.Tq;
+  hipLaunchKernelGGL(k_dp_partial, dim3(w.nchunks, g.Hq), dim3(256), 0, stream, w.x32, w.du32, w.part, R, g.Hq);
+  hipLaunchKernelGGL(k_dp_reduce, dim3(64), dim3(256), 0, stream, w.part, dP, w.nchunks, g.Hq);
+  return hipGetLastError();
+}
+
+}  // namespace plx

@@ -98,36 +98,54 @@ __device__ __forceinline__ float sum8(f16x8 v, float acc) {
 }
 
 // ---- staging buffers inside the caller's workspace ----
+// Slots of the max-abs array (float bits; non-negative floats order like their bits).
+enum MaxSlot { kMaxQ = 0, kMaxK = 1, kMaxV = 2, kMaxP = 3, kMaxDO = 4, kMaxU = 5, kMaxDKB = 6, kMaxDelta = 7,
+               kMaxAlpha = 8 };
+
 struct Staging {
-  uint32_t* maxbits;   // [4]: max |Q|, |K|, |V|, |P| as float bits (non-negative floats order as uints)
+  uint32_t* maxbits;   // [16] max-abs values, see MaxSlot
   _Float16* k16;
   _Float16* k16t;
-  _Float16* v16t;
+  _Float16* v16t;      // forward only (nullptr otherwise)
+  _Float16* v16;       // backward only: V rows, d permuted (nullptr otherwise)
   _Float16* p16t;
+  _Float16* p16;       // backward only: P rows, columns permuted (nullptr otherwise)
   int Tk_pad;
   size_t bytes;        // total workspace used
 };
 
-inline Staging staging_layout(void* ws, int B, int Tk, int Hkv, int Hq) {
+inline size_t ws_take(size_t& off, size_t n) {
+  const size_t at = off;
+  off += (n + 255) / 256 * 256;
+  return at;
+}
+
+// Staging buffers at the start of `ws` (ws may be nullptr to size them).
+inline Staging staging_layout(void* ws, int B, int Tk, int Hkv, int Hq, bool backward = false) {
   Staging s{};
   s.Tk_pad = (Tk + kKeyTile - 1) / kKeyTile * kKeyTile;
   const size_t kv = static_cast<size_t>(B) * s.Tk_pad * Hkv * kD * sizeof(_Float16);
   const size_t p = static_cast<size_t>(Hq) * kD * kD * sizeof(_Float16);
   char* base = static_cast<char*>(ws);
   size_t off = 0;
-  s.maxbits = reinterpret_cast<uint32_t*>(base + off);
-  off += 256;
-  s.k16 = reinterpret_cast<_Float16*>(base + off);
-  off += (kv + 255) / 256 * 256;
-  s.k16t = reinterpret_cast<_Float16*>(base + off);
-  off += (kv + 255) / 256 * 256;
-  s.v16t = reinterpret_cast<_Float16*>(base + off);
-  off += (kv + 255) / 256 * 256;
-  s.p16t = reinterpret_cast<_Float16*>(base + off);
-  off += (p + 255) / 256 * 256;
+  s.maxbits = reinterpret_cast<uint32_t*>(base + ws_take(off, 256));
+  s.k16 = reinterpret_cast<_Float16*>(base + ws_take(off, kv));
+  s.k16t = reinterpret_cast<_Float16*>(base + ws_take(off, kv));
+  if (backward) s.v16 = reinterpret_cast<_Float16*>(base + ws_take(off, kv));
+  else s.v16t = reinterpret_cast<_Float16*>(base + ws_take(off, kv));
+  s.p16t = reinterpret_cast<_Float16*>(base + ws_take(off, p));
+  if (backward) s.p16 = reinterpret_cast<_Float16*>(base + ws_take(off, p));
   s.bytes = off;
   return s;
 }
+
+// max-abs of one more bf16 tensor into maxbits[slot].
+hipError_t launch_absmax(uint32_t* maxbits, int slot, const void* x, int64_t n, hipStream_t stream);
+
+// Query-side fp16 copies (see k_stage_rows in fast_staging.hip).
+hipError_t launch_stage_rows(const void* src, bool f32, const uint32_t* maxbits, int max_idx, _Float16* dst,
+                             _Float16* dstt, _Float16* lo, _Float16* lot, int B, int Tq, int Tq_pad, int Hq,
+                             int lo_rows, int lo_pad, hipStream_t stream);
 
 // Launches the staging kernels: max-abs of q (rows [0, Tq)), k, v, P, then the fp16 copies.
 // q may be nullptr (decode stages q itself).

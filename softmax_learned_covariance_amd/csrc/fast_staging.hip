@@ -6,7 +6,7 @@ namespace plx {
 namespace {
 
 __global__ __launch_bounds__(64) void k_zero_max(uint32_t* maxbits) {
-  if (threadIdx.x < 4) maxbits[threadIdx.x] = 0u;
+  if (threadIdx.x < 16) maxbits[threadIdx.x] = 0u;
 }
 
 // blockIdx.y selects the tensor: 0 q, 1 k, 2 v, 3 P.  Elements are bf16, counts multiples of 8.
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void k_absmax(const u16* q, int64_t nq, const 
 // One block per (64-key tile, kv head, batch): K16 rows, K16t and V16t columns.
 __global__ __launch_bounds__(256) void k_stage_kv(const u16* k, const u16* v, const uint32_t* maxbits,
                                                   _Float16* k16, _Float16* k16t, _Float16* v16t,
-                                                  int Tk, int Tk_pad, int Hkv) {
+                                                  _Float16* v16, int Tk, int Tk_pad, int Hkv) {
   constexpr int LD = kD + 2;  // padded LDS row (halves) for conflict-light column reads
   __shared__ _Float16 ks[kKeyTile * LD];
   __shared__ _Float16 vs[kKeyTile * LD];
@@ -80,6 +80,11 @@ __global__ __launch_bounds__(256) void k_stage_kv(const u16* k, const u16* v, co
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = ks[r * LD + 16 * (c >> 1) + perm16(8 * (c & 1) + e)];
     *reinterpret_cast<f16x8*>(k16 + ((static_cast<int64_t>(b) * Tk_pad + key0 + r) * Hkv + g) * kD + c * 8) = o;
+    if (v16) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = vs[r * LD + 16 * (c >> 1) + perm16(8 * (c & 1) + e)];
+      *reinterpret_cast<f16x8*>(v16 + ((static_cast<int64_t>(b) * Tk_pad + key0 + r) * Hkv + g) * kD + c * 8) = o;
+    }
   }
   // K16t, V16t: d rows, keys permuted within groups of 16
   const int64_t trow = (static_cast<int64_t>(b) * Hkv + g) * kD;
@@ -94,12 +99,13 @@ __global__ __launch_bounds__(256) void k_stage_kv(const u16* k, const u16* v, co
     }
     const int64_t off = (trow + d) * Tk_pad + key0 + c * 8;
     *reinterpret_cast<f16x8*>(k16t + off) = ok;
-    *reinterpret_cast<f16x8*>(v16t + off) = ov;
+    if (v16t) *reinterpret_cast<f16x8*>(v16t + off) = ov;
   }
 }
 
-// One block per query head: P16t[h][a][b'] = sP * P[h][perm(b')][a].
-__global__ __launch_bounds__(256) void k_stage_p(const u16* P, const uint32_t* maxbits, _Float16* p16t) {
+// One block per query head: P16t[h][a][b'] = sP * P[h][perm(b')][a]; optionally P16[h][b][a'] = sP * P[h][b][perm(a')].
+__global__ __launch_bounds__(256) void k_stage_p(const u16* P, const uint32_t* maxbits, _Float16* p16t,
+                                                 _Float16* p16) {
   constexpr int LD = kD + 2;
   __shared__ _Float16 ps[kD * LD];
   const int h = blockIdx.x, t = threadIdx.x;
@@ -113,6 +119,68 @@ __global__ __launch_bounds__(256) void k_stage_p(const u16* P, const uint32_t* m
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = ps[(16 * (c >> 1) + perm16(8 * (c & 1) + e)) * LD + a];
     *reinterpret_cast<f16x8*>(p16t + (static_cast<int64_t>(h) * kD + a) * kD + c * 8) = o;
+    if (p16) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = ps[a * LD + 16 * (c >> 1) + perm16(8 * (c & 1) + e)];
+      *reinterpret_cast<f16x8*>(p16 + (static_cast<int64_t>(h) * kD + a) * kD + c * 8) = o;
+    }
+  }
+}
+
+// Query-side tensors for the key-major backward kernel.  One block per (32-row tile, head, batch):
+// src [B][Tq][Hq][128] (bf16 or fp32) -> dst [B][Hq][Tq_pad][128'] (rows, d permuted) and
+// dstt [B][Hq][128][Tq_pad'] (transposed, rows permuted within groups of 16), scaled by
+// range_scale(max) with max = maxbits[max_idx].  With lo / lot, also the fp16 residuals
+// x*s - hi for rows < lo_rows (lo [B][Hq][lo_pad][128'], lot [B][Hq][128][lo_pad']).
+template <bool F32>
+__global__ __launch_bounds__(256) void k_stage_rows(const void* src, const uint32_t* maxbits, int max_idx,
+                                                    _Float16* dst, _Float16* dstt, _Float16* lo,
+                                                    _Float16* lot, int Tq, int Tq_pad, int Hq,
+                                                    int lo_rows, int lo_pad) {
+  constexpr int LD = kD + 2;
+  __shared__ _Float16 hs[32 * LD];
+  __shared__ _Float16 ls[32 * LD];
+  const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const int r0 = qt * 32;
+  const float sc = range_scale(__uint_as_float(maxbits[max_idx]));
+  const bool want_lo = lo != nullptr && r0 < lo_rows;
+  for (int e = t; e < 32 * kD; e += 256) {
+    const int r = e / kD, d = e % kD, row = r0 + r;
+    float x = 0.f;
+    if (row < Tq) {
+      const int64_t off = ((static_cast<int64_t>(b) * Tq + row) * Hq + h) * kD + d;
+      x = F32 ? static_cast<const float*>(src)[off] : bf16_to_f32(static_cast<const u16*>(src)[off]);
+    }
+    x *= sc;
+    const _Float16 hi = static_cast<_Float16>(x);
+    hs[r * LD + d] = hi;
+    if (want_lo) ls[r * LD + d] = static_cast<_Float16>(x - static_cast<float>(hi));
+  }
+  __syncthreads();
+  const int64_t bh = static_cast<int64_t>(b) * Hq + h;
+  for (int ci = t; ci < 32 * 16; ci += 256) {
+    const int r = ci >> 4, c = ci & 15;
+    f16x8 o, ol;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = 16 * (c >> 1) + perm16(8 * (c & 1) + e);
+      o[e] = hs[r * LD + d];
+      ol[e] = ls[r * LD + d];
+    }
+    *reinterpret_cast<f16x8*>(dst + (bh * Tq_pad + r0 + r) * kD + c * 8) = o;
+    if (want_lo) *reinterpret_cast<f16x8*>(lo + (bh * lo_pad + r0 + r) * kD + c * 8) = ol;
+  }
+  for (int ci = t; ci < kD * 4; ci += 256) {
+    const int d = ci >> 2, c = ci & 3;
+    f16x8 o, ol;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int r = 16 * (c >> 1) + perm16(8 * (c & 1) + e);
+      o[e] = hs[r * LD + d];
+      ol[e] = ls[r * LD + d];
+    }
+    *reinterpret_cast<f16x8*>(dstt + (bh * kD + d) * Tq_pad + r0 + c * 8) = o;
+    if (want_lo) *reinterpret_cast<f16x8*>(lot + (bh * kD + d) * lo_pad + r0 + c * 8) = ol;
   }
 }
 
@@ -130,8 +198,30 @@ hipError_t launch_staging(const Staging& s, const void* q, int64_t q_elems, cons
   if (B > 0 && s.Tk_pad > 0)
     hipLaunchKernelGGL(k_stage_kv, dim3(s.Tk_pad / kKeyTile, Hkv, B), dim3(256), 0, stream,
                        static_cast<const u16*>(k), static_cast<const u16*>(v), s.maxbits, s.k16, s.k16t,
-                       s.v16t, Tk, s.Tk_pad, Hkv);
-  hipLaunchKernelGGL(k_stage_p, dim3(Hq), dim3(256), 0, stream, static_cast<const u16*>(P), s.maxbits, s.p16t);
+                       s.v16t, s.v16, Tk, s.Tk_pad, Hkv);
+  hipLaunchKernelGGL(k_stage_p, dim3(Hq), dim3(256), 0, stream, static_cast<const u16*>(P), s.maxbits, s.p16t,
+                     s.p16);
+  return hipGetLastError();
+}
+
+hipError_t launch_absmax(uint32_t* maxbits, int slot, const void* x, int64_t n, hipStream_t stream) {
+  hipLaunchKernelGGL(k_absmax, dim3(256, 1), dim3(256), 0, stream, static_cast<const u16*>(x), n,
+                     static_cast<const u16*>(nullptr), static_cast<const u16*>(nullptr), int64_t{0},
+                     static_cast<const u16*>(nullptr), int64_t{0}, maxbits + slot);
+  return hipGetLastError();
+}
+
+hipError_t launch_stage_rows(const void* src, bool f32, const uint32_t* maxbits, int max_idx, _Float16* dst,
+                             _Float16* dstt, _Float16* lo, _Float16* lot, int B, int Tq, int Tq_pad, int Hq,
+                             int lo_rows, int lo_pad, hipStream_t stream) {
+  if (B == 0 || Tq_pad == 0) return hipSuccess;
+  dim3 grid(Tq_pad / 32, Hq, B);
+  if (f32)
+    hipLaunchKernelGGL(k_stage_rows<true>, grid, dim3(256), 0, stream, src, maxbits, max_idx, dst, dstt, lo,
+                       lot, Tq, Tq_pad, Hq, lo_rows, lo_pad);
+  else
+    hipLaunchKernelGGL(k_stage_rows<false>, grid, dim3(256), 0, stream, src, maxbits, max_idx, dst, dstt, lo,
+                       lot, Tq, Tq_pad, Hq, lo_rows, lo_pad);
   return hipGetLastError();
 }
 

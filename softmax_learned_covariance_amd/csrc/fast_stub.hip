@@ -1,15 +1,8 @@
-// Fast backward and decode are not written yet: report "not supported" so the
+// The fast decode is not written yet: report "not supported" so the
 // generic kernels serve those calls.
 #include "plx_internal.h"
 
 namespace plx {
-bool fast_bwd_supported(const Geom&) { return false; }
-size_t fast_bwd_workspace(const Geom&) { return 0; }
-hipError_t launch_fast_bwd(const Geom&, const void*, const void*, const void*, const void*,
-                           const float*, const void*, const float*, const float*, const float*,
-                           float*, float*, float*, float*, int, void*, hipStream_t) {
-  return hipErrorNotSupported;
-}
 bool fast_decode_supported(const Geom&) { return false; }
 size_t fast_decode_workspace(const Geom&) { return 0; }
 hipError_t launch_fast_decode(const Geom&, const void*, const void*, const void*, const int32_t*,
