@@ -1,0 +1,413 @@
+// Parallax decode for gfx950: one new query per sequence against a bf16 key/value cache.
+//
+// The decode path of the pages' hardware section (gist.science technical summary
+// of "Parallax: Parameterized Local Linear Attention for Language Modeling",
+// "Hardware-aware algorithm": a dedicated decode kernel in which the softmax and
+// covariance branches share one KV stream).  The probe u = P^T (q - kbar) needs
+// the whole sequence's kbar, so the cache is streamed twice:
+//   pass 1   split-KV partials of the online softmax: m, l, o = sum p v, kbar = sum p k;
+//   combine  m, l, o, kbar over splits -> lse, o, kbar, u = P^T (q - kbar), alpha = u.kbar;
+//   pass 2   split-KV partials of c = sum_j p_j (u.k_j - alpha) (v_j - o) with p_j = exp(s_j - lse);
+//   finish   out = o + sum over splits of c.
+// The work is bandwidth-bound (a few flops per cache byte), so the inner loops
+// are fp32 VALU on LDS-staged bf16 tiles: the cache is read straight from HBM in
+// 16-byte chunks, with no fp16 staging copy.  One workgroup (256 threads) owns
+// one (batch, kv head, key split) and all query heads of that kv head.
+#include <math.h>
+
+#include "fast_common.h"
+#include "plx_internal.h"
+
+namespace plx {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kTile = 64;          // keys per LDS tile
+constexpr int kRowH = kD + 8;      // padded LDS row (bf16 elements)
+constexpr int kMaxG = 4;
+
+struct DecParams {
+  const u16 *q, *kc, *vc, *P;
+  const int32_t* seqlens;
+  float* out;
+  // workspace
+  float *pm, *pl, *po, *pk;      // pass 1 partials: [B][Hq][ns] (m, l) and [B][Hq][ns][128] (o, kbar)
+  float *so, *su, *salpha, *slse;  // combined: o, u [B][Hq][128], alpha, lse [B][Hq]
+  float* pc;                     // pass 2 partials [B][Hq][ns][128]
+  int B, L, Hq, Hkv, G, window, ns, chunk;
+  float scale;
+};
+
+__device__ __forceinline__ void seq_range(const DecParams& p, int b, int& lo, int& hi) {
+  int Lb = p.L;
+  if (p.seqlens) Lb = min(max(p.seqlens[b], 0), p.L);
+  hi = Lb;
+  lo = p.window > 0 ? max(0, Lb - p.window) : 0;
+}
+
+struct __align__(16) DecTiles {
+  union {
+    struct {
+      u16 k[2][kTile * kRowH];
+      u16 v[2][kTile * kRowH];
+    };
+    float red[4][kMaxG][kD * 2];   // after the key loop: the 4 key parts of each accumulator
+  };
+  float q[kMaxG][kD];
+  float u[kMaxG][kD];
+  float s[kMaxG][kTile];
+  float w[kMaxG][kTile];
+  float corr[kMaxG];
+};
+
+__device__ __forceinline__ void tile_load(const DecParams& p, DecTiles& T, int buf, int b, int g, int key0, int hi,
+                                          int tid) {
+  // 64 keys x 16 chunks of 16 bytes, K and V: 4 + 4 chunks per thread
+  uint4 kr[4], vr[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ci = tid + 256 * j, r = ci >> 4, c = ci & 15, key = key0 + r;
+    kr[j] = uint4{0u, 0u, 0u, 0u};
+    vr[j] = uint4{0u, 0u, 0u, 0u};
+    if (key < hi) {
+      const int64_t off = ((static_cast<int64_t>(b) * p.L + key) * p.Hkv + g) * kD + c * 8;
+      kr[j] = *reinterpret_cast<const uint4*>(p.kc + off);
+      vr[j] = *reinterpret_cast<const uint4*>(p.vc + off);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ci = tid + 256 * j, r = ci >> 4, c = ci & 15;
+    *reinterpret_cast<uint4*>(&T.k[buf][r * kRowH + c * 8]) = kr[j];
+    *reinterpret_cast<uint4*>(&T.v[buf][r * kRowH + c * 8]) = vr[j];
+  }
+}
+
+// Dot products of the tile's keys with the G vectors in `vecs` (q or u): dots[h][j].
+// 256 threads; thread t takes dot (t / tpd) and a 128/tpd slice of d.
+template <int G>
+__device__ __forceinline__ void tile_dots(const DecTiles& T, int buf, const float (*vecs)[kD], float (*dots)[kTile],
+                                          int tid) {
+  constexpr int ndots = G * kTile;
+  constexpr int tpd = 256 / ndots;           // threads per dot: 4, 2 or 1
+  constexpr int len = kD / tpd;
+  const int dot = tid / tpd, part = tid % tpd;
+  const int h = dot / kTile, j = dot % kTile;
+  const u16* kr = &T.k[buf][j * kRowH + part * len];
+  const float* vr = &vecs[h][part * len];
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < len; c += 8) {
+    const uint4 w = *reinterpret_cast<const uint4*>(kr + c);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(__uint_as_float(ws[e] << 16), vr[c + 2 * e], acc);
+      acc = fmaf(__uint_as_float(ws[e] & 0xffff0000u), vr[c + 2 * e + 1], acc);
+    }
+  }
+  if constexpr (tpd >= 2) acc += __shfl_xor(acc, 1, 64);
+  if constexpr (tpd >= 4) acc += __shfl_xor(acc, 2, 64);
+  if (part == 0) dots[h][j] = acc;
+}
+
+// ---------------------------------- pass 1 ----------------------------------
+template <int G>
+__global__ __launch_bounds__(256) void k_dec_pass1(DecParams p) {
+  __shared__ DecTiles T;
+  const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  int lo, hi;
+  seq_range(p, b, lo, hi);
+  const int k0 = max(lo, sp * p.chunk), k1 = min(hi, (sp + 1) * p.chunk);
+  const float c2 = p.scale * kLog2e;
+  for (int e = tid; e < G * kD; e += 256) {
+    const int h = e / kD, d = e % kD;
+    T.q[h][d] = bf16_to_f32(p.q[(static_cast<int64_t>(b) * p.Hq + g * G + h) * kD + d]) * c2;  // scores in log2 units
+  }
+  // accumulator ownership: thread t -> dims 2*(t%64), +1 ; keys j = part (mod 4)
+  const int dp = tid & 63, part = tid >> 6;
+  float o[G][2], kb[G][2];
+  float m = -INFINITY, l = 0.f;  // per head, kept by the softmax wave (wave h) and broadcast through LDS
+#pragma unroll
+  for (int h = 0; h < G; ++h) o[h][0] = o[h][1] = kb[h][0] = kb[h][1] = 0.f;
+  const int nt = k1 > k0 ? (k1 - k0 + kTile - 1) / kTile : 0;
+  if (nt > 0) tile_load(p, T, 0, b, g, k0, k1, tid);
+  __syncthreads();
+  for (int it = 0; it < nt; ++it) {
+    const int buf = it & 1, key0 = k0 + it * kTile;
+    tile_dots<G>(T, buf, T.q, T.s, tid);
+    __syncthreads();
+    const int w = tid >> 6, lane = tid & 63;
+    if (w < G) {  // wave h: online softmax of head h over this tile
+      const float sv = key0 + lane < k1 ? T.s[w][lane] : -INFINITY;
+      float tm = sv;
+#pragma unroll
+      for (int o2 = 32; o2 > 0; o2 >>= 1) tm = fmaxf(tm, __shfl_xor(tm, o2, 64));
+      const float mn = fmaxf(m, tm);
+      const float corr = m == -INFINITY ? 0.f : exp2f(m - mn);
+      const float pv = sv == -INFINITY ? 0.f : exp2f(sv - mn);
+      float ts = pv;
+#pragma unroll
+      for (int o2 = 32; o2 > 0; o2 >>= 1) ts += __shfl_xor(ts, o2, 64);
+      l = l * corr + ts;
+      m = mn;
+      T.w[w][lane] = pv;
+      if (lane == 0) T.corr[w] = corr;
+    }
+    if (it + 1 < nt) tile_load(p, T, buf ^ 1, b, g, key0 + kTile, k1, tid);
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float cr = T.corr[h];
+      o[h][0] *= cr;
+      o[h][1] *= cr;
+      kb[h][0] *= cr;
+      kb[h][1] *= cr;
+    }
+#pragma unroll 4
+    for (int j = part; j < kTile; j += 4) {
+      const uint32_t kw = *reinterpret_cast<const uint32_t*>(&T.k[buf][j * kRowH + 2 * dp]);
+      const uint32_t vw = *reinterpret_cast<const uint32_t*>(&T.v[buf][j * kRowH + 2 * dp]);
+      const float k0f = __uint_as_float(kw << 16), k1f = __uint_as_float(kw & 0xffff0000u);
+      const float v0f = __uint_as_float(vw << 16), v1f = __uint_as_float(vw & 0xffff0000u);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float pw = T.w[h][j];
+        o[h][0] = fmaf(pw, v0f, o[h][0]);
+        o[h][1] = fmaf(pw, v1f, o[h][1]);
+        kb[h][0] = fmaf(pw, k0f, kb[h][0]);
+        kb[h][1] = fmaf(pw, k1f, kb[h][1]);
+      }
+    }
+    __syncthreads();
+  }
+  // reduce the 4 key parts and write the partials
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    T.red[part][h][2 * dp] = o[h][0];
+    T.red[part][h][2 * dp + 1] = o[h][1];
+    T.red[part][h][kD + 2 * dp] = kb[h][0];
+    T.red[part][h][kD + 2 * dp + 1] = kb[h][1];
+  }
+  __syncthreads();
+  for (int e = tid; e < G * 2 * kD; e += 256) {
+    const int h = e / (2 * kD), r = e % (2 * kD);
+    const float s = T.red[0][h][r] + T.red[1][h][r] + T.red[2][h][r] + T.red[3][h][r];
+    const int64_t base = ((static_cast<int64_t>(b) * p.Hq + g * G + h) * p.ns + sp) * kD;
+    if (r < kD) p.po[base + r] = s;
+    else p.pk[base + r - kD] = s;
+  }
+  const int w = tid >> 6, lane = tid & 63;
+  if (w < G && lane == 0) {
+    const int64_t si = (static_cast<int64_t>(b) * p.Hq + g * G + w) * p.ns + sp;
+    p.pm[si] = m;
+    p.pl[si] = l;
+  }
+}
+
+// ------------------------------- combine 1 -----------------------------------
+// one block (128 threads) per (batch, query head): lse, o, kbar, u = P^T (q - kbar), alpha
+__global__ __launch_bounds__(128) void k_dec_combine1(DecParams p) {
+  __shared__ float xs[kD];
+  __shared__ float red[2];
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const int64_t bh = static_cast<int64_t>(b) * p.Hq + h;
+  float M = -INFINITY;
+  for (int s = 0; s < p.ns; ++s) M = fmaxf(M, p.pm[bh * p.ns + s]);
+  float L = 0.f, o = 0.f, kb = 0.f;
+  for (int s = 0; s < p.ns; ++s) {
+    const float ms = p.pm[bh * p.ns + s];
+    if (ms == -INFINITY) continue;
+    const float f = exp2f(ms - M);
+    L += p.pl[bh * p.ns + s] * f;
+    o += p.po[(bh * p.ns + s) * kD + d] * f;
+    kb += p.pk[(bh * p.ns + s) * kD + d] * f;
+  }
+  const bool has = L > 0.f;
+  o = has ? o / L : 0.f;
+  kb = has ? kb / L : 0.f;
+  const float qd = bf16_to_f32(p.q[bh * kD + d]);
+  xs[d] = qd - kb;
+  __syncthreads();
+  float u = 0.f;
+  const u16* Ph = p.P + static_cast<int64_t>(h) * kD * kD;
+  for (int bb = 0; bb < kD; ++bb) u = fmaf(bf16_to_f32(Ph[bb * kD + d]), xs[bb], u);  // u[d] = sum_b P[b][d] x[b]
+  float al = u * kb;
+#pragma unroll
+  for (int o2 = 32; o2 > 0; o2 >>= 1) al += __shfl_xor(al, o2, 64);
+  if ((d & 63) == 0) red[d >> 6] = al;
+  __syncthreads();
+  al = red[0] + red[1];
+  p.so[bh * kD + d] = o;
+  p.su[bh * kD + d] = u;
+  if (d == 0) {
+    p.salpha[bh] = al;
+    p.slse[bh] = has ? M + log2f(L) : -INFINITY;   // log2 units of the scaled scores
+  }
+}
+
+// ---------------------------------- pass 2 ----------------------------------
+template <int G>
+__global__ __launch_bounds__(256) void k_dec_pass2(DecParams p) {
+  __shared__ DecTiles T;
+  __shared__ float st[kMaxG][2];  // lse (log2 units), alpha
+  const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  int lo, hi;
+  seq_range(p, b, lo, hi);
+  const int k0 = max(lo, sp * p.chunk), k1 = min(hi, (sp + 1) * p.chunk);
+  const float c2 = p.scale * kLog2e;
+  for (int e = tid; e < G * kD; e += 256) {
+    const int h = e / kD, d = e % kD;
+    const int64_t bh = static_cast<int64_t>(b) * p.Hq + g * G + h;
+    T.q[h][d] = bf16_to_f32(p.q[bh * kD + d]) * c2;
+    T.u[h][d] = p.su[bh * kD + d];
+  }
+  if (tid < G) {
+    const int64_t bh = static_cast<int64_t>(b) * p.Hq + g * G + tid;
+    st[tid][0] = p.slse[bh];
+    st[tid][1] = p.salpha[bh];
+  }
+  const int dp = tid & 63, part = tid >> 6;
+  float cv[G][2], ws[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) cv[h][0] = cv[h][1] = ws[h] = 0.f;
+  const int nt = k1 > k0 ? (k1 - k0 + kTile - 1) / kTile : 0;
+  if (nt > 0) tile_load(p, T, 0, b, g, k0, k1, tid);
+  __syncthreads();
+  for (int it = 0; it < nt; ++it) {
+    const int buf = it & 1, key0 = k0 + it * kTile;
+    tile_dots<G>(T, buf, T.q, T.s, tid);
+    tile_dots<G>(T, buf, T.u, T.w, tid);
+    __syncthreads();
+    // weights w_j = p_j (u.k_j - alpha), p_j = exp2(s_j - lse)
+    for (int e = tid; e < G * kTile; e += 256) {
+      const int h = e / kTile, j = e % kTile;
+      const float lse = st[h][0];
+      const float pw = (key0 + j < k1 && lse > -INFINITY) ? exp2f(T.s[h][j] - lse) : 0.f;
+      T.w[h][j] = pw * (T.w[h][j] - st[h][1]);
+    }
+    if (it + 1 < nt) tile_load(p, T, buf ^ 1, b, g, key0 + kTile, k1, tid);
+    __syncthreads();
+#pragma unroll 4
+    for (int j = part; j < kTile; j += 4) {
+      const uint32_t vw = *reinterpret_cast<const uint32_t*>(&T.v[buf][j * kRowH + 2 * dp]);
+      const float v0f = __uint_as_float(vw << 16), v1f = __uint_as_float(vw & 0xffff0000u);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float wj = T.w[h][j];
+        cv[h][0] = fmaf(wj, v0f, cv[h][0]);
+        cv[h][1] = fmaf(wj, v1f, cv[h][1]);
+        ws[h] += wj;
+      }
+    }
+    __syncthreads();
+  }
+  // partial c = sum w v - (sum w) o
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    T.red[part][h][2 * dp] = cv[h][0];
+    T.red[part][h][2 * dp + 1] = cv[h][1];
+    if (dp == 0) T.red[part][h][kD] = ws[h];
+  }
+  __syncthreads();
+  for (int e = tid; e < G * kD; e += 256) {
+    const int h = e / kD, d = e % kD;
+    const int64_t bh = static_cast<int64_t>(b) * p.Hq + g * G + h;
+    const float s = T.red[0][h][d] + T.red[1][h][d] + T.red[2][h][d] + T.red[3][h][d];
+    const float wsum = T.red[0][h][kD] + T.red[1][h][kD] + T.red[2][h][kD] + T.red[3][h][kD];
+    p.pc[(bh * p.ns + sp) * kD + d] = s - wsum * p.so[bh * kD + d];
+  }
+}
+
+// out = o + sum over splits of c
+__global__ __launch_bounds__(128) void k_dec_finish(DecParams p) {
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const int64_t bh = static_cast<int64_t>(b) * p.Hq + h;
+  float c = 0.f;
+  for (int s = 0; s < p.ns; ++s) c += p.pc[(bh * p.ns + s) * kD + d];
+  p.out[bh * kD + d] = p.so[bh * kD + d] + c;
+}
+
+struct DecWs {
+  float *pm, *pl, *po, *pk, *so, *su, *salpha, *slse, *pc;
+  int ns, chunk;
+  size_t bytes;
+};
+
+DecWs dec_layout(const Geom& g, void* ws) {
+  DecWs w{};
+  const int slices = g.B * g.Hkv;
+  const int ntiles = (g.Tk + kTile - 1) / kTile;
+  int ns = slices > 0 ? (2048 + slices - 1) / slices : 1;
+  ns = ns < 1 ? 1 : (ns > ntiles ? ntiles : ns);
+  if (ns < 1) ns = 1;
+  w.ns = ns;
+  w.chunk = (ntiles + ns - 1) / ns * kTile;
+  char* base = static_cast<char*>(ws);
+  size_t off = 0;
+  const size_t bh = static_cast<size_t>(g.B) * g.Hq;
+  w.pm = reinterpret_cast<float*>(base + ws_take(off, bh * ns * 4));
+  w.pl = reinterpret_cast<float*>(base + ws_take(off, bh * ns * 4));
+  w.po = reinterpret_cast<float*>(base + ws_take(off, bh * ns * kD * 4));
+  w.pk = reinterpret_cast<float*>(base + ws_take(off, bh * ns * kD * 4));
+  w.pc = reinterpret_cast<float*>(base + ws_take(off, bh * ns * kD * 4));
+  w.so = reinterpret_cast<float*>(base + ws_take(off, bh * kD * 4));
+  w.su = reinterpret_cast<float*>(base + ws_take(off, bh * kD * 4));
+  w.salpha = reinterpret_cast<float*>(base + ws_take(off, bh * 4));
+  w.slse = reinterpret_cast<float*>(base + ws_take(off, bh * 4));
+  w.bytes = off;
+  return w;
+}
+
+}  // namespace
+
+bool fast_decode_supported(const Geom& g) {
+  const int G = g.Hq / g.Hkv;
+  return g.bf16 && g.d == kD && !g.p_per_query && (G == 1 || G == 2 || G == 4);
+}
+
+size_t fast_decode_workspace(const Geom& g) { return dec_layout(g, nullptr).bytes; }
+
+hipError_t launch_fast_decode(const Geom& g, const void* q, const void* kc, const void* vc, const int32_t* seqlens,
+                              const void* P, float* out, void* ws, hipStream_t stream) {
+  const DecWs w = dec_layout(g, ws);
+  DecParams p{};
+  p.q = static_cast<const u16*>(q);
+  p.kc = static_cast<const u16*>(kc);
+  p.vc = static_cast<const u16*>(vc);
+  p.P = static_cast<const u16*>(P);
+  p.seqlens = seqlens;
+  p.out = out;
+  p.pm = w.pm;
+  p.pl = w.pl;
+  p.po = w.po;
+  p.pk = w.pk;
+  p.so = w.so;
+  p.su = w.su;
+  p.salpha = w.salpha;
+  p.slse = w.slse;
+  p.pc = w.pc;
+  p.B = g.B;
+  p.L = g.Tk;
+  p.Hq = g.Hq;
+  p.Hkv = g.Hkv;
+  p.G = g.Hq / g.Hkv;
+  p.window = g.window;
+  p.ns = w.ns;
+  p.chunk = w.chunk;
+  p.scale = g.scale;
+  const dim3 grid(w.ns, g.Hkv, g.B);
+  mark_main_begin(stream);
+  if (p.G == 1) hipLaunchKernelGGL(k_dec_pass1<1>, grid, dim3(256), 0, stream, p);
+  else if (p.G == 2) hipLaunchKernelGGL(k_dec_pass1<2>, grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL(k_dec_pass1<4>, grid, dim3(256), 0, stream, p);
+  mark_main_end(stream);
+  hipLaunchKernelGGL(k_dec_combine1, dim3(g.Hq, g.B), dim3(128), 0, stream, p);
+  if (p.G == 1) hipLaunchKernelGGL(k_dec_pass2<1>, grid, dim3(256), 0, stream, p);
+  else if (p.G == 2) hipLaunchKernelGGL(k_dec_pass2<2>, grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL(k_dec_pass2<4>, grid, dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(k_dec_finish, dim3(g.Hq, g.B), dim3(128), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace plx
