@@ -73,17 +73,24 @@ typedef struct {
   int32_t split_rows;     /* bf16 fast path: query rows < split_rows run on the fp32 path; < 0 selects the default */
 } plx_attn_desc;
 
+/* Kernels the profiling hook can bracket. */
+typedef enum {
+  PLX_KERNEL_FWD = 0,          /* forward: the fused two-pass MFMA kernel (generic kernel on the fp32 path) */
+  PLX_KERNEL_BWD_ROWS = 1,     /* backward: query-major kernel (du, dkbar, Delta, dq) */
+  PLX_KERNEL_BWD_KEYS = 2,     /* backward: key-major kernel (dk, dv); the generic key kernel on the fp32 path */
+  PLX_KERNEL_DECODE_PASS1 = 3, /* decode: first split-KV pass (generic kernel on the fp32 path) */
+  PLX_KERNEL_DECODE_PASS2 = 4  /* decode: second split-KV pass */
+} plx_kernel;
+
 /*
- * Profiling hook.  While set, every forward, backward and decode call made on
- * this thread records `before` (a hipEvent_t) on its stream immediately before
- * launching its main kernel and `after` immediately after it, so the caller can
- * time that one kernel with hipEventElapsedTime.  The main kernel is the fused
- * MFMA kernel of the fast path (the forward's two-pass kernel, the backward's
- * key-block kernel, the decode's split-KV kernel) and the widest generic kernel
- * otherwise.  Pass NULL, NULL to turn it off.  This thread-local pair is the
- * library's only state.
+ * Profiling hook.  While set, calls made on this thread record `before` (a
+ * hipEvent_t) on their stream immediately before launching the kernel
+ * `kernel` (a plx_kernel) and `after` immediately after it, so the caller can
+ * time that one kernel with hipEventElapsedTime.  Calls that do not launch that
+ * kernel record nothing.  Pass NULL, NULL to turn it off.  This thread-local
+ * setting is the library's only state.
  */
-void parallax_set_kernel_events(void* before, void* after);
+void parallax_set_kernel_events(int kernel, void* before, void* after);
 
 /* Library version of this header's ABI (PARALLAX_ABI_VERSION). */
 int parallax_abi_version(void);

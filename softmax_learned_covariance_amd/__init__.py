@@ -28,6 +28,7 @@ LIB_PATH = os.path.join(_PKG, "libparallax.so")
 
 PLX_OK, PLX_ERR_INVALID, PLX_ERR_UNSUPPORTED, PLX_ERR_WORKSPACE, PLX_ERR_HIP = range(5)
 PLX_F32, PLX_BF16 = 0, 1
+PLX_KERNEL_FWD, PLX_KERNEL_BWD_ROWS, PLX_KERNEL_BWD_KEYS, PLX_KERNEL_DECODE_PASS1, PLX_KERNEL_DECODE_PASS2 = range(5)
 
 
 class PlxAttnDesc(ctypes.Structure):
@@ -49,7 +50,7 @@ class ParallaxError(RuntimeError):
 _vp, _sz, _st = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
 _DESC = ctypes.POINTER(PlxAttnDesc)
 SIGNATURES = {
-    "parallax_set_kernel_events": (None, [_vp, _vp]),
+    "parallax_set_kernel_events": (None, [ctypes.c_int, _vp, _vp]),
     "parallax_abi_version": (ctypes.c_int, []),
     "parallax_status_string": (ctypes.c_char_p, [_st]),
     "parallax_last_error": (ctypes.c_char_p, []),

@@ -920,7 +920,9 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
     r.row_begin = split;
     r.row_end = g.Tq;
     r.n_rb = (g.Tq - split + r.rows_per_block - 1) / r.rows_per_block;
+    mark_begin(PLX_KERNEL_BWD_ROWS, stream);
     hipLaunchKernelGGL(k_bwd_rows_fast<false>, dim3(g.B * g.Hkv * r.n_rb), dim3(256), 0, stream, r);
+    mark_end(PLX_KERNEL_BWD_ROWS, stream);
   }
   if (split > 0) {
     RowParams r = rp;
@@ -979,9 +981,9 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
     k2.row_lo = split;
     k2.row_hi = g.Tq;
     k2.accumulate = 0;
-    mark_main_begin(stream);
+    mark_begin(PLX_KERNEL_BWD_KEYS, stream);
     hipLaunchKernelGGL(k_bwd_keys_fast<false>, dim3(g.B * g.Hkv * k2.n_kb), dim3(256), 0, stream, k2);
-    mark_main_end(stream);
+    mark_end(PLX_KERNEL_BWD_KEYS, stream);
   }
   if (split > 0) {
     // rows < split: only keys those rows can see, accumulated on top

@@ -397,15 +397,17 @@ hipError_t launch_fast_decode(const Geom& g, const void* q, const void* kc, cons
   p.chunk = w.chunk;
   p.scale = g.scale;
   const dim3 grid(w.ns, g.Hkv, g.B);
-  mark_main_begin(stream);
+  mark_begin(PLX_KERNEL_DECODE_PASS1, stream);
   if (p.G == 1) hipLaunchKernelGGL(k_dec_pass1<1>, grid, dim3(256), 0, stream, p);
   else if (p.G == 2) hipLaunchKernelGGL(k_dec_pass1<2>, grid, dim3(256), 0, stream, p);
   else hipLaunchKernelGGL(k_dec_pass1<4>, grid, dim3(256), 0, stream, p);
-  mark_main_end(stream);
+  mark_end(PLX_KERNEL_DECODE_PASS1, stream);
   hipLaunchKernelGGL(k_dec_combine1, dim3(g.Hq, g.B), dim3(128), 0, stream, p);
+  mark_begin(PLX_KERNEL_DECODE_PASS2, stream);
   if (p.G == 1) hipLaunchKernelGGL(k_dec_pass2<1>, grid, dim3(256), 0, stream, p);
   else if (p.G == 2) hipLaunchKernelGGL(k_dec_pass2<2>, grid, dim3(256), 0, stream, p);
   else hipLaunchKernelGGL(k_dec_pass2<4>, grid, dim3(256), 0, stream, p);
+  mark_end(PLX_KERNEL_DECODE_PASS2, stream);
   hipLaunchKernelGGL(k_dec_finish, dim3(g.Hq, g.B), dim3(128), 0, stream, p);
   return hipGetLastError();
 }

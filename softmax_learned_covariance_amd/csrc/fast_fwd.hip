@@ -505,9 +505,9 @@ hipError_t launch_fast_fwd(const Geom& g, const void* q, const void* k, const vo
     p.row_end = g.Tq;
     p.n_rb = (g.Tq - split + p.rows_per_block - 1) / p.rows_per_block;
     const int blocks = g.B * g.Hkv * p.n_rb;
-    mark_main_begin(stream);
+    mark_begin(PLX_KERNEL_FWD, stream);
     hipLaunchKernelGGL(k_fwd_fast<false>, dim3(blocks), dim3(512), 0, stream, p);
-    mark_main_end(stream);
+    mark_end(PLX_KERNEL_FWD, stream);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -473,7 +473,7 @@ __global__ __launch_bounds__(256) void k_fill(float* p, int64_t n, float val) {
 hipError_t launch_generic_fwd(const Geom& g, const void* q, const void* k, const void* v,
                               const void* P, const int32_t* seqlens, float* out, float* lse,
                               float* kbar, float* osa, int row_begin, int row_end,
-                              hipStream_t stream, bool mark) {
+                              hipStream_t stream, bool mark, int mark_id) {
   if (row_end <= row_begin || g.B == 0) return hipSuccess;
   Args a = make_args(g);
   a.q = q;
@@ -489,7 +489,7 @@ hipError_t launch_generic_fwd(const Geom& g, const void* q, const void* k, const
   a.row_end = row_end;
   dim3 grid((row_end - row_begin + kWaves - 1) / kWaves, g.Hq, g.B);
   const bool two = g.d > 64;
-  if (mark) mark_main_begin(stream);
+  if (mark) mark_begin(mark_id, stream);
   if (g.bf16) {
     if (two) hipLaunchKernelGGL((k_fwd<true, 2>), grid, dim3(256), 0, stream, a);
     else hipLaunchKernelGGL((k_fwd<true, 1>), grid, dim3(256), 0, stream, a);
@@ -497,7 +497,7 @@ hipError_t launch_generic_fwd(const Geom& g, const void* q, const void* k, const
     if (two) hipLaunchKernelGGL((k_fwd<false, 2>), grid, dim3(256), 0, stream, a);
     else hipLaunchKernelGGL((k_fwd<false, 1>), grid, dim3(256), 0, stream, a);
   }
-  if (mark) mark_main_end(stream);
+  if (mark) mark_end(mark_id, stream);
   return hipGetLastError();
 }
 
@@ -551,9 +551,9 @@ hipError_t launch_generic_bwd(const Geom& g, const void* q, const void* k, const
   } while (0)
     PLX_LAUNCH(k_bwd_rows, rgrid);
     if (g.Tk > 0) {
-      mark_main_begin(stream);
+      mark_begin(PLX_KERNEL_BWD_KEYS, stream);
       PLX_LAUNCH(k_bwd_keys, kgrid);
-      mark_main_end(stream);
+      mark_end(PLX_KERNEL_BWD_KEYS, stream);
     }
     PLX_LAUNCH(k_bwd_dq, rgrid);
 #undef PLX_LAUNCH

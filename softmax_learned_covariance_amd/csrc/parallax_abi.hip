@@ -13,6 +13,7 @@ namespace {
 thread_local char g_last_error[512] = "";
 thread_local hipEvent_t g_ev_before = nullptr;
 thread_local hipEvent_t g_ev_after = nullptr;
+thread_local int g_ev_kernel = -1;
 
 plx_status fail(plx_status s, const char* fmt, ...) {
   va_list ap;
@@ -95,17 +96,18 @@ size_t dec_ws(const plx::Geom& g) {
 }  // namespace
 
 namespace plx {
-void mark_main_begin(hipStream_t stream) {
-  if (g_ev_before) (void)hipEventRecord(g_ev_before, stream);
+void mark_begin(int kernel, hipStream_t stream) {
+  if (g_ev_before && kernel == g_ev_kernel) (void)hipEventRecord(g_ev_before, stream);
 }
-void mark_main_end(hipStream_t stream) {
-  if (g_ev_after) (void)hipEventRecord(g_ev_after, stream);
+void mark_end(int kernel, hipStream_t stream) {
+  if (g_ev_after && kernel == g_ev_kernel) (void)hipEventRecord(g_ev_after, stream);
 }
 }  // namespace plx
 
 extern "C" {
 
-void parallax_set_kernel_events(void* before, void* after) {
+void parallax_set_kernel_events(int kernel, void* before, void* after) {
+  g_ev_kernel = kernel;
   g_ev_before = static_cast<hipEvent_t>(before);
   g_ev_after = static_cast<hipEvent_t>(after);
 }
@@ -226,7 +228,7 @@ plx_status parallax_attn_decode(const plx_attn_desc* desc, const void* q, const 
     e = plx::launch_fast_decode(g, q, k_cache, v_cache, seqlens_k, P, out, workspace, stream);
   else
     e = plx::launch_generic_fwd(g, q, k_cache, v_cache, P, seqlens_k, out, nullptr, nullptr,
-                                nullptr, 0, 1, stream, true);
+                                nullptr, 0, 1, stream, true, PLX_KERNEL_DECODE_PASS1);
   return hip_status(e, what);
 }
 

@@ -24,7 +24,7 @@ struct Geom {
 hipError_t launch_generic_fwd(const Geom& g, const void* q, const void* k, const void* v,
                               const void* P, const int32_t* seqlens, float* out, float* lse,
                               float* kbar, float* osa, int row_begin, int row_end,
-                              hipStream_t stream, bool mark);
+                              hipStream_t stream, bool mark, int mark_id = PLX_KERNEL_FWD);
 
 // Workspace of the generic backward in bytes.
 size_t generic_bwd_workspace(const Geom& g);
@@ -56,9 +56,10 @@ hipError_t launch_fast_decode(const Geom& g, const void* q, const void* kc, cons
                               const int32_t* seqlens, const void* P, float* out, void* ws,
                               hipStream_t stream);
 
-// Records the profiling hook's `before` / `after` event on `stream` (no-op when unset).
-void mark_main_begin(hipStream_t stream);
-void mark_main_end(hipStream_t stream);
+// Records the profiling hook's `before` / `after` event on `stream` when `kernel` (a plx_kernel)
+// is the one selected (no-op otherwise).
+void mark_begin(int kernel, hipStream_t stream);
+void mark_end(int kernel, hipStream_t stream);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
