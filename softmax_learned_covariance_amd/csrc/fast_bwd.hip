@@ -113,29 +113,19 @@ __device__ __forceinline__ f16x8 lds_cols(const _Float16* t, int d, int c) {
   return *reinterpret_cast<const f16x8*>(&t[d * kKeyTile + ((c ^ (d & 7)) << 3)]);
 }
 
-// Global -> LDS copy of one key tile through registers (256 threads, 4 chunks per array each).
-__device__ __forceinline__ void row_tile_copy(const RowParams& p, RowTiles& T, int buf, int b, int g, int key0,
-                                              int tid) {
-  uint4 rk[4], rv[4], rt[4];
+// Asynchronous global -> LDS copy of one key tile: K rows, V rows and K^T, 16 wave instructions of
+// 1024 bytes per array, 4 per wave (chunk c of row r sits at slot c ^ (r & 7)).
+__device__ __forceinline__ void row_tile_dma(const RowParams& p, RowTiles& T, int buf, int b, int g, int key0, int w,
+                                             int l) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int ci = tid + 256 * j;
-    const int r = ci >> 4, c = ci & 15;
+    const int i = 4 * w + j;
+    const int r = 4 * i + (l >> 4), c = (l & 15) ^ (r & 7);
     const int64_t roff = ((static_cast<int64_t>(b) * p.Tk_pad + key0 + r) * p.Hkv + g) * kD + c * 8;
-    rk[j] = *reinterpret_cast<const uint4*>(p.k16 + roff);
-    rv[j] = *reinterpret_cast<const uint4*>(p.v16 + roff);
-    const int d = ci >> 3, c2 = ci & 7;
-    rt[j] = *reinterpret_cast<const uint4*>(
-        p.k16t + ((static_cast<int64_t>(b) * p.Hkv + g) * kD + d) * p.Tk_pad + key0 + c2 * 8);
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int ci = tid + 256 * j;
-    const int r = ci >> 4, c = ci & 15;
-    *reinterpret_cast<uint4*>(&T.k[buf][r * kD + ((c ^ (r & 7)) << 3)]) = rk[j];
-    *reinterpret_cast<uint4*>(&T.v[buf][r * kD + ((c ^ (r & 7)) << 3)]) = rv[j];
-    const int d = ci >> 3, c2 = ci & 7;
-    *reinterpret_cast<uint4*>(&T.kt[buf][d * kKeyTile + ((c2 ^ (d & 7)) << 3)]) = rt[j];
+    lds_dma16(p.k16 + roff, &T.k[buf][i * 512]);
+    lds_dma16(p.v16 + roff, &T.v[buf][i * 512]);
+    const int d = 8 * i + (l >> 3), c2 = (l & 7) ^ (d & 7);
+    lds_dma16(p.k16t + ((static_cast<int64_t>(b) * p.Hkv + g) * kD + d) * p.Tk_pad + key0 + c2 * 8, &T.kt[buf][i * 512]);
   }
 }
 
@@ -201,10 +191,12 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) accDU[mt] = f32x16{};
   const float fPG = sPG / (sG * sV);
-  if (t_beg < t_end) row_tile_copy(p, T, 0, b, g, t_beg * kKeyTile, tid);
+  if (t_beg < t_end) row_tile_dma(p, T, 0, b, g, t_beg * kKeyTile, w, l);
+  lds_dma_wait();
   __syncthreads();
   for (int kt = t_beg; kt < t_end; ++kt) {
     const int buf = (kt - t_beg) & 1;
+    if (kt + 1 < t_end) row_tile_dma(p, T, buf ^ 1, b, g, (kt + 1) * kKeyTile, w, l);
     const int key0 = kt * kKeyTile;
     if (key0 < w_kend && key0 + kKeyTile > w_kbeg) {
       const bool full = key0 + kKeyTile <= w_full_end && key0 >= w_full_beg;
@@ -237,11 +229,8 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
         }
       }
     }
+    lds_dma_wait();
     __syncthreads();
-    if (kt + 1 < t_end) {
-      row_tile_copy(p, T, buf ^ 1, b, g, (kt + 1) * kKeyTile, tid);
-      __syncthreads();
-    }
   }
 
   // ---------------- epilogue: u, alpha, P du, dkbar, Delta ----------------
@@ -412,10 +401,12 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
   f32x16 accDQ[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) accDQ[mt] = f32x16{};
-  if (t_beg < t_end) row_tile_copy(p, T, 0, b, g, t_beg * kKeyTile, tid);
+  if (t_beg < t_end) row_tile_dma(p, T, 0, b, g, t_beg * kKeyTile, w, l);
+  lds_dma_wait();
   __syncthreads();
   for (int kt = t_beg; kt < t_end; ++kt) {
     const int buf = (kt - t_beg) & 1;
+    if (kt + 1 < t_end) row_tile_dma(p, T, buf ^ 1, b, g, (kt + 1) * kKeyTile, w, l);
     const int key0 = kt * kKeyTile;
     if (key0 < w_kend && key0 + kKeyTile > w_kbeg) {
       const bool full = key0 + kKeyTile <= w_full_end && key0 >= w_full_beg;
@@ -458,11 +449,8 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
         }
       }
     }
+    lds_dma_wait();
     __syncthreads();
-    if (kt + 1 < t_end) {
-      row_tile_copy(p, T, buf ^ 1, b, g, (kt + 1) * kKeyTile, tid);
-      __syncthreads();
-    }
   }
   if (row_ok) {
     const float fq = p.scale / (sDS * sK);
@@ -514,54 +502,44 @@ __device__ __forceinline__ f16x8 kt_cols(const _Float16* t, int d, int c) {
   return *reinterpret_cast<const f16x8*>(&t[d * 32 + ((c ^ ((d >> 1) & 3)) << 3)]);
 }
 
+// Asynchronous copy of one query tile: per array, the row-major tile (32 rows x 256 B) and the
+// transposed tile (128 rows x 64 B) are 8 wave instructions of 1024 bytes each, 2 + 2 per wave.
+// Row-major chunk c of row r sits at slot c ^ (r & 7); transposed chunk c of row d at c ^ ((d >> 1) & 3).
 template <bool SPLIT>
-__device__ __forceinline__ void key_tile_copy(const KeyParams& p, KeyTiles<SPLIT>& T, int buf, int b, int h, int q0,
-                                              int tid) {
+__device__ __forceinline__ void key_tile_dma(const KeyParams& p, KeyTiles<SPLIT>& T, int buf, int b, int h, int q0,
+                                             int w, int l) {
   constexpr int NR = KeyTiles<SPLIT>::NR;
   const _Float16* srcr[6] = {p.q16, p.do16, p.u16, p.e16, p.u16lo, p.e16lo};
   const _Float16* srct[6] = {p.q16t, p.do16t, p.u16t, p.e16t, p.u16tlo, p.e16tlo};
   const int64_t bh = static_cast<int64_t>(b) * p.Hq + h;
-  // row-major: 32 rows x 16 chunks = 512 chunks per array, 2 per thread
 #pragma unroll
   for (int a = 0; a < NR; ++a) {
     const int pad = a < 4 ? p.Tq_pad : p.lo_pad;
-    uint4 v[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int ci = tid + 256 * j, r = ci >> 4, c = ci & 15;
-      v[j] = *reinterpret_cast<const uint4*>(srcr[a] + (bh * pad + q0 + r) * kD + c * 8);
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int ci = tid + 256 * j, r = ci >> 4, c = ci & 15;
-      *reinterpret_cast<uint4*>(&T.r[buf][a][r * kD + ((c ^ (r & 7)) << 3)]) = v[j];
-    }
-    // transposed: 128 rows x 4 chunks
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int ci = tid + 256 * j, d = ci >> 2, c = ci & 3;
-      v[j] = *reinterpret_cast<const uint4*>(srct[a] + (bh * kD + d) * pad + q0 + c * 8);
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int ci = tid + 256 * j, d = ci >> 2, c = ci & 3;
-      *reinterpret_cast<uint4*>(&T.t[buf][a][d * 32 + ((c ^ ((d >> 1) & 3)) << 3)]) = v[j];
+      const int i = 2 * w + j;
+      const int r = 4 * i + (l >> 4), c = (l & 15) ^ (r & 7);
+      lds_dma16(srcr[a] + (bh * pad + q0 + r) * kD + c * 8, &T.r[buf][a][i * 512]);
+      const int d = 16 * i + (l >> 2), c2 = (l & 3) ^ ((d >> 1) & 3);
+      lds_dma16(srct[a] + (bh * kD + d) * pad + q0 + c2 * 8, &T.t[buf][a][i * 512]);
     }
   }
-  if (tid < 96) {
-    const int which = tid >> 5, r = tid & 31, row = q0 + r;
-    float val = 0.f;
-    if (row < p.Tq) {
-      const int64_t so = bh * p.Tq + row;
-      if (which == 0) {
-        val = p.lse[so] * kLog2e;
-        if (!(val > -INFINITY && val < INFINITY)) val = 0.f;
-      } else {
-        val = which == 1 ? p.alpha[so] : p.delta[so];
-      }
+}
+
+// Row statistics of one query tile (lse in log2 units, alpha, Delta): thread tid < 96 fetches one value.
+__device__ __forceinline__ float key_stat_load(const KeyParams& p, int b, int h, int q0, int tid) {
+  const int which = tid >> 5, r = tid & 31, row = q0 + r;
+  float val = 0.f;
+  if (tid < 96 && row < p.Tq) {
+    const int64_t so = (static_cast<int64_t>(b) * p.Hq + h) * p.Tq + row;
+    if (which == 0) {
+      val = p.lse[so] * kLog2e;
+      if (!(val > -INFINITY && val < INFINITY)) val = 0.f;
+    } else {
+      val = which == 1 ? p.alpha[so] : p.delta[so];
     }
-    T.stat[buf][which][r] = val;
   }
+  return val;
 }
 
 template <bool SPLIT>
@@ -629,12 +607,25 @@ __global__ __launch_bounds__(256) void k_bwd_keys_fast(KeyParams p) {
   const int qt0 = i_lo / 32;
   const int total = n_qt * p.G;
   const int jw_last = min(jw + 31, p.Tk - 1);
-  if (total > 0) key_tile_copy<SPLIT>(p, T, 0, b, g * p.G, qt0 * 32, tid);
+  if (total > 0) {
+    key_tile_dma<SPLIT>(p, T, 0, b, g * p.G, qt0 * 32, w, l);
+    const float sv = key_stat_load(p, b, g * p.G, qt0 * 32, tid);
+    if (tid < 96) T.stat[0][tid >> 5][tid & 31] = sv;
+  }
+  lds_dma_wait();
   __syncthreads();
   for (int it = 0; it < total; ++it) {
     const int buf = NB == 2 ? (it & 1) : 0;
     const int qt = qt0 + it % n_qt;
     const int q0 = qt * 32;
+    // double-buffered: start the next tile's copy now
+    float next_stat = 0.f;
+    const bool pre = NB == 2 && it + 1 < total;
+    if (pre) {
+      const int nit = it + 1, nh = g * p.G + nit / n_qt, nq0 = (qt0 + nit % n_qt) * 32;
+      key_tile_dma<SPLIT>(p, T, buf ^ 1, b, nh, nq0, w, l);
+      next_stat = key_stat_load(p, b, nh, nq0, tid);
+    }
     // wave-uniform skip: no visible pair between these 32 rows and this wave's keys
     const bool any = jw < p.Tk && (!p.causal || jw <= q0 + 31 + off) &&
                      (p.window <= 0 || jw_last > q0 + off - p.window) && q0 + 31 >= p.row_lo && q0 < p.row_hi;
@@ -710,21 +701,17 @@ __global__ __launch_bounds__(256) void k_bwd_keys_fast(KeyParams p) {
         }
       }
     }
-    if (NB == 2) {
+    if (pre && tid < 96) T.stat[buf ^ 1][tid >> 5][tid & 31] = next_stat;
+    if (NB == 1 && it + 1 < total) {
+      // single buffer: wait until every wave is done with the tile, then copy the next one
       __syncthreads();
-      if (it + 1 < total) {
-        const int nit = it + 1;
-        key_tile_copy<SPLIT>(p, T, nit & 1, b, g * p.G + nit / n_qt, (qt0 + nit % n_qt) * 32, tid);
-        __syncthreads();
-      }
-    } else {
-      __syncthreads();
-      if (it + 1 < total) {
-        const int nit = it + 1;
-        key_tile_copy<SPLIT>(p, T, 0, b, g * p.G + nit / n_qt, (qt0 + nit % n_qt) * 32, tid);
-      }
-      __syncthreads();
+      const int nit = it + 1, nh = g * p.G + nit / n_qt, nq0 = (qt0 + nit % n_qt) * 32;
+      key_tile_dma<SPLIT>(p, T, 0, b, nh, nq0, w, l);
+      const float sv = key_stat_load(p, b, nh, nq0, tid);
+      if (tid < 96) T.stat[0][tid >> 5][tid & 31] = sv;
     }
+    lds_dma_wait();
+    __syncthreads();
   }
   if (key_ok) {
     const float fk = 1.f / C, fv = 1.f / (sG * cV);

@@ -97,6 +97,14 @@ __device__ __forceinline__ float sum8(f16x8 v, float acc) {
   return acc;
 }
 
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane l's bytes land at
+// lds_base + 16 * l, so one wave instruction fills 1024 contiguous LDS bytes.  lds_base must be
+// wave-uniform.  Completion is waited for with lds_dma_wait() before the barrier that publishes the data.
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // ---- staging buffers inside the caller's workspace ----
 // Slots of the max-abs array (float bits; non-negative floats order like their bits).
 enum MaxSlot { kMaxQ = 0, kMaxK = 1, kMaxV = 2, kMaxP = 3, kMaxDO = 4, kMaxU = 5, kMaxDKB = 6, kMaxDelta = 7,

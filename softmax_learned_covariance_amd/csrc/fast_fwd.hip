@@ -65,35 +65,20 @@ __device__ __forceinline__ f16x8 lds_vt(const Tiles& T, int buf, int d, int c) {
   return *reinterpret_cast<const f16x8*>(&T.vt[buf][d * kKeyTile + ((c ^ (d & 7)) << 3)]);
 }
 
-// Global -> registers for one key tile: 2 chunks of K rows, 2 of Kt, 2 of Vt per thread.
-struct TileRegs {
-  uint4 k[2], kt[2], vt[2];
-};
-
-__device__ __forceinline__ void tile_load(const FwdParams& p, int b, int g, int key0, bool with_kt,
-                                          int tid, TileRegs& R) {
+// Asynchronous global -> LDS copy of one key tile (K rows, and K^T / V^T tiles): each 16 KB array
+// is 16 wave instructions of 1024 bytes, two per wave.  The LDS position of chunk c of row r is
+// slot c ^ (r & 7), so lane l of instruction i fetches the chunk that belongs at its slot.
+__device__ __forceinline__ void tile_dma(const FwdParams& p, Tiles& T, int buf, int b, int g, int key0, bool with_kt,
+                                         int w, int l) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int ci = tid + 512 * j;
-    const int r = ci >> 4, c = ci & 15;
-    R.k[j] = *reinterpret_cast<const uint4*>(
-        p.k16 + ((static_cast<int64_t>(b) * p.Tk_pad + key0 + r) * p.Hkv + g) * kD + c * 8);
-    const int d = ci >> 3, c2 = ci & 7;
+    const int i = 2 * w + j;
+    const int r = 4 * i + (l >> 4), c = (l & 15) ^ (r & 7);
+    lds_dma16(p.k16 + ((static_cast<int64_t>(b) * p.Tk_pad + key0 + r) * p.Hkv + g) * kD + c * 8, &T.k[buf][i * 512]);
+    const int d = 8 * i + (l >> 3), c2 = (l & 7) ^ (d & 7);
     const int64_t toff = ((static_cast<int64_t>(b) * p.Hkv + g) * kD + d) * p.Tk_pad + key0 + c2 * 8;
-    if (with_kt) R.kt[j] = *reinterpret_cast<const uint4*>(p.k16t + toff);
-    R.vt[j] = *reinterpret_cast<const uint4*>(p.v16t + toff);
-  }
-}
-
-__device__ __forceinline__ void tile_store(Tiles& T, int buf, bool with_kt, int tid, const TileRegs& R) {
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int ci = tid + 512 * j;
-    const int r = ci >> 4, c = ci & 15;
-    *reinterpret_cast<uint4*>(&T.k[buf][r * kD + ((c ^ (r & 7)) << 3)]) = R.k[j];
-    const int d = ci >> 3, c2 = ci & 7;
-    if (with_kt) *reinterpret_cast<uint4*>(&T.kt[buf][d * kKeyTile + ((c2 ^ (d & 7)) << 3)]) = R.kt[j];
-    *reinterpret_cast<uint4*>(&T.vt[buf][d * kKeyTile + ((c2 ^ (d & 7)) << 3)]) = R.vt[j];
+    if (with_kt) lds_dma16(p.k16t + toff, &T.kt[buf][i * 512]);
+    lds_dma16(p.v16t + toff, &T.vt[buf][i * 512]);
   }
 }
 
@@ -184,16 +169,12 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
     accK[mt] = f32x16{};
   }
   float m_used = -INFINITY, lpart = 0.f;
-  TileRegs st;
-  if (t_beg < t_end) {
-    tile_load(p, b, g, t_beg * kKeyTile, true, tid, st);
-    tile_store(T, 0, true, tid, st);
-  }
+  if (t_beg < t_end) tile_dma(p, T, 0, b, g, t_beg * kKeyTile, true, w, l);
+  lds_dma_wait();
   __syncthreads();
   for (int kt = t_beg; kt < t_end; ++kt) {
     const int buf = (kt - t_beg) & 1;
-    const bool more = kt + 1 < t_end;
-    if (more) tile_load(p, b, g, (kt + 1) * kKeyTile, true, tid, st);
+    if (kt + 1 < t_end) tile_dma(p, T, buf ^ 1, b, g, (kt + 1) * kKeyTile, true, w, l);
     const int key0 = kt * kKeyTile;
     if (key0 < w_kend && key0 + kKeyTile > w_kbeg) {
       f32x16 S[2] = {f32x16{}, f32x16{}};
@@ -259,7 +240,7 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
           }
         }
     }
-    if (more) tile_store(T, buf ^ 1, true, tid, st);
+    lds_dma_wait();
     __syncthreads();
   }
 
@@ -374,15 +355,12 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
   for (int mt = 0; mt < 4; ++mt) accC[mt] = f32x16{};
   float rpart = 0.f;
   const float mb2 = has ? lse2 + 24.f : 0.f;  // p * 2^-24 keeps W = p (R - alpha) inside fp16
-  if (t_beg < t_end) {
-    tile_load(p, b, g, t_beg * kKeyTile, false, tid, st);
-    tile_store(T, 0, false, tid, st);
-  }
+  if (t_beg < t_end) tile_dma(p, T, 0, b, g, t_beg * kKeyTile, false, w, l);
+  lds_dma_wait();
   __syncthreads();
   for (int kt = t_beg; kt < t_end; ++kt) {
     const int buf = (kt - t_beg) & 1;
-    const bool more = kt + 1 < t_end;
-    if (more) tile_load(p, b, g, (kt + 1) * kKeyTile, false, tid, st);
+    if (kt + 1 < t_end) tile_dma(p, T, buf ^ 1, b, g, (kt + 1) * kKeyTile, false, w, l);
     const int key0 = kt * kKeyTile;
     if (key0 < w_kend && key0 + kKeyTile > w_kbeg) {
       const bool full = key0 + kKeyTile <= w_full_end && key0 >= w_full_beg;
@@ -429,7 +407,7 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
           }
       }
     }
-    if (more) tile_store(T, buf ^ 1, false, tid, st);
+    lds_dma_wait();
     __syncthreads();
   }
 
