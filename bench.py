@@ -125,6 +125,8 @@ def main():
     ap.add_argument("--split-rows", type=int, default=-1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 1 GiB device copy, the reference for HBM traffic counters")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -140,6 +142,14 @@ def main():
     import workloads as W
 
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: 1 GiB read + 1 GiB written")
+        del src, dst
     w = W.WORKLOADS[args.workload]
     log(f"workload {w}")
     q, k, v, P, dout = W.make_inputs(w, device=dev, with_dout=True)

@@ -107,25 +107,24 @@ struct __align__(16) RowTiles {
 };
 
 __device__ __forceinline__ f16x8 lds_rows(const _Float16* t, int r, int c) {
-  return *reinterpret_cast<const f16x8*>(&t[r * kD + ((c ^ (r & 7)) << 3)]);
+  return *reinterpret_cast<const f16x8*>(&t[c * (kKeyTile * 8) + r * 8]);
 }
 __device__ __forceinline__ f16x8 lds_cols(const _Float16* t, int d, int c) {
-  return *reinterpret_cast<const f16x8*>(&t[d * kKeyTile + ((c ^ (d & 7)) << 3)]);
+  return *reinterpret_cast<const f16x8*>(&t[c * (kD * 8) + d * 8]);
 }
 
-// Asynchronous global -> LDS copy of one key tile: K rows, V rows and K^T, 16 wave instructions of
-// 1024 bytes per array, 4 per wave (chunk c of row r sits at slot c ^ (r & 7)).
-__device__ __forceinline__ void row_tile_dma(const RowParams& p, RowTiles& T, int buf, int b, int g, int key0, int w,
+// Asynchronous global -> LDS copy of one key tile: K rows, V rows and K^T, each one contiguous
+// 16 KB block (16 wave instructions of 1024 bytes, 4 per wave).
+__device__ __forceinline__ void row_tile_dma(const RowParams& p, RowTiles& T, int buf, int b, int g, int kt, int w,
                                              int l) {
+  const int64_t tb = kv_tile(b, g, kt, p.Hkv, p.Tk_pad / kKeyTile);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int i = 4 * w + j;
-    const int r = 4 * i + (l >> 4), c = (l & 15) ^ (r & 7);
-    const int64_t roff = ((static_cast<int64_t>(b) * p.Tk_pad + key0 + r) * p.Hkv + g) * kD + c * 8;
-    lds_dma16(p.k16 + roff, &T.k[buf][i * 512]);
-    lds_dma16(p.v16 + roff, &T.v[buf][i * 512]);
-    const int d = 8 * i + (l >> 3), c2 = (l & 7) ^ (d & 7);
-    lds_dma16(p.k16t + ((static_cast<int64_t>(b) * p.Hkv + g) * kD + d) * p.Tk_pad + key0 + c2 * 8, &T.kt[buf][i * 512]);
+    const int64_t src = tb + i * 512 + l * 8;
+    lds_dma16(p.k16 + src, &T.k[buf][i * 512]);
+    lds_dma16(p.v16 + src, &T.v[buf][i * 512]);
+    lds_dma16(p.k16t + src, &T.kt[buf][i * 512]);
   }
 }
 
@@ -191,12 +190,12 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) accDU[mt] = f32x16{};
   const float fPG = sPG / (sG * sV);
-  if (t_beg < t_end) row_tile_dma(p, T, 0, b, g, t_beg * kKeyTile, w, l);
+  if (t_beg < t_end) row_tile_dma(p, T, 0, b, g, t_beg, w, l);
   lds_dma_wait();
   __syncthreads();
   for (int kt = t_beg; kt < t_end; ++kt) {
     const int buf = (kt - t_beg) & 1;
-    if (kt + 1 < t_end) row_tile_dma(p, T, buf ^ 1, b, g, (kt + 1) * kKeyTile, w, l);
+    if (kt + 1 < t_end) row_tile_dma(p, T, buf ^ 1, b, g, kt + 1, w, l);
     const int key0 = kt * kKeyTile;
     if (key0 < w_kend && key0 + kKeyTile > w_kbeg) {
       const bool full = key0 + kKeyTile <= w_full_end && key0 >= w_full_beg;
@@ -401,12 +400,12 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
   f32x16 accDQ[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) accDQ[mt] = f32x16{};
-  if (t_beg < t_end) row_tile_dma(p, T, 0, b, g, t_beg * kKeyTile, w, l);
+  if (t_beg < t_end) row_tile_dma(p, T, 0, b, g, t_beg, w, l);
   lds_dma_wait();
   __syncthreads();
   for (int kt = t_beg; kt < t_end; ++kt) {
     const int buf = (kt - t_beg) & 1;
-    if (kt + 1 < t_end) row_tile_dma(p, T, buf ^ 1, b, g, (kt + 1) * kKeyTile, w, l);
+    if (kt + 1 < t_end) row_tile_dma(p, T, buf ^ 1, b, g, kt + 1, w, l);
     const int key0 = kt * kKeyTile;
     if (key0 < w_kend && key0 + kKeyTile > w_kbeg) {
       const bool full = key0 + kKeyTile <= w_full_end && key0 >= w_full_beg;
@@ -484,8 +483,8 @@ struct KeyParams {
   int row_lo, row_hi, accumulate, n_kb, key_hi;
 };
 
-// One query tile in LDS.  Row-major tiles [32 rows][128 d'] (16 chunks per row, chunk ^= row & 7);
-// transposed tiles [128 d][32 rows'] (4 chunks per row, chunk ^= (d >> 1) & 3).
+// One query tile in LDS: query-row tiles [16 chunks][32 rows][8] and query-column tiles
+// [4 chunks][128 d][8] (chunk-major, as staged).
 template <bool SPLIT>
 struct __align__(16) KeyTiles {
   static constexpr int NR = SPLIT ? 6 : 4;   // q, dO, u, e (+ u lo, e lo)
@@ -496,32 +495,29 @@ struct __align__(16) KeyTiles {
 };
 
 __device__ __forceinline__ f16x8 kt_rows(const _Float16* t, int r, int c) {
-  return *reinterpret_cast<const f16x8*>(&t[r * kD + ((c ^ (r & 7)) << 3)]);
+  return *reinterpret_cast<const f16x8*>(&t[c * (kQTile * 8) + r * 8]);
 }
 __device__ __forceinline__ f16x8 kt_cols(const _Float16* t, int d, int c) {
-  return *reinterpret_cast<const f16x8*>(&t[d * 32 + ((c ^ ((d >> 1) & 3)) << 3)]);
+  return *reinterpret_cast<const f16x8*>(&t[c * (kD * 8) + d * 8]);
 }
 
-// Asynchronous copy of one query tile: per array, the row-major tile (32 rows x 256 B) and the
-// transposed tile (128 rows x 64 B) are 8 wave instructions of 1024 bytes each, 2 + 2 per wave.
-// Row-major chunk c of row r sits at slot c ^ (r & 7); transposed chunk c of row d at c ^ ((d >> 1) & 3).
+// Asynchronous copy of one query tile: per array, the query-row tile and the query-column tile are
+// contiguous 8 KB blocks (8 wave instructions of 1024 bytes each, 2 + 2 per wave).
 template <bool SPLIT>
 __device__ __forceinline__ void key_tile_dma(const KeyParams& p, KeyTiles<SPLIT>& T, int buf, int b, int h, int q0,
                                              int w, int l) {
   constexpr int NR = KeyTiles<SPLIT>::NR;
   const _Float16* srcr[6] = {p.q16, p.do16, p.u16, p.e16, p.u16lo, p.e16lo};
   const _Float16* srct[6] = {p.q16t, p.do16t, p.u16t, p.e16t, p.u16tlo, p.e16tlo};
-  const int64_t bh = static_cast<int64_t>(b) * p.Hq + h;
 #pragma unroll
   for (int a = 0; a < NR; ++a) {
     const int pad = a < 4 ? p.Tq_pad : p.lo_pad;
+    const int64_t tb = q_tile(b, h, q0 / kQTile, p.Hq, pad / kQTile);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int i = 2 * w + j;
-      const int r = 4 * i + (l >> 4), c = (l & 15) ^ (r & 7);
-      lds_dma16(srcr[a] + (bh * pad + q0 + r) * kD + c * 8, &T.r[buf][a][i * 512]);
-      const int d = 16 * i + (l >> 2), c2 = (l & 3) ^ ((d >> 1) & 3);
-      lds_dma16(srct[a] + (bh * kD + d) * pad + q0 + c2 * 8, &T.t[buf][a][i * 512]);
+      lds_dma16(srcr[a] + tb + i * 512 + l * 8, &T.r[buf][a][i * 512]);
+      lds_dma16(srct[a] + tb + i * 512 + l * 8, &T.t[buf][a][i * 512]);
     }
   }
 }
@@ -586,11 +582,12 @@ __global__ __launch_bounds__(256) void k_bwd_keys_fast(KeyParams p) {
   f16x8 kB[8], vB[8];
   {
     const int kr = key_ok ? key : 0;
-    const int64_t roff = ((static_cast<int64_t>(b) * p.Tk_pad + kr) * p.Hkv + g) * kD + hh * 8;
+    const int64_t roff = kv_tile(b, g, kr / kKeyTile, p.Hkv, p.Tk_pad / kKeyTile) + (kr % kKeyTile) * 8 +
+                         hh * (kKeyTile * 8);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      kB[s] = *reinterpret_cast<const f16x8*>(p.k16 + roff + 16 * s);
-      vB[s] = *reinterpret_cast<const f16x8*>(p.v16 + roff + 16 * s);
+      kB[s] = *reinterpret_cast<const f16x8*>(p.k16 + roff + s * (2 * kKeyTile * 8));
+      vB[s] = *reinterpret_cast<const f16x8*>(p.v16 + roff + s * (2 * kKeyTile * 8));
     }
   }
   f32x16 accK[4], accV[4];
@@ -607,6 +604,8 @@ __global__ __launch_bounds__(256) void k_bwd_keys_fast(KeyParams p) {
   const int qt0 = i_lo / 32;
   const int total = n_qt * p.G;
   const int jw_last = min(jw + 31, p.Tk - 1);
+  const int row_lo_c = p.row_lo, row_hi_c = min(p.row_hi, p.Tq);
+  const bool nocausal = !p.causal, nowindow = p.window <= 0;
   if (total > 0) {
     key_tile_dma<SPLIT>(p, T, 0, b, g * p.G, qt0 * 32, w, l);
     const float sv = key_stat_load(p, b, g * p.G, qt0 * 32, tid);
@@ -645,41 +644,44 @@ __global__ __launch_bounds__(256) void k_bwd_keys_fast(KeyParams p) {
           E = mfma(kt_rows(T.r[buf][5], ql, 2 * s + hh), kB[s], E);
         }
       }
-      float wv[16], wk[16], wp[16], wd[16];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int rr = 8 * j + 4 * hh;  // first of 4 consecutive rows held in registers 4j..4j+3
-        const float4 L2 = *reinterpret_cast<const float4*>(&T.stat[buf][0][rr]);
-        const float4 AL = *reinterpret_cast<const float4*>(&T.stat[buf][1][rr]);
-        const float4 DL = *reinterpret_cast<const float4*>(&T.stat[buf][2][rr]);
-        const float l2[4] = {L2.x, L2.y, L2.z, L2.w}, al[4] = {AL.x, AL.y, AL.z, AL.w};
-        const float dl[4] = {DL.x, DL.y, DL.z, DL.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * j + e, i = q0 + rr + e;
-          float sv = S[r];
-          if (!full) {
-            const bool vis = key_ok && i >= p.row_lo && i < p.row_hi && i < p.Tq && (!p.causal || key <= i + off) &&
-                             (p.window <= 0 || key > i + off - p.window);
-            if (!vis) sv = -INFINITY;
-          }
-          const float pr = __builtin_amdgcn_exp2f(fmaf(sv, cS, -l2[e]));
-          const float tt = fmaf(Tt[r], fT, 1.f - al[e]);
-          const float gt = Gt[r] * fG;
-          const float dp = fmaf(gt, tt, E[r] * fE);
-          wv[r] = pr * tt * cV;
-          wk[r] = pr * gt * c1;
-          wp[r] = pr * c2;
-          wd[r] = pr * (dp - dl[e]) * c3;
-        }
-      }
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
+        // queries 16t..16t+15 of the tile: registers 8t..8t+7 (rows 8j + 4hh + e, j = 2t, 2t+1)
+        float wv[8], wk[8], wp[8], wd[8];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int j = 2 * t + jj;
+          const int rr = 8 * j + 4 * hh;
+          const float4 L2 = *reinterpret_cast<const float4*>(&T.stat[buf][0][rr]);
+          const float4 AL = *reinterpret_cast<const float4*>(&T.stat[buf][1][rr]);
+          const float4 DL = *reinterpret_cast<const float4*>(&T.stat[buf][2][rr]);
+          const float l2[4] = {L2.x, L2.y, L2.z, L2.w}, al[4] = {AL.x, AL.y, AL.z, AL.w};
+          const float dl[4] = {DL.x, DL.y, DL.z, DL.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * j + e, o = 4 * jj + e, i = q0 + rr + e;
+            float sv = S[r];
+            if (!full) {
+              // branch-free visibility test (bitwise, no short-circuit)
+              const bool vis = key_ok & (i >= row_lo_c) & (i < row_hi_c) & ((key <= i + off) | nocausal) &
+                               ((key > i + off - p.window) | nowindow);
+              sv = vis ? sv : -INFINITY;
+            }
+            const float pr = __builtin_amdgcn_exp2f(fmaf(sv, cS, -l2[e]));
+            const float tt = fmaf(Tt[r], fT, 1.f - al[e]);
+            const float gt = Gt[r] * fG;
+            const float dp = fmaf(gt, tt, E[r] * fE);
+            wv[o] = pr * tt * cV;
+            wk[o] = pr * gt * c1;
+            wp[o] = pr * c2;
+            wd[o] = pr * (dp - dl[e]) * c3;
+          }
+        }
         f16x8 vh, vl, kh, kl, ph, pl, dh, dlo;
-        to_operand(wv + 8 * t, 1.f, vh, SPLIT ? &vl : nullptr);
-        to_operand(wk + 8 * t, 1.f, kh, SPLIT ? &kl : nullptr);
-        to_operand(wp + 8 * t, 1.f, ph, SPLIT ? &pl : nullptr);
-        to_operand(wd + 8 * t, 1.f, dh, SPLIT ? &dlo : nullptr);
+        to_operand(wv, 1.f, vh, SPLIT ? &vl : nullptr);
+        to_operand(wk, 1.f, kh, SPLIT ? &kl : nullptr);
+        to_operand(wp, 1.f, ph, SPLIT ? &pl : nullptr);
+        to_operand(wd, 1.f, dh, SPLIT ? &dlo : nullptr);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           const int d = 32 * mt + ql, c = 2 * t + hh;

@@ -2,13 +2,20 @@
 // types, the fp16 staging layout, power-of-two range scales and wave helpers.
 //
 // Staging.  The MFMA kernels compute with fp16 operands (11 significant bits)
-// and fp32 accumulation.  K, V and P are converted once per call by the prep
-// kernels into fp16 copies laid out for the v_mfma_f32_32x32x16_f16 operand
-// registers, so every LDS read in the hot loops is one 16-byte access:
-//   K16   [B][Tk_pad][Hkv][128]  key rows, d permuted within groups of 16
-//   K16t  [B][Hkv][128][Tk_pad]  transposed, keys permuted within groups of 16
-//   V16t  [B][Hkv][128][Tk_pad]  transposed, keys permuted within groups of 16
+// and fp32 accumulation.  K, V, P (and, for the backward, q, dout, u, dkbar)
+// are converted once per call into fp16 copies laid out tile by tile for the
+// v_mfma_f32_32x32x16_f16 operand registers.  A tile is one contiguous block
+// stored "chunk-major": its 16-byte chunks (8 fp16 values) are grouped by
+// chunk index, so
+//   key rows    [16 chunks][64 keys][8]   (K16, V16: d permuted within groups of 16)
+//   key columns [8 chunks][128 d][8]      (K16t, V16t: keys permuted within groups of 16)
+//   query rows  [16 chunks][32 rows][8]   and query columns [4 chunks][128 d][8]
+// with tiles ordered [batch][head][tile].  Copying a tile to LDS is then one
+// contiguous DMA, and an MFMA operand read (32 lanes reading the same chunk of
+// 32 consecutive rows) is a contiguous 512-byte LDS access: no bank conflicts,
+// and the chunk index becomes an immediate offset.
 //   P16t  [Hq][128][128]         P16t[h][a][b'] = P[h][b][a], b permuted within groups of 16
+//   P16   [Hq][128][128]         P16[h][b][a'] = P[h][b][a], a permuted within groups of 16
 // The permutation of a group of 16 is the involution
 //   position 8*hh + e  <->  element 8*(e/4) + 4*hh + (e%4)      (hh in {0,1}, e in 0..7)
 // which is exactly the order in which a 32x32 accumulator tile holds its rows
@@ -35,6 +42,16 @@ typedef uint16_t u16;
 
 constexpr int kD = 128;        // head_dim of the fast path
 constexpr int kKeyTile = 64;   // keys per LDS tile
+constexpr int kQTile = 32;     // query rows per tile of the key-major backward
+
+// First element of key tile kt of (batch b, kv head g) in K16 / V16 / K16t / V16t.
+__host__ __device__ inline int64_t kv_tile(int b, int g, int kt, int Hkv, int ntiles) {
+  return ((static_cast<int64_t>(b) * Hkv + g) * ntiles + kt) * (kKeyTile * kD);
+}
+// First element of query tile qt of (batch b, query head h) in the query-side copies.
+__host__ __device__ inline int64_t q_tile(int b, int h, int qt, int Hq, int nqt) {
+  return ((static_cast<int64_t>(b) * Hq + h) * nqt + qt) * (kQTile * kD);
+}
 
 // permuted position <-> element within a group of 16 (an involution)
 __host__ __device__ constexpr int perm16(int p) { return 8 * ((p & 7) >> 2) + 4 * (p >> 3) + (p & 3); }

@@ -23,7 +23,8 @@
 // layouts in fast_common.h).  Lazy rescaling: the running maximum only moves
 // when a tile's maximum exceeds it by 8 (log2 units), so the accumulators are
 // rarely rescaled; exp2 arguments are then <= 8 and p~ <= 256 still fits fp16.
-// Key tiles are double-buffered in LDS with XOR-swizzled 16-byte chunks.
+// Key tiles (chunk-major, see fast_common.h) are double-buffered in LDS and
+// copied by direct-to-LDS DMA while the previous tile is being computed.
 // Blocks are mapped so that all blocks of one (batch, kv head) run on the same
 // XCD (their K/V stay in that XCD's L2), longest (most keys) first.
 #include <math.h>
@@ -50,35 +51,33 @@ struct FwdParams {
 };
 
 struct __align__(16) Tiles {
-  _Float16 k[2][kKeyTile * kD];    // [key][d'] 16 chunks per row, chunk ^= key & 7
-  _Float16 kt[2][kD * kKeyTile];   // [d][key'] 8 chunks per row, chunk ^= d & 7
+  _Float16 k[2][kKeyTile * kD];    // key rows tile    [16 chunks][64 keys][8]
+  _Float16 kt[2][kD * kKeyTile];   // key columns tile [8 chunks][128 d][8]
   _Float16 vt[2][kD * kKeyTile];
 };
 
 __device__ __forceinline__ f16x8 lds_k(const Tiles& T, int buf, int r, int c) {
-  return *reinterpret_cast<const f16x8*>(&T.k[buf][r * kD + ((c ^ (r & 7)) << 3)]);
+  return *reinterpret_cast<const f16x8*>(&T.k[buf][c * (kKeyTile * 8) + r * 8]);
 }
 __device__ __forceinline__ f16x8 lds_kt(const Tiles& T, int buf, int d, int c) {
-  return *reinterpret_cast<const f16x8*>(&T.kt[buf][d * kKeyTile + ((c ^ (d & 7)) << 3)]);
+  return *reinterpret_cast<const f16x8*>(&T.kt[buf][c * (kD * 8) + d * 8]);
 }
 __device__ __forceinline__ f16x8 lds_vt(const Tiles& T, int buf, int d, int c) {
-  return *reinterpret_cast<const f16x8*>(&T.vt[buf][d * kKeyTile + ((c ^ (d & 7)) << 3)]);
+  return *reinterpret_cast<const f16x8*>(&T.vt[buf][c * (kD * 8) + d * 8]);
 }
 
-// Asynchronous global -> LDS copy of one key tile (K rows, and K^T / V^T tiles): each 16 KB array
-// is 16 wave instructions of 1024 bytes, two per wave.  The LDS position of chunk c of row r is
-// slot c ^ (r & 7), so lane l of instruction i fetches the chunk that belongs at its slot.
-__device__ __forceinline__ void tile_dma(const FwdParams& p, Tiles& T, int buf, int b, int g, int key0, bool with_kt,
+// Asynchronous global -> LDS copy of one key tile (each array is one contiguous 16 KB block:
+// 16 wave instructions of 1024 bytes, two per wave).
+__device__ __forceinline__ void tile_dma(const FwdParams& p, Tiles& T, int buf, int b, int g, int kt, bool with_kt,
                                          int w, int l) {
+  const int64_t tb = kv_tile(b, g, kt, p.Hkv, p.Tk_pad / kKeyTile);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int i = 2 * w + j;
-    const int r = 4 * i + (l >> 4), c = (l & 15) ^ (r & 7);
-    lds_dma16(p.k16 + ((static_cast<int64_t>(b) * p.Tk_pad + key0 + r) * p.Hkv + g) * kD + c * 8, &T.k[buf][i * 512]);
-    const int d = 8 * i + (l >> 3), c2 = (l & 7) ^ (d & 7);
-    const int64_t toff = ((static_cast<int64_t>(b) * p.Hkv + g) * kD + d) * p.Tk_pad + key0 + c2 * 8;
-    if (with_kt) lds_dma16(p.k16t + toff, &T.kt[buf][i * 512]);
-    lds_dma16(p.v16t + toff, &T.vt[buf][i * 512]);
+    const int64_t src = tb + i * 512 + l * 8;
+    lds_dma16(p.k16 + src, &T.k[buf][i * 512]);
+    if (with_kt) lds_dma16(p.k16t + src, &T.kt[buf][i * 512]);
+    lds_dma16(p.v16t + src, &T.vt[buf][i * 512]);
   }
 }
 
@@ -169,12 +168,12 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
     accK[mt] = f32x16{};
   }
   float m_used = -INFINITY, lpart = 0.f;
-  if (t_beg < t_end) tile_dma(p, T, 0, b, g, t_beg * kKeyTile, true, w, l);
+  if (t_beg < t_end) tile_dma(p, T, 0, b, g, t_beg, true, w, l);
   lds_dma_wait();
   __syncthreads();
   for (int kt = t_beg; kt < t_end; ++kt) {
     const int buf = (kt - t_beg) & 1;
-    if (kt + 1 < t_end) tile_dma(p, T, buf ^ 1, b, g, (kt + 1) * kKeyTile, true, w, l);
+    if (kt + 1 < t_end) tile_dma(p, T, buf ^ 1, b, g, kt + 1, true, w, l);
     const int key0 = kt * kKeyTile;
     if (key0 < w_kend && key0 + kKeyTile > w_kbeg) {
       f32x16 S[2] = {f32x16{}, f32x16{}};
@@ -355,12 +354,12 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
   for (int mt = 0; mt < 4; ++mt) accC[mt] = f32x16{};
   float rpart = 0.f;
   const float mb2 = has ? lse2 + 24.f : 0.f;  // p * 2^-24 keeps W = p (R - alpha) inside fp16
-  if (t_beg < t_end) tile_dma(p, T, 0, b, g, t_beg * kKeyTile, false, w, l);
+  if (t_beg < t_end) tile_dma(p, T, 0, b, g, t_beg, false, w, l);
   lds_dma_wait();
   __syncthreads();
   for (int kt = t_beg; kt < t_end; ++kt) {
     const int buf = (kt - t_beg) & 1;
-    if (kt + 1 < t_end) tile_dma(p, T, buf ^ 1, b, g, (kt + 1) * kKeyTile, false, w, l);
+    if (kt + 1 < t_end) tile_dma(p, T, buf ^ 1, b, g, kt + 1, false, w, l);
     const int key0 = kt * kKeyTile;
     if (key0 < w_kend && key0 + kKeyTile > w_kbeg) {
       const bool full = key0 + kKeyTile <= w_full_end && key0 >= w_full_beg;

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void k_absmax(const u16* q, int64_t nq, const 
   }
 }
 
-// One block per (64-key tile, kv head, batch): K16 rows, K16t and V16t columns.
+// One block per (64-key tile, kv head, batch): K16 (and V16) row tiles, K16t (and V16t) column tiles.
 __global__ __launch_bounds__(256) void k_stage_kv(const u16* k, const u16* v, const uint32_t* maxbits,
                                                   _Float16* k16, _Float16* k16t, _Float16* v16t,
                                                   _Float16* v16, int Tk, int Tk_pad, int Hkv) {
@@ -79,15 +79,16 @@ __global__ __launch_bounds__(256) void k_stage_kv(const u16* k, const u16* v, co
     f16x8 o;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = ks[r * LD + 16 * (c >> 1) + perm16(8 * (c & 1) + e)];
-    *reinterpret_cast<f16x8*>(k16 + ((static_cast<int64_t>(b) * Tk_pad + key0 + r) * Hkv + g) * kD + c * 8) = o;
+    const int64_t tb = kv_tile(b, g, kt, Hkv, Tk_pad / kKeyTile);
+    *reinterpret_cast<f16x8*>(k16 + tb + c * (kKeyTile * 8) + r * 8) = o;
     if (v16) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = vs[r * LD + 16 * (c >> 1) + perm16(8 * (c & 1) + e)];
-      *reinterpret_cast<f16x8*>(v16 + ((static_cast<int64_t>(b) * Tk_pad + key0 + r) * Hkv + g) * kD + c * 8) = o;
+      *reinterpret_cast<f16x8*>(v16 + tb + c * (kKeyTile * 8) + r * 8) = o;
     }
   }
   // K16t, V16t: d rows, keys permuted within groups of 16
-  const int64_t trow = (static_cast<int64_t>(b) * Hkv + g) * kD;
+  const int64_t tb = kv_tile(b, g, kt, Hkv, Tk_pad / kKeyTile);
   for (int ci = t; ci < kD * 8; ci += 256) {
     const int d = ci >> 3, c = ci & 7;
     f16x8 ok, ov;
@@ -97,7 +98,7 @@ __global__ __launch_bounds__(256) void k_stage_kv(const u16* k, const u16* v, co
       ok[e] = ks[key * LD + d];
       ov[e] = vs[key * LD + d];
     }
-    const int64_t off = (trow + d) * Tk_pad + key0 + c * 8;
+    const int64_t off = tb + c * (kD * 8) + d * 8;
     *reinterpret_cast<f16x8*>(k16t + off) = ok;
     if (v16t) *reinterpret_cast<f16x8*>(v16t + off) = ov;
   }
@@ -128,10 +129,10 @@ __global__ __launch_bounds__(256) void k_stage_p(const u16* P, const uint32_t* m
 }
 
 // Query-side tensors for the key-major backward kernel.  One block per (32-row tile, head, batch):
-// src [B][Tq][Hq][128] (bf16 or fp32) -> dst [B][Hq][Tq_pad][128'] (rows, d permuted) and
-// dstt [B][Hq][128][Tq_pad'] (transposed, rows permuted within groups of 16), scaled by
-// range_scale(max) with max = maxbits[max_idx].  With lo / lot, also the fp16 residuals
-// x*s - hi for rows < lo_rows (lo [B][Hq][lo_pad][128'], lot [B][Hq][128][lo_pad']).
+// src [B][Tq][Hq][128] (bf16 or fp32) -> dst query-row tiles (d permuted) and dstt query-column
+// tiles (rows permuted within groups of 16), scaled by range_scale(max) with max =
+// maxbits[max_idx].  With lo / lot, also the fp16 residuals x*s - hi for rows < lo_rows (tiles of
+// a [B][Hq][lo_pad] index space).
 template <bool F32>
 __global__ __launch_bounds__(256) void k_stage_rows(const void* src, const uint32_t* maxbits, int max_idx,
                                                     _Float16* dst, _Float16* dstt, _Float16* lo,
@@ -157,7 +158,8 @@ __global__ __launch_bounds__(256) void k_stage_rows(const void* src, const uint3
     if (want_lo) ls[r * LD + d] = static_cast<_Float16>(x - static_cast<float>(hi));
   }
   __syncthreads();
-  const int64_t bh = static_cast<int64_t>(b) * Hq + h;
+  const int64_t tb = q_tile(b, h, qt, Hq, Tq_pad / kQTile);
+  const int64_t tbl = want_lo ? q_tile(b, h, qt, Hq, lo_pad / kQTile) : 0;
   for (int ci = t; ci < 32 * 16; ci += 256) {
     const int r = ci >> 4, c = ci & 15;
     f16x8 o, ol;
@@ -167,8 +169,8 @@ __global__ __launch_bounds__(256) void k_stage_rows(const void* src, const uint3
       o[e] = hs[r * LD + d];
       ol[e] = ls[r * LD + d];
     }
-    *reinterpret_cast<f16x8*>(dst + (bh * Tq_pad + r0 + r) * kD + c * 8) = o;
-    if (want_lo) *reinterpret_cast<f16x8*>(lo + (bh * lo_pad + r0 + r) * kD + c * 8) = ol;
+    *reinterpret_cast<f16x8*>(dst + tb + c * (kQTile * 8) + r * 8) = o;
+    if (want_lo) *reinterpret_cast<f16x8*>(lo + tbl + c * (kQTile * 8) + r * 8) = ol;
   }
   for (int ci = t; ci < kD * 4; ci += 256) {
     const int d = ci >> 2, c = ci & 3;
@@ -179,8 +181,8 @@ __global__ __launch_bounds__(256) void k_stage_rows(const void* src, const uint3
       o[e] = hs[r * LD + d];
       ol[e] = ls[r * LD + d];
     }
-    *reinterpret_cast<f16x8*>(dstt + (bh * kD + d) * Tq_pad + r0 + c * 8) = o;
-    if (want_lo) *reinterpret_cast<f16x8*>(lot + (bh * kD + d) * lo_pad + r0 + c * 8) = ol;
+    *reinterpret_cast<f16x8*>(dstt + tb + c * (kD * 8) + d * 8) = o;
+    if (want_lo) *reinterpret_cast<f16x8*>(lot + tbl + c * (kD * 8) + d * 8) = ol;
   }
 }
 
