@@ -13,6 +13,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [
 """
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -65,6 +66,35 @@ def bwd_keys_flops(w, row_begin=0):
     """Key-major backward kernel: S, T, E, G (8d), dv (2d) and dk (6d) per visible pair."""
     pairs, _ = visible_pairs_rows(w, row_begin)
     return 16 * w.head_dim * pairs
+
+
+# Source files of each timed kernel: a stored traffic figure is used only while they are unchanged.
+KERNEL_SOURCES = {"fwd": ["fast_fwd.hip", "fast_common.h"], "bwd_rows": ["fast_bwd.hip", "fast_common.h"],
+                  "bwd_keys": ["fast_bwd.hip", "fast_common.h"], "decode_pass1": ["fast_decode.hip", "fast_common.h"],
+                  "decode_pass2": ["fast_decode.hip", "fast_common.h"]}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_layer17_decode.txt")
+
+
+def source_hash(name):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[name]:
+        with open(os.path.join(ROOT, "softmax_learned_covariance_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name):
+    """HBM bytes per launch of kernel `name` from the committed FETCH_SIZE/WRITE_SIZE summary
+    (copy-calibrated), or None when the summary is missing or the kernel's sources changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                f = line.split()
+                if len(f) == 6 and f[0] == name:
+                    return float(f[4]) if f[5] == source_hash(name) else None
+    except OSError:
+        pass
+    return None
 
 
 class HipEvents:
@@ -208,8 +238,10 @@ def main():
     value = step_flops / (ms_step * 1e-3) / 1e12
     dom = max(kern, key=lambda n: kern[n]["avg_ms"])
     dk = kern[dom]
+    tr = measured_traffic(dom)
     roofline = {"bound": "mfma", "achieved": dk["tflops"], "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(dk["tflops"] / PEAK_F16_TFLOPS, 4), "traffic": None,
+                "frac": round(dk["tflops"] / PEAK_F16_TFLOPS, 4), "traffic": None if tr is None else round(tr),
+                "traffic_unit": "bytes per launch (HBM, FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
                 "kernel": dom, "avg_ms": dk["avg_ms"], "algorithmic_flop_per_launch": dk["algorithmic_flop"]}
     result = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
@@ -247,6 +279,8 @@ def main():
         p1 = [ev.elapsed_ms(a, b) for a, b in dev_ev[0::2]]
         p2 = [ev.elapsed_ms(a, b) for a, b in dev_ev[1::2]]
         kms1, kms2 = sum(p1) / len(p1), sum(p2) / len(p2)
+        t1, t2 = measured_traffic("decode_pass1"), measured_traffic("decode_pass2")
+        dec_traffic = None if t1 is None or t2 is None else round(t1 + t2)
         cache_bytes = 2 * wd.batch * wd.seqlen_k * wd.heads_kv * wd.head_dim * 2
         other = (wd.batch * wd.heads_q * wd.head_dim) * (2 + 4) + wd.heads_q * wd.head_dim ** 2 * 2
         alg = cache_bytes + other
@@ -258,7 +292,7 @@ def main():
             "kernels": {"pass1": {"avg_ms": round(kms1, 4), "gbs": round(cache_bytes / (kms1 * 1e-3) / 1e9, 1)},
                         "pass2": {"avg_ms": round(kms2, 4), "gbs": round(cache_bytes / (kms2 * 1e-3) / 1e9, 1)}},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": dec_traffic,
                          "algorithmic_bytes_per_call": alg,
                          "note": "algorithmic bytes = one read of the K/V cache; the two-pass method reads it twice"}}
         kms = dt * 1e3
