@@ -56,10 +56,16 @@ def bwd_flops(w, row_begin=0):
 
 
 def bwd_rows_flops(w, row_begin=0):
-    """Algorithmic share of the query-major backward kernel: du (S, G, (pG)K: 6d per pair),
-    dq (ds K: 2d per pair) and P du (2d^2 per row); its recomputation of S, T, E, G for dq is not counted."""
+    """Algorithmic share of the query-major backward kernel: du (S, G, (pG)K: 6d per pair) and
+    P du (2d^2 per row); its recomputation of u = P^T (q - kbar) is not counted."""
     pairs, rows = visible_pairs_rows(w, row_begin)
-    return 8 * w.head_dim * pairs + 2 * w.head_dim ** 2 * rows
+    return 6 * w.head_dim * pairs + 2 * w.head_dim ** 2 * rows
+
+
+def bwd_dq_flops(w, row_begin=0):
+    """dq kernel: scale * ds K (2d per pair) from the stored ds."""
+    pairs, _ = visible_pairs_rows(w, row_begin)
+    return 2 * w.head_dim * pairs
 
 
 def bwd_keys_flops(w, row_begin=0):
@@ -70,7 +76,8 @@ def bwd_keys_flops(w, row_begin=0):
 
 # Source files of each timed kernel: a stored traffic figure is used only while they are unchanged.
 KERNEL_SOURCES = {"fwd": ["fast_fwd.hip", "fast_common.h"], "bwd_rows": ["fast_bwd.hip", "fast_common.h"],
-                  "bwd_keys": ["fast_bwd.hip", "fast_common.h"], "decode_pass1": ["fast_decode.hip", "fast_common.h"],
+                  "bwd_keys": ["fast_bwd.hip", "fast_common.h"], "bwd_dq": ["fast_bwd.hip", "fast_common.h"],
+                  "decode_pass1": ["fast_decode.hip", "fast_common.h"],
                   "decode_pass2": ["fast_decode.hip", "fast_common.h"]}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_layer17_decode.txt")
 
@@ -198,9 +205,11 @@ def main():
         log(f"warmup step {i + 1}/{args.warmup} done")
 
     # Timed region: K steps.  The kernel-event hook brackets one kernel per library call: every
-    # step times the forward kernel, and the backward alternates between its two big kernels.
+    # step times the forward kernel, and the backward cycles through its three main kernels.
     K = args.steps
-    evs = {n: [] for n in ("fwd", "bwd_rows", "bwd_keys")}
+    bwd_cycle = (("bwd_rows", plx.PLX_KERNEL_BWD_ROWS), ("bwd_keys", plx.PLX_KERNEL_BWD_KEYS),
+                 ("bwd_dq", plx.PLX_KERNEL_BWD_DQ))
+    evs = {n: [] for n in ("fwd", "bwd_rows", "bwd_keys", "bwd_dq")}
     pool = [(ev.create(), ev.create()) for _ in range(2 * K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -208,9 +217,9 @@ def main():
         e_f = pool[2 * i]
         lib.parallax_set_kernel_events(plx.PLX_KERNEL_FWD, *e_f)
         out, lse, kbar, o = plx.parallax_attn_fwd(q, k, v, P, split_rows=split)
-        which = "bwd_rows" if i % 2 == 0 else "bwd_keys"
+        which, kid = bwd_cycle[i % 3]
         e_b = pool[2 * i + 1]
-        lib.parallax_set_kernel_events(plx.PLX_KERNEL_BWD_ROWS if i % 2 == 0 else plx.PLX_KERNEL_BWD_KEYS, *e_b)
+        lib.parallax_set_kernel_events(kid, *e_b)
         plx.parallax_attn_bwd(q, k, v, P, out, dout, lse, kbar, o, split_rows=split)
         evs["fwd"].append(e_f)
         evs[which].append(e_b)
@@ -224,7 +233,8 @@ def main():
     r0 = (256 if split < 0 else split) if fast else 0
     r0 = min(r0, w.seqlen_q)
     kern = {}
-    for n, flops_fn in (("fwd", fwd_flops), ("bwd_rows", bwd_rows_flops), ("bwd_keys", bwd_keys_flops)):
+    for n, flops_fn in (("fwd", fwd_flops), ("bwd_rows", bwd_rows_flops), ("bwd_keys", bwd_keys_flops),
+                        ("bwd_dq", bwd_dq_flops)):
         if not evs[n]:
             continue
         ms = sorted(ev.elapsed_ms(a, b) for a, b in evs[n])

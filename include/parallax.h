@@ -76,10 +76,11 @@ typedef struct {
 /* Kernels the profiling hook can bracket. */
 typedef enum {
   PLX_KERNEL_FWD = 0,          /* forward: the fused two-pass MFMA kernel (generic kernel on the fp32 path) */
-  PLX_KERNEL_BWD_ROWS = 1,     /* backward: query-major kernel (du, dkbar, Delta, dq) */
-  PLX_KERNEL_BWD_KEYS = 2,     /* backward: key-major kernel (dk, dv); the generic key kernel on the fp32 path */
+  PLX_KERNEL_BWD_ROWS = 1,     /* backward: query-major kernel (du, dkbar, Delta, P du) */
+  PLX_KERNEL_BWD_KEYS = 2,     /* backward: key-major kernel (dk, dv, ds); the generic key kernel on the fp32 path */
   PLX_KERNEL_DECODE_PASS1 = 3, /* decode: first split-KV pass (generic kernel on the fp32 path) */
-  PLX_KERNEL_DECODE_PASS2 = 4  /* decode: second split-KV pass */
+  PLX_KERNEL_DECODE_PASS2 = 4, /* decode: second split-KV pass */
+  PLX_KERNEL_BWD_DQ = 5        /* backward: dq = P du + scale ds K from the stored ds (bf16 fast path) */
 } plx_kernel;
 
 /*

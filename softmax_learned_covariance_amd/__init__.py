@@ -28,7 +28,8 @@ LIB_PATH = os.path.join(_PKG, "libparallax.so")
 
 PLX_OK, PLX_ERR_INVALID, PLX_ERR_UNSUPPORTED, PLX_ERR_WORKSPACE, PLX_ERR_HIP = range(5)
 PLX_F32, PLX_BF16 = 0, 1
-PLX_KERNEL_FWD, PLX_KERNEL_BWD_ROWS, PLX_KERNEL_BWD_KEYS, PLX_KERNEL_DECODE_PASS1, PLX_KERNEL_DECODE_PASS2 = range(5)
+(PLX_KERNEL_FWD, PLX_KERNEL_BWD_ROWS, PLX_KERNEL_BWD_KEYS, PLX_KERNEL_DECODE_PASS1, PLX_KERNEL_DECODE_PASS2,
+ PLX_KERNEL_BWD_DQ) = range(6)
 
 
 class PlxAttnDesc(ctypes.Structure):

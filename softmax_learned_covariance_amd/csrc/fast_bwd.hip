@@ -128,7 +128,7 @@ __device__ __forceinline__ void row_tile_dma(const RowParams& p, RowTiles& T, in
   }
 }
 
-template <bool SPLIT>
+template <bool SPLIT, bool DQ_PASS>
 __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
   __shared__ RowTiles T;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, ql = l & 31, hh = l >> 5;
@@ -384,6 +384,8 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
     }
   }
 
+  if constexpr (!DQ_PASS) return;   // dq is completed by k_bwd_dq from the stored ds
+
   // ---------------- pass 2: dq ----------------
   const float sU = range_scale(umax), sE = range_scale(emax);
   f16x8 uB[8], uL[SPLIT ? 8 : 1], eB[8], eL[SPLIT ? 8 : 1];
@@ -478,6 +480,7 @@ struct KeyParams {
   const float *lse, *alpha, *delta;
   const uint32_t* maxbits;
   float *dk, *dv;
+  _Float16* ds;        // k_bwd_keys_duo<true>: ds tiles for the dq kernel
   int B, Tq, Tk, Tk_pad, Tq_pad, lo_pad, Hq, Hkv, G, causal, window;
   float scale;
   int row_lo, row_hi, accumulate, n_kb, key_hi;
@@ -739,6 +742,423 @@ __global__ __launch_bounds__(256) void k_bwd_keys_fast(KeyParams p) {
 }
 
 // ------------------------------------------------------------------------------------------
+// key-major kernel with role-split waves (rows >= split) and the dq kernel
+// ------------------------------------------------------------------------------------------
+//
+// 8 waves (2 per SIMD) own 128 keys: wave w has keys jb + 32 (w & 3) + [0, 32).  For each query
+// tile, waves 0-3 compute S and T for their keys, the weights p and tt = T + 1 - alpha, and
+// accumulate dv = (p tt)^T g and the p^T dkbar part of dk.  Through LDS they hand p (fp16, times
+// 2^14) and p tt (fp32) to waves 4-7, which compute G and E, form p G and
+// ds = p (G tt + E - Delta) = G (p tt) + p (E - Delta), and accumulate (p G)^T u + scale ds^T q.
+// Each half issues 32 of the tile's 64 MFMAs, so the two waves sharing a SIMD keep its matrix
+// unit busy while the other one is in its exp / scaling code.
+//
+// With DS_OUT, waves 4-7 also store the tile of ds (as the fp16 operand C scale ds / sQ) in
+// query-major order for the dq kernel.  The transpose costs two MFMAs: the ds operand (keys on
+// lanes) times a permutation matrix gives an accumulator with queries on lanes.
+
+// Scales shared by the key-major kernels and the dq kernel (see the key kernel for the bounds).
+struct KeyScales {
+  float sQ, sK, sV, sG, sU, sE, cS, fT, fE, fG, cV, C, c1, c2, c3;
+};
+
+__device__ __forceinline__ KeyScales key_scales(const uint32_t* MB, float scale) {
+  KeyScales k;
+  k.sQ = range_scale(mx(MB, kMaxQ));
+  k.sK = range_scale(mx(MB, kMaxK));
+  k.sV = range_scale(mx(MB, kMaxV));
+  k.sG = range_scale(mx(MB, kMaxDO));
+  const float maxU = mx(MB, kMaxU), maxE = mx(MB, kMaxDKB), maxK = mx(MB, kMaxK);
+  k.sU = range_scale(maxU);
+  k.sE = range_scale(maxE);
+  k.cS = scale * kLog2e / (k.sQ * k.sK);
+  k.fT = 1.f / (k.sU * k.sK);
+  k.fE = 1.f / (k.sE * k.sK);
+  k.fG = 1.f / (k.sG * k.sV);
+  const float boundG = 128.f * mx(MB, kMaxDO) * mx(MB, kMaxV);
+  const float boundT = 128.f * maxU * maxK + 1.f + mx(MB, kMaxAlpha);
+  const float boundDS = boundG * boundT + 128.f * maxE * maxK + mx(MB, kMaxDelta);
+  k.cV = range_scale(boundT);
+  float C = range_scale(boundG) * k.sU;
+  C = fminf(C, 16384.f * k.sE);
+  C = fminf(C, range_scale(scale * boundDS) * k.sQ);
+  k.C = C;
+  k.c1 = C / k.sU;
+  k.c2 = C / k.sE;
+  k.c3 = scale * C / k.sQ;
+  return k;
+}
+
+// Whether keys [jw, jw + 32) and query rows [q0, q0 + 32) hold a visible pair with a row in [row_lo, row_hi).
+__device__ __forceinline__ bool tile_pair_any(int jw, int q0, int Tk, int off, int causal, int window, int row_lo,
+                                              int row_hi) {
+  const int jw_last = min(jw + 31, Tk - 1);
+  return jw < Tk && (!causal || jw <= q0 + 31 + off) && (window <= 0 || jw_last > q0 + off - window) &&
+         q0 + 31 >= row_lo && q0 < row_hi;
+}
+
+struct __align__(16) KeyTiles2 {
+  _Float16 r[2][4][32 * kD];   // q, dO, u, e query-row tiles (double-buffered)
+  _Float16 t[2][4][kD * 32];   // q, dO, u, e query-column tiles
+  float ptt[4][4][64 * 4];     // per key group: p tt, [register / 4][lane][4]
+  f16x8 p16[4][2][64];         // per key group: 2^14 p for the two 16-query halves
+  float stat[2][3][32];        // lse (log2 units), alpha, Delta of the tile's rows
+};
+static_assert(sizeof(KeyTiles2) <= 160 * 1024, "LDS");
+
+constexpr float kPExch = 16384.f;   // p is handed over as fp16(2^14 p): p <= 1 never overflows
+
+// One query tile into LDS: wave w copies array w (rows q, dO, u, e, then columns), 8 KB each.
+__device__ __forceinline__ void key_tile_dma2(const KeyParams& p, KeyTiles2& T, int buf, int b, int h, int q0,
+                                              int w, int l) {
+  const int64_t tb = q_tile(b, h, q0 / kQTile, p.Hq, p.Tq_pad / kQTile);
+  const _Float16* src = w == 0 ? p.q16 : w == 1 ? p.do16 : w == 2 ? p.u16 : w == 3 ? p.e16
+                      : w == 4 ? p.q16t : w == 5 ? p.do16t : w == 6 ? p.u16t : p.e16t;
+  _Float16* dst = w < 4 ? T.r[buf][w] : T.t[buf][w - 4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) lds_dma16(src + tb + i * 512 + l * 8, dst + i * 512);
+}
+
+template <bool DS_OUT>
+__global__ __launch_bounds__(512) void k_bwd_keys_duo(KeyParams p) {
+  __shared__ KeyTiles2 T;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, ql = l & 31, hh = l >> 5;
+  const int grp = w & 3;
+  const int npairs = p.B * p.Hkv;
+  int pair, kbk;
+  {
+    const int id = blockIdx.x;
+    if ((npairs & 7) == 0) {
+      const int ppx = npairs >> 3, slot = id >> 3;
+      kbk = slot / ppx;  // causal: the first key blocks see the most rows
+      pair = (id & 7) + 8 * (slot % ppx);
+    } else {
+      kbk = id / npairs;
+      pair = id % npairs;
+    }
+  }
+  const int b = pair / p.Hkv, g = pair % p.Hkv;
+  const int off = p.Tk - p.Tq;
+  const int jb = kbk * 128;
+  const int jw = jb + 32 * grp;
+  const int key = jw + ql;
+  const bool key_ok = key < p.Tk;
+  const KeyScales ks = key_scales(p.maxbits, p.scale);
+
+  // query rows that see some key of the block: [i_lo, i_hi), visited for each head of the group
+  const int jmax_b = min(jb + 128, p.key_hi) - 1;
+  const int i_lo = p.causal ? max(p.row_lo, jb - off) : p.row_lo;
+  const int i_hi = p.window > 0 ? min(p.row_hi, jmax_b - off + p.window) : p.row_hi;
+  const int n_qt = i_hi > i_lo ? (i_hi - 1) / 32 - i_lo / 32 + 1 : 0;
+  const int qt0 = i_lo / 32;
+  const int total = n_qt * p.G;
+  const int row_lo_c = p.row_lo, row_hi_c = min(p.row_hi, p.Tq);
+  const bool nocausal = !p.causal, nowindow = p.window <= 0;
+
+  if (total > 0) {
+    key_tile_dma2(p, T, 0, b, g * p.G, qt0 * 32, w, l);
+    const float sv = key_stat_load(p, b, g * p.G, qt0 * 32, tid);
+    if (tid < 96) T.stat[0][tid >> 5][tid & 31] = sv;
+  }
+  lds_dma_wait();
+  __syncthreads();
+
+  // key rows of the wave's keys as B operands (d permuted, as staged)
+  const int kr = key_ok ? key : 0;
+  const int64_t roff = kv_tile(b, g, kr / kKeyTile, p.Hkv, p.Tk_pad / kKeyTile) + (kr % kKeyTile) * 8 +
+                       hh * (kKeyTile * 8);
+  const float* sl = &T.stat[0][0][0];
+
+  if (w < 4) {
+    // ---------------- S, T, p, tt; dv and p^T dkbar ----------------
+    f16x8 kB[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kB[s] = *reinterpret_cast<const f16x8*>(p.k16 + roff + s * (2 * kKeyTile * 8));
+    f32x16 accV[4], accP[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      accV[mt] = f32x16{};
+      accP[mt] = f32x16{};
+    }
+    for (int it = 0; it < total; ++it) {
+      const int buf = it & 1;
+      const int h = g * p.G + it / n_qt, q0 = (qt0 + it % n_qt) * 32;
+      float next_stat = 0.f;
+      const bool pre = it + 1 < total;
+      if (pre) {
+        const int nh = g * p.G + (it + 1) / n_qt, nq0 = (qt0 + (it + 1) % n_qt) * 32;
+        key_tile_dma2(p, T, buf ^ 1, b, nh, nq0, w, l);
+        next_stat = key_stat_load(p, b, nh, nq0, tid);
+      }
+      const bool any = tile_pair_any(jw, q0, p.Tk, off, p.causal, p.window, p.row_lo, p.row_hi);
+      f16x8 vop[2], pop[2];
+      if (any) {
+        const bool full = jw + 32 <= p.Tk && (!p.causal || jw + 31 <= q0 + off) &&
+                          (p.window <= 0 || jw > q0 + 31 + off - p.window) && q0 >= p.row_lo &&
+                          q0 + 32 <= row_hi_c;
+        f32x16 S = {}, Tt = {};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          S = mfma(kt_rows(T.r[buf][0], ql, 2 * s + hh), kB[s], S);
+          Tt = mfma(kt_rows(T.r[buf][2], ql, 2 * s + hh), kB[s], Tt);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          float wv[8], wp[8], pt[8], pe[8];
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int j = 2 * t + jj, rr = 8 * j + 4 * hh;
+            const float4 L2 = *reinterpret_cast<const float4*>(sl + (buf * 3 + 0) * 32 + rr);
+            const float4 AL = *reinterpret_cast<const float4*>(sl + (buf * 3 + 1) * 32 + rr);
+            const float l2[4] = {L2.x, L2.y, L2.z, L2.w}, al[4] = {AL.x, AL.y, AL.z, AL.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * j + e, o = 4 * jj + e, i = q0 + rr + e;
+              float sv = S[r];
+              if (!full) {
+                const bool vis = key_ok & (i >= row_lo_c) & (i < row_hi_c) & ((key <= i + off) | nocausal) &
+                                 ((key > i + off - p.window) | nowindow);
+                sv = vis ? sv : -INFINITY;
+              }
+              const float pr = __builtin_amdgcn_exp2f(fmaf(sv, ks.cS, -l2[e]));
+              const float tt = fmaf(Tt[r], ks.fT, 1.f - al[e]);
+              pt[o] = pr * tt;
+              wv[o] = pt[o] * ks.cV;
+              wp[o] = pr * ks.c2;
+              pe[o] = pr * kPExch;
+            }
+          }
+          to_operand(wv, 1.f, vop[t], nullptr);
+          to_operand(wp, 1.f, pop[t], nullptr);
+          f16x8 ph;
+          to_operand(pe, 1.f, ph, nullptr);
+          T.p16[grp][t][l] = ph;
+          *reinterpret_cast<float4*>(&T.ptt[grp][2 * t][4 * l]) = float4{pt[0], pt[1], pt[2], pt[3]};
+          *reinterpret_cast<float4*>(&T.ptt[grp][2 * t + 1][4 * l]) = float4{pt[4], pt[5], pt[6], pt[7]};
+        }
+      }
+      __syncthreads();
+      if (any) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            const int d = 32 * mt + ql, c = 2 * t + hh;
+            accV[mt] = mfma(kt_cols(T.t[buf][1], d, c), vop[t], accV[mt]);
+            accP[mt] = mfma(kt_cols(T.t[buf][3], d, c), pop[t], accP[mt]);
+          }
+      }
+      if (pre && tid < 96) T.stat[buf ^ 1][tid >> 5][tid & 31] = next_stat;
+      lds_dma_wait();
+      __syncthreads();
+    }
+    // hand the p^T dkbar part of dk to the other half (tile buffers are free now)
+    float* xk = reinterpret_cast<float*>(&T.r[0][0][0]) + grp * (4 * 16 * 64);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4*>(xk + ((mt * 4 + j) * 64 + l) * 4) =
+            float4{accP[mt][4 * j], accP[mt][4 * j + 1], accP[mt][4 * j + 2], accP[mt][4 * j + 3]};
+    __syncthreads();
+    if (key_ok) {
+      const float fv = 1.f / (ks.sG * ks.cV);
+      float* dvr = p.dv + ((static_cast<int64_t>(b) * p.Tk + key) * p.Hkv + g) * kD;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d = 32 * mt + 8 * j + 4 * hh, r = 4 * j;
+          float4 vv = {accV[mt][r] * fv, accV[mt][r + 1] * fv, accV[mt][r + 2] * fv, accV[mt][r + 3] * fv};
+          if (p.accumulate) {
+            const float4 v0 = *reinterpret_cast<const float4*>(dvr + d);
+            vv = float4{vv.x + v0.x, vv.y + v0.y, vv.z + v0.z, vv.w + v0.w};
+          }
+          *reinterpret_cast<float4*>(dvr + d) = vv;
+        }
+    }
+  } else {
+    // ---------------- G, E; dk from p G and ds ----------------
+    f16x8 kB[8], vB[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      kB[s] = *reinterpret_cast<const f16x8*>(p.k16 + roff + s * (2 * kKeyTile * 8));
+      vB[s] = *reinterpret_cast<const f16x8*>(p.v16 + roff + s * (2 * kKeyTile * 8));
+    }
+    // permutation operands: B[k][n] = 1 iff n = 16 t + perm16(k), k = 8 hh + e
+    f16x8 pi[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        pi[t][e] = static_cast<_Float16>(ql == 16 * t + perm16(8 * hh + e) ? 1.f : 0.f);
+    f32x16 accK[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) accK[mt] = f32x16{};
+    const float inv_pe = 1.f / kPExch;
+    for (int it = 0; it < total; ++it) {
+      const int buf = it & 1;
+      const int h = g * p.G + it / n_qt, q0 = (qt0 + it % n_qt) * 32;
+      const bool pre = it + 1 < total;
+      if (pre) {
+        const int nh = g * p.G + (it + 1) / n_qt, nq0 = (qt0 + (it + 1) % n_qt) * 32;
+        key_tile_dma2(p, T, buf ^ 1, b, nh, nq0, w, l);
+      }
+      const bool any = tile_pair_any(jw, q0, p.Tk, off, p.causal, p.window, p.row_lo, p.row_hi);
+      f32x16 E = {}, Gt = {};
+      if (any) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          Gt = mfma(kt_rows(T.r[buf][1], ql, 2 * s + hh), vB[s], Gt);
+          E = mfma(kt_rows(T.r[buf][3], ql, 2 * s + hh), kB[s], E);
+        }
+      }
+      __syncthreads();
+      if (any) {
+        f32x16 DT = {};
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const f16x8 ph = T.p16[grp][t][l];
+          const float4 P0 = *reinterpret_cast<const float4*>(&T.ptt[grp][2 * t][4 * l]);
+          const float4 P1 = *reinterpret_cast<const float4*>(&T.ptt[grp][2 * t + 1][4 * l]);
+          const float pt[8] = {P0.x, P0.y, P0.z, P0.w, P1.x, P1.y, P1.z, P1.w};
+          float wk[8], wd[8];
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int j = 2 * t + jj, rr = 8 * j + 4 * hh;
+            const float4 DL = *reinterpret_cast<const float4*>(sl + (buf * 3 + 2) * 32 + rr);
+            const float dl[4] = {DL.x, DL.y, DL.z, DL.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * j + e, o = 4 * jj + e;
+              const float pr = static_cast<float>(ph[o]) * inv_pe;
+              const float gt = Gt[r] * ks.fG;
+              wk[o] = pr * gt * ks.c1;
+              wd[o] = fmaf(gt, pt[o], pr * fmaf(E[r], ks.fE, -dl[e])) * ks.c3;
+            }
+          }
+          f16x8 kh, dh;
+          to_operand(wk, 1.f, kh, nullptr);
+          to_operand(wd, 1.f, dh, nullptr);
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            const int d = 32 * mt + ql, c = 2 * t + hh;
+            accK[mt] = mfma(kt_cols(T.t[buf][2], d, c), kh, accK[mt]);
+            accK[mt] = mfma(kt_cols(T.t[buf][0], d, c), dh, accK[mt]);
+          }
+          if constexpr (DS_OUT) DT = mfma(dh, pi[t], DT);
+        }
+        if constexpr (DS_OUT) {
+          // DT: lane = query row of the tile, register r = key 8 (r / 4) + 4 hh + r % 4 of the wave's 32
+          const int64_t tile = ((static_cast<int64_t>(b) * p.Hq + h) * (p.Tq_pad / 32) + q0 / 32) * (p.Tk_pad / 32) +
+                               jw / 32;
+          _Float16* dst = p.ds + tile * 1024 + l * 8;
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            f16x8 o;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = static_cast<_Float16>(DT[8 * t + e]);
+            *reinterpret_cast<f16x8*>(dst + t * 512) = o;
+          }
+        }
+      }
+      lds_dma_wait();
+      __syncthreads();
+    }
+    // add the other half's p^T dkbar part, write dk
+    __syncthreads();
+    const float* xk = reinterpret_cast<const float*>(&T.r[0][0][0]) + grp * (4 * 16 * 64);
+    if (key_ok) {
+      const float fk = 1.f / ks.C;
+      float* dkr = p.dk + ((static_cast<int64_t>(b) * p.Tk + key) * p.Hkv + g) * kD;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d = 32 * mt + 8 * j + 4 * hh, r = 4 * j;
+          const float4 a = *reinterpret_cast<const float4*>(xk + ((mt * 4 + j) * 64 + l) * 4);
+          float4 kv = {(accK[mt][r] + a.x) * fk, (accK[mt][r + 1] + a.y) * fk, (accK[mt][r + 2] + a.z) * fk,
+                       (accK[mt][r + 3] + a.w) * fk};
+          if (p.accumulate) {
+            const float4 k0 = *reinterpret_cast<const float4*>(dkr + d);
+            kv = float4{kv.x + k0.x, kv.y + k0.y, kv.z + k0.z, kv.w + k0.w};
+          }
+          *reinterpret_cast<float4*>(dkr + d) = kv;
+        }
+    }
+  }
+}
+
+// dq for rows >= split: dq = P du (already in dq) + scale sum_j ds_ij k_j, with ds from the
+// key-major kernel.  One wave per 32-row query tile, 4 waves per block; per 32-key block the wave
+// loads the stored ds tile (A operand ordering, keys permuted within 16) and the K^T chunks.
+struct DqParams {
+  const _Float16 *ds, *k16t;
+  const uint32_t* maxbits;
+  float* dq;
+  int B, Tq, Tk, Tk_pad, Tq_pad, Hq, Hkv, G, causal, window, row_lo, row_hi, n_rb;
+  float scale;
+};
+
+__global__ __launch_bounds__(256) void k_bwd_dq(DqParams p) {
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, ql = l & 31, hh = l >> 5;
+  const int npairs = p.B * p.Hkv;
+  int pair, u;
+  {
+    const int id = blockIdx.x;
+    if ((npairs & 7) == 0) {
+      const int ppx = npairs >> 3, slot = id >> 3;
+      u = slot / ppx;
+      pair = (id & 7) + 8 * (slot % ppx);
+    } else {
+      u = id / npairs;
+      pair = id % npairs;
+    }
+  }
+  const int b = pair / p.Hkv, g = pair % p.Hkv;
+  const int h = g * p.G + u % p.G;
+  const int rb = p.n_rb - 1 - u / p.G;   // the last rows (most keys) first
+  const int q0 = (p.row_lo / 32) * 32 + rb * 128 + 32 * w;
+  if (q0 >= p.row_hi) return;
+  const int off = p.Tk - p.Tq;
+  const KeyScales ks = key_scales(p.maxbits, p.scale);
+  const int kb_lo = p.window > 0 ? max(0, q0 + off - p.window + 1) / 32 : 0;
+  const int kb_hi = (p.causal ? min(p.Tk - 1, q0 + 31 + off) : p.Tk - 1) / 32;   // inclusive
+  const int64_t tile0 = ((static_cast<int64_t>(b) * p.Hq + h) * (p.Tq_pad / 32) + q0 / 32) * (p.Tk_pad / 32);
+  f32x16 acc[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x16{};
+  for (int kb = kb_lo; kb <= kb_hi; ++kb) {
+    if (!tile_pair_any(32 * kb, q0, p.Tk, off, p.causal, p.window, p.row_lo, p.row_hi)) continue;
+    const _Float16* src = p.ds + (tile0 + kb) * 1024 + l * 8;
+    const f16x8 d0 = *reinterpret_cast<const f16x8*>(src);
+    const f16x8 d1 = *reinterpret_cast<const f16x8*>(src + 512);
+    const _Float16* kt = p.k16t + kv_tile(b, g, kb >> 1, p.Hkv, p.Tk_pad / kKeyTile) + ((kb & 1) * 4 + hh) * (kD * 8);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const f16x8 a0 = *reinterpret_cast<const f16x8*>(kt + (32 * nt + ql) * 8);
+      const f16x8 a1 = *reinterpret_cast<const f16x8*>(kt + 2 * (kD * 8) + (32 * nt + ql) * 8);
+      acc[nt] = mfma(a0, d0, acc[nt]);
+      acc[nt] = mfma(a1, d1, acc[nt]);
+    }
+  }
+  const int row = q0 + ql;
+  if (row >= p.row_lo && row < p.row_hi && row < p.Tq) {
+    const float fq = ks.sQ / (ks.C * ks.sK);
+    float* dqr = p.dq + ((static_cast<int64_t>(b) * p.Tq + row) * p.Hq + h) * kD;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * nt + 8 * j + 4 * hh, r = 4 * j;
+        const float4 q = *reinterpret_cast<const float4*>(dqr + d);
+        *reinterpret_cast<float4*>(dqr + d) = float4{q.x + acc[nt][r] * fq, q.y + acc[nt][r + 1] * fq,
+                                                     q.z + acc[nt][r + 2] * fq, q.w + acc[nt][r + 3] * fq};
+      }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // dP = sum over batch and rows of x du^T: partial sums per row chunk, then a fixed-order sum
 // ------------------------------------------------------------------------------------------
 
@@ -810,6 +1230,7 @@ struct BwdWs {
   _Float16 *q16, *q16t, *do16, *do16t, *u16, *u16t, *e16, *e16t;
   _Float16 *u16lo, *u16tlo, *e16lo, *e16tlo;
   float *u32, *dkb32, *x32, *du32, *alpha, *delta, *part;
+  _Float16* ds;   // [B][Hq][Tq_pad / 32][Tk_pad / 32] tiles of 32 x 32 fp16
   int Tq_pad, lo_rows, lo_pad, nchunks;
   size_t bytes;
 };
@@ -837,6 +1258,8 @@ BwdWs bwd_layout(const Geom& g, int split, void* ws) {
   const int64_t R = static_cast<int64_t>(g.B) * g.Tq;
   w.nchunks = static_cast<int>((R + kPChunk - 1) / kPChunk);
   w.part = reinterpret_cast<float*>(base + ws_take(off, static_cast<size_t>(w.nchunks) * g.Hq * kD * kD * 4));
+  const size_t ds_bytes = static_cast<size_t>(g.B) * g.Hq * (w.Tq_pad / 32) * (w.st.Tk_pad / 32) * 1024 * 2;
+  w.ds = reinterpret_cast<_Float16*>(base + ws_take(off, ds_bytes));
   w.bytes = off;
   return w;
 }
@@ -910,7 +1333,7 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
     r.row_end = g.Tq;
     r.n_rb = (g.Tq - split + r.rows_per_block - 1) / r.rows_per_block;
     mark_begin(PLX_KERNEL_BWD_ROWS, stream);
-    hipLaunchKernelGGL(k_bwd_rows_fast<false>, dim3(g.B * g.Hkv * r.n_rb), dim3(256), 0, stream, r);
+    hipLaunchKernelGGL((k_bwd_rows_fast<false, false>), dim3(g.B * g.Hkv * r.n_rb), dim3(256), 0, stream, r);
     mark_end(PLX_KERNEL_BWD_ROWS, stream);
   }
   if (split > 0) {
@@ -918,7 +1341,7 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
     r.row_begin = 0;
     r.row_end = split;
     r.n_rb = (split + r.rows_per_block - 1) / r.rows_per_block;
-    hipLaunchKernelGGL(k_bwd_rows_fast<true>, dim3(g.B * g.Hkv * r.n_rb), dim3(256), 0, stream, r);
+    hipLaunchKernelGGL((k_bwd_rows_fast<true, true>), dim3(g.B * g.Hkv * r.n_rb), dim3(256), 0, stream, r);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -970,8 +1393,9 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
     k2.row_lo = split;
     k2.row_hi = g.Tq;
     k2.accumulate = 0;
+    k2.ds = w.ds;
     mark_begin(PLX_KERNEL_BWD_KEYS, stream);
-    hipLaunchKernelGGL(k_bwd_keys_fast<false>, dim3(g.B * g.Hkv * k2.n_kb), dim3(256), 0, stream, k2);
+    hipLaunchKernelGGL(k_bwd_keys_duo<true>, dim3(g.B * g.Hkv * k2.n_kb), dim3(512), 0, stream, k2);
     mark_end(PLX_KERNEL_BWD_KEYS, stream);
   }
   if (split > 0) {
@@ -991,9 +1415,34 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (split < g.Tq) {
+    DqParams dp{};
+    dp.ds = w.ds;
+    dp.k16t = w.st.k16t;
+    dp.maxbits = w.st.maxbits;
+    dp.dq = dq;
+    dp.B = g.B;
+    dp.Tq = g.Tq;
+    dp.Tk = g.Tk;
+    dp.Tk_pad = w.st.Tk_pad;
+    dp.Tq_pad = w.Tq_pad;
+    dp.Hq = g.Hq;
+    dp.Hkv = g.Hkv;
+    dp.G = G;
+    dp.causal = g.causal;
+    dp.window = g.window;
+    dp.row_lo = split;
+    dp.row_hi = g.Tq;
+    dp.n_rb = (g.Tq - (split / 32) * 32 + 127) / 128;
+    dp.scale = g.scale;
+    mark_begin(PLX_KERNEL_BWD_DQ, stream);
+    hipLaunchKernelGGL(k_bwd_dq, dim3(g.B * g.Hkv * G * dp.n_rb), dim3(256), 0, stream, dp);
+    mark_end(PLX_KERNEL_BWD_DQ, stream);
+  }
   const int R = g.B * g.Tq;
   hipLaunchKernelGGL(k_dp_partial, dim3(w.nchunks, g.Hq), dim3(256), 0, stream, w.x32, w.du32, w.part, R, g.Hq);
-  hipLaunchKernelGGL(k_dp_reduce, dim3(64), dim3(256), 0, stream, w.part, dP, w.nchunks, g.Hq);
+  const int nred = (g.Hq * kD * kD + 255) / 256;
+  hipLaunchKernelGGL(k_dp_reduce, dim3(nred), dim3(256), 0, stream, w.part, dP, w.nchunks, g.Hq);
   return hipGetLastError();
 }
 
