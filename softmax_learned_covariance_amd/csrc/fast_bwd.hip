@@ -95,7 +95,8 @@ struct RowParams {
   const _Float16 *k16, *k16t, *v16, *p16t, *p16;
   uint32_t* maxbits;
   float *dq, *u32, *dkb32, *x32, *du32, *st_alpha, *st_delta;
-  int B, Tq, Tk, Tk_pad, Hq, Hkv, G, causal, window;
+  float* rstat;        // per 32-row tile: lse (log2 units), alpha, Delta of each row, [B][Hq][Tq_pad / 32][3][32]
+  int B, Tq, Tk, Tk_pad, Tq_pad, Hq, Hkv, G, causal, window;
   float scale;
   int row_begin, row_end, rows_per_block, n_rb;
 };
@@ -371,6 +372,10 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
   if (row_ok && hh == 0) {
     p.st_alpha[soff] = alpha;
     p.st_delta[soff] = delta;
+    float* rs = p.rstat + ((static_cast<int64_t>(b) * p.Hq + h) * (p.Tq_pad / 32) + row / 32) * 96 + row % 32;
+    rs[0] = lse2;
+    rs[32] = alpha;
+    rs[64] = delta;
   }
   {
     // per-tensor maxima for the key-major pass (rows outside the range contribute 0)
@@ -481,6 +486,8 @@ struct KeyParams {
   const uint32_t* maxbits;
   float *dk, *dv;
   _Float16* ds;        // k_bwd_keys_duo<true>: ds tiles for the dq kernel
+  const float* rstat;  // row statistics per 32-row tile (see RowParams)
+  int64_t qstride;     // elements between consecutive query-side copies q16, q16t, do16, do16t, u16, u16t, e16, e16t
   int B, Tq, Tk, Tk_pad, Tq_pad, lo_pad, Hq, Hkv, G, causal, window;
   float scale;
   int row_lo, row_hi, accumulate, n_kb, key_hi;
@@ -808,15 +815,27 @@ static_assert(sizeof(KeyTiles2) <= 160 * 1024, "LDS");
 
 constexpr float kPExch = 16384.f;   // p is handed over as fp16(2^14 p): p <= 1 never overflows
 
-// One query tile into LDS: wave w copies array w (rows q, dO, u, e, then columns), 8 KB each.
-__device__ __forceinline__ void key_tile_dma2(const KeyParams& p, KeyTiles2& T, int buf, int b, int h, int q0,
-                                              int w, int l) {
+// One query tile into LDS: wave w copies array w (rows q, dO, u, e, then columns), 8 KB each, and
+// wave 0 also the tile's 96 row statistics (lanes 0-23, 16 bytes each).  The destinations are named
+// per field (T.r[buf][a], T.t[buf][a]) so that the compiler can tell the copy into one buffer from
+// the reads of the other and does not make those reads wait for it.
+__device__ __forceinline__ void key_tile_dma_rows(const KeyParams& p, KeyTiles2& T, int buf, int b, int h, int q0,
+                                                  int a, int l) {
   const int64_t tb = q_tile(b, h, q0 / kQTile, p.Hq, p.Tq_pad / kQTile);
-  const _Float16* src = w == 0 ? p.q16 : w == 1 ? p.do16 : w == 2 ? p.u16 : w == 3 ? p.e16
-                      : w == 4 ? p.q16t : w == 5 ? p.do16t : w == 6 ? p.u16t : p.e16t;
-  _Float16* dst = w < 4 ? T.r[buf][w] : T.t[buf][w - 4];
+  const _Float16* src = p.q16 + (2 * a) * p.qstride;   // q, dO, u, e rows (consecutive in the workspace)
 #pragma unroll
-  for (int i = 0; i < 8; ++i) lds_dma16(src + tb + i * 512 + l * 8, dst + i * 512);
+  for (int i = 0; i < 8; ++i) lds_dma16(src + tb + i * 512 + l * 8, &T.r[buf][a][i * 512]);
+  if (a == 0 && l < 24) {
+    const float* st = p.rstat + ((static_cast<int64_t>(b) * p.Hq + h) * (p.Tq_pad / 32) + q0 / 32) * 96;
+    lds_dma16(st + 4 * l, &T.stat[buf][0][0]);
+  }
+}
+__device__ __forceinline__ void key_tile_dma_cols(const KeyParams& p, KeyTiles2& T, int buf, int b, int h, int q0,
+                                                  int a, int l) {
+  const int64_t tb = q_tile(b, h, q0 / kQTile, p.Hq, p.Tq_pad / kQTile);
+  const _Float16* src = p.q16 + (2 * a + 1) * p.qstride;   // q, dO, u, e columns
+#pragma unroll
+  for (int i = 0; i < 8; ++i) lds_dma16(src + tb + i * 512 + l * 8, &T.t[buf][a][i * 512]);
 }
 
 template <bool DS_OUT>
@@ -855,10 +874,14 @@ __global__ __launch_bounds__(512) void k_bwd_keys_duo(KeyParams p) {
   const int row_lo_c = p.row_lo, row_hi_c = min(p.row_hi, p.Tq);
   const bool nocausal = !p.causal, nowindow = p.window <= 0;
 
+  // Query tiles are visited from the last one down, the heads of the group interleaved: the blocks
+  // of one (batch, kv head) running together then read the same tile at about the same time, so it
+  // comes from L2 instead of once per block from memory.
+  auto tile_head = [&](int it) { return g * p.G + it % p.G; };
+  auto tile_row = [&](int it) { return (qt0 + n_qt - 1 - it / p.G) * 32; };
   if (total > 0) {
-    key_tile_dma2(p, T, 0, b, g * p.G, qt0 * 32, w, l);
-    const float sv = key_stat_load(p, b, g * p.G, qt0 * 32, tid);
-    if (tid < 96) T.stat[0][tid >> 5][tid & 31] = sv;
+    if (w < 4) key_tile_dma_rows(p, T, 0, b, tile_head(0), tile_row(0), w, l);
+    else key_tile_dma_cols(p, T, 0, b, tile_head(0), tile_row(0), w - 4, l);
   }
   lds_dma_wait();
   __syncthreads();
@@ -867,13 +890,12 @@ __global__ __launch_bounds__(512) void k_bwd_keys_duo(KeyParams p) {
   const int kr = key_ok ? key : 0;
   const int64_t roff = kv_tile(b, g, kr / kKeyTile, p.Hkv, p.Tk_pad / kKeyTile) + (kr % kKeyTile) * 8 +
                        hh * (kKeyTile * 8);
-  const float* sl = &T.stat[0][0][0];
-
   if (w < 4) {
     // ---------------- S, T, p, tt; dv and p^T dkbar ----------------
     f16x8 kB[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) kB[s] = *reinterpret_cast<const f16x8*>(p.k16 + roff + s * (2 * kKeyTile * 8));
+    vm_wait_all();
     f32x16 accV[4], accP[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -882,14 +904,8 @@ __global__ __launch_bounds__(512) void k_bwd_keys_duo(KeyParams p) {
     }
     for (int it = 0; it < total; ++it) {
       const int buf = it & 1;
-      const int h = g * p.G + it / n_qt, q0 = (qt0 + it % n_qt) * 32;
-      float next_stat = 0.f;
-      const bool pre = it + 1 < total;
-      if (pre) {
-        const int nh = g * p.G + (it + 1) / n_qt, nq0 = (qt0 + (it + 1) % n_qt) * 32;
-        key_tile_dma2(p, T, buf ^ 1, b, nh, nq0, w, l);
-        next_stat = key_stat_load(p, b, nh, nq0, tid);
-      }
+      const int h = tile_head(it), q0 = tile_row(it);
+      if (it + 1 < total) key_tile_dma_rows(p, T, buf ^ 1, b, tile_head(it + 1), tile_row(it + 1), w, l);
       const bool any = tile_pair_any(jw, q0, p.Tk, off, p.causal, p.window, p.row_lo, p.row_hi);
       f16x8 vop[2], pop[2];
       if (any) {
@@ -908,8 +924,8 @@ __global__ __launch_bounds__(512) void k_bwd_keys_duo(KeyParams p) {
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj) {
             const int j = 2 * t + jj, rr = 8 * j + 4 * hh;
-            const float4 L2 = *reinterpret_cast<const float4*>(sl + (buf * 3 + 0) * 32 + rr);
-            const float4 AL = *reinterpret_cast<const float4*>(sl + (buf * 3 + 1) * 32 + rr);
+            const float4 L2 = *reinterpret_cast<const float4*>(&T.stat[buf][0][rr]);
+            const float4 AL = *reinterpret_cast<const float4*>(&T.stat[buf][1][rr]);
             const float l2[4] = {L2.x, L2.y, L2.z, L2.w}, al[4] = {AL.x, AL.y, AL.z, AL.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -937,7 +953,7 @@ __global__ __launch_bounds__(512) void k_bwd_keys_duo(KeyParams p) {
           *reinterpret_cast<float4*>(&T.ptt[grp][2 * t + 1][4 * l]) = float4{pt[4], pt[5], pt[6], pt[7]};
         }
       }
-      __syncthreads();
+      lds_barrier();
       if (any) {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -948,7 +964,6 @@ __global__ __launch_bounds__(512) void k_bwd_keys_duo(KeyParams p) {
             accP[mt] = mfma(kt_cols(T.t[buf][3], d, c), pop[t], accP[mt]);
           }
       }
-      if (pre && tid < 96) T.stat[buf ^ 1][tid >> 5][tid & 31] = next_stat;
       lds_dma_wait();
       __syncthreads();
     }
@@ -960,7 +975,7 @@ __global__ __launch_bounds__(512) void k_bwd_keys_duo(KeyParams p) {
       for (int j = 0; j < 4; ++j)
         *reinterpret_cast<float4*>(xk + ((mt * 4 + j) * 64 + l) * 4) =
             float4{accP[mt][4 * j], accP[mt][4 * j + 1], accP[mt][4 * j + 2], accP[mt][4 * j + 3]};
-    __syncthreads();
+    lds_barrier();
     if (key_ok) {
       const float fv = 1.f / (ks.sG * ks.cV);
       float* dvr = p.dv + ((static_cast<int64_t>(b) * p.Tk + key) * p.Hkv + g) * kD;
@@ -985,6 +1000,7 @@ __global__ __launch_bounds__(512) void k_bwd_keys_duo(KeyParams p) {
       kB[s] = *reinterpret_cast<const f16x8*>(p.k16 + roff + s * (2 * kKeyTile * 8));
       vB[s] = *reinterpret_cast<const f16x8*>(p.v16 + roff + s * (2 * kKeyTile * 8));
     }
+    vm_wait_all();
     // permutation operands: B[k][n] = 1 iff n = 16 t + perm16(k), k = 8 hh + e
     f16x8 pi[2];
 #pragma unroll
@@ -998,12 +1014,8 @@ __global__ __launch_bounds__(512) void k_bwd_keys_duo(KeyParams p) {
     const float inv_pe = 1.f / kPExch;
     for (int it = 0; it < total; ++it) {
       const int buf = it & 1;
-      const int h = g * p.G + it / n_qt, q0 = (qt0 + it % n_qt) * 32;
-      const bool pre = it + 1 < total;
-      if (pre) {
-        const int nh = g * p.G + (it + 1) / n_qt, nq0 = (qt0 + (it + 1) % n_qt) * 32;
-        key_tile_dma2(p, T, buf ^ 1, b, nh, nq0, w, l);
-      }
+      const int h = tile_head(it), q0 = tile_row(it);
+      if (it + 1 < total) key_tile_dma_cols(p, T, buf ^ 1, b, tile_head(it + 1), tile_row(it + 1), w - 4, l);
       const bool any = tile_pair_any(jw, q0, p.Tk, off, p.causal, p.window, p.row_lo, p.row_hi);
       f32x16 E = {}, Gt = {};
       if (any) {
@@ -1013,7 +1025,7 @@ __global__ __launch_bounds__(512) void k_bwd_keys_duo(KeyParams p) {
           E = mfma(kt_rows(T.r[buf][3], ql, 2 * s + hh), kB[s], E);
         }
       }
-      __syncthreads();
+      lds_barrier();
       if (any) {
         f32x16 DT = {};
 #pragma unroll
@@ -1026,7 +1038,7 @@ __global__ __launch_bounds__(512) void k_bwd_keys_duo(KeyParams p) {
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj) {
             const int j = 2 * t + jj, rr = 8 * j + 4 * hh;
-            const float4 DL = *reinterpret_cast<const float4*>(sl + (buf * 3 + 2) * 32 + rr);
+            const float4 DL = *reinterpret_cast<const float4*>(&T.stat[buf][2][rr]);
             const float dl[4] = {DL.x, DL.y, DL.z, DL.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -1066,7 +1078,7 @@ __global__ __launch_bounds__(512) void k_bwd_keys_duo(KeyParams p) {
       __syncthreads();
     }
     // add the other half's p^T dkbar part, write dk
-    __syncthreads();
+    lds_barrier();
     const float* xk = reinterpret_cast<const float*>(&T.r[0][0][0]) + grp * (4 * 16 * 64);
     if (key_ok) {
       const float fk = 1.f / ks.C;
@@ -1158,6 +1170,12 @@ __global__ __launch_bounds__(256) void k_bwd_dq(DqParams p) {
   }
 }
 
+// Zeroes n floats (n a multiple of 4; 16-byte aligned).
+__global__ __launch_bounds__(256) void k_zero4(float* x, int64_t n4) {
+  for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < n4; i += 256LL * gridDim.x)
+    reinterpret_cast<float4*>(x)[i] = float4{0.f, 0.f, 0.f, 0.f};
+}
+
 // ------------------------------------------------------------------------------------------
 // dP = sum over batch and rows of x du^T: partial sums per row chunk, then a fixed-order sum
 // ------------------------------------------------------------------------------------------
@@ -1231,6 +1249,8 @@ struct BwdWs {
   _Float16 *u16lo, *u16tlo, *e16lo, *e16tlo;
   float *u32, *dkb32, *x32, *du32, *alpha, *delta, *part;
   _Float16* ds;   // [B][Hq][Tq_pad / 32][Tk_pad / 32] tiles of 32 x 32 fp16
+  float* rstat;   // [B][Hq][Tq_pad / 32][3][32]
+  size_t rstat_n;
   int Tq_pad, lo_rows, lo_pad, nchunks;
   size_t bytes;
 };
@@ -1248,7 +1268,7 @@ BwdWs bwd_layout(const Geom& g, int split, void* ws) {
   const size_t rf = static_cast<size_t>(g.B) * g.Tq * g.Hq * kD * sizeof(float);
   const size_t sf = static_cast<size_t>(g.B) * g.Hq * g.Tq * sizeof(float);
   _Float16** h16[8] = {&w.q16, &w.q16t, &w.do16, &w.do16t, &w.u16, &w.u16t, &w.e16, &w.e16t};
-  for (auto pp : h16) *pp = reinterpret_cast<_Float16*>(base + ws_take(off, qh));
+  for (auto pp : h16) *pp = reinterpret_cast<_Float16*>(base + ws_take(off, qh));   // equal, consecutive blocks
   _Float16** l16[4] = {&w.u16lo, &w.u16tlo, &w.e16lo, &w.e16tlo};
   for (auto pp : l16) *pp = reinterpret_cast<_Float16*>(base + ws_take(off, lh));
   float** f32[4] = {&w.u32, &w.dkb32, &w.x32, &w.du32};
@@ -1260,6 +1280,8 @@ BwdWs bwd_layout(const Geom& g, int split, void* ws) {
   w.part = reinterpret_cast<float*>(base + ws_take(off, static_cast<size_t>(w.nchunks) * g.Hq * kD * kD * 4));
   const size_t ds_bytes = static_cast<size_t>(g.B) * g.Hq * (w.Tq_pad / 32) * (w.st.Tk_pad / 32) * 1024 * 2;
   w.ds = reinterpret_cast<_Float16*>(base + ws_take(off, ds_bytes));
+  w.rstat_n = static_cast<size_t>(g.B) * g.Hq * w.Tq_pad * 3;
+  w.rstat = reinterpret_cast<float*>(base + ws_take(off, w.rstat_n * sizeof(float)));
   w.bytes = off;
   return w;
 }
@@ -1296,6 +1318,8 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
                         g.Hq, 0, 0, stream);
   if (e != hipSuccess) return e;
 
+  // row statistics of padded rows stay 0 (the key-major kernel reads whole 32-row tiles)
+  hipLaunchKernelGGL(k_zero4, dim3(256), dim3(256), 0, stream, w.rstat, static_cast<int64_t>(w.rstat_n / 4));
   RowParams rp{};
   rp.q = static_cast<const u16*>(q);
   rp.dout = static_cast<const u16*>(dout);
@@ -1316,6 +1340,8 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
   rp.du32 = w.du32;
   rp.st_alpha = w.alpha;
   rp.st_delta = w.delta;
+  rp.rstat = w.rstat;
+  rp.Tq_pad = w.Tq_pad;
   rp.B = g.B;
   rp.Tq = g.Tq;
   rp.Tk = g.Tk;
@@ -1370,6 +1396,8 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
   kp.lse = lse;
   kp.alpha = w.alpha;
   kp.delta = w.delta;
+  kp.rstat = w.rstat;
+  kp.qstride = w.q16t - w.q16;
   kp.maxbits = w.st.maxbits;
   kp.dk = dk;
   kp.dv = dv;

@@ -117,10 +117,32 @@ __device__ __forceinline__ float sum8(f16x8 v, float acc) {
 // Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane l's bytes land at
 // lds_base + 16 * l, so one wave instruction fills 1024 contiguous LDS bytes.  lds_base must be
 // wave-uniform.  Completion is waited for with lds_dma_wait() before the barrier that publishes the data.
+// The instruction is issued from inline assembly: the compiler then does not track it, and does not
+// make every later LDS read (of the other buffer) wait for the copy in flight, which it cannot tell
+// apart from the copy's destination.  The instruction has no register results; its address operands
+// are read at issue.
 __device__ __forceinline__ void lds_dma16(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+  const uint32_t lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lds_base);
+  // one wait state between the M0 write and the LDS DMA that reads it (s_nop 0)
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               ::"v"(src), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
 }
 __device__ __forceinline__ void lds_dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// s_waitcnt vmcnt(0) that the compiler sees (lds_dma_wait is opaque to it): placed after a kernel's
+// own global loads that precede a loop, so that the loop carries no waits for them -- which at run
+// time would also wait for the tile copies the compiler does not track.
+__device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Workgroup barrier that publishes this wave's LDS writes only.  __syncthreads() also fences global
+// memory, which makes every wave first wait for its outstanding loads -- including a tile copy that
+// was started early to overlap with this phase.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // ---- staging buffers inside the caller's workspace ----
 // Slots of the max-abs array (float bits; non-negative floats order like their bits).
