@@ -475,6 +475,285 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
 }
 
 // ------------------------------------------------------------------------------------------
+// query-major kernel for rows >= split: du and the per-row epilogue, 8 waves (2 per SIMD)
+// ------------------------------------------------------------------------------------------
+// The first pass and the epilogue of k_bwd_rows_fast for 32 rows per wave and 8 waves per block
+// (dq is completed from the stored ds by k_bwd_dq).  The epilogue re-reads q and kbar where it needs
+// them instead of holding them in registers, so that a wave fits in the 256 registers that two waves
+// per SIMD leave it.
+
+__device__ __forceinline__ void row_tile_dma8(const RowParams& p, RowTiles& T, int buf, int b, int g, int kt, int w,
+                                              int l) {
+  const int64_t tb = kv_tile(b, g, kt, p.Hkv, p.Tk_pad / kKeyTile);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = 2 * w + j;
+    const int64_t src = tb + i * 512 + l * 8;
+    lds_dma16(p.k16 + src, &T.k[buf][i * 512]);
+    lds_dma16(p.v16 + src, &T.v[buf][i * 512]);
+    lds_dma16(p.k16t + src, &T.kt[buf][i * 512]);
+  }
+}
+
+__global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
+  __shared__ RowTiles T;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, ql = l & 31, hh = l >> 5;
+  const int npairs = p.B * p.Hkv;
+  int pair, rb;
+  {
+    const int id = blockIdx.x;
+    if ((npairs & 7) == 0) {
+      const int ppx = npairs >> 3, slot = id >> 3;
+      rb = p.n_rb - 1 - slot / ppx;
+      pair = (id & 7) + 8 * (slot % ppx);
+    } else {
+      rb = p.n_rb - 1 - id / npairs;
+      pair = id % npairs;
+    }
+  }
+  const int b = pair / p.Hkv, g = pair % p.Hkv;
+  const int wph = 8 / p.G;
+  const int h = g * p.G + w / wph;
+  const int r0 = p.row_begin + rb * p.rows_per_block;
+  const int i0 = r0 + (w % wph) * 32;
+  const int row = i0 + ql;
+  const bool row_ok = row < p.row_end;
+  const int off = p.Tk - p.Tq;
+  const uint32_t* MB = p.maxbits;
+  const float sQ = range_scale(mx(MB, kMaxQ)), sK = range_scale(mx(MB, kMaxK));
+  const float sV = range_scale(mx(MB, kMaxV)), sP = range_scale(mx(MB, kMaxP));
+  const float sG = range_scale(mx(MB, kMaxDO));
+  const float cS = p.scale * kLog2e / (sQ * sK);
+  const float boundG = 128.f * mx(MB, kMaxDO) * mx(MB, kMaxV);
+  const float sPG = range_scale(boundG);
+
+  const int64_t qoff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * kD;
+  const int64_t soff = (static_cast<int64_t>(b) * p.Hq + h) * p.Tq + (row_ok ? row : 0);
+  float lse2 = row_ok ? p.lse[soff] * kLog2e : 0.f;
+  if (!(lse2 > -INFINITY && lse2 < INFINITY)) lse2 = 0.f;  // a row without keys: every S is masked
+
+  const int rlast = min(r0 + p.rows_per_block, p.row_end) - 1;
+  const int kend = p.causal ? min(p.Tk, rlast + off + 1) : p.Tk;
+  const int kbeg = p.window > 0 ? max(0, r0 + off - p.window + 1) : 0;
+  const int t_beg = kbeg / kKeyTile;
+  const int t_end = kend > kbeg ? (kend + kKeyTile - 1) / kKeyTile : t_beg;
+  const int wlast = min(i0 + 31, p.row_end - 1);
+  const bool wave_rows = i0 < p.row_end;
+  const int w_kend = wave_rows ? (p.causal ? min(p.Tk, wlast + off + 1) : p.Tk) : 0;
+  const int w_kbeg = p.window > 0 ? max(0, i0 + off - p.window + 1) : 0;
+  const int w_full_end = p.causal ? min(p.Tk, i0 + off + 1) : p.Tk;
+  const int w_full_beg = p.window > 0 ? max(0, wlast + off - p.window + 1) : 0;
+  const int r_kend = row_ok ? (p.causal ? min(p.Tk, row + off + 1) : p.Tk) : 0;
+  const int r_kbeg = p.window > 0 ? max(0, row + off - p.window + 1) : 0;
+
+  f16x8 qB[8], gB[8];
+  load_row_operand(p.q + qoff, row_ok, hh, sQ, qB);
+  load_row_operand(p.dout + qoff, row_ok, hh, sG, gB);
+
+  // ---------------- du = sum_j p_j G_j k_j (scaled) ----------------
+  f32x16 accDU[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) accDU[mt] = f32x16{};
+  const float fPG = sPG / (sG * sV);
+  if (t_beg < t_end) row_tile_dma8(p, T, 0, b, g, t_beg, w, l);
+  lds_dma_wait();
+  __syncthreads();
+  for (int kt = t_beg; kt < t_end; ++kt) {
+    const int buf = (kt - t_beg) & 1;
+    if (kt + 1 < t_end) row_tile_dma8(p, T, buf ^ 1, b, g, kt + 1, w, l);
+    const int key0 = kt * kKeyTile;
+    if (key0 < w_kend && key0 + kKeyTile > w_kbeg) {
+      const bool full = key0 + kKeyTile <= w_full_end && key0 >= w_full_beg;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16 S = {}, Gt = {};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          S = mfma(lds_rows(T.k[buf], 32 * kb + ql, 2 * s + hh), qB[s], S);
+          Gt = mfma(lds_rows(T.v[buf], 32 * kb + ql, 2 * s + hh), gB[s], Gt);
+        }
+        float pg[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+          float sv = S[r];
+          if (!full && (key >= r_kend || key < r_kbeg)) sv = -INFINITY;
+          pg[r] = __builtin_amdgcn_exp2f(fmaf(sv, cS, -lse2)) * Gt[r] * fPG;
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          f16x8 hi;
+          to_operand(pg + 8 * t, 1.f, hi, nullptr);
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+            accDU[mt] = mfma(lds_cols(T.kt[buf], 32 * mt + ql, 4 * kb + 2 * t + hh), hi, accDU[mt]);
+        }
+      }
+    }
+    lds_dma_wait();
+    __syncthreads();
+  }
+
+  // ---------------- epilogue ----------------
+  // row vectors in the accumulator layout: element (mt, r) is d = 32 mt + 8 (r/4) + 4 hh + r%4
+  float go = 0.f, gout = 0.f, gabs = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d = 32 * mt + 8 * j + 4 * hh;
+      float gv[4] = {0.f, 0.f, 0.f, 0.f};
+      float4 ov = {0.f, 0.f, 0.f, 0.f}, outv = {0.f, 0.f, 0.f, 0.f};
+      if (row_ok) {
+        load4_bf16(p.dout + qoff + d, gv);
+        ov = *reinterpret_cast<const float4*>(p.osa + qoff + d);
+        outv = *reinterpret_cast<const float4*>(p.out + qoff + d);
+      }
+      go += gv[0] * ov.x + gv[1] * ov.y + gv[2] * ov.z + gv[3] * ov.w;
+      gout += gv[0] * outv.x + gv[1] * outv.y + gv[2] * outv.z + gv[3] * outv.w;
+      gabs += fabsf(gv[0]) + fabsf(gv[1]) + fabsf(gv[2]) + fabsf(gv[3]);
+    }
+  go = xor32_sum(go);
+  gout = xor32_sum(gout);
+  gabs = xor32_sum(gabs);
+  // du = sum p G k - (g.o) kbar (in place) and x = q - kbar, both written out for dP
+  float xmax = 0.f, dumax = 0.f;
+  {
+    const float fdu = 1.f / (sPG * sK);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * mt + 8 * j + 4 * hh;
+        float qv[4] = {0.f, 0.f, 0.f, 0.f};
+        float4 kv = {0.f, 0.f, 0.f, 0.f};
+        if (row_ok) {
+          load4_bf16(p.q + qoff + d, qv);
+          kv = *reinterpret_cast<const float4*>(p.kbar + qoff + d);
+        }
+        const float k4[4] = {kv.x, kv.y, kv.z, kv.w};
+        float x4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * j + e;
+          x4[e] = qv[e] - k4[e];
+          accDU[mt][r] = accDU[mt][r] * fdu - go * k4[e];
+          xmax = fmaxf(xmax, fabsf(x4[e]));
+          dumax = fmaxf(dumax, fabsf(accDU[mt][r]));
+        }
+        if (row_ok) {
+          *reinterpret_cast<float4*>(p.x32 + qoff + d) = float4{x4[0], x4[1], x4[2], x4[3]};
+          *reinterpret_cast<float4*>(p.du32 + qoff + d) =
+              float4{accDU[mt][4 * j], accDU[mt][4 * j + 1], accDU[mt][4 * j + 2], accDU[mt][4 * j + 3]};
+        }
+      }
+  }
+  xmax = xor32_max(xmax);
+  dumax = xor32_max(dumax);
+  const float sX = range_scale(xmax), sDU = range_scale(dumax);
+  // (P du)^T = P16 du^T
+  f32x16 accPD[4];
+  {
+    f16x8 dB[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) tile_operand(accDU[s >> 1], s & 1, sDU, dB[s], nullptr);
+    const _Float16* pr = p.p16 + (static_cast<int64_t>(h) * kD + ql) * kD + hh * 8;
+#pragma unroll
+    for (int am = 0; am < 4; ++am) {
+      accPD[am] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) accPD[am] = mfma(*reinterpret_cast<const f16x8*>(pr + 32 * am * kD + 16 * s), dB[s], accPD[am]);
+    }
+  }
+  // U^T = P16t X^T, with x = q - kbar re-read: operand s holds d = 16 s + 8 (e/4) + 4 hh + e%4
+  f32x16 accU[4];
+  {
+    f16x8 xB[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      float x8[8];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int d = 16 * s + 8 * half + 4 * hh;
+        float qv[4] = {0.f, 0.f, 0.f, 0.f};
+        float4 kv = {0.f, 0.f, 0.f, 0.f};
+        if (row_ok) {
+          load4_bf16(p.q + qoff + d, qv);
+          kv = *reinterpret_cast<const float4*>(p.kbar + qoff + d);
+        }
+        x8[4 * half + 0] = qv[0] - kv.x;
+        x8[4 * half + 1] = qv[1] - kv.y;
+        x8[4 * half + 2] = qv[2] - kv.z;
+        x8[4 * half + 3] = qv[3] - kv.w;
+      }
+      to_operand(x8, sX, xB[s], nullptr);
+    }
+    const _Float16* prt = p.p16t + (static_cast<int64_t>(h) * kD + ql) * kD + hh * 8;
+#pragma unroll
+    for (int am = 0; am < 4; ++am) {
+      accU[am] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) accU[am] = mfma(*reinterpret_cast<const f16x8*>(prt + 32 * am * kD + 16 * s), xB[s], accU[am]);
+    }
+  }
+  // u, dq0 = P du (completed by k_bwd_dq), dkbar = -(g.o) u - P du, alpha = u.kbar, Delta = g.out + dkbar.kbar
+  float alpha = 0.f, dkk = 0.f, umax = 0.f, emax = 0.f;
+  {
+    const float fu = 1.f / (sX * sP), fpd = 1.f / (sP * sDU);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * mt + 8 * j + 4 * hh;
+        float4 kv = {0.f, 0.f, 0.f, 0.f};
+        if (row_ok) kv = *reinterpret_cast<const float4*>(p.kbar + qoff + d);
+        const float k4[4] = {kv.x, kv.y, kv.z, kv.w};
+        float u4[4], pd4[4], dk4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * j + e;
+          u4[e] = accU[mt][r] * fu;
+          pd4[e] = accPD[mt][r] * fpd;
+          dk4[e] = -go * u4[e] - pd4[e];
+          alpha += u4[e] * k4[e];
+          dkk += dk4[e] * k4[e];
+          umax = fmaxf(umax, fabsf(u4[e]));
+          emax = fmaxf(emax, fabsf(dk4[e]));
+        }
+        if (row_ok) {
+          *reinterpret_cast<float4*>(p.dq + qoff + d) = float4{pd4[0], pd4[1], pd4[2], pd4[3]};
+          *reinterpret_cast<float4*>(p.u32 + qoff + d) = float4{u4[0], u4[1], u4[2], u4[3]};
+          *reinterpret_cast<float4*>(p.dkb32 + qoff + d) = float4{dk4[0], dk4[1], dk4[2], dk4[3]};
+        }
+      }
+  }
+  alpha = xor32_sum(alpha);
+  dkk = xor32_sum(dkk);
+  umax = xor32_max(umax);
+  emax = xor32_max(emax);
+  const float delta = gout + dkk;
+  if (row_ok && hh == 0) {
+    p.st_alpha[soff] = alpha;
+    p.st_delta[soff] = delta;
+    float* rs = p.rstat + ((static_cast<int64_t>(b) * p.Hq + h) * (p.Tq_pad / 32) + row / 32) * 96 + row % 32;
+    rs[0] = lse2;
+    rs[32] = alpha;
+    rs[64] = delta;
+  }
+  {
+    // per-tensor maxima for the key-major pass (rows outside the range contribute 0)
+    const float wu = wave_max(row_ok ? umax : 0.f), we = wave_max(row_ok ? emax : 0.f);
+    const float wd = wave_max(row_ok ? fabsf(delta) : 0.f), wa = wave_max(row_ok ? fabsf(alpha) : 0.f);
+    if (l == 0) {
+      atomicMax(&p.maxbits[kMaxU], __float_as_uint(wu));
+      atomicMax(&p.maxbits[kMaxDKB], __float_as_uint(we));
+      atomicMax(&p.maxbits[kMaxDelta], __float_as_uint(wd));
+      atomicMax(&p.maxbits[kMaxAlpha], __float_as_uint(wa));
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // key-major kernel: dk, dv
 // ------------------------------------------------------------------------------------------
 
@@ -1358,8 +1637,10 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
     r.row_begin = split;
     r.row_end = g.Tq;
     r.n_rb = (g.Tq - split + r.rows_per_block - 1) / r.rows_per_block;
+    r.rows_per_block = 32 * 8 / G;
+    r.n_rb = (g.Tq - split + r.rows_per_block - 1) / r.rows_per_block;
     mark_begin(PLX_KERNEL_BWD_ROWS, stream);
-    hipLaunchKernelGGL((k_bwd_rows_fast<false, false>), dim3(g.B * g.Hkv * r.n_rb), dim3(256), 0, stream, r);
+    hipLaunchKernelGGL(k_bwd_du, dim3(g.B * g.Hkv * r.n_rb), dim3(512), 0, stream, r);
     mark_end(PLX_KERNEL_BWD_ROWS, stream);
   }
   if (split > 0) {
