@@ -1381,57 +1381,105 @@ __global__ __launch_bounds__(512) void k_bwd_keys_duo(KeyParams p) {
 }
 
 // dq for rows >= split: dq = P du (already in dq) + scale sum_j ds_ij k_j, with ds from the
-// key-major kernel.  One wave per 32-row query tile, 4 waves per block; per 32-key block the wave
-// loads the stored ds tile (A operand ordering, keys permuted within 16) and the K^T chunks.
+// key-major kernel.  One 512-thread block (8 waves) owns a (batch, kv head) and 256 / G rows of each
+// query head of the group, like the forward; each wave owns a 32-row tile.  The K^T tiles are shared
+// by the block through LDS (double-buffered, copied by DMA); each wave streams its stored ds tiles
+// (A operand ordering, keys permuted within 16) from memory one key tile ahead.
 struct DqParams {
   const _Float16 *ds, *k16t;
   const uint32_t* maxbits;
   float* dq;
-  int B, Tq, Tk, Tk_pad, Tq_pad, Hq, Hkv, G, causal, window, row_lo, row_hi, n_rb;
+  int B, Tq, Tk, Tk_pad, Tq_pad, Hq, Hkv, G, causal, window, row_lo, row_hi, row_begin, rows_per_block, n_rb;
   float scale;
 };
 
-__global__ __launch_bounds__(256) void k_bwd_dq(DqParams p) {
+struct __align__(16) DqTiles {
+  _Float16 kt[2][kKeyTile * kD];
+};
+
+__global__ __launch_bounds__(512) void k_bwd_dq(DqParams p) {
+  __shared__ DqTiles T;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, ql = l & 31, hh = l >> 5;
-  const int npairs = p.B * p.Hkv;
-  int pair, u;
+  int pair, rb;
   {
-    const int id = blockIdx.x;
+    const int npairs = p.B * p.Hkv, id = blockIdx.x;
     if ((npairs & 7) == 0) {
       const int ppx = npairs >> 3, slot = id >> 3;
-      u = slot / ppx;
+      rb = p.n_rb - 1 - slot / ppx;
       pair = (id & 7) + 8 * (slot % ppx);
     } else {
-      u = id / npairs;
+      rb = p.n_rb - 1 - id / npairs;
       pair = id % npairs;
     }
   }
   const int b = pair / p.Hkv, g = pair % p.Hkv;
-  const int h = g * p.G + u % p.G;
-  const int rb = p.n_rb - 1 - u / p.G;   // the last rows (most keys) first
-  const int q0 = (p.row_lo / 32) * 32 + rb * 128 + 32 * w;
-  if (q0 >= p.row_hi) return;
+  const int wph = 8 / p.G;
+  const int h = g * p.G + w / wph;
+  const int r0 = p.row_begin + rb * p.rows_per_block;
+  const int q0 = r0 + (w % wph) * 32;
+  const bool wave_ok = q0 < p.row_hi;
   const int off = p.Tk - p.Tq;
   const KeyScales ks = key_scales(p.maxbits, p.scale);
-  const int kb_lo = p.window > 0 ? max(0, q0 + off - p.window + 1) / 32 : 0;
-  const int kb_hi = (p.causal ? min(p.Tk - 1, q0 + 31 + off) : p.Tk - 1) / 32;   // inclusive
+  // keys the block's rows can see: tiles [t_beg, t_end)
+  const int rlast = min(r0 + p.rows_per_block, p.row_hi) - 1;
+  const int kend = p.causal ? min(p.Tk, rlast + off + 1) : p.Tk;
+  const int kbeg = p.window > 0 ? max(0, r0 + off - p.window + 1) : 0;
+  const int t_beg = kbeg / kKeyTile;
+  const int t_end = kend > kbeg ? (kend + kKeyTile - 1) / kKeyTile : t_beg;
   const int64_t tile0 = ((static_cast<int64_t>(b) * p.Hq + h) * (p.Tq_pad / 32) + q0 / 32) * (p.Tk_pad / 32);
+  // a 32-key block holds a stored ds tile iff the key-major kernel saw a visible pair there
+  auto vis = [&](int kb32) {
+    return wave_ok && tile_pair_any(32 * kb32, q0, p.Tk, off, p.causal, p.window, p.row_lo, p.row_hi);
+  };
+  // Loads are unconditional (from an in-bounds tile; blocks without a stored tile are skipped at the
+  // MFMAs), so that no value joins a branch and the compiler does not wait for a prefetch early.
+  const int64_t tile_rd = wave_ok ? tile0 : 0;
+  auto load_ds = [&](int kt, f16x8 (&d)[4]) {
+#pragma unroll
+    for (int kbh = 0; kbh < 2; ++kbh) {
+      const _Float16* src = p.ds + (tile_rd + 2 * kt + kbh) * 1024 + l * 8;
+      d[2 * kbh] = *reinterpret_cast<const f16x8*>(src);
+      d[2 * kbh + 1] = *reinterpret_cast<const f16x8*>(src + 512);
+    }
+  };
+  auto dma_k = [&](int kt, int buf) {
+    const int64_t tb = kv_tile(b, g, kt, p.Hkv, p.Tk_pad / kKeyTile);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int i = 2 * w + j;
+      lds_dma16(p.k16t + tb + i * 512 + l * 8, &T.kt[buf][i * 512]);
+    }
+  };
   f32x16 acc[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x16{};
-  for (int kb = kb_lo; kb <= kb_hi; ++kb) {
-    if (!tile_pair_any(32 * kb, q0, p.Tk, off, p.causal, p.window, p.row_lo, p.row_hi)) continue;
-    const _Float16* src = p.ds + (tile0 + kb) * 1024 + l * 8;
-    const f16x8 d0 = *reinterpret_cast<const f16x8*>(src);
-    const f16x8 d1 = *reinterpret_cast<const f16x8*>(src + 512);
-    const _Float16* kt = p.k16t + kv_tile(b, g, kb >> 1, p.Hkv, p.Tk_pad / kKeyTile) + ((kb & 1) * 4 + hh) * (kD * 8);
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const f16x8 a0 = *reinterpret_cast<const f16x8*>(kt + (32 * nt + ql) * 8);
-      const f16x8 a1 = *reinterpret_cast<const f16x8*>(kt + 2 * (kD * 8) + (32 * nt + ql) * 8);
-      acc[nt] = mfma(a0, d0, acc[nt]);
-      acc[nt] = mfma(a1, d1, acc[nt]);
+  f16x8 dcur[4], dnxt[4];
+  if (t_beg < t_end) {
+    dma_k(t_beg, 0);
+    load_ds(t_beg, dcur);
+  }
+  lds_dma_wait();
+  __syncthreads();
+  for (int kt = t_beg; kt < t_end; ++kt) {
+    const int buf = (kt - t_beg) & 1;
+    if (kt + 1 < t_end) {
+      dma_k(kt + 1, buf ^ 1);
+      load_ds(kt + 1, dnxt);
     }
+#pragma unroll
+    for (int kbh = 0; kbh < 2; ++kbh) {
+      if (vis(2 * kt + kbh)) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            acc[nt] = mfma(lds_cols(T.kt[buf], 32 * nt + ql, 4 * kbh + 2 * t + hh), dcur[2 * kbh + t], acc[nt]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dcur[i] = dnxt[i];
+    lds_dma_wait();
+    __syncthreads();
   }
   const int row = q0 + ql;
   if (row >= p.row_lo && row < p.row_hi && row < p.Tq) {
@@ -1742,10 +1790,12 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
     dp.window = g.window;
     dp.row_lo = split;
     dp.row_hi = g.Tq;
-    dp.n_rb = (g.Tq - (split / 32) * 32 + 127) / 128;
+    dp.row_begin = (split / 32) * 32;   // ds tiles are 32-row aligned
+    dp.rows_per_block = 32 * 8 / G;
+    dp.n_rb = (g.Tq - dp.row_begin + dp.rows_per_block - 1) / dp.rows_per_block;
     dp.scale = g.scale;
     mark_begin(PLX_KERNEL_BWD_DQ, stream);
-    hipLaunchKernelGGL(k_bwd_dq, dim3(g.B * g.Hkv * G * dp.n_rb), dim3(256), 0, stream, dp);
+    hipLaunchKernelGGL(k_bwd_dq, dim3(g.B * g.Hkv * dp.n_rb), dim3(512), 0, stream, dp);
     mark_end(PLX_KERNEL_BWD_DQ, stream);
   }
   const int R = g.B * g.Tq;

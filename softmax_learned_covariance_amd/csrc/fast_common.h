@@ -128,7 +128,12 @@ __device__ __forceinline__ void lds_dma16(const void* src, void* lds_base) {
                ::"v"(src), "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory", "m0");
 }
-__device__ __forceinline__ void lds_dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// The wait is issued twice: as assembly (always kept) and as the builtin, so that the compiler also
+// knows that its own loads issued before it have completed.
+__device__ __forceinline__ void lds_dma_wait() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
 
 // s_waitcnt vmcnt(0) that the compiler sees (lds_dma_wait is opaque to it): placed after a kernel's
 // own global loads that precede a loop, so that the loop carries no waits for them -- which at run
