@@ -132,7 +132,7 @@ __device__ __forceinline__ void row_tile_dma(const RowParams& p, RowTiles& T, in
 template <bool SPLIT, bool DQ_PASS>
 __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
   __shared__ RowTiles T;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, ql = l & 31, hh = l >> 5;
+  const int tid = threadIdx.x, w = wave_id(), l = tid & 63, ql = l & 31, hh = l >> 5;
   const int npairs = p.B * p.Hkv;
   int pair, rb;
   {
@@ -497,7 +497,7 @@ __device__ __forceinline__ void row_tile_dma8(const RowParams& p, RowTiles& T, i
 
 __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
   __shared__ RowTiles T;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, ql = l & 31, hh = l >> 5;
+  const int tid = threadIdx.x, w = wave_id(), l = tid & 63, ql = l & 31, hh = l >> 5;
   const int npairs = p.B * p.Hkv;
   int pair, rb;
   {
@@ -764,7 +764,7 @@ struct KeyParams {
   const float *lse, *alpha, *delta;
   const uint32_t* maxbits;
   float *dk, *dv;
-  _Float16* ds;        // k_bwd_keys_duo<true>: ds tiles for the dq kernel
+  _Float16* ds;        // k_bwd_keys_pipe<true>: ds tiles for the dq kernel
   const float* rstat;  // row statistics per 32-row tile (see RowParams)
   int64_t qstride;     // elements between consecutive query-side copies q16, q16t, do16, do16t, u16, u16t, e16, e16t
   int B, Tq, Tk, Tk_pad, Tq_pad, lo_pad, Hq, Hkv, G, causal, window;
@@ -831,7 +831,7 @@ template <bool SPLIT>
 __global__ __launch_bounds__(256) void k_bwd_keys_fast(KeyParams p) {
   __shared__ KeyTiles<SPLIT> T;
   constexpr int NB = KeyTiles<SPLIT>::NB;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, ql = l & 31, hh = l >> 5;
+  const int tid = threadIdx.x, w = wave_id(), l = tid & 63, ql = l & 31, hh = l >> 5;
   const int npairs = p.B * p.Hkv;
   int pair, kbk;
   {
@@ -1028,18 +1028,25 @@ __global__ __launch_bounds__(256) void k_bwd_keys_fast(KeyParams p) {
 }
 
 // ------------------------------------------------------------------------------------------
-// key-major kernel with role-split waves (rows >= split) and the dq kernel
+// key-major kernel with role-split, pipelined waves (rows >= split) and the dq kernel
 // ------------------------------------------------------------------------------------------
 //
-// 8 waves (2 per SIMD) own 128 keys: wave w has keys jb + 32 (w & 3) + [0, 32).  For each query
-// tile, waves 0-3 compute S and T for their keys, the weights p and tt = T + 1 - alpha, and
-// accumulate dv = (p tt)^T g and the p^T dkbar part of dk.  Through LDS they hand p (fp16, times
-// 2^14) and p tt (fp32) to waves 4-7, which compute G and E, form p G and
-// ds = p (G tt + E - Delta) = G (p tt) + p (E - Delta), and accumulate (p G)^T u + scale ds^T q.
-// Each half issues 32 of the tile's 64 MFMAs, so the two waves sharing a SIMD keep its matrix
-// unit busy while the other one is in its exp / scaling code.
+// 8 waves (2 per SIMD) own 128 keys: wave w has keys jb + 32 (w & 3) + [0, 32).  Waves 0-3 ("V")
+// compute S and T of their keys against a query tile, the weights p and tt = T + 1 - alpha, and
+// accumulate dv = (p tt)^T g.  Through LDS they hand p (fp16, times 2^14) and p tt (fp32) to waves
+// 4-7 ("K"), which compute G and E, form p G and ds = p (G tt + E - Delta) = G (p tt) + p (E - Delta),
+// and accumulate dk = (p G)^T u + p^T dkbar + scale ds^T q.
 //
-// With DS_OUT, waves 4-7 also store the tile of ds (as the fp16 operand C scale ds / sQ) in
+// The K waves run one query tile behind: in the first phase of iteration i the V waves multiply
+// S and T of tile i and then compute their weights, while the K waves compute the weights of tile
+// i - 1 and then multiply its dk products, so that on each SIMD one wave's matrix work overlaps the
+// other's vector work; the second phase holds the V waves' dv products of tile i and the K waves'
+// G and E of tile i (24 + 2 and 24 of the 66 MFMAs per tile are in the first phase).  A query tile is kept in LDS in row layout only ([16 chunks][32 rows][8], 32 KB
+// for q, dO, u, e); the column-layout operands of the products over queries are read from it with
+// the gfx950 transpose load ds_read_b64_tr_b16 (two per operand).  Three tile buffers (tile i - 1
+// for the K waves, tile i, and the copy of tile i + 1 in flight) and two exchange buffers fit in LDS.
+//
+// With DS_OUT, the K waves also store the tile of ds (as the fp16 operand C scale ds / sQ) in
 // query-major order for the dq kernel.  The transpose costs two MFMAs: the ds operand (keys on
 // lanes) times a permutation matrix gives an accumulator with queries on lanes.
 
@@ -1083,44 +1090,60 @@ __device__ __forceinline__ bool tile_pair_any(int jw, int q0, int Tk, int off, i
          q0 + 31 >= row_lo && q0 < row_hi;
 }
 
-struct __align__(16) KeyTiles2 {
-  _Float16 r[2][4][32 * kD];   // q, dO, u, e query-row tiles (double-buffered)
-  _Float16 t[2][4][kD * 32];   // q, dO, u, e query-column tiles
-  float ptt[4][4][64 * 4];     // per key group: p tt, [register / 4][lane][4]
-  f16x8 p16[4][2][64];         // per key group: 2^14 p for the two 16-query halves
-  float stat[2][3][32];        // lse (log2 units), alpha, Delta of the tile's rows
+struct __align__(16) KeyTiles3 {
+  _Float16 r[3][4][32 * kD];   // q, dO, u, e query-row tiles, three buffers
+  float ptt[2][4][4][64 * 4];  // exchange (two buffers): per key group p tt, [register / 4][lane][4]
+  f16x8 p16[2][4][2][64];      // exchange: per key group 2^14 p for the two 16-query halves
+  float stat[3][3][32];        // lse (log2 units), alpha, Delta of the tile's rows
 };
-static_assert(sizeof(KeyTiles2) <= 160 * 1024, "LDS");
+static_assert(sizeof(KeyTiles3) <= 160 * 1024, "LDS");
 
 constexpr float kPExch = 16384.f;   // p is handed over as fp16(2^14 p): p <= 1 never overflows
 
-// One query tile into LDS: wave w copies array w (rows q, dO, u, e, then columns), 8 KB each, and
-// wave 0 also the tile's 96 row statistics (lanes 0-23, 16 bytes each).  The destinations are named
-// per field (T.r[buf][a], T.t[buf][a]) so that the compiler can tell the copy into one buffer from
-// the reads of the other and does not make those reads wait for it.
-__device__ __forceinline__ void key_tile_dma_rows(const KeyParams& p, KeyTiles2& T, int buf, int b, int h, int q0,
-                                                  int a, int l) {
+// One query tile into LDS buffer `buf`: 32 KB (4 arrays of 8 KB, consecutive in the workspace), one
+// quarter array per wave (4 instructions), and the tile's 96 row statistics (wave 0, lanes 0-23).
+__device__ __forceinline__ void key_tile_dma3(const KeyParams& p, KeyTiles3& T, int buf, int b, int h, int q0,
+                                              int w, int l) {
   const int64_t tb = q_tile(b, h, q0 / kQTile, p.Hq, p.Tq_pad / kQTile);
-  const _Float16* src = p.q16 + (2 * a) * p.qstride;   // q, dO, u, e rows (consecutive in the workspace)
+  const int a = w >> 1;
+  const _Float16* src = p.q16 + (2 * a) * p.qstride + tb;   // q, dO, u, e rows
 #pragma unroll
-  for (int i = 0; i < 8; ++i) lds_dma16(src + tb + i * 512 + l * 8, &T.r[buf][a][i * 512]);
-  if (a == 0 && l < 24) {
+  for (int j = 0; j < 4; ++j) {
+    const int i = 4 * (w & 1) + j;
+    lds_dma16(src + i * 512 + l * 8, &T.r[buf][a][i * 512]);
+  }
+  if (w == 0 && l < 24) {
     const float* st = p.rstat + ((static_cast<int64_t>(b) * p.Hq + h) * (p.Tq_pad / 32) + q0 / 32) * 96;
     lds_dma16(st + 4 * l, &T.stat[buf][0][0]);
   }
 }
-__device__ __forceinline__ void key_tile_dma_cols(const KeyParams& p, KeyTiles2& T, int buf, int b, int h, int q0,
-                                                  int a, int l) {
-  const int64_t tb = q_tile(b, h, q0 / kQTile, p.Hq, p.Tq_pad / kQTile);
-  const _Float16* src = p.q16 + (2 * a + 1) * p.qstride;   // q, dO, u, e columns
-#pragma unroll
-  for (int i = 0; i < 8; ++i) lds_dma16(src + tb + i * 512 + l * 8, &T.t[buf][a][i * 512]);
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// Column-layout operand (lane = d = 32 mt + l % 32, 8 query rows per lane in the permuted order of
+// the staged column tiles: chunk 2 t + hh) of one query-row tile in LDS, by two transpose loads.
+// ds_read_b64_tr_b16 transposes 4 x 4 blocks of 16-bit values within each group of 16 lanes: lane i
+// of a group receives element i % 4 of the 8 bytes addressed by lane 4 j + i / 4, as its element j.
+// Source lane 4 j + a of group G therefore points at the 4 consecutive d (a block of 4 positions of
+// the permuted row layout) 16 (2 mt + G % 2) + 4 a + [0, 4) of row 16 t + 4 (G / 2) + j (+ 8).
+__device__ __forceinline__ int tr_lane_offset(int l) {
+  const int G = l >> 4, s = l & 15, j = s >> 2, a = s & 3;
+  return (2 * (G & 1) + (a & 1)) * 256 + (4 * (G >> 1) + j) * 8 + 4 * (a >> 1);
+}
+__device__ __forceinline__ f16x8 tr_cols(const _Float16* rows, int lane_off, int mt, int t) {
+  const _Float16* src = rows + lane_off + mt * 1024 + t * 128;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)src);
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(src + 64));
+  // whole-vector casts (a bit cast of an element of a vector is not reliable here)
+  const f16x4 lo_h = __builtin_bit_cast(f16x4, lo), hi_h = __builtin_bit_cast(f16x4, hi);
+  return __builtin_shufflevector(lo_h, hi_h, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 template <bool DS_OUT>
-__global__ __launch_bounds__(512) void k_bwd_keys_duo(KeyParams p) {
-  __shared__ KeyTiles2 T;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, ql = l & 31, hh = l >> 5;
+__global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
+  __shared__ KeyTiles3 T;
+  const int tid = threadIdx.x, w = wave_id(), l = tid & 63, ql = l & 31, hh = l >> 5;
   const int grp = w & 3;
   const int npairs = p.B * p.Hkv;
   int pair, kbk;
@@ -1152,42 +1175,39 @@ __global__ __launch_bounds__(512) void k_bwd_keys_duo(KeyParams p) {
   const int total = n_qt * p.G;
   const int row_lo_c = p.row_lo, row_hi_c = min(p.row_hi, p.Tq);
   const bool nocausal = !p.causal, nowindow = p.window <= 0;
-
   // Query tiles are visited from the last one down, the heads of the group interleaved: the blocks
   // of one (batch, kv head) running together then read the same tile at about the same time, so it
   // comes from L2 instead of once per block from memory.
   auto tile_head = [&](int it) { return g * p.G + it % p.G; };
   auto tile_row = [&](int it) { return (qt0 + n_qt - 1 - it / p.G) * 32; };
-  if (total > 0) {
-    if (w < 4) key_tile_dma_rows(p, T, 0, b, tile_head(0), tile_row(0), w, l);
-    else key_tile_dma_cols(p, T, 0, b, tile_head(0), tile_row(0), w - 4, l);
-  }
+  auto tile_any = [&](int it) {
+    return tile_pair_any(jw, tile_row(it), p.Tk, off, p.causal, p.window, p.row_lo, p.row_hi);
+  };
+  if (total > 0) key_tile_dma3(p, T, 0, b, tile_head(0), tile_row(0), w, l);
   lds_dma_wait();
   __syncthreads();
 
-  // key rows of the wave's keys as B operands (d permuted, as staged)
   const int kr = key_ok ? key : 0;
   const int64_t roff = kv_tile(b, g, kr / kKeyTile, p.Hkv, p.Tk_pad / kKeyTile) + (kr % kKeyTile) * 8 +
                        hh * (kKeyTile * 8);
+  const int tro = tr_lane_offset(l);
+
   if (w < 4) {
-    // ---------------- S, T, p, tt; dv and p^T dkbar ----------------
+    // ---------------- V waves: S, T, p, tt of tile it; dv and p^T dkbar ----------------
     f16x8 kB[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) kB[s] = *reinterpret_cast<const f16x8*>(p.k16 + roff + s * (2 * kKeyTile * 8));
     vm_wait_all();
-    f32x16 accV[4], accP[4];
+    f32x16 accV[4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      accV[mt] = f32x16{};
-      accP[mt] = f32x16{};
-    }
-    for (int it = 0; it < total; ++it) {
-      const int buf = it & 1;
-      const int h = tile_head(it), q0 = tile_row(it);
-      if (it + 1 < total) key_tile_dma_rows(p, T, buf ^ 1, b, tile_head(it + 1), tile_row(it + 1), w, l);
-      const bool any = tile_pair_any(jw, q0, p.Tk, off, p.causal, p.window, p.row_lo, p.row_hi);
-      f16x8 vop[2], pop[2];
+    for (int mt = 0; mt < 4; ++mt) accV[mt] = f32x16{};
+    for (int it = 0; it <= total; ++it) {
+      const int buf = it % 3, xb = it & 1;
+      if (it + 1 < total) key_tile_dma3(p, T, (it + 1) % 3, b, tile_head(it + 1), tile_row(it + 1), w, l);
+      const bool any = it < total && tile_any(it);
+      f16x8 vop[2];
       if (any) {
+        const int q0 = tile_row(it);
         const bool full = jw + 32 <= p.Tk && (!p.causal || jw + 31 <= q0 + off) &&
                           (p.window <= 0 || jw > q0 + 31 + off - p.window) && q0 >= p.row_lo &&
                           q0 + 32 <= row_hi_c;
@@ -1199,7 +1219,7 @@ __global__ __launch_bounds__(512) void k_bwd_keys_duo(KeyParams p) {
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          float wv[8], wp[8], pt[8], pe[8];
+          float wv[8], pt[8], pe[8];
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj) {
             const int j = 2 * t + jj, rr = 8 * j + 4 * hh;
@@ -1219,17 +1239,15 @@ __global__ __launch_bounds__(512) void k_bwd_keys_duo(KeyParams p) {
               const float tt = fmaf(Tt[r], ks.fT, 1.f - al[e]);
               pt[o] = pr * tt;
               wv[o] = pt[o] * ks.cV;
-              wp[o] = pr * ks.c2;
               pe[o] = pr * kPExch;
             }
           }
           to_operand(wv, 1.f, vop[t], nullptr);
-          to_operand(wp, 1.f, pop[t], nullptr);
           f16x8 ph;
           to_operand(pe, 1.f, ph, nullptr);
-          T.p16[grp][t][l] = ph;
-          *reinterpret_cast<float4*>(&T.ptt[grp][2 * t][4 * l]) = float4{pt[0], pt[1], pt[2], pt[3]};
-          *reinterpret_cast<float4*>(&T.ptt[grp][2 * t + 1][4 * l]) = float4{pt[4], pt[5], pt[6], pt[7]};
+          T.p16[xb][grp][t][l] = ph;
+          *reinterpret_cast<float4*>(&T.ptt[xb][grp][2 * t][4 * l]) = float4{pt[0], pt[1], pt[2], pt[3]};
+          *reinterpret_cast<float4*>(&T.ptt[xb][grp][2 * t + 1][4 * l]) = float4{pt[4], pt[5], pt[6], pt[7]};
         }
       }
       lds_barrier();
@@ -1237,24 +1255,11 @@ __global__ __launch_bounds__(512) void k_bwd_keys_duo(KeyParams p) {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt) {
-            const int d = 32 * mt + ql, c = 2 * t + hh;
-            accV[mt] = mfma(kt_cols(T.t[buf][1], d, c), vop[t], accV[mt]);
-            accP[mt] = mfma(kt_cols(T.t[buf][3], d, c), pop[t], accP[mt]);
-          }
+          for (int mt = 0; mt < 4; ++mt) accV[mt] = mfma(tr_cols(T.r[buf][1], tro, mt, t), vop[t], accV[mt]);
       }
       lds_dma_wait();
       __syncthreads();
     }
-    // hand the p^T dkbar part of dk to the other half (tile buffers are free now)
-    float* xk = reinterpret_cast<float*>(&T.r[0][0][0]) + grp * (4 * 16 * 64);
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<float4*>(xk + ((mt * 4 + j) * 64 + l) * 4) =
-            float4{accP[mt][4 * j], accP[mt][4 * j + 1], accP[mt][4 * j + 2], accP[mt][4 * j + 3]};
-    lds_barrier();
     if (key_ok) {
       const float fv = 1.f / (ks.sG * ks.cV);
       float* dvr = p.dv + ((static_cast<int64_t>(b) * p.Tk + key) * p.Hkv + g) * kD;
@@ -1272,7 +1277,7 @@ __global__ __launch_bounds__(512) void k_bwd_keys_duo(KeyParams p) {
         }
     }
   } else {
-    // ---------------- G, E; dk from p G and ds ----------------
+    // ---------------- K waves: dk products of tile it - 1; G, E of tile it ----------------
     f16x8 kB[8], vB[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -1291,33 +1296,23 @@ __global__ __launch_bounds__(512) void k_bwd_keys_duo(KeyParams p) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) accK[mt] = f32x16{};
     const float inv_pe = 1.f / kPExch;
-    for (int it = 0; it < total; ++it) {
-      const int buf = it & 1;
-      const int h = tile_head(it), q0 = tile_row(it);
-      if (it + 1 < total) key_tile_dma_cols(p, T, buf ^ 1, b, tile_head(it + 1), tile_row(it + 1), w - 4, l);
-      const bool any = tile_pair_any(jw, q0, p.Tk, off, p.causal, p.window, p.row_lo, p.row_hi);
-      f32x16 E = {}, Gt = {};
-      if (any) {
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          Gt = mfma(kt_rows(T.r[buf][1], ql, 2 * s + hh), vB[s], Gt);
-          E = mfma(kt_rows(T.r[buf][3], ql, 2 * s + hh), kB[s], E);
-        }
-      }
-      lds_barrier();
-      if (any) {
+    f32x16 E = {}, Gt = {};   // of the previous tile
+    for (int it = 0; it <= total; ++it) {
+      const int buf = it % 3, pbuf = (it + 2) % 3, pxb = (it + 1) & 1;
+      if (it + 1 < total) key_tile_dma3(p, T, (it + 1) % 3, b, tile_head(it + 1), tile_row(it + 1), w, l);
+      if (it >= 1 && tile_any(it - 1)) {
         f32x16 DT = {};
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const f16x8 ph = T.p16[grp][t][l];
-          const float4 P0 = *reinterpret_cast<const float4*>(&T.ptt[grp][2 * t][4 * l]);
-          const float4 P1 = *reinterpret_cast<const float4*>(&T.ptt[grp][2 * t + 1][4 * l]);
+          const f16x8 ph = T.p16[pxb][grp][t][l];
+          const float4 P0 = *reinterpret_cast<const float4*>(&T.ptt[pxb][grp][2 * t][4 * l]);
+          const float4 P1 = *reinterpret_cast<const float4*>(&T.ptt[pxb][grp][2 * t + 1][4 * l]);
           const float pt[8] = {P0.x, P0.y, P0.z, P0.w, P1.x, P1.y, P1.z, P1.w};
-          float wk[8], wd[8];
+          float wk[8], wd[8], wp[8];
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj) {
             const int j = 2 * t + jj, rr = 8 * j + 4 * hh;
-            const float4 DL = *reinterpret_cast<const float4*>(&T.stat[buf][2][rr]);
+            const float4 DL = *reinterpret_cast<const float4*>(&T.stat[pbuf][2][rr]);
             const float dl[4] = {DL.x, DL.y, DL.z, DL.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -1325,24 +1320,26 @@ __global__ __launch_bounds__(512) void k_bwd_keys_duo(KeyParams p) {
               const float pr = static_cast<float>(ph[o]) * inv_pe;
               const float gt = Gt[r] * ks.fG;
               wk[o] = pr * gt * ks.c1;
+              wp[o] = pr * ks.c2;
               wd[o] = fmaf(gt, pt[o], pr * fmaf(E[r], ks.fE, -dl[e])) * ks.c3;
             }
           }
-          f16x8 kh, dh;
+          f16x8 kh, dh, ph2;
           to_operand(wk, 1.f, kh, nullptr);
+          to_operand(wp, 1.f, ph2, nullptr);
           to_operand(wd, 1.f, dh, nullptr);
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) {
-            const int d = 32 * mt + ql, c = 2 * t + hh;
-            accK[mt] = mfma(kt_cols(T.t[buf][2], d, c), kh, accK[mt]);
-            accK[mt] = mfma(kt_cols(T.t[buf][0], d, c), dh, accK[mt]);
+            accK[mt] = mfma(tr_cols(T.r[pbuf][2], tro, mt, t), kh, accK[mt]);
+            accK[mt] = mfma(tr_cols(T.r[pbuf][3], tro, mt, t), ph2, accK[mt]);
+            accK[mt] = mfma(tr_cols(T.r[pbuf][0], tro, mt, t), dh, accK[mt]);
           }
           if constexpr (DS_OUT) DT = mfma(dh, pi[t], DT);
         }
         if constexpr (DS_OUT) {
           // DT: lane = query row of the tile, register r = key 8 (r / 4) + 4 hh + r % 4 of the wave's 32
-          const int64_t tile = ((static_cast<int64_t>(b) * p.Hq + h) * (p.Tq_pad / 32) + q0 / 32) * (p.Tk_pad / 32) +
-                               jw / 32;
+          const int64_t tile = ((static_cast<int64_t>(b) * p.Hq + tile_head(it - 1)) * (p.Tq_pad / 32) +
+                                tile_row(it - 1) / 32) * (p.Tk_pad / 32) + jw / 32;
           _Float16* dst = p.ds + tile * 1024 + l * 8;
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
@@ -1353,12 +1350,20 @@ __global__ __launch_bounds__(512) void k_bwd_keys_duo(KeyParams p) {
           }
         }
       }
+      lds_barrier();
+      if (it < total && tile_any(it)) {
+        E = f32x16{};
+        Gt = f32x16{};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          Gt = mfma(kt_rows(T.r[buf][1], ql, 2 * s + hh), vB[s], Gt);
+          E = mfma(kt_rows(T.r[buf][3], ql, 2 * s + hh), kB[s], E);
+        }
+      }
       lds_dma_wait();
       __syncthreads();
     }
-    // add the other half's p^T dkbar part, write dk
-    lds_barrier();
-    const float* xk = reinterpret_cast<const float*>(&T.r[0][0][0]) + grp * (4 * 16 * 64);
+    // write dk
     if (key_ok) {
       const float fk = 1.f / ks.C;
       float* dkr = p.dk + ((static_cast<int64_t>(b) * p.Tk + key) * p.Hkv + g) * kD;
@@ -1367,9 +1372,7 @@ __global__ __launch_bounds__(512) void k_bwd_keys_duo(KeyParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int d = 32 * mt + 8 * j + 4 * hh, r = 4 * j;
-          const float4 a = *reinterpret_cast<const float4*>(xk + ((mt * 4 + j) * 64 + l) * 4);
-          float4 kv = {(accK[mt][r] + a.x) * fk, (accK[mt][r + 1] + a.y) * fk, (accK[mt][r + 2] + a.z) * fk,
-                       (accK[mt][r + 3] + a.w) * fk};
+          float4 kv = {accK[mt][r] * fk, accK[mt][r + 1] * fk, accK[mt][r + 2] * fk, accK[mt][r + 3] * fk};
           if (p.accumulate) {
             const float4 k0 = *reinterpret_cast<const float4*>(dkr + d);
             kv = float4{kv.x + k0.x, kv.y + k0.y, kv.z + k0.z, kv.w + k0.w};
@@ -1399,7 +1402,7 @@ struct __align__(16) DqTiles {
 
 __global__ __launch_bounds__(512) void k_bwd_dq(DqParams p) {
   __shared__ DqTiles T;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, ql = l & 31, hh = l >> 5;
+  const int tid = threadIdx.x, w = wave_id(), l = tid & 63, ql = l & 31, hh = l >> 5;
   int pair, rb;
   {
     const int npairs = p.B * p.Hkv, id = blockIdx.x;
@@ -1752,7 +1755,7 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
     k2.accumulate = 0;
     k2.ds = w.ds;
     mark_begin(PLX_KERNEL_BWD_KEYS, stream);
-    hipLaunchKernelGGL(k_bwd_keys_duo<true>, dim3(g.B * g.Hkv * k2.n_kb), dim3(512), 0, stream, k2);
+    hipLaunchKernelGGL(k_bwd_keys_pipe<true>, dim3(g.B * g.Hkv * k2.n_kb), dim3(512), 0, stream, k2);
     mark_end(PLX_KERNEL_BWD_KEYS, stream);
   }
   if (split > 0) {

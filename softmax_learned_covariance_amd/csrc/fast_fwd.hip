@@ -109,7 +109,7 @@ __device__ __forceinline__ void load_q_operand(const u16* qrow, bool ok, int hh,
 template <bool SPLIT>
 __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
   __shared__ Tiles T;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, ql = l & 31, hh = l >> 5;
+  const int tid = threadIdx.x, w = wave_id(), l = tid & 63, ql = l & 31, hh = l >> 5;
 
   // block -> (batch, kv head, row block)
   int pair, rb;
