@@ -759,45 +759,39 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
 
 struct KeyParams {
   const _Float16 *k16, *v16;
-  const _Float16 *q16, *q16t, *do16, *do16t, *u16, *u16t, *e16, *e16t;
-  const _Float16 *u16lo, *u16tlo, *e16lo, *e16tlo;
+  const _Float16 *q16, *do16, *u16, *e16, *u16lo, *e16lo;   // query-row tiles (and lo halves of u, e)
   const float *lse, *alpha, *delta;
   const uint32_t* maxbits;
   float *dk, *dv;
   _Float16* ds;        // k_bwd_keys_pipe<true>: ds tiles for the dq kernel
   const float* rstat;  // row statistics per 32-row tile (see RowParams)
-  int64_t qstride;     // elements between consecutive query-side copies q16, q16t, do16, do16t, u16, u16t, e16, e16t
+  int64_t qstride;     // elements between the consecutive query-row copies q16, do16, u16, e16
   int B, Tq, Tk, Tk_pad, Tq_pad, lo_pad, Hq, Hkv, G, causal, window;
   float scale;
   int row_lo, row_hi, accumulate, n_kb, key_hi;
 };
 
-// One query tile in LDS: query-row tiles [16 chunks][32 rows][8] and query-column tiles
-// [4 chunks][128 d][8] (chunk-major, as staged).
+// One query tile in LDS: query-row tiles [16 chunks][32 rows][8] (chunk-major, as staged); the
+// column-layout operands are read from them with transpose loads (tr_cols).
 template <bool SPLIT>
 struct __align__(16) KeyTiles {
   static constexpr int NR = SPLIT ? 6 : 4;   // q, dO, u, e (+ u lo, e lo)
   static constexpr int NB = SPLIT ? 1 : 2;
   _Float16 r[NB][NR][32 * kD];
-  _Float16 t[NB][NR][kD * 32];
   float stat[NB][3][32];                     // lse2, alpha, delta of the tile's rows
 };
 
 __device__ __forceinline__ f16x8 kt_rows(const _Float16* t, int r, int c) {
   return *reinterpret_cast<const f16x8*>(&t[c * (kQTile * 8) + r * 8]);
 }
-__device__ __forceinline__ f16x8 kt_cols(const _Float16* t, int d, int c) {
-  return *reinterpret_cast<const f16x8*>(&t[c * (kD * 8) + d * 8]);
-}
 
-// Asynchronous copy of one query tile: per array, the query-row tile and the query-column tile are
-// contiguous 8 KB blocks (8 wave instructions of 1024 bytes each, 2 + 2 per wave).
+// Asynchronous copy of one query tile: per array, the query-row tile is one contiguous 8 KB block
+// (8 wave instructions of 1024 bytes, 2 per wave).
 template <bool SPLIT>
 __device__ __forceinline__ void key_tile_dma(const KeyParams& p, KeyTiles<SPLIT>& T, int buf, int b, int h, int q0,
                                              int w, int l) {
   constexpr int NR = KeyTiles<SPLIT>::NR;
   const _Float16* srcr[6] = {p.q16, p.do16, p.u16, p.e16, p.u16lo, p.e16lo};
-  const _Float16* srct[6] = {p.q16t, p.do16t, p.u16t, p.e16t, p.u16tlo, p.e16tlo};
 #pragma unroll
   for (int a = 0; a < NR; ++a) {
     const int pad = a < 4 ? p.Tq_pad : p.lo_pad;
@@ -806,7 +800,6 @@ __device__ __forceinline__ void key_tile_dma(const KeyParams& p, KeyTiles<SPLIT>
     for (int j = 0; j < 2; ++j) {
       const int i = 2 * w + j;
       lds_dma16(srcr[a] + tb + i * 512 + l * 8, &T.r[buf][a][i * 512]);
-      lds_dma16(srct[a] + tb + i * 512 + l * 8, &T.t[buf][a][i * 512]);
     }
   }
 }
@@ -832,6 +825,7 @@ __global__ __launch_bounds__(256) void k_bwd_keys_fast(KeyParams p) {
   __shared__ KeyTiles<SPLIT> T;
   constexpr int NB = KeyTiles<SPLIT>::NB;
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, ql = l & 31, hh = l >> 5;
+  const int tro = tr_lane_offset(l);
   const int npairs = p.B * p.Hkv;
   int pair, kbk;
   {
@@ -973,15 +967,14 @@ __global__ __launch_bounds__(256) void k_bwd_keys_fast(KeyParams p) {
         to_operand(wd, 1.f, dh, SPLIT ? &dlo : nullptr);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-          const int d = 32 * mt + ql, c = 2 * t + hh;
-          const f16x8 ag = kt_cols(T.t[buf][1], d, c), aq = kt_cols(T.t[buf][0], d, c);
-          const f16x8 au = kt_cols(T.t[buf][2], d, c), ae = kt_cols(T.t[buf][3], d, c);
+          const f16x8 ag = tr_cols(T.r[buf][1], tro, mt, t), aq = tr_cols(T.r[buf][0], tro, mt, t);
+          const f16x8 au = tr_cols(T.r[buf][2], tro, mt, t), ae = tr_cols(T.r[buf][3], tro, mt, t);
           accV[mt] = mfma(ag, vh, accV[mt]);
           accK[mt] = mfma(au, kh, accK[mt]);
           accK[mt] = mfma(ae, ph, accK[mt]);
           accK[mt] = mfma(aq, dh, accK[mt]);
           if constexpr (SPLIT) {
-            const f16x8 aul = kt_cols(T.t[buf][4], d, c), ael = kt_cols(T.t[buf][5], d, c);
+            const f16x8 aul = tr_cols(T.r[buf][4], tro, mt, t), ael = tr_cols(T.r[buf][5], tro, mt, t);
             accV[mt] = mfma(ag, vl, accV[mt]);
             accK[mt] = mfma(au, kl, accK[mt]);
             accK[mt] = mfma(aul, kh, accK[mt]);
@@ -1106,7 +1099,7 @@ __device__ __forceinline__ void key_tile_dma3(const KeyParams& p, KeyTiles3& T, 
                                               int w, int l) {
   const int64_t tb = q_tile(b, h, q0 / kQTile, p.Hq, p.Tq_pad / kQTile);
   const int a = w >> 1;
-  const _Float16* src = p.q16 + (2 * a) * p.qstride + tb;   // q, dO, u, e rows
+  const _Float16* src = p.q16 + a * p.qstride + tb;   // q, dO, u, e rows
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int i = 4 * (w & 1) + j;
@@ -1116,28 +1109,6 @@ __device__ __forceinline__ void key_tile_dma3(const KeyParams& p, KeyTiles3& T, 
     const float* st = p.rstat + ((static_cast<int64_t>(b) * p.Hq + h) * (p.Tq_pad / 32) + q0 / 32) * 96;
     lds_dma16(st + 4 * l, &T.stat[buf][0][0]);
   }
-}
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-
-// Column-layout operand (lane = d = 32 mt + l % 32, 8 query rows per lane in the permuted order of
-// the staged column tiles: chunk 2 t + hh) of one query-row tile in LDS, by two transpose loads.
-// ds_read_b64_tr_b16 transposes 4 x 4 blocks of 16-bit values within each group of 16 lanes: lane i
-// of a group receives element i % 4 of the 8 bytes addressed by lane 4 j + i / 4, as its element j.
-// Source lane 4 j + a of group G therefore points at the 4 consecutive d (a block of 4 positions of
-// the permuted row layout) 16 (2 mt + G % 2) + 4 a + [0, 4) of row 16 t + 4 (G / 2) + j (+ 8).
-__device__ __forceinline__ int tr_lane_offset(int l) {
-  const int G = l >> 4, s = l & 15, j = s >> 2, a = s & 3;
-  return (2 * (G & 1) + (a & 1)) * 256 + (4 * (G >> 1) + j) * 8 + 4 * (a >> 1);
-}
-__device__ __forceinline__ f16x8 tr_cols(const _Float16* rows, int lane_off, int mt, int t) {
-  const _Float16* src = rows + lane_off + mt * 1024 + t * 128;
-  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)src);
-  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(src + 64));
-  // whole-vector casts (a bit cast of an element of a vector is not reliable here)
-  const f16x4 lo_h = __builtin_bit_cast(f16x4, lo), hi_h = __builtin_bit_cast(f16x4, hi);
-  return __builtin_shufflevector(lo_h, hi_h, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 template <bool DS_OUT>
@@ -1575,8 +1546,7 @@ __global__ __launch_bounds__(256) void k_dp_reduce(const float* part, float* dP,
 
 struct BwdWs {
   Staging st;
-  _Float16 *q16, *q16t, *do16, *do16t, *u16, *u16t, *e16, *e16t;
-  _Float16 *u16lo, *u16tlo, *e16lo, *e16tlo;
+  _Float16 *q16, *do16, *u16, *e16, *u16lo, *e16lo;
   float *u32, *dkb32, *x32, *du32, *alpha, *delta, *part;
   _Float16* ds;   // [B][Hq][Tq_pad / 32][Tk_pad / 32] tiles of 32 x 32 fp16
   float* rstat;   // [B][Hq][Tq_pad / 32][3][32]
@@ -1597,9 +1567,9 @@ BwdWs bwd_layout(const Geom& g, int split, void* ws) {
   const size_t lh = static_cast<size_t>(g.B) * g.Hq * w.lo_pad * kD * sizeof(_Float16);
   const size_t rf = static_cast<size_t>(g.B) * g.Tq * g.Hq * kD * sizeof(float);
   const size_t sf = static_cast<size_t>(g.B) * g.Hq * g.Tq * sizeof(float);
-  _Float16** h16[8] = {&w.q16, &w.q16t, &w.do16, &w.do16t, &w.u16, &w.u16t, &w.e16, &w.e16t};
+  _Float16** h16[4] = {&w.q16, &w.do16, &w.u16, &w.e16};
   for (auto pp : h16) *pp = reinterpret_cast<_Float16*>(base + ws_take(off, qh));   // equal, consecutive blocks
-  _Float16** l16[4] = {&w.u16lo, &w.u16tlo, &w.e16lo, &w.e16tlo};
+  _Float16** l16[2] = {&w.u16lo, &w.e16lo};
   for (auto pp : l16) *pp = reinterpret_cast<_Float16*>(base + ws_take(off, lh));
   float** f32[4] = {&w.u32, &w.dkb32, &w.x32, &w.du32};
   for (auto pp : f32) *pp = reinterpret_cast<float*>(base + ws_take(off, rf));
@@ -1642,10 +1612,8 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
   if (e != hipSuccess) return e;
   e = launch_absmax(w.st.maxbits, kMaxDO, dout, static_cast<int64_t>(g.B) * g.Tq * g.Hq * kD, stream);
   if (e != hipSuccess) return e;
-  launch_stage_rows(q, false, w.st.maxbits, kMaxQ, w.q16, w.q16t, nullptr, nullptr, g.B, g.Tq, w.Tq_pad, g.Hq, 0,
-                    0, stream);
-  e = launch_stage_rows(dout, false, w.st.maxbits, kMaxDO, w.do16, w.do16t, nullptr, nullptr, g.B, g.Tq, w.Tq_pad,
-                        g.Hq, 0, 0, stream);
+  launch_stage_rows(q, false, w.st.maxbits, kMaxQ, w.q16, nullptr, g.B, g.Tq, w.Tq_pad, g.Hq, 0, 0, stream);
+  e = launch_stage_rows(dout, false, w.st.maxbits, kMaxDO, w.do16, nullptr, g.B, g.Tq, w.Tq_pad, g.Hq, 0, 0, stream);
   if (e != hipSuccess) return e;
 
   // row statistics of padded rows stay 0 (the key-major kernel reads whole 32-row tiles)
@@ -1704,32 +1672,26 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // fp16 copies of u and dkbar (lo parts for rows < split)
-  launch_stage_rows(w.u32, true, w.st.maxbits, kMaxU, w.u16, w.u16t, split > 0 ? w.u16lo : nullptr, w.u16tlo, g.B,
-                    g.Tq, w.Tq_pad, g.Hq, split, w.lo_pad, stream);
-  e = launch_stage_rows(w.dkb32, true, w.st.maxbits, kMaxDKB, w.e16, w.e16t, split > 0 ? w.e16lo : nullptr,
-                        w.e16tlo, g.B, g.Tq, w.Tq_pad, g.Hq, split, w.lo_pad, stream);
+  launch_stage_rows(w.u32, true, w.st.maxbits, kMaxU, w.u16, split > 0 ? w.u16lo : nullptr, g.B, g.Tq, w.Tq_pad, g.Hq,
+                    split, w.lo_pad, stream);
+  e = launch_stage_rows(w.dkb32, true, w.st.maxbits, kMaxDKB, w.e16, split > 0 ? w.e16lo : nullptr, g.B, g.Tq,
+                        w.Tq_pad, g.Hq, split, w.lo_pad, stream);
   if (e != hipSuccess) return e;
 
   KeyParams kp{};
   kp.k16 = w.st.k16;
   kp.v16 = w.st.v16;
   kp.q16 = w.q16;
-  kp.q16t = w.q16t;
   kp.do16 = w.do16;
-  kp.do16t = w.do16t;
   kp.u16 = w.u16;
-  kp.u16t = w.u16t;
   kp.e16 = w.e16;
-  kp.e16t = w.e16t;
   kp.u16lo = w.u16lo;
-  kp.u16tlo = w.u16tlo;
   kp.e16lo = w.e16lo;
-  kp.e16tlo = w.e16tlo;
   kp.lse = lse;
   kp.alpha = w.alpha;
   kp.delta = w.delta;
   kp.rstat = w.rstat;
-  kp.qstride = w.q16t - w.q16;
+  kp.qstride = w.do16 - w.q16;
   kp.maxbits = w.st.maxbits;
   kp.dk = dk;
   kp.dv = dv;

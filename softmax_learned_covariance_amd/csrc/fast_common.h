@@ -153,6 +153,29 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// Column-layout operand (lane = d = 32 mt + l % 32, 8 query rows per lane in the permuted order of
+// a column tile: chunk 2 t + hh) read from a query-row tile ([16 chunks][32 rows][8]) in LDS with two
+// gfx950 transpose loads.  ds_read_b64_tr_b16 transposes 4 x 4 blocks of 16-bit values within each
+// group of 16 lanes: lane i of a group receives element i % 4 of the 8 bytes addressed by lane
+// 4 j + i / 4, as its element j.  Source lane 4 j + a of group G therefore points at the 4
+// consecutive d 16 (2 mt + G % 2) + 4 a + [0, 4) (a run of 4 positions of the row layout) of row
+// 16 t + 4 (G / 2) + j (and + 8 for the second load).
+__device__ __forceinline__ int tr_lane_offset(int l) {
+  const int G = l >> 4, s = l & 15, j = s >> 2, a = s & 3;
+  return (2 * (G & 1) + (a & 1)) * 256 + (4 * (G >> 1) + j) * 8 + 4 * (a >> 1);
+}
+__device__ __forceinline__ f16x8 tr_cols(const _Float16* rows, int lane_off, int mt, int t) {
+  const _Float16* src = rows + lane_off + mt * 1024 + t * 128;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)src);
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(src + 64));
+  // whole-vector casts (a bit cast of an element of a vector is not reliable here)
+  const f16x4 lo_h = __builtin_bit_cast(f16x4, lo), hi_h = __builtin_bit_cast(f16x4, hi);
+  return __builtin_shufflevector(lo_h, hi_h, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // ---- staging buffers inside the caller's workspace ----
 // Slots of the max-abs array (float bits; non-negative floats order like their bits).
 enum MaxSlot { kMaxQ = 0, kMaxK = 1, kMaxV = 2, kMaxP = 3, kMaxDO = 4, kMaxU = 5, kMaxDKB = 6, kMaxDelta = 7,
@@ -198,10 +221,10 @@ inline Staging staging_layout(void* ws, int B, int Tk, int Hkv, int Hq, bool bac
 // max-abs of one more bf16 tensor into maxbits[slot].
 hipError_t launch_absmax(uint32_t* maxbits, int slot, const void* x, int64_t n, hipStream_t stream);
 
-// Query-side fp16 copies (see k_stage_rows in fast_staging.hip).
+// Query-side fp16 copies in the row-tile layout (see k_stage_rows in fast_staging.hip).
 hipError_t launch_stage_rows(const void* src, bool f32, const uint32_t* maxbits, int max_idx, _Float16* dst,
-                             _Float16* dstt, _Float16* lo, _Float16* lot, int B, int Tq, int Tq_pad, int Hq,
-                             int lo_rows, int lo_pad, hipStream_t stream);
+                             _Float16* lo, int B, int Tq, int Tq_pad, int Hq, int lo_rows, int lo_pad,
+                             hipStream_t stream);
 
 // Launches the staging kernels: max-abs of q (rows [0, Tq)), k, v, P, then the fp16 copies.
 // q may be nullptr (decode stages q itself).

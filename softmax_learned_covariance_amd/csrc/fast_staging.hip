@@ -133,56 +133,71 @@ __global__ __launch_bounds__(256) void k_stage_p(const u16* P, const uint32_t* m
 // tiles (rows permuted within groups of 16), scaled by range_scale(max) with max =
 // maxbits[max_idx].  With lo / lot, also the fp16 residuals x*s - hi for rows < lo_rows (tiles of
 // a [B][Hq][lo_pad] index space).
+// Query-side fp16 copies in the row-tile layout [16 chunks][32 rows][8] (d permuted within groups
+// of 16, tiles ordered [batch][head][tile]), times the tensor's range scale, and optionally the low
+// halves x - fp16(x) for rows < lo_rows.  One block per 32-row tile: each thread reads 8 consecutive
+// d of a row (coalesced), the two 4-d runs go through LDS to their chunks (a run of 4 d is a run of
+// 4 positions), and each thread writes whole 16-byte chunks (consecutive rows of a chunk are
+// contiguous).
 template <bool F32>
 __global__ __launch_bounds__(256) void k_stage_rows(const void* src, const uint32_t* maxbits, int max_idx,
-                                                    _Float16* dst, _Float16* dstt, _Float16* lo,
-                                                    _Float16* lot, int Tq, int Tq_pad, int Hq,
+                                                    _Float16* dst, _Float16* lo, int Tq, int Tq_pad, int Hq,
                                                     int lo_rows, int lo_pad) {
-  constexpr int LD = kD + 2;
-  __shared__ _Float16 hs[32 * LD];
-  __shared__ _Float16 ls[32 * LD];
+  __shared__ uint2 hs[16 * 32 * 2];   // [chunk][row][half of the chunk]
+  __shared__ uint2 ls[16 * 32 * 2];
   const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
   const int r0 = qt * 32;
   const float sc = range_scale(__uint_as_float(maxbits[max_idx]));
   const bool want_lo = lo != nullptr && r0 < lo_rows;
-  for (int e = t; e < 32 * kD; e += 256) {
-    const int r = e / kD, d = e % kD, row = r0 + r;
-    float x = 0.f;
+#pragma unroll
+  for (int rep = 0; rep < 2; ++rep) {
+    const int i = t + 256 * rep, r = i >> 4, k = i & 15, row = r0 + r;   // d = 8 k .. 8 k + 7
+    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (row < Tq) {
-      const int64_t off = ((static_cast<int64_t>(b) * Tq + row) * Hq + h) * kD + d;
-      x = F32 ? static_cast<const float*>(src)[off] : bf16_to_f32(static_cast<const u16*>(src)[off]);
+      const int64_t off = ((static_cast<int64_t>(b) * Tq + row) * Hq + h) * kD + 8 * k;
+      if constexpr (F32) {
+        const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + off);
+        const float4 c = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + off + 4);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = c.x; x[5] = c.y; x[6] = c.z; x[7] = c.w;
+      } else {
+        const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const u16*>(src) + off);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[2 * j] = __uint_as_float(ws[j] << 16);
+          x[2 * j + 1] = __uint_as_float(ws[j] & 0xffff0000u);
+        }
+      }
     }
-    x *= sc;
-    const _Float16 hi = static_cast<_Float16>(x);
-    hs[r * LD + d] = hi;
-    if (want_lo) ls[r * LD + d] = static_cast<_Float16>(x - static_cast<float>(hi));
+    f16x8 hi, lw;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = x[e] * sc;
+      hi[e] = static_cast<_Float16>(v);
+      lw[e] = static_cast<_Float16>(v - static_cast<float>(hi[e]));
+    }
+    // d 8k + [0,4) and 8k + [4,8) are position runs 4 (k&1) + [0,4) of chunks 2 (k/2) and 2 (k/2) + 1
+    const int c0 = 2 * (k >> 1), half = k & 1;
+    const uint4 hv = __builtin_bit_cast(uint4, hi), lv = __builtin_bit_cast(uint4, lw);
+    hs[(c0 * 32 + r) * 2 + half] = uint2{hv.x, hv.y};
+    hs[((c0 + 1) * 32 + r) * 2 + half] = uint2{hv.z, hv.w};
+    if (want_lo) {
+      ls[(c0 * 32 + r) * 2 + half] = uint2{lv.x, lv.y};
+      ls[((c0 + 1) * 32 + r) * 2 + half] = uint2{lv.z, lv.w};
+    }
   }
   __syncthreads();
   const int64_t tb = q_tile(b, h, qt, Hq, Tq_pad / kQTile);
   const int64_t tbl = want_lo ? q_tile(b, h, qt, Hq, lo_pad / kQTile) : 0;
-  for (int ci = t; ci < 32 * 16; ci += 256) {
-    const int r = ci >> 4, c = ci & 15;
-    f16x8 o, ol;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = 16 * (c >> 1) + perm16(8 * (c & 1) + e);
-      o[e] = hs[r * LD + d];
-      ol[e] = ls[r * LD + d];
+  for (int rep = 0; rep < 2; ++rep) {
+    const int j = t + 256 * rep, c = j >> 5, r = j & 31;
+    const uint2 a = hs[(c * 32 + r) * 2], a2 = hs[(c * 32 + r) * 2 + 1];
+    *reinterpret_cast<uint4*>(dst + tb + c * (kQTile * 8) + r * 8) = uint4{a.x, a.y, a2.x, a2.y};
+    if (want_lo) {
+      const uint2 m = ls[(c * 32 + r) * 2], m2 = ls[(c * 32 + r) * 2 + 1];
+      *reinterpret_cast<uint4*>(lo + tbl + c * (kQTile * 8) + r * 8) = uint4{m.x, m.y, m2.x, m2.y};
     }
-    *reinterpret_cast<f16x8*>(dst + tb + c * (kQTile * 8) + r * 8) = o;
-    if (want_lo) *reinterpret_cast<f16x8*>(lo + tbl + c * (kQTile * 8) + r * 8) = ol;
-  }
-  for (int ci = t; ci < kD * 4; ci += 256) {
-    const int d = ci >> 2, c = ci & 3;
-    f16x8 o, ol;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int r = 16 * (c >> 1) + perm16(8 * (c & 1) + e);
-      o[e] = hs[r * LD + d];
-      ol[e] = ls[r * LD + d];
-    }
-    *reinterpret_cast<f16x8*>(dstt + tb + c * (kD * 8) + d * 8) = o;
-    if (want_lo) *reinterpret_cast<f16x8*>(lot + tbl + c * (kD * 8) + d * 8) = ol;
   }
 }
 
@@ -214,16 +229,16 @@ hipError_t launch_absmax(uint32_t* maxbits, int slot, const void* x, int64_t n, 
 }
 
 hipError_t launch_stage_rows(const void* src, bool f32, const uint32_t* maxbits, int max_idx, _Float16* dst,
-                             _Float16* dstt, _Float16* lo, _Float16* lot, int B, int Tq, int Tq_pad, int Hq,
-                             int lo_rows, int lo_pad, hipStream_t stream) {
+                             _Float16* lo, int B, int Tq, int Tq_pad, int Hq, int lo_rows, int lo_pad,
+                             hipStream_t stream) {
   if (B == 0 || Tq_pad == 0) return hipSuccess;
   dim3 grid(Tq_pad / 32, Hq, B);
   if (f32)
-    hipLaunchKernelGGL(k_stage_rows<true>, grid, dim3(256), 0, stream, src, maxbits, max_idx, dst, dstt, lo,
-                       lot, Tq, Tq_pad, Hq, lo_rows, lo_pad);
+    hipLaunchKernelGGL(k_stage_rows<true>, grid, dim3(256), 0, stream, src, maxbits, max_idx, dst, lo, Tq, Tq_pad,
+                       Hq, lo_rows, lo_pad);
   else
-    hipLaunchKernelGGL(k_stage_rows<false>, grid, dim3(256), 0, stream, src, maxbits, max_idx, dst, dstt, lo,
-                       lot, Tq, Tq_pad, Hq, lo_rows, lo_pad);
+    hipLaunchKernelGGL(k_stage_rows<false>, grid, dim3(256), 0, stream, src, maxbits, max_idx, dst, lo, Tq, Tq_pad,
+                       Hq, lo_rows, lo_pad);
   return hipGetLastError();
 }
 
