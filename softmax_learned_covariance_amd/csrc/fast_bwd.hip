@@ -572,14 +572,16 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
           S = mfma(lds_rows(T.k[buf], 32 * kb + ql, 2 * s + hh), qB[s], S);
           Gt = mfma(lds_rows(T.v[buf], 32 * kb + ql, 2 * s + hh), gB[s], Gt);
         }
+        if (!full) {   // tiles on the causal / window edge only
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (key >= r_kend || key < r_kbeg) S[r] = -INFINITY;
+          }
+        }
         float pg[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          float sv = S[r];
-          if (!full && (key >= r_kend || key < r_kbeg)) sv = -INFINITY;
-          pg[r] = __builtin_amdgcn_exp2f(fmaf(sv, cS, -lse2)) * Gt[r] * fPG;
-        }
+        for (int r = 0; r < 16; ++r) pg[r] = __builtin_amdgcn_exp2f(fmaf(S[r], cS, -lse2)) * Gt[r] * fPG;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           f16x8 hi;
@@ -1149,8 +1151,9 @@ __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
   // Query tiles are visited from the last one down, the heads of the group interleaved: the blocks
   // of one (batch, kv head) running together then read the same tile at about the same time, so it
   // comes from L2 instead of once per block from memory.
-  auto tile_head = [&](int it) { return g * p.G + it % p.G; };
-  auto tile_row = [&](int it) { return (qt0 + n_qt - 1 - it / p.G) * 32; };
+  const int gsh = p.G == 4 ? 2 : p.G == 2 ? 1 : 0;   // the fast path has G in {1, 2, 4}
+  auto tile_head = [&](int it) { return g * p.G + (it & (p.G - 1)); };
+  auto tile_row = [&](int it) { return (qt0 + n_qt - 1 - (it >> gsh)) * 32; };
   auto tile_any = [&](int it) {
     return tile_pair_any(jw, tile_row(it), p.Tk, off, p.causal, p.window, p.row_lo, p.row_hi);
   };
@@ -1188,6 +1191,15 @@ __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
           S = mfma(kt_rows(T.r[buf][0], ql, 2 * s + hh), kB[s], S);
           Tt = mfma(kt_rows(T.r[buf][2], ql, 2 * s + hh), kB[s], Tt);
         }
+        if (!full) {   // tiles on the causal / window / row-range edge only
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int i = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const bool vis = key_ok & (i >= row_lo_c) & (i < row_hi_c) & ((key <= i + off) | nocausal) &
+                             ((key > i + off - p.window) | nowindow);
+            if (!vis) S[r] = -INFINITY;
+          }
+        }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           float wv[8], pt[8], pe[8];
@@ -1199,14 +1211,8 @@ __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
             const float l2[4] = {L2.x, L2.y, L2.z, L2.w}, al[4] = {AL.x, AL.y, AL.z, AL.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int r = 4 * j + e, o = 4 * jj + e, i = q0 + rr + e;
-              float sv = S[r];
-              if (!full) {
-                const bool vis = key_ok & (i >= row_lo_c) & (i < row_hi_c) & ((key <= i + off) | nocausal) &
-                                 ((key > i + off - p.window) | nowindow);
-                sv = vis ? sv : -INFINITY;
-              }
-              const float pr = __builtin_amdgcn_exp2f(fmaf(sv, ks.cS, -l2[e]));
+              const int r = 4 * j + e, o = 4 * jj + e;
+              const float pr = __builtin_amdgcn_exp2f(fmaf(S[r], ks.cS, -l2[e]));
               const float tt = fmaf(Tt[r], ks.fT, 1.f - al[e]);
               pt[o] = pr * tt;
               wv[o] = pt[o] * ks.cV;
