@@ -1305,11 +1305,21 @@ __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
           to_operand(wk, 1.f, kh, nullptr);
           to_operand(wp, 1.f, ph2, nullptr);
           to_operand(wd, 1.f, dh, nullptr);
+          // column operands of d tile mt + 1 are read while tile mt is multiplied
+          f16x8 au[2], ae[2], aq[2];
+          au[0] = tr_cols(T.r[pbuf][2], tro, 0, t);
+          ae[0] = tr_cols(T.r[pbuf][3], tro, 0, t);
+          aq[0] = tr_cols(T.r[pbuf][0], tro, 0, t);
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) {
-            accK[mt] = mfma(tr_cols(T.r[pbuf][2], tro, mt, t), kh, accK[mt]);
-            accK[mt] = mfma(tr_cols(T.r[pbuf][3], tro, mt, t), ph2, accK[mt]);
-            accK[mt] = mfma(tr_cols(T.r[pbuf][0], tro, mt, t), dh, accK[mt]);
+            if (mt < 3) {
+              au[(mt + 1) & 1] = tr_cols(T.r[pbuf][2], tro, mt + 1, t);
+              ae[(mt + 1) & 1] = tr_cols(T.r[pbuf][3], tro, mt + 1, t);
+              aq[(mt + 1) & 1] = tr_cols(T.r[pbuf][0], tro, mt + 1, t);
+            }
+            accK[mt] = mfma(au[mt & 1], kh, accK[mt]);
+            accK[mt] = mfma(ae[mt & 1], ph2, accK[mt]);
+            accK[mt] = mfma(aq[mt & 1], dh, accK[mt]);
           }
           if constexpr (DS_OUT) DT = mfma(dh, pi[t], DT);
         }
