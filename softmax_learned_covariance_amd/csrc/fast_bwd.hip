@@ -13,18 +13,20 @@
 //   dv_j    = sum_i p_ij (t_ij + 1 - alpha_i) g_i
 //   dk_j    = sum_i p_ij G_ij u_i + p_ij dkbar_i + scale ds_ij q_i
 //
-// Kernels (one stream, in order):
+// Kernels (one stream, in order), for query rows >= split_rows:
 //   staging   fp16 copies of K, V, P and of q, dout in the MFMA operand layouts;
-//   rows      query-major, two passes over the key tiles like the forward:
-//             pass 1 accumulates du (S, G and (p G) K on MFMA), the epilogue forms
-//             u, alpha, P du, dkbar, Delta, and pass 2 accumulates dq (S, T, E, G and
-//             ds K on MFMA) -- every quantity of a row stays in its lane;
-//   staging 2 fp16 copies of u and dkbar (per-tensor scales from the row pass);
-//   keys      key-major: each wave owns 32 keys and streams query tiles, recomputing
-//             S, T, E, G and accumulating dv = (p tt)^T g and
-//             dk = (p G)^T u + p^T dkbar + scale ds^T q on MFMA;
+//   du        query-major, one pass over the key tiles (S, G and (p G) K on MFMA); its
+//             epilogue forms u, alpha, P du (the first part of dq), dkbar, Delta and the
+//             per-tile row statistics -- every quantity of a row stays in its lane;
+//   staging 2 fp16 copies of u and dkbar (per-tensor scales from the du pass);
+//   keys      key-major: a block owns 128 keys and streams query tiles; four waves
+//             recompute S, T, E, G and the weights, four waves accumulate
+//             dv = (p tt)^T g and dk = (p G)^T u + p^T dkbar + scale ds^T q on MFMA and
+//             store each 32 x 32 tile of ds;
+//   dq        query-major: dq += scale ds K from the stored ds tiles;
 //   dP        sum over rows of (q - kbar) du^T, then a fixed-order reduction.
-// Rows below split_rows run the same kernels with hi + lo fp16 operand pairs.
+// Rows below split_rows run two-pass row and key kernels with hi + lo fp16 operand pairs
+// (the row kernel then also forms dq itself).
 // Everything is deterministic (no atomics on results).
 #include <math.h>
 
