@@ -767,7 +767,7 @@ struct KeyParams {
   const float *lse, *alpha, *delta;
   const uint32_t* maxbits;
   float *dk, *dv;
-  _Float16* ds;        // k_bwd_keys_pipe<true>: ds tiles for the dq kernel
+  _Float16* ds;        // k_bwd_keys_pipe: ds tiles for the dq kernel
   const float* rstat;  // row statistics per 32-row tile (see RowParams)
   int64_t qstride;     // elements between the consecutive query-row copies q16, do16, u16, e16
   int B, Tq, Tk, Tk_pad, Tq_pad, lo_pad, Hq, Hkv, G, causal, window;
@@ -787,6 +787,10 @@ struct __align__(16) KeyTiles {
 
 __device__ __forceinline__ f16x8 kt_rows(const _Float16* t, int r, int c) {
   return *reinterpret_cast<const f16x8*>(&t[c * (kQTile * 8) + r * 8]);
+}
+// The same from a tile stored with the per-chunk row swizzle (row_slot_swz).
+__device__ __forceinline__ f16x8 kt_rows_swz(const _Float16* t, int r, int c) {
+  return *reinterpret_cast<const f16x8*>(&t[c * (kQTile * 8) + row_slot_swz(r, c) * 8]);
 }
 
 // Asynchronous copy of one query tile: per array, the query-row tile is one contiguous 8 KB block
@@ -1029,23 +1033,21 @@ __global__ __launch_bounds__(256) void k_bwd_keys_fast(KeyParams p) {
 // ------------------------------------------------------------------------------------------
 //
 // 8 waves (2 per SIMD) own 128 keys: wave w has keys jb + 32 (w & 3) + [0, 32).  Waves 0-3 ("V")
-// compute S and T of their keys against a query tile, the weights p and tt = T + 1 - alpha, and
-// accumulate dv = (p tt)^T g.  Through LDS they hand p (fp16, times 2^14) and p tt (fp32) to waves
-// 4-7 ("K"), which compute G and E, form p G and ds = p (G tt + E - Delta) = G (p tt) + p (E - Delta),
-// and accumulate dk = (p G)^T u + p^T dkbar + scale ds^T q.
+// compute S, T, E and G of their keys against a query tile and every weight of the tile (p tt, p G,
+// p, ds); they hand the four fp16 operands to waves 4-7 ("K") through LDS.  The K waves accumulate
+// dv = (p tt)^T g and dk = (p G)^T u + p^T dkbar + scale ds^T q and store the ds tile for the dq
+// kernel, one query tile behind the V waves.  A tile has two phases: the V waves' MFMAs while the K
+// waves take the previous tile's operands from the exchange, then (after a barrier) the V waves'
+// vector work beside the K waves' MFMAs.  The two roles issue about as many MFMAs each, and every
+// SIMD holds one wave of each role, so one wave's vector work runs beside the other's matrix work.  A query tile is kept in LDS in row layout only
+// ([16 chunks][32 rows][8], 32 KB for q, dO, u, e); the column-layout operands of the products over
+// queries are read from it with the gfx950 transpose load ds_read_b64_tr_b16 (two per operand).  Three
+// tile buffers (tile i - 1 for the K waves, tile i, and the copy of tile i + 1 in flight) and the
+// exchange fit in LDS.
 //
-// The K waves run one query tile behind: in the first phase of iteration i the V waves multiply
-// S and T of tile i and then compute their weights, while the K waves compute the weights of tile
-// i - 1 and then multiply its dk products, so that on each SIMD one wave's matrix work overlaps the
-// other's vector work; the second phase holds the V waves' dv products of tile i and the K waves'
-// G and E of tile i (24 + 2 and 24 of the 66 MFMAs per tile are in the first phase).  A query tile is kept in LDS in row layout only ([16 chunks][32 rows][8], 32 KB
-// for q, dO, u, e); the column-layout operands of the products over queries are read from it with
-// the gfx950 transpose load ds_read_b64_tr_b16 (two per operand).  Three tile buffers (tile i - 1
-// for the K waves, tile i, and the copy of tile i + 1 in flight) and two exchange buffers fit in LDS.
-//
-// With DS_OUT, the K waves also store the tile of ds (as the fp16 operand C scale ds / sQ) in
-// query-major order for the dq kernel.  The transpose costs two MFMAs: the ds operand (keys on
-// lanes) times a permutation matrix gives an accumulator with queries on lanes.
+// The K waves store the tile of ds (as the fp16 operand C scale ds / sQ) in query-major order for
+// the dq kernel.  The transpose costs two MFMAs: the ds operand (keys on lanes) times a permutation
+// matrix gives an accumulator with queries on lanes.
 
 // Scales shared by the key-major kernels and the dq kernel (see the key kernel for the bounds).
 struct KeyScales {
@@ -1089,16 +1091,15 @@ __device__ __forceinline__ bool tile_pair_any(int jw, int q0, int Tk, int off, i
 
 struct __align__(16) KeyTiles3 {
   _Float16 r[3][4][32 * kD];   // q, dO, u, e query-row tiles, three buffers
-  float ptt[2][4][4][64 * 4];  // exchange (two buffers): per key group p tt, [register / 4][lane][4]
-  f16x8 p16[2][4][2][64];      // exchange: per key group 2^14 p for the two 16-query halves
+  f16x8 x[4][4][2][64];        // exchange: per key group p G c1, p c2, ds c3, p tt cV
   float stat[3][3][32];        // lse (log2 units), alpha, Delta of the tile's rows
 };
 static_assert(sizeof(KeyTiles3) <= 160 * 1024, "LDS");
 
-constexpr float kPExch = 16384.f;   // p is handed over as fp16(2^14 p): p <= 1 never overflows
-
 // One query tile into LDS buffer `buf`: 32 KB (4 arrays of 8 KB, consecutive in the workspace), one
 // quarter array per wave (4 instructions), and the tile's 96 row statistics (wave 0, lanes 0-23).
+// The rows of each chunk land swizzled (row_slot_swz): lane l of an instruction fills row slot l % 32
+// of chunk 2 i + l / 32 and so fetches the row that belongs there.
 __device__ __forceinline__ void key_tile_dma3(const KeyParams& p, KeyTiles3& T, int buf, int b, int h, int q0,
                                               int w, int l) {
   const int64_t tb = q_tile(b, h, q0 / kQTile, p.Hq, p.Tq_pad / kQTile);
@@ -1106,8 +1107,8 @@ __device__ __forceinline__ void key_tile_dma3(const KeyParams& p, KeyTiles3& T, 
   const _Float16* src = p.q16 + a * p.qstride + tb;   // q, dO, u, e rows
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int i = 4 * (w & 1) + j;
-    lds_dma16(src + i * 512 + l * 8, &T.r[buf][a][i * 512]);
+    const int i = 4 * (w & 1) + j, ch = 2 * i + (l >> 5);
+    lds_dma16(src + ch * 256 + row_slot_swz(l & 31, ch) * 8, &T.r[buf][a][i * 512]);
   }
   if (w == 0 && l < 24) {
     const float* st = p.rstat + ((static_cast<int64_t>(b) * p.Hq + h) * (p.Tq_pad / 32) + q0 / 32) * 96;
@@ -1115,7 +1116,6 @@ __device__ __forceinline__ void key_tile_dma3(const KeyParams& p, KeyTiles3& T, 
   }
 }
 
-template <bool DS_OUT>
 __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
   __shared__ KeyTiles3 T;
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, ql = l & 31, hh = l >> 5;
@@ -1166,33 +1166,51 @@ __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
   const int kr = key_ok ? key : 0;
   const int64_t roff = kv_tile(b, g, kr / kKeyTile, p.Hkv, p.Tk_pad / kKeyTile) + (kr % kKeyTile) * 8 +
                        hh * (kKeyTile * 8);
-  const int tro = tr_lane_offset(l);
+  const int2 tro = tr_lane_offsets_swz(l);
 
   if (w < 4) {
-    // ---------------- V waves: S, T, p, tt of tile it; dv and p^T dkbar ----------------
-    f16x8 kB[8];
+    // ---------------- V waves: S, T, E, G and the weights of tile it ----------------
+    f16x8 kB[8], vB[8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) kB[s] = *reinterpret_cast<const f16x8*>(p.k16 + roff + s * (2 * kKeyTile * 8));
+    for (int s = 0; s < 8; ++s) {
+      kB[s] = *reinterpret_cast<const f16x8*>(p.k16 + roff + s * (2 * kKeyTile * 8));
+      vB[s] = *reinterpret_cast<const f16x8*>(p.v16 + roff + s * (2 * kKeyTile * 8));
+    }
     vm_wait_all();
-    f32x16 accV[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) accV[mt] = f32x16{};
     for (int it = 0; it <= total; ++it) {
-      const int buf = it % 3, xb = it & 1;
+      const int buf = it % 3;
       if (it + 1 < total) key_tile_dma3(p, T, (it + 1) % 3, b, tile_head(it + 1), tile_row(it + 1), w, l);
       const bool any = it < total && tile_any(it);
-      f16x8 vop[2];
+      f32x16 S = {}, Tt = {}, E = {}, Gt = {};
+      if (any) {
+        // The row operands (q, dO, u, e) of chunk s + 2 are read while the MFMAs of chunk s run; the
+        // scheduling barriers keep the compiler from moving the reads next to their MFMAs.
+        f16x8 a[3][4];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int o = 0; o < 4; ++o) a[s][o] = kt_rows_swz(T.r[buf][o], ql, 2 * s + hh);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          if (s + 2 < 8) {
+#pragma unroll
+            for (int o = 0; o < 4; ++o) a[(s + 2) % 3][o] = kt_rows_swz(T.r[buf][o], ql, 2 * (s + 2) + hh);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          S = mfma(a[s % 3][0], kB[s], S);
+          Gt = mfma(a[s % 3][1], vB[s], Gt);
+          Tt = mfma(a[s % 3][2], kB[s], Tt);
+          E = mfma(a[s % 3][3], kB[s], E);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // the K waves have taken the previous tile's operands from the exchange
+      lds_barrier();
       if (any) {
         const int q0 = tile_row(it);
         const bool full = jw + 32 <= p.Tk && (!p.causal || jw + 31 <= q0 + off) &&
                           (p.window <= 0 || jw > q0 + 31 + off - p.window) && q0 >= p.row_lo &&
                           q0 + 32 <= row_hi_c;
-        f32x16 S = {}, Tt = {};
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          S = mfma(kt_rows(T.r[buf][0], ql, 2 * s + hh), kB[s], S);
-          Tt = mfma(kt_rows(T.r[buf][2], ql, 2 * s + hh), kB[s], Tt);
-        }
         if (!full) {   // tiles on the causal / window / row-range edge only
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -1204,37 +1222,105 @@ __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          float wv[8], pt[8], pe[8];
+          float wv[8], wk[8], wp[8], wd[8];
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj) {
             const int j = 2 * t + jj, rr = 8 * j + 4 * hh;
             const float4 L2 = *reinterpret_cast<const float4*>(&T.stat[buf][0][rr]);
             const float4 AL = *reinterpret_cast<const float4*>(&T.stat[buf][1][rr]);
+            const float4 DL = *reinterpret_cast<const float4*>(&T.stat[buf][2][rr]);
             const float l2[4] = {L2.x, L2.y, L2.z, L2.w}, al[4] = {AL.x, AL.y, AL.z, AL.w};
+            const float dl[4] = {DL.x, DL.y, DL.z, DL.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = 4 * j + e, o = 4 * jj + e;
               const float pr = __builtin_amdgcn_exp2f(fmaf(S[r], ks.cS, -l2[e]));
               const float tt = fmaf(Tt[r], ks.fT, 1.f - al[e]);
-              pt[o] = pr * tt;
-              wv[o] = pt[o] * ks.cV;
-              pe[o] = pr * kPExch;
+              const float pt = pr * tt;
+              const float gt = Gt[r] * ks.fG;
+              wv[o] = pt * ks.cV;
+              wk[o] = pr * gt * ks.c1;
+              wp[o] = pr * ks.c2;
+              wd[o] = fmaf(gt, pt, pr * fmaf(E[r], ks.fE, -dl[e])) * ks.c3;
             }
           }
-          to_operand(wv, 1.f, vop[t], nullptr);
-          f16x8 ph;
-          to_operand(pe, 1.f, ph, nullptr);
-          T.p16[xb][grp][t][l] = ph;
-          *reinterpret_cast<float4*>(&T.ptt[xb][grp][2 * t][4 * l]) = float4{pt[0], pt[1], pt[2], pt[3]};
-          *reinterpret_cast<float4*>(&T.ptt[xb][grp][2 * t + 1][4 * l]) = float4{pt[4], pt[5], pt[6], pt[7]};
+          f16x8 ok, op, od, ov;
+          to_operand(wk, 1.f, ok, nullptr);
+          to_operand(wp, 1.f, op, nullptr);
+          to_operand(wd, 1.f, od, nullptr);
+          to_operand(wv, 1.f, ov, nullptr);
+          T.x[grp][0][t][l] = ok;
+          T.x[grp][1][t][l] = op;
+          T.x[grp][2][t][l] = od;
+          T.x[grp][3][t][l] = ov;
         }
       }
+      lds_dma_wait();
+      __syncthreads();
+    }
+  } else {
+    // ---------------- K waves: dv and dk products and the ds tile of tile it - 1 ----------------
+    // permutation operands: B[k][n] = 1 iff n = 16 t + perm16(k), k = 8 hh + e
+    f16x8 pi[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        pi[t][e] = static_cast<_Float16>(ql == 16 * t + perm16(8 * hh + e) ? 1.f : 0.f);
+    f32x16 accK[4], accV[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) accK[mt] = accV[mt] = f32x16{};
+    for (int it = 0; it <= total; ++it) {
+      const int pbuf = (it + 2) % 3;
+      if (it + 1 < total) key_tile_dma3(p, T, (it + 1) % 3, b, tile_head(it + 1), tile_row(it + 1), w, l);
+      const bool has = it >= 1 && tile_any(it - 1);
+      // operands of tile it - 1, taken before the V waves overwrite the exchange with tile it
+      f16x8 xk[2], xp[2], xd[2], xv[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        xk[t] = T.x[grp][0][t][l];
+        xp[t] = T.x[grp][1][t][l];
+        xd[t] = T.x[grp][2][t][l];
+        xv[t] = T.x[grp][3][t][l];
+      }
       lds_barrier();
-      if (any) {
+      if (has) {
+        f32x16 DT = {};
+        // step n = (t, mt) = (n / 4, n % 4) multiplies the column operands (u, e, q, dO) of d tile mt
+        // and query half t; the operands of step n + 2 are read while step n runs
+        f16x8 c[3][4];
+        auto load_cols = [&](int n, f16x8(&dst)[4]) {
+          const int t = n >> 2, mt = n & 3;
+          dst[0] = tr_cols_swz(T.r[pbuf][2], tro, mt, t);
+          dst[1] = tr_cols_swz(T.r[pbuf][3], tro, mt, t);
+          dst[2] = tr_cols_swz(T.r[pbuf][0], tro, mt, t);
+          dst[3] = tr_cols_swz(T.r[pbuf][1], tro, mt, t);
+        };
+        load_cols(0, c[0]);
+        load_cols(1, c[1]);
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int n = 0; n < 8; ++n) {
+          const int t = n >> 2, mt = n & 3;
+          if (n + 2 < 8) load_cols(n + 2, c[(n + 2) % 3]);
+          __builtin_amdgcn_sched_barrier(0);
+          accK[mt] = mfma(c[n % 3][0], xk[t], accK[mt]);
+          accV[mt] = mfma(c[n % 3][3], xv[t], accV[mt]);
+          accK[mt] = mfma(c[n % 3][1], xp[t], accK[mt]);
+          accK[mt] = mfma(c[n % 3][2], xd[t], accK[mt]);
+          if (mt == 3) DT = mfma(xd[t], pi[t], DT);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // DT: lane = query row of the tile, register r = key 8 (r / 4) + 4 hh + r % 4 of the wave's 32
+        const int64_t tile = ((static_cast<int64_t>(b) * p.Hq + tile_head(it - 1)) * (p.Tq_pad / 32) +
+                              tile_row(it - 1) / 32) * (p.Tk_pad / 32) + jw / 32;
+        _Float16* dst = p.ds + tile * 1024 + l * 8;
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt) accV[mt] = mfma(tr_cols(T.r[buf][1], tro, mt, t), vop[t], accV[mt]);
+        for (int t = 0; t < 2; ++t) {
+          f16x8 o;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = static_cast<_Float16>(DT[8 * t + e]);
+          *reinterpret_cast<f16x8*>(dst + t * 512) = o;
+        }
       }
       lds_dma_wait();
       __syncthreads();
@@ -1254,106 +1340,6 @@ __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
           }
           *reinterpret_cast<float4*>(dvr + d) = vv;
         }
-    }
-  } else {
-    // ---------------- K waves: dk products of tile it - 1; G, E of tile it ----------------
-    f16x8 kB[8], vB[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      kB[s] = *reinterpret_cast<const f16x8*>(p.k16 + roff + s * (2 * kKeyTile * 8));
-      vB[s] = *reinterpret_cast<const f16x8*>(p.v16 + roff + s * (2 * kKeyTile * 8));
-    }
-    vm_wait_all();
-    // permutation operands: B[k][n] = 1 iff n = 16 t + perm16(k), k = 8 hh + e
-    f16x8 pi[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        pi[t][e] = static_cast<_Float16>(ql == 16 * t + perm16(8 * hh + e) ? 1.f : 0.f);
-    f32x16 accK[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) accK[mt] = f32x16{};
-    const float inv_pe = 1.f / kPExch;
-    f32x16 E = {}, Gt = {};   // of the previous tile
-    for (int it = 0; it <= total; ++it) {
-      const int buf = it % 3, pbuf = (it + 2) % 3, pxb = (it + 1) & 1;
-      if (it + 1 < total) key_tile_dma3(p, T, (it + 1) % 3, b, tile_head(it + 1), tile_row(it + 1), w, l);
-      if (it >= 1 && tile_any(it - 1)) {
-        f32x16 DT = {};
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const f16x8 ph = T.p16[pxb][grp][t][l];
-          const float4 P0 = *reinterpret_cast<const float4*>(&T.ptt[pxb][grp][2 * t][4 * l]);
-          const float4 P1 = *reinterpret_cast<const float4*>(&T.ptt[pxb][grp][2 * t + 1][4 * l]);
-          const float pt[8] = {P0.x, P0.y, P0.z, P0.w, P1.x, P1.y, P1.z, P1.w};
-          float wk[8], wd[8], wp[8];
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            const int j = 2 * t + jj, rr = 8 * j + 4 * hh;
-            const float4 DL = *reinterpret_cast<const float4*>(&T.stat[pbuf][2][rr]);
-            const float dl[4] = {DL.x, DL.y, DL.z, DL.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * j + e, o = 4 * jj + e;
-              const float pr = static_cast<float>(ph[o]) * inv_pe;
-              const float gt = Gt[r] * ks.fG;
-              wk[o] = pr * gt * ks.c1;
-              wp[o] = pr * ks.c2;
-              wd[o] = fmaf(gt, pt[o], pr * fmaf(E[r], ks.fE, -dl[e])) * ks.c3;
-            }
-          }
-          f16x8 kh, dh, ph2;
-          to_operand(wk, 1.f, kh, nullptr);
-          to_operand(wp, 1.f, ph2, nullptr);
-          to_operand(wd, 1.f, dh, nullptr);
-          // column operands of d tile mt + 1 are read while tile mt is multiplied
-          f16x8 au[2], ae[2], aq[2];
-          au[0] = tr_cols(T.r[pbuf][2], tro, 0, t);
-          ae[0] = tr_cols(T.r[pbuf][3], tro, 0, t);
-          aq[0] = tr_cols(T.r[pbuf][0], tro, 0, t);
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt) {
-            if (mt < 3) {
-              au[(mt + 1) & 1] = tr_cols(T.r[pbuf][2], tro, mt + 1, t);
-              ae[(mt + 1) & 1] = tr_cols(T.r[pbuf][3], tro, mt + 1, t);
-              aq[(mt + 1) & 1] = tr_cols(T.r[pbuf][0], tro, mt + 1, t);
-            }
-            accK[mt] = mfma(au[mt & 1], kh, accK[mt]);
-            accK[mt] = mfma(ae[mt & 1], ph2, accK[mt]);
-            accK[mt] = mfma(aq[mt & 1], dh, accK[mt]);
-          }
-          if constexpr (DS_OUT) DT = mfma(dh, pi[t], DT);
-        }
-        if constexpr (DS_OUT) {
-          // DT: lane = query row of the tile, register r = key 8 (r / 4) + 4 hh + r % 4 of the wave's 32
-          const int64_t tile = ((static_cast<int64_t>(b) * p.Hq + tile_head(it - 1)) * (p.Tq_pad / 32) +
-                                tile_row(it - 1) / 32) * (p.Tk_pad / 32) + jw / 32;
-          _Float16* dst = p.ds + tile * 1024 + l * 8;
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            f16x8 o;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = static_cast<_Float16>(DT[8 * t + e]);
-            *reinterpret_cast<f16x8*>(dst + t * 512) = o;
-          }
-        }
-      }
-      lds_barrier();
-      if (it < total && tile_any(it)) {
-        E = f32x16{};
-        Gt = f32x16{};
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          Gt = mfma(kt_rows(T.r[buf][1], ql, 2 * s + hh), vB[s], Gt);
-          E = mfma(kt_rows(T.r[buf][3], ql, 2 * s + hh), kB[s], E);
-        }
-      }
-      lds_dma_wait();
-      __syncthreads();
-    }
-    // write dk
-    if (key_ok) {
       const float fk = 1.f / ks.C;
       float* dkr = p.dk + ((static_cast<int64_t>(b) * p.Tk + key) * p.Hkv + g) * kD;
 #pragma unroll
@@ -1735,7 +1721,7 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
     k2.accumulate = 0;
     k2.ds = w.ds;
     mark_begin(PLX_KERNEL_BWD_KEYS, stream);
-    hipLaunchKernelGGL(k_bwd_keys_pipe<true>, dim3(g.B * g.Hkv * k2.n_kb), dim3(512), 0, stream, k2);
+    hipLaunchKernelGGL(k_bwd_keys_pipe, dim3(g.B * g.Hkv * k2.n_kb), dim3(512), 0, stream, k2);
     mark_end(PLX_KERNEL_BWD_KEYS, stream);
   }
   if (split > 0) {

@@ -176,6 +176,26 @@ __device__ __forceinline__ f16x8 tr_cols(const _Float16* rows, int lane_off, int
   return __builtin_shufflevector(lo_h, hi_h, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// The same operand from a row tile whose rows are stored XOR-swizzled per chunk: row r of chunk c sits
+// in row slot r ^ 4 (c % 4).  The unswizzled tile puts the four chunks of a d tile 512 bytes apart,
+// so the 16 lanes of a group, which read two chunks, meet in the same banks (and 32 lanes, four
+// chunks, four times); with the swizzle every lane of a transpose load hits its own banks.  Returns
+// the lane's element offsets of the first load (rows r) and the second (rows r + 8).
+__device__ __forceinline__ int2 tr_lane_offsets_swz(int l) {
+  const int G = l >> 4, s = l & 15, j = s >> 2, a = s & 3;
+  const int c = 2 * (G & 1) + (a & 1), r = 4 * (G >> 1) + j, x = 4 * c;
+  return int2{c * 256 + (r ^ x) * 8 + 4 * (a >> 1), c * 256 + ((r + 8) ^ x) * 8 + 4 * (a >> 1)};
+}
+__device__ __forceinline__ f16x8 tr_cols_swz(const _Float16* rows, int2 lane_off, int mt, int t) {
+  const _Float16* base = rows + mt * 1024 + t * 128;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(base + lane_off.x));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(base + lane_off.y));
+  const f16x4 lo_h = __builtin_bit_cast(f16x4, lo), hi_h = __builtin_bit_cast(f16x4, hi);
+  return __builtin_shufflevector(lo_h, hi_h, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// Row slot of row r of chunk c in a swizzled row tile (an involution: also the row held by slot r).
+__device__ __forceinline__ int row_slot_swz(int r, int c) { return r ^ (4 * (c & 3)); }
+
 // ---- staging buffers inside the caller's workspace ----
 // Slots of the max-abs array (float bits; non-negative floats order like their bits).
 enum MaxSlot { kMaxQ = 0, kMaxK = 1, kMaxV = 2, kMaxP = 3, kMaxDO = 4, kMaxU = 5, kMaxDKB = 6, kMaxDelta = 7,
