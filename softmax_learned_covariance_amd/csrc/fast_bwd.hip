@@ -97,7 +97,7 @@ struct RowParams {
   const _Float16 *k16, *k16t, *v16, *p16t, *p16;
   uint32_t* maxbits;
   float *dq, *u32, *dkb32, *x32, *du32, *st_alpha, *st_delta;
-  float* rstat;        // per 32-row tile: lse (log2 units), alpha, Delta of each row, [B][Hq][Tq_pad / 32][3][32]
+  float* rstat;        // per 32-row tile: lse (log2 units), 1 - alpha, Delta of each row, [B][Hq][Tq_pad / 32][3][32]
   int B, Tq, Tk, Tk_pad, Tq_pad, Hq, Hkv, G, causal, window;
   float scale;
   int row_begin, row_end, rows_per_block, n_rb;
@@ -376,7 +376,7 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
     p.st_delta[soff] = delta;
     float* rs = p.rstat + ((static_cast<int64_t>(b) * p.Hq + h) * (p.Tq_pad / 32) + row / 32) * 96 + row % 32;
     rs[0] = lse2;
-    rs[32] = alpha;
+    rs[32] = 1.f - alpha;
     rs[64] = delta;
   }
   {
@@ -741,7 +741,7 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
     p.st_delta[soff] = delta;
     float* rs = p.rstat + ((static_cast<int64_t>(b) * p.Hq + h) * (p.Tq_pad / 32) + row / 32) * 96 + row % 32;
     rs[0] = lse2;
-    rs[32] = alpha;
+    rs[32] = 1.f - alpha;
     rs[64] = delta;
   }
   {
@@ -1049,6 +1049,9 @@ __global__ __launch_bounds__(256) void k_bwd_keys_fast(KeyParams p) {
 // the dq kernel.  The transpose costs two MFMAs: the ds operand (keys on lanes) times a permutation
 // matrix gives an accumulator with queries on lanes.
 
+// s_getreg operand for the SIMD_ID field (bits 5:4) of the HW_ID hardware register.
+constexpr int kHwIdSimd = (1 << 11) | (4 << 6) | 4;
+
 // Scales shared by the key-major kernels and the dq kernel (see the key kernel for the bounds).
 struct KeyScales {
   float sQ, sK, sV, sG, sU, sE, cS, fT, fE, fG, cV, C, c1, c2, c3;
@@ -1092,7 +1095,7 @@ __device__ __forceinline__ bool tile_pair_any(int jw, int q0, int Tk, int off, i
 struct __align__(16) KeyTiles3 {
   _Float16 r[3][4][32 * kD];   // q, dO, u, e query-row tiles, three buffers
   f16x8 x[4][4][2][64];        // exchange: per key group p G c1, p c2, ds c3, p tt cV
-  float stat[3][3][32];        // lse (log2 units), alpha, Delta of the tile's rows
+  float stat[3][3][32];        // lse (log2 units), 1 - alpha, Delta of the tile's rows
 };
 static_assert(sizeof(KeyTiles3) <= 160 * 1024, "LDS");
 
@@ -1118,8 +1121,24 @@ __device__ __forceinline__ void key_tile_dma3(const KeyParams& p, KeyTiles3& T, 
 
 __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
   __shared__ KeyTiles3 T;
+  __shared__ int wave_simd[8];
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, ql = l & 31, hh = l >> 5;
-  const int grp = w & 3;
+  // Roles follow the SIMDs: the two waves a SIMD holds become the V and the K wave of one key group,
+  // so that every SIMD runs one wave's vector work beside the other's MFMAs.  (The dispatcher need
+  // not place waves w and w + 4 together; at 2 waves per SIMD each SIMD holds exactly two.)
+  const int simd = __builtin_amdgcn_s_getreg(kHwIdSimd);
+  if (l == 0) wave_simd[w] = simd;
+  __syncthreads();
+  int below = 0, counts = 0;
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const int sv = __builtin_amdgcn_readfirstlane(wave_simd[v]);
+    below += (sv == simd) & (v < w);
+    counts += 1 << (8 * (sv & 3));
+  }
+  const bool paired = counts == 0x02020202;
+  const bool is_v = paired ? below == 0 : w < 4;
+  const int grp = paired ? simd : (w & 3);
   const int npairs = p.B * p.Hkv;
   int pair, kbk;
   {
@@ -1168,7 +1187,7 @@ __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
                        hh * (kKeyTile * 8);
   const int2 tro = tr_lane_offsets_swz(l);
 
-  if (w < 4) {
+  if (is_v) {
     // ---------------- V waves: S, T, E, G and the weights of tile it ----------------
     f16x8 kB[8], vB[8];
 #pragma unroll
@@ -1182,6 +1201,7 @@ __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
       if (it + 1 < total) key_tile_dma3(p, T, (it + 1) % 3, b, tile_head(it + 1), tile_row(it + 1), w, l);
       const bool any = it < total && tile_any(it);
       f32x16 S = {}, Tt = {}, E = {}, Gt = {};
+      float4 st[3][4];   // row statistics of the tile: lse, 1 - alpha, Delta of rows 8 j + 4 hh + [0, 4)
       if (any) {
         // The row operands (q, dO, u, e) of chunk s + 2 are read while the MFMAs of chunk s run; the
         // scheduling barriers keep the compiler from moving the reads next to their MFMAs.
@@ -1195,6 +1215,12 @@ __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
           if (s + 2 < 8) {
 #pragma unroll
             for (int o = 0; o < 4; ++o) a[(s + 2) % 3][o] = kt_rows_swz(T.r[buf][o], ql, 2 * (s + 2) + hh);
+          }
+          if (s == 6) {   // the statistics are read while the last MFMAs run
+#pragma unroll
+            for (int k = 0; k < 3; ++k)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) st[k][j] = *reinterpret_cast<const float4*>(&T.stat[buf][k][8 * j + 4 * hh]);
           }
           __builtin_amdgcn_sched_barrier(0);
           S = mfma(a[s % 3][0], kB[s], S);
@@ -1220,39 +1246,42 @@ __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
             if (!vis) S[r] = -INFINITY;
           }
         }
+        // Stage by stage over the 16 rows of the lane, so that neighbouring instructions are
+        // independent: p, tt = 1 - alpha + T, g = G, b = g tt + dkbar.k - Delta.
+        float pr[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pr[r] = fmaf(S[r], ks.cS, -st[0][r >> 2][r & 3]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(pr[r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          Tt[r] = fmaf(Tt[r], ks.fT, st[1][r >> 2][r & 3]);
+          Gt[r] = Gt[r] * ks.fG;
+          E[r] = fmaf(E[r], ks.fE, -st[2][r >> 2][r & 3]);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) E[r] = fmaf(Gt[r], Tt[r], E[r]);
+        __builtin_amdgcn_sched_barrier(0);
+        // operands p G c1, p c2, p b c3 (= ds c3) and p tt cV
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          float wv[8], wk[8], wp[8], wd[8];
+          float w[8];
+          f16x8 o;
 #pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            const int j = 2 * t + jj, rr = 8 * j + 4 * hh;
-            const float4 L2 = *reinterpret_cast<const float4*>(&T.stat[buf][0][rr]);
-            const float4 AL = *reinterpret_cast<const float4*>(&T.stat[buf][1][rr]);
-            const float4 DL = *reinterpret_cast<const float4*>(&T.stat[buf][2][rr]);
-            const float l2[4] = {L2.x, L2.y, L2.z, L2.w}, al[4] = {AL.x, AL.y, AL.z, AL.w};
-            const float dl[4] = {DL.x, DL.y, DL.z, DL.w};
+          for (int e = 0; e < 8; ++e) w[e] = pr[8 * t + e] * Gt[8 * t + e];
+          to_operand(w, ks.c1, o, nullptr);
+          T.x[grp][0][t][l] = o;
+          to_operand(&pr[8 * t], ks.c2, o, nullptr);
+          T.x[grp][1][t][l] = o;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * j + e, o = 4 * jj + e;
-              const float pr = __builtin_amdgcn_exp2f(fmaf(S[r], ks.cS, -l2[e]));
-              const float tt = fmaf(Tt[r], ks.fT, 1.f - al[e]);
-              const float pt = pr * tt;
-              const float gt = Gt[r] * ks.fG;
-              wv[o] = pt * ks.cV;
-              wk[o] = pr * gt * ks.c1;
-              wp[o] = pr * ks.c2;
-              wd[o] = fmaf(gt, pt, pr * fmaf(E[r], ks.fE, -dl[e])) * ks.c3;
-            }
-          }
-          f16x8 ok, op, od, ov;
-          to_operand(wk, 1.f, ok, nullptr);
-          to_operand(wp, 1.f, op, nullptr);
-          to_operand(wd, 1.f, od, nullptr);
-          to_operand(wv, 1.f, ov, nullptr);
-          T.x[grp][0][t][l] = ok;
-          T.x[grp][1][t][l] = op;
-          T.x[grp][2][t][l] = od;
-          T.x[grp][3][t][l] = ov;
+          for (int e = 0; e < 8; ++e) w[e] = pr[8 * t + e] * E[8 * t + e];
+          to_operand(w, ks.c3, o, nullptr);
+          T.x[grp][2][t][l] = o;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) w[e] = pr[8 * t + e] * Tt[8 * t + e];
+          to_operand(w, ks.cV, o, nullptr);
+          T.x[grp][3][t][l] = o;
         }
       }
       lds_dma_wait();
