@@ -569,11 +569,29 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         f32x16 S = {}, Gt = {};
+        // K and V row operands of chunk s + 2 are read while the MFMAs of chunk s run; the
+        // scheduling barriers keep the compiler from moving the reads next to their MFMAs
+        f16x8 a[3][2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          a[s][0] = lds_rows(T.k[buf], 32 * kb + ql, 2 * s + hh);
+          a[s][1] = lds_rows(T.v[buf], 32 * kb + ql, 2 * s + hh);
+        }
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-          S = mfma(lds_rows(T.k[buf], 32 * kb + ql, 2 * s + hh), qB[s], S);
-          Gt = mfma(lds_rows(T.v[buf], 32 * kb + ql, 2 * s + hh), gB[s], Gt);
+          if (s + 2 < 8) {
+            a[(s + 2) % 3][0] = lds_rows(T.k[buf], 32 * kb + ql, 2 * (s + 2) + hh);
+            a[(s + 2) % 3][1] = lds_rows(T.v[buf], 32 * kb + ql, 2 * (s + 2) + hh);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          S = mfma(a[s % 3][0], qB[s], S);
+          Gt = mfma(a[s % 3][1], gB[s], Gt);
+          __builtin_amdgcn_sched_barrier(0);
         }
+        // the K^T operands of the first du products, read while the weights are formed
+        f16x8 kc[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) kc[mt] = lds_cols(T.kt[buf], 32 * mt + ql, 4 * kb + hh);
         if (!full) {   // tiles on the causal / window edge only
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -589,8 +607,10 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
           f16x8 hi;
           to_operand(pg + 8 * t, 1.f, hi, nullptr);
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-            accDU[mt] = mfma(lds_cols(T.kt[buf], 32 * mt + ql, 4 * kb + 2 * t + hh), hi, accDU[mt]);
+          for (int mt = 0; mt < 4; ++mt) {
+            accDU[mt] = mfma(kc[mt], hi, accDU[mt]);
+            if (t == 0) kc[mt] = lds_cols(T.kt[buf], 32 * mt + ql, 4 * kb + 2 + hh);
+          }
         }
       }
     }
