@@ -1665,7 +1665,8 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
   if (e != hipSuccess) return e;
   e = launch_absmax(w.st.maxbits, kMaxDO, dout, static_cast<int64_t>(g.B) * g.Tq * g.Hq * kD, stream);
   if (e != hipSuccess) return e;
-  launch_stage_rows(q, false, w.st.maxbits, kMaxQ, w.q16, nullptr, g.B, g.Tq, w.Tq_pad, g.Hq, 0, 0, stream);
+  e = launch_stage_rows(q, false, w.st.maxbits, kMaxQ, w.q16, nullptr, g.B, g.Tq, w.Tq_pad, g.Hq, 0, 0, stream);
+  if (e != hipSuccess) return e;
   e = launch_stage_rows(dout, false, w.st.maxbits, kMaxDO, w.do16, nullptr, g.B, g.Tq, w.Tq_pad, g.Hq, 0, 0, stream);
   if (e != hipSuccess) return e;
 
@@ -1704,6 +1705,17 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
   rp.window = g.window;
   rp.scale = g.scale;
   rp.rows_per_block = 32 * 4 / G;
+  // The kernels for rows < split (few blocks, bound by latency) run on a side lane beside the main
+  // ones: the row kernel beside the du kernel, the key kernel beside the dq kernel.
+  const bool use_side = split > 0 && split < g.Tq;
+  SideLane side = use_side ? side_fork(stream) : SideLane{stream, stream};
+  if (split > 0) {
+    RowParams r = rp;
+    r.row_begin = 0;
+    r.row_end = split;
+    r.n_rb = (split + r.rows_per_block - 1) / r.rows_per_block;
+    hipLaunchKernelGGL((k_bwd_rows_fast<true, true>), dim3(g.B * g.Hkv * r.n_rb), dim3(256), 0, side.stream, r);
+  }
   if (split < g.Tq) {
     RowParams r = rp;
     r.row_begin = split;
@@ -1715,18 +1727,14 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
     hipLaunchKernelGGL(k_bwd_du, dim3(g.B * g.Hkv * r.n_rb), dim3(512), 0, stream, r);
     mark_end(PLX_KERNEL_BWD_ROWS, stream);
   }
-  if (split > 0) {
-    RowParams r = rp;
-    r.row_begin = 0;
-    r.row_end = split;
-    r.n_rb = (split + r.rows_per_block - 1) / r.rows_per_block;
-    hipLaunchKernelGGL((k_bwd_rows_fast<true, true>), dim3(g.B * g.Hkv * r.n_rb), dim3(256), 0, stream, r);
-  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  e = side_join(side);
+  if (e != hipSuccess) return e;
   // fp16 copies of u and dkbar (lo parts for rows < split)
-  launch_stage_rows(w.u32, true, w.st.maxbits, kMaxU, w.u16, split > 0 ? w.u16lo : nullptr, g.B, g.Tq, w.Tq_pad, g.Hq,
-                    split, w.lo_pad, stream);
+  e = launch_stage_rows(w.u32, true, w.st.maxbits, kMaxU, w.u16, split > 0 ? w.u16lo : nullptr, g.B, g.Tq, w.Tq_pad,
+                        g.Hq, split, w.lo_pad, stream);
+  if (e != hipSuccess) return e;
   e = launch_stage_rows(w.dkb32, true, w.st.maxbits, kMaxDKB, w.e16, split > 0 ? w.e16lo : nullptr, g.B, g.Tq,
                         w.Tq_pad, g.Hq, split, w.lo_pad, stream);
   if (e != hipSuccess) return e;
@@ -1773,6 +1781,8 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
     hipLaunchKernelGGL(k_bwd_keys_pipe, dim3(g.B * g.Hkv * k2.n_kb), dim3(512), 0, stream, k2);
     mark_end(PLX_KERNEL_BWD_KEYS, stream);
   }
+  // the key kernel for rows < split adds onto dk, dv: the side lane waits for the key-major kernel
+  side = use_side ? side_fork(stream) : SideLane{stream, stream};
   if (split > 0) {
     // rows < split: only keys those rows can see, accumulated on top
     const int off = g.Tk - g.Tq;
@@ -1785,7 +1795,7 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
       k2.accumulate = 1;
       k2.key_hi = khi;
       k2.n_kb = (khi + 127) / 128;
-      hipLaunchKernelGGL(k_bwd_keys_fast<true>, dim3(g.B * g.Hkv * k2.n_kb), dim3(256), 0, stream, k2);
+      hipLaunchKernelGGL(k_bwd_keys_fast<true>, dim3(g.B * g.Hkv * k2.n_kb), dim3(256), 0, side.stream, k2);
     }
   }
   e = hipGetLastError();
@@ -1816,11 +1826,14 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
     hipLaunchKernelGGL(k_bwd_dq, dim3(g.B * g.Hkv * dp.n_rb), dim3(512), 0, stream, dp);
     mark_end(PLX_KERNEL_BWD_DQ, stream);
   }
+  // dP = sum over rows of x du^T
   const int R = g.B * g.Tq;
   hipLaunchKernelGGL(k_dp_partial, dim3(w.nchunks, g.Hq), dim3(256), 0, stream, w.x32, w.du32, w.part, R, g.Hq);
   const int nred = (g.Hq * kD * kD + 255) / 256;
   hipLaunchKernelGGL(k_dp_reduce, dim3(nred), dim3(256), 0, stream, w.part, dP, w.nchunks, g.Hq);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return side_join(side);
 }
 
 }  // namespace plx

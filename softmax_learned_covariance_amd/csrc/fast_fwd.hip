@@ -476,6 +476,17 @@ hipError_t launch_fast_fwd(const Geom& g, const void* q, const void* k, const vo
     p.scale = g.scale;
     p.rows_per_block = 32 * kWaves / p.G;
   }
+  // rows [0, split) (the same kernel with hi + lo operands) run on the side lane beside the rest
+  const SideLane side = split > 0 && split < g.Tq ? side_fork(stream) : SideLane{stream, stream};
+  if (split > 0) {
+    FwdParams p = base;
+    p.row_begin = 0;
+    p.n_rb = (split + p.rows_per_block - 1) / p.rows_per_block;
+    p.row_end = split;
+    hipLaunchKernelGGL(k_fwd_fast<true>, dim3(g.B * g.Hkv * p.n_rb), dim3(512), 0, side.stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (split < g.Tq) {
     FwdParams p = base;
     p.row_begin = split;
@@ -488,15 +499,7 @@ hipError_t launch_fast_fwd(const Geom& g, const void* q, const void* k, const vo
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (split > 0) {
-    // rows [0, split): the same kernel with hi + lo operands
-    FwdParams p = base;
-    p.row_begin = 0;
-    p.n_rb = (split + p.rows_per_block - 1) / p.rows_per_block;
-    p.row_end = split;
-    hipLaunchKernelGGL(k_fwd_fast<true>, dim3(g.B * g.Hkv * p.n_rb), dim3(512), 0, stream, p);
-    e = hipGetLastError();
-  }
+  e = side_join(side);
   return e;
 }
 

@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "plx_internal.h"
 
 namespace {
@@ -96,6 +98,48 @@ size_t dec_ws(const plx::Geom& g) {
 }  // namespace
 
 namespace plx {
+
+namespace {
+// One non-blocking helper stream per device, created on first use and kept for the life of the
+// process.  It is only ever ordered through events recorded by the call that uses it.
+constexpr int kMaxDevices = 64;
+hipStream_t g_side[kMaxDevices];
+bool g_side_tried[kMaxDevices];
+std::mutex g_side_mutex;
+
+hipStream_t side_stream() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_side_mutex);
+  if (!g_side_tried[dev]) {
+    g_side_tried[dev] = true;
+    if (hipStreamCreateWithFlags(&g_side[dev], hipStreamNonBlocking) != hipSuccess) g_side[dev] = nullptr;
+  }
+  return g_side[dev];
+}
+}  // namespace
+
+SideLane side_fork(hipStream_t main) {
+  SideLane s{main, main};
+  hipStream_t side = side_stream();
+  hipEvent_t ev = nullptr;
+  if (!side || hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) return s;
+  if (hipEventRecord(ev, main) == hipSuccess && hipStreamWaitEvent(side, ev, 0) == hipSuccess) s.stream = side;
+  (void)hipEventDestroy(ev);
+  return s;
+}
+
+hipError_t side_join(const SideLane& s) {
+  if (s.stream == s.main) return hipSuccess;
+  hipEvent_t ev = nullptr;
+  hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(ev, s.stream);
+  if (e == hipSuccess) e = hipStreamWaitEvent(s.main, ev, 0);
+  (void)hipEventDestroy(ev);
+  return e;
+}
+
 void mark_begin(int kernel, hipStream_t stream) {
   if (g_ev_before && kernel == g_ev_kernel) (void)hipEventRecord(g_ev_before, stream);
 }

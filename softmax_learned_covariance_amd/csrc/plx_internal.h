@@ -61,6 +61,17 @@ hipError_t launch_fast_decode(const Geom& g, const void* q, const void* kc, cons
 void mark_begin(int kernel, hipStream_t stream);
 void mark_end(int kernel, hipStream_t stream);
 
+// A second lane of work beside the caller's stream: small kernels that do not depend on the
+// main kernel running at the same time go there.  side_fork makes the helper stream wait for
+// everything enqueued on `main` so far; side_join makes `main` wait for everything enqueued on the
+// helper stream so far.  Without a helper stream (creation failed) `stream` is `main` itself.
+struct SideLane {
+  hipStream_t stream;
+  hipStream_t main;
+};
+SideLane side_fork(hipStream_t main);
+hipError_t side_join(const SideLane& lane);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace plx
