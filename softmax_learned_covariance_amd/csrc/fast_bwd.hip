@@ -1536,52 +1536,69 @@ __global__ __launch_bounds__(256) void k_zero4(float* x, int64_t n4) {
 
 constexpr int kPChunk = 256;  // rows per partial
 
-// block (chunk, head): 256 threads, each owns an 8 x 8 block of the 128 x 128 result
+// block (chunk, head): 4 waves; wave w owns rows 32 w .. 32 w + 31 of the 128 x 128 result as four
+// 32 x 32 fp32 MFMA tiles (v_mfma_f32_32x32x2_f32: two input rows per instruction, the products and
+// sums in fp32).  Tile bt holds the result columns 4 j + bt (j = 0..31), so that a lane loads the du
+// columns 4 j .. 4 j + 3 of a row as one float4 and stores four tiles' values as one float4.
 __global__ __launch_bounds__(256) void k_dp_partial(const float* x32, const float* du32, float* part, int R, int Hq) {
-  __shared__ float xs[32][kD + 4];
-  __shared__ float ds_[32][kD + 4];
-  const int c = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
-  const int bi = (t >> 4) * 8, ai = (t & 15) * 8;
-  float acc[8][8];
+  const int c = blockIdx.x, h = blockIdx.y;
+  const int w = wave_id(), l = threadIdx.x & 63, ql = l & 31, hh = l >> 5;
+  f32x16 acc[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
+  for (int bt = 0; bt < 4; ++bt) acc[bt] = f32x16{};
   const int r_beg = c * kPChunk, r_end = min(R, r_beg + kPChunk);
-  for (int r0 = r_beg; r0 < r_end; r0 += 32) {
-    for (int e = t; e < 32 * kD; e += 256) {
-      const int rr = e / kD, d = e % kD, r = r0 + rr;
-      float xv = 0.f, dv = 0.f;
-      if (r < r_end) {
-        const int64_t o = (static_cast<int64_t>(r) * Hq + h) * kD + d;
-        xv = x32[o];
-        dv = du32[o];
-      }
-      xs[rr][d] = xv;
-      ds_[rr][d] = dv;
+  const int64_t rs = static_cast<int64_t>(Hq) * kD;
+  const float* xp = x32 + h * kD + 32 * w + ql;
+  const float* dp = du32 + h * kD + 4 * ql;
+  // 8 rows per step; the loads of step i + 1 are in flight while step i is multiplied.  Whole
+  // 16-row pairs of steps need no bounds checks; a last partial pair is checked row by row.
+  float a[2][4];
+  float4 bq[2][4];
+  auto load_step = [&](int r0, int sb, bool check) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = r0 + 2 * u + hh;
+      const bool ok = !check || r < r_end;
+      const int64_t o = static_cast<int64_t>(ok ? r : r_beg) * rs;
+      const float xv = xp[o];
+      const float4 dv = *reinterpret_cast<const float4*>(dp + o);
+      a[sb][u] = ok ? xv : 0.f;
+      bq[sb][u] = ok ? dv : float4{0.f, 0.f, 0.f, 0.f};
     }
-    __syncthreads();
-    for (int rr = 0; rr < 32; ++rr) {
-      float xa[8], da[8];
+  };
+  auto mul_step = [&](int sb) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        xa[i] = xs[rr][bi + i];
-        da[i] = ds_[rr][ai + i];
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(xa[i], da[j], acc[i][j]);
+    for (int u = 0; u < 4; ++u) {
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[sb][u], bq[sb][u].x, acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[sb][u], bq[sb][u].y, acc[1], 0, 0, 0);
+      acc[2] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[sb][u], bq[sb][u].z, acc[2], 0, 0, 0);
+      acc[3] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[sb][u], bq[sb][u].w, acc[3], 0, 0, 0);
     }
-    __syncthreads();
+  };
+  const int r_full = r_beg + (r_end - r_beg) / 16 * 16;
+  if (r_beg < r_full) load_step(r_beg, 0, false);
+  for (int r0 = r_beg; r0 < r_full; r0 += 16) {
+    load_step(r0 + 8, 1, false);
+    __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the MFMAs of the other buffer
+    mul_step(0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_step(r0 + 16 < r_full ? r0 + 16 : r0, 0, false);   // (the last step re-reads rows in range)
+    __builtin_amdgcn_sched_barrier(0);
+    mul_step(1);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  float* dst = part + (static_cast<int64_t>(c) * Hq + h) * kD * kD;
+  if (r_full < r_end) {
+    load_step(r_full, 0, true);
+    load_step(r_full + 8, 1, true);
+    mul_step(0);
+    mul_step(1);
+  }
+  // register r of tile bt: result row 32 w + 8 (r / 4) + 4 hh + r % 4, column 4 ql + bt
+  float* dst = part + (static_cast<int64_t>(c) * Hq + h) * kD * kD + 4 * ql;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; j += 4)
-      *reinterpret_cast<float4*>(dst + (bi + i) * kD + ai + j) =
-          float4{acc[i][j], acc[i][j + 1], acc[i][j + 2], acc[i][j + 3]};
+  for (int r = 0; r < 16; ++r)
+    *reinterpret_cast<float4*>(dst + (32 * w + 8 * (r >> 2) + 4 * hh + (r & 3)) * kD) =
+        float4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
 }
 
 __global__ __launch_bounds__(256) void k_dp_reduce(const float* part, float* dP, int nchunks, int Hq) {

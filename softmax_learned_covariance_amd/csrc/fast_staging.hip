@@ -20,13 +20,19 @@ __global__ __launch_bounds__(256) void k_absmax(const u16* q, int64_t nq, const 
   if (src) {
     const int64_t nvec = n / 8;
     const uint4* s4 = reinterpret_cast<const uint4*>(src);
-    for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < nvec; i += 256LL * gridDim.x) {
-      const uint4 w = s4[i];
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    // a block reads 16 KB contiguous per step, four independent 16-byte loads in flight per thread
+    for (int64_t i = blockIdx.x * 1024LL + threadIdx.x; i < nvec; i += 1024LL * gridDim.x) {
+      uint4 w[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        m = fmaxf(m, fabsf(__uint_as_float(ws[j] << 16)));
-        m = fmaxf(m, fabsf(__uint_as_float(ws[j] & 0xffff0000u)));
+      for (int u = 0; u < 4; ++u) w[u] = i + 256 * u < nvec ? s4[i + 256 * u] : uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t ws[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          m = fmaxf(m, fabsf(__uint_as_float(ws[j] << 16)));
+          m = fmaxf(m, fabsf(__uint_as_float(ws[j] & 0xffff0000u)));
+        }
       }
     }
   }
@@ -209,7 +215,7 @@ hipError_t launch_staging(const Staging& s, const void* q, int64_t q_elems, cons
   const int64_t nkv = static_cast<int64_t>(B) * Tk * Hkv * kD;
   const int64_t np = static_cast<int64_t>(Hq) * kD * kD;
   hipLaunchKernelGGL(k_zero_max, dim3(1), dim3(64), 0, stream, s.maxbits);
-  hipLaunchKernelGGL(k_absmax, dim3(512, 4), dim3(256), 0, stream, static_cast<const u16*>(q), q_elems,
+  hipLaunchKernelGGL(k_absmax, dim3(1024, 4), dim3(256), 0, stream, static_cast<const u16*>(q), q_elems,
                      static_cast<const u16*>(k), static_cast<const u16*>(v), nkv,
                      static_cast<const u16*>(P), np, s.maxbits);
   if (B > 0 && s.Tk_pad > 0)
@@ -222,7 +228,7 @@ hipError_t launch_staging(const Staging& s, const void* q, int64_t q_elems, cons
 }
 
 hipError_t launch_absmax(uint32_t* maxbits, int slot, const void* x, int64_t n, hipStream_t stream) {
-  hipLaunchKernelGGL(k_absmax, dim3(256, 1), dim3(256), 0, stream, static_cast<const u16*>(x), n,
+  hipLaunchKernelGGL(k_absmax, dim3(1024, 1), dim3(256), 0, stream, static_cast<const u16*>(x), n,
                      static_cast<const u16*>(nullptr), static_cast<const u16*>(nullptr), int64_t{0},
                      static_cast<const u16*>(nullptr), int64_t{0}, maxbits + slot);
   return hipGetLastError();
