@@ -177,10 +177,26 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
     const int key0 = kt * kKeyTile;
     if (key0 < w_kend && key0 + kKeyTile > w_kbeg) {
       f32x16 S[2] = {f32x16{}, f32x16{}};
+      {
+        // the key-row operands of chunk s + 2 are read while the MFMAs of chunk s run (the
+        // scheduling barriers keep the compiler from moving the reads next to their MFMAs)
+        f16x8 a[3][2];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        S[0] = mfma(lds_k(T, buf, ql, 2 * s + hh), qB[s], S[0]);
-        S[1] = mfma(lds_k(T, buf, 32 + ql, 2 * s + hh), qB[s], S[1]);
+        for (int s = 0; s < 2; ++s) {
+          a[s][0] = lds_k(T, buf, ql, 2 * s + hh);
+          a[s][1] = lds_k(T, buf, 32 + ql, 2 * s + hh);
+        }
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          if (s + 2 < 8) {
+            a[(s + 2) % 3][0] = lds_k(T, buf, ql, 2 * (s + 2) + hh);
+            a[(s + 2) % 3][1] = lds_k(T, buf, 32 + ql, 2 * (s + 2) + hh);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          S[0] = mfma(a[s % 3][0], qB[s], S[0]);
+          S[1] = mfma(a[s % 3][1], qB[s], S[1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       const bool full = key0 + kKeyTile <= w_full_end && key0 >= w_full_beg;
       if (!full) {
@@ -225,19 +241,30 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
           lpart = sum8(pL[i], lpart);
         }
       }
+      {
+        // step n = (mt, i): the V^T and K^T column operands of step n + 2 are read while step n runs
+        f16x8 c[3][2];
+        auto load_c = [&](int n, f16x8(&dst)[2]) {
+          const int mt = n >> 2, i = n & 3;
+          dst[0] = lds_vt(T, buf, 32 * mt + ql, 2 * i + hh);
+          dst[1] = lds_kt(T, buf, 32 * mt + ql, 2 * i + hh);
+        };
+        load_c(0, c[0]);
+        load_c(1, c[1]);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f16x8 av = lds_vt(T, buf, 32 * mt + ql, 2 * i + hh);
-          const f16x8 ak = lds_kt(T, buf, 32 * mt + ql, 2 * i + hh);
-          accO[mt] = mfma(av, pB[i], accO[mt]);
-          accK[mt] = mfma(ak, pB[i], accK[mt]);
+        for (int n = 0; n < 16; ++n) {
+          const int mt = n >> 2, i = n & 3;
+          if (n + 2 < 16) load_c(n + 2, c[(n + 2) % 3]);
+          __builtin_amdgcn_sched_barrier(0);
+          accO[mt] = mfma(c[n % 3][0], pB[i], accO[mt]);
+          accK[mt] = mfma(c[n % 3][1], pB[i], accK[mt]);
           if constexpr (SPLIT) {
-            accO[mt] = mfma(av, pL[i], accO[mt]);
-            accK[mt] = mfma(ak, pL[i], accK[mt]);
+            accO[mt] = mfma(c[n % 3][0], pL[i], accO[mt]);
+            accK[mt] = mfma(c[n % 3][1], pL[i], accK[mt]);
           }
+          __builtin_amdgcn_sched_barrier(0);
         }
+      }
     }
     lds_dma_wait();
     __syncthreads();
@@ -366,12 +393,19 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         f32x16 S = {}, R = {};
+        {
+          f16x8 a[3];   // key-row operands two chunks ahead
+          a[0] = lds_k(T, buf, 32 * kb + ql, hh);
+          a[1] = lds_k(T, buf, 32 * kb + ql, 2 + hh);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const f16x8 a = lds_k(T, buf, 32 * kb + ql, 2 * s + hh);
-          S = mfma(a, qB[s], S);
-          R = mfma(a, uB[s], R);
-          if constexpr (SPLIT) R = mfma(a, uL[s], R);
+          for (int s = 0; s < 8; ++s) {
+            if (s + 2 < 8) a[(s + 2) % 3] = lds_k(T, buf, 32 * kb + ql, 2 * (s + 2) + hh);
+            __builtin_amdgcn_sched_barrier(0);
+            S = mfma(a[s % 3], qB[s], S);
+            R = mfma(a[s % 3], uB[s], R);
+            if constexpr (SPLIT) R = mfma(a[s % 3], uL[s], R);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
         if (!full) {
 #pragma unroll
@@ -396,14 +430,21 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
             rpart = sum8(wL[t], rpart);
           }
         }
+        {
+          // step n = (mt, t): V^T column operands two steps ahead
+          f16x8 c[3];
+          c[0] = lds_vt(T, buf, ql, 4 * kb + hh);
+          c[1] = lds_vt(T, buf, ql, 4 * kb + 2 + hh);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const f16x8 av = lds_vt(T, buf, 32 * mt + ql, 4 * kb + 2 * t + hh);
-            accC[mt] = mfma(av, wB[t], accC[mt]);
-            if constexpr (SPLIT) accC[mt] = mfma(av, wL[t], accC[mt]);
+          for (int n = 0; n < 8; ++n) {
+            const int mt = n >> 1, t = n & 1;
+            if (n + 2 < 8) c[(n + 2) % 3] = lds_vt(T, buf, 32 * ((n + 2) >> 1) + ql, 4 * kb + 2 * ((n + 2) & 1) + hh);
+            __builtin_amdgcn_sched_barrier(0);
+            accC[mt] = mfma(c[n % 3], wB[t], accC[mt]);
+            if constexpr (SPLIT) accC[mt] = mfma(c[n % 3], wL[t], accC[mt]);
+            __builtin_amdgcn_sched_barrier(0);
           }
+        }
       }
     }
     lds_dma_wait();
