@@ -60,27 +60,48 @@ struct __align__(16) DecTiles {
   float corr[kMaxG];
 };
 
-__device__ __forceinline__ void tile_load(const DecParams& p, DecTiles& T, int buf, int b, int g, int key0, int hi,
-                                          int tid) {
-  // 64 keys x 16 chunks of 16 bytes, K and V: 4 + 4 chunks per thread
-  uint4 kr[4], vr[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int ci = tid + 256 * j, r = ci >> 4, c = ci & 15, key = key0 + r;
-    kr[j] = uint4{0u, 0u, 0u, 0u};
-    vr[j] = uint4{0u, 0u, 0u, 0u};
-    if (key < hi) {
-      const int64_t off = ((static_cast<int64_t>(b) * p.L + key) * p.Hkv + g) * kD + c * 8;
-      kr[j] = *reinterpret_cast<const uint4*>(p.kc + off);
-      vr[j] = *reinterpret_cast<const uint4*>(p.vc + off);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int ci = tid + 256 * j, r = ci >> 4, c = ci & 15;
-    *reinterpret_cast<uint4*>(&T.k[buf][r * kRowH + c * 8]) = kr[j];
-    *reinterpret_cast<uint4*>(&T.v[buf][r * kRowH + c * 8]) = vr[j];
-  }
+// A K and V tile (64 keys x 16 chunks of 16 bytes each, 4 + 4 chunks per thread) is fetched into
+// registers one tile ahead and stored into LDS after the current tile's work, so that the loads are in
+// flight while it runs (the loops' barriers are lds_barrier(), which does not wait for them).  Keys at
+// or beyond `hi` read the last valid key (their weight is 0).
+// (eight named registers rather than an array: an array live across the loop stays in scratch memory)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+struct TileRegs {
+  u32x4 k0, k1, k2, k3, v0, v1, v2, v3;
+};
+
+__device__ __forceinline__ u32x4 fetch16(const u16* base, const DecParams& p, int b, int g, int key, int c) {
+  return *reinterpret_cast<const u32x4*>(base + ((static_cast<int64_t>(b) * p.L + key) * p.Hkv + g) * kD + c * 8);
+}
+
+__device__ __forceinline__ TileRegs tile_fetch(const DecParams& p, int b, int g, int key0, int hi, int tid) {
+  const int r = tid >> 4, c = tid & 15;   // chunk j of the thread: row r + 16 j, chunk c
+  const int ka = min(key0 + r, hi - 1), kb = min(key0 + r + 16, hi - 1);
+  const int kc = min(key0 + r + 32, hi - 1), kd = min(key0 + r + 48, hi - 1);
+  TileRegs R;
+  R.k0 = fetch16(p.kc, p, b, g, ka, c);
+  R.k1 = fetch16(p.kc, p, b, g, kb, c);
+  R.k2 = fetch16(p.kc, p, b, g, kc, c);
+  R.k3 = fetch16(p.kc, p, b, g, kd, c);
+  R.v0 = fetch16(p.vc, p, b, g, ka, c);
+  R.v1 = fetch16(p.vc, p, b, g, kb, c);
+  R.v2 = fetch16(p.vc, p, b, g, kc, c);
+  R.v3 = fetch16(p.vc, p, b, g, kd, c);
+  return R;
+}
+
+__device__ __forceinline__ void tile_store(const TileRegs& R, DecTiles& T, int buf, int tid) {
+  const int r = tid >> 4, c = tid & 15;
+  u16* k = &T.k[buf][r * kRowH + c * 8];
+  u16* v = &T.v[buf][r * kRowH + c * 8];
+  *reinterpret_cast<u32x4*>(k) = R.k0;
+  *reinterpret_cast<u32x4*>(k + 16 * kRowH) = R.k1;
+  *reinterpret_cast<u32x4*>(k + 32 * kRowH) = R.k2;
+  *reinterpret_cast<u32x4*>(k + 48 * kRowH) = R.k3;
+  *reinterpret_cast<u32x4*>(v) = R.v0;
+  *reinterpret_cast<u32x4*>(v + 16 * kRowH) = R.v1;
+  *reinterpret_cast<u32x4*>(v + 32 * kRowH) = R.v2;
+  *reinterpret_cast<u32x4*>(v + 48 * kRowH) = R.v3;
 }
 
 // Dot products of the tile's keys with the G vectors in `vecs` (q or u): dots[h][j].
@@ -131,12 +152,17 @@ __global__ __launch_bounds__(256) void k_dec_pass1(DecParams p) {
 #pragma unroll
   for (int h = 0; h < G; ++h) o[h][0] = o[h][1] = kb[h][0] = kb[h][1] = 0.f;
   const int nt = k1 > k0 ? (k1 - k0 + kTile - 1) / kTile : 0;
-  if (nt > 0) tile_load(p, T, 0, b, g, k0, k1, tid);
+  TileRegs R{};
+  if (nt > 0) {
+    R = tile_fetch(p, b, g, k0, k1, tid);
+    tile_store(R, T, 0, tid);
+  }
   __syncthreads();
   for (int it = 0; it < nt; ++it) {
     const int buf = it & 1, key0 = k0 + it * kTile;
+    R = tile_fetch(p, b, g, key0 + kTile, k1, tid);   // (past the last tile: rereads the last key)
     tile_dots<G>(T, buf, T.q, T.s, tid);
-    __syncthreads();
+    lds_barrier();
     const int w = tid >> 6, lane = tid & 63;
     if (w < G) {  // wave h: online softmax of head h over this tile
       const float sv = key0 + lane < k1 ? T.s[w][lane] : -INFINITY;
@@ -154,8 +180,7 @@ __global__ __launch_bounds__(256) void k_dec_pass1(DecParams p) {
       T.w[w][lane] = pv;
       if (lane == 0) T.corr[w] = corr;
     }
-    if (it + 1 < nt) tile_load(p, T, buf ^ 1, b, g, key0 + kTile, k1, tid);
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float cr = T.corr[h];
@@ -179,7 +204,8 @@ __global__ __launch_bounds__(256) void k_dec_pass1(DecParams p) {
         kb[h][1] = fmaf(pw, k1f, kb[h][1]);
       }
     }
-    __syncthreads();
+    tile_store(R, T, buf ^ 1, tid);
+    lds_barrier();
   }
   // reduce the 4 key parts and write the partials
 #pragma unroll
@@ -272,13 +298,18 @@ __global__ __launch_bounds__(256) void k_dec_pass2(DecParams p) {
 #pragma unroll
   for (int h = 0; h < G; ++h) cv[h][0] = cv[h][1] = ws[h] = 0.f;
   const int nt = k1 > k0 ? (k1 - k0 + kTile - 1) / kTile : 0;
-  if (nt > 0) tile_load(p, T, 0, b, g, k0, k1, tid);
+  TileRegs R{};
+  if (nt > 0) {
+    R = tile_fetch(p, b, g, k0, k1, tid);
+    tile_store(R, T, 0, tid);
+  }
   __syncthreads();
   for (int it = 0; it < nt; ++it) {
     const int buf = it & 1, key0 = k0 + it * kTile;
+    R = tile_fetch(p, b, g, key0 + kTile, k1, tid);   // (past the last tile: rereads the last key)
     tile_dots<G>(T, buf, T.q, T.s, tid);
     tile_dots<G>(T, buf, T.u, T.w, tid);
-    __syncthreads();
+    lds_barrier();
     // weights w_j = p_j (u.k_j - alpha), p_j = exp2(s_j - lse)
     for (int e = tid; e < G * kTile; e += 256) {
       const int h = e / kTile, j = e % kTile;
@@ -286,8 +317,7 @@ __global__ __launch_bounds__(256) void k_dec_pass2(DecParams p) {
       const float pw = (key0 + j < k1 && lse > -INFINITY) ? exp2f(T.s[h][j] - lse) : 0.f;
       T.w[h][j] = pw * (T.w[h][j] - st[h][1]);
     }
-    if (it + 1 < nt) tile_load(p, T, buf ^ 1, b, g, key0 + kTile, k1, tid);
-    __syncthreads();
+    lds_barrier();
 #pragma unroll 4
     for (int j = part; j < kTile; j += 4) {
       const uint32_t vw = *reinterpret_cast<const uint32_t*>(&T.v[buf][j * kRowH + 2 * dp]);
@@ -300,7 +330,8 @@ __global__ __launch_bounds__(256) void k_dec_pass2(DecParams p) {
         ws[h] += wj;
       }
     }
-    __syncthreads();
+    tile_store(R, T, buf ^ 1, tid);
+    lds_barrier();
   }
   // partial c = sum w v - (sum w) o
 #pragma unroll
