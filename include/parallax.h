@@ -70,7 +70,7 @@ typedef struct {
   float   softmax_scale;  /* <= 0 selects 1/sqrt(head_dim) */
   int32_t dtype;          /* plx_dtype of q, k, v, P, dout */
   int32_t p_per_query;    /* 0: P is [Hq][d][d]; 1: P is [B][Tq][Hq][d][d] (forward only) */
-  int32_t split_rows;     /* bf16 fast path: query rows < split_rows run on the fp32 path; < 0 selects the default */
+  int32_t split_rows;     /* bf16 fast path: query rows < max(split_rows, 16) use hi + lo fp16 operand pairs (about 22 bits); < 0 selects the default, 256 */
 } plx_attn_desc;
 
 /* Kernels the profiling hook can bracket. */

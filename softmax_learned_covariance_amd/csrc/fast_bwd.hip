@@ -1674,6 +1674,7 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
                            void* ws, hipStream_t stream) {
   // The workspace is sized for the default split; a larger request is clamped to it.
   int split = split_rows < 0 ? bwd_split(g) : split_rows;
+  if (split < kMinSplitRows) split = kMinSplitRows;
   if (split > bwd_split(g)) split = bwd_split(g);
   const BwdWs w = bwd_layout(g, bwd_split(g), ws);
   const int G = g.Hq / g.Hkv;

@@ -488,7 +488,8 @@ hipError_t launch_fast_fwd(const Geom& g, const void* q, const void* k, const vo
                            int split_rows, void* ws, hipStream_t stream) {
   const Staging s = staging_layout(ws, g.B, g.Tk, g.Hkv, g.Hq);
   float* o_ws = reinterpret_cast<float*>(static_cast<char*>(ws) + s.bytes);
-  const int split = split_rows < 0 ? 0 : (split_rows > g.Tq ? g.Tq : split_rows);
+  int split = split_rows < kMinSplitRows ? kMinSplitRows : split_rows;
+  if (split > g.Tq) split = g.Tq;
   hipError_t e = launch_staging(s, q, static_cast<int64_t>(g.B) * g.Tq * g.Hq * kD, k, v, P, g.B, g.Tk,
                                 g.Hkv, g.Hq, stream);
   if (e != hipSuccess) return e;

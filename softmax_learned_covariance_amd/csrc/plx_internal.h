@@ -17,6 +17,12 @@ struct Geom {
   int p_per_query;
 };
 
+// bf16 fast path: the first query rows see only a few keys, and their correction terms cancel
+// badly in single fp16 operands (max|err|/rms near 4e-2 in the first rows' dq and the first
+// keys' dk when they do).  Rows below this bound always take the hi + lo operand pairs, whatever
+// split the caller asks for.
+constexpr int kMinSplitRows = 16;
+
 // ---- generic kernels: fp32 arithmetic on fp32 or bf16 inputs, any head_dim <= 128 ----
 
 // Forward rows [row_begin, row_end) of every (batch, query head).  seqlens (nullable)

@@ -100,7 +100,7 @@ def test_mask_counts(plx, dtype, Tq, Tk, causal, window):
     k = torch.randn((2, Tk, 2, d), generator=g, device="cuda").to(dtype)
     v = torch.randn((2, Tk, 2, d), generator=g, device="cuda").to(dtype)
     P = (torch.randn((4, d, d), generator=g, device="cuda") * 0.02).to(dtype)
-    # split_rows=0 sends every row of the bf16 case through the MFMA kernel
+    # split_rows=0: rows from the 16th on take the single-operand MFMA kernel, the rest its hi + lo twin
     out, lse, _, _ = _run_fwd(plx, q, k, v, P, causal=causal, window=window, split_rows=0)
     got = np.rint(np.exp(host(lse))).astype(np.int64)
     want = np.array([oracle.visible_range(i, Tq, Tk, causal, window)[1] -
@@ -158,6 +158,43 @@ def test_bf16_backward_small(plx, T):
     for name, got, want in zip(("dq", "dk", "dv", "dP"), grads, ref):
         e = rel_err(host(got), want)
         assert e <= BF16_TOL, f"{name}: {e:.2e}"
+
+
+@pytest.mark.parametrize("T,Tk,causal,window,Hkv,split", [
+    (300, 300, True, 100, 8, -1),    # sliding window
+    (260, 260, False, 0, 8, -1),     # bidirectional
+    (129, 257, False, 64, 8, -1),    # bidirectional window, more keys than queries
+    (200, 333, True, 0, 8, -1),      # causal, more keys than queries
+    (333, 200, True, 0, 8, -1),      # causal, more queries than keys
+    (257, 257, True, 0, 16, -1),     # one query head per key/value head
+    (257, 257, True, 0, 4, -1),      # four query heads per key/value head
+    (300, 300, True, 0, 8, 0),       # smallest split: rows >= 16 on single fp16 operands
+])
+def test_bf16_backward_masks_and_groups(plx, T, Tk, causal, window, Hkv, split):
+    w = W.scaled(W.WORKLOADS["train06"], batch=2, seqlen_q=T, seqlen_k=Tk, heads_kv=Hkv)
+    _announce(f"bf16 backward T={T} Tk={Tk} causal={causal} window={window} Hkv={Hkv} split={split}")
+    q, k, v, P, dout = W.make_inputs(w, device="cuda", with_dout=True)
+    kw = dict(causal=causal, window=window, split_rows=split)
+    out, lse, kbar, o = _run_fwd(plx, q, k, v, P, **kw)
+    grads = plx.parallax_attn_bwd(q, k, v, P, out, dout, lse, kbar, o, **kw)
+    torch.cuda.synchronize()
+    ref = oracle.bwd(host(q), host(k), host(v), host(P), host(dout), causal=causal, window=window)
+    for name, got, want in zip(("dq", "dk", "dv", "dP"), grads, ref):
+        e = rel_err(host(got), want)
+        assert e <= BF16_TOL, f"{name}: {e:.2e}"
+
+
+@pytest.mark.parametrize("Hkv", [16, 4, 2])
+def test_bf16_forward_groups(plx, Hkv):
+    """Query heads per key/value head of 1, 4 and 8 (the 0.6B layer uses 2)."""
+    w = W.scaled(W.WORKLOADS["layer06"], batch=2, seqlen_q=450, seqlen_k=450, heads_kv=Hkv)
+    _announce(f"bf16 forward Hkv={Hkv}")
+    q, k, v, P = W.make_inputs(w, device="cuda")
+    for split in (-1, 0):
+        out, lse, kbar, o = _run_fwd(plx, q, k, v, P, window=200, split_rows=split)
+        ref = oracle.fwd(host(q), host(k), host(v), host(P), causal=True, window=200)
+        assert rel_err(host(out), ref[0]) <= BF16_TOL, split
+        assert rel_err(host(kbar), ref[2]) <= BF16_TOL, split
 
 
 def test_empty_and_degenerate(plx):
@@ -280,3 +317,15 @@ def test_decode_seqlens_and_window(plx):
                 ref[b] = oracle.decode(host(q[b:b + 1]), host(kc[b:b + 1, lo:L]), host(vc[b:b + 1, lo:L]), host(P))[0]
         assert np.all(host(out)[2] == 0)
         assert rel_err(host(out), ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("Hkv", [16, 4])
+def test_decode_groups(plx, Hkv):
+    """Decode with one and with four query heads per key/value head."""
+    w = W.scaled(W.WORKLOADS["decode"], batch=3, seqlen_k=2100, heads_kv=Hkv)
+    _announce(f"decode Hkv={Hkv}")
+    q, kc, vc, P = W.make_inputs(w, device="cuda")
+    out = plx.parallax_attn_decode(q, kc, vc, P)
+    torch.cuda.synchronize()
+    ref = oracle.decode(host(q), host(kc), host(vc), host(P))
+    assert rel_err(host(out), ref) <= BF16_TOL
