@@ -1536,12 +1536,27 @@ __global__ __launch_bounds__(256) void k_zero4(float* x, int64_t n4) {
 
 constexpr int kPChunk = 256;  // rows per partial
 
-// block (chunk, head): 4 waves; wave w owns rows 32 w .. 32 w + 31 of the 128 x 128 result as four
-// 32 x 32 fp32 MFMA tiles (v_mfma_f32_32x32x2_f32: two input rows per instruction, the products and
-// sums in fp32).  Tile bt holds the result columns 4 j + bt (j = 0..31), so that a lane loads the du
-// columns 4 j .. 4 j + 3 of a row as one float4 and stores four tiles' values as one float4.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// x = hi + lo, hi = bf16(x), lo = bf16(x - hi): about 16 significant bits; with fp32 accumulation
+// hi.hi + hi.lo + lo.hi is a product good to about 2^-16 relative.
+__device__ __forceinline__ void split_bf16(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 t = static_cast<__bf16>(x[e]);
+    hi[e] = t;
+    lo[e] = static_cast<__bf16>(x[e] - static_cast<float>(t));
+  }
+}
+
+// block (head, chunk): 4 waves; wave w owns rows 32 w .. 32 w + 31 of the 128 x 128 result as four
+// 32 x 32 tiles, each summed over 16 input rows per step by three bf16 MFMAs (hi.hi, hi.lo, lo.hi;
+// v_mfma_f32_32x32x16_bf16, fp32 accumulation).  Lane (ql, hh) takes rows 8 hh .. 8 hh + 7 of a
+// step: x at column 32 w + ql, du at columns 4 ql .. 4 ql + 3 (one float4 a row), so that tile bt
+// holds the result columns 4 j + bt (j = 0..31) and a lane stores four tiles' values as one float4.
 __global__ __launch_bounds__(256) void k_dp_partial(const float* x32, const float* du32, float* part, int R, int Hq) {
-  const int c = blockIdx.x, h = blockIdx.y;
+  // the heads of one row chunk are consecutive blocks, so they read the same rows at about the same time
+  const int h = blockIdx.x % Hq, c = blockIdx.x / Hq;
   const int w = wave_id(), l = threadIdx.x & 63, ql = l & 31, hh = l >> 5;
   f32x16 acc[4];
 #pragma unroll
@@ -1550,46 +1565,60 @@ __global__ __launch_bounds__(256) void k_dp_partial(const float* x32, const floa
   const int64_t rs = static_cast<int64_t>(Hq) * kD;
   const float* xp = x32 + h * kD + 32 * w + ql;
   const float* dp = du32 + h * kD + 4 * ql;
-  // 8 rows per step; the loads of step i + 1 are in flight while step i is multiplied.  Whole
-  // 16-row pairs of steps need no bounds checks; a last partial pair is checked row by row.
-  float a[2][4];
-  float4 bq[2][4];
+  // The loads of step i + 1 are in flight while step i is converted and multiplied.  Whole 32-row
+  // pairs of steps need no bounds checks; in a last partial pair, rows past the chunk read row
+  // r_beg and count as zero.
+  float xa[2][8];
+  float4 db[2][8];
   auto load_step = [&](int r0, int sb, bool check) {
+    const float* xr = xp + static_cast<int64_t>(r0 + 8 * hh) * rs;
+    const float* dr = dp + static_cast<int64_t>(r0 + 8 * hh) * rs;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = r0 + 2 * u + hh;
-      const bool ok = !check || r < r_end;
-      const int64_t o = static_cast<int64_t>(ok ? r : r_beg) * rs;
-      const float xv = xp[o];
-      const float4 dv = *reinterpret_cast<const float4*>(dp + o);
-      a[sb][u] = ok ? xv : 0.f;
-      bq[sb][u] = ok ? dv : float4{0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < 8; ++e) {
+      if (!check) {
+        xa[sb][e] = xr[e * rs];
+        db[sb][e] = *reinterpret_cast<const float4*>(dr + e * rs);
+      } else {
+        const int r = r0 + 8 * hh + e;
+        const bool ok = r < r_end;
+        const int64_t o = static_cast<int64_t>(ok ? r : r_beg) * rs;
+        const float xv = xp[o];
+        const float4 dv = *reinterpret_cast<const float4*>(dp + o);
+        xa[sb][e] = ok ? xv : 0.f;
+        db[sb][e] = ok ? dv : float4{0.f, 0.f, 0.f, 0.f};
+      }
     }
   };
   auto mul_step = [&](int sb) {
+    bf16x8 xh, xl;
+    split_bf16(xa[sb], xh, xl);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[sb][u], bq[sb][u].x, acc[0], 0, 0, 0);
-      acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[sb][u], bq[sb][u].y, acc[1], 0, 0, 0);
-      acc[2] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[sb][u], bq[sb][u].z, acc[2], 0, 0, 0);
-      acc[3] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[sb][u], bq[sb][u].w, acc[3], 0, 0, 0);
+    for (int bt = 0; bt < 4; ++bt) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = bt == 0 ? db[sb][e].x : bt == 1 ? db[sb][e].y : bt == 2 ? db[sb][e].z : db[sb][e].w;
+      bf16x8 dh, dl;
+      split_bf16(v, dh, dl);
+      acc[bt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xh, dh, acc[bt], 0, 0, 0);
+      acc[bt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xh, dl, acc[bt], 0, 0, 0);
+      acc[bt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xl, dh, acc[bt], 0, 0, 0);
     }
   };
-  const int r_full = r_beg + (r_end - r_beg) / 16 * 16;
+  const int r_full = r_beg + (r_end - r_beg) / 32 * 32;
   if (r_beg < r_full) load_step(r_beg, 0, false);
-  for (int r0 = r_beg; r0 < r_full; r0 += 16) {
-    load_step(r0 + 8, 1, false);
-    __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the MFMAs of the other buffer
+  for (int r0 = r_beg; r0 < r_full; r0 += 32) {
+    load_step(r0 + 16, 1, false);
+    __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the work on the other buffer
     mul_step(0);
     __builtin_amdgcn_sched_barrier(0);
-    load_step(r0 + 16 < r_full ? r0 + 16 : r0, 0, false);   // (the last step re-reads rows in range)
+    load_step(r0 + 32 < r_full ? r0 + 32 : r0, 0, false);   // (the last pair re-reads rows in range)
     __builtin_amdgcn_sched_barrier(0);
     mul_step(1);
     __builtin_amdgcn_sched_barrier(0);
   }
   if (r_full < r_end) {
     load_step(r_full, 0, true);
-    load_step(r_full + 8, 1, true);
+    load_step(r_full + 16, 1, true);
     mul_step(0);
     mul_step(1);
   }
@@ -1604,8 +1633,17 @@ __global__ __launch_bounds__(256) void k_dp_partial(const float* x32, const floa
 __global__ __launch_bounds__(256) void k_dp_reduce(const float* part, float* dP, int nchunks, int Hq) {
   const int64_t n = static_cast<int64_t>(Hq) * kD * kD;
   for (int64_t e = blockIdx.x * 256LL + threadIdx.x; e < n; e += 256LL * gridDim.x) {
+    // in chunk order; eight loads are issued before their adds
     float s = 0.f;
-    for (int c = 0; c < nchunks; ++c) s += part[c * n + e];
+    int c = 0;
+    for (; c + 8 <= nchunks; c += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = part[(c + u) * n + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; c < nchunks; ++c) s += part[c * n + e];
     dP[e] = s;
   }
 }
@@ -1846,7 +1884,7 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
   }
   // dP = sum over rows of x du^T
   const int R = g.B * g.Tq;
-  hipLaunchKernelGGL(k_dp_partial, dim3(w.nchunks, g.Hq), dim3(256), 0, stream, w.x32, w.du32, w.part, R, g.Hq);
+  hipLaunchKernelGGL(k_dp_partial, dim3(g.Hq * w.nchunks), dim3(256), 0, stream, w.x32, w.du32, w.part, R, g.Hq);
   const int nred = (g.Hq * kD * kD + 255) / 256;
   hipLaunchKernelGGL(k_dp_reduce, dim3(nred), dim3(256), 0, stream, w.part, dP, w.nchunks, g.Hq);
   e = hipGetLastError();

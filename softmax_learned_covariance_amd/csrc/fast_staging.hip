@@ -9,13 +9,21 @@ __global__ __launch_bounds__(64) void k_zero_max(uint32_t* maxbits) {
   if (threadIdx.x < 16) maxbits[threadIdx.x] = 0u;
 }
 
-// blockIdx.y selects the tensor: 0 q, 1 k, 2 v, 3 P.  Elements are bf16, counts multiples of 8.
+// Blocks per tensor slice.  Every block ends in one atomicMax on the same few words, and those
+// serialise in L2, so fewer and longer blocks are faster than many short ones.
+constexpr int kAbsmaxBlocks = 256;
+
+// Max |x| of q, k, v and P into maxbits[0..3].  Elements are bf16, counts multiples of 8.
 __global__ __launch_bounds__(256) void k_absmax(const u16* q, int64_t nq, const u16* k, const u16* v,
                                                 int64_t nkv, const u16* P, int64_t np,
                                                 uint32_t* maxbits) {
-  const int which = blockIdx.y;
-  const u16* src = which == 0 ? q : which == 1 ? k : which == 2 ? v : P;
-  const int64_t n = which == 0 ? nq : which == 3 ? np : nkv;
+  // grid.y: 0 and 1 the two halves of q (q is G times larger than k or v, so the halves keep the
+  // slices about even), 2 k, 3 v, 4 P; grid.y = 1 for a single tensor in q
+  const int part = blockIdx.y;
+  const int64_t qh = gridDim.y == 1 ? nq : (nq / 16) * 8;   // first half of q, whole 16-byte vectors
+  const u16* src = part == 0 ? q : part == 1 ? (q ? q + qh : nullptr) : part == 2 ? k : part == 3 ? v : P;
+  const int64_t n = part == 0 ? qh : part == 1 ? nq - qh : part == 4 ? np : nkv;
+  const int which = part <= 1 ? 0 : part - 1;
   float m = 0.f;
   if (src) {
     const int64_t nvec = n / 8;
@@ -215,7 +223,7 @@ hipError_t launch_staging(const Staging& s, const void* q, int64_t q_elems, cons
   const int64_t nkv = static_cast<int64_t>(B) * Tk * Hkv * kD;
   const int64_t np = static_cast<int64_t>(Hq) * kD * kD;
   hipLaunchKernelGGL(k_zero_max, dim3(1), dim3(64), 0, stream, s.maxbits);
-  hipLaunchKernelGGL(k_absmax, dim3(1024, 4), dim3(256), 0, stream, static_cast<const u16*>(q), q_elems,
+  hipLaunchKernelGGL(k_absmax, dim3(kAbsmaxBlocks, 5), dim3(256), 0, stream, static_cast<const u16*>(q), q_elems,
                      static_cast<const u16*>(k), static_cast<const u16*>(v), nkv,
                      static_cast<const u16*>(P), np, s.maxbits);
   if (B > 0 && s.Tk_pad > 0)
@@ -228,7 +236,7 @@ hipError_t launch_staging(const Staging& s, const void* q, int64_t q_elems, cons
 }
 
 hipError_t launch_absmax(uint32_t* maxbits, int slot, const void* x, int64_t n, hipStream_t stream) {
-  hipLaunchKernelGGL(k_absmax, dim3(1024, 1), dim3(256), 0, stream, static_cast<const u16*>(x), n,
+  hipLaunchKernelGGL(k_absmax, dim3(kAbsmaxBlocks, 1), dim3(256), 0, stream, static_cast<const u16*>(x), n,
                      static_cast<const u16*>(nullptr), static_cast<const u16*>(nullptr), int64_t{0},
                      static_cast<const u16*>(nullptr), int64_t{0}, maxbits + slot);
   return hipGetLastError();
