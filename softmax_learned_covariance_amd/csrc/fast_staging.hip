@@ -62,7 +62,8 @@ __global__ __launch_bounds__(256) void k_stage_kv(const u16* k, const u16* v, co
   constexpr int LD = kD + 2;  // padded LDS row (halves) for conflict-light column reads
   __shared__ _Float16 ks[kKeyTile * LD];
   __shared__ _Float16 vs[kKeyTile * LD];
-  const int kt = blockIdx.x, g = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  // the kv heads of one key tile are consecutive blocks, so they read the same rows together
+  const int g = blockIdx.x % Hkv, kt = blockIdx.x / Hkv, b = blockIdx.z, t = threadIdx.x;
   const int key0 = kt * kKeyTile;
   const float sK = range_scale(__uint_as_float(maxbits[1]));
   const float sV = range_scale(__uint_as_float(maxbits[2]));
@@ -159,7 +160,8 @@ __global__ __launch_bounds__(256) void k_stage_rows(const void* src, const uint3
                                                     int lo_rows, int lo_pad) {
   __shared__ uint2 hs[16 * 32 * 2];   // [chunk][row][half of the chunk]
   __shared__ uint2 ls[16 * 32 * 2];
-  const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  // the heads of one row tile are consecutive blocks, so they read the same rows together
+  const int h = blockIdx.x % Hq, qt = blockIdx.x / Hq, b = blockIdx.z, t = threadIdx.x;
   const int r0 = qt * 32;
   const float sc = range_scale(__uint_as_float(maxbits[max_idx]));
   const bool want_lo = lo != nullptr && r0 < lo_rows;
@@ -227,7 +229,7 @@ hipError_t launch_staging(const Staging& s, const void* q, int64_t q_elems, cons
                      static_cast<const u16*>(k), static_cast<const u16*>(v), nkv,
                      static_cast<const u16*>(P), np, s.maxbits);
   if (B > 0 && s.Tk_pad > 0)
-    hipLaunchKernelGGL(k_stage_kv, dim3(s.Tk_pad / kKeyTile, Hkv, B), dim3(256), 0, stream,
+    hipLaunchKernelGGL(k_stage_kv, dim3(Hkv * (s.Tk_pad / kKeyTile), 1, B), dim3(256), 0, stream,
                        static_cast<const u16*>(k), static_cast<const u16*>(v), s.maxbits, s.k16, s.k16t,
                        s.v16t, s.v16, Tk, s.Tk_pad, Hkv);
   hipLaunchKernelGGL(k_stage_p, dim3(Hq), dim3(256), 0, stream, static_cast<const u16*>(P), s.maxbits, s.p16t,
@@ -246,7 +248,7 @@ hipError_t launch_stage_rows(const void* src, bool f32, const uint32_t* maxbits,
                              _Float16* lo, int B, int Tq, int Tq_pad, int Hq, int lo_rows, int lo_pad,
                              hipStream_t stream) {
   if (B == 0 || Tq_pad == 0) return hipSuccess;
-  dim3 grid(Tq_pad / 32, Hq, B);
+  dim3 grid(Hq * (Tq_pad / 32), 1, B);
   if (f32)
     hipLaunchKernelGGL(k_stage_rows<true>, grid, dim3(256), 0, stream, src, maxbits, max_idx, dst, lo, Tq, Tq_pad,
                        Hq, lo_rows, lo_pad);
