@@ -765,14 +765,24 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
     rs[64] = delta;
   }
   {
-    // per-tensor maxima for the key-major pass (rows outside the range contribute 0)
+    // per-tensor maxima for the key-major pass (rows outside the range contribute 0), combined over
+    // the block first: the atomics all go to the same few words, where they serialise
+    __shared__ float red[4][8];
     const float wu = wave_max(row_ok ? umax : 0.f), we = wave_max(row_ok ? emax : 0.f);
     const float wd = wave_max(row_ok ? fabsf(delta) : 0.f), wa = wave_max(row_ok ? fabsf(alpha) : 0.f);
     if (l == 0) {
-      atomicMax(&p.maxbits[kMaxU], __float_as_uint(wu));
-      atomicMax(&p.maxbits[kMaxDKB], __float_as_uint(we));
-      atomicMax(&p.maxbits[kMaxDelta], __float_as_uint(wd));
-      atomicMax(&p.maxbits[kMaxAlpha], __float_as_uint(wa));
+      red[0][w] = wu;
+      red[1][w] = we;
+      red[2][w] = wd;
+      red[3][w] = wa;
+    }
+    __syncthreads();
+    if (tid < 4) {
+      float m = 0.f;
+#pragma unroll
+      for (int v = 0; v < 8; ++v) m = fmaxf(m, red[tid][v]);
+      const int slot = tid == 0 ? kMaxU : tid == 1 ? kMaxDKB : tid == 2 ? kMaxDelta : kMaxAlpha;
+      atomicMax(&p.maxbits[slot], __float_as_uint(m));
     }
   }
 }

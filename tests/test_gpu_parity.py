@@ -234,6 +234,22 @@ def test_determinism(plx):
         assert torch.equal(x, y)
 
 
+def test_split_rows_floor(plx):
+    """The first 16 query rows always take the hi + lo operand pairs: split_rows 0 and 16 give the same bits."""
+    _announce("split_rows floor")
+    w = W.scaled(W.WORKLOADS["train06"], batch=1, seqlen_q=300, seqlen_k=300)
+    q, k, v, P, dout = W.make_inputs(w, device="cuda", with_dout=True)
+    a = _run_fwd(plx, q, k, v, P, split_rows=0)
+    b = _run_fwd(plx, q, k, v, P, split_rows=16)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    ga = plx.parallax_attn_bwd(q, k, v, P, *a[:1], dout, *a[1:], split_rows=0)
+    gb = plx.parallax_attn_bwd(q, k, v, P, *b[:1], dout, *b[1:], split_rows=16)
+    torch.cuda.synchronize()
+    for x, y in zip(ga, gb):
+        assert torch.equal(x, y)
+
+
 # --------------------------------------------------------------------------------------
 # full-size workloads, sampled rows
 # --------------------------------------------------------------------------------------
