@@ -48,8 +48,8 @@ __device__ __forceinline__ void seq_range(const DecParams& p, int b, int& lo, in
 struct __align__(16) DecTiles {
   union {
     struct {
-      u16 k[2][kTile * kRowH];
-      u16 v[2][kTile * kRowH];
+      u16 k[1][kTile * kRowH];
+      u16 v[1][kTile * kRowH];
     };
     float red[4][kMaxG][kD * 2];   // after the key loop: the 4 key parts of each accumulator
   };
@@ -60,9 +60,11 @@ struct __align__(16) DecTiles {
   float corr[kMaxG];
 };
 
-// A K and V tile (64 keys x 16 chunks of 16 bytes each, 4 + 4 chunks per thread) is fetched into
-// registers one tile ahead and stored into LDS after the current tile's work, so that the loads are in
-// flight while it runs (the loops' barriers are lds_barrier(), which does not wait for them).  Keys at
+// One K and V tile in LDS (about 41 KB with the rest, so three workgroups fit a CU; measured, three
+// stream the cache faster than two with double-buffered tiles, and than four).  The next tile (64
+// keys x 16 chunks of 16 bytes each, 4 + 4 chunks per thread) is fetched into registers at the start
+// of an iteration and stored into LDS after the current tile's work and a barrier, so that the loads
+// are in flight while it runs (the loops' barriers are lds_barrier(), which does not wait for them).  Keys at
 // or beyond `hi` read the last valid key (their weight is 0).
 // (eight named registers rather than an array: an array live across the loop stays in scratch memory)
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -159,7 +161,7 @@ __global__ __launch_bounds__(256) void k_dec_pass1(DecParams p) {
   }
   __syncthreads();
   for (int it = 0; it < nt; ++it) {
-    const int buf = it & 1, key0 = k0 + it * kTile;
+    const int buf = 0, key0 = k0 + it * kTile;
     R = tile_fetch(p, b, g, key0 + kTile, k1, tid);   // (past the last tile: rereads the last key)
     tile_dots<G>(T, buf, T.q, T.s, tid);
     lds_barrier();
@@ -204,7 +206,8 @@ __global__ __launch_bounds__(256) void k_dec_pass1(DecParams p) {
         kb[h][1] = fmaf(pw, k1f, kb[h][1]);
       }
     }
-    tile_store(R, T, buf ^ 1, tid);
+    lds_barrier();
+    tile_store(R, T, 0, tid);
     lds_barrier();
   }
   // reduce the 4 key parts and write the partials
@@ -305,7 +308,7 @@ __global__ __launch_bounds__(256) void k_dec_pass2(DecParams p) {
   }
   __syncthreads();
   for (int it = 0; it < nt; ++it) {
-    const int buf = it & 1, key0 = k0 + it * kTile;
+    const int buf = 0, key0 = k0 + it * kTile;
     R = tile_fetch(p, b, g, key0 + kTile, k1, tid);   // (past the last tile: rereads the last key)
     tile_dots<G>(T, buf, T.q, T.s, tid);
     tile_dots<G>(T, buf, T.u, T.w, tid);
@@ -330,7 +333,8 @@ __global__ __launch_bounds__(256) void k_dec_pass2(DecParams p) {
         ws[h] += wj;
       }
     }
-    tile_store(R, T, buf ^ 1, tid);
+    lds_barrier();
+    tile_store(R, T, 0, tid);
     lds_barrier();
   }
   // partial c = sum w v - (sum w) o
