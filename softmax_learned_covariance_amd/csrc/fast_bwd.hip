@@ -1731,10 +1731,6 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
   if (e != hipSuccess) return e;
   e = launch_absmax(w.st.maxbits, kMaxDO, dout, static_cast<int64_t>(g.B) * g.Tq * g.Hq * kD, stream);
   if (e != hipSuccess) return e;
-  e = launch_stage_rows(q, false, w.st.maxbits, kMaxQ, w.q16, nullptr, g.B, g.Tq, w.Tq_pad, g.Hq, 0, 0, stream);
-  if (e != hipSuccess) return e;
-  e = launch_stage_rows(dout, false, w.st.maxbits, kMaxDO, w.do16, nullptr, g.B, g.Tq, w.Tq_pad, g.Hq, 0, 0, stream);
-  if (e != hipSuccess) return e;
 
   // row statistics of padded rows stay 0 (the key-major kernel reads whole 32-row tiles)
   hipLaunchKernelGGL(k_zero4, dim3(256), dim3(256), 0, stream, w.rstat, static_cast<int64_t>(w.rstat_n / 4));
@@ -1772,9 +1768,16 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
   rp.scale = g.scale;
   rp.rows_per_block = 32 * 4 / G;
   // The kernels for rows < split (few blocks, bound by latency) run on a side lane beside the main
-  // ones: the row kernel beside the du kernel, the key kernel beside the dq kernel.
+  // ones: the row kernel beside the du kernel, the key kernel beside the dq kernel.  The fp16 query
+  // tiles of q and dout are first read by the key-major kernel, so their staging also runs on the
+  // side lane beside du.
   const bool use_side = split > 0 && split < g.Tq;
   SideLane side = use_side ? side_fork(stream) : SideLane{stream, stream};
+  e = launch_stage_rows(q, false, w.st.maxbits, kMaxQ, w.q16, nullptr, g.B, g.Tq, w.Tq_pad, g.Hq, 0, 0, side.stream);
+  if (e != hipSuccess) return e;
+  e = launch_stage_rows(dout, false, w.st.maxbits, kMaxDO, w.do16, nullptr, g.B, g.Tq, w.Tq_pad, g.Hq, 0, 0,
+                        side.stream);
+  if (e != hipSuccess) return e;
   if (split > 0) {
     RowParams r = rp;
     r.row_begin = 0;
