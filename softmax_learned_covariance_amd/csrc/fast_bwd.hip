@@ -1726,10 +1726,8 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
   if (split > bwd_split(g)) split = bwd_split(g);
   const BwdWs w = bwd_layout(g, bwd_split(g), ws);
   const int G = g.Hq / g.Hkv;
-  hipError_t e = launch_staging(w.st, q, static_cast<int64_t>(g.B) * g.Tq * g.Hq * kD, k, v, P, g.B, g.Tk, g.Hkv,
-                                g.Hq, stream);
-  if (e != hipSuccess) return e;
-  e = launch_absmax(w.st.maxbits, kMaxDO, dout, static_cast<int64_t>(g.B) * g.Tq * g.Hq * kD, stream);
+  const int64_t q_elems = static_cast<int64_t>(g.B) * g.Tq * g.Hq * kD;
+  hipError_t e = launch_staging(w.st, q, q_elems, k, v, P, g.B, g.Tk, g.Hkv, g.Hq, stream, dout, q_elems, kMaxDO);
   if (e != hipSuccess) return e;
 
   // row statistics of padded rows stay 0 (the key-major kernel reads whole 32-row tiles)

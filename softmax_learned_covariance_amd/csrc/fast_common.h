@@ -238,18 +238,17 @@ inline Staging staging_layout(void* ws, int B, int Tk, int Hkv, int Hq, bool bac
   return s;
 }
 
-// max-abs of one more bf16 tensor into maxbits[slot].
-hipError_t launch_absmax(uint32_t* maxbits, int slot, const void* x, int64_t n, hipStream_t stream);
-
 // Query-side fp16 copies in the row-tile layout (see k_stage_rows in fast_staging.hip).
 hipError_t launch_stage_rows(const void* src, bool f32, const uint32_t* maxbits, int max_idx, _Float16* dst,
                              _Float16* lo, int B, int Tq, int Tq_pad, int Hq, int lo_rows, int lo_pad,
                              hipStream_t stream);
 
-// Launches the staging kernels: max-abs of q (rows [0, Tq)), k, v, P, then the fp16 copies.
-// q may be nullptr (decode stages q itself).
+// Launches the staging kernels: max-abs of q (rows [0, Tq)), k, v, P (and of one more bf16 tensor,
+// `extra`, into maxbits[extra_slot]) in one launch, then the fp16 copies.  q may be nullptr (decode
+// stages q itself).
 hipError_t launch_staging(const Staging& s, const void* q, int64_t q_elems, const void* k,
                           const void* v, const void* P, int B, int Tk, int Hkv, int Hq,
-                          hipStream_t stream);
+                          hipStream_t stream, const void* extra = nullptr, int64_t extra_elems = 0,
+                          int extra_slot = 0);
 
 }  // namespace plx

@@ -13,17 +13,36 @@ __global__ __launch_bounds__(64) void k_zero_max(uint32_t* maxbits) {
 // serialise in L2, so fewer and longer blocks are faster than many short ones.
 constexpr int kAbsmaxBlocks = 256;
 
-// Max |x| of q, k, v and P into maxbits[0..3].  Elements are bf16, counts multiples of 8.
-__global__ __launch_bounds__(256) void k_absmax(const u16* q, int64_t nq, const u16* k, const u16* v,
-                                                int64_t nkv, const u16* P, int64_t np,
-                                                uint32_t* maxbits) {
-  // grid.y: 0 and 1 the two halves of q (q is G times larger than k or v, so the halves keep the
-  // slices about even), 2 k, 3 v, 4 P; grid.y = 1 for a single tensor in q
+// Up to eight bf16 tensor slices, each with the maxbits slot its max |x| goes to.
+struct AbsmaxJob {
+  const u16* src[8];
+  int64_t n[8];   // elements, a multiple of 8
+  int slot[8];
+  int parts;
+};
+
+// Adds the slices of `t` to the job: large tensors in two halves, so that the slices of one launch
+// are about even (q and dout are G times larger than k and v).
+__host__ inline void absmax_add(AbsmaxJob& j, const void* t, int64_t n, int slot, bool halve) {
+  if (t == nullptr || n <= 0) return;
+  const u16* p = static_cast<const u16*>(t);
+  const int64_t h = halve ? (n / 16) * 8 : n;   // whole 16-byte vectors
+  j.src[j.parts] = p;
+  j.n[j.parts] = h;
+  j.slot[j.parts++] = slot;
+  if (h < n) {
+    j.src[j.parts] = p + h;
+    j.n[j.parts] = n - h;
+    j.slot[j.parts++] = slot;
+  }
+}
+
+// Max |x| of each slice (grid.y) into maxbits[slot].
+__global__ __launch_bounds__(256) void k_absmax(AbsmaxJob job, uint32_t* maxbits) {
   const int part = blockIdx.y;
-  const int64_t qh = gridDim.y == 1 ? nq : (nq / 16) * 8;   // first half of q, whole 16-byte vectors
-  const u16* src = part == 0 ? q : part == 1 ? (q ? q + qh : nullptr) : part == 2 ? k : part == 3 ? v : P;
-  const int64_t n = part == 0 ? qh : part == 1 ? nq - qh : part == 4 ? np : nkv;
-  const int which = part <= 1 ? 0 : part - 1;
+  const u16* src = job.src[part];
+  const int64_t n = job.n[part];
+  const int which = job.slot[part];
   float m = 0.f;
   if (src) {
     const int64_t nvec = n / 8;
@@ -221,13 +240,18 @@ __global__ __launch_bounds__(256) void k_stage_rows(const void* src, const uint3
 
 hipError_t launch_staging(const Staging& s, const void* q, int64_t q_elems, const void* k,
                           const void* v, const void* P, int B, int Tk, int Hkv, int Hq,
-                          hipStream_t stream) {
+                          hipStream_t stream, const void* extra, int64_t extra_elems, int extra_slot) {
   const int64_t nkv = static_cast<int64_t>(B) * Tk * Hkv * kD;
   const int64_t np = static_cast<int64_t>(Hq) * kD * kD;
   hipLaunchKernelGGL(k_zero_max, dim3(1), dim3(64), 0, stream, s.maxbits);
-  hipLaunchKernelGGL(k_absmax, dim3(kAbsmaxBlocks, 5), dim3(256), 0, stream, static_cast<const u16*>(q), q_elems,
-                     static_cast<const u16*>(k), static_cast<const u16*>(v), nkv,
-                     static_cast<const u16*>(P), np, s.maxbits);
+  AbsmaxJob job{};
+  absmax_add(job, q, q_elems, kMaxQ, true);
+  absmax_add(job, k, nkv, kMaxK, false);
+  absmax_add(job, v, nkv, kMaxV, false);
+  absmax_add(job, P, np, kMaxP, false);
+  absmax_add(job, extra, extra_elems, extra_slot, true);
+  if (job.parts > 0)
+    hipLaunchKernelGGL(k_absmax, dim3(kAbsmaxBlocks, job.parts), dim3(256), 0, stream, job, s.maxbits);
   if (B > 0 && s.Tk_pad > 0)
     hipLaunchKernelGGL(k_stage_kv, dim3(Hkv * (s.Tk_pad / kKeyTile), 1, B), dim3(256), 0, stream,
                        static_cast<const u16*>(k), static_cast<const u16*>(v), s.maxbits, s.k16, s.k16t,
@@ -237,12 +261,6 @@ hipError_t launch_staging(const Staging& s, const void* q, int64_t q_elems, cons
   return hipGetLastError();
 }
 
-hipError_t launch_absmax(uint32_t* maxbits, int slot, const void* x, int64_t n, hipStream_t stream) {
-  hipLaunchKernelGGL(k_absmax, dim3(kAbsmaxBlocks, 1), dim3(256), 0, stream, static_cast<const u16*>(x), n,
-                     static_cast<const u16*>(nullptr), static_cast<const u16*>(nullptr), int64_t{0},
-                     static_cast<const u16*>(nullptr), int64_t{0}, maxbits + slot);
-  return hipGetLastError();
-}
 
 hipError_t launch_stage_rows(const void* src, bool f32, const uint32_t* maxbits, int max_idx, _Float16* dst,
                              _Float16* lo, int B, int Tq, int Tq_pad, int Hq, int lo_rows, int lo_pad,
