@@ -256,6 +256,28 @@ def test_bf16_generic_head_dims(plx, d):
     assert rel_err(host(outd), oracle.decode(host(qd), host(kc), host(vc), host(Pd))) <= BF16_TOL
 
 
+@pytest.mark.parametrize("B,T,Hq,Hkv", [(1, 200, 6, 3), (3, 5, 2, 1), (1, 97, 8, 2)])
+def test_bf16_odd_shapes(plx, B, T, Hq, Hkv):
+    """(batch, kv head) counts that are not a multiple of 8 (the other block order), rows fewer than the
+    16 that always take the hi + lo operands, and four query heads per key/value head."""
+    _announce(f"bf16 odd shapes B={B} T={T} Hq={Hq} Hkv={Hkv}")
+    w = W.scaled(W.WORKLOADS["train06"], batch=B, seqlen_q=T, seqlen_k=T, heads_q=Hq, heads_kv=Hkv)
+    q, k, v, P, dout = W.make_inputs(w, device="cuda", with_dout=True)
+    out, lse, kbar, o = _run_fwd(plx, q, k, v, P)
+    grads = plx.parallax_attn_bwd(q, k, v, P, out, dout, lse, kbar, o)
+    torch.cuda.synchronize()
+    assert rel_err(host(out), oracle.fwd(host(q), host(k), host(v), host(P), causal=True)[0]) <= BF16_TOL
+    rb = oracle.bwd(host(q), host(k), host(v), host(P), host(dout), causal=True)
+    for name, got, want in zip(("dq", "dk", "dv", "dP"), grads, rb):
+        e = rel_err(host(got), want)
+        assert e <= BF16_TOL, f"{name}: {e:.2e}"
+    wd = W.scaled(W.WORKLOADS["decode"], batch=B, seqlen_k=T + 60, heads_q=Hq, heads_kv=Hkv)
+    qd, kc, vc, Pd = W.make_inputs(wd, device="cuda")
+    outd = plx.parallax_attn_decode(qd, kc, vc, Pd)
+    torch.cuda.synchronize()
+    assert rel_err(host(outd), oracle.decode(host(qd), host(kc), host(vc), host(Pd))) <= BF16_TOL
+
+
 def test_split_rows_floor(plx):
     """The first 16 query rows always take the hi + lo operand pairs: split_rows 0 and 16 give the same bits."""
     _announce("split_rows floor")
