@@ -128,3 +128,15 @@ def test_decode_validation(plx):
     assert _dec(plx, _desc(plx, Tq=1, p_per_query=True)) == E.PLX_ERR_UNSUPPORTED
     assert _dec(plx, _desc(plx, Tq=1), q=None) == E.PLX_ERR_INVALID
     assert _dec(plx, _desc(plx, Tq=1, B=0)) == E.PLX_OK
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The library has no multi-GPU path: bench.py --gpus 2 stops with a message before touching a GPU."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300, cwd=root)
+    assert r.returncode == 2
+    assert "--gpus 1" in r.stderr
+    assert r.stdout.strip() == ""
