@@ -142,6 +142,48 @@ def fwd(q, k, v, P, causal=True, window=0, scale=None, rows=None):
     return out, lse, kbar, osa
 
 
+def fwd_probe(q, k, v, rho, causal=True, window=0, scale=None, rows=None):
+    """Parallax forward with the probe supplied per query row, the pages' own form.
+
+    gist.science technical summary, "Core mechanism": out_i = o^SA_i - Sigma_KV^(i) rho_i, where the
+    probe rho_i = W_R x_i is a learned map of the layer input (computed here by the caller) and
+    Sigma_KV^(i) is the key/value covariance of the query's softmax neighbourhood, read as
+    Sigma_KV^(i) = sum_j p_ij (v_j - o_i)(k_j - kbar_i)^T.  So
+      out_i = o_i - sum_j p_ij (rho_i . (k_j - kbar_i)) (v_j - o_i),
+    which is fwd() with u_i = -rho_i.
+
+    q, rho [B,Tq,Hq,d]; k, v [B,Tk,Hkv,d].  Returns float64 out [B,Tq,Hq,d] and lse [B,Hq,Tq]
+    (rows outside ``rows`` are NaN).
+    Pinned by: rho = 0 vs torch SDPA; rho = -u of fwd() reproduces fwd(); the covariance matrix
+    built with numpy.cov (aweights = p) applied to rho; constant V.
+    """
+    q, k, v, rho = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(rho)
+    B, Tq, Hq, d = q.shape
+    _, Tk, Hkv, _ = k.shape
+    assert Hq % Hkv == 0 and rho.shape == q.shape
+    grp = Hq // Hkv
+    if scale is None or scale <= 0:
+        scale = 1.0 / np.sqrt(d)
+    out = np.full(q.shape, np.nan)
+    lse = np.full((B, Hq, Tq), np.nan)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // grp
+            K, V = k[b, :, g, :], v[b, :, g, :]
+            for rr, lo, hi in _row_blocks(Tq, Tk, causal, window, rows):
+                Qr, Rr = q[b, rr, h, :], rho[b, rr, h, :]
+                mask = _mask_rows(rr, lo, hi, Tq, Tk, causal, window)
+                Kj, Vj = K[lo:hi], V[lo:hi]
+                p, l = _softmax_rows(scale * (Qr @ Kj.T), mask)
+                o = p @ Vj
+                kb = p @ Kj
+                t = Rr @ Kj.T - np.sum(Rr * kb, axis=1, keepdims=True)      # rho_i . (k_j - kbar_i)
+                w = p * t
+                out[b, rr, h] = o - (w @ Vj - np.sum(w, axis=1, keepdims=True) * o)
+                lse[b, h, rr] = l
+    return out, lse
+
+
 def bwd(q, k, v, P, dout, causal=True, window=0, scale=None):
     """Gradients of sum(dout * out) with respect to q, k, v and P (chain rule of ``fwd``).
 

@@ -377,9 +377,67 @@ def pin_decode(orc):
             _close(out[b, h], want, 1e-10, f"decode batch {b} head {h}")
 
 
+# ---------------------------------------------------------------------------
+# probe-form pins (out_i = o_i - Sigma_KV^(i) rho_i with rho supplied per row)
+# ---------------------------------------------------------------------------
+
+def pin_probe_zero_is_sdpa(orc):
+    """rho = 0 leaves softmax attention (torch SDPA in float64), causal and not, GQA."""
+    q, k, v, _ = _rand_case(21)
+    scale = 1.0 / math.sqrt(q.shape[-1])
+    for causal in (True, False):
+        out, _ = orc.fwd_probe(q, k, v, np.zeros_like(q), causal=causal)
+        _close(out, _sdpa(q, k, v, causal, scale), 1e-12, f"probe rho=0 causal={causal}")
+
+
+def pin_probe_covariance_matrix(orc):
+    """out_i = o_i - Sigma_KV^(i) rho_i with Sigma_KV^(i) built by numpy.cov (aweights = p) and a random
+    rho, with a window, GQA 4 query heads on 2 key/value heads."""
+    q, k, v, _ = _rand_case(22, B=1, Tq=9, Tk=12, Hq=4, Hkv=2, d=5)
+    d = q.shape[-1]
+    scale = 1.0 / math.sqrt(d)
+    rho = _rng(23).standard_normal(q.shape)
+    window = 5
+    out, _ = orc.fwd_probe(q, k, v, rho, causal=True, window=window)
+    for h in range(4):
+        g = h // 2
+        for i in range(q.shape[1]):
+            ip = i + 3
+            lo = max(0, ip - window + 1)
+            Kj, Vj = k[0, lo:ip + 1, g], v[0, lo:ip + 1, g]
+            p = scipy.special.softmax(scale * (Kj @ q[0, i, h]))
+            o = np.average(Vj, axis=0, weights=p)
+            want = o - _weighted_cov(Vj, Kj, p) @ rho[0, i, h]
+            _close(out[0, i, h], want, 1e-10, f"probe covariance head {h} row {i}")
+
+
+def pin_probe_matches_projector_form(orc):
+    """With rho_i = -P_h^T (q_i - kbar_i), kbar taken from the projector form, the probe form reproduces it."""
+    q, k, v, P = _rand_case(24, p_std=0.7)
+    out, lse, kbar, _ = orc.fwd(q, k, v, P, causal=True, window=7)
+    rho = -np.einsum("bthx,hxa->btha", q - kbar, P)
+    out2, lse2 = orc.fwd_probe(q, k, v, rho, causal=True, window=7)
+    _close(out2, out, 1e-12, "probe form vs projector form")
+    _close(lse2, lse, 1e-12, "probe form lse")
+
+
+def pin_probe_constant_values(orc):
+    """Constant values: the covariance is zero, so the output is that value for any probe."""
+    q, k, v, _ = _rand_case(25)
+    v[:] = v[:, :1]
+    rho = 5.0 * _rng(26).standard_normal(q.shape)
+    out, _ = orc.fwd_probe(q, k, v, rho, causal=True)
+    for h in range(q.shape[2]):
+        _close(out[:, :, h], np.broadcast_to(v[:, :1, h // 2], out[:, :, h].shape), 1e-12, "probe constant V")
+
+
+PROBE_PINS = [pin_probe_zero_is_sdpa, pin_probe_covariance_matrix, pin_probe_matches_projector_form,
+              pin_probe_constant_values]
+
+
 FORWARD_PINS = [pin_zero_projector_is_sdpa, pin_bottom_right_alignment, pin_mask_counts,
                 pin_exact_lla_is_ridge_wls, pin_covariance_form, pin_constant_values,
                 pin_single_key_rows, pin_affine_values, pin_linear_in_projector, pin_hand_examples]
 BACKWARD_PINS = [pin_bwd_finite_differences, pin_bwd_autograd, pin_bwd_zero_projector_is_sdpa]
 DECODE_PINS = [pin_decode]
-ALL_PINS = FORWARD_PINS + BACKWARD_PINS + DECODE_PINS
+ALL_PINS = FORWARD_PINS + BACKWARD_PINS + DECODE_PINS + PROBE_PINS

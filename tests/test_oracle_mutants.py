@@ -39,6 +39,14 @@ MUTANTS = [
     ("bwd dq scale", "dq[b, rr, h] += Pdu + scale * (ds @ Kj)", "dq[b, rr, h] += Pdu + (ds @ Kj)"),
     ("bwd dk kbar term", "+ p.T @ dkb +", "+ 0.0 * p.T @ dkb +"),
     ("decode ignores seqlens", "L = Lmax if seqlens is None else int(seqlens[b])", "L = Lmax"),
+    ("probe correction sign", "out[b, rr, h] = o - (w @ Vj", "out[b, rr, h] = o + (w @ Vj"),
+    ("probe centrings dropped",
+     "t = Rr @ Kj.T - np.sum(Rr * kb, axis=1, keepdims=True)      # rho_i . (k_j - kbar_i)\n"
+     "                w = p * t\n                out[b, rr, h] = o - (w @ Vj - np.sum(w, axis=1, keepdims=True) * o)",
+     "t = Rr @ Kj.T\n                w = p * t\n                out[b, rr, h] = o - (w @ Vj)"),
+    ("probe dotted with q", "t = Rr @ Kj.T", "t = Qr @ Kj.T"),
+    # (the key mean inside t may be any per-row constant, since sum_j p_j (v_j - o) = 0: replacing it is
+    # an equivalent program, not a mistake)
 ]
 
 
