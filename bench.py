@@ -9,7 +9,10 @@ decode workload (64 queries against a 32768-long cache) is timed after the
 steps and reported in its own object.  One JSON line goes to stdout; progress
 goes to stderr.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+The probe-form forward (caller-supplied probe rho, one pass) is timed on the
+same layer shape after the steps and reported in its own object too.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode] [--no-probe]
 """
 import argparse
 import ctypes
@@ -47,6 +50,12 @@ def fwd_flops(w, row_begin=0):
     """Forward: 12d per visible pair (pass 1 QK^T 2d + p[V|K] 4d, pass 2 QK^T 2d + UK^T 2d + WV 2d) + 2d^2 per row (u)."""
     pairs, rows = visible_pairs_rows(w, row_begin)
     return 12 * w.head_dim * pairs + 2 * w.head_dim ** 2 * rows
+
+
+def probe_flops(w, row_begin=0):
+    """Probe-form forward: 8d per visible pair (Q K^T, rho K^T, p V and (p r) V)."""
+    pairs, _ = visible_pairs_rows(w, row_begin)
+    return 8 * w.head_dim * pairs
 
 
 def bwd_flops(w, row_begin=0):
@@ -162,6 +171,7 @@ def main():
     ap.add_argument("--split-rows", type=int, default=-1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy, the reference for HBM traffic counters")
     args = ap.parse_args()
@@ -266,6 +276,36 @@ def main():
         "kernels": kern,
         "roofline": roofline,
     }
+
+    if not args.no_probe:
+        log("probe-form forward")
+        rho = W.make_probe(w, device=dev)
+        for _ in range(2):
+            plx.parallax_attn_fwd_probe(q, k, v, rho, split_rows=split)
+        torch.cuda.synchronize()
+        Kp = max(6, K)
+        pev = [(ev.create(), ev.create()) for _ in range(Kp)]
+        t0 = time.perf_counter()
+        for i in range(Kp):
+            lib.parallax_set_kernel_events(plx.PLX_KERNEL_FWD_PROBE, *pev[i])
+            plx.parallax_attn_fwd_probe(q, k, v, rho, split_rows=split)
+        lib.parallax_set_kernel_events(0, None, None)
+        torch.cuda.synchronize()
+        dtp = (time.perf_counter() - t0) / Kp
+        pms = sorted(ev.elapsed_ms(a, b) for a, b in pev)
+        pavg = sum(pms) / len(pms)
+        pfl = probe_flops(w, r0)
+        ptf = pfl / (pavg * 1e-3) / 1e12
+        result["probe"] = {
+            "workload": f"{w.name} probe-form forward: B={w.batch}, T={w.seqlen_q}, Hq={w.heads_q}, "
+                        f"Hkv={w.heads_kv}, d={w.head_dim}, causal, bf16 inputs, rho ~ N(0, (0.02 sqrt(d))^2)",
+            "ms_per_call": round(dtp * 1e3, 4),
+            "tflops_per_call": round(probe_flops(w) / dtp / 1e12, 3),
+            "kernel": {"avg_ms": round(pavg, 4), "median_ms": round(pms[len(pms) // 2], 4), "launches": len(pms),
+                       "algorithmic_flop": pfl, "tflops": round(ptf, 3),
+                       "frac_of_peak": round(ptf / PEAK_F16_TFLOPS, 4)}}
+        log(f"probe forward {dtp * 1e3:.3f} ms/call, kernel {pavg:.3f} ms ({ptf:.0f} TFLOP/s)")
+        del rho
 
     if not args.no_decode:
         wd = W.WORKLOADS["decode"]

@@ -80,7 +80,8 @@ typedef enum {
   PLX_KERNEL_BWD_KEYS = 2,     /* backward: key-major kernel (dk, dv, ds); the generic key kernel on the fp32 path */
   PLX_KERNEL_DECODE_PASS1 = 3, /* decode: first split-KV pass (generic kernel on the fp32 path) */
   PLX_KERNEL_DECODE_PASS2 = 4, /* decode: second split-KV pass */
-  PLX_KERNEL_BWD_DQ = 5        /* backward: dq = P du + scale ds K from the stored ds (bf16 fast path) */
+  PLX_KERNEL_BWD_DQ = 5,       /* backward: dq = P du + scale ds K from the stored ds (bf16 fast path) */
+  PLX_KERNEL_FWD_PROBE = 6     /* probe-form forward: the one-pass MFMA kernel */
 } plx_kernel;
 
 /*
@@ -121,6 +122,33 @@ plx_status parallax_attn_fwd(const plx_attn_desc* desc,
                              const void* q, const void* k, const void* v, const void* P,
                              float* out, float* lse, float* kbar, float* o_sa,
                              void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Probe-form forward.  Bytes of workspace needed for `desc` (0 if none); returns 0 for an
+ * invalid desc.
+ */
+size_t parallax_attn_fwd_probe_workspace(const plx_attn_desc* desc);
+
+/*
+ * Probe-form forward: the pages' own statement of the output (gist.science technical
+ * summary, "Core mechanism"; the intensity argument of its "Hardware-aware algorithm"
+ * section), with the probe rho_i supplied per query row instead of built from P:
+ *
+ *   out_i = o_i - Sigma_i rho_i,   Sigma_i = sum_j p_ij (v_j - o_i)(k_j - kbar_i)^T
+ *         = o_i - sum_j p_ij (rho_i . (k_j - kbar_i)) (v_j - o_i)
+ *
+ * (the forward above with u_i = -rho_i).  rho_i = W_R x_i is the caller's projection of the
+ * layer input.  Because rho does not depend on kbar, one pass over the keys suffices.
+ *   q, rho [B][Tq][Hq][d]     k, v [B][Tk][Hkv][d]     dtype desc->dtype
+ *   out    [B][Tq][Hq][d] fp32 (required)
+ *   lse    [B][Hq][Tq]    fp32 as in the forward (nullable)
+ * Supported: bf16, head_dim 128, heads_q / heads_kv in {1, 2, 4, 8}, p_per_query 0; any other
+ * valid desc returns PLX_ERR_UNSUPPORTED.  Masks, empty rows and split_rows as in the forward.
+ */
+plx_status parallax_attn_fwd_probe(const plx_attn_desc* desc,
+                                   const void* q, const void* k, const void* v, const void* rho,
+                                   float* out, float* lse,
+                                   void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* Backward.  Bytes of workspace needed for `desc`; returns 0 for an invalid desc. */
 size_t parallax_attn_bwd_workspace(const plx_attn_desc* desc);

@@ -12,6 +12,7 @@ Functions (same names as the C entry points):
     out, lse, kbar, o = parallax_attn_fwd(q, k, v, P, causal=True, window=0, scale=None)
     dq, dk, dv, dP    = parallax_attn_bwd(q, k, v, P, out, dout, lse, kbar, o, causal=True, ...)
     out               = parallax_attn_decode(q, k_cache, v_cache, P, seqlens=None, window=0, scale=None)
+    out, lse          = parallax_attn_fwd_probe(q, k, v, rho, causal=True, window=0, scale=None)
 
 Layouts: q [B,Tq,Hq,d] (decode [B,Hq,d]); k, v [B,Tk,Hkv,d]; P [Hq,d,d] (or
 [B,Tq,Hq,d,d] per query, forward only); outputs float32.
@@ -29,7 +30,7 @@ LIB_PATH = os.path.join(_PKG, "libparallax.so")
 PLX_OK, PLX_ERR_INVALID, PLX_ERR_UNSUPPORTED, PLX_ERR_WORKSPACE, PLX_ERR_HIP = range(5)
 PLX_F32, PLX_BF16 = 0, 1
 (PLX_KERNEL_FWD, PLX_KERNEL_BWD_ROWS, PLX_KERNEL_BWD_KEYS, PLX_KERNEL_DECODE_PASS1, PLX_KERNEL_DECODE_PASS2,
- PLX_KERNEL_BWD_DQ) = range(6)
+ PLX_KERNEL_BWD_DQ, PLX_KERNEL_FWD_PROBE) = range(7)
 
 
 class PlxAttnDesc(ctypes.Structure):
@@ -57,6 +58,8 @@ SIGNATURES = {
     "parallax_last_error": (ctypes.c_char_p, []),
     "parallax_attn_fwd_workspace": (_sz, [_DESC]),
     "parallax_attn_fwd": (_st, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "parallax_attn_fwd_probe_workspace": (_sz, [_DESC]),
+    "parallax_attn_fwd_probe": (_st, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "parallax_attn_bwd_workspace": (_sz, [_DESC]),
     "parallax_attn_bwd": (_st, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -154,6 +157,27 @@ def parallax_attn_fwd(q, k, v, P, causal=True, window=0, scale=None, split_rows=
     return out, lse, kbar, osa
 
 
+def parallax_attn_fwd_probe(q, k, v, rho, causal=True, window=0, scale=None, split_rows=-1):
+    """Probe-form forward, rho [B,Tq,Hq,d] like q; returns (out, lse), float32 (see include/parallax.h)."""
+    B, Tq, Hq, d = q.shape
+    Tk, Hkv = k.shape[1], k.shape[2]
+    dt = _dtype_code(q)
+    _need(k, "k", q.dtype, (B, Tk, Hkv, d), q.device)
+    _need(v, "v", q.dtype, (B, Tk, Hkv, d), q.device)
+    _need(rho, "rho", q.dtype, (B, Tq, Hq, d), q.device)
+    _need(q, "q", q.dtype, (B, Tq, Hq, d), q.device)
+    desc = make_desc(B, Tq, Tk, Hq, Hkv, d, causal, window, scale, dt, False, split_rows)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    out = torch.empty((B, Tq, Hq, d), **f32)
+    lse = torch.empty((B, Hq, Tq), **f32)
+    lib = get_lib()
+    nws = lib.parallax_attn_fwd_probe_workspace(ctypes.byref(desc))
+    ws = _workspace(nws, q.device)
+    _check(lib.parallax_attn_fwd_probe(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(rho), _ptr(out),
+                                       _ptr(lse), _ptr(ws), nws, _stream()))
+    return out, lse
+
+
 def parallax_attn_bwd(q, k, v, P, out, dout, lse, kbar, o_sa, causal=True, window=0, scale=None,
                       split_rows=-1):
     """Backward; returns (dq, dk, dv, dP), all float32 (see include/parallax.h)."""
@@ -207,3 +231,4 @@ def parallax_attn_decode(q, k_cache, v_cache, P, seqlens=None, window=0, scale=N
 fwd = parallax_attn_fwd
 bwd = parallax_attn_bwd
 decode = parallax_attn_decode
+fwd_probe = parallax_attn_fwd_probe

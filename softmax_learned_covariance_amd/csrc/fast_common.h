@@ -199,7 +199,7 @@ __device__ __forceinline__ int row_slot_swz(int r, int c) { return r ^ (4 * (c &
 // ---- staging buffers inside the caller's workspace ----
 // Slots of the max-abs array (float bits; non-negative floats order like their bits).
 enum MaxSlot { kMaxQ = 0, kMaxK = 1, kMaxV = 2, kMaxP = 3, kMaxDO = 4, kMaxU = 5, kMaxDKB = 6, kMaxDelta = 7,
-               kMaxAlpha = 8 };
+               kMaxAlpha = 8, kMaxRho = 9 };
 
 struct Staging {
   uint32_t* maxbits;   // [16] max-abs values, see MaxSlot

@@ -42,6 +42,7 @@ constexpr float kTau = 8.f;
 
 struct FwdParams {
   const u16* q;
+  const u16* rho;   // probe form only: the caller's probe, like q
   const _Float16 *k16, *k16t, *v16t, *p16t;
   const uint32_t* maxbits;
   float *out, *lse, *kbar, *osa;
@@ -471,6 +472,237 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// Probe form, one pass (gist.science summary, "Core mechanism": out_i = o^SA_i - Sigma_KV^(i) rho_i
+// with the probe rho_i = W_R x_i supplied by the caller; "Hardware-aware algorithm": one KV stream
+// for both branches, the QK and RK products sharing the K operand).  With the probe known up front
+//   out = o - (sum_j p_j r_j v_j - a o),   r_j = rho . k_j,   a = sum_j p_j r_j (= rho . kbar),
+// so o, c = sum p r v, l and sum p r accumulate together in one online-softmax pass.  Per 32-key
+// half of a tile: S = K Q^T and R = K rho^T share the K operand; o += V^T p~ and c += V^T (p~ R)
+// share the V^T operand, so every operand read from LDS feeds two MFMAs.  rho is an input (bf16, exact in fp16 after its power-of-two scale), so its
+// operand lives in LDS, one 8 KB block per wave; q stays in registers.
+// W = p~ R is carried at 2^-32: |R| <= d 2^32 in the scaled units and p~ <= 2^8, so W stays
+// below 2^15 whatever the data.
+// ------------------------------------------------------------------------------------------
+
+constexpr float kProbeW = 2.3283064365386963e-10f;   // 2^-32
+
+struct __align__(16) ProbeTiles {
+  _Float16 k[2][kKeyTile * kD];    // key rows tile    [16 chunks][64 keys][8]
+  _Float16 vt[2][kD * kKeyTile];   // value columns    [8 chunks][128 d][8]
+  f16x8 rho[kWaves][8][64];        // per wave: the rho operand of each lane, 8 k-steps
+};
+
+__device__ __forceinline__ void probe_tile_dma(const FwdParams& p, ProbeTiles& T, int buf, int b, int g, int kt,
+                                               int w, int l) {
+  const int64_t tb = kv_tile(b, g, kt, p.Hkv, p.Tk_pad / kKeyTile);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = 2 * w + j;
+    const int64_t src = tb + i * 512 + l * 8;
+    lds_dma16(p.k16 + src, &T.k[buf][i * 512]);
+    lds_dma16(p.v16t + src, &T.vt[buf][i * 512]);
+  }
+}
+
+__device__ __forceinline__ f16x8 lds_k_probe(const ProbeTiles& T, int buf, int r, int c) {
+  return *reinterpret_cast<const f16x8*>(&T.k[buf][c * (kKeyTile * 8) + r * 8]);
+}
+__device__ __forceinline__ f16x8 lds_vt_probe(const ProbeTiles& T, int buf, int d, int c) {
+  return *reinterpret_cast<const f16x8*>(&T.vt[buf][c * (kD * 8) + d * 8]);
+}
+
+template <bool SPLIT>
+__global__ __launch_bounds__(512) void k_fwd_probe(FwdParams p) {
+  __shared__ ProbeTiles T;
+  const int tid = threadIdx.x, w = wave_id(), l = tid & 63, ql = l & 31, hh = l >> 5;
+
+  int pair, rb;
+  {
+    const int npairs = p.B * p.Hkv, id = blockIdx.x;
+    if ((npairs & 7) == 0) {
+      const int ppx = npairs >> 3, slot = id >> 3;
+      rb = p.n_rb - 1 - slot / ppx;
+      pair = (id & 7) + 8 * (slot % ppx);
+    } else {
+      rb = p.n_rb - 1 - id / npairs;
+      pair = id % npairs;
+    }
+  }
+  const int b = pair / p.Hkv, g = pair % p.Hkv;
+  const int wph = kWaves / p.G;
+  const int h = g * p.G + w / wph;
+  const int r0 = p.row_begin + rb * p.rows_per_block;
+  const int i0 = r0 + (w % wph) * 32;
+  const int row = i0 + ql;
+  const bool row_ok = row < p.row_end;
+  const int off = p.Tk - p.Tq;
+
+  const float sQ = range_scale(__uint_as_float(p.maxbits[kMaxQ]));
+  const float sK = range_scale(__uint_as_float(p.maxbits[kMaxK]));
+  const float sV = range_scale(__uint_as_float(p.maxbits[kMaxV]));
+  const float sR = range_scale(__uint_as_float(p.maxbits[kMaxRho]));
+  const float cS = p.scale * kLog2e / (sQ * sK);
+
+  const int64_t qoff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * kD;
+
+  const int rlast = min(r0 + p.rows_per_block, p.row_end) - 1;
+  const int kend = p.causal ? min(p.Tk, rlast + off + 1) : p.Tk;
+  const int kbeg = p.window > 0 ? max(0, r0 + off - p.window + 1) : 0;
+  const int t_beg = kbeg / kKeyTile;
+  const int t_end = kend > kbeg ? (kend + kKeyTile - 1) / kKeyTile : t_beg;
+  const int wlast = min(i0 + 31, p.row_end - 1);
+  const bool wave_rows = i0 < p.row_end;
+  const int w_kend = wave_rows ? (p.causal ? min(p.Tk, wlast + off + 1) : p.Tk) : 0;
+  const int w_kbeg = p.window > 0 ? max(0, i0 + off - p.window + 1) : 0;
+  const int w_full_end = p.causal ? min(p.Tk, i0 + off + 1) : p.Tk;
+  const int w_full_beg = p.window > 0 ? max(0, wlast + off - p.window + 1) : 0;
+  const int r_kend = row_ok ? (p.causal ? min(p.Tk, row + off + 1) : p.Tk) : 0;
+  const int r_kbeg = p.window > 0 ? max(0, row + off - p.window + 1) : 0;
+
+  f16x8 qB[8];
+  load_q_operand(p.q + qoff, row_ok, hh, sQ, qB);
+  {
+    // the lane's rho operand into the wave's LDS block (read back by the same lane only)
+    f16x8 rB[8];
+    load_q_operand(p.rho + qoff, row_ok, hh, sR, rB);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) T.rho[w][s][l] = rB[s];
+  }
+
+  f32x16 accO[4], accC[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    accO[mt] = f32x16{};
+    accC[mt] = f32x16{};
+  }
+  float m_used = -INFINITY, lpart = 0.f, rpart = 0.f;
+  if (t_beg < t_end) probe_tile_dma(p, T, 0, b, g, t_beg, w, l);
+  lds_dma_wait();
+  __syncthreads();
+  for (int kt = t_beg; kt < t_end; ++kt) {
+    const int buf = (kt - t_beg) & 1;
+    if (kt + 1 < t_end) probe_tile_dma(p, T, buf ^ 1, b, g, kt + 1, w, l);
+    const int key0 = kt * kKeyTile;
+    if (key0 < w_kend && key0 + kKeyTile > w_kbeg) {
+      const bool full = key0 + kKeyTile <= w_full_end && key0 >= w_full_beg;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16 S = {}, R = {};
+        {
+          // key-row and rho operands of chunk s + 1 are read while the MFMAs of chunk s run
+          f16x8 a[2], r[2];
+          a[0] = lds_k_probe(T, buf, 32 * kb + ql, hh);
+          r[0] = T.rho[w][0][l];
+#pragma unroll
+          for (int s = 0; s < 8; ++s) {
+            if (s + 1 < 8) {
+              a[(s + 1) & 1] = lds_k_probe(T, buf, 32 * kb + ql, 2 * (s + 1) + hh);
+              r[(s + 1) & 1] = T.rho[w][s + 1][l];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            S = mfma(a[s & 1], qB[s], S);
+            R = mfma(a[s & 1], r[s & 1], R);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        if (!full) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (key >= r_kend || key < r_kbeg) S[r] = -INFINITY;
+          }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[r]);
+        mx = xor32_max(mx);
+        const float mt_ = mx * cS;
+        const bool need = mt_ > m_used + kTau;
+        if (__ballot(need) != 0) {
+          const float f = need ? exp2f(m_used - mt_) : 1.f;
+          m_used = need ? mt_ : m_used;
+          lpart *= f;
+          rpart *= f;
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            accO[mt] *= f;
+            accC[mt] *= f;
+          }
+        }
+        const float mb = m_used == -INFINITY ? 0.f : m_used;
+        f16x8 pB[2], wB[2], pL[SPLIT ? 2 : 1], wL[SPLIT ? 2 : 1];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          float e[8], x[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            e[j] = __builtin_amdgcn_exp2f(fmaf(S[8 * t + j], cS, -mb));
+            x[j] = e[j] * R[8 * t + j] * kProbeW;
+          }
+          pB[t] = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+          wB[t] = pack8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+          lpart = sum8(pB[t], lpart);
+          rpart = sum8(wB[t], rpart);
+          if constexpr (SPLIT) {
+            pL[t] = pack_lo(e, pB[t]);
+            wL[t] = pack_lo(x, wB[t]);
+            lpart = sum8(pL[t], lpart);
+            rpart = sum8(wL[t], rpart);
+          }
+        }
+        {
+          // step n = (mt, t): V^T column operands two steps ahead, each feeding o and c
+          f16x8 c[3];
+          c[0] = lds_vt_probe(T, buf, ql, 4 * kb + hh);
+          c[1] = lds_vt_probe(T, buf, ql, 4 * kb + 2 + hh);
+#pragma unroll
+          for (int n = 0; n < 8; ++n) {
+            const int mt = n >> 1, t = n & 1;
+            if (n + 2 < 8) c[(n + 2) % 3] = lds_vt_probe(T, buf, 32 * ((n + 2) >> 1) + ql, 4 * kb + 2 * ((n + 2) & 1) + hh);
+            __builtin_amdgcn_sched_barrier(0);
+            accO[mt] = mfma(c[n % 3], pB[t], accO[mt]);
+            accC[mt] = mfma(c[n % 3], wB[t], accC[mt]);
+            if constexpr (SPLIT) {
+              accO[mt] = mfma(c[n % 3], pL[t], accO[mt]);
+              accC[mt] = mfma(c[n % 3], wL[t], accC[mt]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+    }
+    lds_dma_wait();
+    __syncthreads();
+  }
+
+  // out = o - (c - a o), o = accO / (l sV), c = accC 2^32 / (l sR sK sV), a = rpart 2^32 / (l sR sK)
+  const float L = xor32_sum(lpart);
+  const float RS = xor32_sum(rpart);
+  const bool has = L > 0.f;
+  const float invL = has ? 1.f / L : 0.f;
+  if (row_ok) {
+    if (p.lse && hh == 0)
+      p.lse[(static_cast<int64_t>(b) * p.Hq + h) * p.Tq + row] = has ? (m_used + __log2f(L)) * kLn2 : -INFINITY;
+    const float fo = invL / sV;
+    const float fc = fo / sK / (kProbeW * sR);
+    const float a = RS * invL / sK / (kProbeW * sR);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * mt + 8 * j + 4 * hh;
+        float r4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float o = accO[mt][4 * j + e] * fo;
+          r4[e] = o - accC[mt][4 * j + e] * fc + a * o;
+        }
+        *reinterpret_cast<float4*>(p.out + qoff + d) = float4{r4[0], r4[1], r4[2], r4[3]};
+      }
+  }
+}
+
 }  // namespace
 
 bool fast_fwd_supported(const Geom& g) {
@@ -543,6 +775,65 @@ hipError_t launch_fast_fwd(const Geom& g, const void* q, const void* k, const vo
   }
   e = side_join(side);
   return e;
+}
+
+bool fast_probe_supported(const Geom& g) { return fast_fwd_supported(g); }
+
+size_t fast_probe_workspace(const Geom& g) { return staging_layout(nullptr, g.B, g.Tk, g.Hkv, g.Hq).bytes; }
+
+hipError_t launch_fast_probe(const Geom& g, const void* q, const void* k, const void* v, const void* rho,
+                             float* out, float* lse, int split_rows, void* ws, hipStream_t stream) {
+  const Staging s = staging_layout(ws, g.B, g.Tk, g.Hkv, g.Hq);
+  int split = split_rows < kMinSplitRows ? kMinSplitRows : split_rows;
+  if (split > g.Tq) split = g.Tq;
+  const int64_t q_elems = static_cast<int64_t>(g.B) * g.Tq * g.Hq * kD;
+  // K/V into their fp16 tile layouts; max |q|, |k|, |v|, |rho| for the operand scales (no projector)
+  hipError_t e = launch_staging(s, q, q_elems, k, v, nullptr, g.B, g.Tk, g.Hkv, g.Hq, stream, rho, q_elems, kMaxRho);
+  if (e != hipSuccess) return e;
+  FwdParams base{};
+  {
+    FwdParams& p = base;
+    p.q = static_cast<const u16*>(q);
+    p.rho = static_cast<const u16*>(rho);
+    p.k16 = s.k16;
+    p.v16t = s.v16t;
+    p.maxbits = s.maxbits;
+    p.out = out;
+    p.lse = lse;
+    p.B = g.B;
+    p.Tq = g.Tq;
+    p.Tk = g.Tk;
+    p.Tk_pad = s.Tk_pad;
+    p.Hq = g.Hq;
+    p.Hkv = g.Hkv;
+    p.G = g.Hq / g.Hkv;
+    p.causal = g.causal;
+    p.window = g.window;
+    p.scale = g.scale;
+    p.rows_per_block = 32 * kWaves / p.G;
+  }
+  const SideLane side = split > 0 && split < g.Tq ? side_fork(stream) : SideLane{stream, stream};
+  if (split > 0) {
+    FwdParams p = base;
+    p.row_begin = 0;
+    p.n_rb = (split + p.rows_per_block - 1) / p.rows_per_block;
+    p.row_end = split;
+    hipLaunchKernelGGL(k_fwd_probe<true>, dim3(g.B * g.Hkv * p.n_rb), dim3(512), 0, side.stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (split < g.Tq) {
+    FwdParams p = base;
+    p.row_begin = split;
+    p.row_end = g.Tq;
+    p.n_rb = (g.Tq - split + p.rows_per_block - 1) / p.rows_per_block;
+    mark_begin(PLX_KERNEL_FWD_PROBE, stream);
+    hipLaunchKernelGGL(k_fwd_probe<false>, dim3(g.B * g.Hkv * p.n_rb), dim3(512), 0, stream, p);
+    mark_end(PLX_KERNEL_FWD_PROBE, stream);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return side_join(side);
 }
 
 }  // namespace plx

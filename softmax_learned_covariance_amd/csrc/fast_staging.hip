@@ -256,7 +256,8 @@ hipError_t launch_staging(const Staging& s, const void* q, int64_t q_elems, cons
     hipLaunchKernelGGL(k_stage_kv, dim3(Hkv * (s.Tk_pad / kKeyTile), 1, B), dim3(256), 0, stream,
                        static_cast<const u16*>(k), static_cast<const u16*>(v), s.maxbits, s.k16, s.k16t,
                        s.v16t, s.v16, Tk, s.Tk_pad, Hkv);
-  hipLaunchKernelGGL(k_stage_p, dim3(Hq), dim3(256), 0, stream, static_cast<const u16*>(P), s.maxbits, s.p16t,
+  if (P)
+    hipLaunchKernelGGL(k_stage_p, dim3(Hq), dim3(256), 0, stream, static_cast<const u16*>(P), s.maxbits, s.p16t,
                      s.p16);
   return hipGetLastError();
 }

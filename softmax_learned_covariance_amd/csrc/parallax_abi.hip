@@ -201,6 +201,33 @@ plx_status parallax_attn_fwd(const plx_attn_desc* desc, const void* q, const voi
   return hip_status(e, what);
 }
 
+size_t parallax_attn_fwd_probe_workspace(const plx_attn_desc* desc) {
+  plx::Geom g;
+  if (check_desc(desc, "parallax_attn_fwd_probe_workspace", &g) != PLX_OK) return 0;
+  return plx::fast_probe_supported(g) ? plx::fast_probe_workspace(g) : 0;
+}
+
+plx_status parallax_attn_fwd_probe(const plx_attn_desc* desc, const void* q, const void* k,
+                                   const void* v, const void* rho, float* out, float* lse,
+                                   void* workspace, size_t workspace_bytes, void* hip_stream) {
+  const char* what = "parallax_attn_fwd_probe";
+  plx::Geom g;
+  plx_status st = check_desc(desc, what, &g);
+  if (st != PLX_OK) return st;
+  if (!plx::fast_probe_supported(g))
+    return fail(PLX_ERR_UNSUPPORTED,
+                "%s: only bf16, head_dim 128, heads_q/heads_kv in {1,2,4,8} and p_per_query 0 are supported", what);
+  const bool empty = g.B == 0 || g.Tq == 0;
+  if (!empty && (!q || !rho || !out))
+    return fail(PLX_ERR_INVALID, "%s: q, rho and out must not be NULL", what);
+  if (!empty && g.Tk > 0 && (!k || !v)) return fail(PLX_ERR_INVALID, "%s: k and v must not be NULL", what);
+  st = check_ws(plx::fast_probe_workspace(g), workspace, workspace_bytes, what);
+  if (st != PLX_OK) return st;
+  if (empty) return ok();
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  return hip_status(plx::launch_fast_probe(g, q, k, v, rho, out, lse, split_rows_of(desc), workspace, stream), what);
+}
+
 size_t parallax_attn_bwd_workspace(const plx_attn_desc* desc) {
   plx::Geom g;
   if (check_desc(desc, "parallax_attn_bwd_workspace", &g) != PLX_OK) return 0;

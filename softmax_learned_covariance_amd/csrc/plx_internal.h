@@ -42,6 +42,12 @@ hipError_t launch_generic_bwd(const Geom& g, const void* q, const void* k, const
                               hipStream_t stream);
 
 // ---- bf16 MFMA fast path (head_dim 128) ----
+// Probe form (the caller supplies rho per query row): out = o - Sigma_KV rho, one pass over K/V.
+bool fast_probe_supported(const Geom& g);
+size_t fast_probe_workspace(const Geom& g);
+hipError_t launch_fast_probe(const Geom& g, const void* q, const void* k, const void* v, const void* rho,
+                             float* out, float* lse, int split_rows, void* ws, hipStream_t stream);
+
 bool fast_fwd_supported(const Geom& g);
 size_t fast_fwd_workspace(const Geom& g);
 hipError_t launch_fast_fwd(const Geom& g, const void* q, const void* k, const void* v,

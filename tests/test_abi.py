@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(plx):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     out = subprocess.run(["nm", "-D", "--defined-only", plx.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (parallax_\w+)", out))
     missing = [n for n in names if n not in exported]
@@ -128,6 +128,31 @@ def test_decode_validation(plx):
     assert _dec(plx, _desc(plx, Tq=1, p_per_query=True)) == E.PLX_ERR_UNSUPPORTED
     assert _dec(plx, _desc(plx, Tq=1), q=None) == E.PLX_ERR_INVALID
     assert _dec(plx, _desc(plx, Tq=1, B=0)) == E.PLX_OK
+
+
+def _probe(plx, desc, q=FAKE, rho=FAKE, out=FAKE, ws=FAKE, nws=1 << 40):
+    lib = plx.get_lib()
+    return lib.parallax_attn_fwd_probe(ctypes.byref(desc), q, FAKE, FAKE, rho, out, None, ws, nws, None)
+
+
+def test_probe_validation(plx):
+    E = plx
+    lib = plx.get_lib()
+    bf = dict(dtype=plx.PLX_BF16, d=128)
+    assert _probe(plx, _desc(plx)) == E.PLX_ERR_UNSUPPORTED             # fp32
+    assert _probe(plx, _desc(plx, dtype=plx.PLX_BF16)) == E.PLX_ERR_UNSUPPORTED   # head_dim 16
+    assert _probe(plx, _desc(plx, Hq=3, Hkv=1, **bf)) == E.PLX_ERR_UNSUPPORTED    # 3 heads per group
+    assert _probe(plx, _desc(plx, Hq=3, Hkv=2, **bf)) == E.PLX_ERR_INVALID
+    d = _desc(plx, **bf)
+    need = lib.parallax_attn_fwd_probe_workspace(ctypes.byref(d))
+    assert need > 0
+    assert lib.parallax_attn_fwd_probe_workspace(ctypes.byref(_desc(plx))) == 0
+    assert _probe(plx, d, nws=need - 1) == E.PLX_ERR_WORKSPACE
+    assert _probe(plx, d, ws=None, nws=need) == E.PLX_ERR_INVALID
+    assert _probe(plx, d, rho=None) == E.PLX_ERR_INVALID
+    assert b"rho" in lib.parallax_last_error()
+    assert _probe(plx, d, out=None) == E.PLX_ERR_INVALID
+    assert _probe(plx, _desc(plx, B=0, **bf)) == E.PLX_OK
 
 
 def test_bench_refuses_more_than_one_gpu():

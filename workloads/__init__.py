@@ -18,7 +18,10 @@ order, Q, K, V, P and (for the backward) dO, each as float32 N(0,1) (P then
 multiplied by its standard deviation).  For bf16 workloads each tensor is then
 rounded to bfloat16 with round-to-nearest-even (torch's conversion).  For
 ``layer17`` each K row is scaled to Euclidean norm sqrt(d) in float32 before
-rounding.  Generation runs on whatever device is asked for; CPU and GPU
+rounding.  The probe-form forward takes a per-row probe rho like q: ``make_probe`` draws
+it from a second generator seeded with seed + 1000, float32 N(0, (p_std *
+sqrt(d))^2) (the spread u = P^T q has for these P and q), then rounds it the
+same way.  Generation runs on whatever device is asked for; CPU and GPU
 generators give different (but each deterministic) streams, so a test always
 draws its inputs once and hands the same tensors to both sides.
 """
@@ -108,6 +111,15 @@ def make_inputs(w: Workload, device="cpu", with_dout: bool = False,
     if with_dout:
         out.append(dout.to(td))
     return tuple(out)
+
+
+def make_probe(w: Workload, device="cpu", seed: Optional[int] = None):
+    """Draw the per-row probe rho [B, Tq, Hq, d] of the probe-form forward (storage dtype of ``w``)."""
+    g = torch.Generator(device=device)
+    g.manual_seed((w.seed if seed is None else seed) + 1000)
+    shape = (w.batch, w.seqlen_q, w.heads_q, w.head_dim)
+    rho = torch.randn(shape, generator=g, device=device, dtype=torch.float32) * (w.p_std * math.sqrt(w.head_dim))
+    return rho.to(w.torch_dtype)
 
 
 def to_f64_numpy(t: torch.Tensor):
