@@ -152,8 +152,9 @@ def fwd_probe(q, k, v, rho, causal=True, window=0, scale=None, rows=None):
       out_i = o_i - sum_j p_ij (rho_i . (k_j - kbar_i)) (v_j - o_i),
     which is fwd() with u_i = -rho_i.
 
-    q, rho [B,Tq,Hq,d]; k, v [B,Tk,Hkv,d].  Returns float64 out [B,Tq,Hq,d] and lse [B,Hq,Tq]
-    (rows outside ``rows`` are NaN).
+    q, rho [B,Tq,Hq,d]; k, v [B,Tk,Hkv,d].  Returns float64 out [B,Tq,Hq,d], lse [B,Hq,Tq], the
+    softmax output o [B,Tq,Hq,d] and rk [B,Hq,Tq] = rho_i . kbar_i (rows outside ``rows`` are NaN);
+    o and rk are what ``bwd_probe`` needs besides lse.
     Pinned by: rho = 0 vs torch SDPA; rho = -u of fwd() reproduces fwd(); the covariance matrix
     built with numpy.cov (aweights = p) applied to rho; constant V.
     """
@@ -165,7 +166,9 @@ def fwd_probe(q, k, v, rho, causal=True, window=0, scale=None, rows=None):
     if scale is None or scale <= 0:
         scale = 1.0 / np.sqrt(d)
     out = np.full(q.shape, np.nan)
+    osa = np.full(q.shape, np.nan)
     lse = np.full((B, Hq, Tq), np.nan)
+    rk = np.full((B, Hq, Tq), np.nan)
     for b in range(B):
         for h in range(Hq):
             g = h // grp
@@ -180,8 +183,62 @@ def fwd_probe(q, k, v, rho, causal=True, window=0, scale=None, rows=None):
                 t = Rr @ Kj.T - np.sum(Rr * kb, axis=1, keepdims=True)      # rho_i . (k_j - kbar_i)
                 w = p * t
                 out[b, rr, h] = o - (w @ Vj - np.sum(w, axis=1, keepdims=True) * o)
+                osa[b, rr, h] = o
                 lse[b, h, rr] = l
-    return out, lse
+                rk[b, h, rr] = np.sum(Rr * kb, axis=1)
+    return out, lse, osa, rk
+
+
+def bwd_probe(q, k, v, rho, dout, causal=True, window=0, scale=None):
+    """Gradients of sum(dout * out) of ``fwd_probe`` with respect to q, k, v and rho.
+
+    The pages give no backward.  Written in the probe's own terms, with r_ij = rho_i . k_j and
+    a_i = rho_i . kbar_i = sum_j p_ij r_ij, the forward is
+      out_i = (1 + a_i) o_i - sum_j p_ij r_ij v_j
+    (the centrings of the covariance cancel against sum_j p_ij (v_j - o_i) = 0).  With g = dout,
+    G_ij = g_i . v_j and go_i = g_i . o_i, differentiating through p, o, a and r:
+      drho_i = go_i kbar_i - sum_j p_ij G_ij k_j
+      dv_j   = sum_i p_ij (1 + a_i - r_ij) g_i
+      dp_ij  = G_ij (1 + a_i - r_ij) + go_i r_ij          (a and o depend on p too)
+      ds_ij  = p_ij (dp_ij - sum_l p_il dp_il)
+      dq_i   = scale sum_j ds_ij k_j
+      dk_j   = sum_i [p_ij (go_i - G_ij) rho_i + scale ds_ij q_i]
+    dk, dv are summed over the query heads sharing a key/value head.
+    Pinned by: central finite differences of ``fwd_probe``; torch.autograd of an independent torch
+    forward; rho = 0 against torch SDPA's backward.
+    """
+    q, k, v, rho, g_all = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(rho), _as_f64(dout)
+    B, Tq, Hq, d = q.shape
+    _, Tk, Hkv, _ = k.shape
+    grp = Hq // Hkv
+    if scale is None or scale <= 0:
+        scale = 1.0 / np.sqrt(d)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    drho = np.zeros_like(rho)
+    for b in range(B):
+        for h in range(Hq):
+            gk = h // grp
+            K, V = k[b, :, gk, :], v[b, :, gk, :]
+            for rr, lo, hi in _row_blocks(Tq, Tk, causal, window, None):
+                Qr, Rr, G = q[b, rr, h, :], rho[b, rr, h, :], g_all[b, rr, h, :]
+                mask = _mask_rows(rr, lo, hi, Tq, Tk, causal, window)
+                Kj, Vj = K[lo:hi], V[lo:hi]
+                p, _ = _softmax_rows(scale * (Qr @ Kj.T), mask)
+                o = p @ Vj
+                kb = p @ Kj
+                r = Rr @ Kj.T                                    # r_ij = rho_i . k_j
+                a = np.sum(p * r, axis=1, keepdims=True)         # a_i = rho_i . kbar_i
+                gv = G @ Vj.T                                    # G_ij = g_i . v_j
+                go = np.sum(G * o, axis=1, keepdims=True)        # go_i = g_i . o_i
+                drho[b, rr, h] = go * kb - (p * gv) @ Kj
+                dv[b, lo:hi, gk] += (p * (1.0 + a - r)).T @ G
+                dp = gv * (1.0 + a - r) + go * r
+                ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+                dq[b, rr, h] = scale * (ds @ Kj)
+                dk[b, lo:hi, gk] += (p * (go - gv)).T @ Rr + scale * (ds.T @ Qr)
+    return dq, dk, dv, drho
 
 
 def bwd(q, k, v, P, dout, causal=True, window=0, scale=None):

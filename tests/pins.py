@@ -386,7 +386,7 @@ def pin_probe_zero_is_sdpa(orc):
     q, k, v, _ = _rand_case(21)
     scale = 1.0 / math.sqrt(q.shape[-1])
     for causal in (True, False):
-        out, _ = orc.fwd_probe(q, k, v, np.zeros_like(q), causal=causal)
+        out = orc.fwd_probe(q, k, v, np.zeros_like(q), causal=causal)[0]
         _close(out, _sdpa(q, k, v, causal, scale), 1e-12, f"probe rho=0 causal={causal}")
 
 
@@ -398,7 +398,7 @@ def pin_probe_covariance_matrix(orc):
     scale = 1.0 / math.sqrt(d)
     rho = _rng(23).standard_normal(q.shape)
     window = 5
-    out, _ = orc.fwd_probe(q, k, v, rho, causal=True, window=window)
+    out = orc.fwd_probe(q, k, v, rho, causal=True, window=window)[0]
     for h in range(4):
         g = h // 2
         for i in range(q.shape[1]):
@@ -414,11 +414,13 @@ def pin_probe_covariance_matrix(orc):
 def pin_probe_matches_projector_form(orc):
     """With rho_i = -P_h^T (q_i - kbar_i), kbar taken from the projector form, the probe form reproduces it."""
     q, k, v, P = _rand_case(24, p_std=0.7)
-    out, lse, kbar, _ = orc.fwd(q, k, v, P, causal=True, window=7)
+    out, lse, kbar, o = orc.fwd(q, k, v, P, causal=True, window=7)
     rho = -np.einsum("bthx,hxa->btha", q - kbar, P)
-    out2, lse2 = orc.fwd_probe(q, k, v, rho, causal=True, window=7)
+    out2, lse2, o2, rk = orc.fwd_probe(q, k, v, rho, causal=True, window=7)
     _close(out2, out, 1e-12, "probe form vs projector form")
     _close(lse2, lse, 1e-12, "probe form lse")
+    _close(o2, o, 1e-12, "probe form softmax output")
+    _close(rk, np.einsum("bthd,bthd->bht", rho, kbar), 1e-12, "probe form rho . kbar")
 
 
 def pin_probe_constant_values(orc):
@@ -426,13 +428,103 @@ def pin_probe_constant_values(orc):
     q, k, v, _ = _rand_case(25)
     v[:] = v[:, :1]
     rho = 5.0 * _rng(26).standard_normal(q.shape)
-    out, _ = orc.fwd_probe(q, k, v, rho, causal=True)
+    out = orc.fwd_probe(q, k, v, rho, causal=True)[0]
     for h in range(q.shape[2]):
         _close(out[:, :, h], np.broadcast_to(v[:, :1, h // 2], out[:, :, h].shape), 1e-12, "probe constant V")
 
 
+def pin_probe_bwd_finite_differences(orc):
+    """Central finite differences of sum(dout * fwd_probe) in float64 match bwd_probe for q, k, v and rho
+    (causal GQA, a window, more keys than queries)."""
+    r = _rng(27)
+    for (Tq, Tk, window) in [(7, 7, 0), (5, 8, 0), (8, 8, 3)]:
+        B, Hq, Hkv, d = 1, 2, 1, 3
+        q = r.standard_normal((B, Tq, Hq, d))
+        k = r.standard_normal((B, Tk, Hkv, d))
+        v = r.standard_normal((B, Tk, Hkv, d))
+        rho = r.standard_normal((B, Tq, Hq, d))
+        g = r.standard_normal((B, Tq, Hq, d))
+        grads = orc.bwd_probe(q, k, v, rho, g, causal=True, window=window)
+        eps = 1e-6
+        for idx, x in enumerate((q, k, v, rho)):
+            num = np.zeros_like(x)
+            it = np.nditer(x, flags=["multi_index"])
+            for _ in it:
+                mi = it.multi_index
+                old = x[mi]
+                x[mi] = old + eps
+                fp = np.sum(g * orc.fwd_probe(q, k, v, rho, causal=True, window=window)[0])
+                x[mi] = old - eps
+                fm = np.sum(g * orc.fwd_probe(q, k, v, rho, causal=True, window=window)[0])
+                x[mi] = old
+                num[mi] = (fp - fm) / (2 * eps)
+            _close(grads[idx], num, 2e-7, f"probe finite differences arg {idx} Tq={Tq} Tk={Tk} W={window}")
+
+
+def _torch_probe_forward(q, k, v, rho, causal, scale):
+    """Independent dense torch forward of the probe form: o minus the covariance matrix applied to rho."""
+    B, Tq, Hq, d = q.shape
+    Tk, Hkv = k.shape[1], k.shape[2]
+    K = k.repeat_interleave(Hq // Hkv, dim=2)
+    V = v.repeat_interleave(Hq // Hkv, dim=2)
+    s = torch.einsum("bihd,bjhd->bhij", q, K) * scale
+    if causal:
+        i = torch.arange(Tq)[:, None] + (Tk - Tq)
+        j = torch.arange(Tk)[None, :]
+        s = s.masked_fill(j > i, float("-inf"))
+    p = torch.softmax(s, dim=-1)
+    o = torch.einsum("bhij,bjhd->bihd", p, V)
+    kb = torch.einsum("bhij,bjhd->bihd", p, K)
+    Kc = K[:, None, :, :, :] - kb[:, :, None, :, :]          # b i j h d
+    Vc = V[:, None, :, :, :] - o[:, :, None, :, :]
+    sigma = torch.einsum("bhij,bijhx,bijhy->bihxy", p, Vc, Kc)   # Sigma_KV per row: [b i h d_v d_k]
+    return o - torch.einsum("bihxy,bihy->bihx", sigma, rho)
+
+
+def pin_probe_bwd_autograd(orc):
+    """torch.autograd (float64) through an independent dense torch forward of the probe form matches bwd_probe."""
+    q, k, v, _ = _rand_case(28, B=2, Tq=10, Tk=13, Hq=4, Hkv=2, d=5)
+    rho = 0.7 * _rng(29).standard_normal(q.shape)
+    g = _rng(30).standard_normal(q.shape)
+    T = [torch.from_numpy(x.copy()).requires_grad_(True) for x in (q, k, v, rho)]
+    out = _torch_probe_forward(*T, causal=True, scale=1.0 / math.sqrt(5))
+    out.backward(torch.from_numpy(g))
+    grads = orc.bwd_probe(q, k, v, rho, g, causal=True)
+    for name, a, t in zip(("q", "k", "v", "rho"), grads, T):
+        _close(a, t.grad.numpy(), 1e-11, f"probe autograd d{name}")
+
+
+def pin_probe_bwd_sdpa_and_covariance(orc):
+    """rho = 0: dq, dk, dv equal torch SDPA's backward.  For any rho, out is linear in rho with slope
+    -Sigma_KV^(i), so drho_i = -Sigma_KV^(i)T dout_i (Sigma_KV built with numpy.cov, aweights = p)."""
+    q, k, v, _ = _rand_case(31, B=1, Tq=12, Tk=12, Hq=4, Hkv=2, d=6)
+    g = _rng(32).standard_normal(q.shape)
+    d = q.shape[-1]
+    scale = 1.0 / math.sqrt(d)
+    Q = torch.from_numpy(q.copy()).permute(0, 2, 1, 3).requires_grad_(True)
+    Kt = torch.from_numpy(k.copy()).requires_grad_(True)
+    Vt = torch.from_numpy(v.copy()).requires_grad_(True)
+    K = Kt.permute(0, 2, 1, 3).repeat_interleave(2, dim=1)
+    V = Vt.permute(0, 2, 1, 3).repeat_interleave(2, dim=1)
+    o = torch.nn.functional.scaled_dot_product_attention(Q, K, V, is_causal=True)
+    o.permute(0, 2, 1, 3).backward(torch.from_numpy(g))
+    dq, dk, dv, _ = orc.bwd_probe(q, k, v, np.zeros_like(q), g, causal=True)
+    _close(dq, Q.grad.permute(0, 2, 1, 3).numpy(), 1e-12, "rho=0 dq")
+    _close(dk, Kt.grad.numpy(), 1e-12, "rho=0 dk")
+    _close(dv, Vt.grad.numpy(), 1e-12, "rho=0 dv")
+    rho = _rng(33).standard_normal(q.shape)
+    drho = orc.bwd_probe(q, k, v, rho, g, causal=True)[3]
+    for h in range(4):
+        for i in range(12):
+            Kj, Vj = k[0, :i + 1, h // 2], v[0, :i + 1, h // 2]
+            p = scipy.special.softmax(scale * (Kj @ q[0, i, h]))
+            want = -_weighted_cov(Vj, Kj, p).T @ g[0, i, h]
+            _close(drho[0, i, h], want, 1e-12, f"drho head {h} row {i}")
+
+
 PROBE_PINS = [pin_probe_zero_is_sdpa, pin_probe_covariance_matrix, pin_probe_matches_projector_form,
-              pin_probe_constant_values]
+              pin_probe_constant_values, pin_probe_bwd_finite_differences, pin_probe_bwd_autograd,
+              pin_probe_bwd_sdpa_and_covariance]
 
 
 FORWARD_PINS = [pin_zero_projector_is_sdpa, pin_bottom_right_alignment, pin_mask_counts,

@@ -45,6 +45,11 @@ MUTANTS = [
      "                w = p * t\n                out[b, rr, h] = o - (w @ Vj - np.sum(w, axis=1, keepdims=True) * o)",
      "t = Rr @ Kj.T\n                w = p * t\n                out[b, rr, h] = o - (w @ Vj)"),
     ("probe dotted with q", "t = Rr @ Kj.T", "t = Qr @ Kj.T"),
+    ("probe bwd drho sign", "drho[b, rr, h] = go * kb - (p * gv) @ Kj", "drho[b, rr, h] = (p * gv) @ Kj - go * kb"),
+    ("probe bwd dp misses a(p)", "dp = gv * (1.0 + a - r) + go * r", "dp = gv * (1.0 + a - r)"),
+    ("probe bwd dk rho term sign", "(p * (go - gv)).T @ Rr", "(p * (gv - go)).T @ Rr"),
+    ("probe bwd dv drops a", "dv[b, lo:hi, gk] += (p * (1.0 + a - r)).T @ G", "dv[b, lo:hi, gk] += (p * (1.0 - r)).T @ G"),
+    ("probe bwd dq scale", "dq[b, rr, h] = scale * (ds @ Kj)", "dq[b, rr, h] = ds @ Kj"),
     # (the key mean inside t may be any per-row constant, since sum_j p_j (v_j - o) = 0: replacing it is
     # an equivalent program, not a mistake)
 ]
