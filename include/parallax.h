@@ -142,12 +142,38 @@ size_t parallax_attn_fwd_probe_workspace(const plx_attn_desc* desc);
  *   q, rho [B][Tq][Hq][d]     k, v [B][Tk][Hkv][d]     dtype desc->dtype
  *   out    [B][Tq][Hq][d] fp32 (required)
  *   lse    [B][Hq][Tq]    fp32 as in the forward (nullable)
+ *   o_sa   [B][Tq][Hq][d] fp32 softmax-attention output o (nullable)
+ *   rk     [B][Hq][Tq]    fp32 rho_i . kbar_i (nullable)
+ * The probe-form backward needs lse, o_sa and rk from the same call.
  * Supported: bf16, head_dim 128, heads_q / heads_kv in {1, 2, 4, 8}, p_per_query 0; any other
  * valid desc returns PLX_ERR_UNSUPPORTED.  Masks, empty rows and split_rows as in the forward.
  */
 plx_status parallax_attn_fwd_probe(const plx_attn_desc* desc,
                                    const void* q, const void* k, const void* v, const void* rho,
-                                   float* out, float* lse,
+                                   float* out, float* lse, float* o_sa, float* rk,
+                                   void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Probe-form backward.  Bytes of workspace needed for `desc`; returns 0 for an invalid desc. */
+size_t parallax_attn_bwd_probe_workspace(const plx_attn_desc* desc);
+
+/*
+ * Probe-form backward: gradients of sum(dout * out) of parallax_attn_fwd_probe.  The pages give
+ * no backward; this is the chain rule of that forward with rho an input:
+ *   drho_i = (g_i.o_i) kbar_i - sum_j p_ij (g_i.v_j) k_j      (g = dout)
+ * and dq, dk, dv as in the backward above with u_i = -rho_i and no projector term.
+ *   q, k, v, rho        as in the probe-form forward
+ *   out, lse, o_sa, rk  that forward's outputs for the same inputs (all required)
+ *   dout  [B][Tq][Hq][d]   dtype desc->dtype
+ *   dq, drho [B][Tq][Hq][d] fp32     dk, dv [B][Tk][Hkv][d] fp32 (summed over the query heads of each group)
+ * Every gradient is overwritten.  Results are deterministic.
+ * Supported: bf16, head_dim 128, heads_q / heads_kv in {1, 2, 4}, p_per_query 0; any other valid desc
+ * returns PLX_ERR_UNSUPPORTED.  Empty problems write zero gradients.
+ */
+plx_status parallax_attn_bwd_probe(const plx_attn_desc* desc,
+                                   const void* q, const void* k, const void* v, const void* rho,
+                                   const float* out, const void* dout,
+                                   const float* lse, const float* o_sa, const float* rk,
+                                   float* dq, float* dk, float* dv, float* drho,
                                    void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* Backward.  Bytes of workspace needed for `desc`; returns 0 for an invalid desc. */

@@ -12,7 +12,8 @@ Functions (same names as the C entry points):
     out, lse, kbar, o = parallax_attn_fwd(q, k, v, P, causal=True, window=0, scale=None)
     dq, dk, dv, dP    = parallax_attn_bwd(q, k, v, P, out, dout, lse, kbar, o, causal=True, ...)
     out               = parallax_attn_decode(q, k_cache, v_cache, P, seqlens=None, window=0, scale=None)
-    out, lse          = parallax_attn_fwd_probe(q, k, v, rho, causal=True, window=0, scale=None)
+    out, lse, o, rk   = parallax_attn_fwd_probe(q, k, v, rho, causal=True, window=0, scale=None)
+    dq, dk, dv, drho  = parallax_attn_bwd_probe(q, k, v, rho, out, dout, lse, o, rk, causal=True, ...)
 
 Layouts: q [B,Tq,Hq,d] (decode [B,Hq,d]); k, v [B,Tk,Hkv,d]; P [Hq,d,d] (or
 [B,Tq,Hq,d,d] per query, forward only); outputs float32.
@@ -59,7 +60,10 @@ SIGNATURES = {
     "parallax_attn_fwd_workspace": (_sz, [_DESC]),
     "parallax_attn_fwd": (_st, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "parallax_attn_fwd_probe_workspace": (_sz, [_DESC]),
-    "parallax_attn_fwd_probe": (_st, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "parallax_attn_fwd_probe": (_st, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "parallax_attn_bwd_probe_workspace": (_sz, [_DESC]),
+    "parallax_attn_bwd_probe": (_st, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "parallax_attn_bwd_workspace": (_sz, [_DESC]),
     "parallax_attn_bwd": (_st, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -158,7 +162,7 @@ def parallax_attn_fwd(q, k, v, P, causal=True, window=0, scale=None, split_rows=
 
 
 def parallax_attn_fwd_probe(q, k, v, rho, causal=True, window=0, scale=None, split_rows=-1):
-    """Probe-form forward, rho [B,Tq,Hq,d] like q; returns (out, lse), float32 (see include/parallax.h)."""
+    """Probe-form forward, rho [B,Tq,Hq,d] like q; returns (out, lse, o_sa, rk), float32 (see include/parallax.h)."""
     B, Tq, Hq, d = q.shape
     Tk, Hkv = k.shape[1], k.shape[2]
     dt = _dtype_code(q)
@@ -170,12 +174,44 @@ def parallax_attn_fwd_probe(q, k, v, rho, causal=True, window=0, scale=None, spl
     f32 = dict(dtype=torch.float32, device=q.device)
     out = torch.empty((B, Tq, Hq, d), **f32)
     lse = torch.empty((B, Hq, Tq), **f32)
+    osa = torch.empty((B, Tq, Hq, d), **f32)
+    rk = torch.empty((B, Hq, Tq), **f32)
     lib = get_lib()
     nws = lib.parallax_attn_fwd_probe_workspace(ctypes.byref(desc))
     ws = _workspace(nws, q.device)
     _check(lib.parallax_attn_fwd_probe(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(rho), _ptr(out),
-                                       _ptr(lse), _ptr(ws), nws, _stream()))
-    return out, lse
+                                       _ptr(lse), _ptr(osa), _ptr(rk), _ptr(ws), nws, _stream()))
+    return out, lse, osa, rk
+
+
+def parallax_attn_bwd_probe(q, k, v, rho, out, dout, lse, o_sa, rk, causal=True, window=0, scale=None,
+                            split_rows=-1):
+    """Probe-form backward; returns (dq, dk, dv, drho), all float32 (see include/parallax.h)."""
+    B, Tq, Hq, d = q.shape
+    Tk, Hkv = k.shape[1], k.shape[2]
+    dt = _dtype_code(q)
+    dev = q.device
+    _need(k, "k", q.dtype, (B, Tk, Hkv, d), dev)
+    _need(v, "v", q.dtype, (B, Tk, Hkv, d), dev)
+    _need(rho, "rho", q.dtype, (B, Tq, Hq, d), dev)
+    _need(dout, "dout", q.dtype, (B, Tq, Hq, d), dev)
+    for name, t in (("out", out), ("o_sa", o_sa)):
+        _need(t, name, torch.float32, (B, Tq, Hq, d), dev)
+    for name, t in (("lse", lse), ("rk", rk)):
+        _need(t, name, torch.float32, (B, Hq, Tq), dev)
+    desc = make_desc(B, Tq, Tk, Hq, Hkv, d, causal, window, scale, dt, False, split_rows)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq = torch.empty((B, Tq, Hq, d), **f32)
+    dk = torch.empty((B, Tk, Hkv, d), **f32)
+    dv = torch.empty((B, Tk, Hkv, d), **f32)
+    drho = torch.empty((B, Tq, Hq, d), **f32)
+    lib = get_lib()
+    nws = lib.parallax_attn_bwd_probe_workspace(ctypes.byref(desc))
+    ws = _workspace(nws, dev)
+    _check(lib.parallax_attn_bwd_probe(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(rho), _ptr(out),
+                                       _ptr(dout), _ptr(lse), _ptr(o_sa), _ptr(rk), _ptr(dq), _ptr(dk),
+                                       _ptr(dv), _ptr(drho), _ptr(ws), nws, _stream()))
+    return dq, dk, dv, drho
 
 
 def parallax_attn_bwd(q, k, v, P, out, dout, lse, kbar, o_sa, causal=True, window=0, scale=None,
@@ -232,3 +268,4 @@ fwd = parallax_attn_fwd
 bwd = parallax_attn_bwd
 decode = parallax_attn_decode
 fwd_probe = parallax_attn_fwd_probe
+bwd_probe = parallax_attn_bwd_probe

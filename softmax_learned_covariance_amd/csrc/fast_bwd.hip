@@ -98,6 +98,10 @@ struct RowParams {
   uint32_t* maxbits;
   float *dq, *u32, *dkb32, *x32, *du32, *st_alpha, *st_delta;
   float* rstat;        // per 32-row tile: lse (log2 units), 1 - alpha, Delta of each row, [B][Hq][Tq_pad / 32][3][32]
+  // probe form (u = -rho supplied per row, no projector): rho, rho . kbar from the forward, drho out
+  const u16* rho;
+  const float* rk;
+  float* drho;
   int B, Tq, Tk, Tk_pad, Tq_pad, Hq, Hkv, G, causal, window;
   float scale;
   int row_begin, row_end, rows_per_block, n_rb;
@@ -131,7 +135,61 @@ __device__ __forceinline__ void row_tile_dma(const RowParams& p, RowTiles& T, in
   }
 }
 
-template <bool SPLIT, bool DQ_PASS>
+// g.o, g.out and |g|_1 of the lane's query row (its two half-lanes combined).
+__device__ __forceinline__ void row_dots(const RowParams& p, int64_t qoff, bool row_ok, int hh, float& go,
+                                         float& gout, float& gabs) {
+  go = 0.f;
+  gout = 0.f;
+  gabs = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d = 32 * mt + 8 * j + 4 * hh;
+      float gv[4] = {0.f, 0.f, 0.f, 0.f};
+      float4 ov = {0.f, 0.f, 0.f, 0.f}, outv = {0.f, 0.f, 0.f, 0.f};
+      if (row_ok) {
+        load4_bf16(p.dout + qoff + d, gv);
+        ov = *reinterpret_cast<const float4*>(p.osa + qoff + d);
+        outv = *reinterpret_cast<const float4*>(p.out + qoff + d);
+      }
+      go += gv[0] * ov.x + gv[1] * ov.y + gv[2] * ov.z + gv[3] * ov.w;
+      gout += gv[0] * outv.x + gv[1] * outv.y + gv[2] * outv.z + gv[3] * outv.w;
+      gabs += fabsf(gv[0]) + fabsf(gv[1]) + fabsf(gv[2]) + fabsf(gv[3]);
+    }
+  go = xor32_sum(go);
+  gout = xor32_sum(gout);
+  gabs = xor32_sum(gabs);
+}
+
+// Probe form: the per-row vectors the key-major pass needs, from the supplied probe.  u = -rho,
+// dkbar = -(g.o) u = (g.o) rho, drho = -du, and dq starts at 0 (no projector term).  Writes u, dkbar,
+// drho and the zero dq of the lane's half-row; `du` holds du in the accumulator layout.
+__device__ __forceinline__ void probe_row_vectors(const RowParams& p, int64_t qoff, bool row_ok, int hh, float go,
+                                                  const f32x16 (&du)[4], f32x16 (&u)[4], f32x16 (&dkb)[4]) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d = 32 * mt + 8 * j + 4 * hh;
+      float rv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (row_ok) load4_bf16(p.rho + qoff + d, rv);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        u[mt][4 * j + e] = -rv[e];
+        dkb[mt][4 * j + e] = go * rv[e];
+      }
+      if (row_ok) {
+        const int r = 4 * j;
+        *reinterpret_cast<float4*>(p.drho + qoff + d) = float4{-du[mt][r], -du[mt][r + 1], -du[mt][r + 2], -du[mt][r + 3]};
+        *reinterpret_cast<float4*>(p.dq + qoff + d) = float4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<float4*>(p.u32 + qoff + d) = float4{u[mt][r], u[mt][r + 1], u[mt][r + 2], u[mt][r + 3]};
+        *reinterpret_cast<float4*>(p.dkb32 + qoff + d) = float4{dkb[mt][r], dkb[mt][r + 1], dkb[mt][r + 2], dkb[mt][r + 3]};
+      }
+    }
+}
+
+template <bool SPLIT, bool DQ_PASS, bool PROBE>
 __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
   __shared__ RowTiles T;
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, ql = l & 31, hh = l >> 5;
@@ -163,7 +221,7 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
   const float maxK = mx(MB, kMaxK);
   const float cS = p.scale * kLog2e / (sQ * sK);
   const float boundG = 128.f * mx(MB, kMaxDO) * mx(MB, kMaxV);
-  const float sPG = range_scale(boundG);
+  const float sPG = range_scale(PROBE ? 2.f * boundG : boundG);   // probe form: |G - g.o| <= 2 boundG
 
   const int64_t qoff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * kD;
   const int64_t soff = (static_cast<int64_t>(b) * p.Hq + h) * p.Tq + (row_ok ? row : 0);
@@ -187,6 +245,23 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
   f16x8 qB[8], gB[8];
   load_row_operand(p.q + qoff, row_ok, hh, sQ, qB);
   load_row_operand(p.dout + qoff, row_ok, hh, sG, gB);
+
+  // probe form: du = sum_j p_j (G_j - g.o) k_j directly (kbar is not an input), so g.o comes first
+  float go_pre = 0.f;
+  if constexpr (PROBE) {
+#pragma unroll
+    for (int d = 4 * hh; d < kD; d += 8) {
+      float gv[4] = {0.f, 0.f, 0.f, 0.f};
+      float4 ov = {0.f, 0.f, 0.f, 0.f};
+      if (row_ok) {
+        load4_bf16(p.dout + qoff + d, gv);
+        ov = *reinterpret_cast<const float4*>(p.osa + qoff + d);
+      }
+      go_pre += gv[0] * ov.x + gv[1] * ov.y + gv[2] * ov.z + gv[3] * ov.w;
+    }
+    go_pre = xor32_sum(go_pre);
+  }
+  const float goS = go_pre * sG * sV;   // g.o in the units of the G tile
 
   // ---------------- pass 1: du ----------------
   f32x16 accDU[4];
@@ -216,7 +291,7 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
           const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
           float sv = S[r];
           if (!full && (key >= r_kend || key < r_kbeg)) sv = -INFINITY;
-          pg[r] = __builtin_amdgcn_exp2f(fmaf(sv, cS, -lse2)) * Gt[r] * fPG;
+          pg[r] = __builtin_amdgcn_exp2f(fmaf(sv, cS, -lse2)) * (PROBE ? Gt[r] - goS : Gt[r]) * fPG;
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -237,139 +312,145 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
 
   // ---------------- epilogue: u, alpha, P du, dkbar, Delta ----------------
   // row vectors in the accumulator layout: element (mt, r) is d = 32 mt + 8 (r/4) + 4 hh + r%4
-  float go = 0.f, gout = 0.f, gabs = 0.f;
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d = 32 * mt + 8 * j + 4 * hh;
-      float gv[4] = {0.f, 0.f, 0.f, 0.f};
-      float4 ov = {0.f, 0.f, 0.f, 0.f}, outv = {0.f, 0.f, 0.f, 0.f};
-      if (row_ok) {
-        load4_bf16(p.dout + qoff + d, gv);
-        ov = *reinterpret_cast<const float4*>(p.osa + qoff + d);
-        outv = *reinterpret_cast<const float4*>(p.out + qoff + d);
-      }
-      go += gv[0] * ov.x + gv[1] * ov.y + gv[2] * ov.z + gv[3] * ov.w;
-      gout += gv[0] * outv.x + gv[1] * outv.y + gv[2] * outv.z + gv[3] * outv.w;
-      gabs += fabsf(gv[0]) + fabsf(gv[1]) + fabsf(gv[2]) + fabsf(gv[3]);
-    }
-  go = xor32_sum(go);
-  gout = xor32_sum(gout);
-  gabs = xor32_sum(gabs);
-  // kbar, x = q - kbar (written out for dP), du = sum p G k - (g.o) kbar (in place, written out)
-  float kbv[4][16], xv[4][16];
-  float xmax = 0.f, dumax = 0.f;
-  {
+  float go, gout, gabs;
+  row_dots(p, qoff, row_ok, hh, go, gout, gabs);
+  if constexpr (PROBE) go = go_pre;   // the value du was formed with
+  f32x16 accU[4], accPD[4];
+  float alpha = 0.f, dkk = 0.f, umax = 0.f, emax = 0.f, u1 = 0.f, e1 = 0.f;
+  if constexpr (PROBE) {
     const float fdu = 1.f / (sPG * sK);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = 32 * mt + 8 * j + 4 * hh;
-        float qv[4] = {0.f, 0.f, 0.f, 0.f};
-        float4 kv = {0.f, 0.f, 0.f, 0.f};
-        if (row_ok) {
-          load4_bf16(p.q + qoff + d, qv);
-          kv = *reinterpret_cast<const float4*>(p.kbar + qoff + d);
-        }
-        const float k4[4] = {kv.x, kv.y, kv.z, kv.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * j + e;
-          kbv[mt][r] = k4[e];
-          xv[mt][r] = qv[e] - k4[e];
-          accDU[mt][r] = accDU[mt][r] * fdu - go * k4[e];
-          xmax = fmaxf(xmax, fabsf(xv[mt][r]));
-          dumax = fmaxf(dumax, fabsf(accDU[mt][r]));
-        }
-        if (row_ok) {
-          *reinterpret_cast<float4*>(p.x32 + qoff + d) =
-              float4{xv[mt][4 * j], xv[mt][4 * j + 1], xv[mt][4 * j + 2], xv[mt][4 * j + 3]};
-          *reinterpret_cast<float4*>(p.du32 + qoff + d) =
-              float4{accDU[mt][4 * j], accDU[mt][4 * j + 1], accDU[mt][4 * j + 2], accDU[mt][4 * j + 3]};
-        }
-      }
-  }
-  xmax = xor32_max(xmax);
-  dumax = xor32_max(dumax);
-  const float sX = range_scale(xmax), sDU = range_scale(dumax);
-  // U^T = P16t X^T, then (P du)^T = P16 du^T
-  f32x16 accU[4], accPD[4];
-  {
-    f16x8 xB[8], xL[SPLIT ? 8 : 1];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) to_operand(&xv[s >> 1][(s & 1) * 8], sX, xB[s], SPLIT ? &xL[SPLIT ? s : 0] : nullptr);
-    const _Float16* prt = p.p16t + (static_cast<int64_t>(h) * kD + ql) * kD + hh * 8;
-#pragma unroll
-    for (int am = 0; am < 4; ++am) {
-      accU[am] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const f16x8 at = *reinterpret_cast<const f16x8*>(prt + 32 * am * kD + 16 * s);
-        accU[am] = mfma(at, xB[s], accU[am]);
-        if constexpr (SPLIT) accU[am] = mfma(at, xL[SPLIT ? s : 0], accU[am]);
-      }
-    }
-  }
-  {
-    f16x8 dB[8], dL[SPLIT ? 8 : 1];
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-      tile_operand(accDU[s >> 1], s & 1, sDU, dB[s], SPLIT ? &dL[SPLIT ? s : 0] : nullptr);
-    const _Float16* pr = p.p16 + (static_cast<int64_t>(h) * kD + ql) * kD + hh * 8;
-#pragma unroll
-    for (int am = 0; am < 4; ++am) {
-      accPD[am] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const f16x8 a = *reinterpret_cast<const f16x8*>(pr + 32 * am * kD + 16 * s);
-        accPD[am] = mfma(a, dB[s], accPD[am]);
-        if constexpr (SPLIT) accPD[am] = mfma(a, dL[SPLIT ? s : 0], accPD[am]);
-      }
-    }
-  }
-  // u (in accU), dq0 = P du (written to dq now, completed after pass 2), dkbar (in accPD), alpha, Delta
-  float alpha = 0.f, dkk = 0.f, umax = 0.f, emax = 0.f, u1 = 0.f, e1 = 0.f;
-  {
-    const float fu = 1.f / (sX * sP), fpd = 1.f / (sP * sDU);
+    for (int mt = 0; mt < 4; ++mt) accDU[mt] *= fdu;
+    probe_row_vectors(p, qoff, row_ok, hh, go, accDU, accU, accPD);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = 32 * mt + 8 * j + 4 * hh;
-        float pd4[4];
+      for (int r = 0; r < 16; ++r) {
+        umax = fmaxf(umax, fabsf(accU[mt][r]));
+        emax = fmaxf(emax, fabsf(accPD[mt][r]));
+        u1 += fabsf(accU[mt][r]);
+        e1 += fabsf(accPD[mt][r]);
+      }
+    umax = xor32_max(umax);
+    emax = xor32_max(emax);
+    u1 = xor32_sum(u1);
+    e1 = xor32_sum(e1);
+    const float rk = row_ok ? p.rk[soff] : 0.f;   // rho . kbar
+    alpha = -rk;                                  // u . kbar
+    dkk = go * rk;                                // dkbar . kbar
+  } else {
+    // kbar, x = q - kbar (written out for dP), du = sum p G k - (g.o) kbar (in place, written out)
+    float kbv[4][16], xv[4][16];
+    float xmax = 0.f, dumax = 0.f;
+    {
+      const float fdu = 1.f / (sPG * sK);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * j + e;
-          const float u = accU[mt][r] * fu;
-          const float pd = accPD[mt][r] * fpd;
-          const float dk = -go * u - pd;
-          pd4[e] = pd;
-          accU[mt][r] = u;
-          accPD[mt][r] = dk;
-          alpha += u * kbv[mt][r];
-          dkk += dk * kbv[mt][r];
-          umax = fmaxf(umax, fabsf(u));
-          emax = fmaxf(emax, fabsf(dk));
-          u1 += fabsf(u);
-          e1 += fabsf(dk);
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d = 32 * mt + 8 * j + 4 * hh;
+          float qv[4] = {0.f, 0.f, 0.f, 0.f};
+          float4 kv = {0.f, 0.f, 0.f, 0.f};
+          if (row_ok) {
+            load4_bf16(p.q + qoff + d, qv);
+            kv = *reinterpret_cast<const float4*>(p.kbar + qoff + d);
+          }
+          const float k4[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * j + e;
+            kbv[mt][r] = k4[e];
+            xv[mt][r] = qv[e] - k4[e];
+            accDU[mt][r] = accDU[mt][r] * fdu - go * k4[e];
+            xmax = fmaxf(xmax, fabsf(xv[mt][r]));
+            dumax = fmaxf(dumax, fabsf(accDU[mt][r]));
+          }
+          if (row_ok) {
+            *reinterpret_cast<float4*>(p.x32 + qoff + d) =
+                float4{xv[mt][4 * j], xv[mt][4 * j + 1], xv[mt][4 * j + 2], xv[mt][4 * j + 3]};
+            *reinterpret_cast<float4*>(p.du32 + qoff + d) =
+                float4{accDU[mt][4 * j], accDU[mt][4 * j + 1], accDU[mt][4 * j + 2], accDU[mt][4 * j + 3]};
+          }
         }
-        if (row_ok) {
-          *reinterpret_cast<float4*>(p.dq + qoff + d) = float4{pd4[0], pd4[1], pd4[2], pd4[3]};
-          *reinterpret_cast<float4*>(p.u32 + qoff + d) =
-              float4{accU[mt][4 * j], accU[mt][4 * j + 1], accU[mt][4 * j + 2], accU[mt][4 * j + 3]};
-          *reinterpret_cast<float4*>(p.dkb32 + qoff + d) =
-              float4{accPD[mt][4 * j], accPD[mt][4 * j + 1], accPD[mt][4 * j + 2], accPD[mt][4 * j + 3]};
+    }
+    xmax = xor32_max(xmax);
+    dumax = xor32_max(dumax);
+    const float sX = range_scale(xmax), sDU = range_scale(dumax);
+    // U^T = P16t X^T, then (P du)^T = P16 du^T
+    {
+      f16x8 xB[8], xL[SPLIT ? 8 : 1];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) to_operand(&xv[s >> 1][(s & 1) * 8], sX, xB[s], SPLIT ? &xL[SPLIT ? s : 0] : nullptr);
+      const _Float16* prt = p.p16t + (static_cast<int64_t>(h) * kD + ql) * kD + hh * 8;
+#pragma unroll
+      for (int am = 0; am < 4; ++am) {
+        accU[am] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const f16x8 at = *reinterpret_cast<const f16x8*>(prt + 32 * am * kD + 16 * s);
+          accU[am] = mfma(at, xB[s], accU[am]);
+          if constexpr (SPLIT) accU[am] = mfma(at, xL[SPLIT ? s : 0], accU[am]);
         }
       }
+    }
+    {
+      f16x8 dB[8], dL[SPLIT ? 8 : 1];
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        tile_operand(accDU[s >> 1], s & 1, sDU, dB[s], SPLIT ? &dL[SPLIT ? s : 0] : nullptr);
+      const _Float16* pr = p.p16 + (static_cast<int64_t>(h) * kD + ql) * kD + hh * 8;
+#pragma unroll
+      for (int am = 0; am < 4; ++am) {
+        accPD[am] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const f16x8 a = *reinterpret_cast<const f16x8*>(pr + 32 * am * kD + 16 * s);
+          accPD[am] = mfma(a, dB[s], accPD[am]);
+          if constexpr (SPLIT) accPD[am] = mfma(a, dL[SPLIT ? s : 0], accPD[am]);
+        }
+      }
+    }
+    // u (in accU), dq0 = P du (written to dq now, completed after pass 2), dkbar (in accPD), alpha, Delta
+    {
+      const float fu = 1.f / (sX * sP), fpd = 1.f / (sP * sDU);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d = 32 * mt + 8 * j + 4 * hh;
+          float pd4[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * j + e;
+            const float u = accU[mt][r] * fu;
+            const float pd = accPD[mt][r] * fpd;
+            const float dk = -go * u - pd;
+            pd4[e] = pd;
+            accU[mt][r] = u;
+            accPD[mt][r] = dk;
+            alpha += u * kbv[mt][r];
+            dkk += dk * kbv[mt][r];
+            umax = fmaxf(umax, fabsf(u));
+            emax = fmaxf(emax, fabsf(dk));
+            u1 += fabsf(u);
+            e1 += fabsf(dk);
+          }
+          if (row_ok) {
+            *reinterpret_cast<float4*>(p.dq + qoff + d) = float4{pd4[0], pd4[1], pd4[2], pd4[3]};
+            *reinterpret_cast<float4*>(p.u32 + qoff + d) =
+                float4{accU[mt][4 * j], accU[mt][4 * j + 1], accU[mt][4 * j + 2], accU[mt][4 * j + 3]};
+            *reinterpret_cast<float4*>(p.dkb32 + qoff + d) =
+                float4{accPD[mt][4 * j], accPD[mt][4 * j + 1], accPD[mt][4 * j + 2], accPD[mt][4 * j + 3]};
+          }
+        }
+    }
+    alpha = xor32_sum(alpha);
+    dkk = xor32_sum(dkk);
+    umax = xor32_max(umax);
+    emax = xor32_max(emax);
+    u1 = xor32_sum(u1);
+    e1 = xor32_sum(e1);
   }
-  alpha = xor32_sum(alpha);
-  dkk = xor32_sum(dkk);
-  umax = xor32_max(umax);
-  emax = xor32_max(emax);
-  u1 = xor32_sum(u1);
-  e1 = xor32_sum(e1);
   const float delta = gout + dkk;
   if (row_ok && hh == 0) {
     p.st_alpha[soff] = alpha;
@@ -497,6 +578,7 @@ __device__ __forceinline__ void row_tile_dma8(const RowParams& p, RowTiles& T, i
   }
 }
 
+template <bool PROBE>
 __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
   __shared__ RowTiles T;
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, ql = l & 31, hh = l >> 5;
@@ -527,7 +609,7 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
   const float sG = range_scale(mx(MB, kMaxDO));
   const float cS = p.scale * kLog2e / (sQ * sK);
   const float boundG = 128.f * mx(MB, kMaxDO) * mx(MB, kMaxV);
-  const float sPG = range_scale(boundG);
+  const float sPG = range_scale(PROBE ? 2.f * boundG : boundG);   // probe form: |G - g.o| <= 2 boundG
 
   const int64_t qoff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * kD;
   const int64_t soff = (static_cast<int64_t>(b) * p.Hq + h) * p.Tq + (row_ok ? row : 0);
@@ -551,6 +633,23 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
   f16x8 qB[8], gB[8];
   load_row_operand(p.q + qoff, row_ok, hh, sQ, qB);
   load_row_operand(p.dout + qoff, row_ok, hh, sG, gB);
+
+  // probe form: du = sum_j p_j (G_j - g.o) k_j directly (kbar is not an input), so g.o comes first
+  float go_pre = 0.f;
+  if constexpr (PROBE) {
+#pragma unroll
+    for (int d = 4 * hh; d < kD; d += 8) {
+      float gv[4] = {0.f, 0.f, 0.f, 0.f};
+      float4 ov = {0.f, 0.f, 0.f, 0.f};
+      if (row_ok) {
+        load4_bf16(p.dout + qoff + d, gv);
+        ov = *reinterpret_cast<const float4*>(p.osa + qoff + d);
+      }
+      go_pre += gv[0] * ov.x + gv[1] * ov.y + gv[2] * ov.z + gv[3] * ov.w;
+    }
+    go_pre = xor32_sum(go_pre);
+  }
+  const float goS = go_pre * sG * sV;   // g.o in the units of the G tile
 
   // ---------------- du = sum_j p_j G_j k_j (scaled) ----------------
   f32x16 accDU[4];
@@ -601,7 +700,7 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
         }
         float pg[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) pg[r] = __builtin_amdgcn_exp2f(fmaf(S[r], cS, -lse2)) * Gt[r] * fPG;
+        for (int r = 0; r < 16; ++r) pg[r] = __builtin_amdgcn_exp2f(fmaf(S[r], cS, -lse2)) * (PROBE ? Gt[r] - goS : Gt[r]) * fPG;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           f16x8 hi;
@@ -620,141 +719,154 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
 
   // ---------------- epilogue ----------------
   // row vectors in the accumulator layout: element (mt, r) is d = 32 mt + 8 (r/4) + 4 hh + r%4
-  float go = 0.f, gout = 0.f, gabs = 0.f;
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d = 32 * mt + 8 * j + 4 * hh;
-      float gv[4] = {0.f, 0.f, 0.f, 0.f};
-      float4 ov = {0.f, 0.f, 0.f, 0.f}, outv = {0.f, 0.f, 0.f, 0.f};
-      if (row_ok) {
-        load4_bf16(p.dout + qoff + d, gv);
-        ov = *reinterpret_cast<const float4*>(p.osa + qoff + d);
-        outv = *reinterpret_cast<const float4*>(p.out + qoff + d);
-      }
-      go += gv[0] * ov.x + gv[1] * ov.y + gv[2] * ov.z + gv[3] * ov.w;
-      gout += gv[0] * outv.x + gv[1] * outv.y + gv[2] * outv.z + gv[3] * outv.w;
-      gabs += fabsf(gv[0]) + fabsf(gv[1]) + fabsf(gv[2]) + fabsf(gv[3]);
-    }
-  go = xor32_sum(go);
-  gout = xor32_sum(gout);
-  gabs = xor32_sum(gabs);
-  // du = sum p G k - (g.o) kbar (in place) and x = q - kbar, both written out for dP
-  float xmax = 0.f, dumax = 0.f;
-  {
+  float go, gout, gabs;
+  row_dots(p, qoff, row_ok, hh, go, gout, gabs);
+  if constexpr (PROBE) go = go_pre;   // the value du was formed with
+  float alpha = 0.f, dkk = 0.f, umax = 0.f, emax = 0.f;
+  if constexpr (PROBE) {
+    // u = -rho, dkbar = (g.o) rho, drho = -du, dq starts at 0 (no projector term)
     const float fdu = 1.f / (sPG * sK);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = 32 * mt + 8 * j + 4 * hh;
-        float qv[4] = {0.f, 0.f, 0.f, 0.f};
-        float4 kv = {0.f, 0.f, 0.f, 0.f};
-        if (row_ok) {
-          load4_bf16(p.q + qoff + d, qv);
-          kv = *reinterpret_cast<const float4*>(p.kbar + qoff + d);
-        }
-        const float k4[4] = {kv.x, kv.y, kv.z, kv.w};
-        float x4[4];
+        float rv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (row_ok) load4_bf16(p.rho + qoff + d, rv);
+        float dr[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = 4 * j + e;
-          x4[e] = qv[e] - k4[e];
-          accDU[mt][r] = accDU[mt][r] * fdu - go * k4[e];
-          xmax = fmaxf(xmax, fabsf(x4[e]));
-          dumax = fmaxf(dumax, fabsf(accDU[mt][r]));
+          dr[e] = -accDU[mt][4 * j + e] * fdu;
+          umax = fmaxf(umax, fabsf(rv[e]));
+          emax = fmaxf(emax, fabsf(go * rv[e]));
         }
         if (row_ok) {
-          *reinterpret_cast<float4*>(p.x32 + qoff + d) = float4{x4[0], x4[1], x4[2], x4[3]};
-          *reinterpret_cast<float4*>(p.du32 + qoff + d) =
-              float4{accDU[mt][4 * j], accDU[mt][4 * j + 1], accDU[mt][4 * j + 2], accDU[mt][4 * j + 3]};
+          *reinterpret_cast<float4*>(p.drho + qoff + d) = float4{dr[0], dr[1], dr[2], dr[3]};
+          *reinterpret_cast<float4*>(p.dq + qoff + d) = float4{0.f, 0.f, 0.f, 0.f};
+          *reinterpret_cast<float4*>(p.u32 + qoff + d) = float4{-rv[0], -rv[1], -rv[2], -rv[3]};
+          *reinterpret_cast<float4*>(p.dkb32 + qoff + d) = float4{go * rv[0], go * rv[1], go * rv[2], go * rv[3]};
         }
       }
-  }
-  xmax = xor32_max(xmax);
-  dumax = xor32_max(dumax);
-  const float sX = range_scale(xmax), sDU = range_scale(dumax);
-  // (P du)^T = P16 du^T
-  f32x16 accPD[4];
-  {
-    f16x8 dB[8];
+    umax = xor32_max(umax);
+    emax = xor32_max(emax);
+    const float rk = row_ok ? p.rk[soff] : 0.f;   // rho . kbar
+    alpha = -rk;                                  // u . kbar
+    dkk = go * rk;                                // dkbar . kbar
+  } else {
+    // du = sum p G k - (g.o) kbar (in place) and x = q - kbar, both written out for dP
+    float xmax = 0.f, dumax = 0.f;
+    {
+      const float fdu = 1.f / (sPG * sK);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) tile_operand(accDU[s >> 1], s & 1, sDU, dB[s], nullptr);
-    const _Float16* pr = p.p16 + (static_cast<int64_t>(h) * kD + ql) * kD + hh * 8;
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int am = 0; am < 4; ++am) {
-      accPD[am] = f32x16{};
+        for (int j = 0; j < 4; ++j) {
+          const int d = 32 * mt + 8 * j + 4 * hh;
+          float qv[4] = {0.f, 0.f, 0.f, 0.f};
+          float4 kv = {0.f, 0.f, 0.f, 0.f};
+          if (row_ok) {
+            load4_bf16(p.q + qoff + d, qv);
+            kv = *reinterpret_cast<const float4*>(p.kbar + qoff + d);
+          }
+          const float k4[4] = {kv.x, kv.y, kv.z, kv.w};
+          float x4[4];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) accPD[am] = mfma(*reinterpret_cast<const f16x8*>(pr + 32 * am * kD + 16 * s), dB[s], accPD[am]);
-    }
-  }
-  // U^T = P16t X^T, with x = q - kbar re-read: operand s holds d = 16 s + 8 (e/4) + 4 hh + e%4
-  f32x16 accU[4];
-  {
-    f16x8 xB[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      float x8[8];
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int d = 16 * s + 8 * half + 4 * hh;
-        float qv[4] = {0.f, 0.f, 0.f, 0.f};
-        float4 kv = {0.f, 0.f, 0.f, 0.f};
-        if (row_ok) {
-          load4_bf16(p.q + qoff + d, qv);
-          kv = *reinterpret_cast<const float4*>(p.kbar + qoff + d);
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * j + e;
+            x4[e] = qv[e] - k4[e];
+            accDU[mt][r] = accDU[mt][r] * fdu - go * k4[e];
+            xmax = fmaxf(xmax, fabsf(x4[e]));
+            dumax = fmaxf(dumax, fabsf(accDU[mt][r]));
+          }
+          if (row_ok) {
+            *reinterpret_cast<float4*>(p.x32 + qoff + d) = float4{x4[0], x4[1], x4[2], x4[3]};
+            *reinterpret_cast<float4*>(p.du32 + qoff + d) =
+                float4{accDU[mt][4 * j], accDU[mt][4 * j + 1], accDU[mt][4 * j + 2], accDU[mt][4 * j + 3]};
+          }
         }
-        x8[4 * half + 0] = qv[0] - kv.x;
-        x8[4 * half + 1] = qv[1] - kv.y;
-        x8[4 * half + 2] = qv[2] - kv.z;
-        x8[4 * half + 3] = qv[3] - kv.w;
+    }
+    xmax = xor32_max(xmax);
+    dumax = xor32_max(dumax);
+    const float sX = range_scale(xmax), sDU = range_scale(dumax);
+    // (P du)^T = P16 du^T
+    f32x16 accU[4], accPD[4];
+    {
+      f16x8 dB[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) tile_operand(accDU[s >> 1], s & 1, sDU, dB[s], nullptr);
+      const _Float16* pr = p.p16 + (static_cast<int64_t>(h) * kD + ql) * kD + hh * 8;
+#pragma unroll
+      for (int am = 0; am < 4; ++am) {
+        accPD[am] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) accPD[am] = mfma(*reinterpret_cast<const f16x8*>(pr + 32 * am * kD + 16 * s), dB[s], accPD[am]);
       }
-      to_operand(x8, sX, xB[s], nullptr);
     }
-    const _Float16* prt = p.p16t + (static_cast<int64_t>(h) * kD + ql) * kD + hh * 8;
+    // U^T = P16t X^T, with x = q - kbar re-read: operand s holds d = 16 s + 8 (e/4) + 4 hh + e%4
+    {
+      f16x8 xB[8];
 #pragma unroll
-    for (int am = 0; am < 4; ++am) {
-      accU[am] = f32x16{};
+      for (int s = 0; s < 8; ++s) {
+        float x8[8];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) accU[am] = mfma(*reinterpret_cast<const f16x8*>(prt + 32 * am * kD + 16 * s), xB[s], accU[am]);
-    }
-  }
-  // u, dq0 = P du (completed by k_bwd_dq), dkbar = -(g.o) u - P du, alpha = u.kbar, Delta = g.out + dkbar.kbar
-  float alpha = 0.f, dkk = 0.f, umax = 0.f, emax = 0.f;
-  {
-    const float fu = 1.f / (sX * sP), fpd = 1.f / (sP * sDU);
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = 32 * mt + 8 * j + 4 * hh;
-        float4 kv = {0.f, 0.f, 0.f, 0.f};
-        if (row_ok) kv = *reinterpret_cast<const float4*>(p.kbar + qoff + d);
-        const float k4[4] = {kv.x, kv.y, kv.z, kv.w};
-        float u4[4], pd4[4], dk4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * j + e;
-          u4[e] = accU[mt][r] * fu;
-          pd4[e] = accPD[mt][r] * fpd;
-          dk4[e] = -go * u4[e] - pd4[e];
-          alpha += u4[e] * k4[e];
-          dkk += dk4[e] * k4[e];
-          umax = fmaxf(umax, fabsf(u4[e]));
-          emax = fmaxf(emax, fabsf(dk4[e]));
+        for (int half = 0; half < 2; ++half) {
+          const int d = 16 * s + 8 * half + 4 * hh;
+          float qv[4] = {0.f, 0.f, 0.f, 0.f};
+          float4 kv = {0.f, 0.f, 0.f, 0.f};
+          if (row_ok) {
+            load4_bf16(p.q + qoff + d, qv);
+            kv = *reinterpret_cast<const float4*>(p.kbar + qoff + d);
+          }
+          x8[4 * half + 0] = qv[0] - kv.x;
+          x8[4 * half + 1] = qv[1] - kv.y;
+          x8[4 * half + 2] = qv[2] - kv.z;
+          x8[4 * half + 3] = qv[3] - kv.w;
         }
-        if (row_ok) {
-          *reinterpret_cast<float4*>(p.dq + qoff + d) = float4{pd4[0], pd4[1], pd4[2], pd4[3]};
-          *reinterpret_cast<float4*>(p.u32 + qoff + d) = float4{u4[0], u4[1], u4[2], u4[3]};
-          *reinterpret_cast<float4*>(p.dkb32 + qoff + d) = float4{dk4[0], dk4[1], dk4[2], dk4[3]};
-        }
+        to_operand(x8, sX, xB[s], nullptr);
       }
+      const _Float16* prt = p.p16t + (static_cast<int64_t>(h) * kD + ql) * kD + hh * 8;
+#pragma unroll
+      for (int am = 0; am < 4; ++am) {
+        accU[am] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) accU[am] = mfma(*reinterpret_cast<const f16x8*>(prt + 32 * am * kD + 16 * s), xB[s], accU[am]);
+      }
+    }
+    // u, dq0 = P du (completed by k_bwd_dq), dkbar = -(g.o) u - P du, alpha = u.kbar, Delta = g.out + dkbar.kbar
+    {
+      const float fu = 1.f / (sX * sP), fpd = 1.f / (sP * sDU);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d = 32 * mt + 8 * j + 4 * hh;
+          float4 kv = {0.f, 0.f, 0.f, 0.f};
+          if (row_ok) kv = *reinterpret_cast<const float4*>(p.kbar + qoff + d);
+          const float k4[4] = {kv.x, kv.y, kv.z, kv.w};
+          float u4[4], pd4[4], dk4[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * j + e;
+            u4[e] = accU[mt][r] * fu;
+            pd4[e] = accPD[mt][r] * fpd;
+            dk4[e] = -go * u4[e] - pd4[e];
+            alpha += u4[e] * k4[e];
+            dkk += dk4[e] * k4[e];
+            umax = fmaxf(umax, fabsf(u4[e]));
+            emax = fmaxf(emax, fabsf(dk4[e]));
+          }
+          if (row_ok) {
+            *reinterpret_cast<float4*>(p.dq + qoff + d) = float4{pd4[0], pd4[1], pd4[2], pd4[3]};
+            *reinterpret_cast<float4*>(p.u32 + qoff + d) = float4{u4[0], u4[1], u4[2], u4[3]};
+            *reinterpret_cast<float4*>(p.dkb32 + qoff + d) = float4{dk4[0], dk4[1], dk4[2], dk4[3]};
+          }
+        }
+    }
+    alpha = xor32_sum(alpha);
+    dkk = xor32_sum(dkk);
+    umax = xor32_max(umax);
+    emax = xor32_max(emax);
   }
-  alpha = xor32_sum(alpha);
-  dkk = xor32_sum(dkk);
-  umax = xor32_max(umax);
-  emax = xor32_max(emax);
   const float delta = gout + dkk;
   if (row_ok && hh == 0) {
     p.st_alpha[soff] = alpha;
@@ -1716,10 +1828,29 @@ bool fast_bwd_supported(const Geom& g) {
 
 size_t fast_bwd_workspace(const Geom& g) { return bwd_layout(g, bwd_split(g), nullptr).bytes; }
 
-hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const void* v, const void* P,
-                           const float* out, const void* dout, const float* lse, const float* kbar,
-                           const float* osa, float* dq, float* dk, float* dv, float* dP, int split_rows,
-                           void* ws, hipStream_t stream) {
+bool fast_probe_bwd_supported(const Geom& g) { return fast_bwd_supported(g); }
+
+size_t fast_probe_bwd_workspace(const Geom& g) { return fast_bwd_workspace(g); }
+
+hipError_t launch_zero_f32(float* x, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_zero4, dim3(256), dim3(256), 0, stream, x, n / 4);
+  return hipGetLastError();
+}
+
+namespace {
+
+struct BwdArgs {
+  const void *q, *k, *v, *P, *dout, *rho;   // rho != nullptr: the probe form (P unused)
+  const float *out, *lse, *kbar, *osa, *rk;
+  float *dq, *dk, *dv, *dP, *drho;
+};
+
+hipError_t bwd_impl(const Geom& g, const BwdArgs& a, int split_rows, void* ws, hipStream_t stream) {
+  const bool probe = a.rho != nullptr;
+  const void *q = a.q, *k = a.k, *v = a.v, *P = a.P, *dout = a.dout;
+  const float *out = a.out, *lse = a.lse, *kbar = a.kbar, *osa = a.osa;
+  float *dq = a.dq, *dk = a.dk, *dv = a.dv, *dP = a.dP;
   // The workspace is sized for the default split; a larger request is clamped to it.
   int split = split_rows < 0 ? bwd_split(g) : split_rows;
   if (split < kMinSplitRows) split = kMinSplitRows;
@@ -1753,6 +1884,9 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
   rp.st_alpha = w.alpha;
   rp.st_delta = w.delta;
   rp.rstat = w.rstat;
+  rp.rho = static_cast<const u16*>(a.rho);
+  rp.rk = a.rk;
+  rp.drho = a.drho;
   rp.Tq_pad = w.Tq_pad;
   rp.B = g.B;
   rp.Tq = g.Tq;
@@ -1781,7 +1915,10 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
     r.row_begin = 0;
     r.row_end = split;
     r.n_rb = (split + r.rows_per_block - 1) / r.rows_per_block;
-    hipLaunchKernelGGL((k_bwd_rows_fast<true, true>), dim3(g.B * g.Hkv * r.n_rb), dim3(256), 0, side.stream, r);
+    if (probe)
+      hipLaunchKernelGGL((k_bwd_rows_fast<true, true, true>), dim3(g.B * g.Hkv * r.n_rb), dim3(256), 0, side.stream, r);
+    else
+      hipLaunchKernelGGL((k_bwd_rows_fast<true, true, false>), dim3(g.B * g.Hkv * r.n_rb), dim3(256), 0, side.stream, r);
   }
   if (split < g.Tq) {
     RowParams r = rp;
@@ -1791,7 +1928,10 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
     r.rows_per_block = 32 * 8 / G;
     r.n_rb = (g.Tq - split + r.rows_per_block - 1) / r.rows_per_block;
     mark_begin(PLX_KERNEL_BWD_ROWS, stream);
-    hipLaunchKernelGGL(k_bwd_du, dim3(g.B * g.Hkv * r.n_rb), dim3(512), 0, stream, r);
+    if (probe)
+      hipLaunchKernelGGL(k_bwd_du<true>, dim3(g.B * g.Hkv * r.n_rb), dim3(512), 0, stream, r);
+    else
+      hipLaunchKernelGGL(k_bwd_du<false>, dim3(g.B * g.Hkv * r.n_rb), dim3(512), 0, stream, r);
     mark_end(PLX_KERNEL_BWD_ROWS, stream);
   }
   e = hipGetLastError();
@@ -1893,14 +2033,60 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
     hipLaunchKernelGGL(k_bwd_dq, dim3(g.B * g.Hkv * dp.n_rb), dim3(512), 0, stream, dp);
     mark_end(PLX_KERNEL_BWD_DQ, stream);
   }
-  // dP = sum over rows of x du^T
-  const int R = g.B * g.Tq;
-  hipLaunchKernelGGL(k_dp_partial, dim3(g.Hq * w.nchunks), dim3(256), 0, stream, w.x32, w.du32, w.part, R, g.Hq);
-  const int nred = (g.Hq * kD * kD + 255) / 256;
-  hipLaunchKernelGGL(k_dp_reduce, dim3(nred), dim3(256), 0, stream, w.part, dP, w.nchunks, g.Hq);
+  if (!probe) {
+    // dP = sum over rows of x du^T
+    const int R = g.B * g.Tq;
+    hipLaunchKernelGGL(k_dp_partial, dim3(g.Hq * w.nchunks), dim3(256), 0, stream, w.x32, w.du32, w.part, R, g.Hq);
+    const int nred = (g.Hq * kD * kD + 255) / 256;
+    hipLaunchKernelGGL(k_dp_reduce, dim3(nred), dim3(256), 0, stream, w.part, dP, w.nchunks, g.Hq);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return side_join(side);
+}
+
+}  // namespace
+
+hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const void* v, const void* P,
+                           const float* out, const void* dout, const float* lse, const float* kbar,
+                           const float* osa, float* dq, float* dk, float* dv, float* dP, int split_rows,
+                           void* ws, hipStream_t stream) {
+  BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.P = P;
+  a.dout = dout;
+  a.out = out;
+  a.lse = lse;
+  a.kbar = kbar;
+  a.osa = osa;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dP = dP;
+  return bwd_impl(g, a, split_rows, ws, stream);
+}
+
+hipError_t launch_fast_probe_bwd(const Geom& g, const void* q, const void* k, const void* v, const void* rho,
+                                 const float* out, const void* dout, const float* lse, const float* osa,
+                                 const float* rk, float* dq, float* dk, float* dv, float* drho, int split_rows,
+                                 void* ws, hipStream_t stream) {
+  BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.rho = rho;
+  a.dout = dout;
+  a.out = out;
+  a.lse = lse;
+  a.osa = osa;
+  a.rk = rk;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.drho = drho;
+  return bwd_impl(g, a, split_rows, ws, stream);
 }
 
 }  // namespace plx

@@ -46,6 +46,7 @@ struct FwdParams {
   const _Float16 *k16, *k16t, *v16t, *p16t;
   const uint32_t* maxbits;
   float *out, *lse, *kbar, *osa;
+  float* rk;        // probe form only: rho . kbar per row, [B][Hq][Tq] (nullable)
   int B, Tq, Tk, Tk_pad, Hq, Hkv, G, causal, window;
   float scale;
   int row_begin, row_end, rows_per_block, n_rb;  // rows [row_begin, row_end)
@@ -682,23 +683,27 @@ __global__ __launch_bounds__(512) void k_fwd_probe(FwdParams p) {
   const bool has = L > 0.f;
   const float invL = has ? 1.f / L : 0.f;
   if (row_ok) {
-    if (p.lse && hh == 0)
-      p.lse[(static_cast<int64_t>(b) * p.Hq + h) * p.Tq + row] = has ? (m_used + __log2f(L)) * kLn2 : -INFINITY;
     const float fo = invL / sV;
     const float fc = fo / sK / (kProbeW * sR);
-    const float a = RS * invL / sK / (kProbeW * sR);
+    const float a = RS * invL / sK / (kProbeW * sR);   // rho . kbar
+    if (hh == 0) {
+      const int64_t soff = (static_cast<int64_t>(b) * p.Hq + h) * p.Tq + row;
+      if (p.lse) p.lse[soff] = has ? (m_used + __log2f(L)) * kLn2 : -INFINITY;
+      if (p.rk) p.rk[soff] = a;
+    }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = 32 * mt + 8 * j + 4 * hh;
-        float r4[4];
+        float r4[4], o4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float o = accO[mt][4 * j + e] * fo;
-          r4[e] = o - accC[mt][4 * j + e] * fc + a * o;
+          o4[e] = accO[mt][4 * j + e] * fo;
+          r4[e] = o4[e] - accC[mt][4 * j + e] * fc + a * o4[e];
         }
         *reinterpret_cast<float4*>(p.out + qoff + d) = float4{r4[0], r4[1], r4[2], r4[3]};
+        if (p.osa) *reinterpret_cast<float4*>(p.osa + qoff + d) = float4{o4[0], o4[1], o4[2], o4[3]};
       }
   }
 }
@@ -782,7 +787,8 @@ bool fast_probe_supported(const Geom& g) { return fast_fwd_supported(g); }
 size_t fast_probe_workspace(const Geom& g) { return staging_layout(nullptr, g.B, g.Tk, g.Hkv, g.Hq).bytes; }
 
 hipError_t launch_fast_probe(const Geom& g, const void* q, const void* k, const void* v, const void* rho,
-                             float* out, float* lse, int split_rows, void* ws, hipStream_t stream) {
+                             float* out, float* lse, float* osa, float* rk, int split_rows, void* ws,
+                             hipStream_t stream) {
   const Staging s = staging_layout(ws, g.B, g.Tk, g.Hkv, g.Hq);
   int split = split_rows < kMinSplitRows ? kMinSplitRows : split_rows;
   if (split > g.Tq) split = g.Tq;
@@ -800,6 +806,8 @@ hipError_t launch_fast_probe(const Geom& g, const void* q, const void* k, const 
     p.maxbits = s.maxbits;
     p.out = out;
     p.lse = lse;
+    p.osa = osa;
+    p.rk = rk;
     p.B = g.B;
     p.Tq = g.Tq;
     p.Tk = g.Tk;

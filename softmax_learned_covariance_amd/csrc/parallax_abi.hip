@@ -208,8 +208,8 @@ size_t parallax_attn_fwd_probe_workspace(const plx_attn_desc* desc) {
 }
 
 plx_status parallax_attn_fwd_probe(const plx_attn_desc* desc, const void* q, const void* k,
-                                   const void* v, const void* rho, float* out, float* lse,
-                                   void* workspace, size_t workspace_bytes, void* hip_stream) {
+                                   const void* v, const void* rho, float* out, float* lse, float* o_sa,
+                                   float* rk, void* workspace, size_t workspace_bytes, void* hip_stream) {
   const char* what = "parallax_attn_fwd_probe";
   plx::Geom g;
   plx_status st = check_desc(desc, what, &g);
@@ -225,7 +225,55 @@ plx_status parallax_attn_fwd_probe(const plx_attn_desc* desc, const void* q, con
   if (st != PLX_OK) return st;
   if (empty) return ok();
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  return hip_status(plx::launch_fast_probe(g, q, k, v, rho, out, lse, split_rows_of(desc), workspace, stream), what);
+  return hip_status(plx::launch_fast_probe(g, q, k, v, rho, out, lse, o_sa, rk, split_rows_of(desc), workspace,
+                                           stream),
+                    what);
+}
+
+size_t parallax_attn_bwd_probe_workspace(const plx_attn_desc* desc) {
+  plx::Geom g;
+  if (check_desc(desc, "parallax_attn_bwd_probe_workspace", &g) != PLX_OK) return 0;
+  if (!plx::fast_probe_bwd_supported(g)) return 0;
+  return plx::fast_probe_bwd_workspace(g);
+}
+
+plx_status parallax_attn_bwd_probe(const plx_attn_desc* desc, const void* q, const void* k, const void* v,
+                                   const void* rho, const float* out, const void* dout, const float* lse,
+                                   const float* o_sa, const float* rk, float* dq, float* dk, float* dv,
+                                   float* drho, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  const char* what = "parallax_attn_bwd_probe";
+  plx::Geom g;
+  plx_status st = check_desc(desc, what, &g);
+  if (st != PLX_OK) return st;
+  // the empty cases only write zeros; the kernels need every extent >= 1
+  plx::Geom gs = g;
+  gs.B = gs.Tq = gs.Tk = 1;
+  if (!plx::fast_probe_bwd_supported(gs))
+    return fail(PLX_ERR_UNSUPPORTED,
+                "%s: only bf16, head_dim 128, heads_q/heads_kv in {1,2,4} and p_per_query 0 are supported", what);
+  const bool rows = g.B > 0 && g.Tq > 0;
+  const bool keys = g.B > 0 && g.Tk > 0;
+  if (rows && (!q || !rho || !out || !dout || !lse || !o_sa || !rk || !dq || !drho))
+    return fail(PLX_ERR_INVALID, "%s: q, rho, out, dout, lse, o_sa, rk, dq and drho must not be NULL", what);
+  if (keys && (!k || !v || !dk || !dv)) return fail(PLX_ERR_INVALID, "%s: k, v, dk and dv must not be NULL", what);
+  const size_t need = plx::fast_probe_bwd_supported(g) ? plx::fast_probe_bwd_workspace(g) : 0;
+  st = check_ws(need, workspace, workspace_bytes, what);
+  if (st != PLX_OK) return st;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  hipError_t e = hipSuccess;
+  if (rows && keys) {
+    e = plx::launch_fast_probe_bwd(g, q, k, v, rho, out, dout, lse, o_sa, rk, dq, dk, dv, drho,
+                                   split_rows_of(desc), workspace, stream);
+  } else {
+    // no pair is visible: every gradient is zero
+    const int64_t nq = static_cast<int64_t>(g.B) * g.Tq * g.Hq * g.d;
+    const int64_t nk = static_cast<int64_t>(g.B) * g.Tk * g.Hkv * g.d;
+    if (rows && e == hipSuccess) e = plx::launch_zero_f32(dq, nq, stream);
+    if (rows && e == hipSuccess) e = plx::launch_zero_f32(drho, nq, stream);
+    if (keys && e == hipSuccess) e = plx::launch_zero_f32(dk, nk, stream);
+    if (keys && e == hipSuccess) e = plx::launch_zero_f32(dv, nk, stream);
+  }
+  return hip_status(e, what);
 }
 
 size_t parallax_attn_bwd_workspace(const plx_attn_desc* desc) {

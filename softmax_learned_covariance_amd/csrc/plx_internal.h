@@ -46,7 +46,16 @@ hipError_t launch_generic_bwd(const Geom& g, const void* q, const void* k, const
 bool fast_probe_supported(const Geom& g);
 size_t fast_probe_workspace(const Geom& g);
 hipError_t launch_fast_probe(const Geom& g, const void* q, const void* k, const void* v, const void* rho,
-                             float* out, float* lse, int split_rows, void* ws, hipStream_t stream);
+                             float* out, float* lse, float* osa, float* rk, int split_rows, void* ws,
+                             hipStream_t stream);
+// Its backward (u = -rho, no projector): dq, dk, dv and drho.
+bool fast_probe_bwd_supported(const Geom& g);
+size_t fast_probe_bwd_workspace(const Geom& g);
+hipError_t launch_fast_probe_bwd(const Geom& g, const void* q, const void* k, const void* v, const void* rho,
+                                 const float* out, const void* dout, const float* lse, const float* osa,
+                                 const float* rk, float* dq, float* dk, float* dv, float* drho, int split_rows,
+                                 void* ws, hipStream_t stream);
+hipError_t launch_zero_f32(float* x, int64_t n, hipStream_t stream);   // n a multiple of 4
 
 bool fast_fwd_supported(const Geom& g);
 size_t fast_fwd_workspace(const Geom& g);

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(plx):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     out = subprocess.run(["nm", "-D", "--defined-only", plx.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (parallax_\w+)", out))
     missing = [n for n in names if n not in exported]
@@ -132,7 +132,7 @@ def test_decode_validation(plx):
 
 def _probe(plx, desc, q=FAKE, rho=FAKE, out=FAKE, ws=FAKE, nws=1 << 40):
     lib = plx.get_lib()
-    return lib.parallax_attn_fwd_probe(ctypes.byref(desc), q, FAKE, FAKE, rho, out, None, ws, nws, None)
+    return lib.parallax_attn_fwd_probe(ctypes.byref(desc), q, FAKE, FAKE, rho, out, None, None, None, ws, nws, None)
 
 
 def test_probe_validation(plx):
@@ -153,6 +153,29 @@ def test_probe_validation(plx):
     assert b"rho" in lib.parallax_last_error()
     assert _probe(plx, d, out=None) == E.PLX_ERR_INVALID
     assert _probe(plx, _desc(plx, B=0, **bf)) == E.PLX_OK
+
+
+def test_probe_backward_validation(plx):
+    E = plx
+    lib = plx.get_lib()
+    bf = dict(dtype=plx.PLX_BF16, d=128)
+
+    def call(desc, ws=FAKE, nws=1 << 40, **null):
+        args = {n: FAKE for n in ("q", "k", "v", "rho", "out", "dout", "lse", "osa", "rk", "dq", "dk", "dv", "drho")}
+        args.update(null)
+        return lib.parallax_attn_bwd_probe(ctypes.byref(desc), *args.values(), ws, nws, None)
+
+    assert call(_desc(plx)) == E.PLX_ERR_UNSUPPORTED                      # fp32
+    assert call(_desc(plx, Hq=8, Hkv=1, **bf)) == E.PLX_ERR_UNSUPPORTED   # 8 query heads per group
+    d = _desc(plx, **bf)
+    need = lib.parallax_attn_bwd_probe_workspace(ctypes.byref(d))
+    assert need > 0
+    assert call(d, nws=need - 1) == E.PLX_ERR_WORKSPACE
+    assert call(d, ws=None, nws=need) == E.PLX_ERR_INVALID
+    for name in ("rho", "rk", "osa", "drho", "dk"):
+        assert call(d, **{name: None}) == E.PLX_ERR_INVALID, name
+    assert call(_desc(plx, B=0, **bf)) == E.PLX_OK
+    assert lib.parallax_attn_bwd_probe_workspace(ctypes.byref(_desc(plx, B=0, **bf))) == 0
 
 
 def test_bench_refuses_more_than_one_gpu():
