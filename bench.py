@@ -9,8 +9,9 @@ decode workload (64 queries against a 32768-long cache) is timed after the
 steps and reported in its own object.  One JSON line goes to stdout; progress
 goes to stderr.
 
-The probe-form forward (caller-supplied probe rho, one pass) is timed on the
-same layer shape after the steps and reported in its own object too.
+The probe-form forward (caller-supplied probe rho, one pass) and a probe-form
+forward + backward step are timed on the same layer shape after the steps and
+reported in their own object too.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode] [--no-probe]
 """
@@ -58,6 +59,12 @@ def probe_flops(w, row_begin=0):
     return 8 * w.head_dim * pairs
 
 
+def probe_bwd_flops(w, row_begin=0):
+    """Probe-form backward: 24d per visible pair (no projector terms)."""
+    pairs, _ = visible_pairs_rows(w, row_begin)
+    return 24 * w.head_dim * pairs
+
+
 def bwd_flops(w, row_begin=0):
     """Backward: 24d per visible pair + 4d^2 per row (P du and the dP outer product)."""
     pairs, rows = visible_pairs_rows(w, row_begin)
@@ -87,7 +94,8 @@ def bwd_keys_flops(w, row_begin=0):
 KERNEL_SOURCES = {"fwd": ["fast_fwd.hip", "fast_common.h"], "bwd_rows": ["fast_bwd.hip", "fast_common.h"],
                   "bwd_keys": ["fast_bwd.hip", "fast_common.h"], "bwd_dq": ["fast_bwd.hip", "fast_common.h"],
                   "decode_pass1": ["fast_decode.hip", "fast_common.h"],
-                  "decode_pass2": ["fast_decode.hip", "fast_common.h"]}
+                  "decode_pass2": ["fast_decode.hip", "fast_common.h"],
+                  "probe": ["fast_fwd.hip", "fast_common.h"]}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_layer17_decode.txt")
 
 
@@ -303,8 +311,28 @@ def main():
             "tflops_per_call": round(probe_flops(w) / dtp / 1e12, 3),
             "kernel": {"avg_ms": round(pavg, 4), "median_ms": round(pms[len(pms) // 2], 4), "launches": len(pms),
                        "algorithmic_flop": pfl, "tflops": round(ptf, 3),
-                       "frac_of_peak": round(ptf / PEAK_F16_TFLOPS, 4)}}
+                       "frac_of_peak": round(ptf / PEAK_F16_TFLOPS, 4)},
+            "roofline": {"bound": "mfma", "achieved": round(ptf, 3), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(ptf / PEAK_F16_TFLOPS, 4),
+                         "traffic": None if measured_traffic("probe") is None else round(measured_traffic("probe"))}}
         log(f"probe forward {dtp * 1e3:.3f} ms/call, kernel {pavg:.3f} ms ({ptf:.0f} TFLOP/s)")
+
+        def probe_step():
+            f = plx.parallax_attn_fwd_probe(q, k, v, rho, split_rows=split)
+            plx.parallax_attn_bwd_probe(q, k, v, rho, f[0], dout, *f[1:], split_rows=split)
+
+        probe_step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(Kp):
+            probe_step()
+        torch.cuda.synchronize()
+        dts = (time.perf_counter() - t0) / Kp
+        sfl = probe_flops(w) + probe_bwd_flops(w)
+        result["probe"]["step"] = {"what": "probe-form forward + backward (dq, dk, dv, drho)",
+                                   "ms_per_step": round(dts * 1e3, 4), "tflops": round(sfl / dts / 1e12, 3),
+                                   "algorithmic_flop": sfl, "steps": Kp}
+        log(f"probe step {dts * 1e3:.3f} ms ({sfl / dts / 1e12:.0f} TFLOP/s)")
         del rho
 
     if not args.no_decode:
