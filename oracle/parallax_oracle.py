@@ -323,6 +323,37 @@ def decode(q, k_cache, v_cache, P, seqlens=None, scale=None):
     return out
 
 
+def decode_paged(q, k_pages, v_pages, block_table, P, seqlens=None, seqlen_k=None, window=0, scale=None):
+    """Decode against a paged cache: key j of sequence b is row j % page_size of page
+    block_table[b][j // page_size].  Each sequence's keys are gathered through its table into a
+    contiguous array (a change of storage only), then the newest ``window`` of them (all when
+    window <= 0) go through ``decode``.
+
+    q [B,Hq,d]; pages [num_pages, page_size, Hkv, d]; block_table [B, max_pages] ints; seqlens [B]
+    (None: every sequence has seqlen_k = max_pages * page_size keys).  Returns out [B,Hq,d].
+    Pinned by: a shuffled page pool with its table equals ``decode`` on the contiguous cache,
+    with ragged lengths that end inside a page and a window.
+    """
+    q = _as_f64(q)
+    k_pages, v_pages = _as_f64(k_pages), _as_f64(v_pages)
+    block_table = np.asarray(block_table)
+    B = q.shape[0]
+    page = k_pages.shape[1]
+    Lmax = block_table.shape[1] * page if seqlen_k is None else int(seqlen_k)
+    out = np.zeros(q.shape)
+    for b in range(B):
+        L = Lmax if seqlens is None else min(max(int(seqlens[b]), 0), Lmax)
+        lo = max(0, L - window) if window > 0 else 0
+        if L - lo == 0:
+            continue
+        j = np.arange(lo, L)
+        pages_of_j = block_table[b, j // page]
+        Kb = k_pages[pages_of_j, j % page]                     # [L - lo, Hkv, d]
+        Vb = v_pages[pages_of_j, j % page]
+        out[b] = decode(q[b:b + 1], Kb[None], Vb[None], P, scale=scale)[0]
+    return out
+
+
 def exact_lla_projector(q, k, causal=True, window=0, scale=None, lam=1e-2):
     """Per-query projector P_i = (Sigma_q,i + lam I)^-1 that turns the operator into exact ridge LLA.
 

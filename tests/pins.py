@@ -377,6 +377,43 @@ def pin_decode(orc):
             _close(out[b, h], want, 1e-10, f"decode batch {b} head {h}")
 
 
+def pin_decode_paged(orc):
+    """A shuffled page pool with its block table gives exactly ``decode`` on the contiguous cache:
+    pages of 4 keys, ragged lengths ending inside a page (and 0), with and without a window."""
+    r = _rng(17)
+    B, L, Hq, Hkv, d, page = 3, 14, 4, 2, 5, 4
+    q = r.standard_normal((B, Hq, d))
+    kc = r.standard_normal((B, L, Hkv, d))
+    vc = r.standard_normal((B, L, Hkv, d))
+    P = r.standard_normal((Hq, d, d)) * 0.4
+    seqlens = np.array([14, 7, 0])
+    npb = (L + page - 1) // page                                 # pages per sequence
+    perm = r.permutation(B * npb + 3)                            # pool with 3 spare pages
+    pool_k = r.standard_normal((B * npb + 3, page, Hkv, d))     # spare slots hold junk
+    pool_v = r.standard_normal((B * npb + 3, page, Hkv, d))
+    table = np.zeros((B, npb), dtype=np.int64)
+    for b in range(B):
+        for t in range(npb):
+            pg = perm[b * npb + t]
+            table[b, t] = pg
+            n = min(page, L - t * page)
+            pool_k[pg, :n] = kc[b, t * page:t * page + n]
+            pool_v[pg, :n] = vc[b, t * page:t * page + n]
+    got = orc.decode_paged(q, pool_k, pool_v, table, P, seqlens=seqlens, seqlen_k=L)
+    want = orc.decode(q, kc, vc, P, seqlens=seqlens)
+    _close(got, want, 0.0, "paged decode vs contiguous")
+    W = 5
+    got = orc.decode_paged(q, pool_k, pool_v, table, P, seqlens=seqlens, seqlen_k=L, window=W)
+    for b in range(B):
+        Lb = seqlens[b]
+        if Lb == 0:
+            _close(got[b], 0.0, 0.0, "paged decode empty sequence")
+            continue
+        lo = max(0, Lb - W)
+        want = orc.decode(q[b:b + 1], kc[b:b + 1, lo:Lb], vc[b:b + 1, lo:Lb], P)
+        _close(got[b], want[0], 0.0, f"paged decode window batch {b}")
+
+
 # ---------------------------------------------------------------------------
 # probe-form pins (out_i = o_i - Sigma_KV^(i) rho_i with rho supplied per row)
 # ---------------------------------------------------------------------------
@@ -531,5 +568,5 @@ FORWARD_PINS = [pin_zero_projector_is_sdpa, pin_bottom_right_alignment, pin_mask
                 pin_exact_lla_is_ridge_wls, pin_covariance_form, pin_constant_values,
                 pin_single_key_rows, pin_affine_values, pin_linear_in_projector, pin_hand_examples]
 BACKWARD_PINS = [pin_bwd_finite_differences, pin_bwd_autograd, pin_bwd_zero_projector_is_sdpa]
-DECODE_PINS = [pin_decode]
+DECODE_PINS = [pin_decode, pin_decode_paged]
 ALL_PINS = FORWARD_PINS + BACKWARD_PINS + DECODE_PINS + PROBE_PINS

@@ -45,6 +45,9 @@ MUTANTS = [
      "                w = p * t\n                out[b, rr, h] = o - (w @ Vj - np.sum(w, axis=1, keepdims=True) * o)",
      "t = Rr @ Kj.T\n                w = p * t\n                out[b, rr, h] = o - (w @ Vj)"),
     ("probe dotted with q", "t = Rr @ Kj.T", "t = Qr @ Kj.T"),
+    ("paged decode page offset", "Kb = k_pages[pages_of_j, j % page]", "Kb = k_pages[pages_of_j, (j + 1) % page]"),
+    ("paged decode ignores window", "lo = max(0, L - window) if window > 0 else 0\n        if L - lo == 0",
+     "lo = 0\n        if L - lo == 0"),
     ("probe bwd drho sign", "drho[b, rr, h] = go * kb - (p * gv) @ Kj", "drho[b, rr, h] = (p * gv) @ Kj - go * kb"),
     ("probe bwd dp misses a(p)", "dp = gv * (1.0 + a - r) + go * r", "dp = gv * (1.0 + a - r)"),
     ("probe bwd dk rho term sign", "(p * (go - gv)).T @ Rr", "(p * (gv - go)).T @ Rr"),
