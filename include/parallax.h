@@ -216,6 +216,37 @@ plx_status parallax_attn_decode(const plx_attn_desc* desc,
                                 const int32_t* seqlens_k, const void* P, float* out,
                                 void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/*
+ * Paged decode.  Bytes of workspace needed for `desc` (the same as parallax_attn_decode's); returns 0
+ * for an invalid or unsupported desc.
+ */
+size_t parallax_attn_decode_paged_workspace(const plx_attn_desc* desc);
+
+/*
+ * Decode against a paged key/value cache (serving caches that grow page by page; the pages' decode
+ * benchmark spans batch sizes and context lengths): the same result as parallax_attn_decode on the
+ * sequences the block table describes.  Key j of sequence b is slot j % page_size of page
+ * block_table[b][j / page_size].
+ *   q            [B][Hq][d]                     dtype desc->dtype
+ *   k_pages, v_pages [num_pages][page_size][Hkv][d]   dtype desc->dtype
+ *   block_table  [B][max_pages] int32 device array, max_pages = ceil(desc->seqlen_k / page_size);
+ *                only the entries that cover keys < seqlens_k[b] are read
+ *   seqlens_k    [B] int32 device array (nullable: every sequence has desc->seqlen_k keys)
+ *   P [Hq][d][d]     out [B][Hq][d] fp32
+ * desc->seqlen_q must be 1 and desc->seqlen_k is the longest sequence the table can describe.
+ * page_size must be a power of two (1 .. 65536) and num_pages >= 1.  Block-table entries outside
+ * [0, num_pages) are clamped into the pool: that sequence's output is then wrong, but nothing is
+ * read outside the caller's arrays.
+ * Supported: bf16, head_dim 128, heads_q / heads_kv in {1, 2, 4}, p_per_query 0; any other valid
+ * desc returns PLX_ERR_UNSUPPORTED.  window as in parallax_attn_decode.
+ */
+plx_status parallax_attn_decode_paged(const plx_attn_desc* desc, const void* q,
+                                      const void* k_pages, const void* v_pages,
+                                      int32_t num_pages, int32_t page_size,
+                                      const int32_t* block_table, const int32_t* seqlens_k,
+                                      const void* P, float* out,
+                                      void* workspace, size_t workspace_bytes, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

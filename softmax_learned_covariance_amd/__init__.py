@@ -14,6 +14,7 @@ Functions (same names as the C entry points):
     out               = parallax_attn_decode(q, k_cache, v_cache, P, seqlens=None, window=0, scale=None)
     out, lse, o, rk   = parallax_attn_fwd_probe(q, k, v, rho, causal=True, window=0, scale=None)
     dq, dk, dv, drho  = parallax_attn_bwd_probe(q, k, v, rho, out, dout, lse, o, rk, causal=True, ...)
+    out               = parallax_attn_decode_paged(q, k_pages, v_pages, block_table, P, seqlens=None, ...)
 
 Layouts: q [B,Tq,Hq,d] (decode [B,Hq,d]); k, v [B,Tk,Hkv,d]; P [Hq,d,d] (or
 [B,Tq,Hq,d,d] per query, forward only); outputs float32.
@@ -69,6 +70,9 @@ SIGNATURES = {
                                 _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "parallax_attn_decode_workspace": (_sz, [_DESC]),
     "parallax_attn_decode": (_st, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "parallax_attn_decode_paged_workspace": (_sz, [_DESC]),
+    "parallax_attn_decode_paged": (_st, [_DESC, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp, _vp,
+                                         _vp, _sz, _vp]),
 }
 
 
@@ -264,8 +268,40 @@ def parallax_attn_decode(q, k_cache, v_cache, P, seqlens=None, window=0, scale=N
     return out
 
 
+def parallax_attn_decode_paged(q, k_pages, v_pages, block_table, P, seqlens=None, seqlen_k=None, window=0,
+                               scale=None):
+    """Decode against a paged cache: q [B,Hq,d]; pages [num_pages,page_size,Hkv,d]; block_table int32
+    [B,max_pages]; seqlens int32 [B] or None; seqlen_k defaults to max_pages * page_size.
+    Returns out [B,Hq,d] float32 (see include/parallax.h)."""
+    B, Hq, d = q.shape
+    num_pages, page_size, Hkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    dt = _dtype_code(q)
+    dev = q.device
+    _need(k_pages, "k_pages", q.dtype, (num_pages, page_size, Hkv, d), dev)
+    _need(v_pages, "v_pages", q.dtype, (num_pages, page_size, Hkv, d), dev)
+    _need(P, "P", q.dtype, (Hq, d, d), dev)
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table: expected int32 [B, max_pages], got {block_table.dtype} {tuple(block_table.shape)}")
+    _need(block_table, "block_table", torch.int32, tuple(block_table.shape), dev)
+    Lmax = block_table.shape[1] * page_size if seqlen_k is None else int(seqlen_k)
+    if (Lmax + page_size - 1) // page_size > block_table.shape[1]:
+        raise ValueError(f"seqlen_k={Lmax} needs more than the block table's {block_table.shape[1]} pages")
+    if seqlens is not None:
+        _need(seqlens, "seqlens", torch.int32, (B,), dev)
+    desc = make_desc(B, 1, Lmax, Hq, Hkv, d, True, window, scale, dt, False, -1)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    lib = get_lib()
+    nws = lib.parallax_attn_decode_paged_workspace(ctypes.byref(desc))
+    ws = _workspace(nws, dev)
+    _check(lib.parallax_attn_decode_paged(ctypes.byref(desc), _ptr(q), _ptr(k_pages), _ptr(v_pages), num_pages,
+                                          page_size, _ptr(block_table), _ptr(seqlens), _ptr(P), _ptr(out),
+                                          _ptr(ws), nws, _stream()))
+    return out
+
+
 fwd = parallax_attn_fwd
 bwd = parallax_attn_bwd
 decode = parallax_attn_decode
 fwd_probe = parallax_attn_fwd_probe
 bwd_probe = parallax_attn_bwd_probe
+decode_paged = parallax_attn_decode_paged

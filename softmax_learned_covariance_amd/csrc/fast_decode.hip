@@ -13,6 +13,9 @@
 // are fp32 VALU on LDS-staged bf16 tiles: the cache is read straight from HBM in
 // 16-byte chunks, with no fp16 staging copy.  One workgroup (256 threads) owns
 // one (batch, kv head, key split) and all query heads of that kv head.
+// The cache is either one contiguous [B][L][Hkv][d] array per tensor or a pool of
+// pages [num_pages][page_size][Hkv][d] with a per-sequence block table (the PAGED
+// instantiations): key j of sequence b lives in page block_table[b][j / page_size].
 #include <math.h>
 
 #include "fast_common.h"
@@ -29,6 +32,8 @@ constexpr int kMaxG = 4;
 struct DecParams {
   const u16 *q, *kc, *vc, *P;
   const int32_t* seqlens;
+  const int32_t* block_table;    // paged cache: [B][max_pages] page indices
+  int max_pages, page_shift, num_pages;
   float* out;
   // workspace
   float *pm, *pl, *po, *pk;      // pass 1 partials: [B][Hq][ns] (m, l) and [B][Hq][ns][128] (o, kbar)
@@ -72,23 +77,40 @@ struct TileRegs {
   u32x4 k0, k1, k2, k3, v0, v1, v2, v3;
 };
 
-__device__ __forceinline__ u32x4 fetch16(const u16* base, const DecParams& p, int b, int g, int key, int c) {
-  return *reinterpret_cast<const u32x4*>(base + ((static_cast<int64_t>(b) * p.L + key) * p.Hkv + g) * kD + c * 8);
+// Cache row (token slot) of key `key` of sequence b.  A paged cache looks the page up in the block
+// table; entries outside [0, num_pages) are clamped into the pool, so a bad table gives wrong values
+// for that sequence but never an access outside the caller's arrays.
+template <bool PAGED>
+__device__ __forceinline__ int64_t cache_row(const DecParams& p, int b, int key) {
+  if constexpr (PAGED) {
+    int pg = p.block_table[static_cast<int64_t>(b) * p.max_pages + (key >> p.page_shift)];
+    pg = min(max(pg, 0), p.num_pages - 1);
+    return (static_cast<int64_t>(pg) << p.page_shift) + (key & ((1 << p.page_shift) - 1));
+  } else {
+    return static_cast<int64_t>(b) * p.L + key;
+  }
 }
 
+__device__ __forceinline__ u32x4 fetch16(const u16* base, const DecParams& p, int64_t row, int g, int c) {
+  return *reinterpret_cast<const u32x4*>(base + (row * p.Hkv + g) * kD + c * 8);
+}
+
+template <bool PAGED>
 __device__ __forceinline__ TileRegs tile_fetch(const DecParams& p, int b, int g, int key0, int hi, int tid) {
   const int r = tid >> 4, c = tid & 15;   // chunk j of the thread: row r + 16 j, chunk c
-  const int ka = min(key0 + r, hi - 1), kb = min(key0 + r + 16, hi - 1);
-  const int kc = min(key0 + r + 32, hi - 1), kd = min(key0 + r + 48, hi - 1);
+  const int64_t ra = cache_row<PAGED>(p, b, min(key0 + r, hi - 1));
+  const int64_t rb = cache_row<PAGED>(p, b, min(key0 + r + 16, hi - 1));
+  const int64_t rc = cache_row<PAGED>(p, b, min(key0 + r + 32, hi - 1));
+  const int64_t rd = cache_row<PAGED>(p, b, min(key0 + r + 48, hi - 1));
   TileRegs R;
-  R.k0 = fetch16(p.kc, p, b, g, ka, c);
-  R.k1 = fetch16(p.kc, p, b, g, kb, c);
-  R.k2 = fetch16(p.kc, p, b, g, kc, c);
-  R.k3 = fetch16(p.kc, p, b, g, kd, c);
-  R.v0 = fetch16(p.vc, p, b, g, ka, c);
-  R.v1 = fetch16(p.vc, p, b, g, kb, c);
-  R.v2 = fetch16(p.vc, p, b, g, kc, c);
-  R.v3 = fetch16(p.vc, p, b, g, kd, c);
+  R.k0 = fetch16(p.kc, p, ra, g, c);
+  R.k1 = fetch16(p.kc, p, rb, g, c);
+  R.k2 = fetch16(p.kc, p, rc, g, c);
+  R.k3 = fetch16(p.kc, p, rd, g, c);
+  R.v0 = fetch16(p.vc, p, ra, g, c);
+  R.v1 = fetch16(p.vc, p, rb, g, c);
+  R.v2 = fetch16(p.vc, p, rc, g, c);
+  R.v3 = fetch16(p.vc, p, rd, g, c);
   return R;
 }
 
@@ -135,7 +157,7 @@ __device__ __forceinline__ void tile_dots(const DecTiles& T, int buf, const floa
 }
 
 // ---------------------------------- pass 1 ----------------------------------
-template <int G>
+template <int G, bool PAGED>
 __global__ __launch_bounds__(256) void k_dec_pass1(DecParams p) {
   __shared__ DecTiles T;
   const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
@@ -156,13 +178,13 @@ __global__ __launch_bounds__(256) void k_dec_pass1(DecParams p) {
   const int nt = k1 > k0 ? (k1 - k0 + kTile - 1) / kTile : 0;
   TileRegs R{};
   if (nt > 0) {
-    R = tile_fetch(p, b, g, k0, k1, tid);
+    R = tile_fetch<PAGED>(p, b, g, k0, k1, tid);
     tile_store(R, T, 0, tid);
   }
   __syncthreads();
   for (int it = 0; it < nt; ++it) {
     const int buf = 0, key0 = k0 + it * kTile;
-    R = tile_fetch(p, b, g, key0 + kTile, k1, tid);   // (past the last tile: rereads the last key)
+    R = tile_fetch<PAGED>(p, b, g, key0 + kTile, k1, tid);   // (past the last tile: rereads the last key)
     tile_dots<G>(T, buf, T.q, T.s, tid);
     lds_barrier();
     const int w = tid >> 6, lane = tid & 63;
@@ -276,7 +298,7 @@ __global__ __launch_bounds__(128) void k_dec_combine1(DecParams p) {
 }
 
 // ---------------------------------- pass 2 ----------------------------------
-template <int G>
+template <int G, bool PAGED>
 __global__ __launch_bounds__(256) void k_dec_pass2(DecParams p) {
   __shared__ DecTiles T;
   __shared__ float st[kMaxG][2];  // lse (log2 units), alpha
@@ -303,13 +325,13 @@ __global__ __launch_bounds__(256) void k_dec_pass2(DecParams p) {
   const int nt = k1 > k0 ? (k1 - k0 + kTile - 1) / kTile : 0;
   TileRegs R{};
   if (nt > 0) {
-    R = tile_fetch(p, b, g, k0, k1, tid);
+    R = tile_fetch<PAGED>(p, b, g, k0, k1, tid);
     tile_store(R, T, 0, tid);
   }
   __syncthreads();
   for (int it = 0; it < nt; ++it) {
     const int buf = 0, key0 = k0 + it * kTile;
-    R = tile_fetch(p, b, g, key0 + kTile, k1, tid);   // (past the last tile: rereads the last key)
+    R = tile_fetch<PAGED>(p, b, g, key0 + kTile, k1, tid);   // (past the last tile: rereads the last key)
     tile_dots<G>(T, buf, T.q, T.s, tid);
     tile_dots<G>(T, buf, T.u, T.w, tid);
     lds_barrier();
@@ -403,8 +425,31 @@ bool fast_decode_supported(const Geom& g) {
 
 size_t fast_decode_workspace(const Geom& g) { return dec_layout(g, nullptr).bytes; }
 
+namespace {
+
+template <int G, bool PAGED>
+void launch_passes(const DecParams& p, const dim3& grid, int Hq, int B, hipStream_t stream) {
+  mark_begin(PLX_KERNEL_DECODE_PASS1, stream);
+  hipLaunchKernelGGL((k_dec_pass1<G, PAGED>), grid, dim3(256), 0, stream, p);
+  mark_end(PLX_KERNEL_DECODE_PASS1, stream);
+  hipLaunchKernelGGL(k_dec_combine1, dim3(Hq, B), dim3(128), 0, stream, p);
+  mark_begin(PLX_KERNEL_DECODE_PASS2, stream);
+  hipLaunchKernelGGL((k_dec_pass2<G, PAGED>), grid, dim3(256), 0, stream, p);
+  mark_end(PLX_KERNEL_DECODE_PASS2, stream);
+  hipLaunchKernelGGL(k_dec_finish, dim3(Hq, B), dim3(128), 0, stream, p);
+}
+
+template <bool PAGED>
+void launch_all(const DecParams& p, const dim3& grid, int Hq, int B, hipStream_t stream) {
+  if (p.G == 1) launch_passes<1, PAGED>(p, grid, Hq, B, stream);
+  else if (p.G == 2) launch_passes<2, PAGED>(p, grid, Hq, B, stream);
+  else launch_passes<4, PAGED>(p, grid, Hq, B, stream);
+}
+
+}  // namespace
+
 hipError_t launch_fast_decode(const Geom& g, const void* q, const void* kc, const void* vc, const int32_t* seqlens,
-                              const void* P, float* out, void* ws, hipStream_t stream) {
+                              const void* P, float* out, void* ws, hipStream_t stream, const PagedCache* paged) {
   const DecWs w = dec_layout(g, ws);
   DecParams p{};
   p.q = static_cast<const u16*>(q);
@@ -432,18 +477,17 @@ hipError_t launch_fast_decode(const Geom& g, const void* q, const void* kc, cons
   p.chunk = w.chunk;
   p.scale = g.scale;
   const dim3 grid(w.ns, g.Hkv, g.B);
-  mark_begin(PLX_KERNEL_DECODE_PASS1, stream);
-  if (p.G == 1) hipLaunchKernelGGL(k_dec_pass1<1>, grid, dim3(256), 0, stream, p);
-  else if (p.G == 2) hipLaunchKernelGGL(k_dec_pass1<2>, grid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL(k_dec_pass1<4>, grid, dim3(256), 0, stream, p);
-  mark_end(PLX_KERNEL_DECODE_PASS1, stream);
-  hipLaunchKernelGGL(k_dec_combine1, dim3(g.Hq, g.B), dim3(128), 0, stream, p);
-  mark_begin(PLX_KERNEL_DECODE_PASS2, stream);
-  if (p.G == 1) hipLaunchKernelGGL(k_dec_pass2<1>, grid, dim3(256), 0, stream, p);
-  else if (p.G == 2) hipLaunchKernelGGL(k_dec_pass2<2>, grid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL(k_dec_pass2<4>, grid, dim3(256), 0, stream, p);
-  mark_end(PLX_KERNEL_DECODE_PASS2, stream);
-  hipLaunchKernelGGL(k_dec_finish, dim3(g.Hq, g.B), dim3(128), 0, stream, p);
+  if (paged) {
+    p.block_table = paged->block_table;
+    p.max_pages = paged->max_pages;
+    p.num_pages = paged->num_pages;
+    int shift = 0;
+    while ((1 << shift) < paged->page_size) ++shift;
+    p.page_shift = shift;
+    launch_all<true>(p, grid, g.Hq, g.B, stream);
+  } else {
+    launch_all<false>(p, grid, g.Hq, g.B, stream);
+  }
   return hipGetLastError();
 }
 

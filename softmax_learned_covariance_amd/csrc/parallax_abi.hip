@@ -351,4 +351,43 @@ plx_status parallax_attn_decode(const plx_attn_desc* desc, const void* q, const 
   return hip_status(e, what);
 }
 
+size_t parallax_attn_decode_paged_workspace(const plx_attn_desc* desc) {
+  plx::Geom g;
+  if (check_desc(desc, "parallax_attn_decode_paged_workspace", &g) != PLX_OK) return 0;
+  if (g.Tq != 1 || g.p_per_query || !plx::fast_decode_supported(g)) return 0;
+  g.causal = 1;
+  return plx::fast_decode_workspace(g);
+}
+
+plx_status parallax_attn_decode_paged(const plx_attn_desc* desc, const void* q, const void* k_pages,
+                                      const void* v_pages, int32_t num_pages, int32_t page_size,
+                                      const int32_t* block_table, const int32_t* seqlens_k, const void* P,
+                                      float* out, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  const char* what = "parallax_attn_decode_paged";
+  plx::Geom g;
+  plx_status st = check_desc(desc, what, &g);
+  if (st != PLX_OK) return st;
+  if (g.Tq != 1) return fail(PLX_ERR_INVALID, "%s: seqlen_q must be 1 (got %d)", what, g.Tq);
+  if (page_size < 1 || page_size > 65536 || (page_size & (page_size - 1)) != 0)
+    return fail(PLX_ERR_INVALID, "%s: page_size=%d is not a power of two in [1, 65536]", what, page_size);
+  if (num_pages < 1) return fail(PLX_ERR_INVALID, "%s: num_pages=%d < 1", what, num_pages);
+  if (!plx::fast_decode_supported(g))
+    return fail(PLX_ERR_UNSUPPORTED,
+                "%s: only bf16, head_dim 128, heads_q/heads_kv in {1,2,4} and p_per_query 0 are supported", what);
+  g.causal = 1;
+  const size_t need = plx::fast_decode_workspace(g);
+  if (g.B == 0) {
+    st = check_ws(need, workspace, workspace_bytes, what);
+    return st != PLX_OK ? st : ok();
+  }
+  if (!q || !P || !out) return fail(PLX_ERR_INVALID, "%s: q, P and out must not be NULL", what);
+  if (g.Tk > 0 && (!k_pages || !v_pages || !block_table))
+    return fail(PLX_ERR_INVALID, "%s: k_pages, v_pages and block_table must not be NULL", what);
+  st = check_ws(need, workspace, workspace_bytes, what);
+  if (st != PLX_OK) return st;
+  plx::PagedCache pc{block_table, num_pages, page_size, (g.Tk + page_size - 1) / page_size};
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  return hip_status(plx::launch_fast_decode(g, q, k_pages, v_pages, seqlens_k, P, out, workspace, stream, &pc), what);
+}
+
 }  // extern "C"

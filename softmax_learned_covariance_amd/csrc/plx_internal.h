@@ -73,9 +73,15 @@ hipError_t launch_fast_bwd(const Geom& g, const void* q, const void* k, const vo
 
 bool fast_decode_supported(const Geom& g);
 size_t fast_decode_workspace(const Geom& g);
+// A paged key/value cache: pages [num_pages][page_size][Hkv][d] (page_size a power of two) and a block
+// table [B][max_pages] of page indices, max_pages = ceil(L / page_size).
+struct PagedCache {
+  const int32_t* block_table;
+  int num_pages, page_size, max_pages;
+};
 hipError_t launch_fast_decode(const Geom& g, const void* q, const void* kc, const void* vc,
                               const int32_t* seqlens, const void* P, float* out, void* ws,
-                              hipStream_t stream);
+                              hipStream_t stream, const PagedCache* paged = nullptr);
 
 // Records the profiling hook's `before` / `after` event on `stream` when `kernel` (a plx_kernel)
 // is the one selected (no-op otherwise).

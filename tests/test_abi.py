@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(plx):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     out = subprocess.run(["nm", "-D", "--defined-only", plx.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (parallax_\w+)", out))
     missing = [n for n in names if n not in exported]
@@ -176,6 +176,31 @@ def test_probe_backward_validation(plx):
         assert call(d, **{name: None}) == E.PLX_ERR_INVALID, name
     assert call(_desc(plx, B=0, **bf)) == E.PLX_OK
     assert lib.parallax_attn_bwd_probe_workspace(ctypes.byref(_desc(plx, B=0, **bf))) == 0
+
+
+def test_paged_decode_validation(plx):
+    E = plx
+    lib = plx.get_lib()
+    bf = dict(dtype=plx.PLX_BF16, d=128, Tq=1)
+
+    def call(desc, num_pages=4, page=16, table=FAKE, q=FAKE, ws=FAKE, nws=1 << 40):
+        return lib.parallax_attn_decode_paged(ctypes.byref(desc), q, FAKE, FAKE, num_pages, page, table, None,
+                                              FAKE, FAKE, ws, nws, None)
+
+    d = _desc(plx, **bf)
+    assert call(_desc(plx, dtype=plx.PLX_BF16, d=128, Tq=2)) == E.PLX_ERR_INVALID
+    for page in (0, 3, 48, 1 << 17):
+        assert call(d, page=page) == E.PLX_ERR_INVALID, page
+    assert b"page_size" in lib.parallax_last_error()
+    assert call(d, num_pages=0) == E.PLX_ERR_INVALID
+    assert call(_desc(plx, Tq=1)) == E.PLX_ERR_UNSUPPORTED                       # fp32
+    assert call(_desc(plx, Hq=8, Hkv=1, **bf)) == E.PLX_ERR_UNSUPPORTED          # 8 query heads per group
+    assert call(d, table=None) == E.PLX_ERR_INVALID
+    assert call(d, q=None) == E.PLX_ERR_INVALID
+    need = lib.parallax_attn_decode_paged_workspace(ctypes.byref(d))
+    assert need > 0 and need == lib.parallax_attn_decode_workspace(ctypes.byref(d))
+    assert call(d, nws=need - 1) == E.PLX_ERR_WORKSPACE
+    assert call(_desc(plx, B=0, **bf), ws=None, nws=0) in (E.PLX_OK, E.PLX_ERR_INVALID)
 
 
 def test_bench_refuses_more_than_one_gpu():

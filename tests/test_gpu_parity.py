@@ -389,3 +389,91 @@ def test_decode_groups(plx, Hkv):
     torch.cuda.synchronize()
     ref = oracle.decode(host(q), host(kc), host(vc), host(P))
     assert rel_err(host(out), ref) <= BF16_TOL
+
+
+# --------------------------------------------------------------------------------------
+# decode against a paged cache
+# --------------------------------------------------------------------------------------
+
+def _to_pages(kc, vc, page, spare=3, seed=0):
+    """Scatter a contiguous cache [B,L,Hkv,d] into a shuffled page pool (storage only) and its table."""
+    B, L, Hkv, d = kc.shape
+    npb = (L + page - 1) // page
+    pad = npb * page - L
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    perm = torch.randperm(B * npb + spare, generator=g)[:B * npb].to(kc.device)
+    pools = []
+    for c in (kc, vc):
+        cp = torch.nn.functional.pad(c, (0, 0, 0, 0, 0, pad)) if pad else c
+        pool = torch.randn((B * npb + spare, page, Hkv, d), device=kc.device).to(c.dtype)   # junk in spare pages
+        pool[perm] = cp.reshape(B * npb, page, Hkv, d)
+        pools.append(pool)
+    return pools[0], pools[1], perm.reshape(B, npb).to(torch.int32).contiguous()
+
+
+@pytest.mark.parametrize("page", [16, 64, 256])
+def test_decode_paged(plx, page):
+    """Paged decode gives bit for bit the contiguous decode of the same keys (same arithmetic, other
+    addresses), and matches the oracle; ragged lengths ending inside a page, an empty sequence, a window."""
+    _announce(f"paged decode page={page}")
+    w = W.scaled(W.WORKLOADS["decode"], batch=5, seqlen_k=1500)
+    q, kc, vc, P = W.make_inputs(w, device="cuda")
+    kp, vp, table = _to_pages(kc, vc, page)
+    seqlens = torch.tensor([1500, 1, 0, 777, 1024], dtype=torch.int32, device="cuda")
+    for window in (0, 100):
+        ref_c = plx.parallax_attn_decode(q, kc, vc, P, seqlens=seqlens, window=window)
+        out = plx.parallax_attn_decode_paged(q, kp, vp, table, P, seqlens=seqlens, seqlen_k=1500, window=window)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_c), window
+        ref = oracle.decode_paged(host(q), host(kp), host(vp), host(table).astype(np.int64), host(P),
+                                  seqlens=host(seqlens).astype(int), seqlen_k=1500, window=window)
+        assert rel_err(host(out), ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("Hkv", [16, 4])
+def test_decode_paged_groups(plx, Hkv):
+    _announce(f"paged decode Hkv={Hkv}")
+    w = W.scaled(W.WORKLOADS["decode"], batch=3, seqlen_k=700, heads_kv=Hkv)
+    q, kc, vc, P = W.make_inputs(w, device="cuda")
+    kp, vp, table = _to_pages(kc, vc, 32, seed=1)
+    out = plx.parallax_attn_decode_paged(q, kp, vp, table, P, seqlen_k=700)
+    torch.cuda.synchronize()
+    ref = oracle.decode_paged(host(q), host(kp), host(vp), host(table).astype(np.int64), host(P), seqlen_k=700)
+    assert rel_err(host(out), ref) <= BF16_TOL
+
+
+def test_full_size_decode_paged(plx):
+    """B=64 sequences of 32768 keys in 256-key pages: bit-identical to the contiguous decode, and sampled
+    batch entries against the oracle."""
+    w = W.WORKLOADS["decode"]
+    _announce("full-size paged decode (page 256)")
+    q, kc, vc, P = W.make_inputs(w, device="cuda")
+    kp, vp, table = _to_pages(kc, vc, 256, seed=2)
+    out_c = plx.parallax_attn_decode(q, kc, vc, P)
+    del kc, vc
+    out = plx.parallax_attn_decode_paged(q, kp, vp, table, P)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_c)
+    bsel = [0, 33]
+    used = table[bsel].reshape(-1).long()              # only the pages those sequences use go to the host
+    sub_table = np.arange(used.numel()).reshape(len(bsel), -1)
+    ref = oracle.decode_paged(host(q[bsel]), host(kp[used]), host(vp[used]), sub_table, host(P))
+    assert rel_err(host(out[bsel]), ref) <= BF16_TOL
+
+
+def test_decode_paged_clamps_bad_entries(plx):
+    """A block-table entry outside the pool is clamped into it: that sequence reads some page of the pool
+    (no access outside it) and the other sequences are unaffected."""
+    _announce("paged decode with an out-of-range table entry")
+    w = W.scaled(W.WORKLOADS["decode"], batch=3, seqlen_k=256)
+    q, kc, vc, P = W.make_inputs(w, device="cuda")
+    kp, vp, table = _to_pages(kc, vc, 64, spare=0, seed=3)
+    good = plx.parallax_attn_decode_paged(q, kp, vp, table, P)
+    bad_table = table.clone()
+    bad_table[1, 2] = kp.shape[0] + 1000
+    bad_table[1, 3] = -5
+    bad = plx.parallax_attn_decode_paged(q, kp, vp, bad_table, P)
+    torch.cuda.synchronize()
+    assert torch.isfinite(bad).all()
+    assert torch.equal(bad[0], good[0]) and torch.equal(bad[2], good[2])
