@@ -180,6 +180,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the decode batch/context sweep")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy, the reference for HBM traffic counters")
     args = ap.parse_args()
@@ -375,6 +376,54 @@ def main():
                          "note": "algorithmic bytes = one read of the K/V cache; the two-pass method reads it twice"}}
         kms = dt * 1e3
         log(f"decode {kms:.3f} ms/kernel, {gbs:.0f} GB/s")
+
+        # the same keys in a shuffled pool of 256-key pages with a block table
+        page = 256
+        npb = wd.seqlen_k // page
+        gperm = torch.Generator(device="cpu")
+        gperm.manual_seed(5)
+        perm = torch.randperm(wd.batch * npb, generator=gperm).to(dev)
+        kp = torch.empty((wd.batch * npb, page, wd.heads_kv, wd.head_dim), dtype=kc.dtype, device=dev)
+        kp[perm] = kc.reshape(wd.batch * npb, page, wd.heads_kv, wd.head_dim)
+        del kc
+        vp = torch.empty_like(kp)
+        vp[perm] = vc.reshape(wd.batch * npb, page, wd.heads_kv, wd.head_dim)
+        del vc
+        table = perm.reshape(wd.batch, npb).to(torch.int32).contiguous()
+        for _ in range(2):
+            plx.parallax_attn_decode_paged(qd, kp, vp, table, Pd)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(Kd):
+            plx.parallax_attn_decode_paged(qd, kp, vp, table, Pd)
+        torch.cuda.synchronize()
+        dtpg = (time.perf_counter() - t0) / Kd
+        result["decode"]["paged"] = {"page_size": page, "ms_per_call": round(dtpg * 1e3, 4),
+                                     "tokens_per_s": round(wd.batch / dtpg, 1),
+                                     "gbs": round(alg / dtpg / 1e9, 1)}
+        log(f"paged decode {dtpg * 1e3:.3f} ms/call")
+        del kp, vp, table, perm
+
+        if not args.no_sweep:
+            # decode across batch sizes and context lengths (the pages' decode benchmark axes)
+            sweep = []
+            for Bs, Ls in ((1, 32768), (8, 32768), (64, 4096), (64, 16384), (256, 8192)):
+                ws_ = W.scaled(wd, batch=Bs, seqlen_k=Ls)
+                qs, ks, vs, Ps = W.make_inputs(ws_, device=dev)
+                for _ in range(2):
+                    plx.parallax_attn_decode(qs, ks, vs, Ps)
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(5):
+                    plx.parallax_attn_decode(qs, ks, vs, Ps)
+                torch.cuda.synchronize()
+                dts = (time.perf_counter() - t0) / 5
+                by = 2 * Bs * Ls * ws_.heads_kv * ws_.head_dim * 2
+                sweep.append({"batch": Bs, "context": Ls, "ms_per_call": round(dts * 1e3, 4),
+                              "tokens_per_s": round(Bs / dts, 1), "gbs_one_read": round(by / dts / 1e9, 1)})
+                log(f"decode sweep B={Bs} L={Ls}: {dts * 1e3:.3f} ms")
+                del qs, ks, vs, Ps
+            result["decode"]["sweep"] = sweep
 
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on host cores)")

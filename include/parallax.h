@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define PARALLAX_ABI_VERSION 1
+#define PARALLAX_ABI_VERSION 2
 
 typedef enum {
   PLX_OK = 0,
@@ -71,6 +71,9 @@ typedef struct {
   int32_t dtype;          /* plx_dtype of q, k, v, P, dout */
   int32_t p_per_query;    /* 0: P is [Hq][d][d]; 1: P is [B][Tq][Hq][d][d] (forward only) */
   int32_t split_rows;     /* bf16 fast path: query rows < max(split_rows, 16) use hi + lo fp16 operand pairs (about 22 bits); < 0 selects the default, 256 */
+  int32_t out_dtype;      /* plx_dtype of `out` in the forwards and decodes (0 = PLX_F32). PLX_BF16 (rounded to
+                             nearest even from the fp32 result) needs the bf16 fast path; the backwards read
+                             an fp32 `out` and require PLX_F32 */
 } plx_attn_desc;
 
 /* Kernels the profiling hook can bracket. */
@@ -112,15 +115,18 @@ size_t parallax_attn_fwd_workspace(const plx_attn_desc* desc);
  * Forward: the output equation above for every query row.
  *   q     [B][Tq][Hq][d]              k, v  [B][Tk][Hkv][d]
  *   P     [Hq][d][d], or [B][Tq][Hq][d][d] when desc->p_per_query
- *   out   [B][Tq][Hq][d] fp32 (required)
+ *   out   [B][Tq][Hq][d] fp32, or bf16 when desc->out_dtype is PLX_BF16 (required)
  *   lse   [B][Hq][Tq]    fp32, natural-log softmax denominator of the scaled scores (nullable)
  *   kbar  [B][Tq][Hq][d] fp32 softmax-weighted key mean (nullable)
  *   o_sa  [B][Tq][Hq][d] fp32 softmax-attention output o (nullable)
- * The backward needs lse, kbar and o_sa from the same call.
+ *   cor   [B][Hq][Tq]    fp32 correction-to-output ratio |out_i - o_i| / |out_i| (Euclidean norms over
+ *                        d, from the fp32 result; 0 where out_i = 0), the pages' diagnostic of how much the
+ *                        covariance branch moves the output (nullable; bf16 fast path only)
+ * The backward needs lse, kbar and o_sa from the same call, and an fp32 out.
  */
 plx_status parallax_attn_fwd(const plx_attn_desc* desc,
                              const void* q, const void* k, const void* v, const void* P,
-                             float* out, float* lse, float* kbar, float* o_sa,
+                             void* out, float* lse, float* kbar, float* o_sa, float* cor,
                              void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
@@ -140,17 +146,18 @@ size_t parallax_attn_fwd_probe_workspace(const plx_attn_desc* desc);
  * (the forward above with u_i = -rho_i).  rho_i = W_R x_i is the caller's projection of the
  * layer input.  Because rho does not depend on kbar, one pass over the keys suffices.
  *   q, rho [B][Tq][Hq][d]     k, v [B][Tk][Hkv][d]     dtype desc->dtype
- *   out    [B][Tq][Hq][d] fp32 (required)
+ *   out    [B][Tq][Hq][d] fp32, or bf16 when desc->out_dtype is PLX_BF16 (required)
  *   lse    [B][Hq][Tq]    fp32 as in the forward (nullable)
  *   o_sa   [B][Tq][Hq][d] fp32 softmax-attention output o (nullable)
  *   rk     [B][Hq][Tq]    fp32 rho_i . kbar_i (nullable)
+ *   cor    [B][Hq][Tq]    fp32 correction-to-output ratio as in the forward (nullable)
  * The probe-form backward needs lse, o_sa and rk from the same call.
  * Supported: bf16, head_dim 128, heads_q / heads_kv in {1, 2, 4, 8}, p_per_query 0; any other
  * valid desc returns PLX_ERR_UNSUPPORTED.  Masks, empty rows and split_rows as in the forward.
  */
 plx_status parallax_attn_fwd_probe(const plx_attn_desc* desc,
                                    const void* q, const void* k, const void* v, const void* rho,
-                                   float* out, float* lse, float* o_sa, float* rk,
+                                   void* out, float* lse, float* o_sa, float* rk, float* cor,
                                    void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* Probe-form backward.  Bytes of workspace needed for `desc`; returns 0 for an invalid desc. */
@@ -209,11 +216,12 @@ size_t parallax_attn_decode_workspace(const plx_attn_desc* desc);
  * [0, Lmax]; a sequence of length 0 gets out = 0.
  *   q        [B][Hq][d]            k_cache, v_cache [B][Lmax][Hkv][d]
  *   seqlens_k [B] int32 device array (nullable)
- *   P        [Hq][d][d]            out [B][Hq][d] fp32
+ *   P        [Hq][d][d]            out [B][Hq][d] fp32, or bf16 when desc->out_dtype is PLX_BF16
+ *   cor      [B][Hq] fp32 correction-to-output ratio as in the forward (nullable; bf16 fast path only)
  */
 plx_status parallax_attn_decode(const plx_attn_desc* desc,
                                 const void* q, const void* k_cache, const void* v_cache,
-                                const int32_t* seqlens_k, const void* P, float* out,
+                                const int32_t* seqlens_k, const void* P, void* out, float* cor,
                                 void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
@@ -232,7 +240,7 @@ size_t parallax_attn_decode_paged_workspace(const plx_attn_desc* desc);
  *   block_table  [B][max_pages] int32 device array, max_pages = ceil(desc->seqlen_k / page_size);
  *                only the entries that cover keys < seqlens_k[b] are read
  *   seqlens_k    [B] int32 device array (nullable: every sequence has desc->seqlen_k keys)
- *   P [Hq][d][d]     out [B][Hq][d] fp32
+ *   P [Hq][d][d]     out [B][Hq][d] fp32 (bf16 when desc->out_dtype is PLX_BF16)     cor [B][Hq] (nullable)
  * desc->seqlen_q must be 1 and desc->seqlen_k is the longest sequence the table can describe.
  * page_size must be a power of two (1 .. 65536) and num_pages >= 1.  Block-table entries outside
  * [0, num_pages) are clamped into the pool: that sequence's output is then wrong, but nothing is
@@ -244,7 +252,7 @@ plx_status parallax_attn_decode_paged(const plx_attn_desc* desc, const void* q,
                                       const void* k_pages, const void* v_pages,
                                       int32_t num_pages, int32_t page_size,
                                       const int32_t* block_table, const int32_t* seqlens_k,
-                                      const void* P, float* out,
+                                      const void* P, void* out, float* cor,
                                       void* workspace, size_t workspace_bytes, void* hip_stream);
 
 #ifdef __cplusplus

@@ -42,6 +42,7 @@ class PlxAttnDesc(ctypes.Structure):
         ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("causal", ctypes.c_int32), ("window", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
         ("dtype", ctypes.c_int32), ("p_per_query", ctypes.c_int32), ("split_rows", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
     ]
 
 
@@ -59,9 +60,9 @@ SIGNATURES = {
     "parallax_status_string": (ctypes.c_char_p, [_st]),
     "parallax_last_error": (ctypes.c_char_p, []),
     "parallax_attn_fwd_workspace": (_sz, [_DESC]),
-    "parallax_attn_fwd": (_st, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "parallax_attn_fwd": (_st, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "parallax_attn_fwd_probe_workspace": (_sz, [_DESC]),
-    "parallax_attn_fwd_probe": (_st, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "parallax_attn_fwd_probe": (_st, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "parallax_attn_bwd_probe_workspace": (_sz, [_DESC]),
     "parallax_attn_bwd_probe": (_st, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                       _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -69,10 +70,10 @@ SIGNATURES = {
     "parallax_attn_bwd": (_st, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "parallax_attn_decode_workspace": (_sz, [_DESC]),
-    "parallax_attn_decode": (_st, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "parallax_attn_decode": (_st, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "parallax_attn_decode_paged_workspace": (_sz, [_DESC]),
     "parallax_attn_decode_paged": (_st, [_DESC, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp, _vp,
-                                         _vp, _sz, _vp]),
+                                         _vp, _vp, _sz, _vp]),
 }
 
 
@@ -132,17 +133,28 @@ def _need(t, name, dtype, shape, device):
 
 
 def make_desc(B, Tq, Tk, Hq, Hkv, d, causal=True, window=0, scale=None, dtype=PLX_BF16,
-              p_per_query=False, split_rows=-1) -> PlxAttnDesc:
+              p_per_query=False, split_rows=-1, out_dtype=PLX_F32) -> PlxAttnDesc:
     return PlxAttnDesc(B, Tq, Tk, Hq, Hkv, d, int(bool(causal)), int(window or 0),
-                       float(scale) if scale else 0.0, dtype, int(bool(p_per_query)), int(split_rows))
+                       float(scale) if scale else 0.0, dtype, int(bool(p_per_query)), int(split_rows),
+                       int(out_dtype))
+
+
+def _out_code(out_dtype):
+    if out_dtype in (None, torch.float32):
+        return PLX_F32, torch.float32
+    if out_dtype == torch.bfloat16:
+        return PLX_BF16, torch.bfloat16
+    raise TypeError(f"out_dtype must be float32 or bfloat16, not {out_dtype}")
 
 
 def _workspace(nbytes, device):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
-def parallax_attn_fwd(q, k, v, P, causal=True, window=0, scale=None, split_rows=-1):
-    """Forward; returns (out, lse, kbar, o_sa), all float32 (see include/parallax.h)."""
+def parallax_attn_fwd(q, k, v, P, causal=True, window=0, scale=None, split_rows=-1, out_dtype=torch.float32,
+                      cor=False):
+    """Forward; returns (out, lse, kbar, o_sa), float32 (out in `out_dtype`), plus the per-row
+    correction-to-output ratio [B,Hq,Tq] when cor=True (see include/parallax.h)."""
     B, Tq, Hq, d = q.shape
     Tk, Hkv = k.shape[1], k.shape[2]
     dt = _dtype_code(q)
@@ -151,22 +163,26 @@ def parallax_attn_fwd(q, k, v, P, causal=True, window=0, scale=None, split_rows=
     _need(k, "k", q.dtype, (B, Tk, Hkv, d), q.device)
     _need(v, "v", q.dtype, (B, Tk, Hkv, d), q.device)
     _need(P, "P", q.dtype, (B, Tq, Hq, d, d) if per_query else (Hq, d, d), q.device)
-    desc = make_desc(B, Tq, Tk, Hq, Hkv, d, causal, window, scale, dt, per_query, split_rows)
+    oc, odt = _out_code(out_dtype)
+    desc = make_desc(B, Tq, Tk, Hq, Hkv, d, causal, window, scale, dt, per_query, split_rows, oc)
     f32 = dict(dtype=torch.float32, device=q.device)
-    out = torch.empty((B, Tq, Hq, d), **f32)
+    out = torch.empty((B, Tq, Hq, d), dtype=odt, device=q.device)
     lse = torch.empty((B, Hq, Tq), **f32)
     kbar = torch.empty((B, Tq, Hq, d), **f32)
     osa = torch.empty((B, Tq, Hq, d), **f32)
+    ratio = torch.empty((B, Hq, Tq), **f32) if cor else None
     lib = get_lib()
     nws = lib.parallax_attn_fwd_workspace(ctypes.byref(desc))
     ws = _workspace(nws, q.device)
     _check(lib.parallax_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(P), _ptr(out),
-                                 _ptr(lse), _ptr(kbar), _ptr(osa), _ptr(ws), nws, _stream()))
-    return out, lse, kbar, osa
+                                 _ptr(lse), _ptr(kbar), _ptr(osa), _ptr(ratio), _ptr(ws), nws, _stream()))
+    return (out, lse, kbar, osa, ratio) if cor else (out, lse, kbar, osa)
 
 
-def parallax_attn_fwd_probe(q, k, v, rho, causal=True, window=0, scale=None, split_rows=-1):
-    """Probe-form forward, rho [B,Tq,Hq,d] like q; returns (out, lse, o_sa, rk), float32 (see include/parallax.h)."""
+def parallax_attn_fwd_probe(q, k, v, rho, causal=True, window=0, scale=None, split_rows=-1, out_dtype=torch.float32,
+                            cor=False):
+    """Probe-form forward, rho [B,Tq,Hq,d] like q; returns (out, lse, o_sa, rk), float32 (out in `out_dtype`),
+    plus the correction-to-output ratio when cor=True (see include/parallax.h)."""
     B, Tq, Hq, d = q.shape
     Tk, Hkv = k.shape[1], k.shape[2]
     dt = _dtype_code(q)
@@ -174,18 +190,20 @@ def parallax_attn_fwd_probe(q, k, v, rho, causal=True, window=0, scale=None, spl
     _need(v, "v", q.dtype, (B, Tk, Hkv, d), q.device)
     _need(rho, "rho", q.dtype, (B, Tq, Hq, d), q.device)
     _need(q, "q", q.dtype, (B, Tq, Hq, d), q.device)
-    desc = make_desc(B, Tq, Tk, Hq, Hkv, d, causal, window, scale, dt, False, split_rows)
+    oc, odt = _out_code(out_dtype)
+    desc = make_desc(B, Tq, Tk, Hq, Hkv, d, causal, window, scale, dt, False, split_rows, oc)
     f32 = dict(dtype=torch.float32, device=q.device)
-    out = torch.empty((B, Tq, Hq, d), **f32)
+    out = torch.empty((B, Tq, Hq, d), dtype=odt, device=q.device)
     lse = torch.empty((B, Hq, Tq), **f32)
     osa = torch.empty((B, Tq, Hq, d), **f32)
     rk = torch.empty((B, Hq, Tq), **f32)
+    ratio = torch.empty((B, Hq, Tq), **f32) if cor else None
     lib = get_lib()
     nws = lib.parallax_attn_fwd_probe_workspace(ctypes.byref(desc))
     ws = _workspace(nws, q.device)
     _check(lib.parallax_attn_fwd_probe(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(rho), _ptr(out),
-                                       _ptr(lse), _ptr(osa), _ptr(rk), _ptr(ws), nws, _stream()))
-    return out, lse, osa, rk
+                                       _ptr(lse), _ptr(osa), _ptr(rk), _ptr(ratio), _ptr(ws), nws, _stream()))
+    return (out, lse, osa, rk, ratio) if cor else (out, lse, osa, rk)
 
 
 def parallax_attn_bwd_probe(q, k, v, rho, out, dout, lse, o_sa, rk, causal=True, window=0, scale=None,
@@ -247,8 +265,10 @@ def parallax_attn_bwd(q, k, v, P, out, dout, lse, kbar, o_sa, causal=True, windo
     return dq, dk, dv, dP
 
 
-def parallax_attn_decode(q, k_cache, v_cache, P, seqlens=None, window=0, scale=None):
-    """Decode; q [B,Hq,d], caches [B,Lmax,Hkv,d], seqlens int32 [B] or None; returns out [B,Hq,d] float32."""
+def parallax_attn_decode(q, k_cache, v_cache, P, seqlens=None, window=0, scale=None, out_dtype=torch.float32,
+                         cor=False):
+    """Decode; q [B,Hq,d], caches [B,Lmax,Hkv,d], seqlens int32 [B] or None; returns out [B,Hq,d] (float32 or
+    `out_dtype`), and the correction-to-output ratio [B,Hq] as well when cor=True."""
     B, Hq, d = q.shape
     Lmax, Hkv = k_cache.shape[1], k_cache.shape[2]
     dt = _dtype_code(q)
@@ -258,18 +278,20 @@ def parallax_attn_decode(q, k_cache, v_cache, P, seqlens=None, window=0, scale=N
     _need(P, "P", q.dtype, (Hq, d, d), dev)
     if seqlens is not None:
         _need(seqlens, "seqlens", torch.int32, (B,), dev)
-    desc = make_desc(B, 1, Lmax, Hq, Hkv, d, True, window, scale, dt, False, -1)
-    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    oc, odt = _out_code(out_dtype)
+    desc = make_desc(B, 1, Lmax, Hq, Hkv, d, True, window, scale, dt, False, -1, oc)
+    out = torch.empty((B, Hq, d), dtype=odt, device=dev)
+    ratio = torch.empty((B, Hq), dtype=torch.float32, device=dev) if cor else None
     lib = get_lib()
     nws = lib.parallax_attn_decode_workspace(ctypes.byref(desc))
     ws = _workspace(nws, dev)
     _check(lib.parallax_attn_decode(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                                    _ptr(seqlens), _ptr(P), _ptr(out), _ptr(ws), nws, _stream()))
-    return out
+                                    _ptr(seqlens), _ptr(P), _ptr(out), _ptr(ratio), _ptr(ws), nws, _stream()))
+    return (out, ratio) if cor else out
 
 
 def parallax_attn_decode_paged(q, k_pages, v_pages, block_table, P, seqlens=None, seqlen_k=None, window=0,
-                               scale=None):
+                               scale=None, out_dtype=torch.float32, cor=False):
     """Decode against a paged cache: q [B,Hq,d]; pages [num_pages,page_size,Hkv,d]; block_table int32
     [B,max_pages]; seqlens int32 [B] or None; seqlen_k defaults to max_pages * page_size.
     Returns out [B,Hq,d] float32 (see include/parallax.h)."""
@@ -288,15 +310,17 @@ def parallax_attn_decode_paged(q, k_pages, v_pages, block_table, P, seqlens=None
         raise ValueError(f"seqlen_k={Lmax} needs more than the block table's {block_table.shape[1]} pages")
     if seqlens is not None:
         _need(seqlens, "seqlens", torch.int32, (B,), dev)
-    desc = make_desc(B, 1, Lmax, Hq, Hkv, d, True, window, scale, dt, False, -1)
-    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    oc, odt = _out_code(out_dtype)
+    desc = make_desc(B, 1, Lmax, Hq, Hkv, d, True, window, scale, dt, False, -1, oc)
+    out = torch.empty((B, Hq, d), dtype=odt, device=dev)
+    ratio = torch.empty((B, Hq), dtype=torch.float32, device=dev) if cor else None
     lib = get_lib()
     nws = lib.parallax_attn_decode_paged_workspace(ctypes.byref(desc))
     ws = _workspace(nws, dev)
     _check(lib.parallax_attn_decode_paged(ctypes.byref(desc), _ptr(q), _ptr(k_pages), _ptr(v_pages), num_pages,
                                           page_size, _ptr(block_table), _ptr(seqlens), _ptr(P), _ptr(out),
-                                          _ptr(ws), nws, _stream()))
-    return out
+                                          _ptr(ratio), _ptr(ws), nws, _stream()))
+    return (out, ratio) if cor else out
 
 
 fwd = parallax_attn_fwd

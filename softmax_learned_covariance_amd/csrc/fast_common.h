@@ -58,6 +58,22 @@ __host__ __device__ constexpr int perm16(int p) { return 8 * ((p & 7) >> 2) + 4 
 
 __device__ __forceinline__ float bf16_to_f32(u16 b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 
+// fp32 -> bf16 bits, rounded to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Four consecutive output values at element index i of an fp32 or a bf16 output array.
+__device__ __forceinline__ void store_out4(void* out, int64_t i, bool bf16, float a, float b, float c, float d) {
+  if (bf16)
+    *reinterpret_cast<uint2*>(static_cast<u16*>(out) + i) =
+        uint2{f32_to_bf16(a) | (f32_to_bf16(b) << 16), f32_to_bf16(c) | (f32_to_bf16(d) << 16)};
+  else
+    *reinterpret_cast<float4*>(static_cast<float*>(out) + i) = float4{a, b, c, d};
+}
+
 // 2^(15 - E(m)) for the magnitude bound m (1 for m == 0 or non-finite m).
 __device__ __forceinline__ float range_scale(float m) {
   const uint32_t bits = __float_as_uint(m);

@@ -34,7 +34,9 @@ struct DecParams {
   const int32_t* seqlens;
   const int32_t* block_table;    // paged cache: [B][max_pages] page indices
   int max_pages, page_shift, num_pages;
-  float* out;
+  void* out;                     // fp32, or bf16 when out_bf16
+  float* cor;                    // per query |out - o| / |out| [B][Hq] (nullable)
+  int out_bf16;
   // workspace
   float *pm, *pl, *po, *pk;      // pass 1 partials: [B][Hq][ns] (m, l) and [B][Hq][ns][128] (o, kbar)
   float *so, *su, *salpha, *slse;  // combined: o, u [B][Hq][128], alpha, lse [B][Hq]
@@ -382,7 +384,27 @@ __global__ __launch_bounds__(128) void k_dec_finish(DecParams p) {
   const int64_t bh = static_cast<int64_t>(b) * p.Hq + h;
   float c = 0.f;
   for (int s = 0; s < p.ns; ++s) c += p.pc[(bh * p.ns + s) * kD + d];
-  p.out[bh * kD + d] = p.so[bh * kD + d] + c;
+  const float r = p.so[bh * kD + d] + c;
+  if (p.out_bf16) static_cast<u16*>(p.out)[bh * kD + d] = static_cast<u16>(f32_to_bf16(r));
+  else static_cast<float*>(p.out)[bh * kD + d] = r;
+  if (p.cor) {
+    __shared__ float part[2][2];
+    float cc = c * c, oo = r * r;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      cc += __shfl_xor(cc, o, 64);
+      oo += __shfl_xor(oo, o, 64);
+    }
+    if ((d & 63) == 0) {
+      part[d >> 6][0] = cc;
+      part[d >> 6][1] = oo;
+    }
+    __syncthreads();
+    if (d == 0) {
+      const float C = part[0][0] + part[1][0], O = part[0][1] + part[1][1];
+      p.cor[bh] = O > 0.f ? sqrtf(C / O) : 0.f;
+    }
+  }
 }
 
 struct DecWs {
@@ -449,7 +471,8 @@ void launch_all(const DecParams& p, const dim3& grid, int Hq, int B, hipStream_t
 }  // namespace
 
 hipError_t launch_fast_decode(const Geom& g, const void* q, const void* kc, const void* vc, const int32_t* seqlens,
-                              const void* P, float* out, void* ws, hipStream_t stream, const PagedCache* paged) {
+                              const void* P, void* out, float* cor, void* ws, hipStream_t stream,
+                              const PagedCache* paged) {
   const DecWs w = dec_layout(g, ws);
   DecParams p{};
   p.q = static_cast<const u16*>(q);
@@ -458,6 +481,8 @@ hipError_t launch_fast_decode(const Geom& g, const void* q, const void* kc, cons
   p.P = static_cast<const u16*>(P);
   p.seqlens = seqlens;
   p.out = out;
+  p.out_bf16 = g.out_bf16;
+  p.cor = cor;
   p.pm = w.pm;
   p.pl = w.pl;
   p.po = w.po;

@@ -45,8 +45,11 @@ struct FwdParams {
   const u16* rho;   // probe form only: the caller's probe, like q
   const _Float16 *k16, *k16t, *v16t, *p16t;
   const uint32_t* maxbits;
-  float *out, *lse, *kbar, *osa;
-  float* rk;        // probe form only: rho . kbar per row, [B][Hq][Tq] (nullable)
+  void* out;        // fp32, or bf16 when out_bf16
+  float *lse, *kbar, *osa;
+  float* rk;
+  float* cor;       // per row |out - o| / |out|, [B][Hq][Tq] (nullable)
+  int out_bf16;        // probe form only: rho . kbar per row, [B][Hq][Tq] (nullable)
   int B, Tq, Tk, Tk_pad, Hq, Hkv, G, causal, window;
   float scale;
   int row_begin, row_end, rows_per_block, n_rb;  // rows [row_begin, row_end)
@@ -455,6 +458,7 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
 
   // ---------------- epilogue 2: out = o + c - rs o ----------------
   const float RS = xor32_sum(rpart);
+  float cc = 0.f, oo = 0.f;   // |out - o|^2 and |out|^2 of the lane's half-row
   if (row_ok) {
     const float fc = 16777216.f / (sU * sK * sV);
     const float frs = RS * (16777216.f / (sU * sK));
@@ -467,9 +471,19 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
         const float o4[4] = {ov.x, ov.y, ov.z, ov.w};
         float r4[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) r4[e] = o4[e] + accC[mt][4 * j + e] * fc - frs * o4[e];
-        *reinterpret_cast<float4*>(p.out + qoff + d) = float4{r4[0], r4[1], r4[2], r4[3]};
+        for (int e = 0; e < 4; ++e) {
+          r4[e] = o4[e] + accC[mt][4 * j + e] * fc - frs * o4[e];
+          cc = fmaf(r4[e] - o4[e], r4[e] - o4[e], cc);
+          oo = fmaf(r4[e], r4[e], oo);
+        }
+        store_out4(p.out, qoff + d, p.out_bf16, r4[0], r4[1], r4[2], r4[3]);
       }
+  }
+  if (p.cor) {
+    cc = xor32_sum(cc);
+    oo = xor32_sum(oo);
+    if (row_ok && hh == 0)
+      p.cor[(static_cast<int64_t>(b) * p.Hq + h) * p.Tq + row] = oo > 0.f ? sqrtf(cc / oo) : 0.f;
   }
 }
 
@@ -682,6 +696,7 @@ __global__ __launch_bounds__(512) void k_fwd_probe(FwdParams p) {
   const float RS = xor32_sum(rpart);
   const bool has = L > 0.f;
   const float invL = has ? 1.f / L : 0.f;
+  float cc = 0.f, oo = 0.f;   // |out - o|^2 and |out|^2 of the lane's half-row
   if (row_ok) {
     const float fo = invL / sV;
     const float fc = fo / sK / (kProbeW * sR);
@@ -701,10 +716,18 @@ __global__ __launch_bounds__(512) void k_fwd_probe(FwdParams p) {
         for (int e = 0; e < 4; ++e) {
           o4[e] = accO[mt][4 * j + e] * fo;
           r4[e] = o4[e] - accC[mt][4 * j + e] * fc + a * o4[e];
+          cc = fmaf(r4[e] - o4[e], r4[e] - o4[e], cc);
+          oo = fmaf(r4[e], r4[e], oo);
         }
-        *reinterpret_cast<float4*>(p.out + qoff + d) = float4{r4[0], r4[1], r4[2], r4[3]};
+        store_out4(p.out, qoff + d, p.out_bf16, r4[0], r4[1], r4[2], r4[3]);
         if (p.osa) *reinterpret_cast<float4*>(p.osa + qoff + d) = float4{o4[0], o4[1], o4[2], o4[3]};
       }
+  }
+  if (p.cor) {
+    cc = xor32_sum(cc);
+    oo = xor32_sum(oo);
+    if (row_ok && hh == 0)
+      p.cor[(static_cast<int64_t>(b) * p.Hq + h) * p.Tq + row] = oo > 0.f ? sqrtf(cc / oo) : 0.f;
   }
 }
 
@@ -721,7 +744,7 @@ size_t fast_fwd_workspace(const Geom& g) {
 }
 
 hipError_t launch_fast_fwd(const Geom& g, const void* q, const void* k, const void* v,
-                           const void* P, float* out, float* lse, float* kbar, float* osa,
+                           const void* P, void* out, float* lse, float* kbar, float* osa, float* cor,
                            int split_rows, void* ws, hipStream_t stream) {
   const Staging s = staging_layout(ws, g.B, g.Tk, g.Hkv, g.Hq);
   float* o_ws = reinterpret_cast<float*>(static_cast<char*>(ws) + s.bytes);
@@ -740,6 +763,8 @@ hipError_t launch_fast_fwd(const Geom& g, const void* q, const void* k, const vo
     p.p16t = s.p16t;
     p.maxbits = s.maxbits;
     p.out = out;
+    p.out_bf16 = g.out_bf16;
+    p.cor = cor;
     p.lse = lse;
     p.kbar = kbar;
     p.osa = osa ? osa : o_ws;
@@ -787,7 +812,7 @@ bool fast_probe_supported(const Geom& g) { return fast_fwd_supported(g); }
 size_t fast_probe_workspace(const Geom& g) { return staging_layout(nullptr, g.B, g.Tk, g.Hkv, g.Hq).bytes; }
 
 hipError_t launch_fast_probe(const Geom& g, const void* q, const void* k, const void* v, const void* rho,
-                             float* out, float* lse, float* osa, float* rk, int split_rows, void* ws,
+                             void* out, float* lse, float* osa, float* rk, float* cor, int split_rows, void* ws,
                              hipStream_t stream) {
   const Staging s = staging_layout(ws, g.B, g.Tk, g.Hkv, g.Hq);
   int split = split_rows < kMinSplitRows ? kMinSplitRows : split_rows;
@@ -805,6 +830,8 @@ hipError_t launch_fast_probe(const Geom& g, const void* q, const void* k, const 
     p.v16t = s.v16t;
     p.maxbits = s.maxbits;
     p.out = out;
+    p.out_bf16 = g.out_bf16;
+    p.cor = cor;
     p.lse = lse;
     p.osa = osa;
     p.rk = rk;

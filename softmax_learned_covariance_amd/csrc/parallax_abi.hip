@@ -49,6 +49,8 @@ plx_status check_desc(const plx_attn_desc* d, const char* what, plx::Geom* g) {
     return fail(PLX_ERR_UNSUPPORTED, "%s: head_dim=%d > 128 is not supported", what, d->head_dim);
   if (d->dtype != PLX_F32 && d->dtype != PLX_BF16)
     return fail(PLX_ERR_INVALID, "%s: unknown dtype %d", what, d->dtype);
+  if (d->out_dtype != PLX_F32 && d->out_dtype != PLX_BF16)
+    return fail(PLX_ERR_INVALID, "%s: unknown out_dtype %d", what, d->out_dtype);
   if (d->p_per_query != 0 && d->p_per_query != 1)
     return fail(PLX_ERR_INVALID, "%s: p_per_query must be 0 or 1", what);
   if (!(d->softmax_scale == d->softmax_scale) || isinf(d->softmax_scale))
@@ -64,6 +66,7 @@ plx_status check_desc(const plx_attn_desc* d, const char* what, plx::Geom* g) {
   g->scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.f / sqrtf(static_cast<float>(d->head_dim));
   g->bf16 = d->dtype == PLX_BF16;
   g->p_per_query = d->p_per_query;
+  g->out_bf16 = d->out_dtype == PLX_BF16;
   return PLX_OK;
 }
 
@@ -178,8 +181,8 @@ size_t parallax_attn_fwd_workspace(const plx_attn_desc* desc) {
 }
 
 plx_status parallax_attn_fwd(const plx_attn_desc* desc, const void* q, const void* k,
-                             const void* v, const void* P, float* out, float* lse, float* kbar,
-                             float* o_sa, void* workspace, size_t workspace_bytes,
+                             const void* v, const void* P, void* out, float* lse, float* kbar,
+                             float* o_sa, float* cor, void* workspace, size_t workspace_bytes,
                              void* hip_stream) {
   const char* what = "parallax_attn_fwd";
   plx::Geom g;
@@ -192,12 +195,15 @@ plx_status parallax_attn_fwd(const plx_attn_desc* desc, const void* q, const voi
   st = check_ws(fwd_ws(g), workspace, workspace_bytes, what);
   if (st != PLX_OK) return st;
   if (empty) return ok();
+  if (!plx::fast_fwd_supported(g) && (g.out_bf16 || cor))
+    return fail(PLX_ERR_UNSUPPORTED, "%s: bf16 out and cor need the bf16 fast path", what);
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   hipError_t e;
   if (plx::fast_fwd_supported(g))
-    e = plx::launch_fast_fwd(g, q, k, v, P, out, lse, kbar, o_sa, split_rows_of(desc), workspace, stream);
+    e = plx::launch_fast_fwd(g, q, k, v, P, out, lse, kbar, o_sa, cor, split_rows_of(desc), workspace, stream);
   else
-    e = plx::launch_generic_fwd(g, q, k, v, P, nullptr, out, lse, kbar, o_sa, 0, g.Tq, stream, true);
+    e = plx::launch_generic_fwd(g, q, k, v, P, nullptr, static_cast<float*>(out), lse, kbar, o_sa, 0, g.Tq,
+                                stream, true);
   return hip_status(e, what);
 }
 
@@ -208,8 +214,9 @@ size_t parallax_attn_fwd_probe_workspace(const plx_attn_desc* desc) {
 }
 
 plx_status parallax_attn_fwd_probe(const plx_attn_desc* desc, const void* q, const void* k,
-                                   const void* v, const void* rho, float* out, float* lse, float* o_sa,
-                                   float* rk, void* workspace, size_t workspace_bytes, void* hip_stream) {
+                                   const void* v, const void* rho, void* out, float* lse, float* o_sa,
+                                   float* rk, float* cor, void* workspace, size_t workspace_bytes,
+                                   void* hip_stream) {
   const char* what = "parallax_attn_fwd_probe";
   plx::Geom g;
   plx_status st = check_desc(desc, what, &g);
@@ -225,7 +232,7 @@ plx_status parallax_attn_fwd_probe(const plx_attn_desc* desc, const void* q, con
   if (st != PLX_OK) return st;
   if (empty) return ok();
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  return hip_status(plx::launch_fast_probe(g, q, k, v, rho, out, lse, o_sa, rk, split_rows_of(desc), workspace,
+  return hip_status(plx::launch_fast_probe(g, q, k, v, rho, out, lse, o_sa, rk, cor, split_rows_of(desc), workspace,
                                            stream),
                     what);
 }
@@ -245,6 +252,7 @@ plx_status parallax_attn_bwd_probe(const plx_attn_desc* desc, const void* q, con
   plx::Geom g;
   plx_status st = check_desc(desc, what, &g);
   if (st != PLX_OK) return st;
+  if (g.out_bf16) return fail(PLX_ERR_UNSUPPORTED, "%s: the backward reads an fp32 out (out_dtype PLX_F32)", what);
   // the empty cases only write zeros; the kernels need every extent >= 1
   plx::Geom gs = g;
   gs.B = gs.Tq = gs.Tk = 1;
@@ -293,6 +301,7 @@ plx_status parallax_attn_bwd(const plx_attn_desc* desc, const void* q, const voi
   if (st != PLX_OK) return st;
   if (g.p_per_query)
     return fail(PLX_ERR_UNSUPPORTED, "%s: per-query projectors have no backward", what);
+  if (g.out_bf16) return fail(PLX_ERR_UNSUPPORTED, "%s: the backward reads an fp32 out (out_dtype PLX_F32)", what);
   if (!P || !dP) return fail(PLX_ERR_INVALID, "%s: P and dP must not be NULL", what);
   const bool rows = g.B > 0 && g.Tq > 0;
   const bool keys = g.B > 0 && g.Tk > 0;
@@ -323,7 +332,7 @@ size_t parallax_attn_decode_workspace(const plx_attn_desc* desc) {
 
 plx_status parallax_attn_decode(const plx_attn_desc* desc, const void* q, const void* k_cache,
                                 const void* v_cache, const int32_t* seqlens_k, const void* P,
-                                float* out, void* workspace, size_t workspace_bytes,
+                                void* out, float* cor, void* workspace, size_t workspace_bytes,
                                 void* hip_stream) {
   const char* what = "parallax_attn_decode";
   plx::Geom g;
@@ -341,12 +350,14 @@ plx_status parallax_attn_decode(const plx_attn_desc* desc, const void* q, const 
     return fail(PLX_ERR_INVALID, "%s: k_cache and v_cache must not be NULL", what);
   st = check_ws(dec_ws(g), workspace, workspace_bytes, what);
   if (st != PLX_OK) return st;
+  if (!plx::fast_decode_supported(g) && (g.out_bf16 || cor))
+    return fail(PLX_ERR_UNSUPPORTED, "%s: bf16 out and cor need the bf16 fast path", what);
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   hipError_t e;
   if (plx::fast_decode_supported(g))
-    e = plx::launch_fast_decode(g, q, k_cache, v_cache, seqlens_k, P, out, workspace, stream);
+    e = plx::launch_fast_decode(g, q, k_cache, v_cache, seqlens_k, P, out, cor, workspace, stream);
   else
-    e = plx::launch_generic_fwd(g, q, k_cache, v_cache, P, seqlens_k, out, nullptr, nullptr,
+    e = plx::launch_generic_fwd(g, q, k_cache, v_cache, P, seqlens_k, static_cast<float*>(out), nullptr, nullptr,
                                 nullptr, 0, 1, stream, true, PLX_KERNEL_DECODE_PASS1);
   return hip_status(e, what);
 }
@@ -362,7 +373,8 @@ size_t parallax_attn_decode_paged_workspace(const plx_attn_desc* desc) {
 plx_status parallax_attn_decode_paged(const plx_attn_desc* desc, const void* q, const void* k_pages,
                                       const void* v_pages, int32_t num_pages, int32_t page_size,
                                       const int32_t* block_table, const int32_t* seqlens_k, const void* P,
-                                      float* out, void* workspace, size_t workspace_bytes, void* hip_stream) {
+                                      void* out, float* cor, void* workspace, size_t workspace_bytes,
+                                      void* hip_stream) {
   const char* what = "parallax_attn_decode_paged";
   plx::Geom g;
   plx_status st = check_desc(desc, what, &g);
@@ -387,7 +399,8 @@ plx_status parallax_attn_decode_paged(const plx_attn_desc* desc, const void* q, 
   if (st != PLX_OK) return st;
   plx::PagedCache pc{block_table, num_pages, page_size, (g.Tk + page_size - 1) / page_size};
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  return hip_status(plx::launch_fast_decode(g, q, k_pages, v_pages, seqlens_k, P, out, workspace, stream, &pc), what);
+  return hip_status(plx::launch_fast_decode(g, q, k_pages, v_pages, seqlens_k, P, out, cor, workspace, stream, &pc),
+                    what);
 }
 
 }  // extern "C"

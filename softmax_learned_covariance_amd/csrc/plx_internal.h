@@ -15,6 +15,7 @@ struct Geom {
   float scale;
   int bf16;          // 1: inputs are bf16, 0: fp32
   int p_per_query;
+  int out_bf16;      // 1: `out` of the forwards and decodes is bf16 (fast paths only)
 };
 
 // bf16 fast path: the first query rows see only a few keys, and their correction terms cancel
@@ -46,7 +47,7 @@ hipError_t launch_generic_bwd(const Geom& g, const void* q, const void* k, const
 bool fast_probe_supported(const Geom& g);
 size_t fast_probe_workspace(const Geom& g);
 hipError_t launch_fast_probe(const Geom& g, const void* q, const void* k, const void* v, const void* rho,
-                             float* out, float* lse, float* osa, float* rk, int split_rows, void* ws,
+                             void* out, float* lse, float* osa, float* rk, float* cor, int split_rows, void* ws,
                              hipStream_t stream);
 // Its backward (u = -rho, no projector): dq, dk, dv and drho.
 bool fast_probe_bwd_supported(const Geom& g);
@@ -60,7 +61,7 @@ hipError_t launch_zero_f32(float* x, int64_t n, hipStream_t stream);   // n a mu
 bool fast_fwd_supported(const Geom& g);
 size_t fast_fwd_workspace(const Geom& g);
 hipError_t launch_fast_fwd(const Geom& g, const void* q, const void* k, const void* v,
-                           const void* P, float* out, float* lse, float* kbar, float* osa,
+                           const void* P, void* out, float* lse, float* kbar, float* osa, float* cor,
                            int split_rows, void* ws, hipStream_t stream);
 
 bool fast_bwd_supported(const Geom& g);
@@ -80,7 +81,7 @@ struct PagedCache {
   int num_pages, page_size, max_pages;
 };
 hipError_t launch_fast_decode(const Geom& g, const void* q, const void* kc, const void* vc,
-                              const int32_t* seqlens, const void* P, float* out, void* ws,
+                              const int32_t* seqlens, const void* P, void* out, float* cor, void* ws,
                               hipStream_t stream, const PagedCache* paged = nullptr);
 
 // Records the profiling hook's `before` / `after` event on `stream` when `kernel` (a plx_kernel)

@@ -47,8 +47,8 @@ def test_abi_version_and_status_strings(plx):
 
 
 def test_desc_layout_matches_header(plx):
-    # 11 int32 fields and one float, no padding
-    assert ctypes.sizeof(plx.PlxAttnDesc) == 48
+    # 12 int32 fields and one float, no padding
+    assert ctypes.sizeof(plx.PlxAttnDesc) == 52
 
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
@@ -56,17 +56,17 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails val
 
 def _desc(plx, **kw):
     base = dict(B=1, Tq=8, Tk=8, Hq=2, Hkv=1, d=16, causal=True, window=0, scale=None,
-                dtype=plx.PLX_F32, p_per_query=False, split_rows=-1)
+                dtype=plx.PLX_F32, p_per_query=False, split_rows=-1, out_dtype=plx.PLX_F32)
     base.update(kw)
     return plx.make_desc(base["B"], base["Tq"], base["Tk"], base["Hq"], base["Hkv"], base["d"],
                          base["causal"], base["window"], base["scale"], base["dtype"],
-                         base["p_per_query"], base["split_rows"])
+                         base["p_per_query"], base["split_rows"], base["out_dtype"])
 
 
 def _fwd(plx, desc, q=FAKE, k=FAKE, v=FAKE, P=FAKE, out=FAKE, ws=None, nws=0):
     lib = plx.get_lib()
     return lib.parallax_attn_fwd(ctypes.byref(desc) if desc is not None else None, q, k, v, P, out,
-                                 None, None, None, ws, nws, None)
+                                 None, None, None, None, ws, nws, None)
 
 
 def _bwd(plx, desc, ws=FAKE, nws=1 << 40, **null):
@@ -78,7 +78,7 @@ def _bwd(plx, desc, ws=FAKE, nws=1 << 40, **null):
 
 def _dec(plx, desc, q=FAKE, P=FAKE, out=FAKE, ws=FAKE, nws=1 << 40):
     lib = plx.get_lib()
-    return lib.parallax_attn_decode(ctypes.byref(desc), q, FAKE, FAKE, None, P, out, ws, nws, None)
+    return lib.parallax_attn_decode(ctypes.byref(desc), q, FAKE, FAKE, None, P, out, None, ws, nws, None)
 
 
 def test_forward_validation(plx):
@@ -132,7 +132,8 @@ def test_decode_validation(plx):
 
 def _probe(plx, desc, q=FAKE, rho=FAKE, out=FAKE, ws=FAKE, nws=1 << 40):
     lib = plx.get_lib()
-    return lib.parallax_attn_fwd_probe(ctypes.byref(desc), q, FAKE, FAKE, rho, out, None, None, None, ws, nws, None)
+    return lib.parallax_attn_fwd_probe(ctypes.byref(desc), q, FAKE, FAKE, rho, out, None, None, None, None, ws, nws,
+                                       None)
 
 
 def test_probe_validation(plx):
@@ -185,7 +186,7 @@ def test_paged_decode_validation(plx):
 
     def call(desc, num_pages=4, page=16, table=FAKE, q=FAKE, ws=FAKE, nws=1 << 40):
         return lib.parallax_attn_decode_paged(ctypes.byref(desc), q, FAKE, FAKE, num_pages, page, table, None,
-                                              FAKE, FAKE, ws, nws, None)
+                                              FAKE, FAKE, None, ws, nws, None)
 
     d = _desc(plx, **bf)
     assert call(_desc(plx, dtype=plx.PLX_BF16, d=128, Tq=2)) == E.PLX_ERR_INVALID
@@ -201,6 +202,23 @@ def test_paged_decode_validation(plx):
     assert need > 0 and need == lib.parallax_attn_decode_workspace(ctypes.byref(d))
     assert call(d, nws=need - 1) == E.PLX_ERR_WORKSPACE
     assert call(_desc(plx, B=0, **bf), ws=None, nws=0) in (E.PLX_OK, E.PLX_ERR_INVALID)
+
+
+def test_output_options_validation(plx):
+    """out_dtype must be a known dtype; bf16 out and the correction ratio need the bf16 fast path; the
+    backwards read an fp32 out."""
+    E = plx
+    lib = plx.get_lib()
+    assert _fwd(plx, _desc(plx, out_dtype=7)) == E.PLX_ERR_INVALID
+    assert b"out_dtype" in lib.parallax_last_error()
+    assert _fwd(plx, _desc(plx, out_dtype=plx.PLX_BF16)) == E.PLX_ERR_UNSUPPORTED     # fp32 inputs
+    d = _desc(plx)
+    assert lib.parallax_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, None, 0,
+                                 None) == E.PLX_ERR_UNSUPPORTED                          # cor on the fp32 path
+    assert _dec(plx, _desc(plx, Tq=1, out_dtype=plx.PLX_BF16)) == E.PLX_ERR_UNSUPPORTED
+    bfd = _desc(plx, dtype=plx.PLX_BF16, d=128, out_dtype=plx.PLX_BF16)
+    assert _bwd(plx, bfd) == E.PLX_ERR_UNSUPPORTED
+    assert b"fp32 out" in lib.parallax_last_error()
 
 
 def test_bench_refuses_more_than_one_gpu():
