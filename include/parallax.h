@@ -207,17 +207,19 @@ plx_status parallax_attn_bwd(const plx_attn_desc* desc,
 size_t parallax_attn_decode_workspace(const plx_attn_desc* desc);
 
 /*
- * Decode: one new query per sequence against a key/value cache (the decode path
- * of the pages' hardware section).  The new token's key and value are already
- * the last entry of its sequence, so query b sees cache rows
- * [max(0, L_b - window), L_b) with L_b = seqlens_k[b] (or Lmax when seqlens_k is
- * NULL).  desc->seqlen_q must be 1, desc->seqlen_k is Lmax, desc->causal is
- * ignored, desc->p_per_query must be 0.  seqlens_k values are clamped to
- * [0, Lmax]; a sequence of length 0 gets out = 0.
- *   q        [B][Hq][d]            k_cache, v_cache [B][Lmax][Hkv][d]
+ * Decode: T = desc->seqlen_q new queries per sequence against a key/value cache (the
+ * decode path of the pages' hardware section; T > 1 for speculative or chunked
+ * decoding).  The new tokens' keys and values are already the last T entries of their
+ * sequence, so new token t of sequence b sees cache rows [max(0, e - window), e) with
+ * e = L_b - (T - 1 - t) and L_b = seqlens_k[b] (or Lmax when seqlens_k is NULL).
+ * desc->seqlen_k is Lmax, desc->causal is ignored, desc->p_per_query must be 0.
+ * seqlens_k values are clamped to [0, Lmax]; a token that sees no key gets out = 0.
+ * T > 1 needs the bf16 fast path (else PLX_ERR_UNSUPPORTED).
+ *   q        [B][T][Hq][d] (for T = 1 also read as [B][Hq][d])
+ *   k_cache, v_cache [B][Lmax][Hkv][d]
  *   seqlens_k [B] int32 device array (nullable)
- *   P        [Hq][d][d]            out [B][Hq][d] fp32, or bf16 when desc->out_dtype is PLX_BF16
- *   cor      [B][Hq] fp32 correction-to-output ratio as in the forward (nullable; bf16 fast path only)
+ *   P        [Hq][d][d]            out [B][T][Hq][d] fp32, or bf16 when desc->out_dtype is PLX_BF16
+ *   cor      [B][T][Hq] fp32 correction-to-output ratio as in the forward (nullable; bf16 fast path only)
  */
 plx_status parallax_attn_decode(const plx_attn_desc* desc,
                                 const void* q, const void* k_cache, const void* v_cache,
@@ -235,13 +237,13 @@ size_t parallax_attn_decode_paged_workspace(const plx_attn_desc* desc);
  * benchmark spans batch sizes and context lengths): the same result as parallax_attn_decode on the
  * sequences the block table describes.  Key j of sequence b is slot j % page_size of page
  * block_table[b][j / page_size].
- *   q            [B][Hq][d]                     dtype desc->dtype
+ *   q            [B][T][Hq][d], T = desc->seqlen_q  dtype desc->dtype
  *   k_pages, v_pages [num_pages][page_size][Hkv][d]   dtype desc->dtype
  *   block_table  [B][max_pages] int32 device array, max_pages = ceil(desc->seqlen_k / page_size);
  *                only the entries that cover keys < seqlens_k[b] are read
  *   seqlens_k    [B] int32 device array (nullable: every sequence has desc->seqlen_k keys)
- *   P [Hq][d][d]     out [B][Hq][d] fp32 (bf16 when desc->out_dtype is PLX_BF16)     cor [B][Hq] (nullable)
- * desc->seqlen_q must be 1 and desc->seqlen_k is the longest sequence the table can describe.
+ *   P [Hq][d][d]     out [B][T][Hq][d] fp32 (bf16 when desc->out_dtype is PLX_BF16)     cor [B][T][Hq] (nullable)
+ * New tokens as in parallax_attn_decode; desc->seqlen_k is the longest sequence the table can describe.
  * page_size must be a power of two (1 .. 65536) and num_pages >= 1.  Block-table entries outside
  * [0, num_pages) are clamped into the pool: that sequence's output is then wrong, but nothing is
  * read outside the caller's arrays.

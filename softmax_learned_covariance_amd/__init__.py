@@ -267,9 +267,12 @@ def parallax_attn_bwd(q, k, v, P, out, dout, lse, kbar, o_sa, causal=True, windo
 
 def parallax_attn_decode(q, k_cache, v_cache, P, seqlens=None, window=0, scale=None, out_dtype=torch.float32,
                          cor=False):
-    """Decode; q [B,Hq,d], caches [B,Lmax,Hkv,d], seqlens int32 [B] or None; returns out [B,Hq,d] (float32 or
-    `out_dtype`), and the correction-to-output ratio [B,Hq] as well when cor=True."""
-    B, Hq, d = q.shape
+    """Decode; q [B,Hq,d] (one new token) or [B,T,Hq,d] (the last T tokens of each sequence), caches
+    [B,Lmax,Hkv,d], seqlens int32 [B] or None; returns out shaped like q (float32 or `out_dtype`), and the
+    correction-to-output ratio (q's shape without d) as well when cor=True."""
+    lead = q.shape[:-2]
+    B, Hq, d = q.shape[0], q.shape[-2], q.shape[-1]
+    T = q.shape[1] if q.dim() == 4 else 1
     Lmax, Hkv = k_cache.shape[1], k_cache.shape[2]
     dt = _dtype_code(q)
     dev = q.device
@@ -279,9 +282,11 @@ def parallax_attn_decode(q, k_cache, v_cache, P, seqlens=None, window=0, scale=N
     if seqlens is not None:
         _need(seqlens, "seqlens", torch.int32, (B,), dev)
     oc, odt = _out_code(out_dtype)
-    desc = make_desc(B, 1, Lmax, Hq, Hkv, d, True, window, scale, dt, False, -1, oc)
-    out = torch.empty((B, Hq, d), dtype=odt, device=dev)
-    ratio = torch.empty((B, Hq), dtype=torch.float32, device=dev) if cor else None
+    desc = make_desc(B, T, Lmax, Hq, Hkv, d, True, window, scale, dt, False, -1, oc)
+    out = torch.empty((*lead, Hq, d), dtype=odt, device=dev)
+    ratio = torch.empty((*lead, Hq), dtype=torch.float32, device=dev) if cor else None
+    if not q.is_contiguous():
+        raise ValueError("q: must be contiguous")
     lib = get_lib()
     nws = lib.parallax_attn_decode_workspace(ctypes.byref(desc))
     ws = _workspace(nws, dev)
@@ -292,10 +297,14 @@ def parallax_attn_decode(q, k_cache, v_cache, P, seqlens=None, window=0, scale=N
 
 def parallax_attn_decode_paged(q, k_pages, v_pages, block_table, P, seqlens=None, seqlen_k=None, window=0,
                                scale=None, out_dtype=torch.float32, cor=False):
-    """Decode against a paged cache: q [B,Hq,d]; pages [num_pages,page_size,Hkv,d]; block_table int32
-    [B,max_pages]; seqlens int32 [B] or None; seqlen_k defaults to max_pages * page_size.
-    Returns out [B,Hq,d] float32 (see include/parallax.h)."""
-    B, Hq, d = q.shape
+    """Decode against a paged cache: q [B,Hq,d] or [B,T,Hq,d]; pages [num_pages,page_size,Hkv,d]; block_table
+    int32 [B,max_pages]; seqlens int32 [B] or None; seqlen_k defaults to max_pages * page_size.
+    Returns out shaped like q (see include/parallax.h)."""
+    lead = q.shape[:-2]
+    B, Hq, d = q.shape[0], q.shape[-2], q.shape[-1]
+    T = q.shape[1] if q.dim() == 4 else 1
+    if not q.is_contiguous():
+        raise ValueError("q: must be contiguous")
     num_pages, page_size, Hkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
     dt = _dtype_code(q)
     dev = q.device
@@ -311,9 +320,9 @@ def parallax_attn_decode_paged(q, k_pages, v_pages, block_table, P, seqlens=None
     if seqlens is not None:
         _need(seqlens, "seqlens", torch.int32, (B,), dev)
     oc, odt = _out_code(out_dtype)
-    desc = make_desc(B, 1, Lmax, Hq, Hkv, d, True, window, scale, dt, False, -1, oc)
-    out = torch.empty((B, Hq, d), dtype=odt, device=dev)
-    ratio = torch.empty((B, Hq), dtype=torch.float32, device=dev) if cor else None
+    desc = make_desc(B, T, Lmax, Hq, Hkv, d, True, window, scale, dt, False, -1, oc)
+    out = torch.empty((*lead, Hq, d), dtype=odt, device=dev)
+    ratio = torch.empty((*lead, Hq), dtype=torch.float32, device=dev) if cor else None
     lib = get_lib()
     nws = lib.parallax_attn_decode_paged_workspace(ctypes.byref(desc))
     ws = _workspace(nws, dev)

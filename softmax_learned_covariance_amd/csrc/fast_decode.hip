@@ -16,6 +16,9 @@
 // The cache is either one contiguous [B][L][Hkv][d] array per tensor or a pool of
 // pages [num_pages][page_size][Hkv][d] with a per-sequence block table (the PAGED
 // instantiations): key j of sequence b lives in page block_table[b][j / page_size].
+// Several new tokens per sequence (T > 1, the last T entries of the sequence, token t seeing keys
+// [0, L_b - T + 1 + t)) share a workgroup as extra rows: the template's row count is
+// (query heads per kv head) x (tokens in the chunk) <= 4, and longer runs of tokens go in chunks.
 #include <math.h>
 
 #include "fast_common.h"
@@ -42,14 +45,31 @@ struct DecParams {
   float *so, *su, *salpha, *slse;  // combined: o, u [B][Hq][128], alpha, lse [B][Hq]
   float* pc;                     // pass 2 partials [B][Hq][ns][128]
   int B, L, Hq, Hkv, G, window, ns, chunk;
+  int T, t0;                     // new tokens per sequence; first token of this launch's chunk
+  int Tc;                        // tokens in the chunk
   float scale;
 };
 
-__device__ __forceinline__ void seq_range(const DecParams& p, int b, int& lo, int& hi) {
+// Keys [lo, hi) that new token t of sequence b sees.
+__device__ __forceinline__ void row_range(const DecParams& p, int b, int t, int& lo, int& hi) {
   int Lb = p.L;
   if (p.seqlens) Lb = min(max(p.seqlens[b], 0), p.L);
-  hi = Lb;
-  lo = p.window > 0 ? max(0, Lb - p.window) : 0;
+  hi = max(0, Lb - (p.T - 1 - t));
+  lo = p.window > 0 ? max(0, hi - p.window) : 0;
+}
+
+// Keys any token of the chunk sees.
+__device__ __forceinline__ void seq_range(const DecParams& p, int b, int& lo, int& hi) {
+  int l2, h2;
+  row_range(p, b, p.t0, lo, h2);
+  row_range(p, b, p.t0 + p.Tc - 1, l2, hi);
+}
+
+// Index (sequence, token, query head) of row r of a workgroup of kv head g: the rows are the G query
+// heads of the group for each token of the chunk.
+__device__ __forceinline__ int64_t row_bh(const DecParams& p, int b, int g, int r) {
+  const int t = p.t0 + r / p.G;
+  return (static_cast<int64_t>(b) * p.T + t) * p.Hq + g * p.G + r % p.G;
 }
 
 struct __align__(16) DecTiles {
@@ -169,7 +189,15 @@ __global__ __launch_bounds__(256) void k_dec_pass1(DecParams p) {
   const float c2 = p.scale * kLog2e;
   for (int e = tid; e < G * kD; e += 256) {
     const int h = e / kD, d = e % kD;
-    T.q[h][d] = bf16_to_f32(p.q[(static_cast<int64_t>(b) * p.Hq + g * G + h) * kD + d]) * c2;  // scores in log2 units
+    T.q[h][d] = bf16_to_f32(p.q[row_bh(p, b, g, h) * kD + d]) * c2;  // scores in log2 units
+  }
+  // keys of this split that row (tid >> 6) sees (the softmax of row h is done by wave h)
+  int rlo = k0, rhi = k1;
+  if ((tid >> 6) < G) {
+    int a, c;
+    row_range(p, b, p.t0 + (tid >> 6) / p.G, a, c);
+    rlo = max(k0, a);
+    rhi = min(k1, c);
   }
   // accumulator ownership: thread t -> dims 2*(t%64), +1 ; keys j = part (mod 4)
   const int dp = tid & 63, part = tid >> 6;
@@ -191,7 +219,7 @@ __global__ __launch_bounds__(256) void k_dec_pass1(DecParams p) {
     lds_barrier();
     const int w = tid >> 6, lane = tid & 63;
     if (w < G) {  // wave h: online softmax of head h over this tile
-      const float sv = key0 + lane < k1 ? T.s[w][lane] : -INFINITY;
+      const float sv = key0 + lane >= rlo && key0 + lane < rhi ? T.s[w][lane] : -INFINITY;
       float tm = sv;
 #pragma unroll
       for (int o2 = 32; o2 > 0; o2 >>= 1) tm = fmaxf(tm, __shfl_xor(tm, o2, 64));
@@ -246,13 +274,13 @@ __global__ __launch_bounds__(256) void k_dec_pass1(DecParams p) {
   for (int e = tid; e < G * 2 * kD; e += 256) {
     const int h = e / (2 * kD), r = e % (2 * kD);
     const float s = T.red[0][h][r] + T.red[1][h][r] + T.red[2][h][r] + T.red[3][h][r];
-    const int64_t base = ((static_cast<int64_t>(b) * p.Hq + g * G + h) * p.ns + sp) * kD;
+    const int64_t base = (row_bh(p, b, g, h) * p.ns + sp) * kD;
     if (r < kD) p.po[base + r] = s;
     else p.pk[base + r - kD] = s;
   }
   const int w = tid >> 6, lane = tid & 63;
   if (w < G && lane == 0) {
-    const int64_t si = (static_cast<int64_t>(b) * p.Hq + g * G + w) * p.ns + sp;
+    const int64_t si = row_bh(p, b, g, w) * p.ns + sp;
     p.pm[si] = m;
     p.pl[si] = l;
   }
@@ -304,6 +332,7 @@ template <int G, bool PAGED>
 __global__ __launch_bounds__(256) void k_dec_pass2(DecParams p) {
   __shared__ DecTiles T;
   __shared__ float st[kMaxG][2];  // lse (log2 units), alpha
+  __shared__ int rng[kMaxG][2];   // keys of this split each row sees
   const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   int lo, hi;
   seq_range(p, b, lo, hi);
@@ -311,14 +340,18 @@ __global__ __launch_bounds__(256) void k_dec_pass2(DecParams p) {
   const float c2 = p.scale * kLog2e;
   for (int e = tid; e < G * kD; e += 256) {
     const int h = e / kD, d = e % kD;
-    const int64_t bh = static_cast<int64_t>(b) * p.Hq + g * G + h;
+    const int64_t bh = row_bh(p, b, g, h);
     T.q[h][d] = bf16_to_f32(p.q[bh * kD + d]) * c2;
     T.u[h][d] = p.su[bh * kD + d];
   }
   if (tid < G) {
-    const int64_t bh = static_cast<int64_t>(b) * p.Hq + g * G + tid;
+    const int64_t bh = row_bh(p, b, g, tid);
     st[tid][0] = p.slse[bh];
     st[tid][1] = p.salpha[bh];
+    int a, c;
+    row_range(p, b, p.t0 + tid / p.G, a, c);
+    rng[tid][0] = max(k0, a);
+    rng[tid][1] = min(k1, c);
   }
   const int dp = tid & 63, part = tid >> 6;
   float cv[G][2], ws[G];
@@ -341,7 +374,8 @@ __global__ __launch_bounds__(256) void k_dec_pass2(DecParams p) {
     for (int e = tid; e < G * kTile; e += 256) {
       const int h = e / kTile, j = e % kTile;
       const float lse = st[h][0];
-      const float pw = (key0 + j < k1 && lse > -INFINITY) ? exp2f(T.s[h][j] - lse) : 0.f;
+      const int key = key0 + j;
+      const float pw = (key >= rng[h][0] && key < rng[h][1] && lse > -INFINITY) ? exp2f(T.s[h][j] - lse) : 0.f;
       T.w[h][j] = pw * (T.w[h][j] - st[h][1]);
     }
     lds_barrier();
@@ -371,7 +405,7 @@ __global__ __launch_bounds__(256) void k_dec_pass2(DecParams p) {
   __syncthreads();
   for (int e = tid; e < G * kD; e += 256) {
     const int h = e / kD, d = e % kD;
-    const int64_t bh = static_cast<int64_t>(b) * p.Hq + g * G + h;
+    const int64_t bh = row_bh(p, b, g, h);
     const float s = T.red[0][h][d] + T.red[1][h][d] + T.red[2][h][d] + T.red[3][h][d];
     const float wsum = T.red[0][h][kD] + T.red[1][h][kD] + T.red[2][h][kD] + T.red[3][h][kD];
     p.pc[(bh * p.ns + sp) * kD + d] = s - wsum * p.so[bh * kD + d];
@@ -424,7 +458,7 @@ DecWs dec_layout(const Geom& g, void* ws) {
   w.chunk = (ntiles + ns - 1) / ns * kTile;
   char* base = static_cast<char*>(ws);
   size_t off = 0;
-  const size_t bh = static_cast<size_t>(g.B) * g.Hq;
+  const size_t bh = static_cast<size_t>(g.B) * g.Tq * g.Hq;   // one row per (sequence, new token, query head)
   w.pm = reinterpret_cast<float*>(base + ws_take(off, bh * ns * 4));
   w.pl = reinterpret_cast<float*>(base + ws_take(off, bh * ns * 4));
   w.po = reinterpret_cast<float*>(base + ws_take(off, bh * ns * kD * 4));
@@ -449,23 +483,38 @@ size_t fast_decode_workspace(const Geom& g) { return dec_layout(g, nullptr).byte
 
 namespace {
 
-template <int G, bool PAGED>
-void launch_passes(const DecParams& p, const dim3& grid, int Hq, int B, hipStream_t stream) {
-  mark_begin(PLX_KERNEL_DECODE_PASS1, stream);
-  hipLaunchKernelGGL((k_dec_pass1<G, PAGED>), grid, dim3(256), 0, stream, p);
-  mark_end(PLX_KERNEL_DECODE_PASS1, stream);
-  hipLaunchKernelGGL(k_dec_combine1, dim3(Hq, B), dim3(128), 0, stream, p);
-  mark_begin(PLX_KERNEL_DECODE_PASS2, stream);
-  hipLaunchKernelGGL((k_dec_pass2<G, PAGED>), grid, dim3(256), 0, stream, p);
-  mark_end(PLX_KERNEL_DECODE_PASS2, stream);
-  hipLaunchKernelGGL(k_dec_finish, dim3(Hq, B), dim3(128), 0, stream, p);
+// One pass kernel over every chunk of new tokens; rows per workgroup = G x (tokens in the chunk).
+template <bool PASS2, bool PAGED>
+void launch_pass(DecParams p, const dim3& grid, hipStream_t stream) {
+  const int per = 4 / p.G;   // tokens per chunk at most (G is 1, 2 or 4)
+  for (int t0 = 0; t0 < p.T; t0 += p.Tc) {
+    int tc = per;
+    while (tc > p.T - t0) tc >>= 1;   // rows = G x tc stays 1, 2 or 4
+    p.t0 = t0;
+    p.Tc = tc;
+    const int rows = p.G * tc;
+    if (!PASS2) {
+      if (rows == 1) hipLaunchKernelGGL((k_dec_pass1<1, PAGED>), grid, dim3(256), 0, stream, p);
+      else if (rows == 2) hipLaunchKernelGGL((k_dec_pass1<2, PAGED>), grid, dim3(256), 0, stream, p);
+      else hipLaunchKernelGGL((k_dec_pass1<4, PAGED>), grid, dim3(256), 0, stream, p);
+    } else {
+      if (rows == 1) hipLaunchKernelGGL((k_dec_pass2<1, PAGED>), grid, dim3(256), 0, stream, p);
+      else if (rows == 2) hipLaunchKernelGGL((k_dec_pass2<2, PAGED>), grid, dim3(256), 0, stream, p);
+      else hipLaunchKernelGGL((k_dec_pass2<4, PAGED>), grid, dim3(256), 0, stream, p);
+    }
+  }
 }
 
 template <bool PAGED>
-void launch_all(const DecParams& p, const dim3& grid, int Hq, int B, hipStream_t stream) {
-  if (p.G == 1) launch_passes<1, PAGED>(p, grid, Hq, B, stream);
-  else if (p.G == 2) launch_passes<2, PAGED>(p, grid, Hq, B, stream);
-  else launch_passes<4, PAGED>(p, grid, Hq, B, stream);
+void launch_all(const DecParams& p, const dim3& grid, int Hq, int BT, hipStream_t stream) {
+  mark_begin(PLX_KERNEL_DECODE_PASS1, stream);
+  launch_pass<false, PAGED>(p, grid, stream);
+  mark_end(PLX_KERNEL_DECODE_PASS1, stream);
+  hipLaunchKernelGGL(k_dec_combine1, dim3(Hq, BT), dim3(128), 0, stream, p);
+  mark_begin(PLX_KERNEL_DECODE_PASS2, stream);
+  launch_pass<true, PAGED>(p, grid, stream);
+  mark_end(PLX_KERNEL_DECODE_PASS2, stream);
+  hipLaunchKernelGGL(k_dec_finish, dim3(Hq, BT), dim3(128), 0, stream, p);
 }
 
 }  // namespace
@@ -498,6 +547,9 @@ hipError_t launch_fast_decode(const Geom& g, const void* q, const void* kc, cons
   p.Hkv = g.Hkv;
   p.G = g.Hq / g.Hkv;
   p.window = g.window;
+  p.T = g.Tq;
+  p.t0 = 0;
+  p.Tc = g.Tq;
   p.ns = w.ns;
   p.chunk = w.chunk;
   p.scale = g.scale;
@@ -509,9 +561,9 @@ hipError_t launch_fast_decode(const Geom& g, const void* q, const void* kc, cons
     int shift = 0;
     while ((1 << shift) < paged->page_size) ++shift;
     p.page_shift = shift;
-    launch_all<true>(p, grid, g.Hq, g.B, stream);
+    launch_all<true>(p, grid, g.Hq, g.B * g.Tq, stream);
   } else {
-    launch_all<false>(p, grid, g.Hq, g.B, stream);
+    launch_all<false>(p, grid, g.Hq, g.B * g.Tq, stream);
   }
   return hipGetLastError();
 }

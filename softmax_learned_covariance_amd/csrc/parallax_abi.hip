@@ -325,7 +325,8 @@ plx_status parallax_attn_bwd(const plx_attn_desc* desc, const void* q, const voi
 size_t parallax_attn_decode_workspace(const plx_attn_desc* desc) {
   plx::Geom g;
   if (check_desc(desc, "parallax_attn_decode_workspace", &g) != PLX_OK) return 0;
-  if (g.Tq != 1 || g.p_per_query) return 0;
+  if (g.Tq < 1 || g.p_per_query) return 0;
+  if (g.Tq > 1 && !plx::fast_decode_supported(g)) return 0;
   g.causal = 1;
   return dec_ws(g);
 }
@@ -338,8 +339,10 @@ plx_status parallax_attn_decode(const plx_attn_desc* desc, const void* q, const 
   plx::Geom g;
   plx_status st = check_desc(desc, what, &g);
   if (st != PLX_OK) return st;
-  if (g.Tq != 1) return fail(PLX_ERR_INVALID, "%s: seqlen_q must be 1 (got %d)", what, g.Tq);
+  if (g.Tq < 1) return fail(PLX_ERR_INVALID, "%s: seqlen_q must be >= 1 (got %d)", what, g.Tq);
   if (g.p_per_query) return fail(PLX_ERR_UNSUPPORTED, "%s: per-query projectors are not supported", what);
+  if (g.Tq > 1 && !plx::fast_decode_supported(g))
+    return fail(PLX_ERR_UNSUPPORTED, "%s: several new tokens per sequence need the bf16 fast path", what);
   g.causal = 1;  // the new token is the last entry of its sequence: it sees all of it
   if (g.B == 0) {
     st = check_ws(dec_ws(g), workspace, workspace_bytes, what);
@@ -365,7 +368,7 @@ plx_status parallax_attn_decode(const plx_attn_desc* desc, const void* q, const 
 size_t parallax_attn_decode_paged_workspace(const plx_attn_desc* desc) {
   plx::Geom g;
   if (check_desc(desc, "parallax_attn_decode_paged_workspace", &g) != PLX_OK) return 0;
-  if (g.Tq != 1 || g.p_per_query || !plx::fast_decode_supported(g)) return 0;
+  if (g.Tq < 1 || g.p_per_query || !plx::fast_decode_supported(g)) return 0;
   g.causal = 1;
   return plx::fast_decode_workspace(g);
 }
@@ -379,7 +382,7 @@ plx_status parallax_attn_decode_paged(const plx_attn_desc* desc, const void* q, 
   plx::Geom g;
   plx_status st = check_desc(desc, what, &g);
   if (st != PLX_OK) return st;
-  if (g.Tq != 1) return fail(PLX_ERR_INVALID, "%s: seqlen_q must be 1 (got %d)", what, g.Tq);
+  if (g.Tq < 1) return fail(PLX_ERR_INVALID, "%s: seqlen_q must be >= 1 (got %d)", what, g.Tq);
   if (page_size < 1 || page_size > 65536 || (page_size & (page_size - 1)) != 0)
     return fail(PLX_ERR_INVALID, "%s: page_size=%d is not a power of two in [1, 65536]", what, page_size);
   if (num_pages < 1) return fail(PLX_ERR_INVALID, "%s: num_pages=%d < 1", what, num_pages);

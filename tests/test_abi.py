@@ -124,7 +124,8 @@ def test_backward_validation(plx):
 
 def test_decode_validation(plx):
     E = plx
-    assert _dec(plx, _desc(plx, Tq=2)) == E.PLX_ERR_INVALID
+    assert _dec(plx, _desc(plx, Tq=0)) == E.PLX_ERR_INVALID
+    assert _dec(plx, _desc(plx, Tq=2)) == E.PLX_ERR_UNSUPPORTED     # several new tokens: bf16 fast path only
     assert _dec(plx, _desc(plx, Tq=1, p_per_query=True)) == E.PLX_ERR_UNSUPPORTED
     assert _dec(plx, _desc(plx, Tq=1), q=None) == E.PLX_ERR_INVALID
     assert _dec(plx, _desc(plx, Tq=1, B=0)) == E.PLX_OK
@@ -189,7 +190,7 @@ def test_paged_decode_validation(plx):
                                               FAKE, FAKE, None, ws, nws, None)
 
     d = _desc(plx, **bf)
-    assert call(_desc(plx, dtype=plx.PLX_BF16, d=128, Tq=2)) == E.PLX_ERR_INVALID
+    assert call(_desc(plx, dtype=plx.PLX_BF16, d=128, Tq=0)) == E.PLX_ERR_INVALID
     for page in (0, 3, 48, 1 << 17):
         assert call(d, page=page) == E.PLX_ERR_INVALID, page
     assert b"page_size" in lib.parallax_last_error()

@@ -477,3 +477,44 @@ def test_decode_paged_clamps_bad_entries(plx):
     torch.cuda.synchronize()
     assert torch.isfinite(bad).all()
     assert torch.equal(bad[0], good[0]) and torch.equal(bad[2], good[2])
+
+
+# --------------------------------------------------------------------------------------
+# several new tokens per sequence against the cache
+# --------------------------------------------------------------------------------------
+
+def _multi_token_ref(q, kc, vc, P, seqlens, window):
+    """The last T rows of the forward over each sequence's prefix (bottom-right aligned causal)."""
+    B, T = q.shape[0], q.shape[1]
+    ref = np.zeros(q.shape)
+    for b in range(B):
+        L = int(seqlens[b])
+        if L > 0:
+            ref[b] = oracle.fwd(q[b:b + 1], kc[b:b + 1, :L], vc[b:b + 1, :L], P, causal=True, window=window)[0][0]
+    return ref
+
+
+@pytest.mark.parametrize("T,Hkv,window", [(2, 8, 0), (3, 8, 100), (5, 8, 0), (5, 16, 0), (3, 16, 64), (3, 4, 0)])
+def test_decode_multi_token(plx, T, Hkv, window):
+    """T new tokens per sequence (chunks of 4 / G tokens per workgroup), ragged lengths including one
+    shorter than T and an empty sequence, with and without a window; the paged cache agrees bit for bit."""
+    _announce(f"multi-token decode T={T} Hkv={Hkv} window={window}")
+    w = W.scaled(W.WORKLOADS["decode"], batch=4, seqlen_k=600, heads_kv=Hkv)
+    q1, kc, vc, P = W.make_inputs(w, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(40 + T)
+    q = torch.randn((4, T, w.heads_q, w.head_dim), generator=g, device="cuda").to(torch.bfloat16)
+    seqlens = torch.tensor([600, 3, 0, 257], dtype=torch.int32, device="cuda")
+    out = plx.parallax_attn_decode(q, kc, vc, P, seqlens=seqlens, window=window)
+    kp, vp, table = _to_pages(kc, vc, 64, seed=T)
+    outp = plx.parallax_attn_decode_paged(q, kp, vp, table, P, seqlens=seqlens, seqlen_k=600, window=window)
+    torch.cuda.synchronize()
+    assert out.shape == q.shape
+    assert torch.equal(out, outp)
+    ref = _multi_token_ref(host(q), host(kc), host(vc), host(P), host(seqlens).astype(int), window)
+    assert np.all(host(out)[2] == 0) and np.all(host(out)[1, :max(T - 3, 0)] == 0)
+    assert rel_err(host(out), ref) <= BF16_TOL
+    # the last token alone is the one-token decode
+    last = plx.parallax_attn_decode(q[:, -1].contiguous(), kc, vc, P, seqlens=seqlens, window=window)
+    torch.cuda.synchronize()
+    assert rel_err(host(out[:, -1]), host(last)) <= 1e-5
