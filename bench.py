@@ -377,6 +377,23 @@ def main():
         kms = dt * 1e3
         log(f"decode {kms:.3f} ms/kernel, {gbs:.0f} GB/s")
 
+        # four new tokens per sequence (speculative decoding) against the same cache
+        gq = torch.Generator(device=dev)
+        gq.manual_seed(6)
+        q4 = torch.randn((wd.batch, 4, wd.heads_q, wd.head_dim), generator=gq, device=dev).to(qd.dtype)
+        for _ in range(2):
+            plx.parallax_attn_decode(q4, kc, vc, Pd)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(Kd):
+            plx.parallax_attn_decode(q4, kc, vc, Pd)
+        torch.cuda.synchronize()
+        dt4 = (time.perf_counter() - t0) / Kd
+        result["decode"]["four_tokens"] = {"tokens_per_sequence": 4, "ms_per_call": round(dt4 * 1e3, 4),
+                                           "tokens_per_s": round(4 * wd.batch / dt4, 1)}
+        log(f"4-token decode {dt4 * 1e3:.3f} ms/call")
+        del q4
+
         # the same keys in a shuffled pool of 256-key pages with a block table
         page = 256
         npb = wd.seqlen_k // page
