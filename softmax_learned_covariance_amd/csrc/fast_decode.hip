@@ -18,7 +18,7 @@
 // instantiations): key j of sequence b lives in page block_table[b][j / page_size].
 // Several new tokens per sequence (T > 1, the last T entries of the sequence, token t seeing keys
 // [0, L_b - T + 1 + t)) share a workgroup as extra rows: the template's row count is
-// (query heads per kv head) x (tokens in the chunk) <= 4, and longer runs of tokens go in chunks.
+// (query heads per kv head) x (tokens in the chunk) <= 8, and longer runs of tokens go in chunks.
 #include <math.h>
 
 #include "fast_common.h"
@@ -30,7 +30,7 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kTile = 64;          // keys per LDS tile
 constexpr int kRowH = kD + 8;      // padded LDS row (bf16 elements)
-constexpr int kMaxG = 4;
+constexpr int kMaxG = 8;          // rows (query head, new token) per workgroup
 
 struct DecParams {
   const u16 *q, *kc, *vc, *P;
@@ -156,7 +156,28 @@ template <int G>
 __device__ __forceinline__ void tile_dots(const DecTiles& T, int buf, const float (*vecs)[kD], float (*dots)[kTile],
                                           int tid) {
   constexpr int ndots = G * kTile;
-  constexpr int tpd = 256 / ndots;           // threads per dot: 4, 2 or 1
+  if constexpr (ndots > 256) {               // 8 rows: two whole dots per thread
+#pragma unroll
+    for (int rep = 0; rep < ndots / 256; ++rep) {
+      const int dot = tid + 256 * rep;
+      const int h = dot / kTile, j = dot % kTile;
+      const u16* kr = &T.k[buf][j * kRowH];
+      float acc = 0.f;
+#pragma unroll 4
+      for (int c = 0; c < kD; c += 8) {
+        const uint4 w = *reinterpret_cast<const uint4*>(kr + c);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc = fmaf(__uint_as_float(ws[e] << 16), vecs[h][c + 2 * e], acc);
+          acc = fmaf(__uint_as_float(ws[e] & 0xffff0000u), vecs[h][c + 2 * e + 1], acc);
+        }
+      }
+      dots[h][j] = acc;
+    }
+    return;
+  }
+  constexpr int tpd = ndots > 256 ? 1 : 256 / ndots;   // threads per dot: 4, 2 or 1
   constexpr int len = kD / tpd;
   const int dot = tid / tpd, part = tid % tpd;
   const int h = dot / kTile, j = dot % kTile;
@@ -191,18 +212,30 @@ __global__ __launch_bounds__(256) void k_dec_pass1(DecParams p) {
     const int h = e / kD, d = e % kD;
     T.q[h][d] = bf16_to_f32(p.q[row_bh(p, b, g, h) * kD + d]) * c2;  // scores in log2 units
   }
-  // keys of this split that row (tid >> 6) sees (the softmax of row h is done by wave h)
-  int rlo = k0, rhi = k1;
-  if ((tid >> 6) < G) {
-    int a, c;
-    row_range(p, b, p.t0 + (tid >> 6) / p.G, a, c);
-    rlo = max(k0, a);
-    rhi = min(k1, c);
+  // keys of this split that each of the wave's rows sees (the softmax of row h is done by wave h % 4)
+  constexpr int RW = G > 4 ? 2 : 1;   // rows per wave
+  int rlo[RW], rhi[RW];
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    const int r = (tid >> 6) + 4 * i;
+    rlo[i] = k0;
+    rhi[i] = k1;
+    if (r < G) {
+      int a, c;
+      row_range(p, b, p.t0 + r / p.G, a, c);
+      rlo[i] = max(k0, a);
+      rhi[i] = min(k1, c);
+    }
   }
   // accumulator ownership: thread t -> dims 2*(t%64), +1 ; keys j = part (mod 4)
   const int dp = tid & 63, part = tid >> 6;
   float o[G][2], kb[G][2];
-  float m = -INFINITY, l = 0.f;  // per head, kept by the softmax wave (wave h) and broadcast through LDS
+  float m[RW], l[RW];  // per row, kept by the softmax wave and broadcast through LDS
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    m[i] = -INFINITY;
+    l[i] = 0.f;
+  }
 #pragma unroll
   for (int h = 0; h < G; ++h) o[h][0] = o[h][1] = kb[h][0] = kb[h][1] = 0.f;
   const int nt = k1 > k0 ? (k1 - k0 + kTile - 1) / kTile : 0;
@@ -218,21 +251,25 @@ __global__ __launch_bounds__(256) void k_dec_pass1(DecParams p) {
     tile_dots<G>(T, buf, T.q, T.s, tid);
     lds_barrier();
     const int w = tid >> 6, lane = tid & 63;
-    if (w < G) {  // wave h: online softmax of head h over this tile
-      const float sv = key0 + lane >= rlo && key0 + lane < rhi ? T.s[w][lane] : -INFINITY;
-      float tm = sv;
 #pragma unroll
-      for (int o2 = 32; o2 > 0; o2 >>= 1) tm = fmaxf(tm, __shfl_xor(tm, o2, 64));
-      const float mn = fmaxf(m, tm);
-      const float corr = m == -INFINITY ? 0.f : exp2f(m - mn);
-      const float pv = sv == -INFINITY ? 0.f : exp2f(sv - mn);
-      float ts = pv;
+    for (int i = 0; i < RW; ++i) {
+      const int r = w + 4 * i;
+      if (r < G) {  // online softmax of row r over this tile
+        const float sv = key0 + lane >= rlo[i] && key0 + lane < rhi[i] ? T.s[r][lane] : -INFINITY;
+        float tm = sv;
 #pragma unroll
-      for (int o2 = 32; o2 > 0; o2 >>= 1) ts += __shfl_xor(ts, o2, 64);
-      l = l * corr + ts;
-      m = mn;
-      T.w[w][lane] = pv;
-      if (lane == 0) T.corr[w] = corr;
+        for (int o2 = 32; o2 > 0; o2 >>= 1) tm = fmaxf(tm, __shfl_xor(tm, o2, 64));
+        const float mn = fmaxf(m[i], tm);
+        const float corr = m[i] == -INFINITY ? 0.f : exp2f(m[i] - mn);
+        const float pv = sv == -INFINITY ? 0.f : exp2f(sv - mn);
+        float ts = pv;
+#pragma unroll
+        for (int o2 = 32; o2 > 0; o2 >>= 1) ts += __shfl_xor(ts, o2, 64);
+        l[i] = l[i] * corr + ts;
+        m[i] = mn;
+        T.w[r][lane] = pv;
+        if (lane == 0) T.corr[r] = corr;
+      }
     }
     lds_barrier();
 #pragma unroll
@@ -279,10 +316,14 @@ __global__ __launch_bounds__(256) void k_dec_pass1(DecParams p) {
     else p.pk[base + r - kD] = s;
   }
   const int w = tid >> 6, lane = tid & 63;
-  if (w < G && lane == 0) {
-    const int64_t si = row_bh(p, b, g, w) * p.ns + sp;
-    p.pm[si] = m;
-    p.pl[si] = l;
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    const int r = w + 4 * i;
+    if (r < G && lane == 0) {
+      const int64_t si = row_bh(p, b, g, r) * p.ns + sp;
+      p.pm[si] = m[i];
+      p.pl[si] = l[i];
+    }
   }
 }
 
@@ -294,8 +335,10 @@ __global__ __launch_bounds__(128) void k_dec_combine1(DecParams p) {
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int64_t bh = static_cast<int64_t>(b) * p.Hq + h;
   float M = -INFINITY;
+#pragma unroll 8
   for (int s = 0; s < p.ns; ++s) M = fmaxf(M, p.pm[bh * p.ns + s]);
   float L = 0.f, o = 0.f, kb = 0.f;
+#pragma unroll 8
   for (int s = 0; s < p.ns; ++s) {
     const float ms = p.pm[bh * p.ns + s];
     if (ms == -INFINITY) continue;
@@ -417,6 +460,7 @@ __global__ __launch_bounds__(128) void k_dec_finish(DecParams p) {
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int64_t bh = static_cast<int64_t>(b) * p.Hq + h;
   float c = 0.f;
+#pragma unroll 8
   for (int s = 0; s < p.ns; ++s) c += p.pc[(bh * p.ns + s) * kD + d];
   const float r = p.so[bh * kD + d] + c;
   if (p.out_bf16) static_cast<u16*>(p.out)[bh * kD + d] = static_cast<u16>(f32_to_bf16(r));
@@ -486,21 +530,23 @@ namespace {
 // One pass kernel over every chunk of new tokens; rows per workgroup = G x (tokens in the chunk).
 template <bool PASS2, bool PAGED>
 void launch_pass(DecParams p, const dim3& grid, hipStream_t stream) {
-  const int per = 4 / p.G;   // tokens per chunk at most (G is 1, 2 or 4)
+  const int per = kMaxG / p.G;   // tokens per chunk at most (G is 1, 2 or 4)
   for (int t0 = 0; t0 < p.T; t0 += p.Tc) {
     int tc = per;
-    while (tc > p.T - t0) tc >>= 1;   // rows = G x tc stays 1, 2 or 4
+    while (tc > p.T - t0) tc >>= 1;   // rows = G x tc stays 1, 2, 4 or 8
     p.t0 = t0;
     p.Tc = tc;
     const int rows = p.G * tc;
     if (!PASS2) {
       if (rows == 1) hipLaunchKernelGGL((k_dec_pass1<1, PAGED>), grid, dim3(256), 0, stream, p);
       else if (rows == 2) hipLaunchKernelGGL((k_dec_pass1<2, PAGED>), grid, dim3(256), 0, stream, p);
-      else hipLaunchKernelGGL((k_dec_pass1<4, PAGED>), grid, dim3(256), 0, stream, p);
+      else if (rows == 4) hipLaunchKernelGGL((k_dec_pass1<4, PAGED>), grid, dim3(256), 0, stream, p);
+      else hipLaunchKernelGGL((k_dec_pass1<8, PAGED>), grid, dim3(256), 0, stream, p);
     } else {
       if (rows == 1) hipLaunchKernelGGL((k_dec_pass2<1, PAGED>), grid, dim3(256), 0, stream, p);
       else if (rows == 2) hipLaunchKernelGGL((k_dec_pass2<2, PAGED>), grid, dim3(256), 0, stream, p);
-      else hipLaunchKernelGGL((k_dec_pass2<4, PAGED>), grid, dim3(256), 0, stream, p);
+      else if (rows == 4) hipLaunchKernelGGL((k_dec_pass2<4, PAGED>), grid, dim3(256), 0, stream, p);
+      else hipLaunchKernelGGL((k_dec_pass2<8, PAGED>), grid, dim3(256), 0, stream, p);
     }
   }
 }

@@ -494,9 +494,10 @@ def _multi_token_ref(q, kc, vc, P, seqlens, window):
     return ref
 
 
-@pytest.mark.parametrize("T,Hkv,window", [(2, 8, 0), (3, 8, 100), (5, 8, 0), (5, 16, 0), (3, 16, 64), (3, 4, 0)])
+@pytest.mark.parametrize("T,Hkv,window", [(2, 8, 0), (3, 8, 100), (4, 8, 0), (5, 8, 0), (5, 16, 0), (8, 16, 50),
+                                          (3, 16, 64), (3, 4, 0)])
 def test_decode_multi_token(plx, T, Hkv, window):
-    """T new tokens per sequence (chunks of 4 / G tokens per workgroup), ragged lengths including one
+    """T new tokens per sequence (chunks of up to 8 / G tokens per workgroup), ragged lengths including one
     shorter than T and an empty sequence, with and without a window; the paged cache agrees bit for bit."""
     _announce(f"multi-token decode T={T} Hkv={Hkv} window={window}")
     w = W.scaled(W.WORKLOADS["decode"], batch=4, seqlen_k=600, heads_kv=Hkv)
