@@ -495,7 +495,10 @@ DecWs dec_layout(const Geom& g, void* ws) {
   DecWs w{};
   const int slices = g.B * g.Hkv;
   const int ntiles = (g.Tk + kTile - 1) / kTile;
-  int ns = slices > 0 ? (2048 + slices - 1) / slices : 1;
+  // about 2048 workgroups per pass; fewer (1024) for a handful of (sequence, kv head) slices, where the
+  // per-split combine costs more than the extra parallelism gains (measured at 1 and 8 sequences)
+  const int target = slices < 32 ? 1024 : 2048;
+  int ns = slices > 0 ? (target + slices - 1) / slices : 1;
   ns = ns < 1 ? 1 : (ns > ntiles ? ntiles : ns);
   if (ns < 1) ns = 1;
   w.ns = ns;
