@@ -1,4 +1,4 @@
-// Parallax decode for gfx950: one new query per sequence against a bf16 key/value cache.
+// Parallax decode for gfx950: new queries (one or a few per sequence) against a bf16 key/value cache.
 //
 // The decode path of the pages' hardware section (gist.science technical summary
 // of "Parallax: Parameterized Local Linear Attention for Language Modeling",
