@@ -152,7 +152,7 @@ size_t parallax_attn_fwd_probe_workspace(const plx_attn_desc* desc);
  *   rk     [B][Hq][Tq]    fp32 rho_i . kbar_i (nullable)
  *   cor    [B][Hq][Tq]    fp32 correction-to-output ratio as in the forward (nullable)
  * The probe-form backward needs lse, o_sa and rk from the same call.
- * Supported: bf16, head_dim 128, heads_q / heads_kv in {1, 2, 4, 8}, p_per_query 0; any other
+ * Supported: bf16, head_dim 128 or 64, heads_q / heads_kv in {1, 2, 4, 8}, p_per_query 0; any other
  * valid desc returns PLX_ERR_UNSUPPORTED.  Masks, empty rows and split_rows as in the forward.
  */
 plx_status parallax_attn_fwd_probe(const plx_attn_desc* desc,

@@ -265,6 +265,6 @@ hipError_t launch_stage_rows(const void* src, bool f32, const uint32_t* maxbits,
 hipError_t launch_staging(const Staging& s, const void* q, int64_t q_elems, const void* k,
                           const void* v, const void* P, int B, int Tk, int Hkv, int Hq,
                           hipStream_t stream, const void* extra = nullptr, int64_t extra_elems = 0,
-                          int extra_slot = 0);
+                          int extra_slot = 0, int D = kD);   // D: head dim of k, v, P (64 is zero-padded to 128)
 
 }  // namespace plx

@@ -51,6 +51,7 @@ struct FwdParams {
   float* cor;       // per row |out - o| / |out|, [B][Hq][Tq] (nullable)
   int out_bf16;        // probe form only: rho . kbar per row, [B][Hq][Tq] (nullable)
   int B, Tq, Tk, Tk_pad, Hq, Hkv, G, causal, window;
+  int D;            // head dim of the caller's rows (128, or 64 zero-padded to 128 in the operands)
   float scale;
   int row_begin, row_end, rows_per_block, n_rb;  // rows [row_begin, row_end)
 };
@@ -95,12 +96,13 @@ __device__ __forceinline__ void load4_bf16(const u16* src, float* dst) {
   dst[3] = __uint_as_float(w.y & 0xffff0000u);
 }
 
-// B operand of a product over d for one query row: d in the permuted-16 order, scaled by s.
-__device__ __forceinline__ void load_q_operand(const u16* qrow, bool ok, int hh, float s, f16x8 (&qB)[8]) {
+// B operand of a product over d for one query row: d in the permuted-16 order, scaled by s.  Rows
+// of D < 128 elements are zero-padded to 128.
+__device__ __forceinline__ void load_q_operand(const u16* qrow, bool ok, int hh, float s, f16x8 (&qB)[8], int D) {
 #pragma unroll
   for (int st = 0; st < 8; ++st) {
     float a[4] = {0.f, 0.f, 0.f, 0.f}, c[4] = {0.f, 0.f, 0.f, 0.f};
-    if (ok) {
+    if (ok && 16 * st < D) {
       load4_bf16(qrow + 16 * st + 4 * hh, a);
       load4_bf16(qrow + 16 * st + 8 + 4 * hh, c);
     }
@@ -144,7 +146,7 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
   const float sP = range_scale(__uint_as_float(p.maxbits[3]));
   const float cS = p.scale * kLog2e / (sQ * sK);
 
-  const int64_t qoff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * kD;
+  const int64_t qoff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * p.D;
   const u16* qrow = p.q + qoff;
 
   // key ranges: block, wave (first / last row), lane (its row)
@@ -163,7 +165,7 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
   const int r_kbeg = p.window > 0 ? max(0, row + off - p.window + 1) : 0;
 
   f16x8 qB[8];
-  load_q_operand(qrow, row_ok, hh, sQ, qB);
+  load_q_operand(qrow, row_ok, hh, sQ, qB, p.D);
 
   // ---------------- pass 1 ----------------
   f32x16 accO[4], accK[4];
@@ -288,6 +290,7 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = 32 * mt + 8 * j + 4 * hh;
+        if (d >= p.D) continue;   // padding dims of a D < 128 head
         const float fo = invL / sV, fk = invL / sK;
         const float4 ov = {accO[mt][4 * j] * fo, accO[mt][4 * j + 1] * fo, accO[mt][4 * j + 2] * fo,
                            accO[mt][4 * j + 3] * fo};
@@ -313,7 +316,7 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float qv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (row_ok) load4_bf16(qrow + 32 * mt + 8 * j + 4 * hh, qv);
+        if (row_ok && 32 * mt + 8 * j + 4 * hh < p.D) load4_bf16(qrow + 32 * mt + 8 * j + 4 * hh, qv);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * j + e;
@@ -380,7 +383,7 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
   const f16x8* uL = xL;
 
   // ---------------- pass 2 ----------------
-  load_q_operand(qrow, row_ok, hh, sQ, qB);
+  load_q_operand(qrow, row_ok, hh, sQ, qB, p.D);
   f32x16 accC[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) accC[mt] = f32x16{};
@@ -467,6 +470,7 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = 32 * mt + 8 * j + 4 * hh;
+        if (d >= p.D) continue;   // padding dims of a D < 128 head
         const float4 ov = *reinterpret_cast<const float4*>(obuf + qoff + d);
         const float o4[4] = {ov.x, ov.y, ov.z, ov.w};
         float r4[4];
@@ -559,7 +563,7 @@ __global__ __launch_bounds__(512) void k_fwd_probe(FwdParams p) {
   const float sR = range_scale(__uint_as_float(p.maxbits[kMaxRho]));
   const float cS = p.scale * kLog2e / (sQ * sK);
 
-  const int64_t qoff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * kD;
+  const int64_t qoff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * p.D;
 
   const int rlast = min(r0 + p.rows_per_block, p.row_end) - 1;
   const int kend = p.causal ? min(p.Tk, rlast + off + 1) : p.Tk;
@@ -576,11 +580,11 @@ __global__ __launch_bounds__(512) void k_fwd_probe(FwdParams p) {
   const int r_kbeg = p.window > 0 ? max(0, row + off - p.window + 1) : 0;
 
   f16x8 qB[8];
-  load_q_operand(p.q + qoff, row_ok, hh, sQ, qB);
+  load_q_operand(p.q + qoff, row_ok, hh, sQ, qB, p.D);
   {
     // the lane's rho operand into the wave's LDS block (read back by the same lane only)
     f16x8 rB[8];
-    load_q_operand(p.rho + qoff, row_ok, hh, sR, rB);
+    load_q_operand(p.rho + qoff, row_ok, hh, sR, rB, p.D);
 #pragma unroll
     for (int s = 0; s < 8; ++s) T.rho[w][s][l] = rB[s];
   }
@@ -711,6 +715,7 @@ __global__ __launch_bounds__(512) void k_fwd_probe(FwdParams p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = 32 * mt + 8 * j + 4 * hh;
+        if (d >= p.D) continue;   // padding dims of a D < 128 head
         float r4[4], o4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -735,7 +740,7 @@ __global__ __launch_bounds__(512) void k_fwd_probe(FwdParams p) {
 
 bool fast_fwd_supported(const Geom& g) {
   const int G = g.Hq / g.Hkv;
-  return g.bf16 && g.d == kD && !g.p_per_query && (G == 1 || G == 2 || G == 4 || G == 8);
+  return g.bf16 && (g.d == kD || g.d == 64) && !g.p_per_query && (G == 1 || G == 2 || G == 4 || G == 8);
 }
 
 size_t fast_fwd_workspace(const Geom& g) {
@@ -750,8 +755,8 @@ hipError_t launch_fast_fwd(const Geom& g, const void* q, const void* k, const vo
   float* o_ws = reinterpret_cast<float*>(static_cast<char*>(ws) + s.bytes);
   int split = split_rows < kMinSplitRows ? kMinSplitRows : split_rows;
   if (split > g.Tq) split = g.Tq;
-  hipError_t e = launch_staging(s, q, static_cast<int64_t>(g.B) * g.Tq * g.Hq * kD, k, v, P, g.B, g.Tk,
-                                g.Hkv, g.Hq, stream);
+  hipError_t e = launch_staging(s, q, static_cast<int64_t>(g.B) * g.Tq * g.Hq * g.d, k, v, P, g.B, g.Tk,
+                                g.Hkv, g.Hq, stream, nullptr, 0, 0, g.d);
   if (e != hipSuccess) return e;
   FwdParams base{};
   {
@@ -777,6 +782,7 @@ hipError_t launch_fast_fwd(const Geom& g, const void* q, const void* k, const vo
     p.G = g.Hq / g.Hkv;
     p.causal = g.causal;
     p.window = g.window;
+    p.D = g.d;
     p.scale = g.scale;
     p.rows_per_block = 32 * kWaves / p.G;
   }
@@ -817,9 +823,10 @@ hipError_t launch_fast_probe(const Geom& g, const void* q, const void* k, const 
   const Staging s = staging_layout(ws, g.B, g.Tk, g.Hkv, g.Hq);
   int split = split_rows < kMinSplitRows ? kMinSplitRows : split_rows;
   if (split > g.Tq) split = g.Tq;
-  const int64_t q_elems = static_cast<int64_t>(g.B) * g.Tq * g.Hq * kD;
+  const int64_t q_elems = static_cast<int64_t>(g.B) * g.Tq * g.Hq * g.d;
   // K/V into their fp16 tile layouts; max |q|, |k|, |v|, |rho| for the operand scales (no projector)
-  hipError_t e = launch_staging(s, q, q_elems, k, v, nullptr, g.B, g.Tk, g.Hkv, g.Hq, stream, rho, q_elems, kMaxRho);
+  hipError_t e = launch_staging(s, q, q_elems, k, v, nullptr, g.B, g.Tk, g.Hkv, g.Hq, stream, rho, q_elems, kMaxRho,
+                                g.d);
   if (e != hipSuccess) return e;
   FwdParams base{};
   {
@@ -844,6 +851,7 @@ hipError_t launch_fast_probe(const Geom& g, const void* q, const void* k, const 
     p.G = g.Hq / g.Hkv;
     p.causal = g.causal;
     p.window = g.window;
+    p.D = g.d;
     p.scale = g.scale;
     p.rows_per_block = 32 * kWaves / p.G;
   }

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void k_absmax(AbsmaxJob job, uint32_t* maxbits
 // One block per (64-key tile, kv head, batch): K16 (and V16) row tiles, K16t (and V16t) column tiles.
 __global__ __launch_bounds__(256) void k_stage_kv(const u16* k, const u16* v, const uint32_t* maxbits,
                                                   _Float16* k16, _Float16* k16t, _Float16* v16t,
-                                                  _Float16* v16, int Tk, int Tk_pad, int Hkv) {
+                                                  _Float16* v16, int Tk, int Tk_pad, int Hkv, int D) {
   constexpr int LD = kD + 2;  // padded LDS row (halves) for conflict-light column reads
   __shared__ _Float16 ks[kKeyTile * LD];
   __shared__ _Float16 vs[kKeyTile * LD];
@@ -91,8 +91,8 @@ __global__ __launch_bounds__(256) void k_stage_kv(const u16* k, const u16* v, co
     const int r = ci >> 4, c = ci & 15;
     const int key = key0 + r;
     uint4 kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
-    if (key < Tk) {
-      const int64_t off = ((static_cast<int64_t>(b) * Tk + key) * Hkv + g) * kD + c * 8;
+    if (key < Tk && c * 8 < D) {   // a head of D < 128 is zero-padded to 128
+      const int64_t off = ((static_cast<int64_t>(b) * Tk + key) * Hkv + g) * D + c * 8;
       kw = *reinterpret_cast<const uint4*>(k + off);
       vw = *reinterpret_cast<const uint4*>(v + off);
     }
@@ -140,13 +140,16 @@ __global__ __launch_bounds__(256) void k_stage_kv(const u16* k, const u16* v, co
 
 // One block per query head: P16t[h][a][b'] = sP * P[h][perm(b')][a]; optionally P16[h][b][a'] = sP * P[h][b][perm(a')].
 __global__ __launch_bounds__(256) void k_stage_p(const u16* P, const uint32_t* maxbits, _Float16* p16t,
-                                                 _Float16* p16) {
+                                                 _Float16* p16, int D) {
   constexpr int LD = kD + 2;
   __shared__ _Float16 ps[kD * LD];
   const int h = blockIdx.x, t = threadIdx.x;
   const float sP = range_scale(__uint_as_float(maxbits[3]));
-  const u16* src = P + static_cast<int64_t>(h) * kD * kD;
-  for (int e = t; e < kD * kD; e += 256) ps[(e / kD) * LD + (e % kD)] = static_cast<_Float16>(bf16_to_f32(src[e]) * sP);
+  const u16* src = P + static_cast<int64_t>(h) * D * D;
+  for (int e = t; e < kD * kD; e += 256) {   // a D x D projector is zero-padded to 128 x 128
+    const int r = e / kD, c = e % kD;
+    ps[r * LD + c] = r < D && c < D ? static_cast<_Float16>(bf16_to_f32(src[r * D + c]) * sP) : static_cast<_Float16>(0.f);
+  }
   __syncthreads();
   for (int ci = t; ci < kD * 16; ci += 256) {
     const int a = ci >> 4, c = ci & 15;
@@ -240,9 +243,9 @@ __global__ __launch_bounds__(256) void k_stage_rows(const void* src, const uint3
 
 hipError_t launch_staging(const Staging& s, const void* q, int64_t q_elems, const void* k,
                           const void* v, const void* P, int B, int Tk, int Hkv, int Hq,
-                          hipStream_t stream, const void* extra, int64_t extra_elems, int extra_slot) {
-  const int64_t nkv = static_cast<int64_t>(B) * Tk * Hkv * kD;
-  const int64_t np = static_cast<int64_t>(Hq) * kD * kD;
+                          hipStream_t stream, const void* extra, int64_t extra_elems, int extra_slot, int D) {
+  const int64_t nkv = static_cast<int64_t>(B) * Tk * Hkv * D;
+  const int64_t np = static_cast<int64_t>(Hq) * D * D;
   hipLaunchKernelGGL(k_zero_max, dim3(1), dim3(64), 0, stream, s.maxbits);
   AbsmaxJob job{};
   absmax_add(job, q, q_elems, kMaxQ, true);
@@ -255,10 +258,10 @@ hipError_t launch_staging(const Staging& s, const void* q, int64_t q_elems, cons
   if (B > 0 && s.Tk_pad > 0)
     hipLaunchKernelGGL(k_stage_kv, dim3(Hkv * (s.Tk_pad / kKeyTile), 1, B), dim3(256), 0, stream,
                        static_cast<const u16*>(k), static_cast<const u16*>(v), s.maxbits, s.k16, s.k16t,
-                       s.v16t, s.v16, Tk, s.Tk_pad, Hkv);
+                       s.v16t, s.v16, Tk, s.Tk_pad, Hkv, D);
   if (P)
     hipLaunchKernelGGL(k_stage_p, dim3(Hq), dim3(256), 0, stream, static_cast<const u16*>(P), s.maxbits, s.p16t,
-                     s.p16);
+                     s.p16, D);
   return hipGetLastError();
 }
 

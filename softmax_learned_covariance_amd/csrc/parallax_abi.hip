@@ -223,7 +223,8 @@ plx_status parallax_attn_fwd_probe(const plx_attn_desc* desc, const void* q, con
   if (st != PLX_OK) return st;
   if (!plx::fast_probe_supported(g))
     return fail(PLX_ERR_UNSUPPORTED,
-                "%s: only bf16, head_dim 128, heads_q/heads_kv in {1,2,4,8} and p_per_query 0 are supported", what);
+                "%s: only bf16, head_dim 128 or 64, heads_q/heads_kv in {1,2,4,8} and p_per_query 0 are supported",
+                what);
   const bool empty = g.B == 0 || g.Tq == 0;
   if (!empty && (!q || !rho || !out))
     return fail(PLX_ERR_INVALID, "%s: q, rho and out must not be NULL", what);

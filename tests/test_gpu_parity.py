@@ -236,7 +236,8 @@ def test_determinism(plx):
 
 @pytest.mark.parametrize("d", [64, 96])
 def test_bf16_generic_head_dims(plx, d):
-    """Head dims other than 128 take the generic kernels: forward, backward and decode against the oracle."""
+    """Head dims other than 128: d = 64 runs the forward's MFMA path (zero-padded to 128) and d = 96 the
+    generic kernels; backward and decode take the generic kernels for both.  All against the oracle."""
     _announce(f"bf16 generic path d={d}")
     w = W.scaled(W.WORKLOADS["train06"], batch=2, seqlen_q=150, seqlen_k=150, heads_q=4, heads_kv=2, head_dim=d)
     q, k, v, P, dout = W.make_inputs(w, device="cuda", with_dout=True)

@@ -240,3 +240,32 @@ def test_probe_full_size_train_step_sampled(plx):
     assert rel_err(host(drho[sl]), rdr) <= BF16_TOL
     assert rel_err(host(dk[0:1, :, 0:1]), rdk) <= BF16_TOL
     assert rel_err(host(dv[0:1, :, 0:1]), rdv) <= BF16_TOL
+
+
+@pytest.mark.parametrize("T,window", [(1000, 0), (333, 100)])
+def test_probe_head_dim_64(plx, T, window):
+    """Head dim 64 (zero-padded to 128 in the MFMA operands) for the probe-form forward; its backward is
+    not offered at d = 64 and says so."""
+    w = W.scaled(W.WORKLOADS["layer06"], batch=2, seqlen_q=T, seqlen_k=T, head_dim=64)
+    _announce(f"probe forward d=64 T={T} window={window}")
+    _check(plx, w, True, window)
+    q, k, v, _, dout = W.make_inputs(w, device="cuda", with_dout=True)
+    rho = W.make_probe(w, device="cuda")
+    f = _run(plx, q, k, v, rho, window=window)
+    with pytest.raises(plx.ParallaxError):
+        plx.parallax_attn_bwd_probe(q, k, v, rho, f[0], dout, *f[1:], window=window)
+
+
+@pytest.mark.parametrize("T,Hkv", [(1000, 8), (257, 16)])
+def test_forward_head_dim_64(plx, T, Hkv):
+    """The projector-form forward at head dim 64 on the MFMA path: out, o, kbar and lse against the oracle."""
+    w = W.scaled(W.WORKLOADS["layer06"], batch=2, seqlen_q=T, seqlen_k=T, heads_kv=Hkv, head_dim=64)
+    _announce(f"forward d=64 T={T} Hkv={Hkv}")
+    q, k, v, P = W.make_inputs(w, device="cuda")
+    out, lse, kbar, o = plx.parallax_attn_fwd(q, k, v, P)
+    torch.cuda.synchronize()
+    ref = oracle.fwd(host(q), host(k), host(v), host(P), causal=True)
+    assert rel_err(host(out), ref[0]) <= BF16_TOL
+    assert rel_err(host(o), ref[3]) <= BF16_TOL
+    assert rel_err(host(kbar), ref[2]) <= BF16_TOL
+    assert np.max(np.abs(host(lse) - ref[1])) <= 1e-3
