@@ -52,11 +52,11 @@ __device__ __forceinline__ void load4_bf16(const u16* src, float* dst) {
   dst[3] = __uint_as_float(w.y & 0xffff0000u);
 }
 
-__device__ __forceinline__ void load_row_operand(const u16* row, bool ok, int hh, float s, f16x8 (&B)[8]) {
+__device__ __forceinline__ void load_row_operand(const u16* row, bool ok, int hh, float s, f16x8 (&B)[8], int D) {
 #pragma unroll
   for (int st = 0; st < 8; ++st) {
     float a[4] = {0.f, 0.f, 0.f, 0.f}, c[4] = {0.f, 0.f, 0.f, 0.f};
-    if (ok) {
+    if (ok && 16 * st < D) {   // a row of D < 128 elements reads as zero-padded
       load4_bf16(row + 16 * st + 4 * hh, a);
       load4_bf16(row + 16 * st + 8 + 4 * hh, c);
     }
@@ -102,6 +102,7 @@ struct RowParams {
   const u16* rho;
   const float* rk;
   float* drho;
+  int D;               // head dim of the caller's rows (128, or 64 zero-padded to 128 in every operand)
   int B, Tq, Tk, Tk_pad, Tq_pad, Hq, Hkv, G, causal, window;
   float scale;
   int row_begin, row_end, rows_per_block, n_rb;
@@ -149,9 +150,9 @@ __device__ __forceinline__ void row_dots(const RowParams& p, int64_t qoff, bool 
       float gv[4] = {0.f, 0.f, 0.f, 0.f};
       float4 ov = {0.f, 0.f, 0.f, 0.f}, outv = {0.f, 0.f, 0.f, 0.f};
       if (row_ok) {
-        load4_bf16(p.dout + qoff + d, gv);
-        ov = *reinterpret_cast<const float4*>(p.osa + qoff + d);
-        outv = *reinterpret_cast<const float4*>(p.out + qoff + d);
+        if (d < p.D) load4_bf16(p.dout + qoff + d, gv);
+        if (d < p.D) ov = *reinterpret_cast<const float4*>(p.osa + qoff + d);
+        if (d < p.D) outv = *reinterpret_cast<const float4*>(p.out + qoff + d);
       }
       go += gv[0] * ov.x + gv[1] * ov.y + gv[2] * ov.z + gv[3] * ov.w;
       gout += gv[0] * outv.x + gv[1] * outv.y + gv[2] * outv.z + gv[3] * outv.w;
@@ -165,7 +166,8 @@ __device__ __forceinline__ void row_dots(const RowParams& p, int64_t qoff, bool 
 // Probe form: the per-row vectors the key-major pass needs, from the supplied probe.  u = -rho,
 // dkbar = -(g.o) u = (g.o) rho, drho = -du, and dq starts at 0 (no projector term).  Writes u, dkbar,
 // drho and the zero dq of the lane's half-row; `du` holds du in the accumulator layout.
-__device__ __forceinline__ void probe_row_vectors(const RowParams& p, int64_t qoff, bool row_ok, int hh, float go,
+__device__ __forceinline__ void probe_row_vectors(const RowParams& p, int64_t qoff, int64_t woff, bool row_ok, int hh,
+                                                  float go,
                                                   const f32x16 (&du)[4], f32x16 (&u)[4], f32x16 (&dkb)[4]) {
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
@@ -173,7 +175,7 @@ __device__ __forceinline__ void probe_row_vectors(const RowParams& p, int64_t qo
     for (int j = 0; j < 4; ++j) {
       const int d = 32 * mt + 8 * j + 4 * hh;
       float rv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (row_ok) load4_bf16(p.rho + qoff + d, rv);
+      if (row_ok) if (d < p.D) load4_bf16(p.rho + qoff + d, rv);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         u[mt][4 * j + e] = -rv[e];
@@ -181,10 +183,10 @@ __device__ __forceinline__ void probe_row_vectors(const RowParams& p, int64_t qo
       }
       if (row_ok) {
         const int r = 4 * j;
-        *reinterpret_cast<float4*>(p.drho + qoff + d) = float4{-du[mt][r], -du[mt][r + 1], -du[mt][r + 2], -du[mt][r + 3]};
-        *reinterpret_cast<float4*>(p.dq + qoff + d) = float4{0.f, 0.f, 0.f, 0.f};
-        *reinterpret_cast<float4*>(p.u32 + qoff + d) = float4{u[mt][r], u[mt][r + 1], u[mt][r + 2], u[mt][r + 3]};
-        *reinterpret_cast<float4*>(p.dkb32 + qoff + d) = float4{dkb[mt][r], dkb[mt][r + 1], dkb[mt][r + 2], dkb[mt][r + 3]};
+        if (d < p.D) *reinterpret_cast<float4*>(p.drho + qoff + d) = float4{-du[mt][r], -du[mt][r + 1], -du[mt][r + 2], -du[mt][r + 3]};
+        if (d < p.D) *reinterpret_cast<float4*>(p.dq + qoff + d) = float4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<float4*>(p.u32 + woff + d) = float4{u[mt][r], u[mt][r + 1], u[mt][r + 2], u[mt][r + 3]};
+        *reinterpret_cast<float4*>(p.dkb32 + woff + d) = float4{dkb[mt][r], dkb[mt][r + 1], dkb[mt][r + 2], dkb[mt][r + 3]};
       }
     }
 }
@@ -223,7 +225,8 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
   const float boundG = 128.f * mx(MB, kMaxDO) * mx(MB, kMaxV);
   const float sPG = range_scale(PROBE ? 2.f * boundG : boundG);   // probe form: |G - g.o| <= 2 boundG
 
-  const int64_t qoff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * kD;
+  const int64_t qoff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * p.D;   // caller rows
+  const int64_t woff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * kD;    // workspace rows
   const int64_t soff = (static_cast<int64_t>(b) * p.Hq + h) * p.Tq + (row_ok ? row : 0);
   float lse2 = row_ok ? p.lse[soff] * kLog2e : 0.f;
   if (!(lse2 > -INFINITY && lse2 < INFINITY)) lse2 = 0.f;  // a row without keys: every S is masked
@@ -243,8 +246,8 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
   const int r_kbeg = p.window > 0 ? max(0, row + off - p.window + 1) : 0;
 
   f16x8 qB[8], gB[8];
-  load_row_operand(p.q + qoff, row_ok, hh, sQ, qB);
-  load_row_operand(p.dout + qoff, row_ok, hh, sG, gB);
+  load_row_operand(p.q + qoff, row_ok, hh, sQ, qB, p.D);
+  load_row_operand(p.dout + qoff, row_ok, hh, sG, gB, p.D);
 
   // probe form: du = sum_j p_j (G_j - g.o) k_j directly (kbar is not an input), so g.o comes first
   float go_pre = 0.f;
@@ -254,8 +257,8 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
       float gv[4] = {0.f, 0.f, 0.f, 0.f};
       float4 ov = {0.f, 0.f, 0.f, 0.f};
       if (row_ok) {
-        load4_bf16(p.dout + qoff + d, gv);
-        ov = *reinterpret_cast<const float4*>(p.osa + qoff + d);
+        if (d < p.D) load4_bf16(p.dout + qoff + d, gv);
+        if (d < p.D) ov = *reinterpret_cast<const float4*>(p.osa + qoff + d);
       }
       go_pre += gv[0] * ov.x + gv[1] * ov.y + gv[2] * ov.z + gv[3] * ov.w;
     }
@@ -321,7 +324,7 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
     const float fdu = 1.f / (sPG * sK);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) accDU[mt] *= fdu;
-    probe_row_vectors(p, qoff, row_ok, hh, go, accDU, accU, accPD);
+    probe_row_vectors(p, qoff, woff, row_ok, hh, go, accDU, accU, accPD);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -352,8 +355,8 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
           float qv[4] = {0.f, 0.f, 0.f, 0.f};
           float4 kv = {0.f, 0.f, 0.f, 0.f};
           if (row_ok) {
-            load4_bf16(p.q + qoff + d, qv);
-            kv = *reinterpret_cast<const float4*>(p.kbar + qoff + d);
+            if (d < p.D) load4_bf16(p.q + qoff + d, qv);
+            if (d < p.D) kv = *reinterpret_cast<const float4*>(p.kbar + qoff + d);
           }
           const float k4[4] = {kv.x, kv.y, kv.z, kv.w};
 #pragma unroll
@@ -366,9 +369,9 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
             dumax = fmaxf(dumax, fabsf(accDU[mt][r]));
           }
           if (row_ok) {
-            *reinterpret_cast<float4*>(p.x32 + qoff + d) =
+            *reinterpret_cast<float4*>(p.x32 + woff + d) =
                 float4{xv[mt][4 * j], xv[mt][4 * j + 1], xv[mt][4 * j + 2], xv[mt][4 * j + 3]};
-            *reinterpret_cast<float4*>(p.du32 + qoff + d) =
+            *reinterpret_cast<float4*>(p.du32 + woff + d) =
                 float4{accDU[mt][4 * j], accDU[mt][4 * j + 1], accDU[mt][4 * j + 2], accDU[mt][4 * j + 3]};
           }
         }
@@ -436,10 +439,10 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
             e1 += fabsf(dk);
           }
           if (row_ok) {
-            *reinterpret_cast<float4*>(p.dq + qoff + d) = float4{pd4[0], pd4[1], pd4[2], pd4[3]};
-            *reinterpret_cast<float4*>(p.u32 + qoff + d) =
+            if (d < p.D) *reinterpret_cast<float4*>(p.dq + qoff + d) = float4{pd4[0], pd4[1], pd4[2], pd4[3]};
+            *reinterpret_cast<float4*>(p.u32 + woff + d) =
                 float4{accU[mt][4 * j], accU[mt][4 * j + 1], accU[mt][4 * j + 2], accU[mt][4 * j + 3]};
-            *reinterpret_cast<float4*>(p.dkb32 + qoff + d) =
+            *reinterpret_cast<float4*>(p.dkb32 + woff + d) =
                 float4{accPD[mt][4 * j], accPD[mt][4 * j + 1], accPD[mt][4 * j + 2], accPD[mt][4 * j + 3]};
           }
         }
@@ -548,6 +551,7 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = 32 * mt + 8 * j + 4 * hh;
+        if (d >= p.D) continue;   // padding dims of a D < 128 head
         const int r = 4 * j;
         const float4 q0 = *reinterpret_cast<const float4*>(p.dq + qoff + d);  // P du from the epilogue
         *reinterpret_cast<float4*>(p.dq + qoff + d) =
@@ -611,7 +615,8 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
   const float boundG = 128.f * mx(MB, kMaxDO) * mx(MB, kMaxV);
   const float sPG = range_scale(PROBE ? 2.f * boundG : boundG);   // probe form: |G - g.o| <= 2 boundG
 
-  const int64_t qoff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * kD;
+  const int64_t qoff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * p.D;   // caller rows
+  const int64_t woff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * kD;    // workspace rows
   const int64_t soff = (static_cast<int64_t>(b) * p.Hq + h) * p.Tq + (row_ok ? row : 0);
   float lse2 = row_ok ? p.lse[soff] * kLog2e : 0.f;
   if (!(lse2 > -INFINITY && lse2 < INFINITY)) lse2 = 0.f;  // a row without keys: every S is masked
@@ -631,8 +636,8 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
   const int r_kbeg = p.window > 0 ? max(0, row + off - p.window + 1) : 0;
 
   f16x8 qB[8], gB[8];
-  load_row_operand(p.q + qoff, row_ok, hh, sQ, qB);
-  load_row_operand(p.dout + qoff, row_ok, hh, sG, gB);
+  load_row_operand(p.q + qoff, row_ok, hh, sQ, qB, p.D);
+  load_row_operand(p.dout + qoff, row_ok, hh, sG, gB, p.D);
 
   // probe form: du = sum_j p_j (G_j - g.o) k_j directly (kbar is not an input), so g.o comes first
   float go_pre = 0.f;
@@ -642,8 +647,8 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
       float gv[4] = {0.f, 0.f, 0.f, 0.f};
       float4 ov = {0.f, 0.f, 0.f, 0.f};
       if (row_ok) {
-        load4_bf16(p.dout + qoff + d, gv);
-        ov = *reinterpret_cast<const float4*>(p.osa + qoff + d);
+        if (d < p.D) load4_bf16(p.dout + qoff + d, gv);
+        if (d < p.D) ov = *reinterpret_cast<const float4*>(p.osa + qoff + d);
       }
       go_pre += gv[0] * ov.x + gv[1] * ov.y + gv[2] * ov.z + gv[3] * ov.w;
     }
@@ -732,7 +737,7 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
       for (int j = 0; j < 4; ++j) {
         const int d = 32 * mt + 8 * j + 4 * hh;
         float rv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (row_ok) load4_bf16(p.rho + qoff + d, rv);
+        if (row_ok) if (d < p.D) load4_bf16(p.rho + qoff + d, rv);
         float dr[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -741,10 +746,10 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
           emax = fmaxf(emax, fabsf(go * rv[e]));
         }
         if (row_ok) {
-          *reinterpret_cast<float4*>(p.drho + qoff + d) = float4{dr[0], dr[1], dr[2], dr[3]};
-          *reinterpret_cast<float4*>(p.dq + qoff + d) = float4{0.f, 0.f, 0.f, 0.f};
-          *reinterpret_cast<float4*>(p.u32 + qoff + d) = float4{-rv[0], -rv[1], -rv[2], -rv[3]};
-          *reinterpret_cast<float4*>(p.dkb32 + qoff + d) = float4{go * rv[0], go * rv[1], go * rv[2], go * rv[3]};
+          if (d < p.D) *reinterpret_cast<float4*>(p.drho + qoff + d) = float4{dr[0], dr[1], dr[2], dr[3]};
+          if (d < p.D) *reinterpret_cast<float4*>(p.dq + qoff + d) = float4{0.f, 0.f, 0.f, 0.f};
+          *reinterpret_cast<float4*>(p.u32 + woff + d) = float4{-rv[0], -rv[1], -rv[2], -rv[3]};
+          *reinterpret_cast<float4*>(p.dkb32 + woff + d) = float4{go * rv[0], go * rv[1], go * rv[2], go * rv[3]};
         }
       }
     umax = xor32_max(umax);
@@ -765,8 +770,8 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
           float qv[4] = {0.f, 0.f, 0.f, 0.f};
           float4 kv = {0.f, 0.f, 0.f, 0.f};
           if (row_ok) {
-            load4_bf16(p.q + qoff + d, qv);
-            kv = *reinterpret_cast<const float4*>(p.kbar + qoff + d);
+            if (d < p.D) load4_bf16(p.q + qoff + d, qv);
+            if (d < p.D) kv = *reinterpret_cast<const float4*>(p.kbar + qoff + d);
           }
           const float k4[4] = {kv.x, kv.y, kv.z, kv.w};
           float x4[4];
@@ -779,8 +784,8 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
             dumax = fmaxf(dumax, fabsf(accDU[mt][r]));
           }
           if (row_ok) {
-            *reinterpret_cast<float4*>(p.x32 + qoff + d) = float4{x4[0], x4[1], x4[2], x4[3]};
-            *reinterpret_cast<float4*>(p.du32 + qoff + d) =
+            *reinterpret_cast<float4*>(p.x32 + woff + d) = float4{x4[0], x4[1], x4[2], x4[3]};
+            *reinterpret_cast<float4*>(p.du32 + woff + d) =
                 float4{accDU[mt][4 * j], accDU[mt][4 * j + 1], accDU[mt][4 * j + 2], accDU[mt][4 * j + 3]};
           }
         }
@@ -814,8 +819,8 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
           float qv[4] = {0.f, 0.f, 0.f, 0.f};
           float4 kv = {0.f, 0.f, 0.f, 0.f};
           if (row_ok) {
-            load4_bf16(p.q + qoff + d, qv);
-            kv = *reinterpret_cast<const float4*>(p.kbar + qoff + d);
+            if (d < p.D) load4_bf16(p.q + qoff + d, qv);
+            if (d < p.D) kv = *reinterpret_cast<const float4*>(p.kbar + qoff + d);
           }
           x8[4 * half + 0] = qv[0] - kv.x;
           x8[4 * half + 1] = qv[1] - kv.y;
@@ -841,7 +846,7 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
         for (int j = 0; j < 4; ++j) {
           const int d = 32 * mt + 8 * j + 4 * hh;
           float4 kv = {0.f, 0.f, 0.f, 0.f};
-          if (row_ok) kv = *reinterpret_cast<const float4*>(p.kbar + qoff + d);
+          if (row_ok) if (d < p.D) kv = *reinterpret_cast<const float4*>(p.kbar + qoff + d);
           const float k4[4] = {kv.x, kv.y, kv.z, kv.w};
           float u4[4], pd4[4], dk4[4];
 #pragma unroll
@@ -856,9 +861,9 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
             emax = fmaxf(emax, fabsf(dk4[e]));
           }
           if (row_ok) {
-            *reinterpret_cast<float4*>(p.dq + qoff + d) = float4{pd4[0], pd4[1], pd4[2], pd4[3]};
-            *reinterpret_cast<float4*>(p.u32 + qoff + d) = float4{u4[0], u4[1], u4[2], u4[3]};
-            *reinterpret_cast<float4*>(p.dkb32 + qoff + d) = float4{dk4[0], dk4[1], dk4[2], dk4[3]};
+            if (d < p.D) *reinterpret_cast<float4*>(p.dq + qoff + d) = float4{pd4[0], pd4[1], pd4[2], pd4[3]};
+            *reinterpret_cast<float4*>(p.u32 + woff + d) = float4{u4[0], u4[1], u4[2], u4[3]};
+            *reinterpret_cast<float4*>(p.dkb32 + woff + d) = float4{dk4[0], dk4[1], dk4[2], dk4[3]};
           }
         }
     }
@@ -913,6 +918,7 @@ struct KeyParams {
   const float* rstat;  // row statistics per 32-row tile (see RowParams)
   int64_t qstride;     // elements between the consecutive query-row copies q16, do16, u16, e16
   int B, Tq, Tk, Tk_pad, Tq_pad, lo_pad, Hq, Hkv, G, causal, window;
+  int D;               // head dim of dk, dv rows
   float scale;
   int row_lo, row_hi, accumulate, n_kb, key_hi;
 };
@@ -1149,13 +1155,14 @@ __global__ __launch_bounds__(256) void k_bwd_keys_fast(KeyParams p) {
   }
   if (key_ok) {
     const float fk = 1.f / C, fv = 1.f / (sG * cV);
-    float* dkr = p.dk + ((static_cast<int64_t>(b) * p.Tk + key) * p.Hkv + g) * kD;
-    float* dvr = p.dv + ((static_cast<int64_t>(b) * p.Tk + key) * p.Hkv + g) * kD;
+    float* dkr = p.dk + ((static_cast<int64_t>(b) * p.Tk + key) * p.Hkv + g) * p.D;
+    float* dvr = p.dv + ((static_cast<int64_t>(b) * p.Tk + key) * p.Hkv + g) * p.D;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = 32 * mt + 8 * j + 4 * hh, r = 4 * j;
+        if (d >= p.D) continue;   // padding dims of a D < 128 head
         float4 kv = {accK[mt][r] * fk, accK[mt][r + 1] * fk, accK[mt][r + 2] * fk, accK[mt][r + 3] * fk};
         float4 vv = {accV[mt][r] * fv, accV[mt][r + 1] * fv, accV[mt][r + 2] * fv, accV[mt][r + 3] * fv};
         if (p.accumulate) {
@@ -1498,12 +1505,13 @@ __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
     }
     if (key_ok) {
       const float fv = 1.f / (ks.sG * ks.cV);
-      float* dvr = p.dv + ((static_cast<int64_t>(b) * p.Tk + key) * p.Hkv + g) * kD;
+      float* dvr = p.dv + ((static_cast<int64_t>(b) * p.Tk + key) * p.Hkv + g) * p.D;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int d = 32 * mt + 8 * j + 4 * hh, r = 4 * j;
+          if (d >= p.D) continue;   // padding dims of a D < 128 head
           float4 vv = {accV[mt][r] * fv, accV[mt][r + 1] * fv, accV[mt][r + 2] * fv, accV[mt][r + 3] * fv};
           if (p.accumulate) {
             const float4 v0 = *reinterpret_cast<const float4*>(dvr + d);
@@ -1512,12 +1520,13 @@ __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
           *reinterpret_cast<float4*>(dvr + d) = vv;
         }
       const float fk = 1.f / ks.C;
-      float* dkr = p.dk + ((static_cast<int64_t>(b) * p.Tk + key) * p.Hkv + g) * kD;
+      float* dkr = p.dk + ((static_cast<int64_t>(b) * p.Tk + key) * p.Hkv + g) * p.D;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int d = 32 * mt + 8 * j + 4 * hh, r = 4 * j;
+          if (d >= p.D) continue;   // padding dims of a D < 128 head
           float4 kv = {accK[mt][r] * fk, accK[mt][r + 1] * fk, accK[mt][r + 2] * fk, accK[mt][r + 3] * fk};
           if (p.accumulate) {
             const float4 k0 = *reinterpret_cast<const float4*>(dkr + d);
@@ -1539,6 +1548,7 @@ struct DqParams {
   const uint32_t* maxbits;
   float* dq;
   int B, Tq, Tk, Tk_pad, Tq_pad, Hq, Hkv, G, causal, window, row_lo, row_hi, row_begin, rows_per_block, n_rb;
+  int D;               // head dim of dq rows
   float scale;
 };
 
@@ -1633,12 +1643,13 @@ __global__ __launch_bounds__(512) void k_bwd_dq(DqParams p) {
   const int row = q0 + ql;
   if (row >= p.row_lo && row < p.row_hi && row < p.Tq) {
     const float fq = ks.sQ / (ks.C * ks.sK);
-    float* dqr = p.dq + ((static_cast<int64_t>(b) * p.Tq + row) * p.Hq + h) * kD;
+    float* dqr = p.dq + ((static_cast<int64_t>(b) * p.Tq + row) * p.Hq + h) * p.D;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = 32 * nt + 8 * j + 4 * hh, r = 4 * j;
+        if (d >= p.D) continue;   // padding dims of a D < 128 head
         const float4 q = *reinterpret_cast<const float4*>(dqr + d);
         *reinterpret_cast<float4*>(dqr + d) = float4{q.x + acc[nt][r] * fq, q.y + acc[nt][r + 1] * fq,
                                                      q.z + acc[nt][r + 2] * fq, q.w + acc[nt][r + 3] * fq};
@@ -1752,7 +1763,7 @@ __global__ __launch_bounds__(256) void k_dp_partial(const float* x32, const floa
         float4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
 }
 
-__global__ __launch_bounds__(256) void k_dp_reduce(const float* part, float* dP, int nchunks, int Hq) {
+__global__ __launch_bounds__(256) void k_dp_reduce(const float* part, float* dP, int nchunks, int Hq, int D) {
   const int64_t n = static_cast<int64_t>(Hq) * kD * kD;
   for (int64_t e = blockIdx.x * 256LL + threadIdx.x; e < n; e += 256LL * gridDim.x) {
     // in chunk order; eight loads are issued before their adds
@@ -1766,7 +1777,10 @@ __global__ __launch_bounds__(256) void k_dp_reduce(const float* part, float* dP,
       for (int u = 0; u < 8; ++u) s += v[u];
     }
     for (; c < nchunks; ++c) s += part[c * n + e];
-    dP[e] = s;
+    // the partials are 128 x 128 per head; a D < 128 projector takes its D x D corner
+    const int64_t hh = e / (kD * kD);
+    const int a = static_cast<int>((e / kD) % kD), c2 = static_cast<int>(e % kD);
+    if (a < D && c2 < D) dP[(hh * D + a) * D + c2] = s;
   }
 }
 
@@ -1822,7 +1836,7 @@ int bwd_split(const Geom& g) { return 256 < g.Tq ? 256 : g.Tq; }
 
 bool fast_bwd_supported(const Geom& g) {
   const int G = g.Hq / g.Hkv;
-  return g.bf16 && g.d == kD && !g.p_per_query && (G == 1 || G == 2 || G == 4) && g.B > 0 && g.Tq > 0 &&
+  return g.bf16 && (g.d == kD || g.d == 64) && !g.p_per_query && (G == 1 || G == 2 || G == 4) && g.B > 0 && g.Tq > 0 &&
          g.Tk > 0;
 }
 
@@ -1857,8 +1871,8 @@ hipError_t bwd_impl(const Geom& g, const BwdArgs& a, int split_rows, void* ws, h
   if (split > bwd_split(g)) split = bwd_split(g);
   const BwdWs w = bwd_layout(g, bwd_split(g), ws);
   const int G = g.Hq / g.Hkv;
-  const int64_t q_elems = static_cast<int64_t>(g.B) * g.Tq * g.Hq * kD;
-  hipError_t e = launch_staging(w.st, q, q_elems, k, v, P, g.B, g.Tk, g.Hkv, g.Hq, stream, dout, q_elems, kMaxDO);
+  const int64_t q_elems = static_cast<int64_t>(g.B) * g.Tq * g.Hq * g.d;
+  hipError_t e = launch_staging(w.st, q, q_elems, k, v, P, g.B, g.Tk, g.Hkv, g.Hq, stream, dout, q_elems, kMaxDO, g.d);
   if (e != hipSuccess) return e;
 
   // row statistics of padded rows stay 0 (the key-major kernel reads whole 32-row tiles)
@@ -1884,6 +1898,7 @@ hipError_t bwd_impl(const Geom& g, const BwdArgs& a, int split_rows, void* ws, h
   rp.st_alpha = w.alpha;
   rp.st_delta = w.delta;
   rp.rstat = w.rstat;
+  rp.D = g.d;
   rp.rho = static_cast<const u16*>(a.rho);
   rp.rk = a.rk;
   rp.drho = a.drho;
@@ -1905,10 +1920,11 @@ hipError_t bwd_impl(const Geom& g, const BwdArgs& a, int split_rows, void* ws, h
   // side lane beside du.
   const bool use_side = split > 0 && split < g.Tq;
   SideLane side = use_side ? side_fork(stream) : SideLane{stream, stream};
-  e = launch_stage_rows(q, false, w.st.maxbits, kMaxQ, w.q16, nullptr, g.B, g.Tq, w.Tq_pad, g.Hq, 0, 0, side.stream);
+  e = launch_stage_rows(q, false, w.st.maxbits, kMaxQ, w.q16, nullptr, g.B, g.Tq, w.Tq_pad, g.Hq, 0, 0, side.stream,
+                        g.d);
   if (e != hipSuccess) return e;
   e = launch_stage_rows(dout, false, w.st.maxbits, kMaxDO, w.do16, nullptr, g.B, g.Tq, w.Tq_pad, g.Hq, 0, 0,
-                        side.stream);
+                        side.stream, g.d);
   if (e != hipSuccess) return e;
   if (split > 0) {
     RowParams r = rp;
@@ -1959,6 +1975,7 @@ hipError_t bwd_impl(const Geom& g, const BwdArgs& a, int split_rows, void* ws, h
   kp.alpha = w.alpha;
   kp.delta = w.delta;
   kp.rstat = w.rstat;
+  kp.D = g.d;
   kp.qstride = w.do16 - w.q16;
   kp.maxbits = w.st.maxbits;
   kp.dk = dk;
@@ -2013,6 +2030,7 @@ hipError_t bwd_impl(const Geom& g, const BwdArgs& a, int split_rows, void* ws, h
     dp.k16t = w.st.k16t;
     dp.maxbits = w.st.maxbits;
     dp.dq = dq;
+    dp.D = g.d;
     dp.B = g.B;
     dp.Tq = g.Tq;
     dp.Tk = g.Tk;
@@ -2038,7 +2056,7 @@ hipError_t bwd_impl(const Geom& g, const BwdArgs& a, int split_rows, void* ws, h
     const int R = g.B * g.Tq;
     hipLaunchKernelGGL(k_dp_partial, dim3(g.Hq * w.nchunks), dim3(256), 0, stream, w.x32, w.du32, w.part, R, g.Hq);
     const int nred = (g.Hq * kD * kD + 255) / 256;
-    hipLaunchKernelGGL(k_dp_reduce, dim3(nred), dim3(256), 0, stream, w.part, dP, w.nchunks, g.Hq);
+    hipLaunchKernelGGL(k_dp_reduce, dim3(nred), dim3(256), 0, stream, w.part, dP, w.nchunks, g.Hq, g.d);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -257,7 +257,7 @@ inline Staging staging_layout(void* ws, int B, int Tk, int Hkv, int Hq, bool bac
 // Query-side fp16 copies in the row-tile layout (see k_stage_rows in fast_staging.hip).
 hipError_t launch_stage_rows(const void* src, bool f32, const uint32_t* maxbits, int max_idx, _Float16* dst,
                              _Float16* lo, int B, int Tq, int Tq_pad, int Hq, int lo_rows, int lo_pad,
-                             hipStream_t stream);
+                             hipStream_t stream, int D = kD);   // D: row length of a bf16 src (fp32 src rows are 128)
 
 // Launches the staging kernels: max-abs of q (rows [0, Tq)), k, v, P (and of one more bf16 tensor,
 // `extra`, into maxbits[extra_slot]) in one launch, then the fp16 copies.  q may be nullptr (decode

@@ -179,7 +179,7 @@ __global__ __launch_bounds__(256) void k_stage_p(const u16* P, const uint32_t* m
 template <bool F32>
 __global__ __launch_bounds__(256) void k_stage_rows(const void* src, const uint32_t* maxbits, int max_idx,
                                                     _Float16* dst, _Float16* lo, int Tq, int Tq_pad, int Hq,
-                                                    int lo_rows, int lo_pad) {
+                                                    int lo_rows, int lo_pad, int D) {
   __shared__ uint2 hs[16 * 32 * 2];   // [chunk][row][half of the chunk]
   __shared__ uint2 ls[16 * 32 * 2];
   // the heads of one row tile are consecutive blocks, so they read the same rows together
@@ -191,8 +191,8 @@ __global__ __launch_bounds__(256) void k_stage_rows(const void* src, const uint3
   for (int rep = 0; rep < 2; ++rep) {
     const int i = t + 256 * rep, r = i >> 4, k = i & 15, row = r0 + r;   // d = 8 k .. 8 k + 7
     float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (row < Tq) {
-      const int64_t off = ((static_cast<int64_t>(b) * Tq + row) * Hq + h) * kD + 8 * k;
+    if (row < Tq && (F32 || 8 * k < D)) {   // bf16 caller rows of D < 128 elements are zero-padded
+      const int64_t off = ((static_cast<int64_t>(b) * Tq + row) * Hq + h) * (F32 ? kD : D) + 8 * k;
       if constexpr (F32) {
         const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + off);
         const float4 c = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + off + 4);
@@ -268,15 +268,15 @@ hipError_t launch_staging(const Staging& s, const void* q, int64_t q_elems, cons
 
 hipError_t launch_stage_rows(const void* src, bool f32, const uint32_t* maxbits, int max_idx, _Float16* dst,
                              _Float16* lo, int B, int Tq, int Tq_pad, int Hq, int lo_rows, int lo_pad,
-                             hipStream_t stream) {
+                             hipStream_t stream, int D) {
   if (B == 0 || Tq_pad == 0) return hipSuccess;
   dim3 grid(Hq * (Tq_pad / 32), 1, B);
   if (f32)
     hipLaunchKernelGGL(k_stage_rows<true>, grid, dim3(256), 0, stream, src, maxbits, max_idx, dst, lo, Tq, Tq_pad,
-                       Hq, lo_rows, lo_pad);
+                       Hq, lo_rows, lo_pad, D);
   else
     hipLaunchKernelGGL(k_stage_rows<false>, grid, dim3(256), 0, stream, src, maxbits, max_idx, dst, lo, Tq, Tq_pad,
-                       Hq, lo_rows, lo_pad);
+                       Hq, lo_rows, lo_pad, D);
   return hipGetLastError();
 }
 

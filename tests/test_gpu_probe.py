@@ -244,16 +244,11 @@ def test_probe_full_size_train_step_sampled(plx):
 
 @pytest.mark.parametrize("T,window", [(1000, 0), (333, 100)])
 def test_probe_head_dim_64(plx, T, window):
-    """Head dim 64 (zero-padded to 128 in the MFMA operands) for the probe-form forward; its backward is
-    not offered at d = 64 and says so."""
-    w = W.scaled(W.WORKLOADS["layer06"], batch=2, seqlen_q=T, seqlen_k=T, head_dim=64)
-    _announce(f"probe forward d=64 T={T} window={window}")
+    """Head dim 64 (zero-padded to 128 in the MFMA operands) for the probe-form forward and backward."""
+    w = W.scaled(W.WORKLOADS["train06"], batch=2, seqlen_q=T, seqlen_k=T, head_dim=64)
+    _announce(f"probe forward + backward d=64 T={T} window={window}")
     _check(plx, w, True, window)
-    q, k, v, _, dout = W.make_inputs(w, device="cuda", with_dout=True)
-    rho = W.make_probe(w, device="cuda")
-    f = _run(plx, q, k, v, rho, window=window)
-    with pytest.raises(plx.ParallaxError):
-        plx.parallax_attn_bwd_probe(q, k, v, rho, f[0], dout, *f[1:], window=window)
+    _check_bwd(plx, w, True, window)
 
 
 @pytest.mark.parametrize("T,Hkv", [(1000, 8), (257, 16)])
