@@ -45,6 +45,7 @@ struct DecParams {
   float *so, *su, *salpha, *slse;  // combined: o, u [B][Hq][128], alpha, lse [B][Hq]
   float* pc;                     // pass 2 partials [B][Hq][ns][128]
   int B, L, Hq, Hkv, G, window, ns, chunk;
+  int D;                         // head dim of the caller's rows (128, or 64 zero-padded to 128 internally)
   int T, t0;                     // new tokens per sequence; first token of this launch's chunk
   int Tc;                        // tokens in the chunk
   float scale;
@@ -113,8 +114,10 @@ __device__ __forceinline__ int64_t cache_row(const DecParams& p, int b, int key)
   }
 }
 
+// Chunk c (8 elements) of a cache row; chunks past a D < 128 head read as zeros.
 __device__ __forceinline__ u32x4 fetch16(const u16* base, const DecParams& p, int64_t row, int g, int c) {
-  return *reinterpret_cast<const u32x4*>(base + (row * p.Hkv + g) * kD + c * 8);
+  if (c * 8 >= p.D) return u32x4{0u, 0u, 0u, 0u};
+  return *reinterpret_cast<const u32x4*>(base + (row * p.Hkv + g) * p.D + c * 8);
 }
 
 template <bool PAGED>
@@ -210,7 +213,7 @@ __global__ __launch_bounds__(256) void k_dec_pass1(DecParams p) {
   const float c2 = p.scale * kLog2e;
   for (int e = tid; e < G * kD; e += 256) {
     const int h = e / kD, d = e % kD;
-    T.q[h][d] = bf16_to_f32(p.q[row_bh(p, b, g, h) * kD + d]) * c2;  // scores in log2 units
+    T.q[h][d] = d < p.D ? bf16_to_f32(p.q[row_bh(p, b, g, h) * p.D + d]) * c2 : 0.f;  // scores in log2 units
   }
   // keys of this split that each of the wave's rows sees (the softmax of row h is done by wave h % 4)
   constexpr int RW = G > 4 ? 2 : 1;   // rows per wave
@@ -350,12 +353,13 @@ __global__ __launch_bounds__(128) void k_dec_combine1(DecParams p) {
   const bool has = L > 0.f;
   o = has ? o / L : 0.f;
   kb = has ? kb / L : 0.f;
-  const float qd = bf16_to_f32(p.q[bh * kD + d]);
+  const float qd = d < p.D ? bf16_to_f32(p.q[bh * p.D + d]) : 0.f;
   xs[d] = qd - kb;
   __syncthreads();
   float u = 0.f;
-  const u16* Ph = p.P + static_cast<int64_t>(h) * kD * kD;
-  for (int bb = 0; bb < kD; ++bb) u = fmaf(bf16_to_f32(Ph[bb * kD + d]), xs[bb], u);  // u[d] = sum_b P[b][d] x[b]
+  const u16* Ph = p.P + static_cast<int64_t>(h) * p.D * p.D;
+  if (d < p.D)
+    for (int bb = 0; bb < p.D; ++bb) u = fmaf(bf16_to_f32(Ph[bb * p.D + d]), xs[bb], u);  // u[d] = sum_b P[b][d] x[b]
   float al = u * kb;
 #pragma unroll
   for (int o2 = 32; o2 > 0; o2 >>= 1) al += __shfl_xor(al, o2, 64);
@@ -384,7 +388,7 @@ __global__ __launch_bounds__(256) void k_dec_pass2(DecParams p) {
   for (int e = tid; e < G * kD; e += 256) {
     const int h = e / kD, d = e % kD;
     const int64_t bh = row_bh(p, b, g, h);
-    T.q[h][d] = bf16_to_f32(p.q[bh * kD + d]) * c2;
+    T.q[h][d] = d < p.D ? bf16_to_f32(p.q[bh * p.D + d]) * c2 : 0.f;
     T.u[h][d] = p.su[bh * kD + d];
   }
   if (tid < G) {
@@ -463,8 +467,10 @@ __global__ __launch_bounds__(128) void k_dec_finish(DecParams p) {
 #pragma unroll 8
   for (int s = 0; s < p.ns; ++s) c += p.pc[(bh * p.ns + s) * kD + d];
   const float r = p.so[bh * kD + d] + c;
-  if (p.out_bf16) static_cast<u16*>(p.out)[bh * kD + d] = static_cast<u16>(f32_to_bf16(r));
-  else static_cast<float*>(p.out)[bh * kD + d] = r;
+  if (d < p.D) {
+    if (p.out_bf16) static_cast<u16*>(p.out)[bh * p.D + d] = static_cast<u16>(f32_to_bf16(r));
+    else static_cast<float*>(p.out)[bh * p.D + d] = r;
+  }
   if (p.cor) {
     __shared__ float part[2][2];
     float cc = c * c, oo = r * r;
@@ -523,7 +529,7 @@ DecWs dec_layout(const Geom& g, void* ws) {
 
 bool fast_decode_supported(const Geom& g) {
   const int G = g.Hq / g.Hkv;
-  return g.bf16 && g.d == kD && !g.p_per_query && (G == 1 || G == 2 || G == 4);
+  return g.bf16 && (g.d == kD || g.d == 64) && !g.p_per_query && (G == 1 || G == 2 || G == 4);
 }
 
 size_t fast_decode_workspace(const Geom& g) { return dec_layout(g, nullptr).bytes; }
@@ -596,6 +602,7 @@ hipError_t launch_fast_decode(const Geom& g, const void* q, const void* kc, cons
   p.Hkv = g.Hkv;
   p.G = g.Hq / g.Hkv;
   p.window = g.window;
+  p.D = g.d;
   p.T = g.Tq;
   p.t0 = 0;
   p.Tc = g.Tq;

@@ -236,8 +236,8 @@ def test_determinism(plx):
 
 @pytest.mark.parametrize("d", [64, 96])
 def test_bf16_generic_head_dims(plx, d):
-    """Head dims other than 128: d = 64 runs the forward's MFMA path (zero-padded to 128) and d = 96 the
-    generic kernels; backward and decode take the generic kernels for both.  All against the oracle."""
+    """Head dims other than 128: d = 64 runs the MFMA paths (zero-padded to 128) and d = 96 the generic
+    kernels, for forward, backward and decode.  All against the oracle."""
     _announce(f"bf16 generic path d={d}")
     w = W.scaled(W.WORKLOADS["train06"], batch=2, seqlen_q=150, seqlen_k=150, heads_q=4, heads_kv=2, head_dim=d)
     q, k, v, P, dout = W.make_inputs(w, device="cuda", with_dout=True)
@@ -520,3 +520,25 @@ def test_decode_multi_token(plx, T, Hkv, window):
     last = plx.parallax_attn_decode(q[:, -1].contiguous(), kc, vc, P, seqlens=seqlens, window=window)
     torch.cuda.synchronize()
     assert rel_err(host(out[:, -1]), host(last)) <= 1e-5
+
+
+def test_decode_head_dim_64(plx):
+    """Head dim 64 on the decode's fast path (zero-padded to 128 inside): one token and three tokens per
+    sequence, contiguous and paged, against the oracle."""
+    _announce("decode d=64")
+    w = W.scaled(W.WORKLOADS["decode"], batch=3, seqlen_k=700, head_dim=64)
+    q, kc, vc, P = W.make_inputs(w, device="cuda")
+    seqlens = torch.tensor([700, 5, 333], dtype=torch.int32, device="cuda")
+    out = plx.parallax_attn_decode(q, kc, vc, P, seqlens=seqlens)
+    kp, vp, table = _to_pages(kc, vc, 32, seed=9)
+    outp = plx.parallax_attn_decode_paged(q, kp, vp, table, P, seqlens=seqlens, seqlen_k=700)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+    q3 = torch.randn((3, 3, w.heads_q, 64), generator=g, device="cuda").to(torch.bfloat16)
+    out3 = plx.parallax_attn_decode(q3, kc, vc, P, seqlens=seqlens, window=200)
+    torch.cuda.synchronize()
+    assert torch.equal(out, outp)
+    sl = host(seqlens).astype(int)
+    assert rel_err(host(out), oracle.decode(host(q), host(kc), host(vc), host(P), seqlens=sl)) <= BF16_TOL
+    ref3 = _multi_token_ref(host(q3), host(kc), host(vc), host(P), sl, 200)
+    assert rel_err(host(out3), ref3) <= BF16_TOL
