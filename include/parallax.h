@@ -64,7 +64,7 @@ typedef struct {
   int32_t seqlen_k;       /* Tk >= 0 (decode: cache capacity Lmax) */
   int32_t heads_q;        /* Hq >= 1 */
   int32_t heads_kv;       /* Hkv >= 1, Hq % Hkv == 0; query head h uses key/value head h / (Hq/Hkv) */
-  int32_t head_dim;       /* d, 1..128 */
+  int32_t head_dim;       /* d, 1..128 (bf16 with d = 128 or 64 runs the MFMA paths; other d and fp32 the generic fp32 kernels) */
   int32_t causal;         /* nonzero: bottom-right aligned causal mask (ignored by decode) */
   int32_t window;         /* <= 0: no window; > 0: keep only the `window` newest visible keys (the query's own included) */
   float   softmax_scale;  /* <= 0 selects 1/sqrt(head_dim) */
