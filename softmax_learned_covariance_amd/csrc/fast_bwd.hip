@@ -1,4 +1,5 @@
-// Parallax backward for gfx950 (head_dim 128, bf16 inputs, fp16 MFMA).
+// Parallax backward for gfx950 (head_dim 128, or 64 zero-padded to 128; bf16 inputs, fp16 MFMA), for the
+// projector form and the probe form.
 //
 // The pages give no backward; these kernels evaluate the chain rule of the
 // forward definition (output = softmax output plus the key/value covariance

@@ -1,4 +1,4 @@
-// Shared pieces of the MFMA fast path (head_dim 128, bf16 inputs): operand
+// Shared pieces of the MFMA fast path (head_dim 128, or 64 zero-padded to 128; bf16 inputs): operand
 // types, the fp16 staging layout, power-of-two range scales and wave helpers.
 //
 // Staging.  The MFMA kernels compute with fp16 operands (11 significant bits)

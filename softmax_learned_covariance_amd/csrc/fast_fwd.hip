@@ -1,4 +1,5 @@
-// Fused two-pass Parallax forward for gfx950 (head_dim 128, bf16 inputs, fp16 MFMA).
+// Fused two-pass Parallax forward for gfx950 (head_dim 128, or 64 zero-padded to 128; bf16 inputs, fp16 MFMA),
+// and the one-pass probe-form forward.
 //
 // What it computes (gist.science technical summary of "Parallax: Parameterized
 // Local Linear Attention for Language Modeling", "Core mechanism": softmax
