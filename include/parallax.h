@@ -173,8 +173,8 @@ size_t parallax_attn_bwd_probe_workspace(const plx_attn_desc* desc);
  *   dout  [B][Tq][Hq][d]   dtype desc->dtype
  *   dq, drho [B][Tq][Hq][d] fp32     dk, dv [B][Tk][Hkv][d] fp32 (summed over the query heads of each group)
  * Every gradient is overwritten.  Results are deterministic.
- * Supported: bf16, head_dim 128 or 64, heads_q / heads_kv in {1, 2, 4}, p_per_query 0; any other valid
- * desc returns PLX_ERR_UNSUPPORTED.  Empty problems write zero gradients.
+ * Supported: bf16, head_dim 128 or 64, heads_q / heads_kv in {1, 2, 4, 8}, p_per_query 0; any other
+ * valid desc returns PLX_ERR_UNSUPPORTED.  Empty problems write zero gradients.
  */
 plx_status parallax_attn_bwd_probe(const plx_attn_desc* desc,
                                    const void* q, const void* k, const void* v, const void* rho,

@@ -196,7 +196,9 @@ template <bool SPLIT, bool DQ_PASS, bool PROBE>
 __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
   __shared__ RowTiles T;
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, ql = l & 31, hh = l >> 5;
-  const int npairs = p.B * p.Hkv;
+  // four waves: with 8 query heads per kv head, two blocks share a group, four heads each
+  const int hsplit = p.G > 4 ? p.G / 4 : 1;
+  const int npairs = p.B * p.Hkv * hsplit;
   int pair, rb;
   {
     const int id = blockIdx.x;
@@ -209,9 +211,9 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
       pair = id % npairs;
     }
   }
-  const int b = pair / p.Hkv, g = pair % p.Hkv;
-  const int wph = 4 / p.G;
-  const int h = g * p.G + w / wph;
+  const int b = pair / (p.Hkv * hsplit), g = pair % (p.Hkv * hsplit) / hsplit, hpart = pair % hsplit;
+  const int wph = p.G > 4 ? 1 : 4 / p.G;
+  const int h = g * p.G + 4 * hpart + w / wph;
   const int r0 = p.row_begin + rb * p.rows_per_block;
   const int i0 = r0 + (w % wph) * 32;
   const int row = i0 + ql;
@@ -1322,7 +1324,7 @@ __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
   // Query tiles are visited from the last one down, the heads of the group interleaved: the blocks
   // of one (batch, kv head) running together then read the same tile at about the same time, so it
   // comes from L2 instead of once per block from memory.
-  const int gsh = p.G == 4 ? 2 : p.G == 2 ? 1 : 0;   // the fast path has G in {1, 2, 4}
+  const int gsh = p.G == 8 ? 3 : p.G == 4 ? 2 : p.G == 2 ? 1 : 0;   // the fast path has G in {1, 2, 4, 8}
   auto tile_head = [&](int it) { return g * p.G + (it & (p.G - 1)); };
   auto tile_row = [&](int it) { return (qt0 + n_qt - 1 - (it >> gsh)) * 32; };
   auto tile_any = [&](int it) {
@@ -1837,7 +1839,8 @@ int bwd_split(const Geom& g) { return 256 < g.Tq ? 256 : g.Tq; }
 
 bool fast_bwd_supported(const Geom& g) {
   const int G = g.Hq / g.Hkv;
-  return g.bf16 && (g.d == kD || g.d == 64) && !g.p_per_query && (G == 1 || G == 2 || G == 4) && g.B > 0 && g.Tq > 0 &&
+  return g.bf16 && (g.d == kD || g.d == 64) && !g.p_per_query && (G == 1 || G == 2 || G == 4 || G == 8) && g.B > 0 &&
+         g.Tq > 0 &&
          g.Tk > 0;
 }
 
@@ -1914,7 +1917,8 @@ hipError_t bwd_impl(const Geom& g, const BwdArgs& a, int split_rows, void* ws, h
   rp.causal = g.causal;
   rp.window = g.window;
   rp.scale = g.scale;
-  rp.rows_per_block = 32 * 4 / G;
+  rp.rows_per_block = G > 4 ? 32 : 32 * 4 / G;   // split-row kernel: four waves of 32 rows
+  const int hsplit = G > 4 ? G / 4 : 1;           // ... and two blocks per group when G = 8
   // The kernels for rows < split (few blocks, bound by latency) run on a side lane beside the main
   // ones: the row kernel beside the du kernel, the key kernel beside the dq kernel.  The fp16 query
   // tiles of q and dout are first read by the key-major kernel, so their staging also runs on the
@@ -1933,9 +1937,11 @@ hipError_t bwd_impl(const Geom& g, const BwdArgs& a, int split_rows, void* ws, h
     r.row_end = split;
     r.n_rb = (split + r.rows_per_block - 1) / r.rows_per_block;
     if (probe)
-      hipLaunchKernelGGL((k_bwd_rows_fast<true, true, true>), dim3(g.B * g.Hkv * r.n_rb), dim3(256), 0, side.stream, r);
+      hipLaunchKernelGGL((k_bwd_rows_fast<true, true, true>), dim3(g.B * g.Hkv * hsplit * r.n_rb), dim3(256), 0,
+                         side.stream, r);
     else
-      hipLaunchKernelGGL((k_bwd_rows_fast<true, true, false>), dim3(g.B * g.Hkv * r.n_rb), dim3(256), 0, side.stream, r);
+      hipLaunchKernelGGL((k_bwd_rows_fast<true, true, false>), dim3(g.B * g.Hkv * hsplit * r.n_rb), dim3(256), 0,
+                         side.stream, r);
   }
   if (split < g.Tq) {
     RowParams r = rp;

@@ -259,7 +259,7 @@ plx_status parallax_attn_bwd_probe(const plx_attn_desc* desc, const void* q, con
   gs.B = gs.Tq = gs.Tk = 1;
   if (!plx::fast_probe_bwd_supported(gs))
     return fail(PLX_ERR_UNSUPPORTED,
-                "%s: only bf16, head_dim 128 or 64, heads_q/heads_kv in {1,2,4} and p_per_query 0 are supported",
+                "%s: only bf16, head_dim 128 or 64, heads_q/heads_kv in {1,2,4,8} and p_per_query 0 are supported",
                 what);
   const bool rows = g.B > 0 && g.Tq > 0;
   const bool keys = g.B > 0 && g.Tk > 0;

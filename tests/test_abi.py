@@ -168,7 +168,7 @@ def test_probe_backward_validation(plx):
         return lib.parallax_attn_bwd_probe(ctypes.byref(desc), *args.values(), ws, nws, None)
 
     assert call(_desc(plx)) == E.PLX_ERR_UNSUPPORTED                      # fp32
-    assert call(_desc(plx, Hq=8, Hkv=1, **bf)) == E.PLX_ERR_UNSUPPORTED   # 8 query heads per group
+    assert call(_desc(plx, Hq=3, Hkv=1, **bf)) == E.PLX_ERR_UNSUPPORTED   # 3 query heads per group
     d = _desc(plx, **bf)
     need = lib.parallax_attn_bwd_probe_workspace(ctypes.byref(d))
     assert need > 0

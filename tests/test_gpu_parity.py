@@ -169,6 +169,8 @@ def test_bf16_backward_small(plx, T):
     (257, 257, True, 0, 16, -1),     # one query head per key/value head
     (257, 257, True, 0, 4, -1),      # four query heads per key/value head
     (300, 300, True, 0, 8, 0),       # smallest split: rows >= 16 on single fp16 operands
+    (300, 300, True, 0, 2, -1),      # eight query heads per key/value head
+    (129, 200, True, 64, 2, 0),      # eight heads per group, a window, smallest split
 ])
 def test_bf16_backward_masks_and_groups(plx, T, Tk, causal, window, Hkv, split):
     w = W.scaled(W.WORKLOADS["train06"], batch=2, seqlen_q=T, seqlen_k=Tk, heads_kv=Hkv)

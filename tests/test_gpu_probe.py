@@ -178,6 +178,7 @@ def _check_bwd(plx, w, causal=True, window=0, split=-1):
     (257, 257, True, 0, 16, -1),     # one query head per key/value head
     (257, 257, True, 0, 4, -1),      # four query heads per key/value head
     (300, 300, True, 0, 8, 0),       # smallest split: rows >= 16 on single fp16 operands
+    (300, 300, True, 0, 2, -1),      # eight query heads per key/value head
 ])
 def test_probe_backward_small(plx, T, Tk, causal, window, Hkv, split):
     w = W.scaled(W.WORKLOADS["train06"], batch=2, seqlen_q=T, seqlen_k=Tk, heads_kv=Hkv)
