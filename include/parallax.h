@@ -247,7 +247,7 @@ size_t parallax_attn_decode_paged_workspace(const plx_attn_desc* desc);
  * page_size must be a power of two (1 .. 65536) and num_pages >= 1.  Block-table entries outside
  * [0, num_pages) are clamped into the pool: that sequence's output is then wrong, but nothing is
  * read outside the caller's arrays.
- * Supported: bf16, head_dim 128 or 64, heads_q / heads_kv in {1, 2, 4}, p_per_query 0; any other
+ * Supported: bf16, head_dim 128 or 64, heads_q / heads_kv in {1, 2, 4, 8}, p_per_query 0; any other
  * valid desc returns PLX_ERR_UNSUPPORTED.  window as in parallax_attn_decode.
  */
 plx_status parallax_attn_decode_paged(const plx_attn_desc* desc, const void* q,

@@ -529,7 +529,7 @@ DecWs dec_layout(const Geom& g, void* ws) {
 
 bool fast_decode_supported(const Geom& g) {
   const int G = g.Hq / g.Hkv;
-  return g.bf16 && (g.d == kD || g.d == 64) && !g.p_per_query && (G == 1 || G == 2 || G == 4);
+  return g.bf16 && (g.d == kD || g.d == 64) && !g.p_per_query && (G == 1 || G == 2 || G == 4 || G == 8);
 }
 
 size_t fast_decode_workspace(const Geom& g) { return dec_layout(g, nullptr).bytes; }
@@ -539,7 +539,7 @@ namespace {
 // One pass kernel over every chunk of new tokens; rows per workgroup = G x (tokens in the chunk).
 template <bool PASS2, bool PAGED>
 void launch_pass(DecParams p, const dim3& grid, hipStream_t stream) {
-  const int per = kMaxG / p.G;   // tokens per chunk at most (G is 1, 2 or 4)
+  const int per = kMaxG / p.G;   // tokens per chunk at most (G is 1, 2, 4 or 8)
   for (int t0 = 0; t0 < p.T; t0 += p.Tc) {
     int tc = per;
     while (tc > p.T - t0) tc >>= 1;   // rows = G x tc stays 1, 2, 4 or 8

@@ -390,7 +390,7 @@ plx_status parallax_attn_decode_paged(const plx_attn_desc* desc, const void* q, 
   if (num_pages < 1) return fail(PLX_ERR_INVALID, "%s: num_pages=%d < 1", what, num_pages);
   if (!plx::fast_decode_supported(g))
     return fail(PLX_ERR_UNSUPPORTED,
-                "%s: only bf16, head_dim 128 or 64, heads_q/heads_kv in {1,2,4} and p_per_query 0 are supported",
+                "%s: only bf16, head_dim 128 or 64, heads_q/heads_kv in {1,2,4,8} and p_per_query 0 are supported",
                 what);
   g.causal = 1;
   const size_t need = plx::fast_decode_workspace(g);

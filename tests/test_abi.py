@@ -196,7 +196,7 @@ def test_paged_decode_validation(plx):
     assert b"page_size" in lib.parallax_last_error()
     assert call(d, num_pages=0) == E.PLX_ERR_INVALID
     assert call(_desc(plx, Tq=1)) == E.PLX_ERR_UNSUPPORTED                       # fp32
-    assert call(_desc(plx, Hq=8, Hkv=1, **bf)) == E.PLX_ERR_UNSUPPORTED          # 8 query heads per group
+    assert call(_desc(plx, Hq=3, Hkv=1, **bf)) == E.PLX_ERR_UNSUPPORTED          # 3 query heads per group
     assert call(d, table=None) == E.PLX_ERR_INVALID
     assert call(d, q=None) == E.PLX_ERR_INVALID
     need = lib.parallax_attn_decode_paged_workspace(ctypes.byref(d))

@@ -382,9 +382,9 @@ def test_decode_seqlens_and_window(plx):
         assert rel_err(host(out), ref) <= BF16_TOL
 
 
-@pytest.mark.parametrize("Hkv", [16, 4])
+@pytest.mark.parametrize("Hkv", [16, 4, 2])
 def test_decode_groups(plx, Hkv):
-    """Decode with one and with four query heads per key/value head."""
+    """Decode with one, four and eight query heads per key/value head."""
     w = W.scaled(W.WORKLOADS["decode"], batch=3, seqlen_k=2100, heads_kv=Hkv)
     _announce(f"decode Hkv={Hkv}")
     q, kc, vc, P = W.make_inputs(w, device="cuda")
@@ -498,7 +498,7 @@ def _multi_token_ref(q, kc, vc, P, seqlens, window):
 
 
 @pytest.mark.parametrize("T,Hkv,window", [(2, 8, 0), (3, 8, 100), (4, 8, 0), (5, 8, 0), (5, 16, 0), (8, 16, 50),
-                                          (3, 16, 64), (3, 4, 0)])
+                                          (3, 16, 64), (3, 4, 0), (3, 2, 0)])
 def test_decode_multi_token(plx, T, Hkv, window):
     """T new tokens per sequence (chunks of up to 8 / G tokens per workgroup), ragged lengths including one
     shorter than T and an empty sequence, with and without a window; the paged cache agrees bit for bit."""
