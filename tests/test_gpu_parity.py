@@ -544,3 +544,35 @@ def test_decode_head_dim_64(plx):
     assert rel_err(host(out), oracle.decode(host(q), host(kc), host(vc), host(P), seqlens=sl)) <= BF16_TOL
     ref3 = _multi_token_ref(host(q3), host(kc), host(vc), host(P), sl, 200)
     assert rel_err(host(out3), ref3) <= BF16_TOL
+
+
+def test_full_size_multi_token_decode_sampled(plx):
+    """Four new tokens for each of 64 sequences of 32768 keys (two-head groups: one chunk of eight rows);
+    sampled sequences against the forward oracle over their prefix."""
+    w = W.WORKLOADS["decode"]
+    _announce("full-size four-token decode (sampled sequences)")
+    _, kc, vc, P = W.make_inputs(w, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(88)
+    q = torch.randn((w.batch, 4, w.heads_q, w.head_dim), generator=g, device="cuda").to(torch.bfloat16)
+    out = plx.parallax_attn_decode(q, kc, vc, P)
+    torch.cuda.synchronize()
+    bsel = [0, 47]
+    full = np.full(len(bsel), w.seqlen_k)
+    ref = _multi_token_ref(host(q[bsel]), host(kc[bsel]), host(vc[bsel]), host(P), full, 0)
+    assert rel_err(host(out[bsel]), ref) <= BF16_TOL
+
+
+def test_full_size_head_dim_64_sampled(plx):
+    """The 1.7B layer's shape at head dim 64 (B=2, T=8192): forward on the MFMA path, sampled rows."""
+    w = W.scaled(W.WORKLOADS["layer17"], head_dim=64)
+    _announce("full-size forward d=64 (sampled rows)")
+    q, k, v, P = W.make_inputs(w, device="cuda")
+    out, lse, _, _ = _run_fwd(plx, q, k, v, P)
+    uniform, rows = _sample_rows(w.seqlen_q, 29)
+    bsel = [0, w.batch - 1]
+    ref, ref_lse, _, _ = oracle.fwd(host(q[bsel]), host(k[bsel]), host(v[bsel]), host(P), causal=True, rows=rows)
+    got = host(out[bsel])
+    e = sampled_rel_err(got[:, rows], ref[:, rows], ref[:, uniform])
+    assert e <= BF16_TOL, e
+    assert np.max(np.abs(host(lse[bsel])[:, :, rows] - ref_lse[:, :, rows])) <= 1e-3
