@@ -88,7 +88,7 @@ struct __align__(16) DecTiles {
   float corr[kMaxG];
 };
 
-// One K and V tile in LDS (about 41 KB with the rest, so three workgroups fit a CU; measured, three
+// One K and V tile in LDS (about 47 KB with the rest, so three workgroups fit a CU; measured, three
 // stream the cache faster than two with double-buffered tiles, and than four).  The next tile (64
 // keys x 16 chunks of 16 bytes each, 4 + 4 chunks per thread) is fetched into registers at the start
 // of an iteration and stored into LDS after the current tile's work and a barrier, so that the loads
