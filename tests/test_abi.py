@@ -232,3 +232,15 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "--gpus 1" in r.stderr
     assert r.stdout.strip() == ""
+
+
+def test_traffic_summary_rows_parse():
+    """Every kernel row of the committed HBM-traffic summary has the six fields bench.py reads (name,
+    kernel, FETCH KiB, WRITE KiB, bytes, source hash), so no stored figure is silently dropped."""
+    path = os.path.join(ROOT, "profiles", "traffic_layer17_decode.txt")
+    rows = [ln.split() for ln in open(path) if ln.strip() and not ln.startswith("#") and not ln.startswith("name")]
+    assert rows
+    for f in rows:
+        assert len(f) == 6, f
+        float(f[2]), float(f[3]), float(f[4])
+        assert len(f[5]) == 16
