@@ -32,9 +32,19 @@
  *     then returns a description (thread-local).
  *   - Work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL is
  *     the default stream).  Faults during execution surface at the caller's next
- *     synchronisation, not as a status here.  Apart from the thread-local
- *     profiling hook below, the library keeps no state between calls and is
- *     safe to call from several threads.
+ *     synchronisation, not as a status here.  Every call is safe from several
+ *     threads.
+ *   - State kept between calls: the thread-local profiling hook below, and per
+ *     device one helper stream (non-blocking, default priority) with two events,
+ *     created by the first forward or backward on that device that uses it and
+ *     kept until the process ends.  The forward and backward run their small
+ *     first-row kernels on it, ordered after everything the call enqueued on
+ *     `hip_stream` before them; before the call returns, `hip_stream` is made to
+ *     wait for them, so later work on `hip_stream` sees the call complete, as
+ *     with any single-stream call.  Calls on different caller
+ *     streams or threads share the helper stream, so their side kernels can run
+ *     one after another; this orders work and never changes a result.  If the
+ *     helper stream cannot be created, everything runs on `hip_stream`.
  */
 #ifndef PARALLAX_H
 #define PARALLAX_H
@@ -46,7 +56,7 @@
 extern "C" {
 #endif
 
-#define PARALLAX_ABI_VERSION 2
+#define PARALLAX_ABI_VERSION 3
 
 typedef enum {
   PLX_OK = 0,
@@ -92,8 +102,8 @@ typedef enum {
  * hipEvent_t) on their stream immediately before launching the kernel
  * `kernel` (a plx_kernel) and `after` immediately after it, so the caller can
  * time that one kernel with hipEventElapsedTime.  Calls that do not launch that
- * kernel record nothing.  Pass NULL, NULL to turn it off.  This thread-local
- * setting is the library's only state.
+ * kernel record nothing.  Pass NULL, NULL to turn it off.  The setting is
+ * thread-local.
  */
 void parallax_set_kernel_events(int kernel, void* before, void* after);
 
@@ -183,7 +193,14 @@ plx_status parallax_attn_bwd_probe(const plx_attn_desc* desc,
                                    float* dq, float* dk, float* dv, float* drho,
                                    void* workspace, size_t workspace_bytes, void* hip_stream);
 
-/* Backward.  Bytes of workspace needed for `desc`; returns 0 for an invalid desc. */
+/*
+ * Backward.  Bytes of workspace needed for `desc`; returns 0 for an invalid desc.
+ * On the bf16 fast path the workspace holds, besides O(B*T*H*d) staging copies, one fp16 value per
+ * visible (query, key) pair and query head: the key-major kernel stores its ds tiles for the
+ * query-major dq kernel.  The size therefore grows as 2 * B * Hq * Tq_pad * Tk_pad bytes (Tq_pad, Tk_pad:
+ * Tq, Tk rounded up to 32 and 64): about 4.3 GB at B = 2, Hq = 16, T = 8192, and 137 GB at B = 1, Hq = 16,
+ * T = 65536.  Callers that cannot provide it can split the batch or the heads over several calls.
+ */
 size_t parallax_attn_bwd_workspace(const plx_attn_desc* desc);
 
 /*
@@ -239,8 +256,11 @@ size_t parallax_attn_decode_paged_workspace(const plx_attn_desc* desc);
  * block_table[b][j / page_size].
  *   q            [B][T][Hq][d], T = desc->seqlen_q  dtype desc->dtype
  *   k_pages, v_pages [num_pages][page_size][Hkv][d]   dtype desc->dtype
- *   block_table  [B][max_pages] int32 device array, max_pages = ceil(desc->seqlen_k / page_size);
+ *   block_table  [B][block_table_stride] int32 device array: row b lists the pages of sequence b;
  *                only the entries that cover keys < seqlens_k[b] are read
+ *   block_table_stride  entries per row of block_table (a table sized for the cache's capacity may be
+ *                wider than the sequences need); must be >= ceil(desc->seqlen_k / page_size), else
+ *                PLX_ERR_INVALID
  *   seqlens_k    [B] int32 device array (nullable: every sequence has desc->seqlen_k keys)
  *   P [Hq][d][d]     out [B][T][Hq][d] fp32 (bf16 when desc->out_dtype is PLX_BF16)     cor [B][T][Hq] (nullable)
  * New tokens as in parallax_attn_decode; desc->seqlen_k is the longest sequence the table can describe.
@@ -253,7 +273,8 @@ size_t parallax_attn_decode_paged_workspace(const plx_attn_desc* desc);
 plx_status parallax_attn_decode_paged(const plx_attn_desc* desc, const void* q,
                                       const void* k_pages, const void* v_pages,
                                       int32_t num_pages, int32_t page_size,
-                                      const int32_t* block_table, const int32_t* seqlens_k,
+                                      const int32_t* block_table, int32_t block_table_stride,
+                                      const int32_t* seqlens_k,
                                       const void* P, void* out, float* cor,
                                       void* workspace, size_t workspace_bytes, void* hip_stream);
 

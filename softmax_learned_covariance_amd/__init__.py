@@ -72,8 +72,8 @@ SIGNATURES = {
     "parallax_attn_decode_workspace": (_sz, [_DESC]),
     "parallax_attn_decode": (_st, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "parallax_attn_decode_paged_workspace": (_sz, [_DESC]),
-    "parallax_attn_decode_paged": (_st, [_DESC, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp, _vp,
-                                         _vp, _vp, _sz, _vp]),
+    "parallax_attn_decode_paged": (_st, [_DESC, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int32,
+                                         _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 
 
@@ -298,7 +298,8 @@ def parallax_attn_decode(q, k_cache, v_cache, P, seqlens=None, window=0, scale=N
 def parallax_attn_decode_paged(q, k_pages, v_pages, block_table, P, seqlens=None, seqlen_k=None, window=0,
                                scale=None, out_dtype=torch.float32, cor=False):
     """Decode against a paged cache: q [B,Hq,d] or [B,T,Hq,d]; pages [num_pages,page_size,Hkv,d]; block_table
-    int32 [B,max_pages]; seqlens int32 [B] or None; seqlen_k defaults to max_pages * page_size.
+    int32 [B,max_pages] (its width is passed as the row stride, so it may exceed what seqlen_k needs); seqlens int32
+    [B] or None; seqlen_k defaults to max_pages * page_size.
     Returns out shaped like q (see include/parallax.h)."""
     lead = q.shape[:-2]
     B, Hq, d = q.shape[0], q.shape[-2], q.shape[-1]
@@ -327,7 +328,8 @@ def parallax_attn_decode_paged(q, k_pages, v_pages, block_table, P, seqlens=None
     nws = lib.parallax_attn_decode_paged_workspace(ctypes.byref(desc))
     ws = _workspace(nws, dev)
     _check(lib.parallax_attn_decode_paged(ctypes.byref(desc), _ptr(q), _ptr(k_pages), _ptr(v_pages), num_pages,
-                                          page_size, _ptr(block_table), _ptr(seqlens), _ptr(P), _ptr(out),
+                                          page_size, _ptr(block_table), block_table.shape[1], _ptr(seqlens),
+                                          _ptr(P), _ptr(out),
                                           _ptr(ratio), _ptr(ws), nws, _stream()))
     return (out, ratio) if cor else out
 

@@ -27,6 +27,9 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC,
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
+    # inline assembly that names a register the compiler reserves (m0, exec, vcc, ...) is undefined
+    # behaviour: refuse to build it
+    "-Werror=inline-asm",
 ]
 
 

@@ -45,6 +45,26 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float mx(const uint32_t* maxbits, int slot) { return __uint_as_float(maxbits[slot]); }
 
+// Per-row statistics the key-major kernels bound their products with (see RowParams::rowmax).  After
+// the row pass, a suffix maximum along the rows turns entry i into the maximum over rows >= i, and the
+// rows that see key j are rows >= j - (Tk - Tq) (causal), so one load per statistic bounds a key.
+enum RowStat { kStatG = 0, kStatU = 1, kStatE = 2, kStat1mA = 3, kStatDelta = 4, kRowStats = 5 };
+
+__device__ __forceinline__ void rowmax_put(float* rowmax, int b, int g, int Hkv, int Tq_pad, int row, int slot, float v) {
+  atomicMax(reinterpret_cast<uint32_t*>(rowmax) + ((static_cast<int64_t>(b) * Hkv + g) * kRowStats + slot) * Tq_pad + row,
+            __float_as_uint(v));
+}
+
+// Sum of squares of the 64 values of 8 fp16 operands (the lane's half of a 128-element row).
+__device__ __forceinline__ float sumsq8x8(const f16x8 (&x)[8]) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s = fmaf(static_cast<float>(x[i][j]), static_cast<float>(x[i][j]), s);
+  return s;
+}
+
 __device__ __forceinline__ void load4_bf16(const u16* src, float* dst) {
   const uint2 w = *reinterpret_cast<const uint2*>(src);
   dst[0] = __uint_as_float(w.x << 16);
@@ -99,6 +119,9 @@ struct RowParams {
   uint32_t* maxbits;
   float *dq, *u32, *dkb32, *x32, *du32, *st_alpha, *st_delta;
   float* rstat;        // per 32-row tile: lse (log2 units), 1 - alpha, Delta of each row, [B][Hq][Tq_pad / 32][3][32]
+  const float *knorm, *vnorm;   // [B][Hkv][Tk_pad] running maxima of the key and value norms (staging)
+  float* rowmax;       // [B][Hkv][kRowStats][Tq_pad]: per row, the largest |g|, |u|, |dkbar|, |1 - alpha|, |Delta|
+                       // over the group's query heads (atomicMax of non-negative float bits)
   // probe form (u = -rho supplied per row, no projector): rho, rho . kbar from the forward, drho out
   const u16* rho;
   const float* rk;
@@ -225,8 +248,6 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
   const float sG = range_scale(mx(MB, kMaxDO));
   const float maxK = mx(MB, kMaxK);
   const float cS = p.scale * kLog2e / (sQ * sK);
-  const float boundG = 128.f * mx(MB, kMaxDO) * mx(MB, kMaxV);
-  const float sPG = range_scale(PROBE ? 2.f * boundG : boundG);   // probe form: |G - g.o| <= 2 boundG
 
   const int64_t qoff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * p.D;   // caller rows
   const int64_t woff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * kD;    // workspace rows
@@ -251,6 +272,13 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
   f16x8 qB[8], gB[8];
   load_row_operand(p.q + qoff, row_ok, hh, sQ, qB, p.D);
   load_row_operand(p.dout + qoff, row_ok, hh, sG, gB, p.D);
+  // |G_j| = |g.v_j| <= |g| |v_j| with the largest value norm among the keys the row sees (a running
+  // maximum along the sequence), so the scale of p G follows the row instead of the tensors' largest
+  // entries (probe form: |G - g.o| <= 2 |g| max |v_j|)
+  const float gnorm = sqrtf(xor32_sum(sumsq8x8(gB))) / sG;
+  const int64_t nbase = (static_cast<int64_t>(b) * p.Hkv + g) * p.Tk_pad;
+  const float pmV = r_kend > r_kbeg ? p.vnorm[nbase + r_kend - 1] : 0.f;
+  const float sPG = range_scale(PROBE ? 2.f * gnorm * pmV : gnorm * pmV);
 
   // probe form: du = sum_j p_j (G_j - g.o) k_j directly (kbar is not an input), so g.o comes first
   float go_pre = 0.f;
@@ -322,7 +350,7 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
   row_dots(p, qoff, row_ok, hh, go, gout, gabs);
   if constexpr (PROBE) go = go_pre;   // the value du was formed with
   f32x16 accU[4], accPD[4];
-  float alpha = 0.f, dkk = 0.f, umax = 0.f, emax = 0.f, u1 = 0.f, e1 = 0.f;
+  float alpha = 0.f, dkk = 0.f, umax = 0.f, emax = 0.f, u1 = 0.f, e1 = 0.f, u2 = 0.f, e2 = 0.f;
   if constexpr (PROBE) {
     const float fdu = 1.f / (sPG * sK);
 #pragma unroll
@@ -334,11 +362,15 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
       for (int r = 0; r < 16; ++r) {
         umax = fmaxf(umax, fabsf(accU[mt][r]));
         emax = fmaxf(emax, fabsf(accPD[mt][r]));
+        u2 = fmaf(accU[mt][r], accU[mt][r], u2);
+        e2 = fmaf(accPD[mt][r], accPD[mt][r], e2);
         u1 += fabsf(accU[mt][r]);
         e1 += fabsf(accPD[mt][r]);
       }
     umax = xor32_max(umax);
     emax = xor32_max(emax);
+    u2 = xor32_sum(u2);
+    e2 = xor32_sum(e2);
     u1 = xor32_sum(u1);
     e1 = xor32_sum(e1);
     const float rk = row_ok ? p.rk[soff] : 0.f;   // rho . kbar
@@ -438,6 +470,8 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
             dkk += dk * kbv[mt][r];
             umax = fmaxf(umax, fabsf(u));
             emax = fmaxf(emax, fabsf(dk));
+            u2 = fmaf(u, u, u2);
+            e2 = fmaf(dk, dk, e2);
             u1 += fabsf(u);
             e1 += fabsf(dk);
           }
@@ -454,6 +488,8 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
     dkk = xor32_sum(dkk);
     umax = xor32_max(umax);
     emax = xor32_max(emax);
+    u2 = xor32_sum(u2);
+    e2 = xor32_sum(e2);
     u1 = xor32_sum(u1);
     e1 = xor32_sum(e1);
   }
@@ -465,6 +501,9 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
     rs[0] = lse2;
     rs[32] = 1.f - alpha;
     rs[64] = delta;
+    const float st5[kRowStats] = {gnorm, sqrtf(u2), sqrtf(e2), fabsf(1.f - alpha), fabsf(delta)};
+#pragma unroll
+    for (int k = 0; k < kRowStats; ++k) rowmax_put(p.rowmax, b, g, p.Hkv, p.Tq_pad, row, k, st5[k]);
   }
   {
     // per-tensor maxima for the key-major pass (rows outside the range contribute 0)
@@ -488,8 +527,10 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
     tile_operand(accU[s >> 1], s & 1, sU, uB[s], SPLIT ? &uL[SPLIT ? s : 0] : nullptr);
     tile_operand(accPD[s >> 1], s & 1, sE, eB[s], SPLIT ? &eL[SPLIT ? s : 0] : nullptr);
   }
-  // |ds| <= |G| |tt| + |E| + |Delta| with |G| <= |g|_1 max|v|, |tt| <= |u|_1 max|k| + 1 + |alpha|, |E| <= |dkbar|_1 max|k|
-  const float bound_ds = gabs * mx(MB, kMaxV) * (u1 * maxK + 1.f + fabsf(alpha)) + e1 * maxK + fabsf(delta);
+  // |ds| <= |G| |tt| + |E| + |Delta| with |G| <= |g| max|v_j|, |tt| <= |u| max|k_j| + |1 - alpha|,
+  // |E| <= |dkbar| max|k_j|: Euclidean norms, and the largest key and value norms among the row's keys
+  const float pmK = r_kend > r_kbeg ? p.knorm[nbase + r_kend - 1] : 0.f;
+  const float bound_ds = gnorm * pmV * (sqrtf(u2) * pmK + fabsf(1.f - alpha)) + sqrtf(e2) * pmK + fabsf(delta);
   const float sDS = range_scale(bound_ds);
   const float fT = 1.f / (sU * sK), fE = 1.f / (sE * sK), fG = 1.f / (sG * sV);
   const float one_m_alpha = 1.f - alpha;
@@ -615,8 +656,6 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
   const float sV = range_scale(mx(MB, kMaxV)), sP = range_scale(mx(MB, kMaxP));
   const float sG = range_scale(mx(MB, kMaxDO));
   const float cS = p.scale * kLog2e / (sQ * sK);
-  const float boundG = 128.f * mx(MB, kMaxDO) * mx(MB, kMaxV);
-  const float sPG = range_scale(PROBE ? 2.f * boundG : boundG);   // probe form: |G - g.o| <= 2 boundG
 
   const int64_t qoff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * p.D;   // caller rows
   const int64_t woff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * kD;    // workspace rows
@@ -641,6 +680,13 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
   f16x8 qB[8], gB[8];
   load_row_operand(p.q + qoff, row_ok, hh, sQ, qB, p.D);
   load_row_operand(p.dout + qoff, row_ok, hh, sG, gB, p.D);
+  // |G_j| = |g.v_j| <= |g| |v_j| with the largest value norm among the keys the row sees (a running
+  // maximum along the sequence), so the scale of p G follows the row instead of the tensors' largest
+  // entries (probe form: |G - g.o| <= 2 |g| max |v_j|)
+  const float gnorm = sqrtf(xor32_sum(sumsq8x8(gB))) / sG;
+  const int64_t nbase = (static_cast<int64_t>(b) * p.Hkv + g) * p.Tk_pad;
+  const float pmV = r_kend > r_kbeg ? p.vnorm[nbase + r_kend - 1] : 0.f;
+  const float sPG = range_scale(PROBE ? 2.f * gnorm * pmV : gnorm * pmV);
 
   // probe form: du = sum_j p_j (G_j - g.o) k_j directly (kbar is not an input), so g.o comes first
   float go_pre = 0.f;
@@ -730,7 +776,7 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
   float go, gout, gabs;
   row_dots(p, qoff, row_ok, hh, go, gout, gabs);
   if constexpr (PROBE) go = go_pre;   // the value du was formed with
-  float alpha = 0.f, dkk = 0.f, umax = 0.f, emax = 0.f;
+  float alpha = 0.f, dkk = 0.f, umax = 0.f, emax = 0.f, u2 = 0.f, e2 = 0.f;
   if constexpr (PROBE) {
     // u = -rho, dkbar = (g.o) rho, drho = -du, dq starts at 0 (no projector term)
     const float fdu = 1.f / (sPG * sK);
@@ -747,6 +793,8 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
           dr[e] = -accDU[mt][4 * j + e] * fdu;
           umax = fmaxf(umax, fabsf(rv[e]));
           emax = fmaxf(emax, fabsf(go * rv[e]));
+          u2 = fmaf(rv[e], rv[e], u2);
+          e2 = fmaf(go * rv[e], go * rv[e], e2);
         }
         if (row_ok) {
           if (d < p.D) *reinterpret_cast<float4*>(p.drho + qoff + d) = float4{dr[0], dr[1], dr[2], dr[3]};
@@ -757,6 +805,8 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
       }
     umax = xor32_max(umax);
     emax = xor32_max(emax);
+    u2 = xor32_sum(u2);
+    e2 = xor32_sum(e2);
     const float rk = row_ok ? p.rk[soff] : 0.f;   // rho . kbar
     alpha = -rk;                                  // u . kbar
     dkk = go * rk;                                // dkbar . kbar
@@ -862,6 +912,8 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
             dkk += dk4[e] * k4[e];
             umax = fmaxf(umax, fabsf(u4[e]));
             emax = fmaxf(emax, fabsf(dk4[e]));
+            u2 = fmaf(u4[e], u4[e], u2);
+            e2 = fmaf(dk4[e], dk4[e], e2);
           }
           if (row_ok) {
             if (d < p.D) *reinterpret_cast<float4*>(p.dq + qoff + d) = float4{pd4[0], pd4[1], pd4[2], pd4[3]};
@@ -874,6 +926,8 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
     dkk = xor32_sum(dkk);
     umax = xor32_max(umax);
     emax = xor32_max(emax);
+    u2 = xor32_sum(u2);
+    e2 = xor32_sum(e2);
   }
   const float delta = gout + dkk;
   if (row_ok && hh == 0) {
@@ -883,6 +937,9 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
     rs[0] = lse2;
     rs[32] = 1.f - alpha;
     rs[64] = delta;
+    const float st5[kRowStats] = {gnorm, sqrtf(u2), sqrtf(e2), fabsf(1.f - alpha), fabsf(delta)};
+#pragma unroll
+    for (int k = 0; k < kRowStats; ++k) rowmax_put(p.rowmax, b, g, p.Hkv, p.Tq_pad, row, k, st5[k]);
   }
   {
     // per-tensor maxima for the key-major pass (rows outside the range contribute 0), combined over
@@ -918,6 +975,8 @@ struct KeyParams {
   const uint32_t* maxbits;
   float *dk, *dv;
   _Float16* ds;        // k_bwd_keys_pipe: ds tiles for the dq kernel
+  float* dsscale;      // [B][Hkv][Tk_pad / 32]: the scale C of each 32-key group's stored ds tiles
+  const float* rowmax; // suffix maxima of the row statistics (see RowParams::rowmax)
   const float* rstat;  // row statistics per 32-row tile (see RowParams)
   int64_t qstride;     // elements between the consecutive query-row copies q16, do16, u16, e16
   int B, Tq, Tk, Tk_pad, Tq_pad, lo_pad, Hq, Hkv, G, causal, window;
@@ -925,6 +984,41 @@ struct KeyParams {
   float scale;
   int row_lo, row_hi, accumulate, n_kb, key_hi;
 };
+
+// Scales of one key's products in the key-major kernels.  dk accumulates (p G) u + p dkbar + scale ds q
+// on one accumulator, so the three fp16 operands share a scale C: p G C / sU, p C / sE and
+// scale ds C / sQ against the staged u, dkbar and q (scales sU, sE, sQ); dv uses p tt cV.  The bounds
+// are Euclidean: |G_ij| <= |g_i| |v_j|, |tt_ij| <= |u_i| |k_j| + |1 - alpha_i|, |E_ij| <= |dkbar_i| |k_j|,
+// |ds_ij| <= |G| |tt| + |E| + |Delta_i| (p <= 1), with the key's own norms and, for each row statistic,
+// its largest value over the rows that see the key (the suffix maxima of RowParams::rowmax).  So one
+// row or key far larger than the rest changes only the scales of the keys it meets.
+struct KeyLaneScales {
+  float C, cV;
+  bool seen;   // some row can see the key
+};
+
+__device__ __forceinline__ KeyLaneScales key_lane_scales(const KeyParams& p, int b, int g, int key, bool key_ok,
+                                                         float kn, float vn, float sU, float sE, float sQ) {
+  const int off = p.Tk - p.Tq;
+  const int i_min = p.causal ? max(0, key - off) : 0;
+  KeyLaneScales r;
+  r.seen = key_ok && i_min < p.Tq;
+  float st[kRowStats] = {0.f, 0.f, 0.f, 0.f, 0.f};
+  if (r.seen) {
+    const float* rm = p.rowmax + (static_cast<int64_t>(b) * p.Hkv + g) * kRowStats * p.Tq_pad + i_min;
+#pragma unroll
+    for (int k = 0; k < kRowStats; ++k) st[k] = rm[k * p.Tq_pad];
+  }
+  const float gmax = vn * st[kStatG];
+  const float tmax = kn * st[kStatU] + st[kStat1mA];
+  const float emax = kn * st[kStatE];
+  const float dsmax = gmax * tmax + emax + st[kStatDelta];
+  r.cV = range_scale(tmax);
+  float C = range_scale(gmax) * sU;
+  C = fminf(C, 16384.f * sE);
+  r.C = fminf(C, range_scale(p.scale * dsmax) * sQ);
+  return r;
+}
 
 // One query tile in LDS: query-row tiles [16 chunks][32 rows][8] (chunk-major, as staged); the
 // column-layout operands are read from them with transpose loads (tr_cols).
@@ -1011,14 +1105,6 @@ __global__ __launch_bounds__(256) void k_bwd_keys_fast(KeyParams p) {
   const float sU = range_scale(maxU), sE = range_scale(maxE);
   const float cS = p.scale * kLog2e / (sQ * sK);
   const float fT = 1.f / (sU * sK), fE = 1.f / (sE * sK), fG = 1.f / (sG * sV);
-  const float boundG = 128.f * mx(MB, kMaxDO) * mx(MB, kMaxV);
-  const float boundT = 128.f * maxU * maxK + 1.f + mx(MB, kMaxAlpha);
-  const float boundDS = boundG * boundT + 128.f * maxE * maxK + mx(MB, kMaxDelta);
-  const float cV = range_scale(boundT);
-  float C = range_scale(boundG) * sU;
-  C = fminf(C, 16384.f * sE);
-  C = fminf(C, range_scale(p.scale * boundDS) * sQ);
-  const float c1 = C / sU, c2 = C / sE, c3 = p.scale * C / sQ;
 
   // this wave's key rows as B operands (d permuted, as staged)
   f16x8 kB[8], vB[8];
@@ -1032,6 +1118,10 @@ __global__ __launch_bounds__(256) void k_bwd_keys_fast(KeyParams p) {
       vB[s] = *reinterpret_cast<const f16x8*>(p.v16 + roff + s * (2 * kKeyTile * 8));
     }
   }
+  const KeyLaneScales ls = key_lane_scales(p, b, g, key, key_ok, sqrtf(xor32_sum(sumsq8x8(kB))) / sK,
+                                           sqrtf(xor32_sum(sumsq8x8(vB))) / sV, sU, sE, sQ);
+  const float C = ls.C, cV = ls.cV;
+  const float c1 = C / sU, c2 = C / sE, c3 = p.scale * C / sQ;
   f32x16 accK[4], accV[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
@@ -1204,9 +1294,10 @@ __global__ __launch_bounds__(256) void k_bwd_keys_fast(KeyParams p) {
 // s_getreg operand for the SIMD_ID field (bits 5:4) of the HW_ID hardware register.
 constexpr int kHwIdSimd = (1 << 11) | (4 << 6) | 4;
 
-// Scales shared by the key-major kernels and the dq kernel (see the key kernel for the bounds).
+// Tensor scales shared by the key-major kernel and the dq kernel (the products' scales are per key,
+// key_lane_scales).
 struct KeyScales {
-  float sQ, sK, sV, sG, sU, sE, cS, fT, fE, fG, cV, C, c1, c2, c3;
+  float sQ, sK, sV, sG, sU, sE, cS, fT, fE, fG;
 };
 
 __device__ __forceinline__ KeyScales key_scales(const uint32_t* MB, float scale) {
@@ -1215,24 +1306,12 @@ __device__ __forceinline__ KeyScales key_scales(const uint32_t* MB, float scale)
   k.sK = range_scale(mx(MB, kMaxK));
   k.sV = range_scale(mx(MB, kMaxV));
   k.sG = range_scale(mx(MB, kMaxDO));
-  const float maxU = mx(MB, kMaxU), maxE = mx(MB, kMaxDKB), maxK = mx(MB, kMaxK);
-  k.sU = range_scale(maxU);
-  k.sE = range_scale(maxE);
+  k.sU = range_scale(mx(MB, kMaxU));
+  k.sE = range_scale(mx(MB, kMaxDKB));
   k.cS = scale * kLog2e / (k.sQ * k.sK);
   k.fT = 1.f / (k.sU * k.sK);
   k.fE = 1.f / (k.sE * k.sK);
   k.fG = 1.f / (k.sG * k.sV);
-  const float boundG = 128.f * mx(MB, kMaxDO) * mx(MB, kMaxV);
-  const float boundT = 128.f * maxU * maxK + 1.f + mx(MB, kMaxAlpha);
-  const float boundDS = boundG * boundT + 128.f * maxE * maxK + mx(MB, kMaxDelta);
-  k.cV = range_scale(boundT);
-  float C = range_scale(boundG) * k.sU;
-  C = fminf(C, 16384.f * k.sE);
-  C = fminf(C, range_scale(scale * boundDS) * k.sQ);
-  k.C = C;
-  k.c1 = C / k.sU;
-  k.c2 = C / k.sE;
-  k.c3 = scale * C / k.sQ;
   return k;
 }
 
@@ -1248,6 +1327,7 @@ struct __align__(16) KeyTiles3 {
   _Float16 r[3][4][32 * kD];   // q, dO, u, e query-row tiles, three buffers
   f16x8 x[4][4][2][64];        // exchange: per key group p G c1, p c2, ds c3, p tt cV
   float stat[3][3][32];        // lse (log2 units), 1 - alpha, Delta of the tile's rows
+  float ksc[4][2][32];         // per key group: its C (entry 0) and each key's cV (set by the V waves)
 };
 static_assert(sizeof(KeyTiles3) <= 160 * 1024, "LDS");
 
@@ -1347,6 +1427,19 @@ __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
       kB[s] = *reinterpret_cast<const f16x8*>(p.k16 + roff + s * (2 * kKeyTile * 8));
       vB[s] = *reinterpret_cast<const f16x8*>(p.v16 + roff + s * (2 * kKeyTile * 8));
     }
+    // The dk products of the group's 32 keys share one scale, the smallest C among its keys that some
+    // row sees (the stored ds tiles then hold one scale per group); dv takes each key's own cV.
+    const KeyLaneScales kls = key_lane_scales(p, b, g, key, key_ok, sqrtf(xor32_sum(sumsq8x8(kB))) / ks.sK,
+                                              sqrtf(xor32_sum(sumsq8x8(vB))) / ks.sV, ks.sU, ks.sE, ks.sQ);
+    float cgrp = kls.seen ? kls.C : INFINITY;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) cgrp = fminf(cgrp, __shfl_xor(cgrp, o, 64));
+    if (cgrp == INFINITY) cgrp = 1.f;   // no row sees any key of the group: nothing is accumulated
+    cgrp = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(cgrp)));   // (the builtin takes an int)
+    const float c1 = cgrp / ks.sU, c2 = cgrp / ks.sE, c3 = p.scale * cgrp / ks.sQ, cV = kls.cV;
+    if (hh == 0) T.ksc[grp][1][ql] = cV;
+    if (l == 0) T.ksc[grp][0][0] = cgrp;
+    if (l == 0 && jw < p.Tk_pad) p.dsscale[(static_cast<int64_t>(b) * p.Hkv + g) * (p.Tk_pad / 32) + jw / 32] = cgrp;
     vm_wait_all();
     for (int it = 0; it <= total; ++it) {
       const int buf = it % 3;
@@ -1422,17 +1515,17 @@ __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
           f16x8 o;
 #pragma unroll
           for (int e = 0; e < 8; ++e) w[e] = pr[8 * t + e] * Gt[8 * t + e];
-          to_operand(w, ks.c1, o, nullptr);
+          to_operand(w, c1, o, nullptr);
           T.x[grp][0][t][l] = o;
-          to_operand(&pr[8 * t], ks.c2, o, nullptr);
+          to_operand(&pr[8 * t], c2, o, nullptr);
           T.x[grp][1][t][l] = o;
 #pragma unroll
           for (int e = 0; e < 8; ++e) w[e] = pr[8 * t + e] * E[8 * t + e];
-          to_operand(w, ks.c3, o, nullptr);
+          to_operand(w, c3, o, nullptr);
           T.x[grp][2][t][l] = o;
 #pragma unroll
           for (int e = 0; e < 8; ++e) w[e] = pr[8 * t + e] * Tt[8 * t + e];
-          to_operand(w, ks.cV, o, nullptr);
+          to_operand(w, cV, o, nullptr);
           T.x[grp][3][t][l] = o;
         }
       }
@@ -1507,7 +1600,7 @@ __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
       __syncthreads();
     }
     if (key_ok) {
-      const float fv = 1.f / (ks.sG * ks.cV);
+      const float fv = 1.f / (ks.sG * T.ksc[grp][1][ql]);
       float* dvr = p.dv + ((static_cast<int64_t>(b) * p.Tk + key) * p.Hkv + g) * p.D;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -1522,7 +1615,7 @@ __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
           }
           *reinterpret_cast<float4*>(dvr + d) = vv;
         }
-      const float fk = 1.f / ks.C;
+      const float fk = 1.f / T.ksc[grp][0][0];
       float* dkr = p.dk + ((static_cast<int64_t>(b) * p.Tk + key) * p.Hkv + g) * p.D;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -1548,6 +1641,7 @@ __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
 // (A operand ordering, keys permuted within 16) from memory one key tile ahead.
 struct DqParams {
   const _Float16 *ds, *k16t;
+  const float* dsscale;   // per 32-key group: the scale C of its stored ds tiles
   const uint32_t* maxbits;
   float* dq;
   int B, Tq, Tk, Tk_pad, Tq_pad, Hq, Hkv, G, causal, window, row_lo, row_hi, row_begin, rows_per_block, n_rb;
@@ -1612,6 +1706,21 @@ __global__ __launch_bounds__(512) void k_bwd_dq(DqParams p) {
       lds_dma16(p.k16t + tb + i * 512 + l * 8, &T.kt[buf][i * 512]);
     }
   };
+  // Each 32-key group stored its ds tiles at its own scale C (dsscale).  The wave's rows take the
+  // smallest C among the groups they see, and every other group's operand is brought to it by an exact
+  // power of two <= 1 before its products.
+  const float* gsc = p.dsscale + (static_cast<int64_t>(b) * p.Hkv + g) * (p.Tk_pad / 32);
+  float cdq = INFINITY;
+  for (int kb32 = 2 * t_beg + l; kb32 < 2 * t_end; kb32 += 64)
+    if (vis(kb32)) cdq = fminf(cdq, gsc[kb32]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) cdq = fminf(cdq, __shfl_xor(cdq, o, 64));
+  if (cdq == INFINITY) cdq = 1.f;   // no stored tile
+  float fcur[2] = {1.f, 1.f}, fnxt[2] = {1.f, 1.f};
+  auto load_f = [&](int kt, float (&f)[2]) {
+#pragma unroll
+    for (int kbh = 0; kbh < 2; ++kbh) f[kbh] = cdq / gsc[2 * kt + kbh];
+  };
   f32x16 acc[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x16{};
@@ -1619,6 +1728,7 @@ __global__ __launch_bounds__(512) void k_bwd_dq(DqParams p) {
   if (t_beg < t_end) {
     dma_k(t_beg, 0);
     load_ds(t_beg, dcur);
+    load_f(t_beg, fcur);
   }
   lds_dma_wait();
   __syncthreads();
@@ -1627,25 +1737,30 @@ __global__ __launch_bounds__(512) void k_bwd_dq(DqParams p) {
     if (kt + 1 < t_end) {
       dma_k(kt + 1, buf ^ 1);
       load_ds(kt + 1, dnxt);
+      load_f(kt + 1, fnxt);
     }
 #pragma unroll
     for (int kbh = 0; kbh < 2; ++kbh) {
       if (vis(2 * kt + kbh)) {
+        const _Float16 f = static_cast<_Float16>(fcur[kbh]);
+        const f16x8 d0 = dcur[2 * kbh] * f, d1 = dcur[2 * kbh + 1] * f;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-            acc[nt] = mfma(lds_cols(T.kt[buf], 32 * nt + ql, 4 * kbh + 2 * t + hh), dcur[2 * kbh + t], acc[nt]);
+        for (int nt = 0; nt < 4; ++nt) {
+          acc[nt] = mfma(lds_cols(T.kt[buf], 32 * nt + ql, 4 * kbh + hh), d0, acc[nt]);
+          acc[nt] = mfma(lds_cols(T.kt[buf], 32 * nt + ql, 4 * kbh + 2 + hh), d1, acc[nt]);
+        }
       }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) dcur[i] = dnxt[i];
+    fcur[0] = fnxt[0];
+    fcur[1] = fnxt[1];
     lds_dma_wait();
     __syncthreads();
   }
   const int row = q0 + ql;
   if (row >= p.row_lo && row < p.row_hi && row < p.Tq) {
-    const float fq = ks.sQ / (ks.C * ks.sK);
+    const float fq = ks.sQ / (cdq * ks.sK);
     float* dqr = p.dq + ((static_cast<int64_t>(b) * p.Tq + row) * p.Hq + h) * p.D;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
@@ -1798,6 +1913,9 @@ struct BwdWs {
   _Float16* ds;   // [B][Hq][Tq_pad / 32][Tk_pad / 32] tiles of 32 x 32 fp16
   float* rstat;   // [B][Hq][Tq_pad / 32][3][32]
   size_t rstat_n;
+  float* rowmax;  // [B][Hkv][kRowStats][Tq_pad]
+  size_t rowmax_n;
+  float* dsscale; // [B][Hkv][Tk_pad / 32]
   int Tq_pad, lo_rows, lo_pad, nchunks;
   size_t bytes;
 };
@@ -1829,6 +1947,9 @@ BwdWs bwd_layout(const Geom& g, int split, void* ws) {
   w.ds = reinterpret_cast<_Float16*>(base + ws_take(off, ds_bytes));
   w.rstat_n = static_cast<size_t>(g.B) * g.Hq * w.Tq_pad * 3;
   w.rstat = reinterpret_cast<float*>(base + ws_take(off, w.rstat_n * sizeof(float)));
+  w.rowmax_n = static_cast<size_t>(g.B) * g.Hkv * kRowStats * w.Tq_pad;
+  w.rowmax = reinterpret_cast<float*>(base + ws_take(off, w.rowmax_n * sizeof(float)));
+  w.dsscale = reinterpret_cast<float*>(base + ws_take(off, static_cast<size_t>(g.B) * g.Hkv * (w.st.Tk_pad / 32) * sizeof(float)));
   w.bytes = off;
   return w;
 }
@@ -1879,8 +2000,10 @@ hipError_t bwd_impl(const Geom& g, const BwdArgs& a, int split_rows, void* ws, h
   hipError_t e = launch_staging(w.st, q, q_elems, k, v, P, g.B, g.Tk, g.Hkv, g.Hq, stream, dout, q_elems, kMaxDO, g.d);
   if (e != hipSuccess) return e;
 
-  // row statistics of padded rows stay 0 (the key-major kernel reads whole 32-row tiles)
+  // row statistics of padded rows stay 0 (the key-major kernel reads whole 32-row tiles); the per-row
+  // maxima start at 0 for the row kernels' atomicMax
   hipLaunchKernelGGL(k_zero4, dim3(256), dim3(256), 0, stream, w.rstat, static_cast<int64_t>(w.rstat_n / 4));
+  hipLaunchKernelGGL(k_zero4, dim3(256), dim3(256), 0, stream, w.rowmax, static_cast<int64_t>(w.rowmax_n / 4));
   RowParams rp{};
   rp.q = static_cast<const u16*>(q);
   rp.dout = static_cast<const u16*>(dout);
@@ -1902,6 +2025,9 @@ hipError_t bwd_impl(const Geom& g, const BwdArgs& a, int split_rows, void* ws, h
   rp.st_alpha = w.alpha;
   rp.st_delta = w.delta;
   rp.rstat = w.rstat;
+  rp.knorm = w.st.knorm;
+  rp.vnorm = w.st.vnorm;
+  rp.rowmax = w.rowmax;
   rp.D = g.d;
   rp.rho = static_cast<const u16*>(a.rho);
   rp.rk = a.rk;
@@ -1961,6 +2087,9 @@ hipError_t bwd_impl(const Geom& g, const BwdArgs& a, int split_rows, void* ws, h
   if (e != hipSuccess) return e;
   e = side_join(side);
   if (e != hipSuccess) return e;
+  // per (batch, kv head, statistic): the maximum over rows >= i of each row statistic
+  e = launch_scan_max(w.rowmax, w.Tq_pad, g.B * g.Hkv * kRowStats, w.Tq_pad, true, stream);
+  if (e != hipSuccess) return e;
   // fp16 copies of u and dkbar (lo parts for rows < split)
   e = launch_stage_rows(w.u32, true, w.st.maxbits, kMaxU, w.u16, split > 0 ? w.u16lo : nullptr, g.B, g.Tq, w.Tq_pad,
                         g.Hq, split, w.lo_pad, stream);
@@ -1982,6 +2111,8 @@ hipError_t bwd_impl(const Geom& g, const BwdArgs& a, int split_rows, void* ws, h
   kp.alpha = w.alpha;
   kp.delta = w.delta;
   kp.rstat = w.rstat;
+  kp.rowmax = w.rowmax;
+  kp.dsscale = w.dsscale;
   kp.D = g.d;
   kp.qstride = w.do16 - w.q16;
   kp.maxbits = w.st.maxbits;
@@ -2034,6 +2165,7 @@ hipError_t bwd_impl(const Geom& g, const BwdArgs& a, int split_rows, void* ws, h
   if (split < g.Tq) {
     DqParams dp{};
     dp.ds = w.ds;
+    dp.dsscale = w.dsscale;
     dp.k16t = w.st.k16t;
     dp.maxbits = w.st.maxbits;
     dp.dq = dq;

@@ -83,6 +83,15 @@ __device__ __forceinline__ float range_scale(float m) {
   return __builtin_ldexpf(1.f, 15 - E);
 }
 
+// 15 - E(m) as an integer, so that range_scale(m) == 2^range_exp(m) (0 for m == 0 or non-finite m).
+__device__ __forceinline__ int range_exp(float m) {
+  const uint32_t bits = __float_as_uint(m);
+  const int ex = static_cast<int>((bits >> 23) & 0xff);
+  if (m <= 0.f || ex == 0xff) return 0;
+  const int E = (ex == 0) ? -126 : ex - 126;
+  return 15 - E;
+}
+
 // x from lane l ^ 32 combined with x (sum / max) via the gfx950 half-wave swap.
 __device__ __forceinline__ float xor32_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -140,13 +149,19 @@ __device__ __forceinline__ float sum8(f16x8 v, float acc) {
 // The instruction is issued from inline assembly: the compiler then does not track it, and does not
 // make every later LDS read (of the other buffer) wait for the copy in flight, which it cannot tell
 // apart from the copy's destination.  The instruction has no register results; its address operands
-// are read at issue.
+// (the global address and M0, the LDS base) are read at issue.
+// M0 is a register the compiler reserves for itself, so the statement leaves it as it found it: the
+// old value is saved in an SGPR of the statement's own (an early-clobber output, so it shares no
+// register with the inputs) and restored after the issue.
 __device__ __forceinline__ void lds_dma16(const void* src, void* lds_base) {
   const uint32_t lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lds_base);
+  uint32_t saved_m0;
   // one wait state between the M0 write and the LDS DMA that reads it (s_nop 0)
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               ::"v"(src), "s"(__builtin_amdgcn_readfirstlane(lds))
-               : "memory", "m0");
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+               "s_mov_b32 m0, %0"
+               : "=&s"(saved_m0)
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
 }
 // The wait is issued twice: as assembly (always kept) and as the builtin, so that the compiler also
 // knows that its own loads issued before it have completed.
@@ -225,6 +240,8 @@ struct Staging {
   _Float16* v16;       // backward only: V rows, d permuted (nullptr otherwise)
   _Float16* p16t;
   _Float16* p16;       // backward only: P rows, columns permuted (nullptr otherwise)
+  float* knorm;        // [B][Hkv][Tk_pad]: running maximum over keys 0..j of |k_j| (Euclidean, unscaled)
+  float* vnorm;        // the same for |v_j|; directly after knorm
   int Tk_pad;
   size_t bytes;        // total workspace used
 };
@@ -250,9 +267,15 @@ inline Staging staging_layout(void* ws, int B, int Tk, int Hkv, int Hq, bool bac
   else s.v16t = reinterpret_cast<_Float16*>(base + ws_take(off, kv));
   s.p16t = reinterpret_cast<_Float16*>(base + ws_take(off, p));
   if (backward) s.p16 = reinterpret_cast<_Float16*>(base + ws_take(off, p));
+  const size_t nrm = static_cast<size_t>(B) * Hkv * s.Tk_pad * sizeof(float);
+  s.knorm = reinterpret_cast<float*>(base + ws_take(off, 2 * nrm));
+  s.vnorm = s.knorm + static_cast<size_t>(B) * Hkv * s.Tk_pad;
   s.bytes = off;
   return s;
 }
+
+// In-place running maximum (suffix: from the end) along `series` series of n floats, `stride` apart.
+hipError_t launch_scan_max(float* x, int n, int series, int64_t stride, bool suffix, hipStream_t stream);
 
 // Query-side fp16 copies in the row-tile layout (see k_stage_rows in fast_staging.hip).
 hipError_t launch_stage_rows(const void* src, bool f32, const uint32_t* maxbits, int max_idx, _Float16* dst,

@@ -23,7 +23,7 @@
 // directly the B operand of o^T = V^T P~^T and kbar^T = K^T P~^T (fp16 staging
 // layouts in fast_common.h).  Lazy rescaling: the running maximum only moves
 // when a tile's maximum exceeds it by 8 (log2 units), so the accumulators are
-// rarely rescaled; exp2 arguments are then <= 8 and p~ <= 256 still fits fp16.
+// rarely rescaled; p~ = exp2(s - m + 7) <= 2^15 then still fits fp16.
 // Key tiles (chunk-major, see fast_common.h) are double-buffered in LDS and
 // copied by direct-to-LDS DMA while the previous tile is being computed.
 // Blocks are mapped so that all blocks of one (batch, kv head) run on the same
@@ -40,12 +40,17 @@ constexpr int kWaves = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 8.f;
+// p~ = exp2(s - m + kLift): with the lazy rescale s - m <= kTau, so p~ <= 2^(kTau + kLift) = 2^15 stays
+// inside fp16, and weights down to 2^-(14 + kLift) of the row's largest keep fp16's full precision (a
+// sharply peaked row has many keys far below its largest weight; their sum still matters for kbar).
+constexpr float kLift = 7.f;
 
 struct FwdParams {
   const u16* q;
   const u16* rho;   // probe form only: the caller's probe, like q
   const _Float16 *k16, *k16t, *v16t, *p16t;
   const uint32_t* maxbits;
+  const float* knorm;   // [B][Hkv][Tk_pad] running maximum of the key norms (see Staging)
   void* out;        // fp32, or bf16 when out_bf16
   float *lse, *kbar, *osa;
   float* rk;
@@ -234,7 +239,7 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
           accK[mt] *= f;
         }
       }
-      const float mb = m_used == -INFINITY ? 0.f : m_used;
+      const float mb = m_used == -INFINITY ? 0.f : m_used - kLift;
       f16x8 pB[4], pL[SPLIT ? 4 : 1];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -282,7 +287,7 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
   const float L = xor32_sum(lpart);
   const bool has = L > 0.f;
   const float invL = has ? 1.f / L : 0.f;
-  const float lse2 = has ? m_used + __log2f(L) : -INFINITY;
+  const float lse2 = has ? m_used - kLift + __log2f(L) : -INFINITY;   // (L carries the 2^kLift of p~)
   float* obuf = p.osa;
   if (row_ok) {
     if (p.lse && hh == 0) p.lse[(static_cast<int64_t>(b) * p.Hq + h) * p.Tq + row] = lse2 * kLn2;
@@ -309,6 +314,7 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
   float kbv[4][16];
   f16x8 xB[8], xL[SPLIT ? 8 : 1];
   float alpha_s = 0.f, sU = 1.f;
+  float u2sum = 0.f, k2sum = 0.f;   // |U-hat|^2 (scaled units) and |kbar sK|^2 of the row, for pass 2's W scale
   {
     float xv[4][16];
     float xmax = 0.f;
@@ -323,6 +329,7 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
           const int r = 4 * j + e;
           kbv[mt][r] = accK[mt][r] * (invL / sK);
           xv[mt][r] = qv[e] - kbv[mt][r];
+          k2sum = fmaf(accK[mt][r] * invL, accK[mt][r] * invL, k2sum);   // (kbar sK)^2
           xmax = fmaxf(xmax, fabsf(xv[mt][r]));
         }
       }
@@ -335,20 +342,42 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) e[j] = xv[mt][t8 + j] * sX;
       xB[s] = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
-      if constexpr (SPLIT) xL[s] = pack_lo(e, xB[s]);
+      if constexpr (SPLIT) xL[s] = pack_lo(e, xB[s]);   // (single-operand rows form theirs below, one at a time)
     }
-    // U^T = P16t X^T
+    // U^T = P16t X^T.  x always enters as a hi + lo pair: for a sharply peaked row the correction is
+    // one dot product u.(k_1 - k_2) of nearly orthogonal vectors, which amplifies the rounding of u's
+    // inputs; the 32 extra MFMAs per wave are taken once per row block, not per key tile.
     f32x16 accU[4];
     const _Float16* prow = p.p16t + (static_cast<int64_t>(h) * kD + ql) * kD + hh * 8;
 #pragma unroll
-    for (int am = 0; am < 4; ++am) {
-      accU[am] = f32x16{};
+    for (int am = 0; am < 4; ++am) accU[am] = f32x16{};
+    if constexpr (SPLIT) {
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
+      for (int am = 0; am < 4; ++am)
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const f16x8 a = *reinterpret_cast<const f16x8*>(prow + 32 * am * kD + 16 * s);
+          accU[am] = mfma(a, xB[s], accU[am]);
+          accU[am] = mfma(a, xL[s], accU[am]);
+        }
+    } else {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      f16x8 lo;
+      {
+        const int mt = s >> 1, t8 = (s & 1) * 8;
+        float e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[j] = xv[mt][t8 + j] * sX;
+        lo = pack_lo(e, xB[s]);
+      }
+#pragma unroll
+      for (int am = 0; am < 4; ++am) {
         const f16x8 a = *reinterpret_cast<const f16x8*>(prow + 32 * am * kD + 16 * s);
         accU[am] = mfma(a, xB[s], accU[am]);
-        if constexpr (SPLIT) accU[am] = mfma(a, xL[s], accU[am]);
+        accU[am] = mfma(a, lo, accU[am]);
       }
+    }
     }
     const float fu = 1.f / (sX * sP);
     float umax = 0.f;
@@ -376,9 +405,12 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
         float uh = static_cast<float>(xB[s][j]);
         if constexpr (SPLIT) uh += static_cast<float>(xL[s][j]);
         alpha += uh * (kbv[am][t8 + j] * sK);
+        u2sum = fmaf(uh, uh, u2sum);
       }
     }
     alpha_s = xor32_sum(alpha);
+    u2sum = xor32_sum(u2sum);
+    k2sum = xor32_sum(k2sum);
   }
   const f16x8* uB = xB;
   const f16x8* uL = xL;
@@ -389,7 +421,17 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) accC[mt] = f32x16{};
   float rpart = 0.f;
-  const float mb2 = has ? lse2 + 24.f : 0.f;  // p * 2^-24 keeps W = p (R - alpha) inside fp16
+  // W = p (R - alpha) is packed to fp16 as p 2^-wexp (R - alpha), wexp an integer folded into the exp2
+  // argument.  Its range depends on the row: |R_j - alpha| = |U-hat.(k_j - kbar)| <= |U-hat| (|k_j| + |kbar|)
+  // and p <= 1, so the row's bound uses the largest key norm among the keys it sees (a running maximum
+  // along the sequence, from staging) instead of K's largest entry: one key row far larger than the
+  // rest then changes the scale only of the rows that see it, and the other rows' W stay clear of
+  // fp16's subnormals.
+  float mb2 = 0.f;
+  if (has) {
+    const float kmax = r_kend > r_kbeg ? p.knorm[(static_cast<int64_t>(b) * p.Hkv + g) * p.Tk_pad + r_kend - 1] * sK : 0.f;
+    mb2 = lse2 + static_cast<float>(-range_exp(sqrtf(u2sum) * (kmax + sqrtf(k2sum))));
+  }
   if (t_beg < t_end) tile_dma(p, T, 0, b, g, t_beg, false, w, l);
   lds_dma_wait();
   __syncthreads();
@@ -464,8 +506,11 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
   const float RS = xor32_sum(rpart);
   float cc = 0.f, oo = 0.f;   // |out - o|^2 and |out|^2 of the lane's half-row
   if (row_ok) {
-    const float fc = 16777216.f / (sU * sK * sV);
-    const float frs = RS * (16777216.f / (sU * sK));
+    // W was carried as p 2^-wexp (R - alpha), wexp = mb2 - lse2 (an integer; the fp32 sum keeps it to
+    // well within 1/2)
+    const float fw = has ? __builtin_ldexpf(1.f, static_cast<int>(rintf(mb2 - lse2))) : 0.f;
+    const float fc = fw / (sU * sK * sV);
+    const float frs = RS * (fw / (sU * sK));
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -501,11 +546,11 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
 // half of a tile: S = K Q^T and R = K rho^T share the K operand; o += V^T p~ and c += V^T (p~ R)
 // share the V^T operand, so every operand read from LDS feeds two MFMAs.  rho is an input (bf16, exact in fp16 after its power-of-two scale), so its
 // operand lives in LDS, one 8 KB block per wave; q stays in registers.
-// W = p~ R is carried at 2^-32: |R| <= d 2^32 in the scaled units and p~ <= 2^8, so W stays
-// below 2^15 whatever the data.
+// W = p~ R is carried as p~ R 2^-wexp, with wexp set per row from |W| <= 2^15 |rho| |k_j| and the
+// largest key norm among the keys the row sees (as in the projector form's pass 2): one key row far
+// larger than the rest (which sets K's fp16 scale) then does not push the other rows' W into fp16's
+// subnormal range.
 // ------------------------------------------------------------------------------------------
-
-constexpr float kProbeW = 2.3283064365386963e-10f;   // 2^-32
 
 struct __align__(16) ProbeTiles {
   _Float16 k[2][kKeyTile * kD];    // key rows tile    [16 chunks][64 keys][8]
@@ -582,12 +627,25 @@ __global__ __launch_bounds__(512) void k_fwd_probe(FwdParams p) {
 
   f16x8 qB[8];
   load_q_operand(p.q + qoff, row_ok, hh, sQ, qB, p.D);
+  float wfac;   // 2^-wexp
+  int wexp;
   {
     // the lane's rho operand into the wave's LDS block (read back by the same lane only)
     f16x8 rB[8];
     load_q_operand(p.rho + qoff, row_ok, hh, sR, rB, p.D);
+    float r2 = 0.f;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) T.rho[w][s][l] = rB[s];
+    for (int s = 0; s < 8; ++s) {
+      T.rho[w][s][l] = rB[s];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) r2 = fmaf(static_cast<float>(rB[s][j]), static_cast<float>(rB[s][j]), r2);
+    }
+    // |W| = p~ |rho.k_j| <= 2^15 |rho| |k_j| (p~ <= 2^15), with the largest key norm among the keys the
+    // row sees (running maximum along the sequence): the row's scale
+    r2 = xor32_sum(r2);
+    const float kmax = r_kend > r_kbeg ? p.knorm[(static_cast<int64_t>(b) * p.Hkv + g) * p.Tk_pad + r_kend - 1] * sK : 0.f;
+    wexp = -range_exp(32768.f * sqrtf(r2) * kmax);
+    wfac = __builtin_ldexpf(1.f, -wexp);
   }
 
   f32x16 accO[4], accC[4];
@@ -650,7 +708,7 @@ __global__ __launch_bounds__(512) void k_fwd_probe(FwdParams p) {
             accC[mt] *= f;
           }
         }
-        const float mb = m_used == -INFINITY ? 0.f : m_used;
+        const float mb = m_used == -INFINITY ? 0.f : m_used - kLift;
         f16x8 pB[2], wB[2], pL[SPLIT ? 2 : 1], wL[SPLIT ? 2 : 1];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -658,7 +716,7 @@ __global__ __launch_bounds__(512) void k_fwd_probe(FwdParams p) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             e[j] = __builtin_amdgcn_exp2f(fmaf(S[8 * t + j], cS, -mb));
-            x[j] = e[j] * R[8 * t + j] * kProbeW;
+            x[j] = e[j] * R[8 * t + j] * wfac;
           }
           pB[t] = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
           wB[t] = pack8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
@@ -696,7 +754,7 @@ __global__ __launch_bounds__(512) void k_fwd_probe(FwdParams p) {
     __syncthreads();
   }
 
-  // out = o - (c - a o), o = accO / (l sV), c = accC 2^32 / (l sR sK sV), a = rpart 2^32 / (l sR sK)
+  // out = o - (c - a o), o = accO / (l sV), c = accC 2^wexp / (l sR sK sV), a = rpart 2^wexp / (l sR sK)
   const float L = xor32_sum(lpart);
   const float RS = xor32_sum(rpart);
   const bool has = L > 0.f;
@@ -704,11 +762,12 @@ __global__ __launch_bounds__(512) void k_fwd_probe(FwdParams p) {
   float cc = 0.f, oo = 0.f;   // |out - o|^2 and |out|^2 of the lane's half-row
   if (row_ok) {
     const float fo = invL / sV;
-    const float fc = fo / sK / (kProbeW * sR);
-    const float a = RS * invL / sK / (kProbeW * sR);   // rho . kbar
+    const float fw = __builtin_ldexpf(1.f, wexp);
+    const float fc = fo / sK * (fw / sR);
+    const float a = RS * invL / sK * (fw / sR);   // rho . kbar
     if (hh == 0) {
       const int64_t soff = (static_cast<int64_t>(b) * p.Hq + h) * p.Tq + row;
-      if (p.lse) p.lse[soff] = has ? (m_used + __log2f(L)) * kLn2 : -INFINITY;
+      if (p.lse) p.lse[soff] = has ? (m_used - kLift + __log2f(L)) * kLn2 : -INFINITY;
       if (p.rk) p.rk[soff] = a;
     }
 #pragma unroll
@@ -768,6 +827,7 @@ hipError_t launch_fast_fwd(const Geom& g, const void* q, const void* k, const vo
     p.v16t = s.v16t;
     p.p16t = s.p16t;
     p.maxbits = s.maxbits;
+    p.knorm = s.knorm;
     p.out = out;
     p.out_bf16 = g.out_bf16;
     p.cor = cor;
@@ -837,6 +897,7 @@ hipError_t launch_fast_probe(const Geom& g, const void* q, const void* k, const 
     p.k16 = s.k16;
     p.v16t = s.v16t;
     p.maxbits = s.maxbits;
+    p.knorm = s.knorm;
     p.out = out;
     p.out_bf16 = g.out_bf16;
     p.cor = cor;

@@ -74,10 +74,12 @@ __global__ __launch_bounds__(256) void k_absmax(AbsmaxJob job, uint32_t* maxbits
   }
 }
 
-// One block per (64-key tile, kv head, batch): K16 (and V16) row tiles, K16t (and V16t) column tiles.
+// One block per (64-key tile, kv head, batch): K16 (and V16) row tiles, K16t (and V16t) column tiles,
+// and the Euclidean norm of every key and value row (knorm, vnorm [B][Hkv][Tk_pad], 0 past Tk).
 __global__ __launch_bounds__(256) void k_stage_kv(const u16* k, const u16* v, const uint32_t* maxbits,
                                                   _Float16* k16, _Float16* k16t, _Float16* v16t,
-                                                  _Float16* v16, int Tk, int Tk_pad, int Hkv, int D) {
+                                                  _Float16* v16, float* knorm, float* vnorm, int Tk, int Tk_pad,
+                                                  int Hkv, int D) {
   constexpr int LD = kD + 2;  // padded LDS row (halves) for conflict-light column reads
   __shared__ _Float16 ks[kKeyTile * LD];
   __shared__ _Float16 vs[kKeyTile * LD];
@@ -86,7 +88,8 @@ __global__ __launch_bounds__(256) void k_stage_kv(const u16* k, const u16* v, co
   const int key0 = kt * kKeyTile;
   const float sK = range_scale(__uint_as_float(maxbits[1]));
   const float sV = range_scale(__uint_as_float(maxbits[2]));
-  // load 64 rows x 16 chunks of 8 bf16, scale, store fp16 (natural order)
+  // load 64 rows x 16 chunks of 8 bf16, scale, store fp16 (natural order); the 16 chunks of a row are
+  // held by 16 consecutive threads, which also sum the row's squares
   for (int ci = t; ci < kKeyTile * 16; ci += 256) {
     const int r = ci >> 4, c = ci & 15;
     const int key = key0 + r;
@@ -98,12 +101,27 @@ __global__ __launch_bounds__(256) void k_stage_kv(const u16* k, const u16* v, co
     }
     const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w};
     const uint32_t vv[4] = {vw.x, vw.y, vw.z, vw.w};
+    float k2 = 0.f, v2 = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      ks[r * LD + c * 8 + 2 * j] = static_cast<_Float16>(__uint_as_float(kk[j] << 16) * sK);
-      ks[r * LD + c * 8 + 2 * j + 1] = static_cast<_Float16>(__uint_as_float(kk[j] & 0xffff0000u) * sK);
-      vs[r * LD + c * 8 + 2 * j] = static_cast<_Float16>(__uint_as_float(vv[j] << 16) * sV);
-      vs[r * LD + c * 8 + 2 * j + 1] = static_cast<_Float16>(__uint_as_float(vv[j] & 0xffff0000u) * sV);
+      const float k0 = __uint_as_float(kk[j] << 16), k1 = __uint_as_float(kk[j] & 0xffff0000u);
+      const float v0 = __uint_as_float(vv[j] << 16), v1 = __uint_as_float(vv[j] & 0xffff0000u);
+      k2 = fmaf(k0, k0, fmaf(k1, k1, k2));
+      v2 = fmaf(v0, v0, fmaf(v1, v1, v2));
+      ks[r * LD + c * 8 + 2 * j] = static_cast<_Float16>(k0 * sK);
+      ks[r * LD + c * 8 + 2 * j + 1] = static_cast<_Float16>(k1 * sK);
+      vs[r * LD + c * 8 + 2 * j] = static_cast<_Float16>(v0 * sV);
+      vs[r * LD + c * 8 + 2 * j + 1] = static_cast<_Float16>(v1 * sV);
+    }
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) {
+      k2 += __shfl_xor(k2, o, 64);
+      v2 += __shfl_xor(v2, o, 64);
+    }
+    if (c == 0 && knorm) {
+      const int64_t ni = (static_cast<int64_t>(b) * Hkv + g) * Tk_pad + key;
+      knorm[ni] = sqrtf(k2);
+      vnorm[ni] = sqrtf(v2);
     }
   }
   __syncthreads();
@@ -135,6 +153,51 @@ __global__ __launch_bounds__(256) void k_stage_kv(const u16* k, const u16* v, co
     const int64_t off = tb + c * (kD * 8) + d * 8;
     *reinterpret_cast<f16x8*>(k16t + off) = ok;
     if (v16t) *reinterpret_cast<f16x8*>(v16t + off) = ov;
+  }
+}
+
+// Running maximum along each series (one block per series of n floats, series `stride` apart): in
+// place, x[i] = max(x[0..i]) (or, with SUFFIX, max(x[i..n))).  Chunks of 2048 values: each thread takes
+// 8 consecutive values, the block combines the threads' maxima in LDS, and a carry joins the chunks.
+template <bool SUFFIX>
+__global__ __launch_bounds__(256) void k_scan_max(float* x, int n, int64_t stride) {
+  __shared__ float part[256];
+  __shared__ float carry_s;
+  float* s = x + blockIdx.x * stride;
+  const int t = threadIdx.x;
+  float carry = 0.f;   // norms and statistics are >= 0
+  const int nchunks = (n + 2047) / 2048;
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int chunk = SUFFIX ? nchunks - 1 - ch : ch;
+    const int base = chunk * 2048 + 8 * (SUFFIX ? 255 - t : t);   // suffix: thread 0 takes the last run
+    float v[8];
+    float m = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = SUFFIX ? base + 7 - e : base + e;   // in scan order
+      v[e] = i < n ? s[i] : 0.f;
+      m = fmaxf(m, v[e]);
+      v[e] = m;
+    }
+    part[t] = m;
+    __syncthreads();
+    // inclusive scan of the 256 thread maxima (Hillis-Steele)
+    for (int o = 1; o < 256; o <<= 1) {
+      const float y = t >= o ? part[t - o] : 0.f;
+      __syncthreads();
+      part[t] = fmaxf(part[t], y);
+      __syncthreads();
+    }
+    const float before = fmaxf(carry, t > 0 ? part[t - 1] : 0.f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = SUFFIX ? base + 7 - e : base + e;
+      if (i < n) s[i] = fmaxf(before, v[e]);
+    }
+    if (t == 255) carry_s = fmaxf(carry, part[255]);
+    __syncthreads();
+    carry = carry_s;
+    __syncthreads();
   }
 }
 
@@ -255,16 +318,29 @@ hipError_t launch_staging(const Staging& s, const void* q, int64_t q_elems, cons
   absmax_add(job, extra, extra_elems, extra_slot, true);
   if (job.parts > 0)
     hipLaunchKernelGGL(k_absmax, dim3(kAbsmaxBlocks, job.parts), dim3(256), 0, stream, job, s.maxbits);
-  if (B > 0 && s.Tk_pad > 0)
+  if (B > 0 && s.Tk_pad > 0) {
     hipLaunchKernelGGL(k_stage_kv, dim3(Hkv * (s.Tk_pad / kKeyTile), 1, B), dim3(256), 0, stream,
                        static_cast<const u16*>(k), static_cast<const u16*>(v), s.maxbits, s.k16, s.k16t,
-                       s.v16t, s.v16, Tk, s.Tk_pad, Hkv, D);
+                       s.v16t, s.v16, s.knorm, s.vnorm, Tk, s.Tk_pad, Hkv, D);
+    // running maxima of the key and value norms along each sequence (the two arrays are consecutive)
+    hipLaunchKernelGGL(k_scan_max<false>, dim3(2 * B * Hkv), dim3(256), 0, stream, s.knorm, s.Tk_pad,
+                       static_cast<int64_t>(s.Tk_pad));
+  }
   if (P)
     hipLaunchKernelGGL(k_stage_p, dim3(Hq), dim3(256), 0, stream, static_cast<const u16*>(P), s.maxbits, s.p16t,
                      s.p16, D);
   return hipGetLastError();
 }
 
+
+hipError_t launch_scan_max(float* x, int n, int series, int64_t stride, bool suffix, hipStream_t stream) {
+  if (series <= 0 || n <= 0) return hipSuccess;
+  if (suffix)
+    hipLaunchKernelGGL(k_scan_max<true>, dim3(series), dim3(256), 0, stream, x, n, stride);
+  else
+    hipLaunchKernelGGL(k_scan_max<false>, dim3(series), dim3(256), 0, stream, x, n, stride);
+  return hipGetLastError();
+}
 
 hipError_t launch_stage_rows(const void* src, bool f32, const uint32_t* maxbits, int max_idx, _Float16* dst,
                              _Float16* lo, int B, int Tq, int Tq_pad, int Hq, int lo_rows, int lo_pad,

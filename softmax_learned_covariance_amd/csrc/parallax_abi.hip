@@ -103,43 +103,53 @@ size_t dec_ws(const plx::Geom& g) {
 namespace plx {
 
 namespace {
-// One non-blocking helper stream per device, created on first use and kept for the life of the
-// process.  It is only ever ordered through events recorded by the call that uses it.
+// One non-blocking helper stream per device (default priority), created on first use together with
+// two events that order it against the caller's stream, and kept until the process ends.  Fork and
+// join each record one of those events and make the other stream wait for it; the pair runs under
+// the device's mutex, so a wait always refers to the record made by the same call (a stream wait
+// takes the event's most recent record at the time of the wait).
 constexpr int kMaxDevices = 64;
-hipStream_t g_side[kMaxDevices];
-bool g_side_tried[kMaxDevices];
-std::mutex g_side_mutex;
+struct SideState {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool tried = false;
+  std::mutex mutex;
+};
+SideState g_side[kMaxDevices];
 
-hipStream_t side_stream() {
+SideState* side_state() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  std::lock_guard<std::mutex> lock(g_side_mutex);
-  if (!g_side_tried[dev]) {
-    g_side_tried[dev] = true;
-    if (hipStreamCreateWithFlags(&g_side[dev], hipStreamNonBlocking) != hipSuccess) g_side[dev] = nullptr;
+  SideState& s = g_side[dev];
+  std::lock_guard<std::mutex> lock(s.mutex);
+  if (!s.tried) {
+    s.tried = true;
+    bool good = hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking) == hipSuccess;
+    good = good && hipEventCreateWithFlags(&s.fork, hipEventDisableTiming) == hipSuccess;
+    good = good && hipEventCreateWithFlags(&s.join, hipEventDisableTiming) == hipSuccess;
+    if (!good) s.stream = nullptr;   // (whatever was created stays until exit; the lane is not used)
   }
-  return g_side[dev];
+  return s.stream ? &s : nullptr;
 }
 }  // namespace
 
 SideLane side_fork(hipStream_t main) {
-  SideLane s{main, main};
-  hipStream_t side = side_stream();
-  hipEvent_t ev = nullptr;
-  if (!side || hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) return s;
-  if (hipEventRecord(ev, main) == hipSuccess && hipStreamWaitEvent(side, ev, 0) == hipSuccess) s.stream = side;
-  (void)hipEventDestroy(ev);
-  return s;
+  SideLane lane{main, main};
+  SideState* s = side_state();
+  if (!s) return lane;
+  std::lock_guard<std::mutex> lock(s->mutex);
+  if (hipEventRecord(s->fork, main) == hipSuccess && hipStreamWaitEvent(s->stream, s->fork, 0) == hipSuccess)
+    lane.stream = s->stream;
+  return lane;
 }
 
-hipError_t side_join(const SideLane& s) {
-  if (s.stream == s.main) return hipSuccess;
-  hipEvent_t ev = nullptr;
-  hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
-  if (e != hipSuccess) return e;
-  e = hipEventRecord(ev, s.stream);
-  if (e == hipSuccess) e = hipStreamWaitEvent(s.main, ev, 0);
-  (void)hipEventDestroy(ev);
+hipError_t side_join(const SideLane& lane) {
+  if (lane.stream == lane.main) return hipSuccess;
+  SideState* s = side_state();
+  if (!s) return hipErrorInvalidHandle;
+  std::lock_guard<std::mutex> lock(s->mutex);
+  hipError_t e = hipEventRecord(s->join, lane.stream);
+  if (e == hipSuccess) e = hipStreamWaitEvent(lane.main, s->join, 0);
   return e;
 }
 
@@ -377,7 +387,8 @@ size_t parallax_attn_decode_paged_workspace(const plx_attn_desc* desc) {
 
 plx_status parallax_attn_decode_paged(const plx_attn_desc* desc, const void* q, const void* k_pages,
                                       const void* v_pages, int32_t num_pages, int32_t page_size,
-                                      const int32_t* block_table, const int32_t* seqlens_k, const void* P,
+                                      const int32_t* block_table, int32_t block_table_stride,
+                                      const int32_t* seqlens_k, const void* P,
                                       void* out, float* cor, void* workspace, size_t workspace_bytes,
                                       void* hip_stream) {
   const char* what = "parallax_attn_decode_paged";
@@ -388,6 +399,10 @@ plx_status parallax_attn_decode_paged(const plx_attn_desc* desc, const void* q, 
   if (page_size < 1 || page_size > 65536 || (page_size & (page_size - 1)) != 0)
     return fail(PLX_ERR_INVALID, "%s: page_size=%d is not a power of two in [1, 65536]", what, page_size);
   if (num_pages < 1) return fail(PLX_ERR_INVALID, "%s: num_pages=%d < 1", what, num_pages);
+  const int64_t pages_needed = (static_cast<int64_t>(desc->seqlen_k) + page_size - 1) / page_size;
+  if (block_table_stride < pages_needed)
+    return fail(PLX_ERR_INVALID, "%s: block_table_stride=%d < %lld pages needed for seqlen_k=%d", what,
+                block_table_stride, static_cast<long long>(pages_needed), desc->seqlen_k);
   if (!plx::fast_decode_supported(g))
     return fail(PLX_ERR_UNSUPPORTED,
                 "%s: only bf16, head_dim 128 or 64, heads_q/heads_kv in {1,2,4,8} and p_per_query 0 are supported",
@@ -403,7 +418,7 @@ plx_status parallax_attn_decode_paged(const plx_attn_desc* desc, const void* q, 
     return fail(PLX_ERR_INVALID, "%s: k_pages, v_pages and block_table must not be NULL", what);
   st = check_ws(need, workspace, workspace_bytes, what);
   if (st != PLX_OK) return st;
-  plx::PagedCache pc{block_table, num_pages, page_size, (g.Tk + page_size - 1) / page_size};
+  plx::PagedCache pc{block_table, num_pages, page_size, block_table_stride};
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   return hip_status(plx::launch_fast_decode(g, q, k_pages, v_pages, seqlens_k, P, out, cor, workspace, stream, &pc),
                     what);

@@ -185,9 +185,11 @@ def test_paged_decode_validation(plx):
     lib = plx.get_lib()
     bf = dict(dtype=plx.PLX_BF16, d=128, Tq=1)
 
-    def call(desc, num_pages=4, page=16, table=FAKE, q=FAKE, ws=FAKE, nws=1 << 40):
-        return lib.parallax_attn_decode_paged(ctypes.byref(desc), q, FAKE, FAKE, num_pages, page, table, None,
-                                              FAKE, FAKE, None, ws, nws, None)
+    def call(desc, num_pages=4, page=16, table=FAKE, q=FAKE, ws=FAKE, nws=1 << 40, stride=None):
+        if stride is None:
+            stride = (desc.seqlen_k + page - 1) // page if page > 0 else 1
+        return lib.parallax_attn_decode_paged(ctypes.byref(desc), q, FAKE, FAKE, num_pages, page, table, stride,
+                                              None, FAKE, FAKE, None, ws, nws, None)
 
     d = _desc(plx, **bf)
     assert call(_desc(plx, dtype=plx.PLX_BF16, d=128, Tq=0)) == E.PLX_ERR_INVALID
@@ -195,6 +197,11 @@ def test_paged_decode_validation(plx):
         assert call(d, page=page) == E.PLX_ERR_INVALID, page
     assert b"page_size" in lib.parallax_last_error()
     assert call(d, num_pages=0) == E.PLX_ERR_INVALID
+    # the table's row stride must cover seqlen_k; a wider table (sized for the cache's capacity) is fine
+    pages = (d.seqlen_k + 15) // 16
+    assert call(d, stride=pages - 1) == E.PLX_ERR_INVALID
+    assert b"block_table_stride" in lib.parallax_last_error()
+    assert call(d, stride=pages + 7, nws=0) == E.PLX_ERR_WORKSPACE     # passed the stride check
     assert call(_desc(plx, Tq=1)) == E.PLX_ERR_UNSUPPORTED                       # fp32
     assert call(_desc(plx, Hq=3, Hkv=1, **bf)) == E.PLX_ERR_UNSUPPORTED          # 3 query heads per group
     assert call(d, table=None) == E.PLX_ERR_INVALID

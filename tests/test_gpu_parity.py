@@ -314,16 +314,17 @@ def test_full_size_forward_sampled(plx, name):
     w = W.WORKLOADS[name]
     _announce(f"full-size forward {name} (sampled rows)")
     q, k, v, P = W.make_inputs(w, device="cuda")
-    out, lse, _, _ = _run_fwd(plx, q, k, v, P)
+    out, lse, kbar, o = _run_fwd(plx, q, k, v, P)
     uniform, rows = _sample_rows(w.seqlen_q, 17)
     bsel = [0, w.batch - 1]
     qh, kh, vh = host(q[bsel]), host(k[bsel]), host(v[bsel])
     Ph = host(P)
-    ref, ref_lse, _, _ = oracle.fwd(qh, kh, vh, Ph, causal=True, rows=rows)
-    got = host(out[bsel])
-    norm = ref[:, uniform]
-    e = sampled_rel_err(got[:, rows], ref[:, rows], norm)
-    assert e <= BF16_TOL, e
+    ref, ref_lse, ref_kbar, ref_o = oracle.fwd(qh, kh, vh, Ph, causal=True, rows=rows)
+    # out, and the saved kbar and o that the backward reads
+    for what, got_t, want in (("out", out, ref), ("kbar", kbar, ref_kbar), ("o", o, ref_o)):
+        got = host(got_t[bsel])
+        e = sampled_rel_err(got[:, rows], want[:, rows], want[:, uniform])
+        assert e <= BF16_TOL, (what, e)
     assert np.max(np.abs(host(lse[bsel])[:, :, rows] - ref_lse[:, :, rows])) <= 1e-3
 
 
@@ -349,6 +350,33 @@ def test_full_size_train_step_sampled(plx):
         total += oracle.bwd(host(q[b:b + 1, :, 0:2]), host(k[b:b + 1, :, 0:1]), host(v[b:b + 1, :, 0:1]),
                             host(P[0:2]), host(dout[b:b + 1, :, 0:2]), causal=True)[3]
     assert rel_err(host(dP[0:2]), total) <= BF16_TOL
+
+
+def test_full_size_layer17_backward(plx):
+    """The 1.7B-like layer (B=2, T=8192), forward + backward at full size, the configuration the benchmark
+    times.  dq for batch 0, query heads 0-1, all 8192 rows; dk and dv for batch 0, key/value head 0 (the
+    exact sums over both of its query heads); dP for query heads 0-1 summed over both batch entries."""
+    w = W.WORKLOADS["layer17"]
+    _announce("full-size layer17 forward + backward (batch 0 / head group 0 exact)")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.seed + 500)
+    q, k, v, P = W.make_inputs(w, device="cuda")
+    dout = torch.randn(q.shape, generator=g, device="cuda").to(torch.bfloat16)
+    out, lse, kbar, o = _run_fwd(plx, q, k, v, P)
+    dq, dk, dv, dP = plx.parallax_attn_bwd(q, k, v, P, out, dout, lse, kbar, o)
+    torch.cuda.synchronize()
+    sl = (slice(0, 1), slice(None), slice(0, 2))
+    rdq, rdk, rdv, rdP = oracle.bwd(host(q[sl]), host(k[0:1, :, 0:1]), host(v[0:1, :, 0:1]),
+                                    host(P[0:2]), host(dout[sl]), causal=True)
+    for name, got, want in (("dq", dq[sl], rdq), ("dk", dk[0:1, :, 0:1], rdk), ("dv", dv[0:1, :, 0:1], rdv)):
+        e = rel_err(host(got), want)
+        print(f"[parity] layer17 {name}: {e:.2e}", flush=True)
+        assert e <= BF16_TOL, (name, e)
+    total = rdP + oracle.bwd(host(q[1:2, :, 0:2]), host(k[1:2, :, 0:1]), host(v[1:2, :, 0:1]),
+                             host(P[0:2]), host(dout[1:2, :, 0:2]), causal=True)[3]
+    e = rel_err(host(dP[0:2]), total)
+    print(f"[parity] layer17 dP: {e:.2e}", flush=True)
+    assert e <= BF16_TOL, e
 
 
 def test_full_size_decode_sampled(plx):
@@ -463,6 +491,25 @@ def test_full_size_decode_paged(plx):
     sub_table = np.arange(used.numel()).reshape(len(bsel), -1)
     ref = oracle.decode_paged(host(q[bsel]), host(kp[used]), host(vp[used]), sub_table, host(P))
     assert rel_err(host(out[bsel]), ref) <= BF16_TOL
+
+
+def test_decode_paged_wide_table(plx):
+    """A block table sized for the cache's capacity (wider than the sequences need, seqlen_k < width * page):
+    every row is read with the table's own stride, so each sequence still finds its pages."""
+    _announce("paged decode with a table wider than seqlen_k needs")
+    w = W.scaled(W.WORKLOADS["decode"], batch=4, seqlen_k=500)
+    q, kc, vc, P = W.make_inputs(w, device="cuda")
+    kp, vp, table = _to_pages(kc, vc, 64, spare=40, seed=11)       # 8 pages per sequence
+    wide = torch.full((4, 13), 10**6, dtype=torch.int32, device="cuda")   # junk past the used columns
+    wide[:, :table.shape[1]] = table
+    seqlens = torch.tensor([500, 77, 0, 300], dtype=torch.int32, device="cuda")
+    out = plx.parallax_attn_decode_paged(q, kp, vp, wide, P, seqlens=seqlens, seqlen_k=500)
+    ref_c = plx.parallax_attn_decode(q, kc, vc, P, seqlens=seqlens)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_c)
+    ref = oracle.decode_paged(host(q), host(kp), host(vp), host(wide).astype(np.int64), host(P),
+                              seqlens=host(seqlens).astype(int), seqlen_k=500)
+    assert rel_err(host(out), ref) <= BF16_TOL
 
 
 def test_decode_paged_clamps_bad_entries(plx):
