@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define PARALLAX_ABI_VERSION 3
+#define PARALLAX_ABI_VERSION 4
 
 typedef enum {
   PLX_OK = 0,
@@ -277,6 +277,26 @@ plx_status parallax_attn_decode_paged(const plx_attn_desc* desc, const void* q,
                                       const int32_t* seqlens_k,
                                       const void* P, void* out, float* cor,
                                       void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * No-allocation decode, for callers that cannot allocate device memory or pass a workspace: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.  Same arguments, results
+ * and kernels as parallax_attn_decode (bit-identical outputs), without the workspace: its scratch is a
+ * fixed device array inside the library, parallax_attn_decode_noalloc_max_scratch() bytes (64 MiB) on
+ * each GPU it runs on, held until the process ends.  A desc whose decode needs more scratch than that
+ * (parallax_attn_decode_workspace(desc) > the maximum) returns PLX_ERR_WORKSPACE and launches nothing.
+ * The call allocates nothing (no hipMalloc, no allocating library routine); the first call on a device
+ * looks the array's address up once.  Every call on one GPU shares that GPU's array: calls that overlap
+ * in time on one GPU (on different streams, or from several threads) race on it and give undefined
+ * results; calls ordered on one stream are safe.  The kernels overwrite every scratch value they read,
+ * so no clearing is needed between calls.
+ */
+size_t parallax_attn_decode_noalloc_max_scratch(void);
+
+plx_status parallax_attn_decode_noalloc(const plx_attn_desc* desc,
+                                        const void* q, const void* k_cache, const void* v_cache,
+                                        const int32_t* seqlens_k, const void* P, void* out, float* cor,
+                                        void* hip_stream);
 
 #ifdef __cplusplus
 }

@@ -15,6 +15,7 @@ Functions (same names as the C entry points):
     out, lse, o, rk   = parallax_attn_fwd_probe(q, k, v, rho, causal=True, window=0, scale=None)
     dq, dk, dv, drho  = parallax_attn_bwd_probe(q, k, v, rho, out, dout, lse, o, rk, causal=True, ...)
     out               = parallax_attn_decode_paged(q, k_pages, v_pages, block_table, P, seqlens=None, ...)
+    out               = parallax_attn_decode_noalloc(q, k_cache, v_cache, P, seqlens=None, ...)  (no workspace)
 
 Layouts: q [B,Tq,Hq,d] (decode [B,Hq,d]); k, v [B,Tk,Hkv,d]; P [Hq,d,d] (or
 [B,Tq,Hq,d,d] per query, forward only); outputs float32.
@@ -71,6 +72,8 @@ SIGNATURES = {
                                 _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "parallax_attn_decode_workspace": (_sz, [_DESC]),
     "parallax_attn_decode": (_st, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "parallax_attn_decode_noalloc_max_scratch": (_sz, []),
+    "parallax_attn_decode_noalloc": (_st, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "parallax_attn_decode_paged_workspace": (_sz, [_DESC]),
     "parallax_attn_decode_paged": (_st, [_DESC, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int32,
                                          _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -295,6 +298,38 @@ def parallax_attn_decode(q, k_cache, v_cache, P, seqlens=None, window=0, scale=N
     return (out, ratio) if cor else out
 
 
+def parallax_attn_decode_noalloc(q, k_cache, v_cache, P, seqlens=None, window=0, scale=None, out_dtype=torch.float32,
+                                 cor=False, out=None, cor_out=None):
+    """Decode through the no-allocation entry point (the library's fixed scratch instead of a workspace):
+    arguments and results as parallax_attn_decode.  `out` (and `cor_out` with cor=True) may be given
+    preallocated, so that the call allocates nothing at all (e.g. under HIP graph capture)."""
+    lead = q.shape[:-2]
+    B, Hq, d = q.shape[0], q.shape[-2], q.shape[-1]
+    T = q.shape[1] if q.dim() == 4 else 1
+    Lmax, Hkv = k_cache.shape[1], k_cache.shape[2]
+    dt = _dtype_code(q)
+    dev = q.device
+    _need(k_cache, "k_cache", q.dtype, (B, Lmax, Hkv, d), dev)
+    _need(v_cache, "v_cache", q.dtype, (B, Lmax, Hkv, d), dev)
+    _need(P, "P", q.dtype, (Hq, d, d), dev)
+    if seqlens is not None:
+        _need(seqlens, "seqlens", torch.int32, (B,), dev)
+    if not q.is_contiguous():
+        raise ValueError("q: must be contiguous")
+    oc, odt = _out_code(out_dtype)
+    desc = make_desc(B, T, Lmax, Hq, Hkv, d, True, window, scale, dt, False, -1, oc)
+    if out is None:
+        out = torch.empty((*lead, Hq, d), dtype=odt, device=dev)
+    _need(out, "out", odt, (*lead, Hq, d), dev)
+    ratio = None
+    if cor:
+        ratio = cor_out if cor_out is not None else torch.empty((*lead, Hq), dtype=torch.float32, device=dev)
+        _need(ratio, "cor_out", torch.float32, (*lead, Hq), dev)
+    _check(get_lib().parallax_attn_decode_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                                  _ptr(seqlens), _ptr(P), _ptr(out), _ptr(ratio), _stream()))
+    return (out, ratio) if cor else out
+
+
 def parallax_attn_decode_paged(q, k_pages, v_pages, block_table, P, seqlens=None, seqlen_k=None, window=0,
                                scale=None, out_dtype=torch.float32, cor=False):
     """Decode against a paged cache: q [B,Hq,d] or [B,T,Hq,d]; pages [num_pages,page_size,Hkv,d]; block_table
@@ -340,3 +375,4 @@ decode = parallax_attn_decode
 fwd_probe = parallax_attn_fwd_probe
 bwd_probe = parallax_attn_bwd_probe
 decode_paged = parallax_attn_decode_paged
+decode_noalloc = parallax_attn_decode_noalloc

@@ -161,6 +161,37 @@ void mark_end(int kernel, hipStream_t stream) {
 }
 }  // namespace plx
 
+namespace {
+// Scratch of the no-allocation decode entry point: a fixed device array instead of the caller's
+// workspace.  Every GPU the library runs on holds its own copy until the process ends.  Host code
+// never uses the array's name as an address (in host code it is only a stand-in for the symbol):
+// the device address is looked up once per device with hipGetSymbolAddress, with that device current,
+// and kept.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+void* g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mutex;
+
+// The scratch array's device address on the current device (looked up on first use per device).
+hipError_t scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
 extern "C" {
 
 void parallax_set_kernel_events(int kernel, void* before, void* after) {
@@ -422,6 +453,42 @@ plx_status parallax_attn_decode_paged(const plx_attn_desc* desc, const void* q, 
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   return hip_status(plx::launch_fast_decode(g, q, k_pages, v_pages, seqlens_k, P, out, cor, workspace, stream, &pc),
                     what);
+}
+
+size_t parallax_attn_decode_noalloc_max_scratch(void) { return kNoAllocScratchBytes; }
+
+plx_status parallax_attn_decode_noalloc(const plx_attn_desc* desc, const void* q, const void* k_cache,
+                                        const void* v_cache, const int32_t* seqlens_k, const void* P, void* out,
+                                        float* cor, void* hip_stream) {
+  const char* what = "parallax_attn_decode_noalloc";
+  plx::Geom g;
+  plx_status st = check_desc(desc, what, &g);
+  if (st != PLX_OK) return st;
+  if (g.Tq < 1) return fail(PLX_ERR_INVALID, "%s: seqlen_q must be >= 1 (got %d)", what, g.Tq);
+  if (g.p_per_query) return fail(PLX_ERR_UNSUPPORTED, "%s: per-query projectors are not supported", what);
+  if (g.Tq > 1 && !plx::fast_decode_supported(g))
+    return fail(PLX_ERR_UNSUPPORTED, "%s: several new tokens per sequence need the bf16 fast path", what);
+  g.causal = 1;
+  const size_t need = dec_ws(g);
+  if (need > kNoAllocScratchBytes)
+    return fail(PLX_ERR_WORKSPACE, "%s: needs %zu bytes of scratch, more than the fixed %zu (use parallax_attn_decode "
+                "with a workspace)", what, need, kNoAllocScratchBytes);
+  if (g.B == 0) return ok();
+  if (!q || !P || !out) return fail(PLX_ERR_INVALID, "%s: q, P and out must not be NULL", what);
+  if (g.Tk > 0 && (!k_cache || !v_cache))
+    return fail(PLX_ERR_INVALID, "%s: k_cache and v_cache must not be NULL", what);
+  if (!plx::fast_decode_supported(g) && (g.out_bf16 || cor))
+    return fail(PLX_ERR_UNSUPPORTED, "%s: bf16 out and cor need the bf16 fast path", what);
+  void* ws = nullptr;
+  hipError_t e = scratch_ptr(&ws);
+  if (e != hipSuccess) return hip_status(e, what);
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  if (plx::fast_decode_supported(g))
+    e = plx::launch_fast_decode(g, q, k_cache, v_cache, seqlens_k, P, out, cor, ws, stream);
+  else
+    e = plx::launch_generic_fwd(g, q, k_cache, v_cache, P, seqlens_k, static_cast<float*>(out), nullptr, nullptr,
+                                nullptr, 0, 1, stream, true, PLX_KERNEL_DECODE_PASS1);
+  return hip_status(e, what);
 }
 
 }  // extern "C"

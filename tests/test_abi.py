@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(plx):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     out = subprocess.run(["nm", "-D", "--defined-only", plx.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (parallax_\w+)", out))
     missing = [n for n in names if n not in exported]
@@ -210,6 +210,27 @@ def test_paged_decode_validation(plx):
     assert need > 0 and need == lib.parallax_attn_decode_workspace(ctypes.byref(d))
     assert call(d, nws=need - 1) == E.PLX_ERR_WORKSPACE
     assert call(_desc(plx, B=0, **bf), ws=None, nws=0) in (E.PLX_OK, E.PLX_ERR_INVALID)
+
+
+def test_noalloc_decode_validation(plx):
+    """The no-allocation decode validates like the workspace decode and refuses a decode whose scratch
+    exceeds its fixed array -- before any HIP call, so this runs without a GPU."""
+    E = plx
+    lib = plx.get_lib()
+    cap = lib.parallax_attn_decode_noalloc_max_scratch()
+    assert cap == 64 << 20
+
+    def call(desc, q=FAKE):
+        return lib.parallax_attn_decode_noalloc(ctypes.byref(desc), q, FAKE, FAKE, None, FAKE, FAKE, None, None)
+
+    big = _desc(plx, B=4096, Tq=8, Tk=32768, Hq=16, Hkv=8, d=128, dtype=plx.PLX_BF16)
+    assert lib.parallax_attn_decode_workspace(ctypes.byref(big)) > cap
+    assert call(big) == E.PLX_ERR_WORKSPACE
+    assert b"scratch" in lib.parallax_last_error()
+    assert call(_desc(plx, dtype=plx.PLX_BF16, d=128, Tq=0)) == E.PLX_ERR_INVALID
+    assert call(_desc(plx, Tq=3)) == E.PLX_ERR_UNSUPPORTED            # several tokens on the fp32 path
+    assert call(_desc(plx, dtype=plx.PLX_BF16, d=128, Tq=1), q=None) == E.PLX_ERR_INVALID
+    assert call(_desc(plx, B=0, dtype=plx.PLX_BF16, d=128, Tq=1)) == E.PLX_OK
 
 
 def test_output_options_validation(plx):
