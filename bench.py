@@ -95,6 +95,7 @@ KERNEL_SOURCES = {"fwd": ["fast_fwd.hip", "fast_common.h"], "bwd_rows": ["fast_b
                   "bwd_keys": ["fast_bwd.hip", "fast_common.h"], "bwd_dq": ["fast_bwd.hip", "fast_common.h"],
                   "decode_pass1": ["fast_decode.hip", "fast_common.h"],
                   "decode_pass2": ["fast_decode.hip", "fast_common.h"],
+                  "decode_moment": ["fast_decode_moment.hip", "fast_common.h"],
                   "probe": ["fast_fwd.hip", "fast_common.h"]}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_layer17_decode.txt")
 
@@ -346,36 +347,66 @@ def main():
             plx.parallax_attn_decode(qd, kc, vc, Pd)
         torch.cuda.synchronize()
         Kd = max(6, K)
+        cache_bytes = 2 * wd.batch * wd.seqlen_k * wd.heads_kv * wd.head_dim * 2
+        other = (wd.batch * wd.heads_q * wd.head_dim) * (2 + 4) + wd.heads_q * wd.head_dim ** 2 * 2
+        alg = cache_bytes + other
+        keys = wd.batch * wd.seqlen_k * wd.heads_q   # (key, query head) pairs
+        # the default path (the single-read kernel for this shape), timed with its kernel's events
         dev_ev = [(ev.create(), ev.create()) for _ in range(Kd)]
         t0 = time.perf_counter()
         for i in range(Kd):
-            lib.parallax_set_kernel_events(plx.PLX_KERNEL_DECODE_PASS1 if i % 2 == 0 else plx.PLX_KERNEL_DECODE_PASS2,
-                                           *dev_ev[i])
+            lib.parallax_set_kernel_events(plx.PLX_KERNEL_DECODE_MOMENT, *dev_ev[i])
             plx.parallax_attn_decode(qd, kc, vc, Pd)
         lib.parallax_set_kernel_events(0, None, None)
         torch.cuda.synchronize()
         dt = (time.perf_counter() - t0) / Kd
-        p1 = [ev.elapsed_ms(a, b) for a, b in dev_ev[0::2]]
-        p2 = [ev.elapsed_ms(a, b) for a, b in dev_ev[1::2]]
+        kms_m = sum(ev.elapsed_ms(a, b) for a, b in dev_ev) / Kd
+        # the two-pass kernels on the same inputs (pass 1 and pass 2 events on alternate calls)
+        plx.parallax_set_decode_path(plx.PLX_DECODE_TWO_PASS)
+        for _ in range(2):
+            plx.parallax_attn_decode(qd, kc, vc, Pd)
+        torch.cuda.synchronize()
+        dev_ev2 = [(ev.create(), ev.create()) for _ in range(Kd)]
+        t0 = time.perf_counter()
+        for i in range(Kd):
+            lib.parallax_set_kernel_events(plx.PLX_KERNEL_DECODE_PASS1 if i % 2 == 0 else plx.PLX_KERNEL_DECODE_PASS2,
+                                           *dev_ev2[i])
+            plx.parallax_attn_decode(qd, kc, vc, Pd)
+        lib.parallax_set_kernel_events(0, None, None)
+        torch.cuda.synchronize()
+        dt2 = (time.perf_counter() - t0) / Kd
+        plx.parallax_set_decode_path(plx.PLX_DECODE_AUTO)
+        p1 = [ev.elapsed_ms(a, b) for a, b in dev_ev2[0::2]]
+        p2 = [ev.elapsed_ms(a, b) for a, b in dev_ev2[1::2]]
         kms1, kms2 = sum(p1) / len(p1), sum(p2) / len(p2)
         t1, t2 = measured_traffic("decode_pass1"), measured_traffic("decode_pass2")
-        dec_traffic = None if t1 is None or t2 is None else round(t1 + t2)
-        cache_bytes = 2 * wd.batch * wd.seqlen_k * wd.heads_kv * wd.head_dim * 2
-        other = (wd.batch * wd.heads_q * wd.head_dim) * (2 + 4) + wd.heads_q * wd.head_dim ** 2 * 2
-        alg = cache_bytes + other
-        gbs = alg / dt / 1e9
+        gbs = alg / (kms_m * 1e-3) / 1e9
+        # matrix-core work of the single-read kernel as executed: per (key, query head) the moment's
+        # 2 d^2 twice (hi and lo halves of p k), o~ and kbar~ (2 d each, hi and lo weights share one
+        # product), the score (2 d)
+        d = wd.head_dim
+        mfma_flop = keys * (4 * d * d + 4 * d + 2 * d)
         result["decode"] = {
             "workload": f"decode: B={wd.batch} new queries, cache L={wd.seqlen_k}, Hq={wd.heads_q}, "
                         f"Hkv={wd.heads_kv}, d={wd.head_dim}, bf16",
+            "path": "single-read (one pass over the cache, key/value moment on MFMA)",
             "ms_per_call": round(dt * 1e3, 4), "tokens_per_s": round(wd.batch / dt, 1),
-            "kernels": {"pass1": {"avg_ms": round(kms1, 4), "gbs": round(cache_bytes / (kms1 * 1e-3) / 1e9, 1)},
-                        "pass2": {"avg_ms": round(kms2, 4), "gbs": round(cache_bytes / (kms2 * 1e-3) / 1e9, 1)}},
+            "kernels": {"single_read": {"avg_ms": round(kms_m, 4), "gbs": round(gbs, 1),
+                                        "mfma_tflops_executed": round(mfma_flop / (kms_m * 1e-3) / 1e12, 1),
+                                        "mfma_frac_of_bf16_peak": round(mfma_flop / (kms_m * 1e-3) / 1e12 /
+                                                                        PEAK_F16_TFLOPS, 4)}},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": dec_traffic,
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode_moment"),
                          "algorithmic_bytes_per_call": alg,
-                         "note": "algorithmic bytes = one read of the K/V cache; the two-pass method reads it twice"}}
-        kms = dt * 1e3
-        log(f"decode {kms:.3f} ms/kernel, {gbs:.0f} GB/s")
+                         "note": "single-read kernel; algorithmic bytes = one read of the K/V cache + q, P, out"},
+            "two_pass": {"ms_per_call": round(dt2 * 1e3, 4), "tokens_per_s": round(wd.batch / dt2, 1),
+                         "pass1": {"avg_ms": round(kms1, 4), "gbs": round(cache_bytes / (kms1 * 1e-3) / 1e9, 1),
+                                   "traffic": t1},
+                         "pass2": {"avg_ms": round(kms2, 4), "gbs": round(cache_bytes / (kms2 * 1e-3) / 1e9, 1),
+                                   "traffic": t2},
+                         "note": "two split-KV passes, each reading the cache once"}}
+        log(f"decode {dt * 1e3:.3f} ms/call (single-read kernel {kms_m:.3f} ms, {gbs:.0f} GB/s); "
+            f"two-pass {dt2 * 1e3:.3f} ms/call")
 
         # four new tokens per sequence (speculative decoding) against the same cache
         gq = torch.Generator(device=dev)

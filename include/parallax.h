@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define PARALLAX_ABI_VERSION 4
+#define PARALLAX_ABI_VERSION 5
 
 typedef enum {
   PLX_OK = 0,
@@ -94,7 +94,8 @@ typedef enum {
   PLX_KERNEL_DECODE_PASS1 = 3, /* decode: first split-KV pass (generic kernel on the fp32 path) */
   PLX_KERNEL_DECODE_PASS2 = 4, /* decode: second split-KV pass */
   PLX_KERNEL_BWD_DQ = 5,       /* backward: dq = P du + scale ds K from the stored ds (bf16 fast path) */
-  PLX_KERNEL_FWD_PROBE = 6     /* probe-form forward: the one-pass MFMA kernel */
+  PLX_KERNEL_FWD_PROBE = 6,    /* probe-form forward: the one-pass MFMA kernel */
+  PLX_KERNEL_DECODE_MOMENT = 7 /* decode: the single-read kernel (one read of the cache, key/value moment on MFMA) */
 } plx_kernel;
 
 /*
@@ -106,6 +107,19 @@ typedef enum {
  * thread-local.
  */
 void parallax_set_kernel_events(int kernel, void* before, void* after);
+
+/* Decode paths (parallax_set_decode_path). */
+typedef enum {
+  PLX_DECODE_AUTO = 0,     /* the single-read kernel where it applies (see parallax_attn_decode), else two-pass */
+  PLX_DECODE_TWO_PASS = 1  /* always the two-pass split-KV kernels (for comparison and timing) */
+} plx_decode_path;
+
+/*
+ * Selects the decode path for every later decode call of the process (all threads, all devices; the
+ * default is PLX_DECODE_AUTO).  Both paths compute the same operator to the bf16 tolerance; their results
+ * are not bit-identical.  Returns PLX_ERR_INVALID for a value outside plx_decode_path.
+ */
+plx_status parallax_set_decode_path(int32_t path);
 
 /* Library version of this header's ABI (PARALLAX_ABI_VERSION). */
 int parallax_abi_version(void);
@@ -237,6 +251,11 @@ size_t parallax_attn_decode_workspace(const plx_attn_desc* desc);
  *   seqlens_k [B] int32 device array (nullable)
  *   P        [Hq][d][d]            out [B][T][Hq][d] fp32, or bf16 when desc->out_dtype is PLX_BF16
  *   cor      [B][T][Hq] fp32 correction-to-output ratio as in the forward (nullable; bf16 fast path only)
+ * Kernels.  With T = 1, bf16, head_dim 128, heads_q / heads_kv of 1 or 2 and at least 256 (sequence, kv
+ * head) pairs, one workgroup per pair reads its cache rows once: it accumulates o, kbar and the
+ * softmax-weighted moment sum_j p_j v_j k_j^T (fp32, on the matrix cores) and forms the correction from
+ * them, c = (sum_j p_j v_j k_j^T) u - (u.kbar) o; no workspace is used.  Otherwise (or with
+ * PLX_DECODE_TWO_PASS) two split-KV passes run: o and kbar first, the correction with the finished u second.
  */
 plx_status parallax_attn_decode(const plx_attn_desc* desc,
                                 const void* q, const void* k_cache, const void* v_cache,
@@ -268,7 +287,8 @@ size_t parallax_attn_decode_paged_workspace(const plx_attn_desc* desc);
  * [0, num_pages) are clamped into the pool: that sequence's output is then wrong, but nothing is
  * read outside the caller's arrays.
  * Supported: bf16, head_dim 128 or 64, heads_q / heads_kv in {1, 2, 4, 8}, p_per_query 0; any other
- * valid desc returns PLX_ERR_UNSUPPORTED.  window as in parallax_attn_decode.
+ * valid desc returns PLX_ERR_UNSUPPORTED.  window as in parallax_attn_decode.  The single-read kernel (see
+ * parallax_attn_decode) runs here too when page_size >= 64.
  */
 plx_status parallax_attn_decode_paged(const plx_attn_desc* desc, const void* q,
                                       const void* k_pages, const void* v_pages,

@@ -16,6 +16,7 @@ Functions (same names as the C entry points):
     dq, dk, dv, drho  = parallax_attn_bwd_probe(q, k, v, rho, out, dout, lse, o, rk, causal=True, ...)
     out               = parallax_attn_decode_paged(q, k_pages, v_pages, block_table, P, seqlens=None, ...)
     out               = parallax_attn_decode_noalloc(q, k_cache, v_cache, P, seqlens=None, ...)  (no workspace)
+    parallax_set_decode_path(PLX_DECODE_TWO_PASS)   (process-wide decode kernel choice; PLX_DECODE_AUTO default)
 
 Layouts: q [B,Tq,Hq,d] (decode [B,Hq,d]); k, v [B,Tk,Hkv,d]; P [Hq,d,d] (or
 [B,Tq,Hq,d,d] per query, forward only); outputs float32.
@@ -33,7 +34,8 @@ LIB_PATH = os.path.join(_PKG, "libparallax.so")
 PLX_OK, PLX_ERR_INVALID, PLX_ERR_UNSUPPORTED, PLX_ERR_WORKSPACE, PLX_ERR_HIP = range(5)
 PLX_F32, PLX_BF16 = 0, 1
 (PLX_KERNEL_FWD, PLX_KERNEL_BWD_ROWS, PLX_KERNEL_BWD_KEYS, PLX_KERNEL_DECODE_PASS1, PLX_KERNEL_DECODE_PASS2,
- PLX_KERNEL_BWD_DQ, PLX_KERNEL_FWD_PROBE) = range(7)
+ PLX_KERNEL_BWD_DQ, PLX_KERNEL_FWD_PROBE, PLX_KERNEL_DECODE_MOMENT) = range(8)
+PLX_DECODE_AUTO, PLX_DECODE_TWO_PASS = 0, 1
 
 
 class PlxAttnDesc(ctypes.Structure):
@@ -57,6 +59,7 @@ _vp, _sz, _st = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
 _DESC = ctypes.POINTER(PlxAttnDesc)
 SIGNATURES = {
     "parallax_set_kernel_events": (None, [ctypes.c_int, _vp, _vp]),
+    "parallax_set_decode_path": (_st, [ctypes.c_int32]),
     "parallax_abi_version": (ctypes.c_int, []),
     "parallax_status_string": (ctypes.c_char_p, [_st]),
     "parallax_last_error": (ctypes.c_char_p, []),
@@ -266,6 +269,12 @@ def parallax_attn_bwd(q, k, v, P, out, dout, lse, kbar, o_sa, causal=True, windo
                                  _ptr(dout), _ptr(lse), _ptr(kbar), _ptr(o_sa), _ptr(dq), _ptr(dk),
                                  _ptr(dv), _ptr(dP), _ptr(ws), nws, _stream()))
     return dq, dk, dv, dP
+
+
+def parallax_set_decode_path(path):
+    """Selects the decode kernels for the whole process: PLX_DECODE_AUTO (the single-read kernel where it
+    applies) or PLX_DECODE_TWO_PASS (always the two split-KV passes)."""
+    _check(get_lib().parallax_set_decode_path(int(path)))
 
 
 def parallax_attn_decode(q, k_cache, v_cache, P, seqlens=None, window=0, scale=None, out_dtype=torch.float32,

@@ -163,6 +163,20 @@ __device__ __forceinline__ void lds_dma16(const void* src, void* lds_base) {
                : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory");
 }
+// The same copy with the global address split into a wave-uniform base (scalar registers) and a 32-bit
+// per-lane byte offset: the scalar-base addressing form, which needs no 64-bit address per lane.
+__device__ __forceinline__ void lds_dma16_sbase(const void* base, uint32_t voff, void* lds_base) {
+  const uint32_t lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lds_base);
+  const uint64_t bv = reinterpret_cast<uintptr_t>(base);
+  const uint64_t bs = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(bv >> 32))) << 32) |
+                      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(bv)));
+  uint32_t saved_m0;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\t"
+               "s_mov_b32 m0, %0"
+               : "=&s"(saved_m0)
+               : "v"(voff), "s"(bs), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
 // The wait is issued twice: as assembly (always kept) and as the builtin, so that the compiler also
 // knows that its own loads issued before it have completed.
 __device__ __forceinline__ void lds_dma_wait() {

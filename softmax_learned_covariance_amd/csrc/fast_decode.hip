@@ -577,6 +577,8 @@ void launch_all(const DecParams& p, const dim3& grid, int Hq, int BT, hipStream_
 hipError_t launch_fast_decode(const Geom& g, const void* q, const void* kc, const void* vc, const int32_t* seqlens,
                               const void* P, void* out, float* cor, void* ws, hipStream_t stream,
                               const PagedCache* paged) {
+  if (decode_path() == PLX_DECODE_AUTO && moment_decode_supported(g, paged))
+    return launch_moment_decode(g, q, kc, vc, seqlens, P, out, cor, stream, paged);
   const DecWs w = dec_layout(g, ws);
   DecParams p{};
   p.q = static_cast<const u16*>(q);

@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "plx_internal.h"
@@ -16,6 +17,7 @@ thread_local char g_last_error[512] = "";
 thread_local hipEvent_t g_ev_before = nullptr;
 thread_local hipEvent_t g_ev_after = nullptr;
 thread_local int g_ev_kernel = -1;
+std::atomic<int> g_decode_path{PLX_DECODE_AUTO};
 
 plx_status fail(plx_status s, const char* fmt, ...) {
   va_list ap;
@@ -153,6 +155,8 @@ hipError_t side_join(const SideLane& lane) {
   return e;
 }
 
+int decode_path() { return g_decode_path.load(); }
+
 void mark_begin(int kernel, hipStream_t stream) {
   if (g_ev_before && kernel == g_ev_kernel) (void)hipEventRecord(g_ev_before, stream);
 }
@@ -198,6 +202,13 @@ void parallax_set_kernel_events(int kernel, void* before, void* after) {
   g_ev_kernel = kernel;
   g_ev_before = static_cast<hipEvent_t>(before);
   g_ev_after = static_cast<hipEvent_t>(after);
+}
+
+plx_status parallax_set_decode_path(int32_t path) {
+  if (path != PLX_DECODE_AUTO && path != PLX_DECODE_TWO_PASS)
+    return fail(PLX_ERR_INVALID, "parallax_set_decode_path: path must be PLX_DECODE_AUTO or PLX_DECODE_TWO_PASS");
+  g_decode_path.store(path);
+  return PLX_OK;
 }
 
 int parallax_abi_version(void) { return PARALLAX_ABI_VERSION; }

@@ -83,6 +83,15 @@ struct PagedCache {
 hipError_t launch_fast_decode(const Geom& g, const void* q, const void* kc, const void* vc,
                               const int32_t* seqlens, const void* P, void* out, float* cor, void* ws,
                               hipStream_t stream, const PagedCache* paged = nullptr);
+// Single-read decode: one workgroup per (sequence, kv head) reads the cache once and accumulates the
+// softmax-weighted key/value moment on the matrix cores; no workspace.  Applies to bf16, d = 128, one new
+// token, 1 or 2 query heads per kv head, at least 256 (sequence, kv head) pairs, pages of >= 64 keys.
+// launch_fast_decode takes it by itself where it applies, unless the two-pass path is forced.
+bool moment_decode_supported(const Geom& g, const PagedCache* paged);
+hipError_t launch_moment_decode(const Geom& g, const void* q, const void* kc, const void* vc, const int32_t* seqlens,
+                                const void* P, void* out, float* cor, hipStream_t stream, const PagedCache* paged);
+// The decode path in force (a plx_decode_path value; parallax_set_decode_path sets it for the process).
+int decode_path();
 
 // Records the profiling hook's `before` / `after` event on `stream` when `kernel` (a plx_kernel)
 // is the one selected (no-op otherwise).

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(plx):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     out = subprocess.run(["nm", "-D", "--defined-only", plx.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (parallax_\w+)", out))
     missing = [n for n in names if n not in exported]
@@ -272,3 +272,13 @@ def test_traffic_summary_rows_parse():
         assert len(f) == 6, f
         float(f[2]), float(f[3]), float(f[4])
         assert len(f[5]) == 16
+
+
+def test_decode_path_selection(plx):
+    """The process-wide decode path accepts its two values only (no GPU call is made)."""
+    lib = plx.get_lib()
+    for bad in (2, -1, 99):
+        assert lib.parallax_set_decode_path(bad) == plx.PLX_ERR_INVALID
+        assert b"decode_path" in lib.parallax_last_error()
+    assert lib.parallax_set_decode_path(plx.PLX_DECODE_TWO_PASS) == plx.PLX_OK
+    assert lib.parallax_set_decode_path(plx.PLX_DECODE_AUTO) == plx.PLX_OK

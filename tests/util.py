@@ -36,3 +36,20 @@ def ensure_built():
     if not os.path.exists(lib):
         from softmax_learned_covariance_amd import build
         build.build(verbose=False)
+
+
+def to_pages(kc, vc, page, spare=3, seed=0):
+    """Scatter a contiguous cache [B,L,Hkv,d] into a shuffled page pool (storage only) and its table."""
+    B, L, Hkv, d = kc.shape
+    npb = (L + page - 1) // page
+    pad = npb * page - L
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    perm = torch.randperm(B * npb + spare, generator=g)[:B * npb].to(kc.device)
+    pools = []
+    for c in (kc, vc):
+        cp = torch.nn.functional.pad(c, (0, 0, 0, 0, 0, pad)) if pad else c
+        pool = torch.randn((B * npb + spare, page, Hkv, d), device=kc.device).to(c.dtype)   # junk in spare pages
+        pool[perm] = cp.reshape(B * npb, page, Hkv, d)
+        pools.append(pool)
+    return pools[0], pools[1], perm.reshape(B, npb).to(torch.int32).contiguous()
