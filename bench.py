@@ -142,11 +142,23 @@ class HipEvents:
         return ms.value
 
 
-def cpu_baseline(w, target_s=15.0):
-    """The oracle (numpy float64) timed on this host on a bounded sample of the workload.
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
-    Sample: batch entry 0 (all query heads, all T rows), forward + backward;
-    scaled to TFLOP/s with the same algorithmic count.
+
+def cpu_baseline(w):
+    """The oracle (numpy, float64 as in every parity test, and its float32 timing mode) timed on this
+    host on a bounded sample of the workload.
+
+    Sample: batch entry 0 (all query heads, all T rows), forward + backward; scaled to TFLOP/s with the
+    same algorithmic count as the GPU figures.
     """
     import numpy as np
     import torch
@@ -160,15 +172,28 @@ def cpu_baseline(w, target_s=15.0):
     ws = W.scaled(w, batch=1)
     q, k, v, P, dout = W.make_inputs(ws, device="cpu", with_dout=True)
     h = lambda t: t.to(torch.float64).numpy()  # noqa: E731
+    fl = fwd_flops(ws) + bwd_flops(ws)
     t0 = time.perf_counter()
     oracle.fwd(h(q), h(k), h(v), h(P), causal=True)
     oracle.bwd(h(q), h(k), h(v), h(P), h(dout), causal=True)
     dt = time.perf_counter() - t0
-    fl = fwd_flops(ws) + bwd_flops(ws)
+    # the float32 mode on half the heads (8 query, 4 key/value heads), to keep the host time bounded
+    w32 = W.scaled(ws, heads_q=max(1, ws.heads_q // 2), heads_kv=max(1, ws.heads_kv // 2))
+    q, k, v, P, dout = W.make_inputs(w32, device="cpu", with_dout=True)
+    fl32 = fwd_flops(w32) + bwd_flops(w32)
+    with oracle.precision(np.float32):
+        t0 = time.perf_counter()
+        oracle.fwd(h(q), h(k), h(v), h(P), causal=True)
+        oracle.bwd(h(q), h(k), h(v), h(P), h(dout), causal=True)
+        dt32 = time.perf_counter() - t0
     return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"numpy float64 oracle, forward+backward of batch entry 0 (all {ws.heads_q} query heads), "
                       f"all {ws.seqlen_q} rows of the {w.name} workload: {fl / 1e9:.1f} GFLOP in {dt:.1f} s",
-            "seconds": round(dt, 2)}
+            "seconds": round(dt, 2),
+            "fp32": {"value": round(fl32 / dt32 / 1e12, 6), "unit": "TFLOP/s", "seconds": round(dt32, 2),
+                     "sample": f"the same oracle in its float32 timing mode, batch entry 0 with {w32.heads_q} query "
+                               f"and {w32.heads_kv} key/value heads: {fl32 / 1e9:.1f} GFLOP"},
+            "nproc": os.cpu_count(), "cpu_model": _cpu_model(), "blas_threads": int(threads)}
 
 
 def main():
@@ -182,6 +207,13 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the decode batch/context sweep")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the layer06 forward and train06 training-step objects")
+    ap.add_argument("--probe-only", action="store_true",
+                    help="time only the probe form (a profiling run that separates its kernels from the "
+                         "projector form's, which share kernel names)")
+    ap.add_argument("--samples", type=int, default=12,
+                    help="extra kernel-event samples per backward kernel (beyond the timed steps)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy, the reference for HBM traffic counters")
     args = ap.parse_args()
@@ -215,77 +247,97 @@ def main():
     ev = HipEvents()
     split = args.split_rows
 
-    def step():
-        out, lse, kbar, o = plx.parallax_attn_fwd(q, k, v, P, split_rows=split)
-        plx.parallax_attn_bwd(q, k, v, P, out, dout, lse, kbar, o, split_rows=split)
-
-    for i in range(args.warmup):
-        step()
-        torch.cuda.synchronize()
-        log(f"warmup step {i + 1}/{args.warmup} done")
-
-    # Timed region: K steps.  The kernel-event hook brackets one kernel per library call: every
-    # step times the forward kernel, and the backward cycles through its three main kernels.
-    K = args.steps
-    bwd_cycle = (("bwd_rows", plx.PLX_KERNEL_BWD_ROWS), ("bwd_keys", plx.PLX_KERNEL_BWD_KEYS),
-                 ("bwd_dq", plx.PLX_KERNEL_BWD_DQ))
-    evs = {n: [] for n in ("fwd", "bwd_rows", "bwd_keys", "bwd_dq")}
-    pool = [(ev.create(), ev.create()) for _ in range(2 * K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        e_f = pool[2 * i]
-        lib.parallax_set_kernel_events(plx.PLX_KERNEL_FWD, *e_f)
-        out, lse, kbar, o = plx.parallax_attn_fwd(q, k, v, P, split_rows=split)
-        which, kid = bwd_cycle[i % 3]
-        e_b = pool[2 * i + 1]
-        lib.parallax_set_kernel_events(kid, *e_b)
-        plx.parallax_attn_bwd(q, k, v, P, out, dout, lse, kbar, o, split_rows=split)
-        evs["fwd"].append(e_f)
-        evs[which].append(e_b)
-    lib.parallax_set_kernel_events(0, None, None)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    log(f"timed {K} steps in {elapsed:.3f} s")
-
     # the fast path leaves rows < split_rows to its hi/lo-split kernels
     fast = w.dtype == "bf16" and w.head_dim == 128
     r0 = (256 if split < 0 else split) if fast else 0
     r0 = min(r0, w.seqlen_q)
-    kern = {}
-    for n, flops_fn in (("fwd", fwd_flops), ("bwd_rows", bwd_rows_flops), ("bwd_keys", bwd_keys_flops),
-                        ("bwd_dq", bwd_dq_flops)):
-        if not evs[n]:
-            continue
-        ms = sorted(ev.elapsed_ms(a, b) for a, b in evs[n])
-        avg = sum(ms) / len(ms)
-        fl = flops_fn(w, r0)
-        kern[n] = {"avg_ms": round(avg, 4), "median_ms": round(ms[len(ms) // 2], 4), "launches": len(ms),
-                   "algorithmic_flop": fl, "tflops": round(fl / (avg * 1e-3) / 1e12, 3),
-                   "frac_of_peak": round(fl / (avg * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4)}
-    ms_step = elapsed / K * 1e3
-    step_flops = fwd_flops(w) + bwd_flops(w)
-    value = step_flops / (ms_step * 1e-3) / 1e12
-    dom = max(kern, key=lambda n: kern[n]["avg_ms"])
-    dk = kern[dom]
-    tr = measured_traffic(dom)
-    roofline = {"bound": "mfma", "achieved": dk["tflops"], "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(dk["tflops"] / PEAK_F16_TFLOPS, 4), "traffic": None if tr is None else round(tr),
-                "traffic_unit": "bytes per launch (HBM, FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
-                "kernel": dom, "avg_ms": dk["avg_ms"], "algorithmic_flop_per_launch": dk["algorithmic_flop"]}
-    result = {
-        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f16",
-        "data": "synthetic (seeded N(0,1) inputs rounded to bf16, K rows normed to sqrt(d), P ~ N(0, 0.02^2))",
-        "config": {"workload": f"{w.name}: Parallax layer forward+backward, B={w.batch}, T={w.seqlen_q}, "
-                               f"Hq={w.heads_q}, Hkv={w.heads_kv}, d={w.head_dim}, causal, bf16 inputs, fp32 outputs",
-                   "global_batch": w.batch, "seq_len": w.seqlen_q, "parallelism": "single GPU",
-                   "split_rows": r0},
-        "tokens_per_s": round(w.batch * w.seqlen_q / (ms_step * 1e-3), 1),
-        "kernels": kern,
-        "roofline": roofline,
-    }
+    def kernel_samples(call, kid, n):
+        """n calls of `call` with the event hook on kernel `kid`: that kernel's launch times (ms)."""
+        pairs = [(ev.create(), ev.create()) for _ in range(n)]
+        for e in pairs:
+            lib.parallax_set_kernel_events(kid, *e)
+            call()
+        lib.parallax_set_kernel_events(0, None, None)
+        torch.cuda.synchronize()
+        return [ev.elapsed_ms(a, b) for a, b in pairs]
+
+    bwd_cycle = (("bwd_rows", plx.PLX_KERNEL_BWD_ROWS), ("bwd_keys", plx.PLX_KERNEL_BWD_KEYS),
+                 ("bwd_dq", plx.PLX_KERNEL_BWD_DQ))
+    K = args.steps
+    if args.probe_only:
+        result = {"metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1,
+                  "note": "probe form only (a profiling run)"}
+    else:
+        def step():
+            out, lse, kbar, o = plx.parallax_attn_fwd(q, k, v, P, split_rows=split)
+            plx.parallax_attn_bwd(q, k, v, P, out, dout, lse, kbar, o, split_rows=split)
+
+        for i in range(args.warmup):
+            step()
+            torch.cuda.synchronize()
+            log(f"warmup step {i + 1}/{args.warmup} done")
+
+        # Timed region: K steps.  The kernel-event hook brackets one kernel per library call: every
+        # step times the forward kernel, and the backward cycles through its three main kernels.
+        evs = {n: [] for n in ("fwd", "bwd_rows", "bwd_keys", "bwd_dq")}
+        pool = [(ev.create(), ev.create()) for _ in range(2 * K)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            e_f = pool[2 * i]
+            lib.parallax_set_kernel_events(plx.PLX_KERNEL_FWD, *e_f)
+            out, lse, kbar, o = plx.parallax_attn_fwd(q, k, v, P, split_rows=split)
+            which, kid = bwd_cycle[i % 3]
+            e_b = pool[2 * i + 1]
+            lib.parallax_set_kernel_events(kid, *e_b)
+            plx.parallax_attn_bwd(q, k, v, P, out, dout, lse, kbar, o, split_rows=split)
+            evs["fwd"].append(e_f)
+            evs[which].append(e_b)
+        lib.parallax_set_kernel_events(0, None, None)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        log(f"timed {K} steps in {elapsed:.3f} s")
+
+        # more samples of each backward kernel, outside the timed region
+        extra = {}
+        for which, kid in bwd_cycle:
+            extra[which] = kernel_samples(
+                lambda: plx.parallax_attn_bwd(q, k, v, P, out, dout, lse, kbar, o, split_rows=split), kid, args.samples)
+
+        kern = {}
+        for n, flops_fn in (("fwd", fwd_flops), ("bwd_rows", bwd_rows_flops), ("bwd_keys", bwd_keys_flops),
+                            ("bwd_dq", bwd_dq_flops)):
+            if not evs[n]:
+                continue
+            ms = sorted([ev.elapsed_ms(a, b) for a, b in evs[n]] + extra.get(n, []))
+            avg = sum(ms) / len(ms)
+            fl = flops_fn(w, r0)
+            kern[n] = {"avg_ms": round(avg, 4), "median_ms": round(ms[len(ms) // 2], 4), "launches": len(ms),
+                       "algorithmic_flop": fl, "tflops": round(fl / (avg * 1e-3) / 1e12, 3),
+                       "frac_of_peak": round(fl / (avg * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4)}
+        ms_step = elapsed / K * 1e3
+        step_flops = fwd_flops(w) + bwd_flops(w)
+        value = step_flops / (ms_step * 1e-3) / 1e12
+        dom = max(kern, key=lambda n: kern[n]["avg_ms"])
+        dk = kern[dom]
+        tr = measured_traffic(dom)
+        roofline = {"bound": "mfma", "achieved": dk["tflops"], "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(dk["tflops"] / PEAK_F16_TFLOPS, 4), "traffic": None if tr is None else round(tr),
+                    "traffic_unit": "bytes per launch (HBM, FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
+                    "kernel": dom, "avg_ms": dk["avg_ms"], "algorithmic_flop_per_launch": dk["algorithmic_flop"]}
+        result = {
+            "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+            "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+            "data": "synthetic (seeded N(0,1) inputs rounded to bf16, K rows normed to sqrt(d), P ~ N(0, 0.02^2))",
+            "config": {"workload": f"{w.name}: Parallax layer forward+backward, B={w.batch}, T={w.seqlen_q}, "
+                                   f"Hq={w.heads_q}, Hkv={w.heads_kv}, d={w.head_dim}, causal, bf16 inputs, fp32 outputs",
+                       "global_batch": w.batch, "seq_len": w.seqlen_q, "parallelism": "single GPU",
+                       "split_rows": r0},
+            "tokens_per_s": round(w.batch * w.seqlen_q / (ms_step * 1e-3), 1),
+            "kernels": kern,
+            "roofline": roofline,
+        }
 
     if not args.no_probe:
         log("probe-form forward")
@@ -336,6 +388,85 @@ def main():
                                    "algorithmic_flop": sfl, "steps": Kp}
         log(f"probe step {dts * 1e3:.3f} ms ({sfl / dts / 1e12:.0f} TFLOP/s)")
         del rho
+
+    if not args.no_configs:
+        result["configs"] = {}
+        # layer06 (0.6B-like layer) forward
+        w2 = W.WORKLOADS["layer06"]
+        log(f"config {w2.name} forward")
+        q2, k2, v2, P2 = W.make_inputs(w2, device=dev)
+        fwd2 = lambda: plx.parallax_attn_fwd(q2, k2, v2, P2, split_rows=split)  # noqa: E731
+        for _ in range(2):
+            fwd2()
+        torch.cuda.synchronize()
+        n2 = max(10, K)
+        t0 = time.perf_counter()
+        for _ in range(n2):
+            fwd2()
+        torch.cuda.synchronize()
+        dt2c = (time.perf_counter() - t0) / n2
+        ks2 = kernel_samples(fwd2, plx.PLX_KERNEL_FWD, n2)
+        r2 = min(r0, w2.seqlen_q)
+        kfl = fwd_flops(w2, r2)
+        kavg = sum(ks2) / len(ks2)
+        result["configs"]["layer06_fwd"] = {
+            "workload": f"{w2.name}: forward, B={w2.batch}, T={w2.seqlen_q}, Hq={w2.heads_q}, Hkv={w2.heads_kv}, "
+                        f"d={w2.head_dim}, causal, bf16",
+            "ms_per_call": round(dt2c * 1e3, 4), "tflops": round(fwd_flops(w2) / dt2c / 1e12, 3),
+            "tokens_per_s": round(w2.batch * w2.seqlen_q / dt2c, 1),
+            "roofline": {"bound": "mfma", "kernel": "fwd", "avg_ms": round(kavg, 4), "launches": len(ks2),
+                         "achieved": round(kfl / (kavg * 1e-3) / 1e12, 3), "peak": PEAK_F16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(kfl / (kavg * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
+                         "algorithmic_flop_per_launch": kfl}}
+        log(f"layer06 forward {dt2c * 1e3:.3f} ms/call, kernel {kavg:.3f} ms")
+        del q2, k2, v2, P2
+        # train06 (0.6B-like training step): forward + backward
+        w4 = W.WORKLOADS["train06"]
+        log(f"config {w4.name} training step")
+        q4_, k4_, v4_, P4_, d4_ = W.make_inputs(w4, device=dev, with_dout=True)
+        f4 = plx.parallax_attn_fwd(q4_, k4_, v4_, P4_, split_rows=split)
+
+        def step4():
+            f = plx.parallax_attn_fwd(q4_, k4_, v4_, P4_, split_rows=split)
+            plx.parallax_attn_bwd(q4_, k4_, v4_, P4_, f[0], d4_, *f[1:], split_rows=split)
+
+        step4()
+        torch.cuda.synchronize()
+        n4 = max(6, K)
+        t0 = time.perf_counter()
+        for _ in range(n4):
+            step4()
+        torch.cuda.synchronize()
+        dt4c = (time.perf_counter() - t0) / n4
+        r4 = min(r0, w4.seqlen_q)
+        k4 = {}
+        calls = {"fwd": (lambda: plx.parallax_attn_fwd(q4_, k4_, v4_, P4_, split_rows=split), plx.PLX_KERNEL_FWD,
+                         fwd_flops)}
+        bcall = lambda: plx.parallax_attn_bwd(q4_, k4_, v4_, P4_, f4[0], d4_, *f4[1:], split_rows=split)  # noqa: E731
+        for n_, kid in bwd_cycle:
+            calls[n_] = (bcall, kid, {"bwd_rows": bwd_rows_flops, "bwd_keys": bwd_keys_flops,
+                                      "bwd_dq": bwd_dq_flops}[n_])
+        for n_, (call, kid, ffn) in calls.items():
+            ms_ = kernel_samples(call, kid, max(8, args.samples))
+            avg = sum(ms_) / len(ms_)
+            fl_ = ffn(w4, r4)
+            k4[n_] = {"avg_ms": round(avg, 4), "launches": len(ms_), "algorithmic_flop": fl_,
+                      "tflops": round(fl_ / (avg * 1e-3) / 1e12, 3),
+                      "frac_of_peak": round(fl_ / (avg * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4)}
+        dom4 = max(k4, key=lambda n_: k4[n_]["avg_ms"])
+        sfl4 = fwd_flops(w4) + bwd_flops(w4)
+        result["configs"]["train06_step"] = {
+            "workload": f"{w4.name}: forward + backward, B={w4.batch}, T={w4.seqlen_q}, Hq={w4.heads_q}, "
+                        f"Hkv={w4.heads_kv}, d={w4.head_dim}, causal, bf16",
+            "ms_per_step": round(dt4c * 1e3, 4), "tflops": round(sfl4 / dt4c / 1e12, 3),
+            "tokens_per_s": round(w4.batch * w4.seqlen_q / dt4c, 1), "kernels": k4,
+            "roofline": {"bound": "mfma", "kernel": dom4, "avg_ms": k4[dom4]["avg_ms"],
+                         "achieved": k4[dom4]["tflops"], "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": k4[dom4]["frac_of_peak"],
+                         "algorithmic_flop_per_launch": k4[dom4]["algorithmic_flop"]}}
+        log(f"train06 step {dt4c * 1e3:.3f} ms ({sfl4 / dt4c / 1e12:.0f} TFLOP/s)")
+        del q4_, k4_, v4_, P4_, d4_, f4
+        torch.cuda.empty_cache()
 
     if not args.no_decode:
         wd = W.WORKLOADS["decode"]

@@ -1,6 +1,7 @@
 """CPU oracle for the Parallax attention operator (test infrastructure only).
 
-Plain, slow, float64 numpy.  Only the tests, the smoke check and the
+Plain, slow, float64 numpy (a float32 mode exists for the CPU timing baseline
+only; every parity check runs in float64).  Only the tests, the smoke check and the
 benchmark's CPU-baseline leg may import this module; the GPU library never
 does, and this module imports nothing from it.
 
@@ -37,13 +38,32 @@ pinned (see the module docstrings of tests/test_oracle_pins.py).
 """
 from __future__ import annotations
 
+import contextlib
+
 import numpy as np
 
 ROW_BLOCK = 256
 
 
+_WORK_DTYPE = np.float64
+
+
 def _as_f64(x):
-    return np.asarray(x, dtype=np.float64)
+    """The working precision of every function here: float64 unless `precision` says otherwise."""
+    return np.asarray(x, dtype=_WORK_DTYPE)
+
+
+@contextlib.contextmanager
+def precision(dtype):
+    """Runs the oracle's arithmetic in `dtype` inside the block (np.float32 for the CPU timing baseline;
+    the default float64 is what every test uses)."""
+    global _WORK_DTYPE
+    old = _WORK_DTYPE
+    _WORK_DTYPE = np.dtype(dtype).type
+    try:
+        yield
+    finally:
+        _WORK_DTYPE = old
 
 
 def visible_range(i: int, Tq: int, Tk: int, causal: bool, window: int):
@@ -111,10 +131,10 @@ def fwd(q, k, v, P, causal=True, window=0, scale=None, rows=None):
     per_query = P.ndim == 5
     if scale is None or scale <= 0:
         scale = 1.0 / np.sqrt(d)
-    out = np.full(q.shape, np.nan)
-    kbar = np.full(q.shape, np.nan)
-    osa = np.full(q.shape, np.nan)
-    lse = np.full((B, Hq, Tq), np.nan)
+    out = np.full(q.shape, np.nan, dtype=q.dtype)
+    kbar = np.full(q.shape, np.nan, dtype=q.dtype)
+    osa = np.full(q.shape, np.nan, dtype=q.dtype)
+    lse = np.full((B, Hq, Tq), np.nan, dtype=q.dtype)
     for b in range(B):
         for h in range(Hq):
             g = h // grp
@@ -165,10 +185,10 @@ def fwd_probe(q, k, v, rho, causal=True, window=0, scale=None, rows=None):
     grp = Hq // Hkv
     if scale is None or scale <= 0:
         scale = 1.0 / np.sqrt(d)
-    out = np.full(q.shape, np.nan)
-    osa = np.full(q.shape, np.nan)
-    lse = np.full((B, Hq, Tq), np.nan)
-    rk = np.full((B, Hq, Tq), np.nan)
+    out = np.full(q.shape, np.nan, dtype=q.dtype)
+    osa = np.full(q.shape, np.nan, dtype=q.dtype)
+    lse = np.full((B, Hq, Tq), np.nan, dtype=q.dtype)
+    rk = np.full((B, Hq, Tq), np.nan, dtype=q.dtype)
     for b in range(B):
         for h in range(Hq):
             g = h // grp
@@ -312,7 +332,7 @@ def decode(q, k_cache, v_cache, P, seqlens=None, scale=None):
     q = _as_f64(q)
     B, Hq, d = q.shape
     Lmax = k_cache.shape[1]
-    out = np.zeros((B, Hq, d))
+    out = np.zeros((B, Hq, d), dtype=q.dtype)
     for b in range(B):
         L = Lmax if seqlens is None else int(seqlens[b])
         if L == 0:
@@ -340,7 +360,7 @@ def decode_paged(q, k_pages, v_pages, block_table, P, seqlens=None, seqlen_k=Non
     B = q.shape[0]
     page = k_pages.shape[1]
     Lmax = block_table.shape[1] * page if seqlen_k is None else int(seqlen_k)
-    out = np.zeros(q.shape)
+    out = np.zeros(q.shape, dtype=q.dtype)
     for b in range(B):
         L = Lmax if seqlens is None else min(max(int(seqlens[b]), 0), Lmax)
         lo = max(0, L - window) if window > 0 else 0
