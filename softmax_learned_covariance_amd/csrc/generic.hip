@@ -3,10 +3,10 @@
 // One 64-lane wave owns one query row (forward, backward row passes) or one key
 // row (backward key pass); lane l holds dimensions l and l + 64.  Dot products
 // are butterfly reductions across the wave, so every lane ends with the same
-// bits.  These kernels are the fp32 path of the library (fp32 inputs, per-query
-// projectors, head dims other than 128) and compute the first query rows of the
-// bf16 fast path, where few visible keys make the output large and a 16-bit
-// operand would be too coarse.
+// bits.  These kernels are the fp32 path of the library: fp32 inputs, per-query
+// projectors, head dims other than 128 and 64, and query-head groups outside
+// {1, 2, 4, 8}.  (The first query rows of the bf16 path, where few visible keys
+// make the output large, run on that path's hi + lo operand-pair kernels.)
 //
 // Formulas: the output equation of the gist.science technical summary of
 // "Parallax: Parameterized Local Linear Attention for Language Modeling",
