@@ -30,7 +30,8 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kTile = 64;          // keys per LDS tile
 constexpr int kRowH = kD + 8;      // padded LDS row (bf16 elements)
-constexpr int kMaxG = 8;          // rows (query head, new token) per workgroup
+constexpr int kMaxG = 8;          // rows (query head, new token) per workgroup of the fp32 kernels
+constexpr int kMaxRowsM = 16;     // rows per workgroup of the matrix-core kernels
 
 struct DecParams {
   const u16 *q, *kc, *vc, *P;
@@ -491,6 +492,318 @@ __global__ __launch_bounds__(128) void k_dec_finish(DecParams p) {
   }
 }
 
+// ------------------ pass 1 and pass 2 on the matrix cores (3 to 16 rows) ------------------
+// With 3 to 16 rows (query heads x new tokens) per workgroup the fp32 dot products and sums above take
+// more VALU time than a tile takes to arrive.  These variants form the scores (and pass 2's u.k), o, kbar
+// and the correction's sum W v with v_mfma_f32_16x16x32_bf16, rows padded to 16:
+//   scores  S^T (16 keys x 16 rows) = K (16 keys x 32 dims) . Q^T (32 dims x 16 rows), 4 dim steps;
+//   sums    o^T (16 dims x 16 rows) += V^T (16 dims x 32 keys) . P~^T (32 keys x 16 rows), 2 key steps.
+// Lane l always holds row n = l % 16 of its results, so the running maximum, its rescale and the row
+// sums stay per lane.  Wave w scores keys 16 w .. 16 w + 15 of each 64-key tile and forms the sums for
+// dims 32 w .. 32 w + 31 over the whole tile.  The cache's bf16 values and q are used as they are; u, the
+// weights p~ (pass 1) and W = p (u.k - alpha) (pass 2) are bf16 pairs hi + lo (hi rounded, lo the rounded
+// remainder: about 16 bits), each product taking two MFMAs, and l and sum W are summed from the same
+// pairs, so o = sum p~ v / l and c = sum W (v - o) hold for the weights used.  (Single bf16 weights give
+// 2.6e-2 of max error / rms on a sequence of three keys, whose rows are several times the tensor's rms.)
+typedef __bf16 dbf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 dbf16x4 __attribute__((ext_vector_type(4)));
+typedef float df32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRowM = 144;   // tile row stride in bf16 elements (288 bytes: the score row reads and the
+                             // transpose loads of a 16-lane group hit distinct banks)
+constexpr int kPRow = 72;    // weight-tile row stride (144 bytes: the 16 rows' reads hit distinct banks)
+constexpr float kMomTau = 8.f;
+
+struct __align__(16) MDecTiles {
+  u16 k[kTile * kRowM];
+  u16 v[kTile * kRowM];
+  u16 pw[2][16 * kPRow];     // bf16 weights per (hi / lo, row, key)
+  float smax[4][16];         // per (score wave, row): the wave's 16-key maximum (pass 1)
+  float rsum[4][16];         // per (score wave, row): l (pass 1) or sum W (pass 2), after the loop
+};
+
+__device__ __forceinline__ void mtile_store(const TileRegs& R, MDecTiles& T, int tid) {
+  const int r = tid >> 4, c = tid & 15;
+  u16* k = &T.k[r * kRowM + c * 8];
+  u16* v = &T.v[r * kRowM + c * 8];
+  *reinterpret_cast<u32x4*>(k) = R.k0;
+  *reinterpret_cast<u32x4*>(k + 16 * kRowM) = R.k1;
+  *reinterpret_cast<u32x4*>(k + 32 * kRowM) = R.k2;
+  *reinterpret_cast<u32x4*>(k + 48 * kRowM) = R.k3;
+  *reinterpret_cast<u32x4*>(v) = R.v0;
+  *reinterpret_cast<u32x4*>(v + 16 * kRowM) = R.v1;
+  *reinterpret_cast<u32x4*>(v + 32 * kRowM) = R.v2;
+  *reinterpret_cast<u32x4*>(v + 48 * kRowM) = R.v3;
+}
+
+// A operand V^T or K^T (16 dims x 32 keys) for dims 16 db + [0, 16) and keys 32 ks + [0, 32): lane l gets
+// dim 16 db + l % 16 and keys 32 ks + 8 (l / 16) + [0, 8), by two transpose loads (ds_read_b64_tr_b16:
+// lane i of a 16-lane group receives element i % 4 of the 8 bytes that lane 4 j + i / 4 addresses, as its
+// element j), source lane 4 j + a pointing at dims 16 db + 4 a + [0, 4) of key 32 ks + 8 (l / 16) + j
+// (+ 4 for the second load).
+__device__ __forceinline__ dbf16x8 mcols(const u16* tile, int l, int ks, int db) {
+  const int G = l >> 4, j = (l >> 2) & 3, a = l & 3;
+  const u16* src = tile + (32 * ks + 8 * G + j) * kRowM + 16 * db + 4 * a;
+  const v4i16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)src);
+  const v4i16 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(src + 4 * kRowM));
+  const dbf16x4 xb = __builtin_bit_cast(dbf16x4, x), yb = __builtin_bit_cast(dbf16x4, y);
+  return __builtin_shufflevector(xb, yb, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// A operand K (16 keys x 32 dims) of key block kb, dim step st: lane l gets key 16 kb + l % 16 and dims
+// 32 st + 8 (l / 16) + [0, 8) (one 16-byte row read).
+__device__ __forceinline__ dbf16x8 mrows(const u16* tile, int l, int kb, int st) {
+  return __builtin_bit_cast(dbf16x8, *reinterpret_cast<const uint4*>(tile + (16 * kb + (l & 15)) * kRowM + 32 * st +
+                                                                     8 * (l >> 4)));
+}
+
+// B operand of the scores: row n = l % 16 of x (q or u rows of the workgroup, bf16), dims 32 st + 8 (l / 16)
+// + [0, 8); rows >= R and dims >= D read as zeros.  src(n) returns the row's element pointer (bf16).
+__device__ __forceinline__ dbf16x8 mvec_bf16(const u16* row, int l, int st, int D) {
+  const int d0 = 32 * st + 8 * (l >> 4);
+  if (!row || d0 >= D) return dbf16x8{};
+  return __builtin_bit_cast(dbf16x8, *reinterpret_cast<const uint4*>(row + d0));
+}
+
+// Stores a lane's 4 weights (row n, keys k4 .. k4 + 3) as bf16 pairs hi + lo into the weight tiles and
+// returns their sum as the pairs represent them.
+__device__ __forceinline__ float mweights_store(MDecTiles& T, int n, int k4, const float (&x)[4]) {
+  uint32_t hw[2], lw[2];
+  float sum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; r += 2) {
+    const uint32_t h0 = f32_to_bf16(x[r]), h1 = f32_to_bf16(x[r + 1]);
+    const float r0 = x[r] - __uint_as_float(h0 << 16), r1 = x[r + 1] - __uint_as_float(h1 << 16);
+    const uint32_t l0 = f32_to_bf16(r0), l1 = f32_to_bf16(r1);
+    hw[r / 2] = h0 | (h1 << 16);
+    lw[r / 2] = l0 | (l1 << 16);
+    sum += (__uint_as_float(h0 << 16) + __uint_as_float(l0 << 16)) + (__uint_as_float(h1 << 16) + __uint_as_float(l1 << 16));
+  }
+  *reinterpret_cast<uint2*>(&T.pw[0][n * kPRow + k4]) = uint2{hw[0], hw[1]};
+  *reinterpret_cast<uint2*>(&T.pw[1][n * kPRow + k4]) = uint2{lw[0], lw[1]};
+  return sum;
+}
+
+// B operand (32 keys x 16 rows) of the sums: row n = l % 16 of the weight tile `half` (0 hi, 1 lo),
+// keys k0 .. k0 + 7 (16 bytes).
+__device__ __forceinline__ dbf16x8 mweights(const MDecTiles& T, int half, int n, int k0) {
+  return __builtin_bit_cast(dbf16x8, *reinterpret_cast<const uint4*>(&T.pw[half][n * kPRow + k0]));
+}
+
+template <bool PAGED>
+__global__ __launch_bounds__(256) void k_dec_mpass1(DecParams p) {
+  __shared__ MDecTiles T;
+  const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, n = l & 15, G4 = l >> 4;
+  int lo, hi;
+  seq_range(p, b, lo, hi);
+  const int k0 = max(lo, sp * p.chunk), k1 = min(hi, (sp + 1) * p.chunk);
+  const float c2 = p.scale * kLog2e;
+  // the lane's row: its q operand and the keys of this split it sees
+  const bool rowok = n < p.G * p.Tc;   // the workgroup's rows: G query heads x Tc tokens, at most 16
+  int rlo = k0, rhi = k0;
+  const u16* qrow = nullptr;
+  if (rowok) {
+    int a, c;
+    row_range(p, b, p.t0 + n / p.G, a, c);
+    rlo = max(k0, a);
+    rhi = min(k1, c);
+    qrow = p.q + row_bh(p, b, g, n) * p.D;
+  }
+  dbf16x8 qB[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) qB[st] = mvec_bf16(qrow, l, st, p.D);
+  df32x4 accO[2], accK[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) accO[i] = accK[i] = df32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, lpart = 0.f;
+  const int nt = k1 > k0 ? (k1 - k0 + kTile - 1) / kTile : 0;
+  TileRegs Rg{};
+  if (nt > 0) {
+    Rg = tile_fetch<PAGED>(p, b, g, k0, k1, tid);
+    mtile_store(Rg, T, tid);
+  }
+  __syncthreads();
+  for (int it = 0; it < nt; ++it) {
+    const int key0 = k0 + it * kTile;
+    Rg = tile_fetch<PAGED>(p, b, g, key0 + kTile, k1, tid);   // (past the last tile: rereads the last key)
+    // scores of keys 16 w + 4 (l / 16) + [0, 4) for row n
+    df32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mrows(T.k, l, w, st), qB[st], sacc, 0, 0, 0);
+    float sv[4], mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = key0 + 16 * w + 4 * G4 + r;
+      sv[r] = key >= rlo && key < rhi ? sacc[r] * c2 : -INFINITY;
+      mx = fmaxf(mx, sv[r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (l < 16) T.smax[w][l] = mx;
+    lds_barrier();
+    // lazy running maximum of the row (moves only when the tile exceeds it by kMomTau, log2 units)
+    const float tm = fmaxf(fmaxf(T.smax[0][n], T.smax[1][n]), fmaxf(T.smax[2][n], T.smax[3][n]));
+    if (tm > m_run + kMomTau) {
+      const float f = m_run == -INFINITY ? 0.f : exp2f(m_run - tm);
+      m_run = tm;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        accO[i] *= f;
+        accK[i] *= f;
+      }
+      lpart *= f;
+    }
+    float e[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) e[r] = sv[r] == -INFINITY ? 0.f : exp2f(sv[r] - m_run);
+    lpart += mweights_store(T, n, 16 * w + 4 * G4, e);
+    lds_barrier();
+    // o^T and kbar^T for dims 32 w + [0, 32)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const dbf16x8 ph = mweights(T, 0, n, 32 * ks + 8 * G4), pl = mweights(T, 1, n, 32 * ks + 8 * G4);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const dbf16x8 av = mcols(T.v, l, ks, 2 * w + i), ak = mcols(T.k, l, ks, 2 * w + i);
+        accO[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, ph, accO[i], 0, 0, 0);
+        accK[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, ph, accK[i], 0, 0, 0);
+        accO[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pl, accO[i], 0, 0, 0);
+        accK[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, pl, accK[i], 0, 0, 0);
+      }
+    }
+    lds_barrier();
+    mtile_store(Rg, T, tid);
+    lds_barrier();
+  }
+  // l of each row: the lanes of a row in a wave, then the four waves
+  lpart += __shfl_xor(lpart, 16, 64);
+  lpart += __shfl_xor(lpart, 32, 64);
+  if (l < 16) T.rsum[w][l] = lpart;
+  __syncthreads();
+  if (rowok) {
+    const int64_t bh = row_bh(p, b, g, n);
+    const int64_t base = (bh * p.ns + sp) * kD;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d = 16 * (2 * w + i) + 4 * G4 + r;   // accumulator row = dim, column = row n
+        p.po[base + d] = accO[i][r];
+        p.pk[base + d] = accK[i][r];
+      }
+    if (w == 0 && G4 == 0) {
+      p.pm[bh * p.ns + sp] = m_run;
+      p.pl[bh * p.ns + sp] = T.rsum[0][n] + T.rsum[1][n] + T.rsum[2][n] + T.rsum[3][n];
+    }
+  }
+}
+
+template <bool PAGED>
+__global__ __launch_bounds__(256) void k_dec_mpass2(DecParams p) {
+  __shared__ MDecTiles T;
+  const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, n = l & 15, G4 = l >> 4;
+  int lo, hi;
+  seq_range(p, b, lo, hi);
+  const int k0 = max(lo, sp * p.chunk), k1 = min(hi, (sp + 1) * p.chunk);
+  const float c2 = p.scale * kLog2e;
+  const bool rowok = n < p.G * p.Tc;   // the workgroup's rows: G query heads x Tc tokens, at most 16
+  int rlo = k0, rhi = k0;
+  const u16* qrow = nullptr;
+  float lse = -INFINITY, alpha = 0.f;
+  int64_t bh = 0;
+  if (rowok) {
+    int a, c;
+    row_range(p, b, p.t0 + n / p.G, a, c);
+    rlo = max(k0, a);
+    rhi = min(k1, c);
+    bh = row_bh(p, b, g, n);
+    qrow = p.q + bh * p.D;
+    lse = p.slse[bh];
+    alpha = p.salpha[bh];
+  }
+  if (lse == -INFINITY) rhi = rlo;   // a row with no visible key contributes nothing
+  dbf16x8 qB[4], uB[4], uL[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    qB[st] = mvec_bf16(qrow, l, st, p.D);
+    dbf16x8 ub{}, ul{};
+    if (rowok) {
+      const float* ur = p.su + bh * kD + 32 * st + 8 * G4;   // (zero past D)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const __bf16 h = static_cast<__bf16>(ur[e]);
+        ub[e] = h;
+        ul[e] = static_cast<__bf16>(ur[e] - static_cast<float>(h));
+      }
+    }
+    uB[st] = ub;
+    uL[st] = ul;
+  }
+  df32x4 accC[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) accC[i] = df32x4{0.f, 0.f, 0.f, 0.f};
+  float wpart = 0.f;
+  const int nt = k1 > k0 ? (k1 - k0 + kTile - 1) / kTile : 0;
+  TileRegs Rg{};
+  if (nt > 0) {
+    Rg = tile_fetch<PAGED>(p, b, g, k0, k1, tid);
+    mtile_store(Rg, T, tid);
+  }
+  __syncthreads();
+  for (int it = 0; it < nt; ++it) {
+    const int key0 = k0 + it * kTile;
+    Rg = tile_fetch<PAGED>(p, b, g, key0 + kTile, k1, tid);
+    df32x4 sacc = {0.f, 0.f, 0.f, 0.f}, racc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const dbf16x8 kr = mrows(T.k, l, w, st);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr, qB[st], sacc, 0, 0, 0);
+      racc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr, uB[st], racc, 0, 0, 0);
+      racc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr, uL[st], racc, 0, 0, 0);
+    }
+    // W = p (u.k - alpha), p = exp2(s - lse), as bf16 pairs; sum W from the same pairs
+    float wv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = key0 + 16 * w + 4 * G4 + r;
+      wv[r] = key >= rlo && key < rhi ? exp2f(sacc[r] * c2 - lse) * (racc[r] - alpha) : 0.f;
+    }
+    wpart += mweights_store(T, n, 16 * w + 4 * G4, wv);
+    lds_barrier();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const dbf16x8 wh = mweights(T, 0, n, 32 * ks + 8 * G4), wl = mweights(T, 1, n, 32 * ks + 8 * G4);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const dbf16x8 av = mcols(T.v, l, ks, 2 * w + i);
+        accC[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, wh, accC[i], 0, 0, 0);
+        accC[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, wl, accC[i], 0, 0, 0);
+      }
+    }
+    lds_barrier();
+    mtile_store(Rg, T, tid);
+    lds_barrier();
+  }
+  wpart += __shfl_xor(wpart, 16, 64);
+  wpart += __shfl_xor(wpart, 32, 64);
+  if (l < 16) T.rsum[w][l] = wpart;
+  __syncthreads();
+  if (rowok) {
+    const float wsum = T.rsum[0][n] + T.rsum[1][n] + T.rsum[2][n] + T.rsum[3][n];
+    const int64_t base = (bh * p.ns + sp) * kD;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d = 16 * (2 * w + i) + 4 * G4 + r;
+        p.pc[base + d] = accC[i][r] - wsum * p.so[bh * kD + d];   // partial c = sum W v - (sum W) o
+      }
+  }
+}
+
 struct DecWs {
   float *pm, *pl, *po, *pk, *so, *su, *salpha, *slse, *pc;
   int ns, chunk;
@@ -536,26 +849,24 @@ size_t fast_decode_workspace(const Geom& g) { return dec_layout(g, nullptr).byte
 
 namespace {
 
-// One pass kernel over every chunk of new tokens; rows per workgroup = G x (tokens in the chunk).
+// One pass kernel over every chunk of new tokens.  A chunk holds up to 16 / G tokens, so a workgroup has
+// G x (tokens in the chunk) <= 16 rows; 3 to 16 rows run on the matrix-core kernels (rows padded to 16),
+// 1 or 2 rows on the fp32 kernels.
 template <bool PASS2, bool PAGED>
 void launch_pass(DecParams p, const dim3& grid, hipStream_t stream) {
-  const int per = kMaxG / p.G;   // tokens per chunk at most (G is 1, 2, 4 or 8)
+  const int per = kMaxRowsM / p.G;   // tokens per chunk at most (G is 1, 2, 4 or 8)
   for (int t0 = 0; t0 < p.T; t0 += p.Tc) {
-    int tc = per;
-    while (tc > p.T - t0) tc >>= 1;   // rows = G x tc stays 1, 2, 4 or 8
     p.t0 = t0;
-    p.Tc = tc;
-    const int rows = p.G * tc;
+    p.Tc = min(per, p.T - t0);
+    const int rows = p.G * p.Tc;
     if (!PASS2) {
       if (rows == 1) hipLaunchKernelGGL((k_dec_pass1<1, PAGED>), grid, dim3(256), 0, stream, p);
       else if (rows == 2) hipLaunchKernelGGL((k_dec_pass1<2, PAGED>), grid, dim3(256), 0, stream, p);
-      else if (rows == 4) hipLaunchKernelGGL((k_dec_pass1<4, PAGED>), grid, dim3(256), 0, stream, p);
-      else hipLaunchKernelGGL((k_dec_pass1<8, PAGED>), grid, dim3(256), 0, stream, p);
+      else hipLaunchKernelGGL((k_dec_mpass1<PAGED>), grid, dim3(256), 0, stream, p);
     } else {
       if (rows == 1) hipLaunchKernelGGL((k_dec_pass2<1, PAGED>), grid, dim3(256), 0, stream, p);
       else if (rows == 2) hipLaunchKernelGGL((k_dec_pass2<2, PAGED>), grid, dim3(256), 0, stream, p);
-      else if (rows == 4) hipLaunchKernelGGL((k_dec_pass2<4, PAGED>), grid, dim3(256), 0, stream, p);
-      else hipLaunchKernelGGL((k_dec_pass2<8, PAGED>), grid, dim3(256), 0, stream, p);
+      else hipLaunchKernelGGL((k_dec_mpass2<PAGED>), grid, dim3(256), 0, stream, p);
     }
   }
 }

@@ -548,10 +548,12 @@ def test_decode_multi_token(plx, T, Hkv, window):
     ref = _multi_token_ref(host(q), host(kc), host(vc), host(P), host(seqlens).astype(int), window)
     assert np.all(host(out)[2] == 0) and np.all(host(out)[1, :max(T - 3, 0)] == 0)
     assert rel_err(host(out), ref) <= BF16_TOL
-    # the last token alone is the one-token decode
+    # the last token alone is the one-token decode.  With 4 or 8 rows per workgroup the passes run on the
+    # matrix cores with the weights and u as bf16 pairs (about 2^-16 = 1.5e-5 relative each), the one-token
+    # call here on fp32 arithmetic, so the two agree to a few times 1.5e-5, not to fp32 rounding
     last = plx.parallax_attn_decode(q[:, -1].contiguous(), kc, vc, P, seqlens=seqlens, window=window)
     torch.cuda.synchronize()
-    assert rel_err(host(out[:, -1]), host(last)) <= 1e-5
+    assert rel_err(host(out[:, -1]), host(last)) <= 1e-4
 
 
 def test_decode_head_dim_64(plx):
