@@ -1781,6 +1781,14 @@ __global__ __launch_bounds__(256) void k_zero4(float* x, int64_t n4) {
     reinterpret_cast<float4*>(x)[i] = float4{0.f, 0.f, 0.f, 0.f};
 }
 
+// Zeroes two arrays in one launch (n4 float4 each; 16-byte aligned).
+__global__ __launch_bounds__(256) void k_zero4x2(float* x, int64_t n4, float* y, int64_t m4) {
+  for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < n4 + m4; i += 256LL * gridDim.x) {
+    float4* dst = i < n4 ? reinterpret_cast<float4*>(x) + i : reinterpret_cast<float4*>(y) + (i - n4);
+    *dst = float4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
 // ------------------------------------------------------------------------------------------
 // dP = sum over batch and rows of x du^T: partial sums per row chunk, then a fixed-order sum
 // ------------------------------------------------------------------------------------------
@@ -2002,8 +2010,8 @@ hipError_t bwd_impl(const Geom& g, const BwdArgs& a, int split_rows, void* ws, h
 
   // row statistics of padded rows stay 0 (the key-major kernel reads whole 32-row tiles); the per-row
   // maxima start at 0 for the row kernels' atomicMax
-  hipLaunchKernelGGL(k_zero4, dim3(256), dim3(256), 0, stream, w.rstat, static_cast<int64_t>(w.rstat_n / 4));
-  hipLaunchKernelGGL(k_zero4, dim3(256), dim3(256), 0, stream, w.rowmax, static_cast<int64_t>(w.rowmax_n / 4));
+  hipLaunchKernelGGL(k_zero4x2, dim3(256), dim3(256), 0, stream, w.rstat, static_cast<int64_t>(w.rstat_n / 4),
+                     w.rowmax, static_cast<int64_t>(w.rowmax_n / 4));
   RowParams rp{};
   rp.q = static_cast<const u16*>(q);
   rp.dout = static_cast<const u16*>(dout);

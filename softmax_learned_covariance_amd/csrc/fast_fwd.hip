@@ -33,7 +33,14 @@
 #include "fast_common.h"
 #include "plx_internal.h"
 
+#ifndef PLX_FWD_POLY_MASK
+#define PLX_FWD_POLY_MASK 0
+#endif
 namespace plx {
+// Which of each lane's groups of 8 exponentials in the forward's main kernel go through exp2_fma instead
+// of the transcendental unit (bit j: element j of the group).
+constexpr unsigned kFwdPolyMask = PLX_FWD_POLY_MASK;
+
 namespace {
 
 constexpr int kWaves = 8;
@@ -246,7 +253,10 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
         const int kb = i >> 1, t8 = (i & 1) * 8;
         float e[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = __builtin_amdgcn_exp2f(fmaf(S[kb][t8 + j], cS, -mb));
+        for (int j = 0; j < 8; ++j) {
+          const float x = fmaf(S[kb][t8 + j], cS, -mb);
+          e[j] = (!SPLIT && ((kFwdPolyMask >> j) & 1)) ? exp2_fma(x) : __builtin_amdgcn_exp2f(x);
+        }
         pB[i] = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
         lpart = sum8(pB[i], lpart);
         if constexpr (SPLIT) {
@@ -472,7 +482,8 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int r = 8 * t + j;
-            e[j] = __builtin_amdgcn_exp2f(fmaf(S[r], cS, -mb2)) * (R[r] - alpha_s);
+            const float x = fmaf(S[r], cS, -mb2);
+            e[j] = ((!SPLIT && ((kFwdPolyMask >> j) & 1)) ? exp2_fma(x) : __builtin_amdgcn_exp2f(x)) * (R[r] - alpha_s);
           }
           wB[t] = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
           rpart = sum8(wB[t], rpart);

@@ -156,57 +156,48 @@ __global__ __launch_bounds__(256) void k_stage_kv(const u16* k, const u16* v, co
   }
 }
 
-// Running maximum along each series (one block per series of n floats, series `stride` apart): in
-// place, x[i] = max(x[0..i]) (or, with SUFFIX, max(x[i..n))).  Chunks of 2048 values: each thread takes
-// 8 consecutive values, the block combines the threads' maxima in LDS, and a carry joins the chunks.
+// Running maximum along each series (one block per series of n floats, series `stride` apart), in place:
+// x[i] = max(x[0..i]) (with SUFFIX, max(x[i..n))).  Thread t owns the t-th run of ceil(n / 256) positions in
+// scan order: it takes its run's maximum, the 256 maxima are scanned (within each wave by shuffles, then
+// across the four waves through LDS), and each thread rewrites its run with the running maximum started
+// from the maxima of the runs before it.  The values are >= 0 (norms and their bounds).
 template <bool SUFFIX>
 __global__ __launch_bounds__(256) void k_scan_max(float* x, int n, int64_t stride) {
-  __shared__ float part[256];
-  __shared__ float carry_s;
+  __shared__ float wmax[4];
   float* s = x + blockIdx.x * stride;
-  const int t = threadIdx.x;
-  float carry = 0.f;   // norms and statistics are >= 0
-  const int nchunks = (n + 2047) / 2048;
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const int chunk = SUFFIX ? nchunks - 1 - ch : ch;
-    const int base = chunk * 2048 + 8 * (SUFFIX ? 255 - t : t);   // suffix: thread 0 takes the last run
-    float v[8];
-    float m = 0.f;
+  const int t = threadIdx.x, l = t & 63, w = t >> 6;
+  const int run = (n + 255) / 256;
+  const int b0 = min(n, t * run), b1 = min(n, b0 + run);   // positions in scan order
+  float m = 0.f;
+#pragma unroll 8
+  for (int i = b0; i < b1; ++i) m = fmaxf(m, s[SUFFIX ? n - 1 - i : i]);
+  float inc = m;   // inclusive scan over the wave
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int i = SUFFIX ? base + 7 - e : base + e;   // in scan order
-      v[e] = i < n ? s[i] : 0.f;
-      m = fmaxf(m, v[e]);
-      v[e] = m;
-    }
-    part[t] = m;
-    __syncthreads();
-    // inclusive scan of the 256 thread maxima (Hillis-Steele)
-    for (int o = 1; o < 256; o <<= 1) {
-      const float y = t >= o ? part[t - o] : 0.f;
-      __syncthreads();
-      part[t] = fmaxf(part[t], y);
-      __syncthreads();
-    }
-    const float before = fmaxf(carry, t > 0 ? part[t - 1] : 0.f);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int i = SUFFIX ? base + 7 - e : base + e;
-      if (i < n) s[i] = fmaxf(before, v[e]);
-    }
-    if (t == 255) carry_s = fmaxf(carry, part[255]);
-    __syncthreads();
-    carry = carry_s;
-    __syncthreads();
+  for (int o = 1; o < 64; o <<= 1) {
+    const float y = __shfl_up(inc, o, 64);
+    if (l >= o) inc = fmaxf(inc, y);
+  }
+  if (l == 63) wmax[w] = inc;
+  __syncthreads();
+  float before = __shfl_up(inc, 1, 64);
+  if (l == 0) before = 0.f;
+  for (int j = 0; j < w; ++j) before = fmaxf(before, wmax[j]);
+#pragma unroll 8
+  for (int i = b0; i < b1; ++i) {
+    const int k = SUFFIX ? n - 1 - i : i;
+    before = fmaxf(before, s[k]);
+    s[k] = before;
   }
 }
 
-// One block per query head: P16t[h][a][b'] = sP * P[h][perm(b')][a]; optionally P16[h][b][a'] = sP * P[h][b][perm(a')].
+// Eight blocks per query head, each writing 16 rows a of P16t[h][a][b'] = sP * P[h][perm(b')][a] (and, with
+// p16, of P16[h][a][b'] = sP * P[h][a][perm(b')]) from the whole projector staged in LDS.
+constexpr int kStagePParts = 8;
 __global__ __launch_bounds__(256) void k_stage_p(const u16* P, const uint32_t* maxbits, _Float16* p16t,
                                                  _Float16* p16, int D) {
   constexpr int LD = kD + 2;
   __shared__ _Float16 ps[kD * LD];
-  const int h = blockIdx.x, t = threadIdx.x;
+  const int h = blockIdx.x, part = blockIdx.y, t = threadIdx.x;
   const float sP = range_scale(__uint_as_float(maxbits[3]));
   const u16* src = P + static_cast<int64_t>(h) * D * D;
   for (int e = t; e < kD * kD; e += 256) {   // a D x D projector is zero-padded to 128 x 128
@@ -214,17 +205,15 @@ __global__ __launch_bounds__(256) void k_stage_p(const u16* P, const uint32_t* m
     ps[r * LD + c] = r < D && c < D ? static_cast<_Float16>(bf16_to_f32(src[r * D + c]) * sP) : static_cast<_Float16>(0.f);
   }
   __syncthreads();
-  for (int ci = t; ci < kD * 16; ci += 256) {
-    const int a = ci >> 4, c = ci & 15;
-    f16x8 o;
+  const int a = (kD / kStagePParts) * part + (t >> 4), c = t & 15;   // one 16-byte chunk per thread
+  f16x8 o;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = ps[(16 * (c >> 1) + perm16(8 * (c & 1) + e)) * LD + a];
-    *reinterpret_cast<f16x8*>(p16t + (static_cast<int64_t>(h) * kD + a) * kD + c * 8) = o;
-    if (p16) {
+  for (int e = 0; e < 8; ++e) o[e] = ps[(16 * (c >> 1) + perm16(8 * (c & 1) + e)) * LD + a];
+  *reinterpret_cast<f16x8*>(p16t + (static_cast<int64_t>(h) * kD + a) * kD + c * 8) = o;
+  if (p16) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = ps[a * LD + 16 * (c >> 1) + perm16(8 * (c & 1) + e)];
-      *reinterpret_cast<f16x8*>(p16 + (static_cast<int64_t>(h) * kD + a) * kD + c * 8) = o;
-    }
+    for (int e = 0; e < 8; ++e) o[e] = ps[a * LD + 16 * (c >> 1) + perm16(8 * (c & 1) + e)];
+    *reinterpret_cast<f16x8*>(p16 + (static_cast<int64_t>(h) * kD + a) * kD + c * 8) = o;
   }
 }
 
@@ -327,7 +316,7 @@ hipError_t launch_staging(const Staging& s, const void* q, int64_t q_elems, cons
                        static_cast<int64_t>(s.Tk_pad));
   }
   if (P)
-    hipLaunchKernelGGL(k_stage_p, dim3(Hq), dim3(256), 0, stream, static_cast<const u16*>(P), s.maxbits, s.p16t,
+    hipLaunchKernelGGL(k_stage_p, dim3(Hq, kStagePParts), dim3(256), 0, stream, static_cast<const u16*>(P), s.maxbits, s.p16t,
                      s.p16, D);
   return hipGetLastError();
 }
