@@ -420,6 +420,35 @@ def main():
                          "algorithmic_flop_per_launch": kfl}}
         log(f"layer06 forward {dt2c * 1e3:.3f} ms/call, kernel {kavg:.3f} ms")
         del q2, k2, v2, P2
+        # layer17's shape at head dim 64 (the pages' compute-matched control: smaller heads), forward
+        w3 = W.scaled(W.WORKLOADS["layer17"], head_dim=64)
+        log("config layer17 at head dim 64, forward")
+        q3, k3, v3, P3 = W.make_inputs(w3, device=dev)
+        fwd3 = lambda: plx.parallax_attn_fwd(q3, k3, v3, P3, split_rows=split)  # noqa: E731
+        for _ in range(2):
+            fwd3()
+        torch.cuda.synchronize()
+        n3 = max(10, K)
+        t0 = time.perf_counter()
+        for _ in range(n3):
+            fwd3()
+        torch.cuda.synchronize()
+        dt3c = (time.perf_counter() - t0) / n3
+        ks3 = kernel_samples(fwd3, plx.PLX_KERNEL_FWD, n3)
+        kfl3 = fwd_flops(w3, min(r0, w3.seqlen_q))
+        kavg3 = sum(ks3) / len(ks3)
+        result["configs"]["layer17_d64_fwd"] = {
+            "workload": f"{w3.name} at d=64: forward, B={w3.batch}, T={w3.seqlen_q}, Hq={w3.heads_q}, "
+                        f"Hkv={w3.heads_kv}, d={w3.head_dim}, causal, bf16 (flops counted at d=64)",
+            "ms_per_call": round(dt3c * 1e3, 4), "tflops": round(fwd_flops(w3) / dt3c / 1e12, 3),
+            "tokens_per_s": round(w3.batch * w3.seqlen_q / dt3c, 1),
+            "roofline": {"bound": "mfma", "kernel": "fwd", "avg_ms": round(kavg3, 4), "launches": len(ks3),
+                         "achieved": round(kfl3 / (kavg3 * 1e-3) / 1e12, 3), "peak": PEAK_F16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(kfl3 / (kavg3 * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
+                         "algorithmic_flop_per_launch": kfl3}}
+        log(f"layer17 d=64 forward {dt3c * 1e3:.3f} ms/call, kernel {kavg3:.3f} ms "
+            f"({kfl3 / (kavg3 * 1e-3) / 1e12:.0f} TFLOP/s)")
+        del q3, k3, v3, P3
         # train06 (0.6B-like training step): forward + backward
         w4 = W.WORKLOADS["train06"]
         log(f"config {w4.name} training step")

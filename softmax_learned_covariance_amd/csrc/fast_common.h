@@ -1,21 +1,22 @@
-// Shared pieces of the MFMA fast path (head_dim 128, or 64 zero-padded to 128; bf16 inputs): operand
-// types, the fp16 staging layout, power-of-two range scales and wave helpers.
+// Shared pieces of the MFMA fast path (head_dim 128 or 64; bf16 inputs): operand types, the fp16 staging
+// layout, power-of-two range scales and wave helpers.
 //
 // Staging.  The MFMA kernels compute with fp16 operands (11 significant bits)
 // and fp32 accumulation.  K, V, P (and, for the backward, q, dout, u, dkbar)
 // are converted once per call into fp16 copies laid out tile by tile for the
 // v_mfma_f32_32x32x16_f16 operand registers.  A tile is one contiguous block
 // stored "chunk-major": its 16-byte chunks (8 fp16 values) are grouped by
-// chunk index, so
-//   key rows    [16 chunks][64 keys][8]   (K16, V16: d permuted within groups of 16)
-//   key columns [8 chunks][128 d][8]      (K16t, V16t: keys permuted within groups of 16)
-//   query rows  [16 chunks][32 rows][8]   and query columns [4 chunks][128 d][8]
+// chunk index, so, for a staged head dim DH (128, or 64 in the forwards' native layout)
+//   key rows    [DH/8 chunks][64 keys][8] (K16, V16: d permuted within groups of 16)
+//   key columns [8 chunks][DH d][8]       (K16t, V16t: keys permuted within groups of 16)
+//   query rows  [16 chunks][32 rows][8]   and query columns [4 chunks][128 d][8]   (backward: DH = 128)
 // with tiles ordered [batch][head][tile].  Copying a tile to LDS is then one
 // contiguous DMA, and an MFMA operand read (32 lanes reading the same chunk of
 // 32 consecutive rows) is a contiguous 512-byte LDS access: no bank conflicts,
 // and the chunk index becomes an immediate offset.
-//   P16t  [Hq][128][128]         P16t[h][a][b'] = P[h][b][a], b permuted within groups of 16
-//   P16   [Hq][128][128]         P16[h][b][a'] = P[h][b][a], a permuted within groups of 16
+//   P16t  [Hq][DH][DH]           P16t[h][a][b'] = P[h][b][a], b permuted within groups of 16
+//   P16   [Hq][DH][DH]           P16[h][b][a'] = P[h][b][a], a permuted within groups of 16
+// The backward stages a head of 64 zero-padded to DH = 128; the forwards stage it at DH = 64.
 // The permutation of a group of 16 is the involution
 //   position 8*hh + e  <->  element 8*(e/4) + 4*hh + (e%4)      (hh in {0,1}, e in 0..7)
 // which is exactly the order in which a 32x32 accumulator tile holds its rows
@@ -40,13 +41,13 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint16_t u16;
 
-constexpr int kD = 128;        // head_dim of the fast path
+constexpr int kD = 128;        // largest head_dim of the fast path
 constexpr int kKeyTile = 64;   // keys per LDS tile
 constexpr int kQTile = 32;     // query rows per tile of the key-major backward
 
-// First element of key tile kt of (batch b, kv head g) in K16 / V16 / K16t / V16t.
-__host__ __device__ inline int64_t kv_tile(int b, int g, int kt, int Hkv, int ntiles) {
-  return ((static_cast<int64_t>(b) * Hkv + g) * ntiles + kt) * (kKeyTile * kD);
+// First element of key tile kt of (batch b, kv head g) in K16 / V16 / K16t / V16t staged at head dim dh.
+__host__ __device__ inline int64_t kv_tile(int b, int g, int kt, int Hkv, int ntiles, int dh = kD) {
+  return ((static_cast<int64_t>(b) * Hkv + g) * ntiles + kt) * (kKeyTile * dh);
 }
 // First element of query tile qt of (batch b, query head h) in the query-side copies.
 __host__ __device__ inline int64_t q_tile(int b, int h, int qt, int Hq, int nqt) {
@@ -269,6 +270,7 @@ struct Staging {
   float* knorm;        // [B][Hkv][Tk_pad]: running maximum over keys 0..j of |k_j| (Euclidean, unscaled)
   float* vnorm;        // the same for |v_j|; directly after knorm
   int Tk_pad;
+  int dh;              // staged head dim (128, or 64 for the forwards' native layout)
   size_t bytes;        // total workspace used
 };
 
@@ -278,12 +280,13 @@ inline size_t ws_take(size_t& off, size_t n) {
   return at;
 }
 
-// Staging buffers at the start of `ws` (ws may be nullptr to size them).
-inline Staging staging_layout(void* ws, int B, int Tk, int Hkv, int Hq, bool backward = false) {
+// Staging buffers at the start of `ws` (ws may be nullptr to size them), for head dim dh.
+inline Staging staging_layout(void* ws, int B, int Tk, int Hkv, int Hq, bool backward = false, int dh = kD) {
   Staging s{};
   s.Tk_pad = (Tk + kKeyTile - 1) / kKeyTile * kKeyTile;
-  const size_t kv = static_cast<size_t>(B) * s.Tk_pad * Hkv * kD * sizeof(_Float16);
-  const size_t p = static_cast<size_t>(Hq) * kD * kD * sizeof(_Float16);
+  s.dh = dh;
+  const size_t kv = static_cast<size_t>(B) * s.Tk_pad * Hkv * dh * sizeof(_Float16);
+  const size_t p = static_cast<size_t>(Hq) * dh * dh * sizeof(_Float16);
   char* base = static_cast<char*>(ws);
   size_t off = 0;
   s.maxbits = reinterpret_cast<uint32_t*>(base + ws_take(off, 256));
@@ -314,6 +317,6 @@ hipError_t launch_stage_rows(const void* src, bool f32, const uint32_t* maxbits,
 hipError_t launch_staging(const Staging& s, const void* q, int64_t q_elems, const void* k,
                           const void* v, const void* P, int B, int Tk, int Hkv, int Hq,
                           hipStream_t stream, const void* extra = nullptr, int64_t extra_elems = 0,
-                          int extra_slot = 0, int D = kD);   // D: head dim of k, v, P (64 is zero-padded to 128)
+                          int extra_slot = 0, int D = kD);   // D: head dim of k, v, P (zero-padded to s.dh)
 
 }  // namespace plx

@@ -1,5 +1,5 @@
-// Fused two-pass Parallax forward for gfx950 (head_dim 128, or 64 zero-padded to 128; bf16 inputs, fp16 MFMA),
-// and the one-pass probe-form forward.
+// Fused two-pass Parallax forward for gfx950 (head_dim DH = 128 or 64; bf16 inputs, fp16 MFMA), and the
+// one-pass probe-form forward.
 //
 // What it computes (gist.science technical summary of "Parallax: Parameterized
 // Local Linear Attention for Language Modeling", "Core mechanism": softmax
@@ -17,7 +17,8 @@
 // Work split.  One 512-thread workgroup (8 waves, 2 per SIMD) owns one
 // (batch, key/value head) and a block of query rows for every query head of the
 // group, so the group's heads share each K/V tile in LDS.  Each wave owns 32
-// query rows of one head; in the accumulator tiles lane l (l % 32 = query,
+// query rows of one head; products over d take DH / 16 k-steps and the per-row
+// vectors over d (o, kbar, u, c) DH / 32 accumulator tiles; in the accumulator tiles lane l (l % 32 = query,
 // l / 32 = half) holds 16 key or feature rows, so row statistics are lane-local
 // plus one half-wave swap.  S^T = K Q^T puts keys in registers: P~^T is then
 // directly the B operand of o^T = V^T P~^T and kbar^T = K^T P~^T (fp16 staging
@@ -64,35 +65,40 @@ struct FwdParams {
   float* cor;       // per row |out - o| / |out|, [B][Hq][Tq] (nullable)
   int out_bf16;        // probe form only: rho . kbar per row, [B][Hq][Tq] (nullable)
   int B, Tq, Tk, Tk_pad, Hq, Hkv, G, causal, window;
-  int D;            // head dim of the caller's rows (128, or 64 zero-padded to 128 in the operands)
+  int D;            // head dim of the caller's rows (the kernel's DH)
   float scale;
   int row_begin, row_end, rows_per_block, n_rb;  // rows [row_begin, row_end)
 };
 
+template <int DH>
 struct __align__(16) Tiles {
-  _Float16 k[2][kKeyTile * kD];    // key rows tile    [16 chunks][64 keys][8]
-  _Float16 kt[2][kD * kKeyTile];   // key columns tile [8 chunks][128 d][8]
-  _Float16 vt[2][kD * kKeyTile];
+  _Float16 k[2][kKeyTile * DH];    // key rows tile    [DH/8 chunks][64 keys][8]
+  _Float16 kt[2][DH * kKeyTile];   // key columns tile [8 chunks][DH d][8]
+  _Float16 vt[2][DH * kKeyTile];
 };
 
-__device__ __forceinline__ f16x8 lds_k(const Tiles& T, int buf, int r, int c) {
+template <int DH>
+__device__ __forceinline__ f16x8 lds_k(const Tiles<DH>& T, int buf, int r, int c) {
   return *reinterpret_cast<const f16x8*>(&T.k[buf][c * (kKeyTile * 8) + r * 8]);
 }
-__device__ __forceinline__ f16x8 lds_kt(const Tiles& T, int buf, int d, int c) {
-  return *reinterpret_cast<const f16x8*>(&T.kt[buf][c * (kD * 8) + d * 8]);
+template <int DH>
+__device__ __forceinline__ f16x8 lds_kt(const Tiles<DH>& T, int buf, int d, int c) {
+  return *reinterpret_cast<const f16x8*>(&T.kt[buf][c * (DH * 8) + d * 8]);
 }
-__device__ __forceinline__ f16x8 lds_vt(const Tiles& T, int buf, int d, int c) {
-  return *reinterpret_cast<const f16x8*>(&T.vt[buf][c * (kD * 8) + d * 8]);
+template <int DH>
+__device__ __forceinline__ f16x8 lds_vt(const Tiles<DH>& T, int buf, int d, int c) {
+  return *reinterpret_cast<const f16x8*>(&T.vt[buf][c * (DH * 8) + d * 8]);
 }
 
-// Asynchronous global -> LDS copy of one key tile (each array is one contiguous 16 KB block:
-// 16 wave instructions of 1024 bytes, two per wave).
-__device__ __forceinline__ void tile_dma(const FwdParams& p, Tiles& T, int buf, int b, int g, int kt, bool with_kt,
-                                         int w, int l) {
-  const int64_t tb = kv_tile(b, g, kt, p.Hkv, p.Tk_pad / kKeyTile);
+// Asynchronous global -> LDS copy of one key tile (each array is one contiguous block of DH / 8 KB:
+// DH / 8 wave instructions of 1024 bytes, DH / 64 per wave).
+template <int DH>
+__device__ __forceinline__ void tile_dma(const FwdParams& p, Tiles<DH>& T, int buf, int b, int g, int kt,
+                                         bool with_kt, int w, int l) {
+  const int64_t tb = kv_tile(b, g, kt, p.Hkv, p.Tk_pad / kKeyTile, DH);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int i = 2 * w + j;
+  for (int j = 0; j < DH / 64; ++j) {
+    const int i = (DH / 64) * w + j;
     const int64_t src = tb + i * 512 + l * 8;
     lds_dma16(p.k16 + src, &T.k[buf][i * 512]);
     if (with_kt) lds_dma16(p.k16t + src, &T.kt[buf][i * 512]);
@@ -109,13 +115,14 @@ __device__ __forceinline__ void load4_bf16(const u16* src, float* dst) {
   dst[3] = __uint_as_float(w.y & 0xffff0000u);
 }
 
-// B operand of a product over d for one query row: d in the permuted-16 order, scaled by s.  Rows
-// of D < 128 elements are zero-padded to 128.
-__device__ __forceinline__ void load_q_operand(const u16* qrow, bool ok, int hh, float s, f16x8 (&qB)[8], int D) {
+// B operand of a product over d for one query row of NS * 16 elements: d in the permuted-16 order, scaled
+// by s.
+template <int NS>
+__device__ __forceinline__ void load_q_operand(const u16* qrow, bool ok, int hh, float s, f16x8 (&qB)[NS]) {
 #pragma unroll
-  for (int st = 0; st < 8; ++st) {
+  for (int st = 0; st < NS; ++st) {
     float a[4] = {0.f, 0.f, 0.f, 0.f}, c[4] = {0.f, 0.f, 0.f, 0.f};
-    if (ok && 16 * st < D) {
+    if (ok) {
       load4_bf16(qrow + 16 * st + 4 * hh, a);
       load4_bf16(qrow + 16 * st + 8 + 4 * hh, c);
     }
@@ -126,9 +133,10 @@ __device__ __forceinline__ void load_q_operand(const u16* qrow, bool ok, int hh,
 // SPLIT: every operand the kernel computes (p~, q - kbar, u, W) is carried as an
 // fp16 hi + lo pair (two MFMAs, ~22 significant bits); used for the first query
 // rows, whose few visible keys make the output large relative to its rms.
-template <bool SPLIT>
+template <bool SPLIT, int DH>
 __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
-  __shared__ Tiles T;
+  constexpr int NS = DH / 16, NT = DH / 32;   // k-steps and accumulator tiles over d
+  __shared__ Tiles<DH> T;
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, ql = l & 31, hh = l >> 5;
 
   // block -> (batch, kv head, row block)
@@ -159,7 +167,7 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
   const float sP = range_scale(__uint_as_float(p.maxbits[3]));
   const float cS = p.scale * kLog2e / (sQ * sK);
 
-  const int64_t qoff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * p.D;
+  const int64_t qoff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * DH;
   const u16* qrow = p.q + qoff;
 
   // key ranges: block, wave (first / last row), lane (its row)
@@ -177,13 +185,13 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
   const int r_kend = row_ok ? (p.causal ? min(p.Tk, row + off + 1) : p.Tk) : 0;
   const int r_kbeg = p.window > 0 ? max(0, row + off - p.window + 1) : 0;
 
-  f16x8 qB[8];
-  load_q_operand(qrow, row_ok, hh, sQ, qB, p.D);
+  f16x8 qB[NS];
+  load_q_operand(qrow, row_ok, hh, sQ, qB);
 
   // ---------------- pass 1 ----------------
-  f32x16 accO[4], accK[4];
+  f32x16 accO[NT], accK[NT];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < NT; ++mt) {
     accO[mt] = f32x16{};
     accK[mt] = f32x16{};
   }
@@ -207,8 +215,8 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
           a[s][1] = lds_k(T, buf, 32 + ql, 2 * s + hh);
         }
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          if (s + 2 < 8) {
+        for (int s = 0; s < NS; ++s) {
+          if (s + 2 < NS) {
             a[(s + 2) % 3][0] = lds_k(T, buf, ql, 2 * (s + 2) + hh);
             a[(s + 2) % 3][1] = lds_k(T, buf, 32 + ql, 2 * (s + 2) + hh);
           }
@@ -241,7 +249,7 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
         m_used = need ? mt_ : m_used;
         lpart *= f;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
+        for (int mt = 0; mt < NT; ++mt) {
           accO[mt] *= f;
           accK[mt] *= f;
         }
@@ -275,9 +283,9 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
         load_c(0, c[0]);
         load_c(1, c[1]);
 #pragma unroll
-        for (int n = 0; n < 16; ++n) {
+        for (int n = 0; n < 4 * NT; ++n) {
           const int mt = n >> 2, i = n & 3;
-          if (n + 2 < 16) load_c(n + 2, c[(n + 2) % 3]);
+          if (n + 2 < 4 * NT) load_c(n + 2, c[(n + 2) % 3]);
           __builtin_amdgcn_sched_barrier(0);
           accO[mt] = mfma(c[n % 3][0], pB[i], accO[mt]);
           accK[mt] = mfma(c[n % 3][1], pB[i], accK[mt]);
@@ -302,11 +310,10 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
   if (row_ok) {
     if (p.lse && hh == 0) p.lse[(static_cast<int64_t>(b) * p.Hq + h) * p.Tq + row] = lse2 * kLn2;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = 32 * mt + 8 * j + 4 * hh;
-        if (d >= p.D) continue;   // padding dims of a D < 128 head
         const float fo = invL / sV, fk = invL / sK;
         const float4 ov = {accO[mt][4 * j] * fo, accO[mt][4 * j + 1] * fo, accO[mt][4 * j + 2] * fo,
                            accO[mt][4 * j + 3] * fo};
@@ -321,19 +328,19 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
 
   // ---------------- probe u = P^T (q - kbar) ----------------
   // kbar (unscaled) and x = q - kbar in the accumulator layout: lane (row, hh), d = 32 mt + 8 (r/4) + 4 hh + r%4
-  float kbv[4][16];
-  f16x8 xB[8], xL[SPLIT ? 8 : 1];
+  float kbv[NT][16];
+  f16x8 xB[NS], xL[SPLIT ? NS : 1];
   float alpha_s = 0.f, sU = 1.f;
   float u2sum = 0.f, k2sum = 0.f;   // |U-hat|^2 (scaled units) and |kbar sK|^2 of the row, for pass 2's W scale
   {
-    float xv[4][16];
+    float xv[NT][16];
     float xmax = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float qv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (row_ok && 32 * mt + 8 * j + 4 * hh < p.D) load4_bf16(qrow + 32 * mt + 8 * j + 4 * hh, qv);
+        if (row_ok) load4_bf16(qrow + 32 * mt + 8 * j + 4 * hh, qv);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * j + e;
@@ -346,7 +353,7 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
     xmax = xor32_max(xmax);
     const float sX = range_scale(xmax);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < NS; ++s) {
       const int mt = s >> 1, t8 = (s & 1) * 8;
       float e[8];
 #pragma unroll
@@ -357,22 +364,22 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
     // U^T = P16t X^T.  x always enters as a hi + lo pair: for a sharply peaked row the correction is
     // one dot product u.(k_1 - k_2) of nearly orthogonal vectors, which amplifies the rounding of u's
     // inputs; the 32 extra MFMAs per wave are taken once per row block, not per key tile.
-    f32x16 accU[4];
-    const _Float16* prow = p.p16t + (static_cast<int64_t>(h) * kD + ql) * kD + hh * 8;
+    f32x16 accU[NT];
+    const _Float16* prow = p.p16t + (static_cast<int64_t>(h) * DH + ql) * DH + hh * 8;
 #pragma unroll
-    for (int am = 0; am < 4; ++am) accU[am] = f32x16{};
+    for (int am = 0; am < NT; ++am) accU[am] = f32x16{};
     if constexpr (SPLIT) {
 #pragma unroll
-      for (int am = 0; am < 4; ++am)
+      for (int am = 0; am < NT; ++am)
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const f16x8 a = *reinterpret_cast<const f16x8*>(prow + 32 * am * kD + 16 * s);
+        for (int s = 0; s < NS; ++s) {
+          const f16x8 a = *reinterpret_cast<const f16x8*>(prow + 32 * am * DH + 16 * s);
           accU[am] = mfma(a, xB[s], accU[am]);
           accU[am] = mfma(a, xL[s], accU[am]);
         }
     } else {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < NS; ++s) {
       f16x8 lo;
       {
         const int mt = s >> 1, t8 = (s & 1) * 8;
@@ -382,8 +389,8 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
         lo = pack_lo(e, xB[s]);
       }
 #pragma unroll
-      for (int am = 0; am < 4; ++am) {
-        const f16x8 a = *reinterpret_cast<const f16x8*>(prow + 32 * am * kD + 16 * s);
+      for (int am = 0; am < NT; ++am) {
+        const f16x8 a = *reinterpret_cast<const f16x8*>(prow + 32 * am * DH + 16 * s);
         accU[am] = mfma(a, xB[s], accU[am]);
         accU[am] = mfma(a, lo, accU[am]);
       }
@@ -392,7 +399,7 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
     const float fu = 1.f / (sX * sP);
     float umax = 0.f;
 #pragma unroll
-    for (int am = 0; am < 4; ++am)
+    for (int am = 0; am < NT; ++am)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         accU[am][r] *= fu;
@@ -403,7 +410,7 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
     // U-hat operand (reusing xB's registers) and alpha = U-hat . kbar in the scaled units of pass 2
     float alpha = 0.f;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < NS; ++s) {
       const int am = s >> 1, t8 = (s & 1) * 8;
       float e[8];
 #pragma unroll
@@ -426,10 +433,10 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
   const f16x8* uL = xL;
 
   // ---------------- pass 2 ----------------
-  load_q_operand(qrow, row_ok, hh, sQ, qB, p.D);
-  f32x16 accC[4];
+  load_q_operand(qrow, row_ok, hh, sQ, qB);
+  f32x16 accC[NT];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) accC[mt] = f32x16{};
+  for (int mt = 0; mt < NT; ++mt) accC[mt] = f32x16{};
   float rpart = 0.f;
   // W = p (R - alpha) is packed to fp16 as p 2^-wexp (R - alpha), wexp an integer folded into the exp2
   // argument.  Its range depends on the row: |R_j - alpha| = |U-hat.(k_j - kbar)| <= |U-hat| (|k_j| + |kbar|)
@@ -459,8 +466,8 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
           a[0] = lds_k(T, buf, 32 * kb + ql, hh);
           a[1] = lds_k(T, buf, 32 * kb + ql, 2 + hh);
 #pragma unroll
-          for (int s = 0; s < 8; ++s) {
-            if (s + 2 < 8) a[(s + 2) % 3] = lds_k(T, buf, 32 * kb + ql, 2 * (s + 2) + hh);
+          for (int s = 0; s < NS; ++s) {
+            if (s + 2 < NS) a[(s + 2) % 3] = lds_k(T, buf, 32 * kb + ql, 2 * (s + 2) + hh);
             __builtin_amdgcn_sched_barrier(0);
             S = mfma(a[s % 3], qB[s], S);
             R = mfma(a[s % 3], uB[s], R);
@@ -498,9 +505,9 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
           c[0] = lds_vt(T, buf, ql, 4 * kb + hh);
           c[1] = lds_vt(T, buf, ql, 4 * kb + 2 + hh);
 #pragma unroll
-          for (int n = 0; n < 8; ++n) {
+          for (int n = 0; n < 2 * NT; ++n) {
             const int mt = n >> 1, t = n & 1;
-            if (n + 2 < 8) c[(n + 2) % 3] = lds_vt(T, buf, 32 * ((n + 2) >> 1) + ql, 4 * kb + 2 * ((n + 2) & 1) + hh);
+            if (n + 2 < 2 * NT) c[(n + 2) % 3] = lds_vt(T, buf, 32 * ((n + 2) >> 1) + ql, 4 * kb + 2 * ((n + 2) & 1) + hh);
             __builtin_amdgcn_sched_barrier(0);
             accC[mt] = mfma(c[n % 3], wB[t], accC[mt]);
             if constexpr (SPLIT) accC[mt] = mfma(c[n % 3], wL[t], accC[mt]);
@@ -523,11 +530,10 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
     const float fc = fw / (sU * sK * sV);
     const float frs = RS * (fw / (sU * sK));
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = 32 * mt + 8 * j + 4 * hh;
-        if (d >= p.D) continue;   // padding dims of a D < 128 head
         const float4 ov = *reinterpret_cast<const float4*>(obuf + qoff + d);
         const float o4[4] = {ov.x, ov.y, ov.z, ov.w};
         float r4[4];
@@ -563,34 +569,39 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
 // subnormal range.
 // ------------------------------------------------------------------------------------------
 
+template <int DH>
 struct __align__(16) ProbeTiles {
-  _Float16 k[2][kKeyTile * kD];    // key rows tile    [16 chunks][64 keys][8]
-  _Float16 vt[2][kD * kKeyTile];   // value columns    [8 chunks][128 d][8]
-  f16x8 rho[kWaves][8][64];        // per wave: the rho operand of each lane, 8 k-steps
+  _Float16 k[2][kKeyTile * DH];    // key rows tile    [DH/8 chunks][64 keys][8]
+  _Float16 vt[2][DH * kKeyTile];   // value columns    [8 chunks][DH d][8]
+  f16x8 rho[kWaves][DH / 16][64];  // per wave: the rho operand of each lane, DH / 16 k-steps
 };
 
-__device__ __forceinline__ void probe_tile_dma(const FwdParams& p, ProbeTiles& T, int buf, int b, int g, int kt,
+template <int DH>
+__device__ __forceinline__ void probe_tile_dma(const FwdParams& p, ProbeTiles<DH>& T, int buf, int b, int g, int kt,
                                                int w, int l) {
-  const int64_t tb = kv_tile(b, g, kt, p.Hkv, p.Tk_pad / kKeyTile);
+  const int64_t tb = kv_tile(b, g, kt, p.Hkv, p.Tk_pad / kKeyTile, DH);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int i = 2 * w + j;
+  for (int j = 0; j < DH / 64; ++j) {
+    const int i = (DH / 64) * w + j;
     const int64_t src = tb + i * 512 + l * 8;
     lds_dma16(p.k16 + src, &T.k[buf][i * 512]);
     lds_dma16(p.v16t + src, &T.vt[buf][i * 512]);
   }
 }
 
-__device__ __forceinline__ f16x8 lds_k_probe(const ProbeTiles& T, int buf, int r, int c) {
+template <int DH>
+__device__ __forceinline__ f16x8 lds_k_probe(const ProbeTiles<DH>& T, int buf, int r, int c) {
   return *reinterpret_cast<const f16x8*>(&T.k[buf][c * (kKeyTile * 8) + r * 8]);
 }
-__device__ __forceinline__ f16x8 lds_vt_probe(const ProbeTiles& T, int buf, int d, int c) {
-  return *reinterpret_cast<const f16x8*>(&T.vt[buf][c * (kD * 8) + d * 8]);
+template <int DH>
+__device__ __forceinline__ f16x8 lds_vt_probe(const ProbeTiles<DH>& T, int buf, int d, int c) {
+  return *reinterpret_cast<const f16x8*>(&T.vt[buf][c * (DH * 8) + d * 8]);
 }
 
-template <bool SPLIT>
+template <bool SPLIT, int DH>
 __global__ __launch_bounds__(512) void k_fwd_probe(FwdParams p) {
-  __shared__ ProbeTiles T;
+  constexpr int NS = DH / 16, NT = DH / 32;   // k-steps and accumulator tiles over d
+  __shared__ ProbeTiles<DH> T;
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, ql = l & 31, hh = l >> 5;
 
   int pair, rb;
@@ -620,7 +631,7 @@ __global__ __launch_bounds__(512) void k_fwd_probe(FwdParams p) {
   const float sR = range_scale(__uint_as_float(p.maxbits[kMaxRho]));
   const float cS = p.scale * kLog2e / (sQ * sK);
 
-  const int64_t qoff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * p.D;
+  const int64_t qoff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * DH;
 
   const int rlast = min(r0 + p.rows_per_block, p.row_end) - 1;
   const int kend = p.causal ? min(p.Tk, rlast + off + 1) : p.Tk;
@@ -636,17 +647,17 @@ __global__ __launch_bounds__(512) void k_fwd_probe(FwdParams p) {
   const int r_kend = row_ok ? (p.causal ? min(p.Tk, row + off + 1) : p.Tk) : 0;
   const int r_kbeg = p.window > 0 ? max(0, row + off - p.window + 1) : 0;
 
-  f16x8 qB[8];
-  load_q_operand(p.q + qoff, row_ok, hh, sQ, qB, p.D);
+  f16x8 qB[NS];
+  load_q_operand(p.q + qoff, row_ok, hh, sQ, qB);
   float wfac;   // 2^-wexp
   int wexp;
   {
     // the lane's rho operand into the wave's LDS block (read back by the same lane only)
-    f16x8 rB[8];
-    load_q_operand(p.rho + qoff, row_ok, hh, sR, rB, p.D);
+    f16x8 rB[NS];
+    load_q_operand(p.rho + qoff, row_ok, hh, sR, rB);
     float r2 = 0.f;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < NS; ++s) {
       T.rho[w][s][l] = rB[s];
 #pragma unroll
       for (int j = 0; j < 8; ++j) r2 = fmaf(static_cast<float>(rB[s][j]), static_cast<float>(rB[s][j]), r2);
@@ -659,9 +670,9 @@ __global__ __launch_bounds__(512) void k_fwd_probe(FwdParams p) {
     wfac = __builtin_ldexpf(1.f, -wexp);
   }
 
-  f32x16 accO[4], accC[4];
+  f32x16 accO[NT], accC[NT];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < NT; ++mt) {
     accO[mt] = f32x16{};
     accC[mt] = f32x16{};
   }
@@ -684,8 +695,8 @@ __global__ __launch_bounds__(512) void k_fwd_probe(FwdParams p) {
           a[0] = lds_k_probe(T, buf, 32 * kb + ql, hh);
           r[0] = T.rho[w][0][l];
 #pragma unroll
-          for (int s = 0; s < 8; ++s) {
-            if (s + 1 < 8) {
+          for (int s = 0; s < NS; ++s) {
+            if (s + 1 < NS) {
               a[(s + 1) & 1] = lds_k_probe(T, buf, 32 * kb + ql, 2 * (s + 1) + hh);
               r[(s + 1) & 1] = T.rho[w][s + 1][l];
             }
@@ -714,7 +725,7 @@ __global__ __launch_bounds__(512) void k_fwd_probe(FwdParams p) {
           lpart *= f;
           rpart *= f;
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt) {
+          for (int mt = 0; mt < NT; ++mt) {
             accO[mt] *= f;
             accC[mt] *= f;
           }
@@ -746,9 +757,9 @@ __global__ __launch_bounds__(512) void k_fwd_probe(FwdParams p) {
           c[0] = lds_vt_probe(T, buf, ql, 4 * kb + hh);
           c[1] = lds_vt_probe(T, buf, ql, 4 * kb + 2 + hh);
 #pragma unroll
-          for (int n = 0; n < 8; ++n) {
+          for (int n = 0; n < 2 * NT; ++n) {
             const int mt = n >> 1, t = n & 1;
-            if (n + 2 < 8) c[(n + 2) % 3] = lds_vt_probe(T, buf, 32 * ((n + 2) >> 1) + ql, 4 * kb + 2 * ((n + 2) & 1) + hh);
+            if (n + 2 < 2 * NT) c[(n + 2) % 3] = lds_vt_probe(T, buf, 32 * ((n + 2) >> 1) + ql, 4 * kb + 2 * ((n + 2) & 1) + hh);
             __builtin_amdgcn_sched_barrier(0);
             accO[mt] = mfma(c[n % 3], pB[t], accO[mt]);
             accC[mt] = mfma(c[n % 3], wB[t], accC[mt]);
@@ -782,11 +793,10 @@ __global__ __launch_bounds__(512) void k_fwd_probe(FwdParams p) {
       if (p.rk) p.rk[soff] = a;
     }
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = 32 * mt + 8 * j + 4 * hh;
-        if (d >= p.D) continue;   // padding dims of a D < 128 head
         float r4[4], o4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -814,15 +824,18 @@ bool fast_fwd_supported(const Geom& g) {
   return g.bf16 && (g.d == kD || g.d == 64) && !g.p_per_query && (G == 1 || G == 2 || G == 4 || G == 8);
 }
 
+// Head dim of the staged operands: a head of 64 is staged and computed at 64 (no padding).
+static int fwd_dh(const Geom& g) { return g.d == 64 ? 64 : kD; }
+
 size_t fast_fwd_workspace(const Geom& g) {
-  const Staging s = staging_layout(nullptr, g.B, g.Tk, g.Hkv, g.Hq);
-  return s.bytes + align_up(static_cast<size_t>(g.B) * g.Tq * g.Hq * kD * sizeof(float), 256);
+  const Staging s = staging_layout(nullptr, g.B, g.Tk, g.Hkv, g.Hq, false, fwd_dh(g));
+  return s.bytes + align_up(static_cast<size_t>(g.B) * g.Tq * g.Hq * g.d * sizeof(float), 256);
 }
 
 hipError_t launch_fast_fwd(const Geom& g, const void* q, const void* k, const void* v,
                            const void* P, void* out, float* lse, float* kbar, float* osa, float* cor,
                            int split_rows, void* ws, hipStream_t stream) {
-  const Staging s = staging_layout(ws, g.B, g.Tk, g.Hkv, g.Hq);
+  const Staging s = staging_layout(ws, g.B, g.Tk, g.Hkv, g.Hq, false, fwd_dh(g));
   float* o_ws = reinterpret_cast<float*>(static_cast<char*>(ws) + s.bytes);
   int split = split_rows < kMinSplitRows ? kMinSplitRows : split_rows;
   if (split > g.Tq) split = g.Tq;
@@ -865,7 +878,8 @@ hipError_t launch_fast_fwd(const Geom& g, const void* q, const void* k, const vo
     p.row_begin = 0;
     p.n_rb = (split + p.rows_per_block - 1) / p.rows_per_block;
     p.row_end = split;
-    hipLaunchKernelGGL(k_fwd_fast<true>, dim3(g.B * g.Hkv * p.n_rb), dim3(512), 0, side.stream, p);
+    if (s.dh == 64) hipLaunchKernelGGL((k_fwd_fast<true, 64>), dim3(g.B * g.Hkv * p.n_rb), dim3(512), 0, side.stream, p);
+    else hipLaunchKernelGGL((k_fwd_fast<true, kD>), dim3(g.B * g.Hkv * p.n_rb), dim3(512), 0, side.stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -876,7 +890,8 @@ hipError_t launch_fast_fwd(const Geom& g, const void* q, const void* k, const vo
     p.n_rb = (g.Tq - split + p.rows_per_block - 1) / p.rows_per_block;
     const int blocks = g.B * g.Hkv * p.n_rb;
     mark_begin(PLX_KERNEL_FWD, stream);
-    hipLaunchKernelGGL(k_fwd_fast<false>, dim3(blocks), dim3(512), 0, stream, p);
+    if (s.dh == 64) hipLaunchKernelGGL((k_fwd_fast<false, 64>), dim3(blocks), dim3(512), 0, stream, p);
+    else hipLaunchKernelGGL((k_fwd_fast<false, kD>), dim3(blocks), dim3(512), 0, stream, p);
     mark_end(PLX_KERNEL_FWD, stream);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -887,12 +902,14 @@ hipError_t launch_fast_fwd(const Geom& g, const void* q, const void* k, const vo
 
 bool fast_probe_supported(const Geom& g) { return fast_fwd_supported(g); }
 
-size_t fast_probe_workspace(const Geom& g) { return staging_layout(nullptr, g.B, g.Tk, g.Hkv, g.Hq).bytes; }
+size_t fast_probe_workspace(const Geom& g) {
+  return staging_layout(nullptr, g.B, g.Tk, g.Hkv, g.Hq, false, fwd_dh(g)).bytes;
+}
 
 hipError_t launch_fast_probe(const Geom& g, const void* q, const void* k, const void* v, const void* rho,
                              void* out, float* lse, float* osa, float* rk, float* cor, int split_rows, void* ws,
                              hipStream_t stream) {
-  const Staging s = staging_layout(ws, g.B, g.Tk, g.Hkv, g.Hq);
+  const Staging s = staging_layout(ws, g.B, g.Tk, g.Hkv, g.Hq, false, fwd_dh(g));
   int split = split_rows < kMinSplitRows ? kMinSplitRows : split_rows;
   if (split > g.Tq) split = g.Tq;
   const int64_t q_elems = static_cast<int64_t>(g.B) * g.Tq * g.Hq * g.d;
@@ -934,7 +951,8 @@ hipError_t launch_fast_probe(const Geom& g, const void* q, const void* k, const 
     p.row_begin = 0;
     p.n_rb = (split + p.rows_per_block - 1) / p.rows_per_block;
     p.row_end = split;
-    hipLaunchKernelGGL(k_fwd_probe<true>, dim3(g.B * g.Hkv * p.n_rb), dim3(512), 0, side.stream, p);
+    if (s.dh == 64) hipLaunchKernelGGL((k_fwd_probe<true, 64>), dim3(g.B * g.Hkv * p.n_rb), dim3(512), 0, side.stream, p);
+    else hipLaunchKernelGGL((k_fwd_probe<true, kD>), dim3(g.B * g.Hkv * p.n_rb), dim3(512), 0, side.stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -944,7 +962,8 @@ hipError_t launch_fast_probe(const Geom& g, const void* q, const void* k, const 
     p.row_end = g.Tq;
     p.n_rb = (g.Tq - split + p.rows_per_block - 1) / p.rows_per_block;
     mark_begin(PLX_KERNEL_FWD_PROBE, stream);
-    hipLaunchKernelGGL(k_fwd_probe<false>, dim3(g.B * g.Hkv * p.n_rb), dim3(512), 0, stream, p);
+    if (s.dh == 64) hipLaunchKernelGGL((k_fwd_probe<false, 64>), dim3(g.B * g.Hkv * p.n_rb), dim3(512), 0, stream, p);
+    else hipLaunchKernelGGL((k_fwd_probe<false, kD>), dim3(g.B * g.Hkv * p.n_rb), dim3(512), 0, stream, p);
     mark_end(PLX_KERNEL_FWD_PROBE, stream);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -74,13 +74,16 @@ __global__ __launch_bounds__(256) void k_absmax(AbsmaxJob job, uint32_t* maxbits
   }
 }
 
-// One block per (64-key tile, kv head, batch): K16 (and V16) row tiles, K16t (and V16t) column tiles,
-// and the Euclidean norm of every key and value row (knorm, vnorm [B][Hkv][Tk_pad], 0 past Tk).
+// One block per (64-key tile, kv head, batch): K16 (and V16) row tiles, K16t (and V16t) column tiles at the
+// staged head dim DH (rows of D < DH zero-padded), and the Euclidean norm of every key and value row (knorm,
+// vnorm [B][Hkv][Tk_pad], 0 past Tk).
+template <int DH>
 __global__ __launch_bounds__(256) void k_stage_kv(const u16* k, const u16* v, const uint32_t* maxbits,
                                                   _Float16* k16, _Float16* k16t, _Float16* v16t,
                                                   _Float16* v16, float* knorm, float* vnorm, int Tk, int Tk_pad,
                                                   int Hkv, int D) {
-  constexpr int LD = kD + 2;  // padded LDS row (halves) for conflict-light column reads
+  constexpr int LD = DH + 2;   // padded LDS row (halves) for conflict-light column reads
+  constexpr int NC = DH / 8;   // 16-byte chunks per row
   __shared__ _Float16 ks[kKeyTile * LD];
   __shared__ _Float16 vs[kKeyTile * LD];
   // the kv heads of one key tile are consecutive blocks, so they read the same rows together
@@ -88,13 +91,13 @@ __global__ __launch_bounds__(256) void k_stage_kv(const u16* k, const u16* v, co
   const int key0 = kt * kKeyTile;
   const float sK = range_scale(__uint_as_float(maxbits[1]));
   const float sV = range_scale(__uint_as_float(maxbits[2]));
-  // load 64 rows x 16 chunks of 8 bf16, scale, store fp16 (natural order); the 16 chunks of a row are
-  // held by 16 consecutive threads, which also sum the row's squares
-  for (int ci = t; ci < kKeyTile * 16; ci += 256) {
-    const int r = ci >> 4, c = ci & 15;
+  // load 64 rows x NC chunks of 8 bf16, scale, store fp16 (natural order); the chunks of a row are held by
+  // NC consecutive threads, which also sum the row's squares
+  for (int ci = t; ci < kKeyTile * NC; ci += 256) {
+    const int r = ci / NC, c = ci % NC;
     const int key = key0 + r;
     uint4 kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
-    if (key < Tk && c * 8 < D) {   // a head of D < 128 is zero-padded to 128
+    if (key < Tk && c * 8 < D) {
       const int64_t off = ((static_cast<int64_t>(b) * Tk + key) * Hkv + g) * D + c * 8;
       kw = *reinterpret_cast<const uint4*>(k + off);
       vw = *reinterpret_cast<const uint4*>(v + off);
@@ -114,7 +117,7 @@ __global__ __launch_bounds__(256) void k_stage_kv(const u16* k, const u16* v, co
       vs[r * LD + c * 8 + 2 * j + 1] = static_cast<_Float16>(v1 * sV);
     }
 #pragma unroll
-    for (int o = 8; o > 0; o >>= 1) {
+    for (int o = NC / 2; o > 0; o >>= 1) {
       k2 += __shfl_xor(k2, o, 64);
       v2 += __shfl_xor(v2, o, 64);
     }
@@ -125,13 +128,13 @@ __global__ __launch_bounds__(256) void k_stage_kv(const u16* k, const u16* v, co
     }
   }
   __syncthreads();
+  const int64_t tb = kv_tile(b, g, kt, Hkv, Tk_pad / kKeyTile, DH);
   // K16: key rows with d permuted within groups of 16
-  for (int ci = t; ci < kKeyTile * 16; ci += 256) {
-    const int r = ci >> 4, c = ci & 15;
+  for (int ci = t; ci < kKeyTile * NC; ci += 256) {
+    const int r = ci / NC, c = ci % NC;
     f16x8 o;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = ks[r * LD + 16 * (c >> 1) + perm16(8 * (c & 1) + e)];
-    const int64_t tb = kv_tile(b, g, kt, Hkv, Tk_pad / kKeyTile);
     *reinterpret_cast<f16x8*>(k16 + tb + c * (kKeyTile * 8) + r * 8) = o;
     if (v16) {
 #pragma unroll
@@ -140,8 +143,7 @@ __global__ __launch_bounds__(256) void k_stage_kv(const u16* k, const u16* v, co
     }
   }
   // K16t, V16t: d rows, keys permuted within groups of 16
-  const int64_t tb = kv_tile(b, g, kt, Hkv, Tk_pad / kKeyTile);
-  for (int ci = t; ci < kD * 8; ci += 256) {
+  for (int ci = t; ci < DH * 8; ci += 256) {
     const int d = ci >> 3, c = ci & 7;
     f16x8 ok, ov;
 #pragma unroll
@@ -150,7 +152,7 @@ __global__ __launch_bounds__(256) void k_stage_kv(const u16* k, const u16* v, co
       ok[e] = ks[key * LD + d];
       ov[e] = vs[key * LD + d];
     }
-    const int64_t off = tb + c * (kD * 8) + d * 8;
+    const int64_t off = tb + c * (DH * 8) + d * 8;
     *reinterpret_cast<f16x8*>(k16t + off) = ok;
     if (v16t) *reinterpret_cast<f16x8*>(v16t + off) = ov;
   }
@@ -190,30 +192,31 @@ __global__ __launch_bounds__(256) void k_scan_max(float* x, int n, int64_t strid
   }
 }
 
-// Eight blocks per query head, each writing 16 rows a of P16t[h][a][b'] = sP * P[h][perm(b')][a] (and, with
-// p16, of P16[h][a][b'] = sP * P[h][a][perm(b')]) from the whole projector staged in LDS.
-constexpr int kStagePParts = 8;
+// DH / (256 / (DH / 8)) blocks per query head (8 at DH = 128, 2 at 64), each writing 256 / (DH / 8) rows a
+// of P16t[h][a][b'] = sP * P[h][perm(b')][a] (and, with p16, of P16[h][a][b'] = sP * P[h][a][perm(b')]) from
+// the whole projector staged in LDS (a D x D projector zero-padded to DH x DH).
+template <int DH>
 __global__ __launch_bounds__(256) void k_stage_p(const u16* P, const uint32_t* maxbits, _Float16* p16t,
                                                  _Float16* p16, int D) {
-  constexpr int LD = kD + 2;
-  __shared__ _Float16 ps[kD * LD];
+  constexpr int LD = DH + 2, NC = DH / 8, RPB = 256 / NC;
+  __shared__ _Float16 ps[DH * LD];
   const int h = blockIdx.x, part = blockIdx.y, t = threadIdx.x;
   const float sP = range_scale(__uint_as_float(maxbits[3]));
   const u16* src = P + static_cast<int64_t>(h) * D * D;
-  for (int e = t; e < kD * kD; e += 256) {   // a D x D projector is zero-padded to 128 x 128
-    const int r = e / kD, c = e % kD;
+  for (int e = t; e < DH * DH; e += 256) {
+    const int r = e / DH, c = e % DH;
     ps[r * LD + c] = r < D && c < D ? static_cast<_Float16>(bf16_to_f32(src[r * D + c]) * sP) : static_cast<_Float16>(0.f);
   }
   __syncthreads();
-  const int a = (kD / kStagePParts) * part + (t >> 4), c = t & 15;   // one 16-byte chunk per thread
+  const int a = RPB * part + t / NC, c = t % NC;   // one 16-byte chunk per thread
   f16x8 o;
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = ps[(16 * (c >> 1) + perm16(8 * (c & 1) + e)) * LD + a];
-  *reinterpret_cast<f16x8*>(p16t + (static_cast<int64_t>(h) * kD + a) * kD + c * 8) = o;
+  *reinterpret_cast<f16x8*>(p16t + (static_cast<int64_t>(h) * DH + a) * DH + c * 8) = o;
   if (p16) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = ps[a * LD + 16 * (c >> 1) + perm16(8 * (c & 1) + e)];
-    *reinterpret_cast<f16x8*>(p16 + (static_cast<int64_t>(h) * kD + a) * kD + c * 8) = o;
+    *reinterpret_cast<f16x8*>(p16 + (static_cast<int64_t>(h) * DH + a) * DH + c * 8) = o;
   }
 }
 
@@ -308,16 +311,27 @@ hipError_t launch_staging(const Staging& s, const void* q, int64_t q_elems, cons
   if (job.parts > 0)
     hipLaunchKernelGGL(k_absmax, dim3(kAbsmaxBlocks, job.parts), dim3(256), 0, stream, job, s.maxbits);
   if (B > 0 && s.Tk_pad > 0) {
-    hipLaunchKernelGGL(k_stage_kv, dim3(Hkv * (s.Tk_pad / kKeyTile), 1, B), dim3(256), 0, stream,
-                       static_cast<const u16*>(k), static_cast<const u16*>(v), s.maxbits, s.k16, s.k16t,
-                       s.v16t, s.v16, s.knorm, s.vnorm, Tk, s.Tk_pad, Hkv, D);
+    const dim3 grid(Hkv * (s.Tk_pad / kKeyTile), 1, B);
+    if (s.dh == 64)
+      hipLaunchKernelGGL(k_stage_kv<64>, grid, dim3(256), 0, stream, static_cast<const u16*>(k),
+                         static_cast<const u16*>(v), s.maxbits, s.k16, s.k16t, s.v16t, s.v16, s.knorm, s.vnorm, Tk,
+                         s.Tk_pad, Hkv, D);
+    else
+      hipLaunchKernelGGL(k_stage_kv<kD>, grid, dim3(256), 0, stream, static_cast<const u16*>(k),
+                         static_cast<const u16*>(v), s.maxbits, s.k16, s.k16t, s.v16t, s.v16, s.knorm, s.vnorm, Tk,
+                         s.Tk_pad, Hkv, D);
     // running maxima of the key and value norms along each sequence (the two arrays are consecutive)
     hipLaunchKernelGGL(k_scan_max<false>, dim3(2 * B * Hkv), dim3(256), 0, stream, s.knorm, s.Tk_pad,
                        static_cast<int64_t>(s.Tk_pad));
   }
-  if (P)
-    hipLaunchKernelGGL(k_stage_p, dim3(Hq, kStagePParts), dim3(256), 0, stream, static_cast<const u16*>(P), s.maxbits, s.p16t,
-                     s.p16, D);
+  if (P) {
+    if (s.dh == 64)
+      hipLaunchKernelGGL(k_stage_p<64>, dim3(Hq, 2), dim3(256), 0, stream, static_cast<const u16*>(P), s.maxbits,
+                         s.p16t, s.p16, D);
+    else
+      hipLaunchKernelGGL(k_stage_p<kD>, dim3(Hq, 8), dim3(256), 0, stream, static_cast<const u16*>(P), s.maxbits,
+                         s.p16t, s.p16, D);
+  }
   return hipGetLastError();
 }
 
