@@ -420,82 +420,62 @@ def main():
                          "algorithmic_flop_per_launch": kfl}}
         log(f"layer06 forward {dt2c * 1e3:.3f} ms/call, kernel {kavg:.3f} ms")
         del q2, k2, v2, P2
-        # layer17's shape at head dim 64 (the pages' compute-matched control: smaller heads), forward
-        w3 = W.scaled(W.WORKLOADS["layer17"], head_dim=64)
-        log("config layer17 at head dim 64, forward")
-        q3, k3, v3, P3 = W.make_inputs(w3, device=dev)
-        fwd3 = lambda: plx.parallax_attn_fwd(q3, k3, v3, P3, split_rows=split)  # noqa: E731
-        for _ in range(2):
-            fwd3()
-        torch.cuda.synchronize()
-        n3 = max(10, K)
-        t0 = time.perf_counter()
-        for _ in range(n3):
-            fwd3()
-        torch.cuda.synchronize()
-        dt3c = (time.perf_counter() - t0) / n3
-        ks3 = kernel_samples(fwd3, plx.PLX_KERNEL_FWD, n3)
-        kfl3 = fwd_flops(w3, min(r0, w3.seqlen_q))
-        kavg3 = sum(ks3) / len(ks3)
-        result["configs"]["layer17_d64_fwd"] = {
-            "workload": f"{w3.name} at d=64: forward, B={w3.batch}, T={w3.seqlen_q}, Hq={w3.heads_q}, "
-                        f"Hkv={w3.heads_kv}, d={w3.head_dim}, causal, bf16 (flops counted at d=64)",
-            "ms_per_call": round(dt3c * 1e3, 4), "tflops": round(fwd_flops(w3) / dt3c / 1e12, 3),
-            "tokens_per_s": round(w3.batch * w3.seqlen_q / dt3c, 1),
-            "roofline": {"bound": "mfma", "kernel": "fwd", "avg_ms": round(kavg3, 4), "launches": len(ks3),
-                         "achieved": round(kfl3 / (kavg3 * 1e-3) / 1e12, 3), "peak": PEAK_F16_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(kfl3 / (kavg3 * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
-                         "algorithmic_flop_per_launch": kfl3}}
-        log(f"layer17 d=64 forward {dt3c * 1e3:.3f} ms/call, kernel {kavg3:.3f} ms "
-            f"({kfl3 / (kavg3 * 1e-3) / 1e12:.0f} TFLOP/s)")
-        del q3, k3, v3, P3
-        # train06 (0.6B-like training step): forward + backward
-        w4 = W.WORKLOADS["train06"]
-        log(f"config {w4.name} training step")
-        q4_, k4_, v4_, P4_, d4_ = W.make_inputs(w4, device=dev, with_dout=True)
-        f4 = plx.parallax_attn_fwd(q4_, k4_, v4_, P4_, split_rows=split)
 
-        def step4():
-            f = plx.parallax_attn_fwd(q4_, k4_, v4_, P4_, split_rows=split)
-            plx.parallax_attn_bwd(q4_, k4_, v4_, P4_, f[0], d4_, *f[1:], split_rows=split)
+        def train_step_object(w4):
+            """Forward + backward of workload w4: the step time and each main kernel's average launch."""
+            q4_, k4_, v4_, P4_, d4_ = W.make_inputs(w4, device=dev, with_dout=True)
+            f4 = plx.parallax_attn_fwd(q4_, k4_, v4_, P4_, split_rows=split)
 
-        step4()
-        torch.cuda.synchronize()
-        n4 = max(6, K)
-        t0 = time.perf_counter()
-        for _ in range(n4):
+            def step4():
+                f = plx.parallax_attn_fwd(q4_, k4_, v4_, P4_, split_rows=split)
+                plx.parallax_attn_bwd(q4_, k4_, v4_, P4_, f[0], d4_, *f[1:], split_rows=split)
+
             step4()
-        torch.cuda.synchronize()
-        dt4c = (time.perf_counter() - t0) / n4
-        r4 = min(r0, w4.seqlen_q)
-        k4 = {}
-        calls = {"fwd": (lambda: plx.parallax_attn_fwd(q4_, k4_, v4_, P4_, split_rows=split), plx.PLX_KERNEL_FWD,
-                         fwd_flops)}
-        bcall = lambda: plx.parallax_attn_bwd(q4_, k4_, v4_, P4_, f4[0], d4_, *f4[1:], split_rows=split)  # noqa: E731
-        for n_, kid in bwd_cycle:
-            calls[n_] = (bcall, kid, {"bwd_rows": bwd_rows_flops, "bwd_keys": bwd_keys_flops,
-                                      "bwd_dq": bwd_dq_flops}[n_])
-        for n_, (call, kid, ffn) in calls.items():
-            ms_ = kernel_samples(call, kid, max(8, args.samples))
-            avg = sum(ms_) / len(ms_)
-            fl_ = ffn(w4, r4)
-            k4[n_] = {"avg_ms": round(avg, 4), "launches": len(ms_), "algorithmic_flop": fl_,
-                      "tflops": round(fl_ / (avg * 1e-3) / 1e12, 3),
-                      "frac_of_peak": round(fl_ / (avg * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4)}
-        dom4 = max(k4, key=lambda n_: k4[n_]["avg_ms"])
-        sfl4 = fwd_flops(w4) + bwd_flops(w4)
-        result["configs"]["train06_step"] = {
-            "workload": f"{w4.name}: forward + backward, B={w4.batch}, T={w4.seqlen_q}, Hq={w4.heads_q}, "
-                        f"Hkv={w4.heads_kv}, d={w4.head_dim}, causal, bf16",
-            "ms_per_step": round(dt4c * 1e3, 4), "tflops": round(sfl4 / dt4c / 1e12, 3),
-            "tokens_per_s": round(w4.batch * w4.seqlen_q / dt4c, 1), "kernels": k4,
-            "roofline": {"bound": "mfma", "kernel": dom4, "avg_ms": k4[dom4]["avg_ms"],
-                         "achieved": k4[dom4]["tflops"], "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": k4[dom4]["frac_of_peak"],
-                         "algorithmic_flop_per_launch": k4[dom4]["algorithmic_flop"]}}
-        log(f"train06 step {dt4c * 1e3:.3f} ms ({sfl4 / dt4c / 1e12:.0f} TFLOP/s)")
-        del q4_, k4_, v4_, P4_, d4_, f4
-        torch.cuda.empty_cache()
+            torch.cuda.synchronize()
+            n4 = max(6, K)
+            t0 = time.perf_counter()
+            for _ in range(n4):
+                step4()
+            torch.cuda.synchronize()
+            dt4c = (time.perf_counter() - t0) / n4
+            r4 = min(r0, w4.seqlen_q)
+            k4 = {}
+            calls = {"fwd": (lambda: plx.parallax_attn_fwd(q4_, k4_, v4_, P4_, split_rows=split), plx.PLX_KERNEL_FWD,
+                             fwd_flops)}
+            bcall = lambda: plx.parallax_attn_bwd(q4_, k4_, v4_, P4_, f4[0], d4_, *f4[1:], split_rows=split)  # noqa: E731
+            for n_, kid in bwd_cycle:
+                calls[n_] = (bcall, kid, {"bwd_rows": bwd_rows_flops, "bwd_keys": bwd_keys_flops,
+                                          "bwd_dq": bwd_dq_flops}[n_])
+            for n_, (call, kid, ffn) in calls.items():
+                ms_ = kernel_samples(call, kid, max(8, args.samples))
+                avg = sum(ms_) / len(ms_)
+                fl_ = ffn(w4, r4)
+                k4[n_] = {"avg_ms": round(avg, 4), "launches": len(ms_), "algorithmic_flop": fl_,
+                          "tflops": round(fl_ / (avg * 1e-3) / 1e12, 3),
+                          "frac_of_peak": round(fl_ / (avg * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4)}
+            dom4 = max(k4, key=lambda n_: k4[n_]["avg_ms"])
+            sfl4 = fwd_flops(w4) + bwd_flops(w4)
+            obj = {
+                "workload": f"{w4.name}: forward + backward, B={w4.batch}, T={w4.seqlen_q}, Hq={w4.heads_q}, "
+                            f"Hkv={w4.heads_kv}, d={w4.head_dim}, causal, bf16 (flops counted at d={w4.head_dim})",
+                "ms_per_step": round(dt4c * 1e3, 4), "tflops": round(sfl4 / dt4c / 1e12, 3),
+                "tokens_per_s": round(w4.batch * w4.seqlen_q / dt4c, 1), "kernels": k4,
+                "roofline": {"bound": "mfma", "kernel": dom4, "avg_ms": k4[dom4]["avg_ms"],
+                             "achieved": k4[dom4]["tflops"], "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                             "frac": k4[dom4]["frac_of_peak"],
+                             "algorithmic_flop_per_launch": k4[dom4]["algorithmic_flop"]}}
+            log(f"{w4.name} d={w4.head_dim} step {dt4c * 1e3:.3f} ms ({sfl4 / dt4c / 1e12:.0f} TFLOP/s); "
+                + ", ".join(f"{n_} {k4[n_]['avg_ms']:.3f} ms ({k4[n_]['frac_of_peak']:.3f})" for n_ in k4))
+            del q4_, k4_, v4_, P4_, d4_, f4
+            torch.cuda.empty_cache()
+            return obj
+
+        # layer17's shape at head dim 64 (the pages' compute-matched control: smaller heads): forward + backward
+        log("config layer17 at head dim 64, training step")
+        result["configs"]["layer17_d64_step"] = train_step_object(W.scaled(W.WORKLOADS["layer17"], head_dim=64))
+        # train06 (0.6B-like training step): forward + backward
+        log("config train06 training step")
+        result["configs"]["train06_step"] = train_step_object(W.WORKLOADS["train06"])
 
     if not args.no_decode:
         wd = W.WORKLOADS["decode"]

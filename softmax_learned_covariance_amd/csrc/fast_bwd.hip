@@ -1,5 +1,5 @@
-// Parallax backward for gfx950 (head_dim 128, or 64 zero-padded to 128; bf16 inputs, fp16 MFMA), for the
-// projector form and the probe form.
+// Parallax backward for gfx950 (head_dim DH = 128 or 64; bf16 inputs, fp16 MFMA), for the projector form and
+// the probe form.  Products over d take DH / 16 k-steps and vectors over d DH / 32 accumulator tiles.
 //
 // The pages give no backward; these kernels evaluate the chain rule of the
 // forward definition (output = softmax output plus the key/value covariance
@@ -55,11 +55,12 @@ __device__ __forceinline__ void rowmax_put(float* rowmax, int b, int g, int Hkv,
             __float_as_uint(v));
 }
 
-// Sum of squares of the 64 values of 8 fp16 operands (the lane's half of a 128-element row).
-__device__ __forceinline__ float sumsq8x8(const f16x8 (&x)[8]) {
+// Sum of squares of the values of N fp16 operands (the lane's half of a row of 16 N elements).
+template <int N>
+__device__ __forceinline__ float sumsq(const f16x8 (&x)[N]) {
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < N; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) s = fmaf(static_cast<float>(x[i][j]), static_cast<float>(x[i][j]), s);
   return s;
@@ -73,9 +74,10 @@ __device__ __forceinline__ void load4_bf16(const u16* src, float* dst) {
   dst[3] = __uint_as_float(w.y & 0xffff0000u);
 }
 
-__device__ __forceinline__ void load_row_operand(const u16* row, bool ok, int hh, float s, f16x8 (&B)[8], int D) {
+template <int NS>
+__device__ __forceinline__ void load_row_operand(const u16* row, bool ok, int hh, float s, f16x8 (&B)[NS], int D) {
 #pragma unroll
-  for (int st = 0; st < 8; ++st) {
+  for (int st = 0; st < NS; ++st) {
     float a[4] = {0.f, 0.f, 0.f, 0.f}, c[4] = {0.f, 0.f, 0.f, 0.f};
     if (ok && 16 * st < D) {   // a row of D < 128 elements reads as zero-padded
       load4_bf16(row + 16 * st + 4 * hh, a);
@@ -126,33 +128,36 @@ struct RowParams {
   const u16* rho;
   const float* rk;
   float* drho;
-  int D;               // head dim of the caller's rows (128, or 64 zero-padded to 128 in every operand)
+  int D;               // head dim of the caller's rows (the kernels' DH)
   int B, Tq, Tk, Tk_pad, Tq_pad, Hq, Hkv, G, causal, window;
   float scale;
   int row_begin, row_end, rows_per_block, n_rb;
 };
 
+template <int DH>
 struct __align__(16) RowTiles {
-  _Float16 k[2][kKeyTile * kD];
-  _Float16 v[2][kKeyTile * kD];
-  _Float16 kt[2][kD * kKeyTile];
+  _Float16 k[2][kKeyTile * DH];
+  _Float16 v[2][kKeyTile * DH];
+  _Float16 kt[2][DH * kKeyTile];
 };
 
 __device__ __forceinline__ f16x8 lds_rows(const _Float16* t, int r, int c) {
   return *reinterpret_cast<const f16x8*>(&t[c * (kKeyTile * 8) + r * 8]);
 }
+template <int DH>
 __device__ __forceinline__ f16x8 lds_cols(const _Float16* t, int d, int c) {
-  return *reinterpret_cast<const f16x8*>(&t[c * (kD * 8) + d * 8]);
+  return *reinterpret_cast<const f16x8*>(&t[c * (DH * 8) + d * 8]);
 }
 
-// Asynchronous global -> LDS copy of one key tile: K rows, V rows and K^T, each one contiguous
-// 16 KB block (16 wave instructions of 1024 bytes, 4 per wave).
-__device__ __forceinline__ void row_tile_dma(const RowParams& p, RowTiles& T, int buf, int b, int g, int kt, int w,
-                                             int l) {
-  const int64_t tb = kv_tile(b, g, kt, p.Hkv, p.Tk_pad / kKeyTile);
+// Asynchronous global -> LDS copy of one key tile: K rows, V rows and K^T, each one contiguous block of
+// DH / 8 KB (DH / 8 wave instructions of 1024 bytes, DH / 32 per wave of four).
+template <int DH>
+__device__ __forceinline__ void row_tile_dma(const RowParams& p, RowTiles<DH>& T, int buf, int b, int g, int kt,
+                                             int w, int l) {
+  const int64_t tb = kv_tile(b, g, kt, p.Hkv, p.Tk_pad / kKeyTile, DH);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = 4 * w + j;
+  for (int j = 0; j < DH / 32; ++j) {
+    const int i = (DH / 32) * w + j;
     const int64_t src = tb + i * 512 + l * 8;
     lds_dma16(p.k16 + src, &T.k[buf][i * 512]);
     lds_dma16(p.v16 + src, &T.v[buf][i * 512]);
@@ -161,13 +166,14 @@ __device__ __forceinline__ void row_tile_dma(const RowParams& p, RowTiles& T, in
 }
 
 // g.o, g.out and |g|_1 of the lane's query row (its two half-lanes combined).
+template <int NT>
 __device__ __forceinline__ void row_dots(const RowParams& p, int64_t qoff, bool row_ok, int hh, float& go,
                                          float& gout, float& gabs) {
   go = 0.f;
   gout = 0.f;
   gabs = 0.f;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int d = 32 * mt + 8 * j + 4 * hh;
@@ -190,11 +196,12 @@ __device__ __forceinline__ void row_dots(const RowParams& p, int64_t qoff, bool 
 // Probe form: the per-row vectors the key-major pass needs, from the supplied probe.  u = -rho,
 // dkbar = -(g.o) u = (g.o) rho, drho = -du, and dq starts at 0 (no projector term).  Writes u, dkbar,
 // drho and the zero dq of the lane's half-row; `du` holds du in the accumulator layout.
+template <int NT>
 __device__ __forceinline__ void probe_row_vectors(const RowParams& p, int64_t qoff, int64_t woff, bool row_ok, int hh,
                                                   float go,
-                                                  const f32x16 (&du)[4], f32x16 (&u)[4], f32x16 (&dkb)[4]) {
+                                                  const f32x16 (&du)[NT], f32x16 (&u)[NT], f32x16 (&dkb)[NT]) {
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int d = 32 * mt + 8 * j + 4 * hh;
@@ -215,9 +222,10 @@ __device__ __forceinline__ void probe_row_vectors(const RowParams& p, int64_t qo
     }
 }
 
-template <bool SPLIT, bool DQ_PASS, bool PROBE>
+template <bool SPLIT, bool DQ_PASS, bool PROBE, int DH>
 __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
-  __shared__ RowTiles T;
+  constexpr int NS = DH / 16, NT = DH / 32;   // k-steps and accumulator tiles over d
+  __shared__ RowTiles<DH> T;
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, ql = l & 31, hh = l >> 5;
   // four waves: with 8 query heads per kv head, two blocks share a group, four heads each
   const int hsplit = p.G > 4 ? p.G / 4 : 1;
@@ -250,7 +258,7 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
   const float cS = p.scale * kLog2e / (sQ * sK);
 
   const int64_t qoff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * p.D;   // caller rows
-  const int64_t woff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * kD;    // workspace rows
+  const int64_t woff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * DH;    // workspace rows
   const int64_t soff = (static_cast<int64_t>(b) * p.Hq + h) * p.Tq + (row_ok ? row : 0);
   float lse2 = row_ok ? p.lse[soff] * kLog2e : 0.f;
   if (!(lse2 > -INFINITY && lse2 < INFINITY)) lse2 = 0.f;  // a row without keys: every S is masked
@@ -269,13 +277,13 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
   const int r_kend = row_ok ? (p.causal ? min(p.Tk, row + off + 1) : p.Tk) : 0;
   const int r_kbeg = p.window > 0 ? max(0, row + off - p.window + 1) : 0;
 
-  f16x8 qB[8], gB[8];
+  f16x8 qB[NS], gB[NS];
   load_row_operand(p.q + qoff, row_ok, hh, sQ, qB, p.D);
   load_row_operand(p.dout + qoff, row_ok, hh, sG, gB, p.D);
   // |G_j| = |g.v_j| <= |g| |v_j| with the largest value norm among the keys the row sees (a running
   // maximum along the sequence), so the scale of p G follows the row instead of the tensors' largest
   // entries (probe form: |G - g.o| <= 2 |g| max |v_j|)
-  const float gnorm = sqrtf(xor32_sum(sumsq8x8(gB))) / sG;
+  const float gnorm = sqrtf(xor32_sum(sumsq(gB))) / sG;
   const int64_t nbase = (static_cast<int64_t>(b) * p.Hkv + g) * p.Tk_pad;
   const float pmV = r_kend > r_kbeg ? p.vnorm[nbase + r_kend - 1] : 0.f;
   const float sPG = range_scale(PROBE ? 2.f * gnorm * pmV : gnorm * pmV);
@@ -284,7 +292,7 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
   float go_pre = 0.f;
   if constexpr (PROBE) {
 #pragma unroll
-    for (int d = 4 * hh; d < kD; d += 8) {
+    for (int d = 4 * hh; d < DH; d += 8) {
       float gv[4] = {0.f, 0.f, 0.f, 0.f};
       float4 ov = {0.f, 0.f, 0.f, 0.f};
       if (row_ok) {
@@ -298,9 +306,9 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
   const float goS = go_pre * sG * sV;   // g.o in the units of the G tile
 
   // ---------------- pass 1: du ----------------
-  f32x16 accDU[4];
+  f32x16 accDU[NT];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) accDU[mt] = f32x16{};
+  for (int mt = 0; mt < NT; ++mt) accDU[mt] = f32x16{};
   const float fPG = sPG / (sG * sV);
   if (t_beg < t_end) row_tile_dma(p, T, 0, b, g, t_beg, w, l);
   lds_dma_wait();
@@ -315,7 +323,7 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
       for (int kb = 0; kb < 2; ++kb) {
         f32x16 S = {}, Gt = {};
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
+        for (int s = 0; s < NS; ++s) {
           S = mfma(lds_rows(T.k[buf], 32 * kb + ql, 2 * s + hh), qB[s], S);
           Gt = mfma(lds_rows(T.v[buf], 32 * kb + ql, 2 * s + hh), gB[s], Gt);
         }
@@ -332,8 +340,8 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
           f16x8 hi, lo;
           to_operand(pg + 8 * t, 1.f, hi, SPLIT ? &lo : nullptr);
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt) {
-            const f16x8 a = lds_cols(T.kt[buf], 32 * mt + ql, 4 * kb + 2 * t + hh);
+          for (int mt = 0; mt < NT; ++mt) {
+            const f16x8 a = lds_cols<DH>(T.kt[buf], 32 * mt + ql, 4 * kb + 2 * t + hh);
             accDU[mt] = mfma(a, hi, accDU[mt]);
             if constexpr (SPLIT) accDU[mt] = mfma(a, lo, accDU[mt]);
           }
@@ -347,17 +355,17 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
   // ---------------- epilogue: u, alpha, P du, dkbar, Delta ----------------
   // row vectors in the accumulator layout: element (mt, r) is d = 32 mt + 8 (r/4) + 4 hh + r%4
   float go, gout, gabs;
-  row_dots(p, qoff, row_ok, hh, go, gout, gabs);
+  row_dots<NT>(p, qoff, row_ok, hh, go, gout, gabs);
   if constexpr (PROBE) go = go_pre;   // the value du was formed with
-  f32x16 accU[4], accPD[4];
+  f32x16 accU[NT], accPD[NT];
   float alpha = 0.f, dkk = 0.f, umax = 0.f, emax = 0.f, u1 = 0.f, e1 = 0.f, u2 = 0.f, e2 = 0.f;
   if constexpr (PROBE) {
     const float fdu = 1.f / (sPG * sK);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) accDU[mt] *= fdu;
-    probe_row_vectors(p, qoff, woff, row_ok, hh, go, accDU, accU, accPD);
+    for (int mt = 0; mt < NT; ++mt) accDU[mt] *= fdu;
+    probe_row_vectors<NT>(p, qoff, woff, row_ok, hh, go, accDU, accU, accPD);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         umax = fmaxf(umax, fabsf(accU[mt][r]));
@@ -378,12 +386,12 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
     dkk = go * rk;                                // dkbar . kbar
   } else {
     // kbar, x = q - kbar (written out for dP), du = sum p G k - (g.o) kbar (in place, written out)
-    float kbv[4][16], xv[4][16];
+    float kbv[NT][16], xv[NT][16];
     float xmax = 0.f, dumax = 0.f;
     {
       const float fdu = 1.f / (sPG * sK);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int d = 32 * mt + 8 * j + 4 * hh;
@@ -416,33 +424,33 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
     const float sX = range_scale(xmax), sDU = range_scale(dumax);
     // U^T = P16t X^T, then (P du)^T = P16 du^T
     {
-      f16x8 xB[8], xL[SPLIT ? 8 : 1];
+      f16x8 xB[NS], xL[SPLIT ? NS : 1];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) to_operand(&xv[s >> 1][(s & 1) * 8], sX, xB[s], SPLIT ? &xL[SPLIT ? s : 0] : nullptr);
-      const _Float16* prt = p.p16t + (static_cast<int64_t>(h) * kD + ql) * kD + hh * 8;
+      for (int s = 0; s < NS; ++s) to_operand(&xv[s >> 1][(s & 1) * 8], sX, xB[s], SPLIT ? &xL[SPLIT ? s : 0] : nullptr);
+      const _Float16* prt = p.p16t + (static_cast<int64_t>(h) * DH + ql) * DH + hh * 8;
 #pragma unroll
-      for (int am = 0; am < 4; ++am) {
+      for (int am = 0; am < NT; ++am) {
         accU[am] = f32x16{};
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const f16x8 at = *reinterpret_cast<const f16x8*>(prt + 32 * am * kD + 16 * s);
+        for (int s = 0; s < NS; ++s) {
+          const f16x8 at = *reinterpret_cast<const f16x8*>(prt + 32 * am * DH + 16 * s);
           accU[am] = mfma(at, xB[s], accU[am]);
           if constexpr (SPLIT) accU[am] = mfma(at, xL[SPLIT ? s : 0], accU[am]);
         }
       }
     }
     {
-      f16x8 dB[8], dL[SPLIT ? 8 : 1];
+      f16x8 dB[NS], dL[SPLIT ? NS : 1];
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
+      for (int s = 0; s < NS; ++s)
         tile_operand(accDU[s >> 1], s & 1, sDU, dB[s], SPLIT ? &dL[SPLIT ? s : 0] : nullptr);
-      const _Float16* pr = p.p16 + (static_cast<int64_t>(h) * kD + ql) * kD + hh * 8;
+      const _Float16* pr = p.p16 + (static_cast<int64_t>(h) * DH + ql) * DH + hh * 8;
 #pragma unroll
-      for (int am = 0; am < 4; ++am) {
+      for (int am = 0; am < NT; ++am) {
         accPD[am] = f32x16{};
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const f16x8 a = *reinterpret_cast<const f16x8*>(pr + 32 * am * kD + 16 * s);
+        for (int s = 0; s < NS; ++s) {
+          const f16x8 a = *reinterpret_cast<const f16x8*>(pr + 32 * am * DH + 16 * s);
           accPD[am] = mfma(a, dB[s], accPD[am]);
           if constexpr (SPLIT) accPD[am] = mfma(a, dL[SPLIT ? s : 0], accPD[am]);
         }
@@ -452,7 +460,7 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
     {
       const float fu = 1.f / (sX * sP), fpd = 1.f / (sP * sDU);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int d = 32 * mt + 8 * j + 4 * hh;
@@ -521,9 +529,9 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
 
   // ---------------- pass 2: dq ----------------
   const float sU = range_scale(umax), sE = range_scale(emax);
-  f16x8 uB[8], uL[SPLIT ? 8 : 1], eB[8], eL[SPLIT ? 8 : 1];
+  f16x8 uB[NS], uL[SPLIT ? NS : 1], eB[NS], eL[SPLIT ? NS : 1];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
+  for (int s = 0; s < NS; ++s) {
     tile_operand(accU[s >> 1], s & 1, sU, uB[s], SPLIT ? &uL[SPLIT ? s : 0] : nullptr);
     tile_operand(accPD[s >> 1], s & 1, sE, eB[s], SPLIT ? &eL[SPLIT ? s : 0] : nullptr);
   }
@@ -534,9 +542,9 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
   const float sDS = range_scale(bound_ds);
   const float fT = 1.f / (sU * sK), fE = 1.f / (sE * sK), fG = 1.f / (sG * sV);
   const float one_m_alpha = 1.f - alpha;
-  f32x16 accDQ[4];
+  f32x16 accDQ[NT];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) accDQ[mt] = f32x16{};
+  for (int mt = 0; mt < NT; ++mt) accDQ[mt] = f32x16{};
   if (t_beg < t_end) row_tile_dma(p, T, 0, b, g, t_beg, w, l);
   lds_dma_wait();
   __syncthreads();
@@ -550,7 +558,7 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
       for (int kb = 0; kb < 2; ++kb) {
         f32x16 S = {}, Tt = {}, E = {}, Gt = {};
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
+        for (int s = 0; s < NS; ++s) {
           const f16x8 a = lds_rows(T.k[buf], 32 * kb + ql, 2 * s + hh);
           S = mfma(a, qB[s], S);
           Tt = mfma(a, uB[s], Tt);
@@ -577,8 +585,8 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
           f16x8 hi, lo;
           to_operand(ds + 8 * t, 1.f, hi, SPLIT ? &lo : nullptr);
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt) {
-            const f16x8 a = lds_cols(T.kt[buf], 32 * mt + ql, 4 * kb + 2 * t + hh);
+          for (int mt = 0; mt < NT; ++mt) {
+            const f16x8 a = lds_cols<DH>(T.kt[buf], 32 * mt + ql, 4 * kb + 2 * t + hh);
             accDQ[mt] = mfma(a, hi, accDQ[mt]);
             if constexpr (SPLIT) accDQ[mt] = mfma(a, lo, accDQ[mt]);
           }
@@ -591,7 +599,7 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
   if (row_ok) {
     const float fq = p.scale / (sDS * sK);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = 32 * mt + 8 * j + 4 * hh;
@@ -613,12 +621,13 @@ __global__ __launch_bounds__(256) void k_bwd_rows_fast(RowParams p) {
 // them instead of holding them in registers, so that a wave fits in the 256 registers that two waves
 // per SIMD leave it.
 
-__device__ __forceinline__ void row_tile_dma8(const RowParams& p, RowTiles& T, int buf, int b, int g, int kt, int w,
-                                              int l) {
-  const int64_t tb = kv_tile(b, g, kt, p.Hkv, p.Tk_pad / kKeyTile);
+template <int DH>
+__device__ __forceinline__ void row_tile_dma8(const RowParams& p, RowTiles<DH>& T, int buf, int b, int g, int kt,
+                                              int w, int l) {
+  const int64_t tb = kv_tile(b, g, kt, p.Hkv, p.Tk_pad / kKeyTile, DH);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int i = 2 * w + j;
+  for (int j = 0; j < DH / 64; ++j) {
+    const int i = (DH / 64) * w + j;
     const int64_t src = tb + i * 512 + l * 8;
     lds_dma16(p.k16 + src, &T.k[buf][i * 512]);
     lds_dma16(p.v16 + src, &T.v[buf][i * 512]);
@@ -626,9 +635,10 @@ __device__ __forceinline__ void row_tile_dma8(const RowParams& p, RowTiles& T, i
   }
 }
 
-template <bool PROBE>
+template <bool PROBE, int DH>
 __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
-  __shared__ RowTiles T;
+  constexpr int NS = DH / 16, NT = DH / 32;   // k-steps and accumulator tiles over d
+  __shared__ RowTiles<DH> T;
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, ql = l & 31, hh = l >> 5;
   const int npairs = p.B * p.Hkv;
   int pair, rb;
@@ -658,7 +668,7 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
   const float cS = p.scale * kLog2e / (sQ * sK);
 
   const int64_t qoff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * p.D;   // caller rows
-  const int64_t woff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * kD;    // workspace rows
+  const int64_t woff = ((static_cast<int64_t>(b) * p.Tq + (row_ok ? row : 0)) * p.Hq + h) * DH;    // workspace rows
   const int64_t soff = (static_cast<int64_t>(b) * p.Hq + h) * p.Tq + (row_ok ? row : 0);
   float lse2 = row_ok ? p.lse[soff] * kLog2e : 0.f;
   if (!(lse2 > -INFINITY && lse2 < INFINITY)) lse2 = 0.f;  // a row without keys: every S is masked
@@ -677,13 +687,13 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
   const int r_kend = row_ok ? (p.causal ? min(p.Tk, row + off + 1) : p.Tk) : 0;
   const int r_kbeg = p.window > 0 ? max(0, row + off - p.window + 1) : 0;
 
-  f16x8 qB[8], gB[8];
+  f16x8 qB[NS], gB[NS];
   load_row_operand(p.q + qoff, row_ok, hh, sQ, qB, p.D);
   load_row_operand(p.dout + qoff, row_ok, hh, sG, gB, p.D);
   // |G_j| = |g.v_j| <= |g| |v_j| with the largest value norm among the keys the row sees (a running
   // maximum along the sequence), so the scale of p G follows the row instead of the tensors' largest
   // entries (probe form: |G - g.o| <= 2 |g| max |v_j|)
-  const float gnorm = sqrtf(xor32_sum(sumsq8x8(gB))) / sG;
+  const float gnorm = sqrtf(xor32_sum(sumsq(gB))) / sG;
   const int64_t nbase = (static_cast<int64_t>(b) * p.Hkv + g) * p.Tk_pad;
   const float pmV = r_kend > r_kbeg ? p.vnorm[nbase + r_kend - 1] : 0.f;
   const float sPG = range_scale(PROBE ? 2.f * gnorm * pmV : gnorm * pmV);
@@ -692,7 +702,7 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
   float go_pre = 0.f;
   if constexpr (PROBE) {
 #pragma unroll
-    for (int d = 4 * hh; d < kD; d += 8) {
+    for (int d = 4 * hh; d < DH; d += 8) {
       float gv[4] = {0.f, 0.f, 0.f, 0.f};
       float4 ov = {0.f, 0.f, 0.f, 0.f};
       if (row_ok) {
@@ -706,9 +716,9 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
   const float goS = go_pre * sG * sV;   // g.o in the units of the G tile
 
   // ---------------- du = sum_j p_j G_j k_j (scaled) ----------------
-  f32x16 accDU[4];
+  f32x16 accDU[NT];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) accDU[mt] = f32x16{};
+  for (int mt = 0; mt < NT; ++mt) accDU[mt] = f32x16{};
   const float fPG = sPG / (sG * sV);
   if (t_beg < t_end) row_tile_dma8(p, T, 0, b, g, t_beg, w, l);
   lds_dma_wait();
@@ -731,8 +741,8 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
           a[s][1] = lds_rows(T.v[buf], 32 * kb + ql, 2 * s + hh);
         }
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          if (s + 2 < 8) {
+        for (int s = 0; s < NS; ++s) {
+          if (s + 2 < NS) {
             a[(s + 2) % 3][0] = lds_rows(T.k[buf], 32 * kb + ql, 2 * (s + 2) + hh);
             a[(s + 2) % 3][1] = lds_rows(T.v[buf], 32 * kb + ql, 2 * (s + 2) + hh);
           }
@@ -742,9 +752,9 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
           __builtin_amdgcn_sched_barrier(0);
         }
         // the K^T operands of the first du products, read while the weights are formed
-        f16x8 kc[4];
+        f16x8 kc[NT];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) kc[mt] = lds_cols(T.kt[buf], 32 * mt + ql, 4 * kb + hh);
+        for (int mt = 0; mt < NT; ++mt) kc[mt] = lds_cols<DH>(T.kt[buf], 32 * mt + ql, 4 * kb + hh);
         if (!full) {   // tiles on the causal / window edge only
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -760,9 +770,9 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
           f16x8 hi;
           to_operand(pg + 8 * t, 1.f, hi, nullptr);
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt) {
+          for (int mt = 0; mt < NT; ++mt) {
             accDU[mt] = mfma(kc[mt], hi, accDU[mt]);
-            if (t == 0) kc[mt] = lds_cols(T.kt[buf], 32 * mt + ql, 4 * kb + 2 + hh);
+            if (t == 0) kc[mt] = lds_cols<DH>(T.kt[buf], 32 * mt + ql, 4 * kb + 2 + hh);
           }
         }
       }
@@ -774,14 +784,14 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
   // ---------------- epilogue ----------------
   // row vectors in the accumulator layout: element (mt, r) is d = 32 mt + 8 (r/4) + 4 hh + r%4
   float go, gout, gabs;
-  row_dots(p, qoff, row_ok, hh, go, gout, gabs);
+  row_dots<NT>(p, qoff, row_ok, hh, go, gout, gabs);
   if constexpr (PROBE) go = go_pre;   // the value du was formed with
   float alpha = 0.f, dkk = 0.f, umax = 0.f, emax = 0.f, u2 = 0.f, e2 = 0.f;
   if constexpr (PROBE) {
     // u = -rho, dkbar = (g.o) rho, drho = -du, dq starts at 0 (no projector term)
     const float fdu = 1.f / (sPG * sK);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = 32 * mt + 8 * j + 4 * hh;
@@ -816,7 +826,7 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
     {
       const float fdu = 1.f / (sPG * sK);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int d = 32 * mt + 8 * j + 4 * hh;
@@ -847,24 +857,24 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
     dumax = xor32_max(dumax);
     const float sX = range_scale(xmax), sDU = range_scale(dumax);
     // (P du)^T = P16 du^T
-    f32x16 accU[4], accPD[4];
+    f32x16 accU[NT], accPD[NT];
     {
-      f16x8 dB[8];
+      f16x8 dB[NS];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) tile_operand(accDU[s >> 1], s & 1, sDU, dB[s], nullptr);
-      const _Float16* pr = p.p16 + (static_cast<int64_t>(h) * kD + ql) * kD + hh * 8;
+      for (int s = 0; s < NS; ++s) tile_operand(accDU[s >> 1], s & 1, sDU, dB[s], nullptr);
+      const _Float16* pr = p.p16 + (static_cast<int64_t>(h) * DH + ql) * DH + hh * 8;
 #pragma unroll
-      for (int am = 0; am < 4; ++am) {
+      for (int am = 0; am < NT; ++am) {
         accPD[am] = f32x16{};
 #pragma unroll
-        for (int s = 0; s < 8; ++s) accPD[am] = mfma(*reinterpret_cast<const f16x8*>(pr + 32 * am * kD + 16 * s), dB[s], accPD[am]);
+        for (int s = 0; s < NS; ++s) accPD[am] = mfma(*reinterpret_cast<const f16x8*>(pr + 32 * am * DH + 16 * s), dB[s], accPD[am]);
       }
     }
     // U^T = P16t X^T, with x = q - kbar re-read: operand s holds d = 16 s + 8 (e/4) + 4 hh + e%4
     {
-      f16x8 xB[8];
+      f16x8 xB[NS];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
+      for (int s = 0; s < NS; ++s) {
         float x8[8];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -882,19 +892,19 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
         }
         to_operand(x8, sX, xB[s], nullptr);
       }
-      const _Float16* prt = p.p16t + (static_cast<int64_t>(h) * kD + ql) * kD + hh * 8;
+      const _Float16* prt = p.p16t + (static_cast<int64_t>(h) * DH + ql) * DH + hh * 8;
 #pragma unroll
-      for (int am = 0; am < 4; ++am) {
+      for (int am = 0; am < NT; ++am) {
         accU[am] = f32x16{};
 #pragma unroll
-        for (int s = 0; s < 8; ++s) accU[am] = mfma(*reinterpret_cast<const f16x8*>(prt + 32 * am * kD + 16 * s), xB[s], accU[am]);
+        for (int s = 0; s < NS; ++s) accU[am] = mfma(*reinterpret_cast<const f16x8*>(prt + 32 * am * DH + 16 * s), xB[s], accU[am]);
       }
     }
     // u, dq0 = P du (completed by k_bwd_dq), dkbar = -(g.o) u - P du, alpha = u.kbar, Delta = g.out + dkbar.kbar
     {
       const float fu = 1.f / (sX * sP), fpd = 1.f / (sP * sDU);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int d = 32 * mt + 8 * j + 4 * hh;
@@ -1020,13 +1030,13 @@ __device__ __forceinline__ KeyLaneScales key_lane_scales(const KeyParams& p, int
   return r;
 }
 
-// One query tile in LDS: query-row tiles [16 chunks][32 rows][8] (chunk-major, as staged); the
+// One query tile in LDS: query-row tiles [DH/8 chunks][32 rows][8] (chunk-major, as staged); the
 // column-layout operands are read from them with transpose loads (tr_cols).
-template <bool SPLIT>
+template <bool SPLIT, int DH>
 struct __align__(16) KeyTiles {
   static constexpr int NR = SPLIT ? 6 : 4;   // q, dO, u, e (+ u lo, e lo)
   static constexpr int NB = SPLIT ? 1 : 2;
-  _Float16 r[NB][NR][32 * kD];
+  _Float16 r[NB][NR][32 * DH];
   float stat[NB][3][32];                     // lse2, alpha, delta of the tile's rows
 };
 
@@ -1038,20 +1048,20 @@ __device__ __forceinline__ f16x8 kt_rows_swz(const _Float16* t, int r, int c) {
   return *reinterpret_cast<const f16x8*>(&t[c * (kQTile * 8) + row_slot_swz(r, c) * 8]);
 }
 
-// Asynchronous copy of one query tile: per array, the query-row tile is one contiguous 8 KB block
-// (8 wave instructions of 1024 bytes, 2 per wave).
-template <bool SPLIT>
-__device__ __forceinline__ void key_tile_dma(const KeyParams& p, KeyTiles<SPLIT>& T, int buf, int b, int h, int q0,
-                                             int w, int l) {
-  constexpr int NR = KeyTiles<SPLIT>::NR;
+// Asynchronous copy of one query tile: per array, the query-row tile is one contiguous block of DH / 16 KB
+// (DH / 16 wave instructions of 1024 bytes, DH / 64 per wave of four).
+template <bool SPLIT, int DH>
+__device__ __forceinline__ void key_tile_dma(const KeyParams& p, KeyTiles<SPLIT, DH>& T, int buf, int b, int h,
+                                             int q0, int w, int l) {
+  constexpr int NR = KeyTiles<SPLIT, DH>::NR;
   const _Float16* srcr[6] = {p.q16, p.do16, p.u16, p.e16, p.u16lo, p.e16lo};
 #pragma unroll
   for (int a = 0; a < NR; ++a) {
     const int pad = a < 4 ? p.Tq_pad : p.lo_pad;
-    const int64_t tb = q_tile(b, h, q0 / kQTile, p.Hq, pad / kQTile);
+    const int64_t tb = q_tile(b, h, q0 / kQTile, p.Hq, pad / kQTile, DH);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int i = 2 * w + j;
+    for (int j = 0; j < DH / 64; ++j) {
+      const int i = (DH / 64) * w + j;
       lds_dma16(srcr[a] + tb + i * 512 + l * 8, &T.r[buf][a][i * 512]);
     }
   }
@@ -1073,10 +1083,11 @@ __device__ __forceinline__ float key_stat_load(const KeyParams& p, int b, int h,
   return val;
 }
 
-template <bool SPLIT>
+template <bool SPLIT, int DH>
 __global__ __launch_bounds__(256) void k_bwd_keys_fast(KeyParams p) {
-  __shared__ KeyTiles<SPLIT> T;
-  constexpr int NB = KeyTiles<SPLIT>::NB;
+  constexpr int NS = DH / 16, NT = DH / 32;   // k-steps and accumulator tiles over d
+  __shared__ KeyTiles<SPLIT, DH> T;
+  constexpr int NB = KeyTiles<SPLIT, DH>::NB;
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, ql = l & 31, hh = l >> 5;
   const int tro = tr_lane_offset(l);
   const int npairs = p.B * p.Hkv;
@@ -1107,24 +1118,24 @@ __global__ __launch_bounds__(256) void k_bwd_keys_fast(KeyParams p) {
   const float fT = 1.f / (sU * sK), fE = 1.f / (sE * sK), fG = 1.f / (sG * sV);
 
   // this wave's key rows as B operands (d permuted, as staged)
-  f16x8 kB[8], vB[8];
+  f16x8 kB[NS], vB[NS];
   {
     const int kr = key_ok ? key : 0;
-    const int64_t roff = kv_tile(b, g, kr / kKeyTile, p.Hkv, p.Tk_pad / kKeyTile) + (kr % kKeyTile) * 8 +
+    const int64_t roff = kv_tile(b, g, kr / kKeyTile, p.Hkv, p.Tk_pad / kKeyTile, DH) + (kr % kKeyTile) * 8 +
                          hh * (kKeyTile * 8);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < NS; ++s) {
       kB[s] = *reinterpret_cast<const f16x8*>(p.k16 + roff + s * (2 * kKeyTile * 8));
       vB[s] = *reinterpret_cast<const f16x8*>(p.v16 + roff + s * (2 * kKeyTile * 8));
     }
   }
-  const KeyLaneScales ls = key_lane_scales(p, b, g, key, key_ok, sqrtf(xor32_sum(sumsq8x8(kB))) / sK,
-                                           sqrtf(xor32_sum(sumsq8x8(vB))) / sV, sU, sE, sQ);
+  const KeyLaneScales ls = key_lane_scales(p, b, g, key, key_ok, sqrtf(xor32_sum(sumsq(kB))) / sK,
+                                           sqrtf(xor32_sum(sumsq(vB))) / sV, sU, sE, sQ);
   const float C = ls.C, cV = ls.cV;
   const float c1 = C / sU, c2 = C / sE, c3 = p.scale * C / sQ;
-  f32x16 accK[4], accV[4];
+  f32x16 accK[NT], accV[NT];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < NT; ++mt) {
     accK[mt] = f32x16{};
     accV[mt] = f32x16{};
   }
@@ -1139,7 +1150,7 @@ __global__ __launch_bounds__(256) void k_bwd_keys_fast(KeyParams p) {
   const int row_lo_c = p.row_lo, row_hi_c = min(p.row_hi, p.Tq);
   const bool nocausal = !p.causal, nowindow = p.window <= 0;
   if (total > 0) {
-    key_tile_dma<SPLIT>(p, T, 0, b, g * p.G, qt0 * 32, w, l);
+    key_tile_dma<SPLIT, DH>(p, T, 0, b, g * p.G, qt0 * 32, w, l);
     const float sv = key_stat_load(p, b, g * p.G, qt0 * 32, tid);
     if (tid < 96) T.stat[0][tid >> 5][tid & 31] = sv;
   }
@@ -1154,7 +1165,7 @@ __global__ __launch_bounds__(256) void k_bwd_keys_fast(KeyParams p) {
     const bool pre = NB == 2 && it + 1 < total;
     if (pre) {
       const int nit = it + 1, nh = g * p.G + nit / n_qt, nq0 = (qt0 + nit % n_qt) * 32;
-      key_tile_dma<SPLIT>(p, T, buf ^ 1, b, nh, nq0, w, l);
+      key_tile_dma<SPLIT, DH>(p, T, buf ^ 1, b, nh, nq0, w, l);
       next_stat = key_stat_load(p, b, nh, nq0, tid);
     }
     // wave-uniform skip: no visible pair between these 32 rows and this wave's keys
@@ -1166,7 +1177,7 @@ __global__ __launch_bounds__(256) void k_bwd_keys_fast(KeyParams p) {
                         q0 + 32 <= min(p.row_hi, p.Tq);
       f32x16 S = {}, Tt = {}, E = {}, Gt = {};
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
+      for (int s = 0; s < NS; ++s) {
         S = mfma(kt_rows(T.r[buf][0], ql, 2 * s + hh), kB[s], S);
         Gt = mfma(kt_rows(T.r[buf][1], ql, 2 * s + hh), vB[s], Gt);
         Tt = mfma(kt_rows(T.r[buf][2], ql, 2 * s + hh), kB[s], Tt);
@@ -1215,7 +1226,7 @@ __global__ __launch_bounds__(256) void k_bwd_keys_fast(KeyParams p) {
         to_operand(wp, 1.f, ph, SPLIT ? &pl : nullptr);
         to_operand(wd, 1.f, dh, SPLIT ? &dlo : nullptr);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
+        for (int mt = 0; mt < NT; ++mt) {
           const f16x8 ag = tr_cols(T.r[buf][1], tro, mt, t), aq = tr_cols(T.r[buf][0], tro, mt, t);
           const f16x8 au = tr_cols(T.r[buf][2], tro, mt, t), ae = tr_cols(T.r[buf][3], tro, mt, t);
           accV[mt] = mfma(ag, vh, accV[mt]);
@@ -1239,7 +1250,7 @@ __global__ __launch_bounds__(256) void k_bwd_keys_fast(KeyParams p) {
       // single buffer: wait until every wave is done with the tile, then copy the next one
       __syncthreads();
       const int nit = it + 1, nh = g * p.G + nit / n_qt, nq0 = (qt0 + nit % n_qt) * 32;
-      key_tile_dma<SPLIT>(p, T, 0, b, nh, nq0, w, l);
+      key_tile_dma<SPLIT, DH>(p, T, 0, b, nh, nq0, w, l);
       const float sv = key_stat_load(p, b, nh, nq0, tid);
       if (tid < 96) T.stat[0][tid >> 5][tid & 31] = sv;
     }
@@ -1251,11 +1262,10 @@ __global__ __launch_bounds__(256) void k_bwd_keys_fast(KeyParams p) {
     float* dkr = p.dk + ((static_cast<int64_t>(b) * p.Tk + key) * p.Hkv + g) * p.D;
     float* dvr = p.dv + ((static_cast<int64_t>(b) * p.Tk + key) * p.Hkv + g) * p.D;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = 32 * mt + 8 * j + 4 * hh, r = 4 * j;
-        if (d >= p.D) continue;   // padding dims of a D < 128 head
         float4 kv = {accK[mt][r] * fk, accK[mt][r + 1] * fk, accK[mt][r + 2] * fk, accK[mt][r + 3] * fk};
         float4 vv = {accV[mt][r] * fv, accV[mt][r + 1] * fv, accV[mt][r + 2] * fv, accV[mt][r + 3] * fv};
         if (p.accumulate) {
@@ -1323,26 +1333,28 @@ __device__ __forceinline__ bool tile_pair_any(int jw, int q0, int Tk, int off, i
          q0 + 31 >= row_lo && q0 < row_hi;
 }
 
+template <int DH>
 struct __align__(16) KeyTiles3 {
-  _Float16 r[3][4][32 * kD];   // q, dO, u, e query-row tiles, three buffers
+  _Float16 r[3][4][32 * DH];   // q, dO, u, e query-row tiles, three buffers
   f16x8 x[4][4][2][64];        // exchange: per key group p G c1, p c2, ds c3, p tt cV
   float stat[3][3][32];        // lse (log2 units), 1 - alpha, Delta of the tile's rows
   float ksc[4][2][32];         // per key group: its C (entry 0) and each key's cV (set by the V waves)
 };
-static_assert(sizeof(KeyTiles3) <= 160 * 1024, "LDS");
+static_assert(sizeof(KeyTiles3<kD>) <= 160 * 1024, "LDS");
 
-// One query tile into LDS buffer `buf`: 32 KB (4 arrays of 8 KB, consecutive in the workspace), one
-// quarter array per wave (4 instructions), and the tile's 96 row statistics (wave 0, lanes 0-23).
+// One query tile into LDS buffer `buf`: 4 arrays of DH / 16 KB (consecutive in the workspace), half an
+// array per wave (DH / 32 instructions), and the tile's 96 row statistics (wave 0, lanes 0-23).
 // The rows of each chunk land swizzled (row_slot_swz): lane l of an instruction fills row slot l % 32
 // of chunk 2 i + l / 32 and so fetches the row that belongs there.
-__device__ __forceinline__ void key_tile_dma3(const KeyParams& p, KeyTiles3& T, int buf, int b, int h, int q0,
+template <int DH>
+__device__ __forceinline__ void key_tile_dma3(const KeyParams& p, KeyTiles3<DH>& T, int buf, int b, int h, int q0,
                                               int w, int l) {
-  const int64_t tb = q_tile(b, h, q0 / kQTile, p.Hq, p.Tq_pad / kQTile);
+  const int64_t tb = q_tile(b, h, q0 / kQTile, p.Hq, p.Tq_pad / kQTile, DH);
   const int a = w >> 1;
   const _Float16* src = p.q16 + a * p.qstride + tb;   // q, dO, u, e rows
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = 4 * (w & 1) + j, ch = 2 * i + (l >> 5);
+  for (int j = 0; j < DH / 32; ++j) {
+    const int i = (DH / 32) * (w & 1) + j, ch = 2 * i + (l >> 5);
     lds_dma16(src + ch * 256 + row_slot_swz(l & 31, ch) * 8, &T.r[buf][a][i * 512]);
   }
   if (w == 0 && l < 24) {
@@ -1351,8 +1363,10 @@ __device__ __forceinline__ void key_tile_dma3(const KeyParams& p, KeyTiles3& T, 
   }
 }
 
+template <int DH>
 __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
-  __shared__ KeyTiles3 T;
+  constexpr int NS = DH / 16, NT = DH / 32;   // k-steps and accumulator tiles over d
+  __shared__ KeyTiles3<DH> T;
   __shared__ int wave_simd[8];
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, ql = l & 31, hh = l >> 5;
   // Roles follow the SIMDs: the two waves a SIMD holds become the V and the K wave of one key group,
@@ -1415,22 +1429,22 @@ __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
   __syncthreads();
 
   const int kr = key_ok ? key : 0;
-  const int64_t roff = kv_tile(b, g, kr / kKeyTile, p.Hkv, p.Tk_pad / kKeyTile) + (kr % kKeyTile) * 8 +
+  const int64_t roff = kv_tile(b, g, kr / kKeyTile, p.Hkv, p.Tk_pad / kKeyTile, DH) + (kr % kKeyTile) * 8 +
                        hh * (kKeyTile * 8);
   const int2 tro = tr_lane_offsets_swz(l);
 
   if (is_v) {
     // ---------------- V waves: S, T, E, G and the weights of tile it ----------------
-    f16x8 kB[8], vB[8];
+    f16x8 kB[NS], vB[NS];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < NS; ++s) {
       kB[s] = *reinterpret_cast<const f16x8*>(p.k16 + roff + s * (2 * kKeyTile * 8));
       vB[s] = *reinterpret_cast<const f16x8*>(p.v16 + roff + s * (2 * kKeyTile * 8));
     }
     // The dk products of the group's 32 keys share one scale, the smallest C among its keys that some
     // row sees (the stored ds tiles then hold one scale per group); dv takes each key's own cV.
-    const KeyLaneScales kls = key_lane_scales(p, b, g, key, key_ok, sqrtf(xor32_sum(sumsq8x8(kB))) / ks.sK,
-                                              sqrtf(xor32_sum(sumsq8x8(vB))) / ks.sV, ks.sU, ks.sE, ks.sQ);
+    const KeyLaneScales kls = key_lane_scales(p, b, g, key, key_ok, sqrtf(xor32_sum(sumsq(kB))) / ks.sK,
+                                              sqrtf(xor32_sum(sumsq(vB))) / ks.sV, ks.sU, ks.sE, ks.sQ);
     float cgrp = kls.seen ? kls.C : INFINITY;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) cgrp = fminf(cgrp, __shfl_xor(cgrp, o, 64));
@@ -1456,12 +1470,12 @@ __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
 #pragma unroll
           for (int o = 0; o < 4; ++o) a[s][o] = kt_rows_swz(T.r[buf][o], ql, 2 * s + hh);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          if (s + 2 < 8) {
+        for (int s = 0; s < NS; ++s) {
+          if (s + 2 < NS) {
 #pragma unroll
             for (int o = 0; o < 4; ++o) a[(s + 2) % 3][o] = kt_rows_swz(T.r[buf][o], ql, 2 * (s + 2) + hh);
           }
-          if (s == 6) {   // the statistics are read while the last MFMAs run
+          if (s == NS - 2) {   // the statistics are read while the last MFMAs run
 #pragma unroll
             for (int k = 0; k < 3; ++k)
 #pragma unroll
@@ -1541,9 +1555,9 @@ __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         pi[t][e] = static_cast<_Float16>(ql == 16 * t + perm16(8 * hh + e) ? 1.f : 0.f);
-    f32x16 accK[4], accV[4];
+    f32x16 accK[NT], accV[NT];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) accK[mt] = accV[mt] = f32x16{};
+    for (int mt = 0; mt < NT; ++mt) accK[mt] = accV[mt] = f32x16{};
     for (int it = 0; it <= total; ++it) {
       const int pbuf = (it + 2) % 3;
       if (it + 1 < total) key_tile_dma3(p, T, (it + 1) % 3, b, tile_head(it + 1), tile_row(it + 1), w, l);
@@ -1560,11 +1574,11 @@ __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
       lds_barrier();
       if (has) {
         f32x16 DT = {};
-        // step n = (t, mt) = (n / 4, n % 4) multiplies the column operands (u, e, q, dO) of d tile mt
+        // step n = (t, mt) = (n / NT, n % NT) multiplies the column operands (u, e, q, dO) of d tile mt
         // and query half t; the operands of step n + 2 are read while step n runs
         f16x8 c[3][4];
         auto load_cols = [&](int n, f16x8(&dst)[4]) {
-          const int t = n >> 2, mt = n & 3;
+          const int t = n / NT, mt = n % NT;
           dst[0] = tr_cols_swz(T.r[pbuf][2], tro, mt, t);
           dst[1] = tr_cols_swz(T.r[pbuf][3], tro, mt, t);
           dst[2] = tr_cols_swz(T.r[pbuf][0], tro, mt, t);
@@ -1573,15 +1587,15 @@ __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
         load_cols(0, c[0]);
         load_cols(1, c[1]);
 #pragma unroll
-        for (int n = 0; n < 8; ++n) {
-          const int t = n >> 2, mt = n & 3;
-          if (n + 2 < 8) load_cols(n + 2, c[(n + 2) % 3]);
+        for (int n = 0; n < 2 * NT; ++n) {
+          const int t = n / NT, mt = n % NT;
+          if (n + 2 < 2 * NT) load_cols(n + 2, c[(n + 2) % 3]);
           __builtin_amdgcn_sched_barrier(0);
           accK[mt] = mfma(c[n % 3][0], xk[t], accK[mt]);
           accV[mt] = mfma(c[n % 3][3], xv[t], accV[mt]);
           accK[mt] = mfma(c[n % 3][1], xp[t], accK[mt]);
           accK[mt] = mfma(c[n % 3][2], xd[t], accK[mt]);
-          if (mt == 3) DT = mfma(xd[t], pi[t], DT);
+          if (mt == NT - 1) DT = mfma(xd[t], pi[t], DT);
           __builtin_amdgcn_sched_barrier(0);
         }
         // DT: lane = query row of the tile, register r = key 8 (r / 4) + 4 hh + r % 4 of the wave's 32
@@ -1603,11 +1617,10 @@ __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
       const float fv = 1.f / (ks.sG * T.ksc[grp][1][ql]);
       float* dvr = p.dv + ((static_cast<int64_t>(b) * p.Tk + key) * p.Hkv + g) * p.D;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int d = 32 * mt + 8 * j + 4 * hh, r = 4 * j;
-          if (d >= p.D) continue;   // padding dims of a D < 128 head
           float4 vv = {accV[mt][r] * fv, accV[mt][r + 1] * fv, accV[mt][r + 2] * fv, accV[mt][r + 3] * fv};
           if (p.accumulate) {
             const float4 v0 = *reinterpret_cast<const float4*>(dvr + d);
@@ -1618,11 +1631,10 @@ __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
       const float fk = 1.f / T.ksc[grp][0][0];
       float* dkr = p.dk + ((static_cast<int64_t>(b) * p.Tk + key) * p.Hkv + g) * p.D;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int d = 32 * mt + 8 * j + 4 * hh, r = 4 * j;
-          if (d >= p.D) continue;   // padding dims of a D < 128 head
           float4 kv = {accK[mt][r] * fk, accK[mt][r + 1] * fk, accK[mt][r + 2] * fk, accK[mt][r + 3] * fk};
           if (p.accumulate) {
             const float4 k0 = *reinterpret_cast<const float4*>(dkr + d);
@@ -1649,12 +1661,15 @@ struct DqParams {
   float scale;
 };
 
+template <int DH>
 struct __align__(16) DqTiles {
-  _Float16 kt[2][kKeyTile * kD];
+  _Float16 kt[2][kKeyTile * DH];
 };
 
+template <int DH>
 __global__ __launch_bounds__(512) void k_bwd_dq(DqParams p) {
-  __shared__ DqTiles T;
+  constexpr int NT = DH / 32;   // accumulator tiles over d
+  __shared__ DqTiles<DH> T;
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, ql = l & 31, hh = l >> 5;
   int pair, rb;
   {
@@ -1699,10 +1714,10 @@ __global__ __launch_bounds__(512) void k_bwd_dq(DqParams p) {
     }
   };
   auto dma_k = [&](int kt, int buf) {
-    const int64_t tb = kv_tile(b, g, kt, p.Hkv, p.Tk_pad / kKeyTile);
+    const int64_t tb = kv_tile(b, g, kt, p.Hkv, p.Tk_pad / kKeyTile, DH);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int i = 2 * w + j;
+    for (int j = 0; j < DH / 64; ++j) {
+      const int i = (DH / 64) * w + j;
       lds_dma16(p.k16t + tb + i * 512 + l * 8, &T.kt[buf][i * 512]);
     }
   };
@@ -1721,9 +1736,9 @@ __global__ __launch_bounds__(512) void k_bwd_dq(DqParams p) {
 #pragma unroll
     for (int kbh = 0; kbh < 2; ++kbh) f[kbh] = cdq / gsc[2 * kt + kbh];
   };
-  f32x16 acc[4];
+  f32x16 acc[NT];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x16{};
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x16{};
   f16x8 dcur[4], dnxt[4];
   if (t_beg < t_end) {
     dma_k(t_beg, 0);
@@ -1745,9 +1760,9 @@ __global__ __launch_bounds__(512) void k_bwd_dq(DqParams p) {
         const _Float16 f = static_cast<_Float16>(fcur[kbh]);
         const f16x8 d0 = dcur[2 * kbh] * f, d1 = dcur[2 * kbh + 1] * f;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          acc[nt] = mfma(lds_cols(T.kt[buf], 32 * nt + ql, 4 * kbh + hh), d0, acc[nt]);
-          acc[nt] = mfma(lds_cols(T.kt[buf], 32 * nt + ql, 4 * kbh + 2 + hh), d1, acc[nt]);
+        for (int nt = 0; nt < NT; ++nt) {
+          acc[nt] = mfma(lds_cols<DH>(T.kt[buf], 32 * nt + ql, 4 * kbh + hh), d0, acc[nt]);
+          acc[nt] = mfma(lds_cols<DH>(T.kt[buf], 32 * nt + ql, 4 * kbh + 2 + hh), d1, acc[nt]);
         }
       }
     }
@@ -1763,11 +1778,10 @@ __global__ __launch_bounds__(512) void k_bwd_dq(DqParams p) {
     const float fq = ks.sQ / (cdq * ks.sK);
     float* dqr = p.dq + ((static_cast<int64_t>(b) * p.Tq + row) * p.Hq + h) * p.D;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = 32 * nt + 8 * j + 4 * hh, r = 4 * j;
-        if (d >= p.D) continue;   // padding dims of a D < 128 head
         const float4 q = *reinterpret_cast<const float4*>(dqr + d);
         *reinterpret_cast<float4*>(dqr + d) = float4{q.x + acc[nt][r] * fq, q.y + acc[nt][r + 1] * fq,
                                                      q.z + acc[nt][r + 2] * fq, q.w + acc[nt][r + 3] * fq};
@@ -1889,8 +1903,48 @@ __global__ __launch_bounds__(256) void k_dp_partial(const float* x32, const floa
         float4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
 }
 
-__global__ __launch_bounds__(256) void k_dp_reduce(const float* part, float* dP, int nchunks, int Hq, int D) {
-  const int64_t n = static_cast<int64_t>(Hq) * kD * kD;
+// The same partial sums for head dim 64: wave w owns the 32 x 32 tile of result rows 32 (w % 2) and columns
+// 32 (w / 2); lane (ql, hh) takes rows 8 hh .. 8 hh + 7 of a 16-row step, x at the tile's column ql of x and
+// du at its column ql of du.
+__global__ __launch_bounds__(256) void k_dp_partial64(const float* x32, const float* du32, float* part, int R,
+                                                      int Hq) {
+  constexpr int DH = 64;
+  const int h = blockIdx.x % Hq, c = blockIdx.x / Hq;
+  const int w = wave_id(), l = threadIdx.x & 63, ql = l & 31, hh = l >> 5;
+  const int ra = 32 * (w & 1), cb = 32 * (w >> 1);
+  f32x16 acc = f32x16{};
+  const int r_beg = c * kPChunk, r_end = min(R, r_beg + kPChunk);
+  const int64_t rs = static_cast<int64_t>(Hq) * DH;
+  const float* xp = x32 + h * DH + ra + ql;
+  const float* dp = du32 + h * DH + cb + ql;
+  for (int r0 = r_beg; r0 < r_end; r0 += 16) {
+    float xa[8], da[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int r = r0 + 8 * hh + e;
+      const bool ok = r < r_end;
+      const int64_t o = static_cast<int64_t>(ok ? r : r_beg) * rs;
+      const float xv = xp[o], dv = dp[o];
+      xa[e] = ok ? xv : 0.f;
+      da[e] = ok ? dv : 0.f;
+    }
+    bf16x8 xh, xl, dh, dl;
+    split_bf16(xa, xh, xl);
+    split_bf16(da, dh, dl);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xh, dh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xh, dl, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xl, dh, acc, 0, 0, 0);
+  }
+  // register r: result row ra + 8 (r / 4) + 4 hh + r % 4, column cb + ql
+  float* dst = part + (static_cast<int64_t>(c) * Hq + h) * DH * DH + cb + ql;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dst[(ra + 8 * (r >> 2) + 4 * hh + (r & 3)) * DH] = acc[r];
+}
+
+// dP[h] = the sum of the partials in chunk order; the partials are dh x dh per head (a D < dh projector takes
+// their D x D corner).
+__global__ __launch_bounds__(256) void k_dp_reduce(const float* part, float* dP, int nchunks, int Hq, int D, int dh) {
+  const int64_t n = static_cast<int64_t>(Hq) * dh * dh;
   for (int64_t e = blockIdx.x * 256LL + threadIdx.x; e < n; e += 256LL * gridDim.x) {
     // in chunk order; eight loads are issued before their adds
     float s = 0.f;
@@ -1903,9 +1957,8 @@ __global__ __launch_bounds__(256) void k_dp_reduce(const float* part, float* dP,
       for (int u = 0; u < 8; ++u) s += v[u];
     }
     for (; c < nchunks; ++c) s += part[c * n + e];
-    // the partials are 128 x 128 per head; a D < 128 projector takes its D x D corner
-    const int64_t hh = e / (kD * kD);
-    const int a = static_cast<int>((e / kD) % kD), c2 = static_cast<int>(e % kD);
+    const int64_t hh = e / (dh * dh);
+    const int a = static_cast<int>((e / dh) % dh), c2 = static_cast<int>(e % dh);
     if (a < D && c2 < D) dP[(hh * D + a) * D + c2] = s;
   }
 }
@@ -1930,15 +1983,16 @@ struct BwdWs {
 
 BwdWs bwd_layout(const Geom& g, int split, void* ws) {
   BwdWs w{};
-  w.st = staging_layout(ws, g.B, g.Tk, g.Hkv, g.Hq, true);
+  const int dh = g.d == 64 ? 64 : kD;   // a head of 64 is staged and computed at 64
+  w.st = staging_layout(ws, g.B, g.Tk, g.Hkv, g.Hq, true, dh);
   size_t off = w.st.bytes;
   char* base = static_cast<char*>(ws);
   w.Tq_pad = (g.Tq + 31) / 32 * 32;
   w.lo_rows = split;
   w.lo_pad = (split + 31) / 32 * 32;
-  const size_t qh = static_cast<size_t>(g.B) * g.Hq * w.Tq_pad * kD * sizeof(_Float16);
-  const size_t lh = static_cast<size_t>(g.B) * g.Hq * w.lo_pad * kD * sizeof(_Float16);
-  const size_t rf = static_cast<size_t>(g.B) * g.Tq * g.Hq * kD * sizeof(float);
+  const size_t qh = static_cast<size_t>(g.B) * g.Hq * w.Tq_pad * dh * sizeof(_Float16);
+  const size_t lh = static_cast<size_t>(g.B) * g.Hq * w.lo_pad * dh * sizeof(_Float16);
+  const size_t rf = static_cast<size_t>(g.B) * g.Tq * g.Hq * dh * sizeof(float);
   const size_t sf = static_cast<size_t>(g.B) * g.Hq * g.Tq * sizeof(float);
   _Float16** h16[4] = {&w.q16, &w.do16, &w.u16, &w.e16};
   for (auto pp : h16) *pp = reinterpret_cast<_Float16*>(base + ws_take(off, qh));   // equal, consecutive blocks
@@ -1950,7 +2004,7 @@ BwdWs bwd_layout(const Geom& g, int split, void* ws) {
   w.delta = reinterpret_cast<float*>(base + ws_take(off, sf));
   const int64_t R = static_cast<int64_t>(g.B) * g.Tq;
   w.nchunks = static_cast<int>((R + kPChunk - 1) / kPChunk);
-  w.part = reinterpret_cast<float*>(base + ws_take(off, static_cast<size_t>(w.nchunks) * g.Hq * kD * kD * 4));
+  w.part = reinterpret_cast<float*>(base + ws_take(off, static_cast<size_t>(w.nchunks) * g.Hq * dh * dh * 4));
   const size_t ds_bytes = static_cast<size_t>(g.B) * g.Hq * (w.Tq_pad / 32) * (w.st.Tk_pad / 32) * 1024 * 2;
   w.ds = reinterpret_cast<_Float16*>(base + ws_take(off, ds_bytes));
   w.rstat_n = static_cast<size_t>(g.B) * g.Hq * w.Tq_pad * 3;
@@ -2004,6 +2058,7 @@ hipError_t bwd_impl(const Geom& g, const BwdArgs& a, int split_rows, void* ws, h
   if (split > bwd_split(g)) split = bwd_split(g);
   const BwdWs w = bwd_layout(g, bwd_split(g), ws);
   const int G = g.Hq / g.Hkv;
+  const bool d64 = w.st.dh == 64;   // the kernels instantiated for head dim 64
   const int64_t q_elems = static_cast<int64_t>(g.B) * g.Tq * g.Hq * g.d;
   hipError_t e = launch_staging(w.st, q, q_elems, k, v, P, g.B, g.Tk, g.Hkv, g.Hq, stream, dout, q_elems, kMaxDO, g.d);
   if (e != hipSuccess) return e;
@@ -2060,22 +2115,24 @@ hipError_t bwd_impl(const Geom& g, const BwdArgs& a, int split_rows, void* ws, h
   const bool use_side = split > 0 && split < g.Tq;
   SideLane side = use_side ? side_fork(stream) : SideLane{stream, stream};
   e = launch_stage_rows(q, false, w.st.maxbits, kMaxQ, w.q16, nullptr, g.B, g.Tq, w.Tq_pad, g.Hq, 0, 0, side.stream,
-                        g.d);
+                        g.d, w.st.dh);
   if (e != hipSuccess) return e;
   e = launch_stage_rows(dout, false, w.st.maxbits, kMaxDO, w.do16, nullptr, g.B, g.Tq, w.Tq_pad, g.Hq, 0, 0,
-                        side.stream, g.d);
+                        side.stream, g.d, w.st.dh);
   if (e != hipSuccess) return e;
   if (split > 0) {
     RowParams r = rp;
     r.row_begin = 0;
     r.row_end = split;
     r.n_rb = (split + r.rows_per_block - 1) / r.rows_per_block;
-    if (probe)
-      hipLaunchKernelGGL((k_bwd_rows_fast<true, true, true>), dim3(g.B * g.Hkv * hsplit * r.n_rb), dim3(256), 0,
-                         side.stream, r);
-    else
-      hipLaunchKernelGGL((k_bwd_rows_fast<true, true, false>), dim3(g.B * g.Hkv * hsplit * r.n_rb), dim3(256), 0,
-                         side.stream, r);
+    const dim3 grid(g.B * g.Hkv * hsplit * r.n_rb);
+    if (probe) {
+      if (d64) hipLaunchKernelGGL((k_bwd_rows_fast<true, true, true, 64>), grid, dim3(256), 0, side.stream, r);
+      else hipLaunchKernelGGL((k_bwd_rows_fast<true, true, true, kD>), grid, dim3(256), 0, side.stream, r);
+    } else {
+      if (d64) hipLaunchKernelGGL((k_bwd_rows_fast<true, true, false, 64>), grid, dim3(256), 0, side.stream, r);
+      else hipLaunchKernelGGL((k_bwd_rows_fast<true, true, false, kD>), grid, dim3(256), 0, side.stream, r);
+    }
   }
   if (split < g.Tq) {
     RowParams r = rp;
@@ -2085,10 +2142,14 @@ hipError_t bwd_impl(const Geom& g, const BwdArgs& a, int split_rows, void* ws, h
     r.rows_per_block = 32 * 8 / G;
     r.n_rb = (g.Tq - split + r.rows_per_block - 1) / r.rows_per_block;
     mark_begin(PLX_KERNEL_BWD_ROWS, stream);
-    if (probe)
-      hipLaunchKernelGGL(k_bwd_du<true>, dim3(g.B * g.Hkv * r.n_rb), dim3(512), 0, stream, r);
-    else
-      hipLaunchKernelGGL(k_bwd_du<false>, dim3(g.B * g.Hkv * r.n_rb), dim3(512), 0, stream, r);
+    const dim3 grid(g.B * g.Hkv * r.n_rb);
+    if (probe) {
+      if (d64) hipLaunchKernelGGL((k_bwd_du<true, 64>), grid, dim3(512), 0, stream, r);
+      else hipLaunchKernelGGL((k_bwd_du<true, kD>), grid, dim3(512), 0, stream, r);
+    } else {
+      if (d64) hipLaunchKernelGGL((k_bwd_du<false, 64>), grid, dim3(512), 0, stream, r);
+      else hipLaunchKernelGGL((k_bwd_du<false, kD>), grid, dim3(512), 0, stream, r);
+    }
     mark_end(PLX_KERNEL_BWD_ROWS, stream);
   }
   e = hipGetLastError();
@@ -2100,10 +2161,10 @@ hipError_t bwd_impl(const Geom& g, const BwdArgs& a, int split_rows, void* ws, h
   if (e != hipSuccess) return e;
   // fp16 copies of u and dkbar (lo parts for rows < split)
   e = launch_stage_rows(w.u32, true, w.st.maxbits, kMaxU, w.u16, split > 0 ? w.u16lo : nullptr, g.B, g.Tq, w.Tq_pad,
-                        g.Hq, split, w.lo_pad, stream);
+                        g.Hq, split, w.lo_pad, stream, w.st.dh, w.st.dh);
   if (e != hipSuccess) return e;
   e = launch_stage_rows(w.dkb32, true, w.st.maxbits, kMaxDKB, w.e16, split > 0 ? w.e16lo : nullptr, g.B, g.Tq,
-                        w.Tq_pad, g.Hq, split, w.lo_pad, stream);
+                        w.Tq_pad, g.Hq, split, w.lo_pad, stream, w.st.dh, w.st.dh);
   if (e != hipSuccess) return e;
 
   KeyParams kp{};
@@ -2148,7 +2209,8 @@ hipError_t bwd_impl(const Geom& g, const BwdArgs& a, int split_rows, void* ws, h
     k2.accumulate = 0;
     k2.ds = w.ds;
     mark_begin(PLX_KERNEL_BWD_KEYS, stream);
-    hipLaunchKernelGGL(k_bwd_keys_pipe, dim3(g.B * g.Hkv * k2.n_kb), dim3(512), 0, stream, k2);
+    if (d64) hipLaunchKernelGGL(k_bwd_keys_pipe<64>, dim3(g.B * g.Hkv * k2.n_kb), dim3(512), 0, stream, k2);
+    else hipLaunchKernelGGL(k_bwd_keys_pipe<kD>, dim3(g.B * g.Hkv * k2.n_kb), dim3(512), 0, stream, k2);
     mark_end(PLX_KERNEL_BWD_KEYS, stream);
   }
   // the key kernel for rows < split adds onto dk, dv: the side lane waits for the key-major kernel
@@ -2165,7 +2227,8 @@ hipError_t bwd_impl(const Geom& g, const BwdArgs& a, int split_rows, void* ws, h
       k2.accumulate = 1;
       k2.key_hi = khi;
       k2.n_kb = (khi + 127) / 128;
-      hipLaunchKernelGGL(k_bwd_keys_fast<true>, dim3(g.B * g.Hkv * k2.n_kb), dim3(256), 0, side.stream, k2);
+      if (d64) hipLaunchKernelGGL((k_bwd_keys_fast<true, 64>), dim3(g.B * g.Hkv * k2.n_kb), dim3(256), 0, side.stream, k2);
+      else hipLaunchKernelGGL((k_bwd_keys_fast<true, kD>), dim3(g.B * g.Hkv * k2.n_kb), dim3(256), 0, side.stream, k2);
     }
   }
   e = hipGetLastError();
@@ -2195,15 +2258,19 @@ hipError_t bwd_impl(const Geom& g, const BwdArgs& a, int split_rows, void* ws, h
     dp.n_rb = (g.Tq - dp.row_begin + dp.rows_per_block - 1) / dp.rows_per_block;
     dp.scale = g.scale;
     mark_begin(PLX_KERNEL_BWD_DQ, stream);
-    hipLaunchKernelGGL(k_bwd_dq, dim3(g.B * g.Hkv * dp.n_rb), dim3(512), 0, stream, dp);
+    if (d64) hipLaunchKernelGGL(k_bwd_dq<64>, dim3(g.B * g.Hkv * dp.n_rb), dim3(512), 0, stream, dp);
+    else hipLaunchKernelGGL(k_bwd_dq<kD>, dim3(g.B * g.Hkv * dp.n_rb), dim3(512), 0, stream, dp);
     mark_end(PLX_KERNEL_BWD_DQ, stream);
   }
   if (!probe) {
     // dP = sum over rows of x du^T
     const int R = g.B * g.Tq;
-    hipLaunchKernelGGL(k_dp_partial, dim3(g.Hq * w.nchunks), dim3(256), 0, stream, w.x32, w.du32, w.part, R, g.Hq);
-    const int nred = (g.Hq * kD * kD + 255) / 256;
-    hipLaunchKernelGGL(k_dp_reduce, dim3(nred), dim3(256), 0, stream, w.part, dP, w.nchunks, g.Hq, g.d);
+    if (d64)
+      hipLaunchKernelGGL(k_dp_partial64, dim3(g.Hq * w.nchunks), dim3(256), 0, stream, w.x32, w.du32, w.part, R, g.Hq);
+    else
+      hipLaunchKernelGGL(k_dp_partial, dim3(g.Hq * w.nchunks), dim3(256), 0, stream, w.x32, w.du32, w.part, R, g.Hq);
+    const int nred = (g.Hq * w.st.dh * w.st.dh + 255) / 256;
+    hipLaunchKernelGGL(k_dp_reduce, dim3(nred), dim3(256), 0, stream, w.part, dP, w.nchunks, g.Hq, g.d, w.st.dh);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;

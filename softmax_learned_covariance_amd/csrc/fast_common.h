@@ -9,14 +9,14 @@
 // chunk index, so, for a staged head dim DH (128, or 64 in the forwards' native layout)
 //   key rows    [DH/8 chunks][64 keys][8] (K16, V16: d permuted within groups of 16)
 //   key columns [8 chunks][DH d][8]       (K16t, V16t: keys permuted within groups of 16)
-//   query rows  [16 chunks][32 rows][8]   and query columns [4 chunks][128 d][8]   (backward: DH = 128)
+//   query rows  [DH/8 chunks][32 rows][8]
 // with tiles ordered [batch][head][tile].  Copying a tile to LDS is then one
 // contiguous DMA, and an MFMA operand read (32 lanes reading the same chunk of
 // 32 consecutive rows) is a contiguous 512-byte LDS access: no bank conflicts,
 // and the chunk index becomes an immediate offset.
 //   P16t  [Hq][DH][DH]           P16t[h][a][b'] = P[h][b][a], b permuted within groups of 16
 //   P16   [Hq][DH][DH]           P16[h][b][a'] = P[h][b][a], a permuted within groups of 16
-// The backward stages a head of 64 zero-padded to DH = 128; the forwards stage it at DH = 64.
+// A head of 64 is staged at DH = 64 (the kernels are instantiated for both head dims).
 // The permutation of a group of 16 is the involution
 //   position 8*hh + e  <->  element 8*(e/4) + 4*hh + (e%4)      (hh in {0,1}, e in 0..7)
 // which is exactly the order in which a 32x32 accumulator tile holds its rows
@@ -49,9 +49,9 @@ constexpr int kQTile = 32;     // query rows per tile of the key-major backward
 __host__ __device__ inline int64_t kv_tile(int b, int g, int kt, int Hkv, int ntiles, int dh = kD) {
   return ((static_cast<int64_t>(b) * Hkv + g) * ntiles + kt) * (kKeyTile * dh);
 }
-// First element of query tile qt of (batch b, query head h) in the query-side copies.
-__host__ __device__ inline int64_t q_tile(int b, int h, int qt, int Hq, int nqt) {
-  return ((static_cast<int64_t>(b) * Hq + h) * nqt + qt) * (kQTile * kD);
+// First element of query tile qt of (batch b, query head h) in the query-side copies staged at head dim dh.
+__host__ __device__ inline int64_t q_tile(int b, int h, int qt, int Hq, int nqt, int dh = kD) {
+  return ((static_cast<int64_t>(b) * Hq + h) * nqt + qt) * (kQTile * dh);
 }
 
 // permuted position <-> element within a group of 16 (an involution)
@@ -270,7 +270,7 @@ struct Staging {
   float* knorm;        // [B][Hkv][Tk_pad]: running maximum over keys 0..j of |k_j| (Euclidean, unscaled)
   float* vnorm;        // the same for |v_j|; directly after knorm
   int Tk_pad;
-  int dh;              // staged head dim (128, or 64 for the forwards' native layout)
+  int dh;              // staged head dim (128 or 64)
   size_t bytes;        // total workspace used
 };
 
@@ -306,10 +306,10 @@ inline Staging staging_layout(void* ws, int B, int Tk, int Hkv, int Hq, bool bac
 // In-place running maximum (suffix: from the end) along `series` series of n floats, `stride` apart.
 hipError_t launch_scan_max(float* x, int n, int series, int64_t stride, bool suffix, hipStream_t stream);
 
-// Query-side fp16 copies in the row-tile layout (see k_stage_rows in fast_staging.hip).
+// Query-side fp16 copies in the row-tile layout at head dim dh (see k_stage_rows in fast_staging.hip).
 hipError_t launch_stage_rows(const void* src, bool f32, const uint32_t* maxbits, int max_idx, _Float16* dst,
                              _Float16* lo, int B, int Tq, int Tq_pad, int Hq, int lo_rows, int lo_pad,
-                             hipStream_t stream, int D = kD);   // D: row length of a bf16 src (fp32 src rows are 128)
+                             hipStream_t stream, int D, int dh);   // D: row length of a bf16 src (fp32 src rows are dh)
 
 // Launches the staging kernels: max-abs of q (rows [0, Tq)), k, v, P (and of one more bf16 tensor,
 // `extra`, into maxbits[extra_slot]) in one launch, then the fp16 copies.  q may be nullptr (decode

@@ -220,34 +220,32 @@ __global__ __launch_bounds__(256) void k_stage_p(const u16* P, const uint32_t* m
   }
 }
 
-// Query-side tensors for the key-major backward kernel.  One block per (32-row tile, head, batch):
-// src [B][Tq][Hq][128] (bf16 or fp32) -> dst query-row tiles (d permuted) and dstt query-column
-// tiles (rows permuted within groups of 16), scaled by range_scale(max) with max =
-// maxbits[max_idx].  With lo / lot, also the fp16 residuals x*s - hi for rows < lo_rows (tiles of
-// a [B][Hq][lo_pad] index space).
-// Query-side fp16 copies in the row-tile layout [16 chunks][32 rows][8] (d permuted within groups
-// of 16, tiles ordered [batch][head][tile]), times the tensor's range scale, and optionally the low
-// halves x - fp16(x) for rows < lo_rows.  One block per 32-row tile: each thread reads 8 consecutive
-// d of a row (coalesced), the two 4-d runs go through LDS to their chunks (a run of 4 d is a run of
-// 4 positions), and each thread writes whole 16-byte chunks (consecutive rows of a chunk are
-// contiguous).
-template <bool F32>
+// Query-side fp16 copies in the row-tile layout [DH/8 chunks][32 rows][8] (d permuted within groups of 16,
+// tiles ordered [batch][head][tile]), times the tensor's range scale, and optionally the low halves
+// x - fp16(x) for rows < lo_rows (tiles of a [B][Hq][lo_pad] index space).  src is [B][Tq][Hq][row]: bf16
+// caller rows of D elements (zero-padded to DH) or fp32 workspace rows of DH.  One block per 32-row tile:
+// each thread reads 8 consecutive d of a row (coalesced), the two 4-d runs go through LDS to their chunks
+// (a run of 4 d is a run of 4 positions), and each thread writes whole 16-byte chunks (consecutive rows of
+// a chunk are contiguous).
+template <bool F32, int DH>
 __global__ __launch_bounds__(256) void k_stage_rows(const void* src, const uint32_t* maxbits, int max_idx,
                                                     _Float16* dst, _Float16* lo, int Tq, int Tq_pad, int Hq,
                                                     int lo_rows, int lo_pad, int D) {
-  __shared__ uint2 hs[16 * 32 * 2];   // [chunk][row][half of the chunk]
-  __shared__ uint2 ls[16 * 32 * 2];
+  constexpr int NC = DH / 8;                  // chunks per row
+  constexpr int REPS = 32 * NC / 256;         // 16-byte items per thread
+  __shared__ uint2 hs[NC * 32 * 2];   // [chunk][row][half of the chunk]
+  __shared__ uint2 ls[NC * 32 * 2];
   // the heads of one row tile are consecutive blocks, so they read the same rows together
   const int h = blockIdx.x % Hq, qt = blockIdx.x / Hq, b = blockIdx.z, t = threadIdx.x;
   const int r0 = qt * 32;
   const float sc = range_scale(__uint_as_float(maxbits[max_idx]));
   const bool want_lo = lo != nullptr && r0 < lo_rows;
 #pragma unroll
-  for (int rep = 0; rep < 2; ++rep) {
-    const int i = t + 256 * rep, r = i >> 4, k = i & 15, row = r0 + r;   // d = 8 k .. 8 k + 7
+  for (int rep = 0; rep < REPS; ++rep) {
+    const int i = t + 256 * rep, r = i / NC, k = i % NC, row = r0 + r;   // d = 8 k .. 8 k + 7
     float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (row < Tq && (F32 || 8 * k < D)) {   // bf16 caller rows of D < 128 elements are zero-padded
-      const int64_t off = ((static_cast<int64_t>(b) * Tq + row) * Hq + h) * (F32 ? kD : D) + 8 * k;
+    if (row < Tq && (F32 || 8 * k < D)) {
+      const int64_t off = ((static_cast<int64_t>(b) * Tq + row) * Hq + h) * (F32 ? DH : D) + 8 * k;
       if constexpr (F32) {
         const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + off);
         const float4 c = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + off + 4);
@@ -280,10 +278,10 @@ __global__ __launch_bounds__(256) void k_stage_rows(const void* src, const uint3
     }
   }
   __syncthreads();
-  const int64_t tb = q_tile(b, h, qt, Hq, Tq_pad / kQTile);
-  const int64_t tbl = want_lo ? q_tile(b, h, qt, Hq, lo_pad / kQTile) : 0;
+  const int64_t tb = q_tile(b, h, qt, Hq, Tq_pad / kQTile, DH);
+  const int64_t tbl = want_lo ? q_tile(b, h, qt, Hq, lo_pad / kQTile, DH) : 0;
 #pragma unroll
-  for (int rep = 0; rep < 2; ++rep) {
+  for (int rep = 0; rep < REPS; ++rep) {
     const int j = t + 256 * rep, c = j >> 5, r = j & 31;
     const uint2 a = hs[(c * 32 + r) * 2], a2 = hs[(c * 32 + r) * 2 + 1];
     *reinterpret_cast<uint4*>(dst + tb + c * (kQTile * 8) + r * 8) = uint4{a.x, a.y, a2.x, a2.y};
@@ -347,15 +345,24 @@ hipError_t launch_scan_max(float* x, int n, int series, int64_t stride, bool suf
 
 hipError_t launch_stage_rows(const void* src, bool f32, const uint32_t* maxbits, int max_idx, _Float16* dst,
                              _Float16* lo, int B, int Tq, int Tq_pad, int Hq, int lo_rows, int lo_pad,
-                             hipStream_t stream, int D) {
+                             hipStream_t stream, int D, int dh) {
   if (B == 0 || Tq_pad == 0) return hipSuccess;
   dim3 grid(Hq * (Tq_pad / 32), 1, B);
-  if (f32)
-    hipLaunchKernelGGL(k_stage_rows<true>, grid, dim3(256), 0, stream, src, maxbits, max_idx, dst, lo, Tq, Tq_pad,
-                       Hq, lo_rows, lo_pad, D);
-  else
-    hipLaunchKernelGGL(k_stage_rows<false>, grid, dim3(256), 0, stream, src, maxbits, max_idx, dst, lo, Tq, Tq_pad,
-                       Hq, lo_rows, lo_pad, D);
+  if (dh == 64) {
+    if (f32)
+      hipLaunchKernelGGL((k_stage_rows<true, 64>), grid, dim3(256), 0, stream, src, maxbits, max_idx, dst, lo, Tq,
+                         Tq_pad, Hq, lo_rows, lo_pad, D);
+    else
+      hipLaunchKernelGGL((k_stage_rows<false, 64>), grid, dim3(256), 0, stream, src, maxbits, max_idx, dst, lo, Tq,
+                         Tq_pad, Hq, lo_rows, lo_pad, D);
+  } else {
+    if (f32)
+      hipLaunchKernelGGL((k_stage_rows<true, kD>), grid, dim3(256), 0, stream, src, maxbits, max_idx, dst, lo, Tq,
+                         Tq_pad, Hq, lo_rows, lo_pad, D);
+    else
+      hipLaunchKernelGGL((k_stage_rows<false, kD>), grid, dim3(256), 0, stream, src, maxbits, max_idx, dst, lo, Tq,
+                         Tq_pad, Hq, lo_rows, lo_pad, D);
+  }
   return hipGetLastError();
 }
 

@@ -238,7 +238,7 @@ def test_determinism(plx):
 
 @pytest.mark.parametrize("d", [64, 96])
 def test_bf16_generic_head_dims(plx, d):
-    """Head dims other than 128: d = 64 runs the MFMA paths (zero-padded to 128) and d = 96 the generic
+    """Head dims other than 128: d = 64 runs the MFMA paths (their head-dim-64 kernels) and d = 96 the generic
     kernels, for forward, backward and decode.  All against the oracle."""
     _announce(f"bf16 generic path d={d}")
     w = W.scaled(W.WORKLOADS["train06"], batch=2, seqlen_q=150, seqlen_k=150, heads_q=4, heads_kv=2, head_dim=d)

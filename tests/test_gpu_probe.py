@@ -245,7 +245,7 @@ def test_probe_full_size_train_step_sampled(plx):
 
 @pytest.mark.parametrize("T,window", [(1000, 0), (333, 100)])
 def test_probe_head_dim_64(plx, T, window):
-    """Head dim 64 (zero-padded to 128 in the MFMA operands) for the probe-form forward and backward."""
+    """Head dim 64 (the MFMA kernels instantiated for 64) for the probe-form forward and backward."""
     w = W.scaled(W.WORKLOADS["train06"], batch=2, seqlen_q=T, seqlen_k=T, head_dim=64)
     _announce(f"probe forward + backward d=64 T={T} window={window}")
     _check(plx, w, True, window)
