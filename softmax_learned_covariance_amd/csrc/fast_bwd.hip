@@ -1558,8 +1558,20 @@ __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
     f32x16 accK[NT], accV[NT];
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt) accK[mt] = accV[mt] = f32x16{};
+    // A ds tile is stored one iteration after it is formed, at the start of the next one: the wait that
+    // ends an iteration (for the next tile's copy) then finds the stores long done instead of waiting for them.
+    f16x8 ds_hold[2];
+    int64_t ds_at = -1;   // element offset of the held tile in ds (-1: none)
+    auto store_ds = [&]() {
+      if (ds_at >= 0) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) *reinterpret_cast<f16x8*>(p.ds + ds_at + t * 512) = ds_hold[t];
+        ds_at = -1;
+      }
+    };
     for (int it = 0; it <= total; ++it) {
       const int pbuf = (it + 2) % 3;
+      store_ds();
       if (it + 1 < total) key_tile_dma3(p, T, (it + 1) % 3, b, tile_head(it + 1), tile_row(it + 1), w, l);
       const bool has = it >= 1 && tile_any(it - 1);
       // operands of tile it - 1, taken before the V waves overwrite the exchange with tile it
@@ -1601,18 +1613,16 @@ __global__ __launch_bounds__(512) void k_bwd_keys_pipe(KeyParams p) {
         // DT: lane = query row of the tile, register r = key 8 (r / 4) + 4 hh + r % 4 of the wave's 32
         const int64_t tile = ((static_cast<int64_t>(b) * p.Hq + tile_head(it - 1)) * (p.Tq_pad / 32) +
                               tile_row(it - 1) / 32) * (p.Tk_pad / 32) + jw / 32;
-        _Float16* dst = p.ds + tile * 1024 + l * 8;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          f16x8 o;
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] = static_cast<_Float16>(DT[8 * t + e]);
-          *reinterpret_cast<f16x8*>(dst + t * 512) = o;
-        }
+          for (int e = 0; e < 8; ++e) ds_hold[t][e] = static_cast<_Float16>(DT[8 * t + e]);
+        ds_at = tile * 1024 + l * 8;
       }
       lds_dma_wait();
       __syncthreads();
     }
+    store_ds();
     if (key_ok) {
       const float fv = 1.f / (ks.sG * T.ksc[grp][1][ql]);
       float* dvr = p.dv + ((static_cast<int64_t>(b) * p.Tk + key) * p.Hkv + g) * p.D;
