@@ -193,6 +193,55 @@ __device__ __forceinline__ void row_dots(const RowParams& p, int64_t qoff, bool 
   gabs = xor32_sum(gabs);
 }
 
+// g.o and g.out of a wave's 32 query rows i0 .. i0 + 31 (head h, batch b), read a row per half-wave (each
+// half reads one row's DH values contiguously, so the loads are whole cache lines), summed over the half
+// and handed to the lanes that own the row (lanes r and r + 32 of the accumulator layout).
+template <int DH>
+__device__ __forceinline__ void row_dots_wave(const RowParams& p, int b, int h, int i0, int l, float& go, float& gout) {
+  constexpr int PER = DH / 32;   // values of a row per lane
+  const int half = l >> 5, c = l & 31;
+  go = 0.f;
+  gout = 0.f;
+#pragma unroll 4
+  for (int rp = 0; rp < 16; ++rp) {
+    const int row = i0 + 2 * rp + half;
+    float a = 0.f, o = 0.f;
+    if (row < p.row_end) {
+      const int64_t off = ((static_cast<int64_t>(b) * p.Tq + row) * p.Hq + h) * DH + PER * c;
+      if constexpr (PER == 4) {
+        float gv[4];
+        load4_bf16(p.dout + off, gv);
+        const float4 ov = *reinterpret_cast<const float4*>(p.osa + off);
+        const float4 uv = *reinterpret_cast<const float4*>(p.out + off);
+        a = gv[0] * ov.x + gv[1] * ov.y + gv[2] * ov.z + gv[3] * ov.w;
+        o = gv[0] * uv.x + gv[1] * uv.y + gv[2] * uv.z + gv[3] * uv.w;
+      } else {
+        const uint32_t gw = *reinterpret_cast<const uint32_t*>(p.dout + off);
+        const float g0 = __uint_as_float(gw << 16), g1 = __uint_as_float(gw & 0xffff0000u);
+        const float2 ov = *reinterpret_cast<const float2*>(p.osa + off);
+        const float2 uv = *reinterpret_cast<const float2*>(p.out + off);
+        a = g0 * ov.x + g1 * ov.y;
+        o = g0 * uv.x + g1 * uv.y;
+      }
+    }
+#pragma unroll
+    for (int sh = 16; sh > 0; sh >>= 1) {
+      a += __shfl_xor(a, sh, 64);
+      o += __shfl_xor(o, sh, 64);
+    }
+    // row i0 + 2 rp is summed in lanes 0-31, row i0 + 2 rp + 1 in lanes 32-63
+    const float a0 = __shfl(a, 0, 64), a1 = __shfl(a, 32, 64), o0 = __shfl(o, 0, 64), o1 = __shfl(o, 32, 64);
+    if (c == 2 * rp) {
+      go = a0;
+      gout = o0;
+    }
+    if (c == 2 * rp + 1) {
+      go = a1;
+      gout = o1;
+    }
+  }
+}
+
 // Probe form: the per-row vectors the key-major pass needs, from the supplied probe.  u = -rho,
 // dkbar = -(g.o) u = (g.o) rho, drho = -du, and dq starts at 0 (no projector term).  Writes u, dkbar,
 // drho and the zero dq of the lane's half-row; `du` holds du in the accumulator layout.
@@ -698,29 +747,18 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
   const float pmV = r_kend > r_kbeg ? p.vnorm[nbase + r_kend - 1] : 0.f;
   const float sPG = range_scale(PROBE ? 2.f * gnorm * pmV : gnorm * pmV);
 
-  // probe form: du = sum_j p_j (G_j - g.o) k_j directly (kbar is not an input), so g.o comes first
-  float go_pre = 0.f;
-  if constexpr (PROBE) {
-#pragma unroll
-    for (int d = 4 * hh; d < DH; d += 8) {
-      float gv[4] = {0.f, 0.f, 0.f, 0.f};
-      float4 ov = {0.f, 0.f, 0.f, 0.f};
-      if (row_ok) {
-        if (d < p.D) load4_bf16(p.dout + qoff + d, gv);
-        if (d < p.D) ov = *reinterpret_cast<const float4*>(p.osa + qoff + d);
-      }
-      go_pre += gv[0] * ov.x + gv[1] * ov.y + gv[2] * ov.z + gv[3] * ov.w;
-    }
-    go_pre = xor32_sum(go_pre);
-  }
-  const float goS = go_pre * sG * sV;   // g.o in the units of the G tile
+  // g.o and g.out of the row, read while the first tile is being copied (the probe form forms du =
+  // sum_j p_j (G_j - g.o) k_j directly, kbar not being an input, so it needs g.o first)
+  if (t_beg < t_end) row_tile_dma8(p, T, 0, b, g, t_beg, w, l);
+  float go, gout;
+  row_dots_wave<DH>(p, b, h, i0, l, go, gout);
+  const float goS = PROBE ? go * sG * sV : 0.f;   // g.o in the units of the G tile
 
   // ---------------- du = sum_j p_j G_j k_j (scaled) ----------------
   f32x16 accDU[NT];
 #pragma unroll
   for (int mt = 0; mt < NT; ++mt) accDU[mt] = f32x16{};
   const float fPG = sPG / (sG * sV);
-  if (t_beg < t_end) row_tile_dma8(p, T, 0, b, g, t_beg, w, l);
   lds_dma_wait();
   __syncthreads();
   for (int kt = t_beg; kt < t_end; ++kt) {
@@ -783,9 +821,6 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
 
   // ---------------- epilogue ----------------
   // row vectors in the accumulator layout: element (mt, r) is d = 32 mt + 8 (r/4) + 4 hh + r%4
-  float go, gout, gabs;
-  row_dots<NT>(p, qoff, row_ok, hh, go, gout, gabs);
-  if constexpr (PROBE) go = go_pre;   // the value du was formed with
   float alpha = 0.f, dkk = 0.f, umax = 0.f, emax = 0.f, u2 = 0.f, e2 = 0.f;
   if constexpr (PROBE) {
     // u = -rho, dkbar = (g.o) rho, drho = -du, dq starts at 0 (no projector term)
