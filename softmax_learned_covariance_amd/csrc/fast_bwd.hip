@@ -242,6 +242,65 @@ __device__ __forceinline__ void row_dots_wave(const RowParams& p, int b, int h, 
   }
 }
 
+// Row-vector transfers between memory and the accumulator layout (register 4 j + e of d tile mt is d =
+// 32 mt + 8 j + 4 hh + e of row ql) through a wave-private LDS block of 32 rows x kWR floats: a 32-wide d
+// tile of the wave's 32 rows moves as eight rows of 128 contiguous bytes per instruction, instead of 16
+// bytes of each of 32 rows.  Rows at or past row_end read as zeros and are not written.
+constexpr int kWR = 36;   // LDS row stride in floats
+struct WaveRows {
+  float* lds;             // the wave's 32 x kWR floats
+  int64_t base;           // element offset of (row i0, d 0); rows are rstride elements apart
+  int64_t rstride;
+  int nrows;              // rows of the wave that exist (i0 + r < row_end)
+  int l, ql, hh;
+
+  __device__ __forceinline__ void lds_sync() const { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+  // tile mt of an fp32 array (F32) or a bf16 array into v
+  template <bool F32>
+  __device__ __forceinline__ void load(const void* src, int mt, float (&v)[16]) const {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int rr = 8 * it + (l >> 3), c4 = 4 * (l & 7);
+      float4 x = {0.f, 0.f, 0.f, 0.f};
+      if (rr < nrows) {
+        const int64_t o = base + rr * rstride + 32 * mt + c4;
+        if constexpr (F32) {
+          x = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + o);
+        } else {
+          float t[4];
+          load4_bf16(static_cast<const u16*>(src) + o, t);
+          x = float4{t[0], t[1], t[2], t[3]};
+        }
+      }
+      *reinterpret_cast<float4*>(lds + rr * kWR + c4) = x;
+    }
+    lds_sync();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 y = *reinterpret_cast<const float4*>(lds + ql * kWR + 8 * j + 4 * hh);
+      v[4 * j] = y.x;
+      v[4 * j + 1] = y.y;
+      v[4 * j + 2] = y.z;
+      v[4 * j + 3] = y.w;
+    }
+    lds_sync();
+  }
+  // v as tile mt of an fp32 array
+  __device__ __forceinline__ void store(float* dst, int mt, const float (&v)[16]) const {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<float4*>(lds + ql * kWR + 8 * j + 4 * hh) = float4{v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]};
+    lds_sync();
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int rr = 8 * it + (l >> 3), c4 = 4 * (l & 7);
+      const float4 x = *reinterpret_cast<const float4*>(lds + rr * kWR + c4);
+      if (rr < nrows) *reinterpret_cast<float4*>(dst + base + rr * rstride + 32 * mt + c4) = x;
+    }
+    lds_sync();
+  }
+};
+
 // Probe form: the per-row vectors the key-major pass needs, from the supplied probe.  u = -rho,
 // dkbar = -(g.o) u = (g.o) rho, drho = -du, and dq starts at 0 (no projector term).  Writes u, dkbar,
 // drho and the zero dq of the lane's half-row; `du` holds du in the accumulator layout.
@@ -820,34 +879,43 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
   }
 
   // ---------------- epilogue ----------------
-  // row vectors in the accumulator layout: element (mt, r) is d = 32 mt + 8 (r/4) + 4 hh + r%4
+  // row vectors in the accumulator layout: element (mt, r) is d = 32 mt + 8 (r/4) + 4 hh + r%4; they move
+  // to and from memory through the tile buffers, which are free now (every wave has passed the loop)
+  WaveRows wr;
+  wr.lds = reinterpret_cast<float*>(&T) + w * 32 * kWR;
+  wr.rstride = static_cast<int64_t>(p.Hq) * DH;
+  wr.base = ((static_cast<int64_t>(b) * p.Tq + min(i0, p.Tq - 1)) * p.Hq + h) * DH;
+  wr.nrows = max(0, min(32, p.row_end - i0));
+  wr.l = l;
+  wr.ql = ql;
+  wr.hh = hh;
   float alpha = 0.f, dkk = 0.f, umax = 0.f, emax = 0.f, u2 = 0.f, e2 = 0.f;
   if constexpr (PROBE) {
     // u = -rho, dkbar = (g.o) rho, drho = -du, dq starts at 0 (no projector term)
     const float fdu = 1.f / (sPG * sK);
 #pragma unroll
-    for (int mt = 0; mt < NT; ++mt)
+    for (int mt = 0; mt < NT; ++mt) {
+      float rv[16], v[16];
+      wr.load<false>(p.rho, mt, rv);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = 32 * mt + 8 * j + 4 * hh;
-        float rv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (row_ok) if (d < p.D) load4_bf16(p.rho + qoff + d, rv);
-        float dr[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          dr[e] = -accDU[mt][4 * j + e] * fdu;
-          umax = fmaxf(umax, fabsf(rv[e]));
-          emax = fmaxf(emax, fabsf(go * rv[e]));
-          u2 = fmaf(rv[e], rv[e], u2);
-          e2 = fmaf(go * rv[e], go * rv[e], e2);
-        }
-        if (row_ok) {
-          if (d < p.D) *reinterpret_cast<float4*>(p.drho + qoff + d) = float4{dr[0], dr[1], dr[2], dr[3]};
-          if (d < p.D) *reinterpret_cast<float4*>(p.dq + qoff + d) = float4{0.f, 0.f, 0.f, 0.f};
-          *reinterpret_cast<float4*>(p.u32 + woff + d) = float4{-rv[0], -rv[1], -rv[2], -rv[3]};
-          *reinterpret_cast<float4*>(p.dkb32 + woff + d) = float4{go * rv[0], go * rv[1], go * rv[2], go * rv[3]};
-        }
+      for (int r = 0; r < 16; ++r) {
+        umax = fmaxf(umax, fabsf(rv[r]));
+        emax = fmaxf(emax, fabsf(go * rv[r]));
+        u2 = fmaf(rv[r], rv[r], u2);
+        e2 = fmaf(go * rv[r], go * rv[r], e2);
+        v[r] = -accDU[mt][r] * fdu;
       }
+      wr.store(p.drho, mt, v);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v[r] = 0.f;
+      wr.store(p.dq, mt, v);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v[r] = -rv[r];
+      wr.store(p.u32, mt, v);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v[r] = go * rv[r];
+      wr.store(p.dkb32, mt, v);
+    }
     umax = xor32_max(umax);
     emax = xor32_max(emax);
     u2 = xor32_sum(u2);
@@ -861,32 +929,21 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
     {
       const float fdu = 1.f / (sPG * sK);
 #pragma unroll
-      for (int mt = 0; mt < NT; ++mt)
+      for (int mt = 0; mt < NT; ++mt) {
+        float kv[16], qv[16], xv[16], dv[16];
+        wr.load<true>(p.kbar, mt, kv);
+        wr.load<false>(p.q, mt, qv);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int d = 32 * mt + 8 * j + 4 * hh;
-          float qv[4] = {0.f, 0.f, 0.f, 0.f};
-          float4 kv = {0.f, 0.f, 0.f, 0.f};
-          if (row_ok) {
-            if (d < p.D) load4_bf16(p.q + qoff + d, qv);
-            if (d < p.D) kv = *reinterpret_cast<const float4*>(p.kbar + qoff + d);
-          }
-          const float k4[4] = {kv.x, kv.y, kv.z, kv.w};
-          float x4[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * j + e;
-            x4[e] = qv[e] - k4[e];
-            accDU[mt][r] = accDU[mt][r] * fdu - go * k4[e];
-            xmax = fmaxf(xmax, fabsf(x4[e]));
-            dumax = fmaxf(dumax, fabsf(accDU[mt][r]));
-          }
-          if (row_ok) {
-            *reinterpret_cast<float4*>(p.x32 + woff + d) = float4{x4[0], x4[1], x4[2], x4[3]};
-            *reinterpret_cast<float4*>(p.du32 + woff + d) =
-                float4{accDU[mt][4 * j], accDU[mt][4 * j + 1], accDU[mt][4 * j + 2], accDU[mt][4 * j + 3]};
-          }
+        for (int r = 0; r < 16; ++r) {
+          xv[r] = qv[r] - kv[r];
+          accDU[mt][r] = accDU[mt][r] * fdu - go * kv[r];
+          dv[r] = accDU[mt][r];
+          xmax = fmaxf(xmax, fabsf(xv[r]));
+          dumax = fmaxf(dumax, fabsf(accDU[mt][r]));
         }
+        wr.store(p.x32, mt, xv);
+        wr.store(p.du32, mt, dv);
+      }
     }
     xmax = xor32_max(xmax);
     dumax = xor32_max(dumax);
@@ -905,27 +962,21 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
         for (int s = 0; s < NS; ++s) accPD[am] = mfma(*reinterpret_cast<const f16x8*>(pr + 32 * am * DH + 16 * s), dB[s], accPD[am]);
       }
     }
-    // U^T = P16t X^T, with x = q - kbar re-read: operand s holds d = 16 s + 8 (e/4) + 4 hh + e%4
+    // U^T = P16t X^T, with x = q - kbar re-read: operands 2 mt and 2 mt + 1 are registers 0-7 and 8-15 of tile mt
     {
       f16x8 xB[NS];
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        float x8[8];
+      for (int mt = 0; mt < NT; ++mt) {
+        float kv[16], qv[16];
+        wr.load<true>(p.kbar, mt, kv);
+        wr.load<false>(p.q, mt, qv);
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int d = 16 * s + 8 * half + 4 * hh;
-          float qv[4] = {0.f, 0.f, 0.f, 0.f};
-          float4 kv = {0.f, 0.f, 0.f, 0.f};
-          if (row_ok) {
-            if (d < p.D) load4_bf16(p.q + qoff + d, qv);
-            if (d < p.D) kv = *reinterpret_cast<const float4*>(p.kbar + qoff + d);
-          }
-          x8[4 * half + 0] = qv[0] - kv.x;
-          x8[4 * half + 1] = qv[1] - kv.y;
-          x8[4 * half + 2] = qv[2] - kv.z;
-          x8[4 * half + 3] = qv[3] - kv.w;
+        for (int t = 0; t < 2; ++t) {
+          float x8[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x8[e] = qv[8 * t + e] - kv[8 * t + e];
+          to_operand(x8, sX, xB[2 * mt + t], nullptr);
         }
-        to_operand(x8, sX, xB[s], nullptr);
       }
       const _Float16* prt = p.p16t + (static_cast<int64_t>(h) * DH + ql) * DH + hh * 8;
 #pragma unroll
@@ -939,33 +990,25 @@ __global__ __launch_bounds__(512) void k_bwd_du(RowParams p) {
     {
       const float fu = 1.f / (sX * sP), fpd = 1.f / (sP * sDU);
 #pragma unroll
-      for (int mt = 0; mt < NT; ++mt)
+      for (int mt = 0; mt < NT; ++mt) {
+        float kv[16], uv[16], pv[16], ev[16];
+        wr.load<true>(p.kbar, mt, kv);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int d = 32 * mt + 8 * j + 4 * hh;
-          float4 kv = {0.f, 0.f, 0.f, 0.f};
-          if (row_ok) if (d < p.D) kv = *reinterpret_cast<const float4*>(p.kbar + qoff + d);
-          const float k4[4] = {kv.x, kv.y, kv.z, kv.w};
-          float u4[4], pd4[4], dk4[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * j + e;
-            u4[e] = accU[mt][r] * fu;
-            pd4[e] = accPD[mt][r] * fpd;
-            dk4[e] = -go * u4[e] - pd4[e];
-            alpha += u4[e] * k4[e];
-            dkk += dk4[e] * k4[e];
-            umax = fmaxf(umax, fabsf(u4[e]));
-            emax = fmaxf(emax, fabsf(dk4[e]));
-            u2 = fmaf(u4[e], u4[e], u2);
-            e2 = fmaf(dk4[e], dk4[e], e2);
-          }
-          if (row_ok) {
-            if (d < p.D) *reinterpret_cast<float4*>(p.dq + qoff + d) = float4{pd4[0], pd4[1], pd4[2], pd4[3]};
-            *reinterpret_cast<float4*>(p.u32 + woff + d) = float4{u4[0], u4[1], u4[2], u4[3]};
-            *reinterpret_cast<float4*>(p.dkb32 + woff + d) = float4{dk4[0], dk4[1], dk4[2], dk4[3]};
-          }
+        for (int r = 0; r < 16; ++r) {
+          uv[r] = accU[mt][r] * fu;
+          pv[r] = accPD[mt][r] * fpd;
+          ev[r] = -go * uv[r] - pv[r];
+          alpha += uv[r] * kv[r];
+          dkk += ev[r] * kv[r];
+          umax = fmaxf(umax, fabsf(uv[r]));
+          emax = fmaxf(emax, fabsf(ev[r]));
+          u2 = fmaf(uv[r], uv[r], u2);
+          e2 = fmaf(ev[r], ev[r], e2);
         }
+        wr.store(p.dq, mt, pv);
+        wr.store(p.u32, mt, uv);
+        wr.store(p.dkb32, mt, ev);
+      }
     }
     alpha = xor32_sum(alpha);
     dkk = xor32_sum(dkk);
