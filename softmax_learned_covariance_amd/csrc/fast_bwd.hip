@@ -242,65 +242,6 @@ __device__ __forceinline__ void row_dots_wave(const RowParams& p, int b, int h, 
   }
 }
 
-// Row-vector transfers between memory and the accumulator layout (register 4 j + e of d tile mt is d =
-// 32 mt + 8 j + 4 hh + e of row ql) through a wave-private LDS block of 32 rows x kWR floats: a 32-wide d
-// tile of the wave's 32 rows moves as eight rows of 128 contiguous bytes per instruction, instead of 16
-// bytes of each of 32 rows.  Rows at or past row_end read as zeros and are not written.
-constexpr int kWR = 36;   // LDS row stride in floats
-struct WaveRows {
-  float* lds;             // the wave's 32 x kWR floats
-  int64_t base;           // element offset of (row i0, d 0); rows are rstride elements apart
-  int64_t rstride;
-  int nrows;              // rows of the wave that exist (i0 + r < row_end)
-  int l, ql, hh;
-
-  __device__ __forceinline__ void lds_sync() const { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-  // tile mt of an fp32 array (F32) or a bf16 array into v
-  template <bool F32>
-  __device__ __forceinline__ void load(const void* src, int mt, float (&v)[16]) const {
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int rr = 8 * it + (l >> 3), c4 = 4 * (l & 7);
-      float4 x = {0.f, 0.f, 0.f, 0.f};
-      if (rr < nrows) {
-        const int64_t o = base + rr * rstride + 32 * mt + c4;
-        if constexpr (F32) {
-          x = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + o);
-        } else {
-          float t[4];
-          load4_bf16(static_cast<const u16*>(src) + o, t);
-          x = float4{t[0], t[1], t[2], t[3]};
-        }
-      }
-      *reinterpret_cast<float4*>(lds + rr * kWR + c4) = x;
-    }
-    lds_sync();
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float4 y = *reinterpret_cast<const float4*>(lds + ql * kWR + 8 * j + 4 * hh);
-      v[4 * j] = y.x;
-      v[4 * j + 1] = y.y;
-      v[4 * j + 2] = y.z;
-      v[4 * j + 3] = y.w;
-    }
-    lds_sync();
-  }
-  // v as tile mt of an fp32 array
-  __device__ __forceinline__ void store(float* dst, int mt, const float (&v)[16]) const {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<float4*>(lds + ql * kWR + 8 * j + 4 * hh) = float4{v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]};
-    lds_sync();
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int rr = 8 * it + (l >> 3), c4 = 4 * (l & 7);
-      const float4 x = *reinterpret_cast<const float4*>(lds + rr * kWR + c4);
-      if (rr < nrows) *reinterpret_cast<float4*>(dst + base + rr * rstride + 32 * mt + c4) = x;
-    }
-    lds_sync();
-  }
-};
-
 // Probe form: the per-row vectors the key-major pass needs, from the supplied probe.  u = -rho,
 // dkbar = -(g.o) u = (g.o) rho, drho = -du, and dq starts at 0 (no projector term).  Writes u, dkbar,
 // drho and the zero dq of the lane's half-row; `du` holds du in the accumulator layout.

@@ -254,6 +254,73 @@ __device__ __forceinline__ f16x8 tr_cols_swz(const _Float16* rows, int2 lane_off
 // Row slot of row r of chunk c in a swizzled row tile (an involution: also the row held by slot r).
 __device__ __forceinline__ int row_slot_swz(int r, int c) { return r ^ (4 * (c & 3)); }
 
+// Row-vector transfers between memory and the accumulator layout (register 4 j + e of d tile mt is d =
+// 32 mt + 8 j + 4 hh + e of row ql) through a wave-private LDS block of 32 rows x kWR floats: a 32-wide d
+// tile of the wave's 32 rows moves as eight rows of 128 contiguous bytes per instruction, instead of 16
+// bytes of each of 32 rows.  Rows at or past row_end read as zeros and are not written.
+constexpr int kWR = 36;   // LDS row stride in floats
+struct WaveRows {
+  float* lds;             // the wave's 32 x kWR floats
+  int64_t base;           // element offset of (row i0, d 0); rows are rstride elements apart
+  int64_t rstride;
+  int nrows;              // rows of the wave that exist (i0 + r < row_end)
+  int l, ql, hh;
+
+  __device__ __forceinline__ void lds_sync() const { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+  // tile mt of an fp32 array (F32) or a bf16 array into v
+  template <bool F32>
+  __device__ __forceinline__ void load(const void* src, int mt, float (&v)[16]) const {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int rr = 8 * it + (l >> 3), c4 = 4 * (l & 7);
+      float4 x = {0.f, 0.f, 0.f, 0.f};
+      if (rr < nrows) {
+        const int64_t o = base + rr * rstride + 32 * mt + c4;
+        if constexpr (F32) {
+          x = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + o);
+        } else {
+          const uint2 g = *reinterpret_cast<const uint2*>(static_cast<const u16*>(src) + o);
+          x = float4{__uint_as_float(g.x << 16), __uint_as_float(g.x & 0xffff0000u), __uint_as_float(g.y << 16),
+                     __uint_as_float(g.y & 0xffff0000u)};
+        }
+      }
+      *reinterpret_cast<float4*>(lds + rr * kWR + c4) = x;
+    }
+    lds_sync();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 y = *reinterpret_cast<const float4*>(lds + ql * kWR + 8 * j + 4 * hh);
+      v[4 * j] = y.x;
+      v[4 * j + 1] = y.y;
+      v[4 * j + 2] = y.z;
+      v[4 * j + 3] = y.w;
+    }
+    lds_sync();
+  }
+  // v as tile mt of an fp32 array, or (BF16) of a bf16 array (rounded to nearest even)
+  template <bool BF16 = false>
+  __device__ __forceinline__ void store(void* dst, int mt, const float (&v)[16]) const {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<float4*>(lds + ql * kWR + 8 * j + 4 * hh) = float4{v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]};
+    lds_sync();
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int rr = 8 * it + (l >> 3), c4 = 4 * (l & 7);
+      const float4 x = *reinterpret_cast<const float4*>(lds + rr * kWR + c4);
+      if (rr < nrows) {
+        const int64_t o = base + rr * rstride + 32 * mt + c4;
+        if constexpr (BF16)
+          *reinterpret_cast<uint2*>(static_cast<u16*>(dst) + o) =
+              uint2{f32_to_bf16(x.x) | (f32_to_bf16(x.y) << 16), f32_to_bf16(x.z) | (f32_to_bf16(x.w) << 16)};
+        else
+          *reinterpret_cast<float4*>(static_cast<float*>(dst) + o) = x;
+      }
+    }
+    lds_sync();
+  }
+};
+
 // ---- staging buffers inside the caller's workspace ----
 // Slots of the max-abs array (float bits; non-negative floats order like their bits).
 enum MaxSlot { kMaxQ = 0, kMaxK = 1, kMaxV = 2, kMaxP = 3, kMaxDO = 4, kMaxU = 5, kMaxDKB = 6, kMaxDelta = 7,

@@ -307,8 +307,21 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
   const float invL = has ? 1.f / L : 0.f;
   const float lse2 = has ? m_used - kLift + __log2f(L) : -INFINITY;   // (L carries the 2^kLift of p~)
   float* obuf = p.osa;
+  // row vectors move to and from memory through the tile buffers (free between the passes and after the
+  // second), a wave-private block each
+  auto rows_io = [&]() {
+    WaveRows r;
+    r.lds = reinterpret_cast<float*>(&T) + w * 32 * kWR;
+    r.rstride = static_cast<int64_t>(p.Hq) * DH;
+    r.base = ((static_cast<int64_t>(b) * p.Tq + min(i0, p.Tq - 1)) * p.Hq + h) * DH;
+    r.nrows = max(0, min(32, p.row_end - i0));
+    r.l = l;
+    r.ql = ql;
+    r.hh = hh;
+    return r;
+  };
+  if (row_ok && p.lse && hh == 0) p.lse[(static_cast<int64_t>(b) * p.Hq + h) * p.Tq + row] = lse2 * kLn2;
   if (row_ok) {
-    if (p.lse && hh == 0) p.lse[(static_cast<int64_t>(b) * p.Hq + h) * p.Tq + row] = lse2 * kLn2;
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
@@ -449,6 +462,7 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
     const float kmax = r_kend > r_kbeg ? p.knorm[(static_cast<int64_t>(b) * p.Hkv + g) * p.Tk_pad + r_kend - 1] * sK : 0.f;
     mb2 = lse2 + static_cast<float>(-range_exp(sqrtf(u2sum) * (kmax + sqrtf(k2sum))));
   }
+  __syncthreads();   // (every wave is done with its row block in the tile buffers)
   if (t_beg < t_end) tile_dma(p, T, 0, b, g, t_beg, false, w, l);
   lds_dma_wait();
   __syncthreads();
@@ -523,28 +537,26 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
   // ---------------- epilogue 2: out = o + c - rs o ----------------
   const float RS = xor32_sum(rpart);
   float cc = 0.f, oo = 0.f;   // |out - o|^2 and |out|^2 of the lane's half-row
-  if (row_ok) {
+  {
     // W was carried as p 2^-wexp (R - alpha), wexp = mb2 - lse2 (an integer; the fp32 sum keeps it to
     // well within 1/2)
     const float fw = has ? __builtin_ldexpf(1.f, static_cast<int>(rintf(mb2 - lse2))) : 0.f;
     const float fc = fw / (sU * sK * sV);
     const float frs = RS * (fw / (sU * sK));
+    const WaveRows wr = rows_io();
 #pragma unroll
-    for (int mt = 0; mt < NT; ++mt)
+    for (int mt = 0; mt < NT; ++mt) {
+      float ov[16], rv[16];
+      wr.load<true>(obuf, mt, ov);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = 32 * mt + 8 * j + 4 * hh;
-        const float4 ov = *reinterpret_cast<const float4*>(obuf + qoff + d);
-        const float o4[4] = {ov.x, ov.y, ov.z, ov.w};
-        float r4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          r4[e] = o4[e] + accC[mt][4 * j + e] * fc - frs * o4[e];
-          cc = fmaf(r4[e] - o4[e], r4[e] - o4[e], cc);
-          oo = fmaf(r4[e], r4[e], oo);
-        }
-        store_out4(p.out, qoff + d, p.out_bf16, r4[0], r4[1], r4[2], r4[3]);
+      for (int r = 0; r < 16; ++r) {
+        rv[r] = ov[r] + accC[mt][r] * fc - frs * ov[r];
+        cc = fmaf(rv[r] - ov[r], rv[r] - ov[r], cc);
+        oo = fmaf(rv[r], rv[r], oo);
       }
+      if (p.out_bf16) wr.store<true>(p.out, mt, rv);
+      else wr.store(p.out, mt, rv);
+    }
   }
   if (p.cor) {
     cc = xor32_sum(cc);
