@@ -25,9 +25,10 @@
 //             dv = (p tt)^T g and dk = (p G)^T u + p^T dkbar + scale ds^T q on MFMA and
 //             store each 32 x 32 tile of ds;
 //   dq        query-major: dq += scale ds K from the stored ds tiles;
-//   dP        sum over rows of (q - kbar) du^T, then a fixed-order reduction.
+//   dP        sum over rows of (q - kbar) du^T, then a fixed-order reduction (on a helper stream,
+//             beside the key-major kernel).
 // Rows below split_rows run two-pass row and key kernels with hi + lo fp16 operand pairs
-// (the row kernel then also forms dq itself).
+// (the row kernel then also forms dq itself), on the helper stream beside the main kernels.
 // Everything is deterministic (no atomics on results).
 #include <math.h>
 
@@ -2185,6 +2186,22 @@ hipError_t bwd_impl(const Geom& g, const BwdArgs& a, int split_rows, void* ws, h
   if (e != hipSuccess) return e;
   e = side_join(side);
   if (e != hipSuccess) return e;
+  // dP = sum over rows of x du^T (x, du from the row kernels, complete now) on the side lane, beside the
+  // key-major kernel
+  const SideLane dpl = probe ? SideLane{stream, stream} : side_fork(stream);
+  if (!probe) {
+    const int R = g.B * g.Tq;
+    if (d64)
+      hipLaunchKernelGGL(k_dp_partial64, dim3(g.Hq * w.nchunks), dim3(256), 0, dpl.stream, w.x32, w.du32, w.part, R,
+                         g.Hq);
+    else
+      hipLaunchKernelGGL(k_dp_partial, dim3(g.Hq * w.nchunks), dim3(256), 0, dpl.stream, w.x32, w.du32, w.part, R,
+                         g.Hq);
+    const int nred = (g.Hq * w.st.dh * w.st.dh + 255) / 256;
+    hipLaunchKernelGGL(k_dp_reduce, dim3(nred), dim3(256), 0, dpl.stream, w.part, dP, w.nchunks, g.Hq, g.d, w.st.dh);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   // per (batch, kv head, statistic): the maximum over rows >= i of each row statistic
   e = launch_scan_max(w.rowmax, w.Tq_pad, g.B * g.Hkv * kRowStats, w.Tq_pad, true, stream);
   if (e != hipSuccess) return e;
@@ -2291,17 +2308,9 @@ hipError_t bwd_impl(const Geom& g, const BwdArgs& a, int split_rows, void* ws, h
     else hipLaunchKernelGGL(k_bwd_dq<kD>, dim3(g.B * g.Hkv * dp.n_rb), dim3(512), 0, stream, dp);
     mark_end(PLX_KERNEL_BWD_DQ, stream);
   }
-  if (!probe) {
-    // dP = sum over rows of x du^T
-    const int R = g.B * g.Tq;
-    if (d64)
-      hipLaunchKernelGGL(k_dp_partial64, dim3(g.Hq * w.nchunks), dim3(256), 0, stream, w.x32, w.du32, w.part, R, g.Hq);
-    else
-      hipLaunchKernelGGL(k_dp_partial, dim3(g.Hq * w.nchunks), dim3(256), 0, stream, w.x32, w.du32, w.part, R, g.Hq);
-    const int nred = (g.Hq * w.st.dh * w.st.dh + 255) / 256;
-    hipLaunchKernelGGL(k_dp_reduce, dim3(nred), dim3(256), 0, stream, w.part, dP, w.nchunks, g.Hq, g.d, w.st.dh);
-  }
   e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = side_join(dpl);   // (the dP work, and whatever followed it on the side lane)
   if (e != hipSuccess) return e;
   return side_join(side);
 }

@@ -203,9 +203,22 @@ __global__ __launch_bounds__(256) void k_stage_p(const u16* P, const uint32_t* m
   const int h = blockIdx.x, part = blockIdx.y, t = threadIdx.x;
   const float sP = range_scale(__uint_as_float(maxbits[3]));
   const u16* src = P + static_cast<int64_t>(h) * D * D;
-  for (int e = t; e < DH * DH; e += 256) {
-    const int r = e / DH, c = e % DH;
-    ps[r * LD + c] = r < D && c < D ? static_cast<_Float16>(bf16_to_f32(src[r * D + c]) * sP) : static_cast<_Float16>(0.f);
+  if (D == DH) {   // 16-byte loads (8 values) per thread
+    for (int e8 = t; e8 < DH * DH / 8; e8 += 256) {
+      const int r = e8 / (DH / 8), c8 = (e8 % (DH / 8)) * 8;
+      const uint4 wv = *reinterpret_cast<const uint4*>(src + r * DH + c8);
+      const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ps[r * LD + c8 + 2 * j] = static_cast<_Float16>(__uint_as_float(ws[j] << 16) * sP);
+        ps[r * LD + c8 + 2 * j + 1] = static_cast<_Float16>(__uint_as_float(ws[j] & 0xffff0000u) * sP);
+      }
+    }
+  } else {
+    for (int e = t; e < DH * DH; e += 256) {
+      const int r = e / DH, c = e % DH;
+      ps[r * LD + c] = r < D && c < D ? static_cast<_Float16>(bf16_to_f32(src[r * D + c]) * sP) : static_cast<_Float16>(0.f);
+    }
   }
   __syncthreads();
   const int a = RPB * part + t / NC, c = t % NC;   // one 16-byte chunk per thread
