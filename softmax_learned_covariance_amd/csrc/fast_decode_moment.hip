@@ -5,30 +5,39 @@
 // "Parallax: Parameterized Local Linear Attention for Language Modeling", "Hardware-aware algorithm").
 // The probe u = P^T (q - kbar) needs the whole sequence's kbar, so instead of a second pass over the
 // cache this kernel accumulates the softmax-weighted moment of the keys and values with them:
-//   M = sum_j v_j y_j^T  with  y_j = bf16(p~_j k_j)   (d x d per query head),
-//   kbar~ = sum_j y_j,   o~ = sum_j w_j v_j,   l = sum_j w_j,   w_j = bf16(p~_j),
+//   M = sum_j v_j y_j^T,  kbar~ = sum_j y_j  with  y_j = fp16(p~_j k_j)   (d x d per query head),
+//   o~ = sum_j p~_j v_j,  l = sum_j p~_j,
 // and after the last key  o = o~ / l,  kbar = kbar~ / l,  u = P^T (q - kbar),  alpha = u . kbar  and
-//   out = o + M u / l - alpha o.
-// Since sum_j w_j (v_j - o) = 0 exactly for these o and l, M u / l - alpha o = sum_j (u . y_j / l)(v_j - o):
-// the correction of the definition, o + sum_j p_j (u . (k_j - kbar))(v_j - o), with y_j / l in place of
-// p_j k_j.  kbar is summed from the same rounded products as M (not from exact weights times keys) so that
-// this identity holds for the values actually accumulated: otherwise M u / l and alpha o, each of size
-// |u . k| |v|, would cancel with a residue of bf16's rounding of p~ k times that size (about 8e-2 of the
-// output's rms once scores spread over tens of units).
+//   out = o + M u / l - alpha o  =  o + sum_j (u . y_j / l)(v_j - o).
+// kbar is summed from the same rounded products as M, so that M u / l - alpha o is exactly that sum for
+// the values accumulated: each of the two terms is of size |u . k| |v| and they cancel, and a kbar from
+// unrounded products would leave the rounding of p~ k times that size.  The correction of the definition,
+// sum_j p_j (u . (k_j - kbar))(v_j - o), differs from it only through the rounding of y (fp16: 2^-11
+// relative per element).
+//
 // M costs 2 d^2 flop per key and head, far more than the two-pass form, so it runs on the matrix cores:
-// per 16 keys, M_h += V^T Y_h on v_mfma_f32_32x32x16_bf16 with the cache's bf16 rows as they are; o~ takes
-// the rounded weights as a matrix of (query head) columns on the same instruction; kbar~ and l are fp32
-// sums of the rounded values.
+// per 16 keys and head, M += V^T Y on v_mfma_f32_32x32x16_f16, plus one product for kbar~ (a ones row
+// against Y) and, per 16 keys, one for o~ (the weights as fp16 hi + lo rows against V).  The cache is
+// bf16: each value tile is converted in LDS to fp16 times 2^ev, and y is formed as fp16(p~ 2^ek k), with
+// power-of-two scales set from each tile's largest magnitudes so that |v| 2^ev < 2^14 and |k| 2^ek < 2^7
+// (p~ <= 2^8, so y < 2^15).  The scales only decrease along the sequence: a tile that needs a smaller one
+// rescales the accumulators by the exact power of two.  Values down to 2^-27 of the largest seen so far
+// keep fp16's full precision, and the output scales exactly with V (and with K at unchanged scores).
 //
 // One 512-thread workgroup (8 waves) owns one (sequence, key/value head) and its one or two query heads,
 // so no partial results leave the workgroup and no workspace is used.  Wave w owns the key dims
-// 32 (w % 4) + [0, 32) of M and the value dims of tiles 2 (w / 4), 2 (w / 4) + 1.  Key tiles of 64 rows
-// arrive by direct-to-LDS DMA, four buffers deep; rows are stored 256 bytes each with the 16-byte chunks of
-// row r permuted (slot = chunk ^ f(r)) so that the transpose loads (ds_read_b64_tr_b16) that form the
-// k-major operands, and the row loads of the scores, hit distinct banks.  Waves 0-3 compute the next tile's
-// scores (16 keys each, v_mfma_f32_16x16x32_bf16) while all waves run the current tile's products; the
-// running maximum is lazy (it moves only when a tile exceeds it by 8 in log2 units).
+// 32 (w % 4) + [0, 32) of M, and keys 32 (w / 4) + [0, 32) of every tile for all 128 value dims.  Key
+// tiles of 64 rows arrive by direct-to-LDS DMA, four buffers deep; rows are stored 256 bytes each with the
+// 16-byte chunks of row r permuted (slot = chunk ^ f(r)) so that the transpose loads (ds_read_b64_tr_b16)
+// that form the k-major operands, and the row loads of the scores, hit distinct banks.  In the phase that runs
+// the current tile's products, waves 0-3 first compute the next tile's scores (16 keys each,
+// v_mfma_f32_16x16x32_bf16) and waves 4-7 its largest |k| and |v| (so the two waves of each SIMD bring
+// different work); after a barrier every wave sets the next tile's scales, waves 0-3 its weights, and all
+// waves convert their share of its values.  The running
+// maximum is lazy (it moves only when a tile exceeds it by 8 in log2 units).
 #include <math.h>
+
+#include <type_traits>
 
 #include "fast_common.h"
 #include "plx_internal.h"
@@ -38,14 +47,17 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2v __attribute__((ext_vector_type(2)));
 
 constexpr int kMT = 64;        // keys per tile
 constexpr int kMBuf = 4;       // tile buffers
 constexpr float kMLog2e = 1.4426950408889634f;
 constexpr float kMTau = 8.f;
+// scale exponents before the first tile that sets them: the largest either rule can ask for (a bf16
+// magnitude of at least 2^-126; for k capped so that p~ 2^ek stays finite)
+constexpr int kEk0 = 110, kEv0 = 139;
 
 struct MomParams {
   const u16 *q, *kc, *vc, *P;
@@ -59,19 +71,21 @@ struct MomParams {
   float scale;
 };
 
+
 struct __align__(16) MomShared {
   union {
     struct {
-      u16 k[kMBuf][kMT * kD];
-      u16 v[kMBuf][kMT * kD];
+      u16 k[kMBuf][kMT * kD];   // bf16 as copied
+      u16 v[kMBuf][kMT * kD];   // bf16 as copied, then fp16 times 2^ev (converted in place)
     } t;
     float M[2][kD][kD + 1];    // epilogue: the moment of each query head, rows padded against bank conflicts
   };
   uint4 qb[4][64];             // score operands (bf16 q) per (step, lane)
   f32x4 sc[4][64];             // scaled scores of the next tile per (score wave, lane), between the two phases
-  float pt[2][2][kMT];         // p~ of a tile per (buffer, head, key), fp32
-  u16 pw[2][5][kMT];           // the same as bf16 pairs per (buffer, row, key): rows h = hi, HW + h = lo, 2 HW = 0
-  float smax[2][4][2];         // per (buffer, score wave, head): the tile maximum (log2 units)
+  float pt[2][2][kMT];         // p~ 2^ek of a tile per (buffer, head, key)
+  u16 pw[2][5][kMT];           // p~ as fp16 pairs per (buffer, row, key): rows h = hi, HW + h = lo, 2 HW = 0
+  float smax[2][2][16];        // per (buffer, head, 4 score wave + lane row): the largest of 4 keys (log2 units)
+  uint32_t amax[2][4];         // per (buffer, wave 4-7): largest |k| (low half) and |v| (high half) as bf16 bits
   float lsum[4][2];
   float vec[3][2][kD];         // epilogue: o, kbar, u per head
   float opart[2][2][kD];       // epilogue: o~ and kbar~ per (key half, head)
@@ -81,8 +95,6 @@ struct __align__(16) MomShared {
 
 // Chunk permutation of row r within a tile (an involution on 0..15): slot = chunk ^ f(r).
 __device__ __forceinline__ int mswz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
-
-__device__ __forceinline__ float bfv(__bf16 x) { return static_cast<float>(x); }
 
 // Cache row of key `key` of sequence b (paged: page table lookup, the page index clamped into the pool).
 template <bool PAGED>
@@ -123,16 +135,43 @@ __device__ __forceinline__ void mom_dma(const MomParams& p, MomShared& S, int bu
 
 __device__ __forceinline__ void vm_wait4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
 
-// k-major operand (32 dims of tile dt, 16 keys of k-step ks) of a 32x32x16 MFMA from a row tile in LDS:
-// two transpose loads, keys 16 ks + 8 (l / 32) + [0, 4) and + [4, 8).
-__device__ __forceinline__ bf16x8 mom_cols(const u16* tile, const int (&loff)[2], int lj, int ks, int dt) {
+// k-major operand (32 dims, 16 keys) of a 32x32x16 MFMA from a row tile in LDS: two transpose loads at the
+// lane's offsets o[0], o[1] from `base` (keys 8 (l / 32) + [0, 4) and + [4, 8) of the 16).
+__device__ __forceinline__ u32x4 mom_cols(const u16* base, const int (&o)[2]) {
   typedef short s16x4 __attribute__((ext_vector_type(4)));
-  const int extra = ks * 2048 + ((dt ^ lj) << 5);
-  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(tile + loff[0] + extra));
-  const s16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(tile + loff[1] + extra));
-  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  const bf16x4 ah = __builtin_bit_cast(bf16x4, a), ch = __builtin_bit_cast(bf16x4, c);
-  return __builtin_shufflevector(ah, ch, 0, 1, 2, 3, 4, 5, 6, 7);
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(base + o[0]));
+  const s16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(base + o[1]));
+  return __builtin_bit_cast(u32x4, __builtin_shufflevector(a, c, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Largest of each 16-bit half (unsigned), and its wave-wide reduction (every lane gets the result).
+__device__ __forceinline__ uint32_t pkmax(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2v, a),
+                                                                 __builtin_bit_cast(u16x2v, b)));
+}
+// Wave-wide reduction through DPP moves (no LDS round trips): swaps within quads, the half-row and row
+// mirrors leave every lane of a row of 16 with the row's result; broadcasts of lane 15 of rows 0 and 2 into
+// rows 1 and 3, then of lane 31 into rows 2 and 3, leave lane 63 with the wave's.
+__device__ __forceinline__ uint32_t pkmax_wave63(uint32_t x) {
+  auto step = [&](uint32_t v, auto ctrl, auto rows) {
+    const int m = __builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), decltype(ctrl)::value,
+                                              decltype(rows)::value, 0xf, false);
+    return pkmax(v, static_cast<uint32_t>(m));
+  };
+  x = step(x, std::integral_constant<int, 0xB1>{}, std::integral_constant<int, 0xf>{});    // quad_perm 1,0,3,2
+  x = step(x, std::integral_constant<int, 0x4E>{}, std::integral_constant<int, 0xf>{});    // quad_perm 2,3,0,1
+  x = step(x, std::integral_constant<int, 0x141>{}, std::integral_constant<int, 0xf>{});   // row_half_mirror
+  x = step(x, std::integral_constant<int, 0x140>{}, std::integral_constant<int, 0xf>{});   // row_mirror
+  x = step(x, std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xa>{});   // row_bcast:15
+  x = step(x, std::integral_constant<int, 0x143>{}, std::integral_constant<int, 0xc>{});   // row_bcast:31
+  return x;
+}
+
+// The two bf16 halves of x as floats times 2^e, rounded to an fp16 pair.
+__device__ __forceinline__ uint32_t bf16pair_to_f16(uint32_t x, int e) {
+  const f32x2 f = {__builtin_amdgcn_ldexpf(__uint_as_float(x << 16), e),
+                   __builtin_amdgcn_ldexpf(__uint_as_float(x & 0xffff0000u), e)};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
 }
 
 template <int HW, bool PAGED>
@@ -163,31 +202,44 @@ __global__ __launch_bounds__(512) void k_dec_moment(MomParams p) {
       S.qb[st][l] = raw;
     }
   }
-  // transpose-load lane offsets (see mom_cols): lane (G = l / 16, j, a) reads 4 dims of key 8 (G / 2) + j
-  const int lG = l >> 4, lj = (l >> 2) & 3, la = l & 3;
-  int loff[2];
+  const int ks_strip = w & 3, kh = w >> 2;   // K dims 32 ks_strip + [0, 32); keys 32 kh + [0, 32) of each tile
+  // transpose-load lane offsets: lane (G = l / 16, j, a) reads 4 dims of key 8 (G / 2) + j (+ 4 for the
+  // second load) of dim tile dt; ov[dt] for the value tiles, os for the wave's K (and V) strip
+  int ov[4][2], os[2];
+  {
+    const int lG = l >> 4, lj = (l >> 2) & 3, la = l & 3;
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int x = 2 * (lG & 1) + (la >> 1), y = 2 * (lG >> 1) + hh;
-    loff[hh] = (8 * (lG >> 1) + lj + 4 * hh) * kD + ((x ^ y) << 3) + ((la & 1) << 2);
+    for (int hh = 0; hh < 2; ++hh) {
+      const int x = 2 * (lG & 1) + (la >> 1), y = 2 * (lG >> 1) + hh;
+      const int base = (8 * (lG >> 1) + lj + 4 * hh) * kD + ((x ^ y) << 3) + ((la & 1) << 2);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) ov[dt][hh] = base + ((dt ^ lj) << 5);
+      os[hh] = base + ((ks_strip ^ lj) << 5);
+    }
   }
   // score row loads (waves 0-3): key 16 w + m, chunk 4 st + l / 16
   const int sm = l & 15;
   const int soff = (16 * (w & 3) + sm) * kD;
 
-  const int ks_strip = w & 3, kh = w >> 2;   // K dims 32 ks_strip + [0, 32); keys 32 kh + [0, 32) of each tile
-  f32x16 accM[4][HW];                        // M of value tile vt (rows) x the K strip (columns), this key half
-  // o~ of value tile ks_strip in columns h (hi weights of head h) and HW + h (lo), kbar~ of K strip ks_strip
-  // in columns 4 + h and 4 + HW + h (two products into one accumulator, each filling only its own columns)
+  f32x16 accM[4][HW];   // M of value tile vt (rows) x the K strip (columns), this key half, times 2^(ek + ev)
+  // rows h and HW + h: o~ of head h from the hi and lo weights (times 2^ev), over the V strip's dims
+  // (columns); row 4 + h: kbar~ of head h (times 2^ek) over the K strip's dims.  Rows 8 and up stay zero.
   f32x16 accX = f32x16{};
 #pragma unroll
   for (int vt = 0; vt < 4; ++vt)
 #pragma unroll
     for (int h = 0; h < HW; ++h) accM[vt][h] = f32x16{};
+  // A operand that sums Y over keys into row 4 + h: ones in that row
+  f16x8 ones[HW];
+#pragma unroll
+  for (int h = 0; h < HW; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[h][e] = (l & 31) == 4 + h ? static_cast<_Float16>(1.f) : static_cast<_Float16>(0.f);
   float m_run[2] = {-INFINITY, -INFINITY};
   float lpart = 0.f;   // waves 0-3, lanes l % 16 < HW: weights of head l % 16
+  int ek = kEk0, ev = kEv0;   // the current scales' exponents (wave-uniform)
 
-  // scores of tile `tile` (waves 0-3) -> their keys' values in registers and the wave's maxima in LDS
+  // scores of tile `tile` (waves 0-3) -> their keys' values and each lane's maximum (4 keys) in LDS
   auto scores = [&](int tile, int buf) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const u16* kt = S.t.k[buf];
@@ -208,69 +260,115 @@ __global__ __launch_bounds__(512) void k_dec_moment(MomParams p) {
       mx = fmaxf(mx, sc[r]);
     }
     S.sc[w & 3][l] = sc;   // (in LDS across the products, not in registers)
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    if (l < HW) S.smax[tile & 1][w & 3][l] = mx;
+    if ((l & 15) < HW) S.smax[tile & 1][l & 15][4 * (w & 3) + (l >> 4)] = mx;
   };
-  // after the barrier: the tile's maximum per head, the lazy running maximum, the accumulators' rescale,
-  // and (waves 0-3) the tile's weights into LDS
-  auto weights = [&](int tile) {
-    float f[2] = {1.f, 1.f};
-    bool any = false;
+  // largest |k| and |v| of the tile in buffer buf (waves 4-7: 64 bytes of each per thread), as bf16 bits
+  auto absmax = [&](int tile, int buf) {
+    const int j = tid - 256;
+    const uint4* kp = reinterpret_cast<const uint4*>(S.t.k[buf]);
+    const uint4* vp = reinterpret_cast<const uint4*>(S.t.v[buf]);
+    uint32_t mk = 0u, mv = 0u;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint4 a = kp[j + 256 * r], c = vp[j + 256 * r];
+      mk = pkmax(pkmax(mk, a.x & 0x7fff7fffu), pkmax(a.y & 0x7fff7fffu, pkmax(a.z & 0x7fff7fffu, a.w & 0x7fff7fffu)));
+      mv = pkmax(pkmax(mv, c.x & 0x7fff7fffu), pkmax(c.y & 0x7fff7fffu, pkmax(c.z & 0x7fff7fffu, c.w & 0x7fff7fffu)));
+    }
+    // low half: k, high half: v
+    uint32_t x = pkmax(__builtin_amdgcn_perm(mv, mk, 0x05040100u), __builtin_amdgcn_perm(mv, mk, 0x07060302u));
+    x = pkmax_wave63(x);
+    if (l == 63) S.amax[tile & 1][w - 4] = x;
+  };
+  // after the barrier that publishes a tile's maxima (the same values in every wave, kept in scalar
+  // registers): its scales, the lazy running maximum, and the factors f (per head) that the accumulators
+  // take before the tile's products; `any` when one of them moved
+  float f[2] = {1.f, 1.f};
+  int rk = 0, rv = 0;
+  bool any = false;
+  auto decide = [&](int tile) {
+    {
+      const uint4 a = *reinterpret_cast<const uint4*>(S.amax[tile & 1]);
+      const uint32_t x = __builtin_amdgcn_readfirstlane(pkmax(pkmax(a.x, a.y), pkmax(a.z, a.w)));
+      const int kb = static_cast<int>(x & 0xffffu), vb = static_cast<int>(x >> 16);
+      // largest magnitude below 2^(E + 1) (E = biased exponent - 127; subnormals as E = -126)
+      const int nk = kb ? min(ek, 133 - max(kb >> 7, 1)) : ek;   // |k| 2^ek < 2^7
+      const int nv = vb ? min(ev, 140 - max(vb >> 7, 1)) : ev;   // |v| 2^ev < 2^14
+      rk = nk - ek;
+      rv = nv - ev;
+      ek = nk;
+      ev = nv;
+    }
+    f[0] = f[1] = 1.f;
+    any = (rk | rv) != 0;
 #pragma unroll
     for (int h = 0; h < HW; ++h) {
-      // (the same value in every lane: kept in scalar registers)
-      const float tm = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(
-          fmaxf(fmaxf(S.smax[tile & 1][0][h], S.smax[tile & 1][1][h]),
-                fmaxf(S.smax[tile & 1][2][h], S.smax[tile & 1][3][h])))));
+      const float4* sm = reinterpret_cast<const float4*>(S.smax[tile & 1][h]);
+      const float4 a0 = sm[0], a1 = sm[1], a2 = sm[2], a3 = sm[3];
+      const float m4 = fmaxf(fmaxf(fmaxf(a0.x, a0.y), fmaxf(a0.z, a0.w)), fmaxf(fmaxf(a1.x, a1.y), fmaxf(a1.z, a1.w)));
+      const float n4 = fmaxf(fmaxf(fmaxf(a2.x, a2.y), fmaxf(a2.z, a2.w)), fmaxf(fmaxf(a3.x, a3.y), fmaxf(a3.z, a3.w)));
+      const float tm = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(fmaxf(m4, n4))));
       if (tm > m_run[h] + kMTau) {
         f[h] = m_run[h] == -INFINITY ? 0.f : exp2f(m_run[h] - tm);
         m_run[h] = tm;
         any = true;
       }
     }
-    if (any) {   // (uniform: every wave reads the same maxima)
+  };
+  // (waves 0-3) the tile's weights into LDS and the running sums l
+  auto weights = [&](int tile) {
+    const int n = l & 15;
+    lpart *= (HW == 2 && n == 1) ? f[HW - 1] : f[0];
+    if (n < HW) {
+      const float mr = n == 0 ? m_run[0] : m_run[HW - 1];
+      const float mb = mr == -INFINITY ? 0.f : mr;
+      const f32x4 sc = S.sc[w][l];
+      float e[4];
 #pragma unroll
-      for (int vt = 0; vt < 4; ++vt)
-#pragma unroll
-        for (int h = 0; h < HW; ++h) accM[vt][h] *= f[h];
-      const int n = l & 31;   // accX column n (< 8): head n % HW
-      accX *= (HW == 2 && (n & 1)) ? f[HW - 1] : f[0];
-      const int n16 = l & 15;
-      lpart *= (HW == 2 && n16 == 1) ? f[HW - 1] : f[0];
-    }
-    if (w < 4) {
-      const int n = l & 15;
-      if (n < HW) {
-        const float mr = n == 0 ? m_run[0] : m_run[HW - 1];
-        const float mb = mr == -INFINITY ? 0.f : mr;
-        const f32x4 sc = S.sc[w][l];
-        float e[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          e[r] = sc[r] == -INFINITY ? 0.f : exp2f(sc[r] - mb);
-          lpart += e[r];
-        }
-        const int k4 = 16 * w + 4 * (l >> 4);
-        *reinterpret_cast<float4*>(&S.pt[tile & 1][n][k4]) = float4{e[0], e[1], e[2], e[3]};
-        // the weights as bf16 pairs hi + lo: rows n and HW + n of the o~ operand
-        uint32_t hw[2], lw[2];
-#pragma unroll
-        for (int r = 0; r < 4; r += 2) {
-          const uint32_t h0 = f32_to_bf16(e[r]), h1 = f32_to_bf16(e[r + 1]);
-          hw[r / 2] = h0 | (h1 << 16);
-          lw[r / 2] = f32_to_bf16(e[r] - __uint_as_float(h0 << 16)) |
-                      (f32_to_bf16(e[r + 1] - __uint_as_float(h1 << 16)) << 16);
-        }
-        *reinterpret_cast<uint2*>(&S.pw[tile & 1][n][k4]) = uint2{hw[0], hw[1]};
-        *reinterpret_cast<uint2*>(&S.pw[tile & 1][HW + n][k4]) = uint2{lw[0], lw[1]};
+      for (int r = 0; r < 4; ++r) {
+        e[r] = sc[r] == -INFINITY ? 0.f : exp2f(sc[r] - mb);
+        lpart += e[r];
       }
+      const int k4 = 16 * w + 4 * (l >> 4);
+      *reinterpret_cast<float4*>(&S.pt[tile & 1][n][k4]) =
+          float4{__builtin_amdgcn_ldexpf(e[0], ek), __builtin_amdgcn_ldexpf(e[1], ek),
+                 __builtin_amdgcn_ldexpf(e[2], ek), __builtin_amdgcn_ldexpf(e[3], ek)};
+      // the weights as fp16 pairs hi + lo: rows n and HW + n of the o~ operand
+      uint32_t hw[2], lw[2];
+#pragma unroll
+      for (int r = 0; r < 4; r += 2) {
+        const f16x2 hv = __builtin_convertvector((f32x2{e[r], e[r + 1]}), f16x2);
+        const f32x2 rem = {e[r] - static_cast<float>(hv[0]), e[r + 1] - static_cast<float>(hv[1])};
+        hw[r / 2] = __builtin_bit_cast(uint32_t, hv);
+        lw[r / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rem, f16x2));
+      }
+      *reinterpret_cast<uint2*>(&S.pw[tile & 1][n][k4]) = uint2{hw[0], hw[1]};
+      *reinterpret_cast<uint2*>(&S.pw[tile & 1][HW + n][k4]) = uint2{lw[0], lw[1]};
     }
   };
+  // the accumulators into the next tile's scales (after the current tile's products)
+  auto rescale = [&]() {
+#pragma unroll
+    for (int h = 0; h < HW; ++h) {
+      const float fm = __builtin_amdgcn_ldexpf(f[h], rk + rv);
+#pragma unroll
+      for (int vt = 0; vt < 4; ++vt) accM[vt][h] *= fm;
+    }
+    // rows 0-3 (lanes < 32): o~ of head r % HW; rows 4-7 (lanes >= 32): kbar~ of head r
+#pragma unroll
+    for (int r = 0; r < 4; ++r) accX[r] *= __builtin_amdgcn_ldexpf(f[r % HW], l < 32 ? rv : rk);
+  };
+  // the thread's 32 bytes of the value tile in buffer buf: bf16 -> fp16 times 2^ev, in place
+  auto convert_v = [&](int buf) {
+    uint4* vp = reinterpret_cast<uint4*>(S.t.v[buf]);
+    const uint4 a = vp[tid], c = vp[tid + 512];
+    vp[tid] = uint4{bf16pair_to_f16(a.x, ev), bf16pair_to_f16(a.y, ev), bf16pair_to_f16(a.z, ev),
+                    bf16pair_to_f16(a.w, ev)};
+    vp[tid + 512] = uint4{bf16pair_to_f16(c.x, ev), bf16pair_to_f16(c.y, ev), bf16pair_to_f16(c.z, ev),
+                          bf16pair_to_f16(c.w, ev)};
+  };
 
-  // weight rows of the two o~ / kbar~ operands (columns 0 .. 2 HW - 1 and 4 .. 4 + 2 HW - 1; zero row 2 HW)
+  // weight rows of the o~ operand (rows 0 .. 2 HW - 1; zero row 2 HW for the rest)
   const int pw_row = min(l & 31, 2 * HW);
-  const int pw_row2 = (l & 31) >= 4 && (l & 31) < 4 + 2 * HW ? (l & 31) - 4 : 2 * HW;
   // the lane's rows and chunk offsets in the tile copies
   int lrow[2];
   uint32_t lchunk[2];
@@ -282,7 +380,7 @@ __global__ __launch_bounds__(512) void k_dec_moment(MomParams p) {
   for (int i = tid; i < 2 * (5 - 2 * HW) * kMT; i += 512)   // the zero rows of both buffers
     S.pw[i / ((5 - 2 * HW) * kMT)][2 * HW + (i / kMT) % (5 - 2 * HW)][i % kMT] = 0;
 
-  // ---- prologue: tiles 0, 1, 2 in flight, scores and weights of tile 0 ----
+  // ---- prologue: tiles 0, 1, 2 in flight; scores, scales, weights and values of tile 0 ----
   vm_wait_all();   // q and seqlens have arrived (no load of ours is in flight across the loop's waits)
 #pragma unroll
   for (int tt = 0; tt < 3; ++tt)
@@ -295,94 +393,100 @@ __global__ __launch_bounds__(512) void k_dec_moment(MomParams p) {
     }
     lds_barrier();
     if (w < 4) scores(0, 0);
+    else absmax(0, 0);
     lds_barrier();
-    weights(0);
+    decide(0);
+    if (w < 4) weights(0);
+    convert_v(0);
   }
 
   for (int t = 0; t < nt; ++t) {
     const int buf = t % kMBuf, nbuf = (t + 1) % kMBuf;
-    // tile t + 1 has arrived (tile t + 2 may still be in flight); every wave is done with tile t - 1
+    const bool next = t + 1 < nt;
+    // tile t + 1 has arrived (tile t + 2 may still be in flight); tile t's values are converted; every wave
+    // is done with tile t - 1
     if (t + 2 < nt) vm_wait4();
     else lds_dma_wait();
     lds_barrier();
     if (t + 3 < nt) mom_dma<PAGED>(p, S, (t + 3) % kMBuf, b, g, (t0 + t + 3) * kMT, hi, w, lrow, lchunk);
-    if (w < 4 && t + 1 < nt) scores(t + 1, nbuf);
-    // products of tile t: this wave's key half, two steps of 16 keys (ks = 2 kh, 2 kh + 1), each step once
-    // per head.  The bf16 pair y = p~ k of the next (step, head) is formed while the matrix cores run the
-    // current one's 8 products (the scheduling groups below interleave them).
-    const u16* kt = S.t.k[buf];
-    const u16* vt16 = S.t.v[buf];
+    // The next tile's scores (waves 0-3) or largest magnitudes (waves 4-7), then the products of tile t:
+    // this wave's key half, two steps of 16 keys, each step once per head.  The y of the next (step, head)
+    // is formed while the matrix cores run the current one's products (the scheduling groups below
+    // interleave them).
+    const u16* kb16 = S.t.k[buf] + kh * (32 * kD);
+    const u16* vb16 = S.t.v[buf] + kh * (32 * kD);
     const float* pt = &S.pt[t & 1][0][0];
     constexpr int NS = 2 * HW;
-    // y of (step i / HW, head i % HW) for the lane's 8 keys 16 ks + 8 (l / 32) + [0, 8) and K dim
-    // 32 ks_strip + l % 32 as a bf16 pair: hi = y truncated to bf16 (the top 16 bits), lo = the exact
-    // remainder (below 2^-7 |y|) rounded to bf16, so hi + lo is y to about 2^-16 relative.  `ak` returns the
-    // step's K operand (the A operand of kbar~).
-    auto ystep = [&](int i, bf16x8& yh, bf16x8& yl, bf16x8& ak) {
-      const int ks = 2 * kh + i / HW, h = i % HW;
-      ak = mom_cols(kt, loff, lj, ks, ks_strip);
-      const u32x4 kw = __builtin_bit_cast(u32x4, ak);
-      const int kk = 16 * ks + 8 * (l >> 5);
-      const float4 p0 = *reinterpret_cast<const float4*>(pt + h * kMT + kk);
-      const float4 p1 = *reinterpret_cast<const float4*>(pt + h * kMT + kk + 4);
-      const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-      u32x4 hw, lw;
+    // the K strip of step s: key 32 kh + 16 s + 8 (l / 32) + e, dim 32 ks_strip + l % 32, as floats
+    auto kload = [&](int s, float (&kf)[8]) {
+      const u32x4 kw = mom_cols(kb16 + s * (16 * kD), os);
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
-        const float y0 = pv[2 * e2] * __uint_as_float(kw[e2] << 16);
-        const float y1 = pv[2 * e2 + 1] * __uint_as_float(kw[e2] & 0xffff0000u);
-        const uint32_t b0 = __float_as_uint(y0), b1 = __float_as_uint(y1);
-        hw[e2] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);   // the high halves of y0 (low) and y1 (high)
-        const f32x2 r = {y0 - __uint_as_float(b0 & 0xffff0000u), y1 - __uint_as_float(b1 & 0xffff0000u)};
-        lw[e2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
+        kf[2 * e2] = __uint_as_float(kw[e2] << 16);
+        kf[2 * e2 + 1] = __uint_as_float(kw[e2] & 0xffff0000u);
       }
-      yh = __builtin_bit_cast(bf16x8, hw);
-      yl = __builtin_bit_cast(bf16x8, lw);
     };
-    bf16x8 yh, yl, akc;
-    ystep(0, yh, yl, akc);
-    bf16x8 av[4], avs, bo, bo2;
+    // y = fp16(p~ 2^ek k) of (step s, head h)
+    auto yform = [&](int s, int h, const float (&kf)[8]) {
+      const int kk = 32 * kh + 16 * s + 8 * (l >> 5);
+      const float4 p0 = *reinterpret_cast<const float4*>(pt + h * kMT + kk);
+      const float4 p1 = *reinterpret_cast<const float4*>(pt + h * kMT + kk + 4);
+      const f32x2 y01 = {p0.x * kf[0], p0.y * kf[1]}, y23 = {p0.z * kf[2], p0.w * kf[3]};
+      const f32x2 y45 = {p1.x * kf[4], p1.y * kf[5]}, y67 = {p1.z * kf[6], p1.w * kf[7]};
+      const f16x2 a = __builtin_convertvector(y01, f16x2), c = __builtin_convertvector(y23, f16x2);
+      const f16x2 d = __builtin_convertvector(y45, f16x2), e = __builtin_convertvector(y67, f16x2);
+      const f16x4 ac = __builtin_shufflevector(a, c, 0, 1, 2, 3), de = __builtin_shufflevector(d, e, 0, 1, 2, 3);
+      return __builtin_shufflevector(ac, de, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    if (next) {
+      if (w < 4) scores(t + 1, nbuf);
+      else absmax(t + 1, nbuf);
+    }
+    float kf[8];
+    kload(0, kf);
+    f16x8 y = yform(0, 0, kf);
+    f16x8 av[4], avs, wo;
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      const int ks = 2 * kh + i / HW, h = i % HW;
+      const int s = i / HW, h = i % HW;
       if (h == 0) {
 #pragma unroll
-        for (int vt = 0; vt < 4; ++vt) av[vt] = mom_cols(vt16, loff, lj, ks, vt);
-        avs = mom_cols(vt16, loff, lj, ks, ks_strip);
-        // B operands of o~ and kbar~: the weight rows (hi, lo per head, zeros) of the lane's column
-        const int kk = 16 * ks + 8 * (l >> 5);
-        bo = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&S.pw[t & 1][pw_row][kk]));
-        bo2 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&S.pw[t & 1][pw_row2][kk]));
+        for (int vt = 0; vt < 4; ++vt) av[vt] = __builtin_bit_cast(f16x8, mom_cols(vb16 + s * (16 * kD), ov[vt]));
+        avs = __builtin_bit_cast(f16x8, mom_cols(vb16 + s * (16 * kD), os));
+        // A operand of o~: the weight rows (hi, lo per head, zeros) of the lane's row
+        wo = __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(
+                                           &S.pw[t & 1][pw_row][32 * kh + 16 * s + 8 * (l >> 5)]));
       }
       __builtin_amdgcn_sched_barrier(0);
-      // (hi products first, so that two products into one accumulator are not back to back)
+      if (h == 0) accX = mfma(wo, avs, accX);
 #pragma unroll
-      for (int vt = 0; vt < 4; ++vt)
-        accM[vt][h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[vt], yh, accM[vt][h], 0, 0, 0);
-      if (h == 0) accX = __builtin_amdgcn_mfma_f32_32x32x16_bf16(avs, bo, accX, 0, 0, 0);
-#pragma unroll
-      for (int vt = 0; vt < 4; ++vt)
-        accM[vt][h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[vt], yl, accM[vt][h], 0, 0, 0);
-      if (h == 0) accX = __builtin_amdgcn_mfma_f32_32x32x16_bf16(akc, bo2, accX, 0, 0, 0);
+      for (int vt = 0; vt < 4; ++vt) accM[vt][h] = mfma(av[vt], y, accM[vt][h]);
+      accX = mfma(ones[h], y, accX);
       if (i + 1 < NS) {
-        bf16x8 yh2, yl2, ak2;
-        ystep(i + 1, yh2, yl2, ak2);
+        const int s2 = (i + 1) / HW, h2 = (i + 1) % HW;
+        if (h2 == 0) kload(s2, kf);
+        const f16x8 y2 = yform(s2, h2, kf);
         // the next step's LDS reads first, then each product followed by a share of the VALU work
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 6; ++j) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        yh = yh2;
-        yl = yl2;
-        akc = ak2;
+        y = y2;
       }
     }
-    lds_barrier();   // the next tile's maxima are in LDS
-    if (t + 1 < nt) weights(t + 1);
+    lds_barrier();   // the next tile's maxima are in LDS; every wave is done with tile t's values
+    if (next) {
+      decide(t + 1);
+      if (any) rescale();   // (uniform)
+      if (w < 4) weights(t + 1);
+      convert_v(nbuf);
+    }
   }
+  // every wave is done with the tile buffers, which the epilogue reuses
+  lds_barrier();
 
   // ---- epilogue ----
   // the two key halves of each partial: o~ and kbar~ through LDS, M added in place
@@ -391,22 +495,17 @@ __global__ __launch_bounds__(512) void k_dec_moment(MomParams p) {
     lp += __shfl_xor(lp, 16, 64);
     lp += __shfl_xor(lp, 32, 64);
     if (w < 4 && l < HW) S.lsum[w][l] = lp;
-    // o~ of value tile ks_strip: accumulator row 8 (r / 4) + 4 (l / 32) + r % 4 of column l % 32; the hi
-    // and lo columns of a head are HW lanes apart
-    const int n = l & 31;
+    // accX row 4 (l / 32) + r of column l % 32 (r < 4): o~ of head h = rows h (hi) and HW + h (lo) in lanes
+    // < 32, kbar~ of head h = row 4 + h in lanes >= 32
+    const int col = 32 * ks_strip + (l & 31);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float other = __shfl(accX[r], l + HW, 64);
-      if (n < HW) S.opart[kh][n][32 * ks_strip + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3)] = accX[r] + other;
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {   // kbar~ of K strip ks_strip: columns 4 + h and 4 + HW + h
-      const float other = __shfl(accX[r], l + HW, 64);
-      if (n >= 4 && n < 4 + HW) S.kpart[kh][n - 4][32 * ks_strip + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3)] = accX[r] + other;
+    for (int h = 0; h < HW; ++h) {
+      if (l < 32) S.opart[kh][h][col] = accX[h] + accX[HW + h];
+      else S.kpart[kh][h][col] = accX[h];
     }
   }
   // the moment: the second key half writes its partial (the tile buffers are free: every copy has completed
-  // and every wave has passed the loop's last barrier after its last read)
+  // and every wave has passed the barrier after the loop)
   auto mrow_of = [&](int vt, int r) { return 32 * vt + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3); };
   if (kh == 1) {
 #pragma unroll
@@ -433,8 +532,8 @@ __global__ __launch_bounds__(512) void k_dec_moment(MomParams p) {
   if (eh < HW) {
     const float ln = eh == 0 ? Lh[0] : Lh[HW - 1];
     const float inv = ln > 0.f ? 1.f / ln : 0.f;
-    S.vec[0][eh][ea] = (S.opart[0][eh][ea] + S.opart[1][eh][ea]) * inv;
-    S.vec[1][eh][ea] = (S.kpart[0][eh][ea] + S.kpart[1][eh][ea]) * inv;
+    S.vec[0][eh][ea] = __builtin_amdgcn_ldexpf(S.opart[0][eh][ea] + S.opart[1][eh][ea], -ev) * inv;
+    S.vec[1][eh][ea] = __builtin_amdgcn_ldexpf(S.kpart[0][eh][ea] + S.kpart[1][eh][ea], -ek) * inv;
   }
   __syncthreads();
   // u = P^T (q - kbar) and alpha = u . kbar
@@ -461,7 +560,7 @@ __global__ __launch_bounds__(512) void k_dec_moment(MomParams p) {
 #pragma unroll 8
     for (int bb = 0; bb < kD; ++bb) mu = fmaf(S.M[eh][ea][bb], S.vec[2][eh][bb], mu);
     const float o = S.vec[0][eh][ea];
-    const float cval = mu * inv - alpha * o;
+    const float cval = __builtin_amdgcn_ldexpf(mu, -(ek + ev)) * inv - alpha * o;
     const float r = o + cval;
     const int64_t oi = (static_cast<int64_t>(b) * p.Hq + h0 + eh) * kD + ea;
     if (p.out_bf16) static_cast<u16*>(p.out)[oi] = static_cast<u16>(f32_to_bf16(r));

@@ -225,6 +225,75 @@ def test_full_size_decode_moment_vs_two_pass(plx):
     assert err <= BF16_TOL
 
 
+def _pow2(x, e):
+    """x * 2^e exactly (bf16 keeps its significand; the exponents used here stay in range)."""
+    return (x.float() * (2.0 ** e)).to(x.dtype)
+
+
+@pytest.mark.parametrize("c", [20, -20])
+def test_moment_decode_value_scale_is_exact(plx, c):
+    """out is linear in V and the kernel's value scale is a power of two set from the data: V * 2^c gives
+    out * 2^c bit for bit."""
+    _announce(f"single-read decode: V * 2^{c}")
+    w = W.scaled(W.WORKLOADS["decode"], batch=32, seqlen_k=400, heads_q=16, heads_kv=8)
+    q, kc, vc, P = W.make_inputs(w, device="cuda", seed=11)
+    seqlens = _seqlens(32, 400, seed=2)
+    hook = _Hook(plx, plx.PLX_KERNEL_DECODE_MOMENT)
+    try:
+        with hook:
+            out = plx.parallax_attn_decode(q, kc, vc, P, seqlens=seqlens)
+        assert hook.ran(), "the single-read kernel did not run"
+    finally:
+        hook.close()
+    outs = plx.parallax_attn_decode(q, kc, _pow2(vc, c), P, seqlens=seqlens)
+    torch.cuda.synchronize()
+    assert torch.equal(outs, out * 2.0 ** c)
+
+
+@pytest.mark.parametrize("a", [10, -10])
+def test_moment_decode_score_preserving_scale_is_exact(plx, a):
+    """(q, k, P, softmax scale) -> (2^a q, 2^a k, 2^-2a P, 2^-2a scale) leaves every score and the output
+    unchanged; the key scale follows k, so the output is the same bit for bit."""
+    _announce(f"single-read decode: (q, k, P, scale) * (2^{a}, 2^{a}, 2^{-2 * a}, 2^{-2 * a})")
+    w = W.scaled(W.WORKLOADS["decode"], batch=32, seqlen_k=400, heads_q=16, heads_kv=8)
+    q, kc, vc, P = W.make_inputs(w, device="cuda", seed=12)
+    seqlens = _seqlens(32, 400, seed=3)
+    scale = 128 ** -0.5
+    out = plx.parallax_attn_decode(q, kc, vc, P, seqlens=seqlens, scale=scale)
+    outs = plx.parallax_attn_decode(_pow2(q, a), _pow2(kc, a), vc, _pow2(P, -2 * a), seqlens=seqlens,
+                                    scale=scale * 2.0 ** (-2 * a))
+    torch.cuda.synchronize()
+    assert torch.equal(outs, out)
+
+
+@pytest.mark.parametrize("which,e", [("V", 12), ("V", 20), ("K", 6)])
+def test_moment_decode_outlier_rows(plx, which, e):
+    """The last two keys of every sequence 2^e larger than the rest (values or keys): the value scale then
+    puts the other values 2^e lower in fp16 (still in its normal range), and a key tile's scale follows its
+    largest key; against the oracle at the usual bar.
+
+    Keys 2^12 larger are outside this kernel's range: such a key dominates its softmax, kbar is close to
+    it, and out - o is the difference of M u / l and alpha o, each about |u . k| |v| (2^24 times the
+    typical size there), so fp32's rounding of the two alone exceeds the bar.  The two-pass kernels,
+    which form k_j - kbar before the product, cover that case (the range tests run it there)."""
+    _announce(f"single-read decode: outlier {which} rows * 2^{e}")
+    B, L = 32, 500
+    w = W.scaled(W.WORKLOADS["decode"], batch=B, seqlen_k=L, heads_q=16, heads_kv=8)
+    q, kc, vc, P = W.make_inputs(w, device="cuda", seed=13)
+    t = (vc if which == "V" else kc).clone()
+    t[:, L - 2:] = _pow2(t[:, L - 2:], e)
+    if which == "V":
+        vc = t
+    else:
+        kc = t
+    out = plx.parallax_attn_decode(q, kc, vc, P)
+    torch.cuda.synchronize()
+    ref = _decode_ref(q, kc, vc, P, [L] * B, 0)
+    err = rel_err(host(out), ref)
+    print(f"[moment] outlier {which} 2^{e}: err {err:.2e}", flush=True)
+    assert err <= BF16_TOL
+
+
 def test_moment_decode_selection(plx):
     """Below 256 (sequence, key/value head) pairs, with more than two query heads per key/value head, with
     several new tokens or with pages under 64 keys the two-pass kernels run instead."""
