@@ -521,11 +521,12 @@ def main():
         kms1, kms2 = sum(p1) / len(p1), sum(p2) / len(p2)
         t1, t2 = measured_traffic("decode_pass1"), measured_traffic("decode_pass2")
         gbs = alg / (kms_m * 1e-3) / 1e9
-        # matrix-core work of the single-read kernel as executed: per (key, query head) the moment's
-        # 2 d^2 twice (hi and lo halves of p k), o~ and kbar~ (2 d each, hi and lo weights share one
-        # product), the score (2 d)
+        # matrix-core work of the single-read kernel as executed: per (key, query head) the moment's 2 d^2
+        # and kbar~ (a 32-row ones operand against y: 64 d); per key and kv head o~ (32 weight rows against
+        # the values: 64 d) and the scores (16 padded columns: 32 d)
         d = wd.head_dim
-        mfma_flop = keys * (4 * d * d + 4 * d + 2 * d)
+        G = wd.heads_q // wd.heads_kv
+        mfma_flop = keys * (2 * d * d + 64 * d) + keys // G * (64 * d + 32 * d)
         result["decode"] = {
             "workload": f"decode: B={wd.batch} new queries, cache L={wd.seqlen_k}, Hq={wd.heads_q}, "
                         f"Hkv={wd.heads_kv}, d={wd.head_dim}, bf16",
