@@ -31,9 +31,9 @@
 // 16-byte chunks of row r permuted (slot = chunk ^ f(r)) so that the transpose loads (ds_read_b64_tr_b16)
 // that form the k-major operands, and the row loads of the scores, hit distinct banks.  In the phase that runs
 // the current tile's products, waves 0-3 first compute the next tile's scores (16 keys each,
-// v_mfma_f32_16x16x32_bf16) and waves 4-7 its largest |k| and |v| (so the two waves of each SIMD bring
-// different work); after a barrier every wave sets the next tile's scales, waves 0-3 its weights, and all
-// waves convert their share of its values.  The running
+// v_mfma_f32_16x16x32_bf16) and its largest |k|, waves 4-7 its largest |v|; after a barrier every wave
+// sets the next tile's scales, waves 0-3 its weights (one key and head per lane), and all waves convert
+// their share of its values.  The running
 // maximum is lazy (it moves only when a tile exceeds it by 8 in log2 units).
 #include <math.h>
 
@@ -85,7 +85,7 @@ struct __align__(16) MomShared {
   float pt[2][2][kMT];         // p~ 2^ek of a tile per (buffer, head, key)
   u16 pw[2][5][kMT];           // p~ as fp16 pairs per (buffer, row, key): rows h = hi, HW + h = lo, 2 HW = 0
   float smax[2][2][16];        // per (buffer, head, 4 score wave + lane row): the largest of 4 keys (log2 units)
-  uint32_t amax[2][4];         // per (buffer, wave 4-7): largest |k| (low half) and |v| (high half) as bf16 bits
+  uint32_t amax[2][8];         // per (buffer, wave): largest |k| (waves 0-3, low half) or |v| (4-7, high half)
   float lsum[4][2];
   float vec[3][2][kD];         // epilogue: o, kbar, u per head
   float opart[2][2][kD];       // epilogue: o~ and kbar~ per (key half, head)
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(512) void k_dec_moment(MomParams p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) ones[h][e] = (l & 31) == 4 + h ? static_cast<_Float16>(1.f) : static_cast<_Float16>(0.f);
   float m_run[2] = {-INFINITY, -INFINITY};
-  float lpart = 0.f;   // waves 0-3, lanes l % 16 < HW: weights of head l % 16
+  float lpart = 0.f;   // waves 0-3, lanes l < 16 HW: weights of head l / 16 (keys l % 16 of the wave's 16)
   int ek = kEk0, ev = kEv0;   // the current scales' exponents (wave-uniform)
 
   // scores of tile `tile` (waves 0-3) -> their keys' values and each lane's maximum (4 keys) in LDS
@@ -262,22 +262,20 @@ __global__ __launch_bounds__(512) void k_dec_moment(MomParams p) {
     S.sc[w & 3][l] = sc;   // (in LDS across the products, not in registers)
     if ((l & 15) < HW) S.smax[tile & 1][l & 15][4 * (w & 3) + (l >> 4)] = mx;
   };
-  // largest |k| and |v| of the tile in buffer buf (waves 4-7: 64 bytes of each per thread), as bf16 bits
+  // largest |k| (waves 0-3) or |v| (waves 4-7) of the tile in buffer buf as bf16 bits, 64 bytes per thread;
+  // kept in the low (k) or high (v) half of the wave's entry
   auto absmax = [&](int tile, int buf) {
-    const int j = tid - 256;
-    const uint4* kp = reinterpret_cast<const uint4*>(S.t.k[buf]);
-    const uint4* vp = reinterpret_cast<const uint4*>(S.t.v[buf]);
-    uint32_t mk = 0u, mv = 0u;
+    const int j = tid & 255;
+    const uint4* src = reinterpret_cast<const uint4*>(w < 4 ? S.t.k[buf] : S.t.v[buf]);
+    uint32_t m = 0u;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const uint4 a = kp[j + 256 * r], c = vp[j + 256 * r];
-      mk = pkmax(pkmax(mk, a.x & 0x7fff7fffu), pkmax(a.y & 0x7fff7fffu, pkmax(a.z & 0x7fff7fffu, a.w & 0x7fff7fffu)));
-      mv = pkmax(pkmax(mv, c.x & 0x7fff7fffu), pkmax(c.y & 0x7fff7fffu, pkmax(c.z & 0x7fff7fffu, c.w & 0x7fff7fffu)));
+      const uint4 a = src[j + 256 * r];
+      m = pkmax(pkmax(m, a.x & 0x7fff7fffu), pkmax(a.y & 0x7fff7fffu, pkmax(a.z & 0x7fff7fffu, a.w & 0x7fff7fffu)));
     }
-    // low half: k, high half: v
-    uint32_t x = pkmax(__builtin_amdgcn_perm(mv, mk, 0x05040100u), __builtin_amdgcn_perm(mv, mk, 0x07060302u));
-    x = pkmax_wave63(x);
-    if (l == 63) S.amax[tile & 1][w - 4] = x;
+    m = pkmax_wave63(m);
+    const uint32_t m1 = max(m & 0xffffu, m >> 16);
+    if (l == 63) S.amax[tile & 1][w] = w < 4 ? m1 : m1 << 16;
   };
   // after the barrier that publishes a tile's maxima (the same values in every wave, kept in scalar
   // registers): its scales, the lazy running maximum, and the factors f (per head) that the accumulators
@@ -287,8 +285,10 @@ __global__ __launch_bounds__(512) void k_dec_moment(MomParams p) {
   bool any = false;
   auto decide = [&](int tile) {
     {
-      const uint4 a = *reinterpret_cast<const uint4*>(S.amax[tile & 1]);
-      const uint32_t x = __builtin_amdgcn_readfirstlane(pkmax(pkmax(a.x, a.y), pkmax(a.z, a.w)));
+      const uint4 a = *reinterpret_cast<const uint4*>(&S.amax[tile & 1][0]);
+      const uint4 c = *reinterpret_cast<const uint4*>(&S.amax[tile & 1][4]);
+      const uint32_t x = __builtin_amdgcn_readfirstlane(
+          pkmax(pkmax(pkmax(a.x, a.y), pkmax(a.z, a.w)), pkmax(pkmax(c.x, c.y), pkmax(c.z, c.w))));
       const int kb = static_cast<int>(x & 0xffffu), vb = static_cast<int>(x >> 16);
       // largest magnitude below 2^(E + 1) (E = biased exponent - 127; subnormals as E = -126)
       const int nk = kb ? min(ek, 133 - max(kb >> 7, 1)) : ek;   // |k| 2^ek < 2^7
@@ -314,35 +314,25 @@ __global__ __launch_bounds__(512) void k_dec_moment(MomParams p) {
       }
     }
   };
-  // (waves 0-3) the tile's weights into LDS and the running sums l
+  // (waves 0-3) the tile's weights into LDS and the running sums l: lane l < 16 HW takes key 16 w + l % 16
+  // of head l / 16 (its scaled score is element key % 4 of lane 16 (key / 4) + head of the scores)
   auto weights = [&](int tile) {
-    const int n = l & 15;
-    lpart *= (HW == 2 && n == 1) ? f[HW - 1] : f[0];
-    if (n < HW) {
-      const float mr = n == 0 ? m_run[0] : m_run[HW - 1];
+    const int kq = l & 15, n = (l >> 4) & 1;
+    const float fl = n ? f[HW - 1] : f[0];
+    lpart *= fl;
+    if (l < 16 * HW) {
+      const float mr = n ? m_run[HW - 1] : m_run[0];
       const float mb = mr == -INFINITY ? 0.f : mr;
-      const f32x4 sc = S.sc[w][l];
-      float e[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        e[r] = sc[r] == -INFINITY ? 0.f : exp2f(sc[r] - mb);
-        lpart += e[r];
-      }
-      const int k4 = 16 * w + 4 * (l >> 4);
-      *reinterpret_cast<float4*>(&S.pt[tile & 1][n][k4]) =
-          float4{__builtin_amdgcn_ldexpf(e[0], ek), __builtin_amdgcn_ldexpf(e[1], ek),
-                 __builtin_amdgcn_ldexpf(e[2], ek), __builtin_amdgcn_ldexpf(e[3], ek)};
-      // the weights as fp16 pairs hi + lo: rows n and HW + n of the o~ operand
-      uint32_t hw[2], lw[2];
-#pragma unroll
-      for (int r = 0; r < 4; r += 2) {
-        const f16x2 hv = __builtin_convertvector((f32x2{e[r], e[r + 1]}), f16x2);
-        const f32x2 rem = {e[r] - static_cast<float>(hv[0]), e[r + 1] - static_cast<float>(hv[1])};
-        hw[r / 2] = __builtin_bit_cast(uint32_t, hv);
-        lw[r / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rem, f16x2));
-      }
-      *reinterpret_cast<uint2*>(&S.pw[tile & 1][n][k4]) = uint2{hw[0], hw[1]};
-      *reinterpret_cast<uint2*>(&S.pw[tile & 1][HW + n][k4]) = uint2{lw[0], lw[1]};
+      const float sc = reinterpret_cast<const float*>(&S.sc[w][16 * (kq >> 2) + n])[kq & 3];
+      const float e = sc == -INFINITY ? 0.f : exp2f(sc - mb);
+      lpart += e;
+      const int key = 16 * w + kq;
+      S.pt[tile & 1][n][key] = __builtin_amdgcn_ldexpf(e, ek);
+      // the weight as an fp16 pair hi + lo: rows n and HW + n of the o~ operand
+      const _Float16 hv = static_cast<_Float16>(e);
+      const _Float16 lv = static_cast<_Float16>(e - static_cast<float>(hv));
+      S.pw[tile & 1][n][key] = __builtin_bit_cast(u16, hv);
+      S.pw[tile & 1][HW + n][key] = __builtin_bit_cast(u16, lv);
     }
   };
   // the accumulators into the next tile's scales (after the current tile's products)
@@ -393,7 +383,7 @@ __global__ __launch_bounds__(512) void k_dec_moment(MomParams p) {
     }
     lds_barrier();
     if (w < 4) scores(0, 0);
-    else absmax(0, 0);
+    absmax(0, 0);
     lds_barrier();
     decide(0);
     if (w < 4) weights(0);
@@ -409,7 +399,7 @@ __global__ __launch_bounds__(512) void k_dec_moment(MomParams p) {
     else lds_dma_wait();
     lds_barrier();
     if (t + 3 < nt) mom_dma<PAGED>(p, S, (t + 3) % kMBuf, b, g, (t0 + t + 3) * kMT, hi, w, lrow, lchunk);
-    // The next tile's scores (waves 0-3) or largest magnitudes (waves 4-7), then the products of tile t:
+    // The next tile's scores (waves 0-3) and largest magnitudes, then the products of tile t:
     // this wave's key half, two steps of 16 keys, each step once per head.  The y of the next (step, head)
     // is formed while the matrix cores run the current one's products (the scheduling groups below
     // interleave them).
@@ -440,7 +430,7 @@ __global__ __launch_bounds__(512) void k_dec_moment(MomParams p) {
     };
     if (next) {
       if (w < 4) scores(t + 1, nbuf);
-      else absmax(t + 1, nbuf);
+      absmax(t + 1, nbuf);
     }
     float kf[8];
     kload(0, kf);
@@ -492,9 +482,9 @@ __global__ __launch_bounds__(512) void k_dec_moment(MomParams p) {
   // the two key halves of each partial: o~ and kbar~ through LDS, M added in place
   {
     float lp = lpart;
-    lp += __shfl_xor(lp, 16, 64);
-    lp += __shfl_xor(lp, 32, 64);
-    if (w < 4 && l < HW) S.lsum[w][l] = lp;
+#pragma unroll
+    for (int o2 = 1; o2 < 16; o2 <<= 1) lp += __shfl_xor(lp, o2, 64);
+    if (w < 4 && (l & 15) == 0 && l < 16 * HW) S.lsum[w][l >> 4] = lp;
     // accX row 4 (l / 32) + r of column l % 32 (r < 4): o~ of head h = rows h (hi) and HW + h (lo) in lanes
     // < 32, kbar~ of head h = row 4 + h in lanes >= 32
     const int col = 32 * ks_strip + (l & 31);
