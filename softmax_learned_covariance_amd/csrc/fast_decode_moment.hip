@@ -13,7 +13,9 @@
 // the values accumulated: each of the two terms is of size |u . k| |v| and they cancel, and a kbar from
 // unrounded products would leave the rounding of p~ k times that size.  The correction of the definition,
 // sum_j p_j (u . (k_j - kbar))(v_j - o), differs from it only through the rounding of y (fp16: 2^-11
-// relative per element).
+// relative per element).  Where the two terms exceed the output by more than 2^11 (a key far larger than the
+// rest dominates), fp32 alone would lose the difference; such a head's correction is then formed directly
+// from a second read of its keys.
 //
 // M costs 2 d^2 flop per key and head, far more than the two-pass form, so it runs on the matrix cores:
 // per 16 keys and head, M += V^T Y on v_mfma_f32_32x32x16_f16, plus one product for kbar~ (a ones row
@@ -79,6 +81,10 @@ struct __align__(16) MomShared {
       u16 v[kMBuf][kMT * kD];   // bf16 as copied, then fp16 times 2^ev (converted in place)
     } t;
     float M[2][kD][kD + 1];    // epilogue: the moment of each query head, rows padded against bank conflicts
+    struct {
+      float wj[512];        // p_j u.(k_j - kbar) of a batch of 512 keys
+      float cacc[4][kD];    // the correction's partial sums per quarter of a batch
+    } fb;                   // epilogue, after M: the direct correction of a head (see there)
   };
   uint4 qb[4][64];             // score operands (bf16 q) per (step, lane)
   f32x4 sc[4][64];             // scaled scores of the next tile per (score wave, lane), between the two phases
@@ -90,7 +96,8 @@ struct __align__(16) MomShared {
   float vec[3][2][kD];         // epilogue: o, kbar, u per head
   float opart[2][2][kD];       // epilogue: o~ and kbar~ per (key half, head)
   float kpart[2][2][kD];
-  float red[3][2][2];   // per (quantity, head, wave of the head)
+  float red[5][2][2];   // per (quantity, head, wave of the head)
+  float qf[2][kD];      // epilogue: q per head, fp32
 };
 
 // Chunk permutation of row r within a tile (an involution on 0..15): slot = chunk ^ f(r).
@@ -142,6 +149,11 @@ __device__ __forceinline__ u32x4 mom_cols(const u16* base, const int (&o)[2]) {
   const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(base + o[0]));
   const s16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(base + o[1]));
   return __builtin_bit_cast(u32x4, __builtin_shufflevector(a, c, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// A wave-uniform float as the scalar register it is.
+__device__ __forceinline__ float uniform_f(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
 }
 
 // Largest of each 16-bit half (unsigned), and its wave-wide reduction (every lane gets the result).
@@ -318,10 +330,12 @@ __global__ __launch_bounds__(512) void k_dec_moment(MomParams p) {
   // of head l / 16 (its scaled score is element key % 4 of lane 16 (key / 4) + head of the scores)
   auto weights = [&](int tile) {
     const int kq = l & 15, n = (l >> 4) & 1;
-    const float fl = n ? f[HW - 1] : f[0];
+    // (the per-lane choice between two uniform values, each read first as a scalar: a select between two
+    // elements of a register array would become an indexed access, which the compiler moves to LDS)
+    const float fl = n ? uniform_f(f[HW - 1]) : uniform_f(f[0]);
     lpart *= fl;
     if (l < 16 * HW) {
-      const float mr = n ? m_run[HW - 1] : m_run[0];
+      const float mr = n ? uniform_f(m_run[HW - 1]) : uniform_f(m_run[0]);
       const float mb = mr == -INFINITY ? 0.f : mr;
       const float sc = reinterpret_cast<const float*>(&S.sc[w][16 * (kq >> 2) + n])[kq & 3];
       const float e = sc == -INFINITY ? 0.f : exp2f(sc - mb);
@@ -536,12 +550,18 @@ __global__ __launch_bounds__(512) void k_dec_moment(MomParams p) {
     for (int bb = 0; bb < kD; ++bb)
       uval = fmaf(bf16_to_f32(Ph[bb * kD + ea]), bf16_to_f32(qrow[bb]) - S.vec[1][eh][bb], uval);   // u[a] = sum_b P[b][a] x[b]
     aval = uval * S.vec[1][eh][ea];
+    S.qf[eh][ea] = bf16_to_f32(qrow[ea]);
 #pragma unroll
     for (int o2 = 32; o2 > 0; o2 >>= 1) aval += __shfl_xor(aval, o2, 64);
     if (l == 0) S.red[0][eh][(tid >> 6) & 1] = aval;
     S.vec[2][eh][ea] = uval;
   }
   __syncthreads();
+  // The moment form: c = M u / l - alpha o.  Its two terms are each about |u . k| |v| and cancel; when they
+  // exceed the output by more than 2^11 (a key far larger than the rest dominates the softmax, so kbar is
+  // close to it), fp32's rounding of their difference would show, and the head's correction is formed
+  // directly instead, c = sum_j p_j (u . (k_j - kbar)) (v_j - o), from a second read of its keys.
+  float cval = 0.f, oval = 0.f;
   if (eh < HW) {
     const float alpha = S.red[0][eh][0] + S.red[0][eh][1];
     const float ln = eh == 0 ? Lh[0] : Lh[HW - 1];
@@ -549,9 +569,67 @@ __global__ __launch_bounds__(512) void k_dec_moment(MomParams p) {
     float mu = 0.f;
 #pragma unroll 8
     for (int bb = 0; bb < kD; ++bb) mu = fmaf(S.M[eh][ea][bb], S.vec[2][eh][bb], mu);
-    const float o = S.vec[0][eh][ea];
-    const float cval = __builtin_amdgcn_ldexpf(mu, -(ek + ev)) * inv - alpha * o;
-    const float r = o + cval;
+    oval = S.vec[0][eh][ea];
+    const float mterm = __builtin_amdgcn_ldexpf(mu, -(ek + ev)) * inv;
+    cval = mterm - alpha * oval;
+    float cm = fabsf(mterm) + fabsf(alpha * oval), om = fabsf(oval + cval);
+#pragma unroll
+    for (int o2 = 32; o2 > 0; o2 >>= 1) {
+      cm = fmaxf(cm, __shfl_xor(cm, o2, 64));
+      om = fmaxf(om, __shfl_xor(om, o2, 64));
+    }
+    if (l == 0) {
+      S.red[3][eh][(tid >> 6) & 1] = cm;
+      S.red[4][eh][(tid >> 6) & 1] = om;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < HW; ++h) {
+    const float cm = fmaxf(S.red[3][h][0], S.red[3][h][1]), om = fmaxf(S.red[4][h][0], S.red[4][h][1]);
+    if (!(cm > om * 2048.f)) continue;   // (uniform)
+    const float mh = uniform_f(h == 0 ? m_run[0] : m_run[HW - 1]), lh = h == 0 ? Lh[0] : Lh[HW - 1];
+    const float inv = lh > 0.f ? 1.f / lh : 0.f;
+    const int a = tid & 127, part = tid >> 7;
+    float acc = 0.f;
+    for (int j0 = lo; j0 < hi; j0 += 512) {
+      // the weight of key j0 + tid: its score and u . (k - kbar) in fp32 from the cache row
+      const int j = j0 + tid;
+      float wv = 0.f;
+      if (j < hi) {
+        const int64_t row = PAGED ? mrow<true>(p, b, j) : static_cast<int64_t>(b) * p.L + j;
+        const u16* kr = p.kc + (row * p.Hkv + g) * kD;
+        float sc = 0.f, t = 0.f;
+        for (int d0 = 0; d0 < kD; d0 += 8) {
+          const u32x4 kw = __builtin_bit_cast(u32x4, *reinterpret_cast<const uint4*>(kr + d0));
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float kv = __uint_as_float(e & 1 ? kw[e >> 1] & 0xffff0000u : kw[e >> 1] << 16);
+            sc = fmaf(S.qf[h][d0 + e], kv, sc);
+            t = fmaf(S.vec[2][h][d0 + e], kv - S.vec[1][h][d0 + e], t);
+          }
+        }
+        wv = exp2f(sc * c2 - mh) * inv * t;
+      }
+      S.fb.wj[tid] = wv;
+      __syncthreads();
+      // this thread's value dim a over its quarter of the batch
+      const int jq = j0 + 128 * part;
+      const int nq = min(128, hi - jq);   // (the same in both waves of the quarter)
+      const float oa = S.vec[0][h][a];
+      for (int jj = 0; jj < nq; ++jj) {
+        const int64_t row = PAGED ? mrow<true>(p, b, jq + jj) : static_cast<int64_t>(b) * p.L + jq + jj;
+        const float vv = bf16_to_f32(p.vc[(row * p.Hkv + g) * kD + a]);
+        acc = fmaf(S.fb.wj[128 * part + jj], vv - oa, acc);
+      }
+      __syncthreads();
+    }
+    S.fb.cacc[part][a] = acc;
+    __syncthreads();
+    if (eh == h) cval = S.fb.cacc[0][ea] + S.fb.cacc[1][ea] + S.fb.cacc[2][ea] + S.fb.cacc[3][ea];
+  }
+  if (eh < HW) {
+    const float r = oval + cval;
     const int64_t oi = (static_cast<int64_t>(b) * p.Hq + h0 + eh) * kD + ea;
     if (p.out_bf16) static_cast<u16*>(p.out)[oi] = static_cast<u16>(f32_to_bf16(r));
     else static_cast<float*>(p.out)[oi] = r;

@@ -266,16 +266,15 @@ def test_moment_decode_score_preserving_scale_is_exact(plx, a):
     assert torch.equal(outs, out)
 
 
-@pytest.mark.parametrize("which,e", [("V", 12), ("V", 20), ("K", 6)])
+@pytest.mark.parametrize("which,e", [("V", 12), ("V", 20), ("K", 6), ("K", 12), ("K", 20)])
 def test_moment_decode_outlier_rows(plx, which, e):
     """The last two keys of every sequence 2^e larger than the rest (values or keys): the value scale then
     puts the other values 2^e lower in fp16 (still in its normal range), and a key tile's scale follows its
     largest key; against the oracle at the usual bar.
 
-    Keys 2^12 larger are outside this kernel's range: such a key dominates its softmax, kbar is close to
-    it, and out - o is the difference of M u / l and alpha o, each about |u . k| |v| (2^24 times the
-    typical size there), so fp32's rounding of the two alone exceeds the bar.  The two-pass kernels,
-    which form k_j - kbar before the product, cover that case (the range tests run it there)."""
+    Keys 2^12 and more larger dominate their softmax, so kbar is close to them and the moment form's
+    M u / l and alpha o are each far larger than their difference; the kernel detects that and forms
+    those heads' corrections directly from a second read of their keys."""
     _announce(f"single-read decode: outlier {which} rows * 2^{e}")
     B, L = 32, 500
     w = W.scaled(W.WORKLOADS["decode"], batch=B, seqlen_k=L, heads_q=16, heads_kv=8)
