@@ -253,9 +253,12 @@ size_t parallax_attn_decode_workspace(const plx_attn_desc* desc);
  *   cor      [B][T][Hq] fp32 correction-to-output ratio as in the forward (nullable; bf16 fast path only)
  * Kernels.  With T = 1, bf16, head_dim 128, heads_q / heads_kv of 1 or 2 and at least 256 (sequence, kv
  * head) pairs, one workgroup per pair reads its cache rows once: it accumulates o, kbar and the
- * softmax-weighted moment sum_j p_j v_j k_j^T (fp32, on the matrix cores) and forms the correction from
- * them, c = (sum_j p_j v_j k_j^T) u - (u.kbar) o; no workspace is used.  Otherwise (or with
- * PLX_DECODE_TWO_PASS) two split-KV passes run: o and kbar first, the correction with the finished u second.
+ * softmax-weighted moment sum_j p_j v_j k_j^T (fp16 products with power-of-two scales, fp32 sums, on the
+ * matrix cores) and forms the correction from them, c = (sum_j p_j v_j k_j^T) u - (u.kbar) o; no
+ * workspace is used.  A head where the two terms exceed the output by more than 2^11 (a key far larger
+ * than the rest dominating the softmax) has its correction formed directly from a second read of its keys.
+ * Otherwise (or with PLX_DECODE_TWO_PASS) two split-KV passes run: o and kbar first, the correction with the
+ * finished u second.
  */
 plx_status parallax_attn_decode(const plx_attn_desc* desc,
                                 const void* q, const void* k_cache, const void* v_cache,
