@@ -31,12 +31,12 @@
 // 32 (w % 4) + [0, 32) of M, and keys 32 (w / 4) + [0, 32) of every tile for all 128 value dims.  Key
 // tiles of 64 rows arrive by direct-to-LDS DMA, four buffers deep; rows are stored 256 bytes each with the
 // 16-byte chunks of row r permuted (slot = chunk ^ f(r)) so that the transpose loads (ds_read_b64_tr_b16)
-// that form the k-major operands, and the row loads of the scores, hit distinct banks.  In the phase that runs
-// the current tile's products, waves 0-3 first compute the next tile's scores (16 keys each,
+// that form the k-major operands, and the row loads of the scores, hit distinct banks.  In the phase that
+// runs the current tile's products, waves 0-3 first compute the next tile's scores (16 keys each,
 // v_mfma_f32_16x16x32_bf16) and its largest |k|, waves 4-7 its largest |v|; after a barrier every wave
 // sets the next tile's scales, waves 0-3 its weights (one key and head per lane), and all waves convert
-// their share of its values.  The running
-// maximum is lazy (it moves only when a tile exceeds it by 8 in log2 units).
+// their share of its values.  The running maximum is lazy (it moves only when a tile exceeds it by 8 in
+// log2 units).
 #include <math.h>
 
 #include <type_traits>
