@@ -293,6 +293,36 @@ def test_moment_decode_outlier_rows(plx, which, e):
     assert err <= BF16_TOL
 
 
+def test_moment_decode_direct_correction_paged(plx):
+    """The direct correction (key rows 2^12 larger: the heads they dominate take it) reads its keys through
+    the page table too: bit-identical to the contiguous decode, with ragged lengths and a window.  Against
+    the oracle the worst head is one that the outliers do not dominate but push near fp32's limit
+    (1.8e-2 here; the two-pass kernels give 2.4e-2 on it)."""
+    B, L, Hq, Hkv = 32, 700, 16, 8
+    _announce("single-read decode: direct correction through a paged cache")
+    w = W.scaled(W.WORKLOADS["decode"], batch=B, seqlen_k=L, heads_q=Hq, heads_kv=Hkv)
+    q, kc, vc, P = W.make_inputs(w, device="cuda", seed=14)
+    kc = kc.clone()
+    kc[:, 200:202] = _pow2(kc[:, 200:202], 12)
+    kp, vp, table = to_pages(kc, vc, 64, seed=5)
+    seqlens = _seqlens(B, L, seed=6)
+    hook = _Hook(plx, plx.PLX_KERNEL_DECODE_MOMENT)
+    try:
+        for window in (0, 600):
+            ref_c = plx.parallax_attn_decode(q, kc, vc, P, seqlens=seqlens, window=window)
+            with hook:
+                out = plx.parallax_attn_decode_paged(q, kp, vp, table, P, seqlens=seqlens, seqlen_k=L, window=window)
+            assert hook.ran(), "the single-read kernel did not run"
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref_c), window
+            ref = _decode_ref(q, kc, vc, P, host(seqlens).astype(int), window)
+            err = rel_err(host(out), ref)
+            print(f"[moment] direct correction paged window={window}: err {err:.2e}", flush=True)
+            assert err <= BF16_TOL
+    finally:
+        hook.close()
+
+
 def test_moment_decode_selection(plx):
     """Below 256 (sequence, key/value head) pairs, with more than two query heads per key/value head, with
     several new tokens or with pages under 64 keys the two-pass kernels run instead."""
