@@ -266,8 +266,9 @@ def test_moment_decode_score_preserving_scale_is_exact(plx, a):
     assert torch.equal(outs, out)
 
 
-@pytest.mark.parametrize("which,e", [("V", 12), ("V", 20), ("K", 6), ("K", 12), ("K", 20)])
-def test_moment_decode_outlier_rows(plx, which, e):
+@pytest.mark.parametrize("which,e,Hq", [("V", 12, 16), ("V", 20, 16), ("K", 6, 16), ("K", 12, 16), ("K", 20, 16),
+                                         ("K", 12, 8)])
+def test_moment_decode_outlier_rows(plx, which, e, Hq):
     """The last two keys of every sequence 2^e larger than the rest (values or keys): the value scale then
     puts the other values 2^e lower in fp16 (still in its normal range), and a key tile's scale follows its
     largest key; against the oracle at the usual bar.
@@ -275,9 +276,9 @@ def test_moment_decode_outlier_rows(plx, which, e):
     Keys 2^12 and more larger dominate their softmax, so kbar is close to them and the moment form's
     M u / l and alpha o are each far larger than their difference; the kernel detects that and forms
     those heads' corrections directly from a second read of their keys."""
-    _announce(f"single-read decode: outlier {which} rows * 2^{e}")
+    _announce(f"single-read decode: outlier {which} rows * 2^{e}, {Hq} query heads")
     B, L = 32, 500
-    w = W.scaled(W.WORKLOADS["decode"], batch=B, seqlen_k=L, heads_q=16, heads_kv=8)
+    w = W.scaled(W.WORKLOADS["decode"], batch=B, seqlen_k=L, heads_q=Hq, heads_kv=8)
     q, kc, vc, P = W.make_inputs(w, device="cuda", seed=13)
     t = (vc if which == "V" else kc).clone()
     t[:, L - 2:] = _pow2(t[:, L - 2:], e)
@@ -285,11 +286,17 @@ def test_moment_decode_outlier_rows(plx, which, e):
         vc = t
     else:
         kc = t
-    out = plx.parallax_attn_decode(q, kc, vc, P)
+    hook = _Hook(plx, plx.PLX_KERNEL_DECODE_MOMENT)
+    try:
+        with hook:
+            out = plx.parallax_attn_decode(q, kc, vc, P)
+        assert hook.ran(), "the single-read kernel did not run"
+    finally:
+        hook.close()
     torch.cuda.synchronize()
     ref = _decode_ref(q, kc, vc, P, [L] * B, 0)
     err = rel_err(host(out), ref)
-    print(f"[moment] outlier {which} 2^{e}: err {err:.2e}", flush=True)
+    print(f"[moment] outlier {which} 2^{e} Hq={Hq}: err {err:.2e}", flush=True)
     assert err <= BF16_TOL
 
 
