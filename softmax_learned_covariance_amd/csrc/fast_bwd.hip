@@ -93,6 +93,7 @@ __device__ __forceinline__ void to_operand(const float* v, float s, f16x8& hi, f
   float e[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) e[j] = v[j] * s;
+  if (lo) pin8(e);
   hi = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
   if (lo) *lo = pack_lo(e, hi);
 }

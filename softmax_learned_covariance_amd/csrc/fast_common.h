@@ -146,6 +146,16 @@ __device__ __forceinline__ f16x8 pack_lo(const float* x, f16x8 hi) {
                x[6] - static_cast<float>(hi[6]), x[7] - static_cast<float>(hi[7]));
 }
 
+// Makes 8 fp32 values opaque to the optimiser at this point (no instruction is emitted).  A hi + lo pair is
+// formed from pinned values: otherwise the compiler may fold the multiply that produced a value into the
+// hi conversion and into the lo subtraction separately (a mixed-precision fma rounds the exact product
+// once, a multiply followed by a conversion rounds it twice), and for a product next to the midpoint of
+// two fp16 values the two roundings pick different neighbours, leaving hi + lo one fp16 step off.
+__device__ __forceinline__ void pin8(float* x) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) asm("" : "+v"(x[j]));
+}
+
 // Sum of the 8 fp16 values of an operand, accumulated in fp32 (v_dot2 with ones).
 __device__ __forceinline__ float sum8(f16x8 v, float acc) {
   const f16x2 one = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};

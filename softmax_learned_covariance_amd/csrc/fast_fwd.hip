@@ -265,6 +265,7 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
           const float x = fmaf(S[kb][t8 + j], cS, -mb);
           e[j] = (!SPLIT && ((kFwdPolyMask >> j) & 1)) ? exp2_fma(x) : __builtin_amdgcn_exp2f(x);
         }
+        if constexpr (SPLIT) pin8(e);
         pB[i] = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
         lpart = sum8(pB[i], lpart);
         if constexpr (SPLIT) {
@@ -370,7 +371,7 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
       const int mt = s >> 1, t8 = (s & 1) * 8;
       float e[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) e[j] = xv[mt][t8 + j] * sX;
+      for (int j = 0; j < 8; ++j) e[j] = xv[mt][t8 + j] * sX;   // (sX is a power of two: x sX is exact)
       xB[s] = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
       if constexpr (SPLIT) xL[s] = pack_lo(e, xB[s]);   // (single-operand rows form theirs below, one at a time)
     }
@@ -428,6 +429,7 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
       float e[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) e[j] = accU[am][t8 + j] * sU;
+      if constexpr (SPLIT) pin8(e);
       xB[s] = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
       if constexpr (SPLIT) xL[s] = pack_lo(e, xB[s]);
 #pragma unroll
@@ -506,6 +508,7 @@ __global__ __launch_bounds__(512) void k_fwd_fast(FwdParams p) {
             const float x = fmaf(S[r], cS, -mb2);
             e[j] = ((!SPLIT && ((kFwdPolyMask >> j) & 1)) ? exp2_fma(x) : __builtin_amdgcn_exp2f(x)) * (R[r] - alpha_s);
           }
+          if constexpr (SPLIT) pin8(e);
           wB[t] = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
           rpart = sum8(wB[t], rpart);
           if constexpr (SPLIT) {
@@ -751,6 +754,10 @@ __global__ __launch_bounds__(512) void k_fwd_probe(FwdParams p) {
           for (int j = 0; j < 8; ++j) {
             e[j] = __builtin_amdgcn_exp2f(fmaf(S[8 * t + j], cS, -mb));
             x[j] = e[j] * R[8 * t + j] * wfac;
+          }
+          if constexpr (SPLIT) {
+            pin8(e);
+            pin8(x);
           }
           pB[t] = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
           wB[t] = pack8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
