@@ -1012,6 +1012,7 @@ struct KeyParams {
   int64_t qstride;     // elements between the consecutive query-row copies q16, do16, u16, e16
   int B, Tq, Tk, Tk_pad, Tq_pad, lo_pad, Hq, Hkv, G, causal, window;
   int D;               // head dim of dk, dv rows
+  int out_keys;        // k_bwd_keys_fast: keys per batch entry in dk, dv (Tk, or the split rows' buffer)
   float scale;
   int row_lo, row_hi, accumulate, n_kb, key_hi;
 };
@@ -1280,8 +1281,8 @@ __global__ __launch_bounds__(256) void k_bwd_keys_fast(KeyParams p) {
   }
   if (key_ok) {
     const float fk = 1.f / C, fv = 1.f / (sG * cV);
-    float* dkr = p.dk + ((static_cast<int64_t>(b) * p.Tk + key) * p.Hkv + g) * p.D;
-    float* dvr = p.dv + ((static_cast<int64_t>(b) * p.Tk + key) * p.Hkv + g) * p.D;
+    float* dkr = p.dk + ((static_cast<int64_t>(b) * p.out_keys + key) * p.Hkv + g) * p.D;
+    float* dvr = p.dv + ((static_cast<int64_t>(b) * p.out_keys + key) * p.Hkv + g) * p.D;
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
@@ -1834,6 +1835,20 @@ __global__ __launch_bounds__(256) void k_zero4x2(float* x, int64_t n4, float* y,
   }
 }
 
+// dk[b, key] += dklo[b, key] and the same for dv, for the first nkeys keys of every batch entry (n4: float4
+// per key; the buffers hold lo_keys and Tk keys per batch entry; 16-byte aligned).
+__global__ __launch_bounds__(256) void k_add_lo(float* dk, float* dv, const float* dklo, const float* dvlo, int B,
+                                                int64_t nkeys, int64_t lo_keys, int64_t Tk, int64_t n4) {
+  const int64_t per_b = nkeys * n4;
+  for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < 2 * B * per_b; i += 256LL * gridDim.x) {
+    const int64_t t = i / (B * per_b), r = i % (B * per_b), b = r / per_b, k = r % per_b;
+    float4* dst = reinterpret_cast<float4*>(t == 0 ? dk : dv) + b * Tk * n4 + k;
+    const float4 a = reinterpret_cast<const float4*>(t == 0 ? dklo : dvlo)[b * lo_keys * n4 + k];
+    const float4 c = *dst;
+    *dst = float4{c.x + a.x, c.y + a.y, c.z + a.z, c.w + a.w};
+  }
+}
+
 // ------------------------------------------------------------------------------------------
 // dP = sum over batch and rows of x du^T: partial sums per row chunk, then a fixed-order sum
 // ------------------------------------------------------------------------------------------
@@ -2008,7 +2023,8 @@ struct BwdWs {
   float* rowmax;  // [B][Hkv][kRowStats][Tq_pad]
   size_t rowmax_n;
   float* dsscale; // [B][Hkv][Tk_pad / 32]
-  int Tq_pad, lo_rows, lo_pad, nchunks;
+  float *dklo, *dvlo;  // [B][lo_keys][Hkv][D]: the split rows' dk, dv, added to the others' at the end
+  int Tq_pad, lo_rows, lo_pad, nchunks, lo_keys;
   size_t bytes;
 };
 
@@ -2043,6 +2059,13 @@ BwdWs bwd_layout(const Geom& g, int split, void* ws) {
   w.rowmax_n = static_cast<size_t>(g.B) * g.Hkv * kRowStats * w.Tq_pad;
   w.rowmax = reinterpret_cast<float*>(base + ws_take(off, w.rowmax_n * sizeof(float)));
   w.dsscale = reinterpret_cast<float*>(base + ws_take(off, static_cast<size_t>(g.B) * g.Hkv * (w.st.Tk_pad / 32) * sizeof(float)));
+  // the keys that rows < split can see, rounded up to the split key kernel's 128-key blocks
+  const int khi = g.causal && split + g.Tk - g.Tq < g.Tk ? split + g.Tk - g.Tq : g.Tk;
+  const int khi_blocks = (khi + 127) / 128 * 128;
+  w.lo_keys = khi > 0 ? (khi_blocks < g.Tk ? khi_blocks : g.Tk) : 0;
+  const size_t lob = static_cast<size_t>(g.B) * w.lo_keys * g.Hkv * g.d * sizeof(float);
+  w.dklo = reinterpret_cast<float*>(base + ws_take(off, lob));
+  w.dvlo = reinterpret_cast<float*>(base + ws_take(off, lob));
   w.bytes = off;
   return w;
 }
@@ -2140,7 +2163,7 @@ hipError_t bwd_impl(const Geom& g, const BwdArgs& a, int split_rows, void* ws, h
   rp.rows_per_block = G > 4 ? 32 : 32 * 4 / G;   // split-row kernel: four waves of 32 rows
   const int hsplit = G > 4 ? G / 4 : 1;           // ... and two blocks per group when G = 8
   // The kernels for rows < split (few blocks, bound by latency) run on a side lane beside the main
-  // ones: the row kernel beside the du kernel, the key kernel beside the dq kernel.  The fp16 query
+  // ones: the row kernel beside the du kernel, the key kernel beside the key-major one.  The fp16 query
   // tiles of q and dout are first read by the key-major kernel, so their staging also runs on the
   // side lane beside du.
   const bool use_side = split > 0 && split < g.Tq;
@@ -2248,6 +2271,27 @@ hipError_t bwd_impl(const Geom& g, const BwdArgs& a, int split_rows, void* ws, h
   kp.scale = g.scale;
   kp.n_kb = (g.Tk + 127) / 128;
   kp.key_hi = g.Tk;
+  kp.out_keys = g.Tk;
+  // rows < split: only keys those rows can see, written to their own buffers by the hi + lo key kernel on
+  // the side lane while the key-major kernel runs, and added to dk, dv after both
+  const int off = g.Tk - g.Tq;
+  int khi = g.causal ? split - 1 + off + 1 : g.Tk;
+  khi = khi > g.Tk ? g.Tk : khi;
+  const bool lo_keys = split > 0 && khi > 0;
+  side = use_side ? side_fork(stream) : SideLane{stream, stream};
+  if (lo_keys) {
+    KeyParams k2 = kp;
+    k2.row_lo = 0;
+    k2.row_hi = split;
+    k2.accumulate = 0;
+    k2.key_hi = khi;
+    k2.n_kb = (khi + 127) / 128;
+    k2.dk = w.dklo;
+    k2.dv = w.dvlo;
+    k2.out_keys = w.lo_keys;
+    if (d64) hipLaunchKernelGGL((k_bwd_keys_fast<true, 64>), dim3(g.B * g.Hkv * k2.n_kb), dim3(256), 0, side.stream, k2);
+    else hipLaunchKernelGGL((k_bwd_keys_fast<true, kD>), dim3(g.B * g.Hkv * k2.n_kb), dim3(256), 0, side.stream, k2);
+  }
   {
     // every key block, rows >= split, writing
     KeyParams k2 = kp;
@@ -2259,24 +2303,6 @@ hipError_t bwd_impl(const Geom& g, const BwdArgs& a, int split_rows, void* ws, h
     if (d64) hipLaunchKernelGGL(k_bwd_keys_pipe<64>, dim3(g.B * g.Hkv * k2.n_kb), dim3(512), 0, stream, k2);
     else hipLaunchKernelGGL(k_bwd_keys_pipe<kD>, dim3(g.B * g.Hkv * k2.n_kb), dim3(512), 0, stream, k2);
     mark_end(PLX_KERNEL_BWD_KEYS, stream);
-  }
-  // the key kernel for rows < split adds onto dk, dv: the side lane waits for the key-major kernel
-  side = use_side ? side_fork(stream) : SideLane{stream, stream};
-  if (split > 0) {
-    // rows < split: only keys those rows can see, accumulated on top
-    const int off = g.Tk - g.Tq;
-    int khi = g.causal ? split - 1 + off + 1 : g.Tk;
-    khi = khi > g.Tk ? g.Tk : khi;
-    if (khi > 0) {
-      KeyParams k2 = kp;
-      k2.row_lo = 0;
-      k2.row_hi = split;
-      k2.accumulate = 1;
-      k2.key_hi = khi;
-      k2.n_kb = (khi + 127) / 128;
-      if (d64) hipLaunchKernelGGL((k_bwd_keys_fast<true, 64>), dim3(g.B * g.Hkv * k2.n_kb), dim3(256), 0, side.stream, k2);
-      else hipLaunchKernelGGL((k_bwd_keys_fast<true, kD>), dim3(g.B * g.Hkv * k2.n_kb), dim3(256), 0, side.stream, k2);
-    }
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -2313,7 +2339,15 @@ hipError_t bwd_impl(const Geom& g, const BwdArgs& a, int split_rows, void* ws, h
   if (e != hipSuccess) return e;
   e = side_join(dpl);   // (the dP work, and whatever followed it on the side lane)
   if (e != hipSuccess) return e;
-  return side_join(side);
+  e = side_join(side);
+  if (e != hipSuccess) return e;
+  if (lo_keys) {
+    const int64_t n4 = static_cast<int64_t>(g.Hkv) * g.d / 4;
+    hipLaunchKernelGGL(k_add_lo, dim3(256), dim3(256), 0, stream, dk, dv, w.dklo, w.dvlo, g.B,
+                       static_cast<int64_t>(khi), static_cast<int64_t>(w.lo_keys), static_cast<int64_t>(g.Tk), n4);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 }  // namespace
