@@ -80,7 +80,7 @@ typedef struct {
   float   softmax_scale;  /* <= 0 selects 1/sqrt(head_dim) */
   int32_t dtype;          /* plx_dtype of q, k, v, P, dout */
   int32_t p_per_query;    /* 0: P is [Hq][d][d]; 1: P is [B][Tq][Hq][d][d] (forward only) */
-  int32_t split_rows;     /* bf16 fast path: query rows < max(split_rows, 16) use hi + lo fp16 operand pairs (about 22 bits); < 0 selects the default, 256 */
+  int32_t split_rows;     /* bf16 fast path: the first max(split_rows, 16) query rows that see a key (causal with Tq > Tk: counted from row Tq - Tk) use hi + lo fp16 operand pairs (about 22 bits); < 0 selects the default, 256 */
   int32_t out_dtype;      /* plx_dtype of `out` in the forwards and decodes (0 = PLX_F32). PLX_BF16 (rounded to
                              nearest even from the fp32 result) needs the bf16 fast path; the backwards read
                              an fp32 `out` and require PLX_F32 */

@@ -76,6 +76,8 @@ def visible_range(i: int, Tq: int, Tk: int, causal: bool, window: int):
 
 def _softmax_rows(s, mask):
     """Softmax of each row over its visible entries; rows with no visible key give all-zero weights."""
+    if s.shape[1] == 0:   # a block of rows none of which sees a key
+        return np.zeros_like(s), np.full(s.shape[0], -np.inf, dtype=s.dtype)
     s = np.where(mask, s, -np.inf)
     mx = np.max(s, axis=1, keepdims=True)
     mx = np.where(np.isfinite(mx), mx, 0.0)

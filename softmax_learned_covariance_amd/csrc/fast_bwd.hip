@@ -2070,7 +2070,10 @@ BwdWs bwd_layout(const Geom& g, int split, void* ws) {
   return w;
 }
 
-int bwd_split(const Geom& g) { return 256 < g.Tq ? 256 : g.Tq; }
+int bwd_split(const Geom& g) {
+  const int s = 256 + rows_without_keys(g);
+  return s < g.Tq ? s : g.Tq;
+}
 
 }  // namespace
 
@@ -2107,8 +2110,8 @@ hipError_t bwd_impl(const Geom& g, const BwdArgs& a, int split_rows, void* ws, h
   const float *out = a.out, *lse = a.lse, *kbar = a.kbar, *osa = a.osa;
   float *dq = a.dq, *dk = a.dk, *dv = a.dv, *dP = a.dP;
   // The workspace is sized for the default split; a larger request is clamped to it.
-  int split = split_rows < 0 ? bwd_split(g) : split_rows;
-  if (split < kMinSplitRows) split = kMinSplitRows;
+  int split = split_rows < 0 ? bwd_split(g) : split_rows + rows_without_keys(g);
+  if (split < kMinSplitRows + rows_without_keys(g)) split = kMinSplitRows + rows_without_keys(g);
   if (split > bwd_split(g)) split = bwd_split(g);
   const BwdWs w = bwd_layout(g, bwd_split(g), ws);
   const int G = g.Hq / g.Hkv;

@@ -856,7 +856,7 @@ hipError_t launch_fast_fwd(const Geom& g, const void* q, const void* k, const vo
                            int split_rows, void* ws, hipStream_t stream) {
   const Staging s = staging_layout(ws, g.B, g.Tk, g.Hkv, g.Hq, false, fwd_dh(g));
   float* o_ws = reinterpret_cast<float*>(static_cast<char*>(ws) + s.bytes);
-  int split = split_rows < kMinSplitRows ? kMinSplitRows : split_rows;
+  int split = (split_rows < kMinSplitRows ? kMinSplitRows : split_rows) + rows_without_keys(g);
   if (split > g.Tq) split = g.Tq;
   hipError_t e = launch_staging(s, q, static_cast<int64_t>(g.B) * g.Tq * g.Hq * g.d, k, v, P, g.B, g.Tk,
                                 g.Hkv, g.Hq, stream, nullptr, 0, 0, g.d);
@@ -929,7 +929,7 @@ hipError_t launch_fast_probe(const Geom& g, const void* q, const void* k, const 
                              void* out, float* lse, float* osa, float* rk, float* cor, int split_rows, void* ws,
                              hipStream_t stream) {
   const Staging s = staging_layout(ws, g.B, g.Tk, g.Hkv, g.Hq, false, fwd_dh(g));
-  int split = split_rows < kMinSplitRows ? kMinSplitRows : split_rows;
+  int split = (split_rows < kMinSplitRows ? kMinSplitRows : split_rows) + rows_without_keys(g);
   if (split > g.Tq) split = g.Tq;
   const int64_t q_elems = static_cast<int64_t>(g.B) * g.Tq * g.Hq * g.d;
   // K/V into their fp16 tile layouts; max |q|, |k|, |v|, |rho| for the operand scales (no projector)

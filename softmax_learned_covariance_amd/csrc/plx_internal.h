@@ -18,11 +18,17 @@ struct Geom {
   int out_bf16;      // 1: `out` of the forwards and decodes is bf16 (fast paths only)
 };
 
+// Query rows that see no key: with a causal mask (bottom-right aligned) and more query rows than keys, the
+// rows below Tq - Tk.  split_rows counts rows from the first one that sees a key, since the rows that see
+// only a handful of keys are the ones that need hi + lo operand pairs.
+inline int rows_without_keys(const Geom& g) { return g.causal && g.Tq > g.Tk ? g.Tq - g.Tk : 0; }
+
 // bf16 fast path: the first query rows see only a few keys, and their correction terms cancel
 // badly in single fp16 operands (max|err|/rms near 4e-2 in the first rows' dq and the first
 // keys' dk when they do).  Rows below this bound always take the hi + lo operand pairs, whatever
 // split the caller asks for.
 constexpr int kMinSplitRows = 16;
+
 
 // ---- generic kernels: fp32 arithmetic on fp32 or bf16 inputs, any head_dim <= 128 ----
 

@@ -166,6 +166,7 @@ def test_bf16_backward_small(plx, T):
     (129, 257, False, 64, 8, -1),    # bidirectional window, more keys than queries
     (200, 333, True, 0, 8, -1),      # causal, more keys than queries
     (333, 200, True, 0, 8, -1),      # causal, more queries than keys
+    (600, 200, True, 0, 8, -1),      # causal, whole row blocks (and all split rows) with no visible key
     (257, 257, True, 0, 16, -1),     # one query head per key/value head
     (257, 257, True, 0, 4, -1),      # four query heads per key/value head
     (300, 300, True, 0, 8, 0),       # smallest split: rows >= 16 on single fp16 operands

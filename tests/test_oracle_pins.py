@@ -26,3 +26,26 @@ def test_float32_timing_mode():
     for g, r in zip(got, ref):
         assert np.max(np.abs(g - r)) <= 1e-4 * max(1.0, np.max(np.abs(r)))
     assert oracle.fwd(q, k, v, P)[0].dtype == np.float64
+
+
+def test_rows_without_keys():
+    """Causal with more query rows than keys (bottom-right aligned): whole row blocks see no key.  Those
+    rows give zero output and gradients and lse = -inf (all-zero weights); the others equal the same
+    operator on the last Tk query rows alone, where the mask is the plain causal one."""
+    import numpy as np
+    rng = np.random.default_rng(1)
+    B, Tq, Tk, Hq, Hkv, d = 1, 300, 40, 2, 1, 8
+    q = rng.standard_normal((B, Tq, Hq, d))
+    k, v = rng.standard_normal((B, Tk, Hkv, d)), rng.standard_normal((B, Tk, Hkv, d))
+    P = rng.standard_normal((Hq, d, d)) * 0.1
+    dout = rng.standard_normal((B, Tq, Hq, d))
+    out, lse, kbar, o = oracle.fwd(q, k, v, P, causal=True)
+    dq, dk, dv, dP = oracle.bwd(q, k, v, P, dout, causal=True)
+    e = Tq - Tk
+    assert np.all(out[:, :e] == 0) and np.all(o[:, :e] == 0) and np.all(dq[:, :e] == 0)
+    assert np.all(np.isneginf(lse[:, :, :e]))
+    tail = oracle.fwd(q[:, e:], k, v, P, causal=True)
+    gtail = oracle.bwd(q[:, e:], k, v, P, dout[:, e:], causal=True)
+    for got, want in ((out[:, e:], tail[0]), (lse[:, :, e:], tail[1]), (dq[:, e:], gtail[0]), (dk, gtail[1]),
+                      (dv, gtail[2]), (dP, gtail[3])):
+        assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
